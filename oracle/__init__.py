@@ -1,0 +1,190 @@
+"""CPU oracle for the ADAMAS decode path -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never loads it and
+shares no code with it.
+
+The arithmetic lives in ``adamas_oracle.c`` (plain scalar C, built with gcc,
+``-O2 -ffp-contract=off``, OpenMP only across independent heads).  This module
+is marshalling: numpy arrays in, numpy arrays out.  Citations in the C file
+refer to the ADAMAS article (www.lnwmold.com/news/826806) by section:
+§2.1 Hadamard rotation, §2.2 bucketing, §2.3 Manhattan distance, §3.1 packing,
+§5.2 token budget, §6 final attention.
+
+Parity status per function (what pins it is listed in the test-suite):
+  fwht / encode            pinned (closed forms, hand-worked codes)
+  manhattan / score        pinned (brute force, closed-form GEMM identity)
+  select_topk              pinned (exhaustive brute force on tiny inputs)
+  sparse_attend            pinned (dense attention at budget = n, budget = 1)
+  decode_step              pinned by composition of the above
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "adamas_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle shared library with gcc (no GPU toolchain)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+               "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.ora_fwht_f32.argtypes = [P, i32]
+    lib.ora_hadamard_orthonormal_f64.argtypes = [P, P, i32]
+    lib.ora_encode_vec_f32.argtypes = [P, i32, P, P, P]
+    lib.ora_encode_keys.argtypes = [P, i32, i32, i32, i64, i32, P, i64, i64]
+    lib.ora_manhattan.argtypes = [P, P, i32]
+    lib.ora_manhattan.restype = ctypes.c_uint32
+    lib.ora_score.argtypes = [P, P, i32, i32, i32, i32, i64, i64, P]
+    lib.ora_select_row.argtypes = [P, i64, i32, P]
+    lib.ora_select_topk.argtypes = [P, i32, i32, i64, i32, P]
+    lib.ora_sparse_attend.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f64, P, P]
+    lib.ora_decode_step.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, f64, P, P, P]
+    lib.ora_f64_to_bf16.argtypes = [f64]
+    lib.ora_f64_to_bf16.restype = ctypes.c_uint16
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _dtype_tag(a: np.ndarray) -> int:
+    """fp32 arrays are float32; bf16 arrays are carried as uint16 bit patterns."""
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle takes float32 or bf16-as-uint16 arrays, got {a.dtype}")
+
+
+# ---------------------------------------------------------------- rotation
+def fwht_f32(x: np.ndarray) -> np.ndarray:
+    """Unnormalised Sylvester-order FWHT of one vector, binary32 (§2.1)."""
+    y = np.ascontiguousarray(x, dtype=np.float32).copy()
+    _load().ora_fwht_f32(_ptr(y), y.shape[-1])
+    return y
+
+
+def hadamard_orthonormal_f64(x: np.ndarray) -> np.ndarray:
+    """H x / sqrt(d) in binary64 (§2.1's orthonormal rotation)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    _load().ora_hadamard_orthonormal_f64(_ptr(x), _ptr(y), x.shape[-1])
+    return y
+
+
+def encode_vec(x: np.ndarray):
+    """One fp32 vector -> (packed bytes, rotated values, codes)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    packed = np.empty(d // 4, np.uint8)
+    y = np.empty(d, np.float32)
+    codes = np.empty(d, np.int32)
+    _load().ora_encode_vec_f32(_ptr(x), d, _ptr(packed), _ptr(y), _ptr(codes))
+    return packed, y, codes
+
+
+def encode_keys(x: np.ndarray, codes: np.ndarray | None = None, cap: int | None = None,
+                pos: int = 0) -> np.ndarray:
+    """x[batch][heads][n][d] -> codes[batch][heads][cap][d/4], rows [pos, pos+n)."""
+    x = np.ascontiguousarray(x)
+    batch, heads, n, d = x.shape
+    if cap is None:
+        cap = pos + n
+    if codes is None:
+        codes = np.zeros((batch, heads, cap, d // 4), np.uint8)
+    assert codes.shape == (batch, heads, cap, d // 4) and codes.dtype == np.uint8
+    _load().ora_encode_keys(_ptr(x), _dtype_tag(x), batch, heads, n, d, _ptr(codes), cap, pos)
+    return codes
+
+
+# ---------------------------------------------------------------- scoring
+def manhattan(qrow: np.ndarray, krow: np.ndarray, d: int) -> int:
+    return int(_load().ora_manhattan(_ptr(np.ascontiguousarray(qrow, np.uint8)),
+                                     _ptr(np.ascontiguousarray(krow, np.uint8)), d))
+
+
+def score(q_codes: np.ndarray, k_codes: np.ndarray, n_ctx: int | None = None) -> np.ndarray:
+    """q_codes[B][Hq][d/4], k_codes[B][Hkv][cap][d/4] -> dist[B][Hq][n_ctx] (uint16)."""
+    B, Hq, rb = q_codes.shape
+    _, Hkv, cap, rb2 = k_codes.shape
+    assert rb == rb2
+    if n_ctx is None:
+        n_ctx = cap
+    dist = np.empty((B, Hq, n_ctx), np.uint16)
+    _load().ora_score(_ptr(np.ascontiguousarray(q_codes)), _ptr(np.ascontiguousarray(k_codes)),
+                      B, Hq, Hkv, rb * 4, cap, n_ctx, _ptr(dist))
+    return dist
+
+
+def select_topk(dist: np.ndarray, budget: int) -> np.ndarray:
+    """dist[B][Hq][n] -> idx[B][Hq][budget] int32, ascending, -1 padded (§5.2)."""
+    dist = np.ascontiguousarray(dist, np.uint16)
+    B, Hq, n = dist.shape
+    idx = np.empty((B, Hq, budget), np.int32)
+    _load().ora_select_topk(_ptr(dist), B, Hq, n, budget, _ptr(idx))
+    return idx
+
+
+# ---------------------------------------------------------------- attention
+def sparse_attend(q, k, v, idx, scale: float = 0.0):
+    """q[B][Hq][d], k/v[B][Hkv][cap][d], idx[B][Hq][budget] -> (out, out64)."""
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    idx = np.ascontiguousarray(idx, np.int32)
+    dt = _dtype_tag(q)
+    assert _dtype_tag(k) == dt and _dtype_tag(v) == dt
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    budget = idx.shape[-1]
+    out = np.empty((B, Hq, d), q.dtype)
+    out64 = np.empty((B, Hq, d), np.float64)
+    _load().ora_sparse_attend(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(idx), B, Hq, Hkv, d, cap,
+                              budget, float(scale), _ptr(out), _ptr(out64))
+    return out, out64
+
+
+def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0):
+    """Full step for one layer -> (out, out64, idx)."""
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    k_codes = np.ascontiguousarray(k_codes, np.uint8)
+    dt = _dtype_tag(q)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    out = np.empty((B, Hq, d), q.dtype)
+    out64 = np.empty((B, Hq, d), np.float64)
+    idx = np.empty((B, Hq, budget), np.int32)
+    _load().ora_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d, cap,
+                            n_ctx, budget, float(scale), _ptr(out), _ptr(out64), _ptr(idx))
+    return out, out64, idx
+
+
+def f64_to_bf16_bits(x: float) -> int:
+    return int(_load().ora_f64_to_bf16(float(x)))

@@ -1,0 +1,373 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against a closed form, a hand-worked example, an
+invariant the ADAMAS article (www.lnwmold.com/news/826806) states, or brute
+force on tiny inputs -- never against a retyped copy of its own formula.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# independent helpers (not the oracle's code paths)
+def sylvester(d: int) -> np.ndarray:
+    """H_d from the recursion [[H, H], [H, -H]] (§2.1 recursive construction)."""
+    h = np.ones((1, 1), np.int64)
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """Bytes -> 2-bit codes, first code in the top bits, via np.unpackbits."""
+    bits = np.unpackbits(np.asarray(packed, np.uint8).reshape(-1, 1), axis=1)  # MSB first
+    pairs = bits.reshape(-1, 4, 2)
+    return (pairs[..., 0] * 2 + pairs[..., 1]).reshape(np.asarray(packed).shape[:-1] + (-1,))
+
+
+def pack_codes(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, np.uint8).reshape(-1, 4)
+    bits = np.stack([c >> 1 & 1, c & 1], axis=-1).reshape(-1, 8)
+    return np.packbits(bits, axis=1).reshape(-1)
+
+
+def thermometer(codes: np.ndarray) -> np.ndarray:
+    """U(c) in {0,1}^3 with <U(a), U(b)> = min(a, b)."""
+    c = np.asarray(codes)[..., None]
+    return (c >= np.array([1, 2, 3])).astype(np.int64).reshape(c.shape[:-2] + (-1,))
+
+
+# --------------------------------------------------------------------------
+# §2.1 rotation
+@pytest.mark.parametrize("d", [2, 4, 8, 16, 32, 64, 128, 256])
+def test_fwht_columns_are_sylvester_hadamard(ora, d):
+    H = sylvester(d)
+    cols = np.stack([ora.fwht_f32(np.eye(d, dtype=np.float32)[j]) for j in range(d)], axis=1)
+    assert np.array_equal(cols.astype(np.int64), H)
+    i = np.arange(d)
+    popc = np.vectorize(lambda x: bin(x).count("1"))(i[:, None] & i[None, :])
+    assert np.array_equal(H, (-1) ** popc)
+    assert np.array_equal(H, H.T)
+    assert np.array_equal(H @ H.T, d * np.eye(d, dtype=np.int64))
+
+
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_fwht_exact_on_integers(ora, d):
+    # |x| * d < 2^24 keeps every partial sum exact in binary32
+    x = synth.integer_values((50, d), -1000, 1000, seed=d)
+    H = sylvester(d)
+    for row in x:
+        y = ora.fwht_f32(row)
+        assert np.array_equal(y.astype(np.int64), H @ row.astype(np.int64))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwht_f32_within_rounding_bound(ora, d):
+    rng = np.random.default_rng(3)
+    H = sylvester(d).astype(np.float64)
+    for _ in range(20):
+        x = (rng.standard_normal(d) * np.exp(rng.standard_normal(d))).astype(np.float32)
+        y = ora.fwht_f32(x).astype(np.float64)
+        exact = H @ x.astype(np.float64)
+        # log2(d) rounded adds, each with relative error <= 2^-24 of a partial sum
+        bound = math.log2(d) * 2.0 ** -24 * np.abs(H) @ np.abs(x.astype(np.float64)) * 1.01
+        assert np.all(np.abs(y - exact) <= bound)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_orthonormal_rotation_preserves_dot_and_norm(ora, d):
+    rng = np.random.default_rng(d)
+    H = sylvester(d) / math.sqrt(d)
+    assert np.allclose(H @ H.T, np.eye(d), atol=1e-15 * d)
+    for _ in range(20):
+        q, k = rng.standard_normal(d), rng.standard_normal(d)
+        hq, hk = ora.hadamard_orthonormal_f64(q), ora.hadamard_orthonormal_f64(k)
+        assert abs(hq @ hk - q @ k) <= 1e-12 * np.linalg.norm(q) * np.linalg.norm(k)
+        assert abs(np.linalg.norm(hq) - np.linalg.norm(q)) <= 1e-12 * np.linalg.norm(q)
+        assert np.max(np.abs(hq)) >= np.linalg.norm(q) / math.sqrt(d) * (1 - 1e-12)
+
+
+# --------------------------------------------------------------------------
+# §2.2 bucketing + §3.1 packing
+def _golden_encode_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "encode_hand_worked.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            d, x, y, c, hexes = (s.strip() for s in line.split("|"))
+            cases.append((int(d), [float(t) for t in x.split(",")], [float(t) for t in y.split(",")],
+                          [int(t) for t in c.split(",")], bytes.fromhex(hexes.replace(" ", ""))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_encode_cases(), ids=lambda c: f"d{c[0]}-{c[4].hex()}")
+def test_encode_hand_worked(ora, case):
+    d, x, y, codes, packed = case
+    p, yy, cc = ora.encode_vec(np.array(x, np.float32))
+    assert yy.tolist() == y
+    assert cc.tolist() == codes
+    assert bytes(p) == packed
+    assert unpack_codes(p).tolist() == codes
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_encode_unit_vectors_closed_form(ora, d):
+    # H e_j is column j of H (entries +-1, absmax 1): +1 -> code 3, -1 -> code 0
+    H = sylvester(d)
+    for j in range(d):
+        p, _, c = ora.encode_vec(np.eye(d, dtype=np.float32)[j])
+        want = np.where(H[:, j] > 0, 3, 0)
+        assert np.array_equal(c, want)
+        assert np.array_equal(p, pack_codes(want))
+
+
+def test_encode_scale_and_sign_properties(ora):
+    rng = np.random.default_rng(11)
+    for d in (64, 128):
+        for _ in range(200):
+            x = rng.standard_normal(d).astype(np.float32)
+            p, y, c = ora.encode_vec(x)
+            # power-of-two scaling is exact in binary32 -> identical codes
+            for s in (2.0 ** -20, 0.5, 4.0, 2.0 ** 30):
+                assert np.array_equal(ora.encode_vec(x * np.float32(s))[0], p)
+            # negation mirrors the codes when no rotated value sits on a threshold
+            a = np.max(np.abs(y))
+            if not np.any(np.isin(y, [0.0, a / 2, -a / 2])):
+                assert np.array_equal(ora.encode_vec(-x)[2], 3 - c)
+            # the definition, by brute force over the rotated values
+            want = np.select([y < -0.5 * a, y < 0, y < 0.5 * a], [0, 1, 2], 3)
+            assert np.array_equal(c, want)
+
+
+def test_encode_keys_layout(ora):
+    # codes land at rows [pos, pos+n) of a [batch][heads][cap][d/4] cache
+    x = synth.integer_values((2, 3, 5, 64), -9, 9, seed=1)
+    codes = np.full((2, 3, 9, 16), 0x5A, np.uint8)
+    ora.encode_keys(x, codes, cap=9, pos=3)
+    for b, h, t in itertools.product(range(2), range(3), range(9)):
+        if 3 <= t < 8:
+            assert np.array_equal(codes[b, h, t], ora.encode_vec(x[b, h, t - 3])[0])
+        else:
+            assert np.all(codes[b, h, t] == 0x5A)
+
+
+def test_encode_keys_bf16_widening_exact(ora):
+    import torch
+    x = synth.random_values((1, 2, 40, 128), torch.bfloat16, seed=4)
+    xb = synth.to_numpy_bits(x)
+    c1 = ora.encode_keys(xb)
+    c2 = ora.encode_keys(x.float().numpy())
+    assert np.array_equal(c1, c2)
+
+
+# --------------------------------------------------------------------------
+# §2.3 Manhattan distance
+def test_manhattan_exhaustive_small(ora):
+    # every pair of 2-bit code vectors of length 4 (one byte each)
+    allc = np.array(list(itertools.product(range(4), repeat=4)))
+    for a in allc:
+        for b in allc[::7]:
+            got = ora.manhattan(pack_codes(a), pack_codes(b), 4)
+            assert got == int(np.abs(a - b).sum())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_score_gemm_identity_and_metric(ora, d):
+    rng = np.random.default_rng(d)
+    B, Hq, Hkv, n = 2, 6, 3, 300
+    qc = rng.integers(0, 4, size=(B, Hq, d))
+    kc = rng.integers(0, 4, size=(B, Hkv, n, d))
+    qp = pack_codes(qc.reshape(-1, d).reshape(-1)).reshape(B, Hq, d // 4)
+    kp = pack_codes(kc.reshape(-1)).reshape(B, Hkv, n, d // 4)
+    dist = ora.score(qp, kp)
+    G = Hq // Hkv
+    # D = sum(q) + sum(k) - 2 <U(q), U(k)> with the thermometer expansion U
+    for b in range(B):
+        for h in range(Hq):
+            uq = thermometer(qc[b, h])
+            uk = thermometer(kc[b, h // G])
+            want = qc[b, h].sum() + kc[b, h // G].sum(axis=1) - 2 * (uk @ uq)
+            assert np.array_equal(dist[b, h].astype(np.int64), want)
+    # metric facts on packed rows
+    zeros, threes = pack_codes(np.zeros(d, int)), pack_codes(np.full(d, 3))
+    assert ora.manhattan(zeros, threes, d) == 3 * d
+    assert ora.manhattan(threes, threes, d) == 0
+    e0 = ora.encode_vec(np.eye(d, dtype=np.float32)[0])[0]
+    e1 = ora.encode_vec(np.eye(d, dtype=np.float32)[1])[0]
+    assert ora.manhattan(e0, e1, d) == 3 * d // 2
+    for _ in range(50):
+        a, b, c = (pack_codes(rng.integers(0, 4, d)) for _ in range(3))
+        ab, ba = ora.manhattan(a, b, d), ora.manhattan(b, a, d)
+        assert ab == ba and 0 <= ab <= 3 * d
+        assert ab <= ora.manhattan(a, c, d) + ora.manhattan(c, b, d)
+
+
+def test_score_respects_n_ctx_and_gqa_mapping(ora):
+    rng = np.random.default_rng(5)
+    d, n, cap = 64, 37, 50
+    kc = rng.integers(0, 4, size=(1, 2, cap, d))
+    qc = rng.integers(0, 4, size=(1, 4, d))
+    kp = pack_codes(kc.reshape(-1)).reshape(1, 2, cap, d // 4)
+    qp = pack_codes(qc.reshape(-1)).reshape(1, 4, d // 4)
+    dist = ora.score(qp, kp, n_ctx=n)
+    assert dist.shape == (1, 4, n)
+    for h in range(4):
+        want = np.abs(qc[0, h][None, :] - kc[0, h // 2, :n]).sum(axis=1)
+        assert np.array_equal(dist[0, h], want)
+
+
+# --------------------------------------------------------------------------
+# §5.2 budget selection
+def brute_select(dvec, budget):
+    """Rank counting: token t is kept iff fewer than `budget` tokens precede
+    it in (distance, index) order.  No sorting involved."""
+    n = len(dvec)
+    keep = [t for t in range(n)
+            if sum(1 for u in range(n) if (dvec[u], u) < (dvec[t], t)) < budget]
+    return keep + [-1] * (budget - len(keep))
+
+
+def test_select_exhaustive_tiny(ora):
+    for n in range(1, 7):
+        vecs = np.array(list(itertools.product(range(4), repeat=n)), np.uint16)
+        for budget in range(1, n + 3):
+            got = ora.select_topk(vecs.reshape(1, -1, n), budget)[0]
+            for row, dv in zip(got, vecs):
+                assert row.tolist() == brute_select(dv.tolist(), budget)
+
+
+def test_select_ties_lowest_index(ora):
+    d = np.full((1, 1, 1000), 77, np.uint16)
+    assert ora.select_topk(d, 64)[0, 0].tolist() == list(range(64))
+    d[0, 0, 500:] = 76   # the 500 smaller ones win, ties fill from index 0
+    got = ora.select_topk(d, 600)[0, 0]
+    assert got.tolist() == list(range(100)) + list(range(500, 1000))
+
+
+def test_select_random_against_brute(ora):
+    rng = np.random.default_rng(9)
+    for n in (5, 17, 40):
+        for budget in (1, 3, 16, 50):
+            d = rng.integers(0, 8, size=(3, 2, n)).astype(np.uint16)
+            got = ora.select_topk(d, budget)
+            for b in range(3):
+                for h in range(2):
+                    assert got[b, h].tolist() == brute_select(d[b, h].tolist(), budget)
+
+
+# --------------------------------------------------------------------------
+# §6 attention over the selected rows
+def dense_attention(q, k, v, scale):
+    s = (k @ q) * scale
+    w = np.exp(s - s.max())
+    return (w / w.sum()) @ v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attend_full_budget_equals_dense(ora, dtype):
+    import torch
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    B, Hq, Hkv, n, d = 2, 4, 2, 33, 64
+    q = synth.random_values((B, Hq, d), dt, 1)
+    k = synth.random_values((B, Hkv, n, d), dt, 2)
+    v = synth.random_values((B, Hkv, n, d), dt, 3)
+    idx = np.tile(np.arange(n, dtype=np.int32), (B, Hq, 1))
+    out, out64 = ora.sparse_attend(*(synth.to_numpy_bits(t) for t in (q, k, v)), idx)
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    for b in range(B):
+        for h in range(Hq):
+            want = dense_attention(qd[b, h], kd[b, h // 2], vd[b, h // 2], 1 / math.sqrt(d))
+            assert np.allclose(out64[b, h], want, rtol=1e-13, atol=1e-13)
+
+
+def test_attend_single_row_is_exact_v(ora):
+    import torch
+    for dt in (torch.float32, torch.bfloat16):
+        q = synth.random_values((1, 2, 128), dt, 5)
+        k = synth.random_values((1, 2, 10, 128), dt, 6)
+        v = synth.random_values((1, 2, 10, 128), dt, 7)
+        idx = np.array([[[3, -1, -1]], [[7, -1, -1]]], np.int32).reshape(1, 2, 3)
+        out, _ = ora.sparse_attend(*(synth.to_numpy_bits(t) for t in (q, k, v)), idx)
+        vb = synth.to_numpy_bits(v)
+        assert np.array_equal(out[0, 0], vb[0, 0, 3]) and np.array_equal(out[0, 1], vb[0, 1, 7])
+
+
+def test_attend_two_rows_closed_form(ora):
+    q = np.array([[[1.0, 0, 0, 0]]], np.float32)
+    k = np.array([[[[2.0, 0, 0, 0], [0.0, 0, 0, 0]]]], np.float32)
+    v = np.array([[[[1.0, 2, 3, 4], [5.0, 6, 7, 8]]]], np.float32)
+    idx = np.array([[[0, 1]]], np.int32)
+    _, o = ora.sparse_attend(q, k, v, idx, scale=1.0)
+    p0 = 1 / (1 + math.exp(-2.0))   # logistic of s0 - s1 = 2
+    vd = v.astype(np.float64)
+    assert np.allclose(o[0, 0], p0 * vd[0, 0, 0] + (1 - p0) * vd[0, 0, 1], rtol=1e-14, atol=0)
+
+
+def test_attend_order_and_padding_invariance(ora):
+    import torch
+    q = synth.random_values((1, 1, 64), torch.float32, 8)
+    k = synth.random_values((1, 1, 50, 64), torch.float32, 9)
+    v = synth.random_values((1, 1, 50, 64), torch.float32, 10)
+    a = np.array([[[4, 9, 13, 40]]], np.int32)
+    b = np.array([[[40, -1, 13, 4, -1, 9]]], np.int32)
+    _, oa = ora.sparse_attend(q.numpy(), k.numpy(), v.numpy(), a)
+    _, ob = ora.sparse_attend(q.numpy(), k.numpy(), v.numpy(), b)
+    assert np.allclose(oa, ob, rtol=1e-14, atol=1e-15)
+    vs = v.numpy()[0, 0, [4, 9, 13, 40]]
+    assert np.all(oa[0, 0] <= vs.max(axis=0) + 1e-12) and np.all(oa[0, 0] >= vs.min(axis=0) - 1e-12)
+
+
+def test_f64_to_bf16_correct_rounding(ora):
+    rng = np.random.default_rng(2)
+    xs = list(rng.standard_normal(3000) * np.exp(rng.uniform(-40, 40, 3000)))
+    # halfway cases between adjacent bf16 values: ties go to the even pattern
+    xs += [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 2.0 ** -133 * 1.5]
+    for x in xs:
+        bits = ora.f64_to_bf16_bits(x)
+        val = np.array([bits << 16], np.uint32).view(np.float32)[0]
+        # neighbours in bf16: step the pattern by one
+        def as_f(b):
+            return Fraction(float(np.array([b << 16], np.uint32).view(np.float32)[0]))
+        fx, fv = Fraction(x), Fraction(float(val))
+        for nb in (bits - 1, bits + 1):
+            if 0 <= nb < 1 << 16 and (nb & 0x7F80) != 0x7F80:
+                err_v, err_n = abs(fx - fv), abs(fx - as_f(nb))
+                assert err_v < err_n or (err_v == err_n and bits % 2 == 0)
+
+
+# --------------------------------------------------------------------------
+# the composed step
+def test_decode_step_is_composition(ora):
+    w = synth.LLAMA2_32K.replace(hq=4, hkv=2, n_ctx=3000, cap=3100, budget=64)
+    lay = synth.make_layer(w, 0, "cpu")
+    q, k, v = (synth.to_numpy_bits(lay[x]) for x in ("q", "k", "v"))
+    codes = ora.encode_keys(k)
+    out, out64, idx = ora.decode_step(q, k, v, codes, n_ctx=3000, budget=64)
+    qc = ora.encode_keys(q[:, :, None, :])[:, :, 0]
+    dist = ora.score(qc, codes, n_ctx=3000)
+    idx2 = ora.select_topk(dist, 64)
+    assert np.array_equal(idx, idx2)
+    o2, o64 = ora.sparse_attend(q, k, v, idx2)
+    assert np.array_equal(out, o2) and np.array_equal(out64, o64)
+
+
+def test_decode_step_finds_planted_needles(ora):
+    # sanity signal (not a parity bar): most planted needles survive selection
+    w = synth.LLAMA2_32K.replace(hq=4, hkv=4, n_ctx=8192, cap=8192)
+    lay = synth.make_layer(w, 0, "cpu")
+    q, k, v = (synth.to_numpy_bits(lay[x]) for x in ("q", "k", "v"))
+    codes = ora.encode_keys(k)
+    _, _, idx = ora.decode_step(q, k, v, codes, n_ctx=8192, budget=256)
+    found = sum(len(set(lay["needles"][0, h, 0]) & set(idx[0, h].tolist())) for h in range(4))
+    assert found >= 0.75 * 4 * w.needles
