@@ -1,0 +1,242 @@
+"""Python binding of libadamas.so, the MI355X (gfx950) ADAMAS decode path.
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity) and their device pointers, together with torch's current HIP
+stream, are handed to the C ABI declared in include/adamas.h.  Every step of
+the path runs in the library's HIP kernels; there is no fallback.  If the
+library is not built, every call raises.
+
+Method (ADAMAS article, www.lnwmold.com/news/826806): Hadamard rotation
+(§2.1), 2-bit bucketing (§2.2), packed code cache (§3.1), Manhattan scoring
+(§2.3), per-head token budget (§5.2), exact attention over the kept rows (§6).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "AdamasError", "load", "library_path", "encode_keys", "encode_query", "score", "select_topk",
+    "sparse_attend", "decode_step", "workspace_bytes", "Workspace", "OP_SELECT_TOPK",
+    "OP_SPARSE_ATTEND", "OP_DECODE_STEP",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libadamas.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = range(5)
+F32, BF16 = 0, 1
+OP_SELECT_TOPK, OP_SPARSE_ATTEND, OP_DECODE_STEP = 0, 1, 2
+WS_CTRL_BYTES = 65536
+
+_lib = None
+
+
+class AdamasError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = load().adamas_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{what}: {msg} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """dlopen libadamas.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+            "g.build()'` (hipcc --offload-arch=gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    lib.adamas_encode_keys.argtypes = [P, i32, i32, i32, i64, i32, P, i64, i64, P, P]
+    lib.adamas_score.argtypes = [P, P, i32, i32, i32, i32, i64, i64, P, P]
+    lib.adamas_select_topk.argtypes = [P, i32, i32, i64, i32, i32, P, P, sz, P]
+    lib.adamas_sparse_attend.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f32, P, P,
+                                         sz, P]
+    lib.adamas_decode_step.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, f32, P,
+                                       P, P, sz, P]
+    lib.adamas_workspace_bytes.argtypes = [i32, i32, i32, i32, i64, i32, i32]
+    lib.adamas_workspace_bytes.restype = sz
+    lib.adamas_status_string.argtypes = [i32]
+    lib.adamas_status_string.restype = ctypes.c_char_p
+    lib.adamas_version.restype = i32
+    for fn in ("adamas_encode_keys", "adamas_score", "adamas_select_topk", "adamas_sparse_attend",
+               "adamas_decode_step"):
+        getattr(lib, fn).restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise AdamasError(status, what)
+
+
+def _dev_ptr(t: torch.Tensor | None, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported element type {t.dtype} (float32 or bfloat16)")
+
+
+def workspace_bytes(op: int, B: int, Hq: int, Hkv: int, n_ctx: int, budget: int,
+                    head_dim: int) -> int:
+    n = load().adamas_workspace_bytes(op, B, Hq, Hkv, n_ctx, budget, head_dim)
+    if n == 0:
+        raise AdamasError(ERR_INVALID, "adamas_workspace_bytes")
+    return int(n)
+
+
+class Workspace:
+    """A zero-initialised device workspace reused across calls on one stream.
+
+    The library leaves its control bytes zero after every call, so the buffer
+    only grows (re-zeroed on growth) and is never cleared between calls."""
+
+    def __init__(self, device="cuda"):
+        self.device = torch.device(device)
+        self.buf = torch.zeros(0, dtype=torch.uint8, device=self.device)
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, WS_CTRL_BYTES), dtype=torch.uint8,
+                                   device=self.device)
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def _ws_for(device, ws: Workspace | None) -> Workspace:
+    if ws is not None:
+        return ws
+    key = (torch.device(device), torch.cuda.current_stream(device).cuda_stream)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key]
+
+
+# ------------------------------------------------------------------ calls
+def encode_keys(x: torch.Tensor, codes: torch.Tensor, pos: int = 0,
+                x_copy: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """x [batch][heads][n][d] -> codes [batch][heads][cap][d/4] rows [pos, pos+n)."""
+    if x.dim() != 4 or codes.dim() != 4 or codes.dtype != torch.uint8:
+        raise ValueError("x must be [batch][heads][n][d] and codes uint8 [batch][heads][cap][d/4]")
+    batch, heads, n, d = x.shape
+    cap = codes.shape[2]
+    if tuple(codes.shape) != (batch, heads, cap, d // 4):
+        raise ValueError(f"codes shape {tuple(codes.shape)} does not match x {tuple(x.shape)}")
+    if x_copy is not None and (tuple(x_copy.shape) != (batch, heads, cap, d) or
+                               x_copy.dtype != x.dtype):
+        raise ValueError("x_copy must be [batch][heads][cap][d] of x's dtype")
+    st = load().adamas_encode_keys(_dev_ptr(x, "x"), _dtype_code(x), batch, heads, n, d,
+                                   _dev_ptr(codes, "codes"), cap, pos, _dev_ptr(x_copy, "x_copy"),
+                                   _stream(x, stream))
+    _check(st, "adamas_encode_keys")
+    return codes
+
+
+def encode_query(q: torch.Tensor, stream=None) -> torch.Tensor:
+    """q [B][Hq][d] -> q_codes [B][Hq][d/4] (encode_keys with n = cap = 1)."""
+    B, Hq, d = q.shape
+    codes = torch.empty((B, Hq, 1, d // 4), dtype=torch.uint8, device=q.device)
+    encode_keys(q.reshape(B, Hq, 1, d), codes, 0, None, stream)
+    return codes.reshape(B, Hq, d // 4)
+
+
+def score(q_codes: torch.Tensor, k_codes: torch.Tensor, n_ctx: int | None = None,
+          dist: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """-> dist [B][Hq][n_ctx] uint16 (returned as torch.uint16)."""
+    B, Hq, rb = q_codes.shape
+    _, Hkv, cap, rb2 = k_codes.shape
+    if rb != rb2 or q_codes.dtype != torch.uint8 or k_codes.dtype != torch.uint8:
+        raise ValueError("q_codes / k_codes must be uint8 with matching row bytes")
+    n_ctx = cap if n_ctx is None else n_ctx
+    if dist is None:
+        dist = torch.empty((B, Hq, n_ctx), dtype=torch.uint16, device=q_codes.device)
+    st = load().adamas_score(_dev_ptr(q_codes, "q_codes"), _dev_ptr(k_codes, "k_codes"), B, Hq, Hkv,
+                             rb * 4, cap, n_ctx, _dev_ptr(dist, "dist"), _stream(q_codes, stream))
+    _check(st, "adamas_score")
+    return dist
+
+
+def select_topk(dist: torch.Tensor, budget: int, head_dim: int, idx: torch.Tensor | None = None,
+                ws: Workspace | None = None, stream=None) -> torch.Tensor:
+    """dist [B][Hq][n] uint16 -> idx [B][Hq][budget] int32 (ascending, -1 padded)."""
+    B, Hq, n = dist.shape
+    if idx is None:
+        idx = torch.empty((B, Hq, budget), dtype=torch.int32, device=dist.device)
+    nb = load().adamas_workspace_bytes(OP_SELECT_TOPK, B, Hq, 1, n, budget, head_dim)
+    buf = _ws_for(dist.device, ws).get(nb)
+    st = load().adamas_select_topk(_dev_ptr(dist, "dist"), B, Hq, n, head_dim, budget,
+                                   _dev_ptr(idx, "idx"), _dev_ptr(buf, "ws"), buf.numel(),
+                                   _stream(dist, stream))
+    _check(st, "adamas_select_topk")
+    return idx
+
+
+def sparse_attend(q, k, v, idx, scale: float = 0.0, out=None, ws: Workspace | None = None,
+                  stream=None) -> torch.Tensor:
+    """q [B][Hq][d], k/v [B][Hkv][cap][d], idx [B][Hq][budget] -> out [B][Hq][d]."""
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    budget = idx.shape[-1]
+    if k.dtype != q.dtype or v.dtype != q.dtype or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q, k, v must share dtype; k and v share shape")
+    if out is None:
+        out = torch.empty_like(q)
+    nb = load().adamas_workspace_bytes(OP_SPARSE_ATTEND, B, Hq, Hkv, 1, budget, d)
+    buf = _ws_for(q.device, ws).get(nb)
+    st = load().adamas_sparse_attend(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                     _dtype_code(q), _dev_ptr(idx, "idx"), B, Hq, Hkv, d, cap,
+                                     budget, float(scale), _dev_ptr(out, "out"),
+                                     _dev_ptr(buf, "ws"), buf.numel(), _stream(q, stream))
+    _check(st, "adamas_sparse_attend")
+    return out
+
+
+def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0, out=None,
+                idx_out=None, ws: Workspace | None = None, stream=None) -> torch.Tensor:
+    """One fused decode step of one layer -> out [B][Hq][d] (idx_out optional)."""
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    if k.dtype != q.dtype or v.dtype != q.dtype or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q, k, v must share dtype; k and v share shape")
+    if tuple(k_codes.shape) != (B, Hkv, cap, d // 4) or k_codes.dtype != torch.uint8:
+        raise ValueError("k_codes must be uint8 [B][Hkv][cap][d/4]")
+    if out is None:
+        out = torch.empty_like(q)
+    nb = load().adamas_workspace_bytes(OP_DECODE_STEP, B, Hq, Hkv, n_ctx, budget, d)
+    buf = _ws_for(q.device, ws).get(nb)
+    st = load().adamas_decode_step(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                   _dev_ptr(k_codes, "k_codes"), _dtype_code(q), B, Hq, Hkv, d,
+                                   cap, n_ctx, budget, float(scale), _dev_ptr(out, "out"),
+                                   _dev_ptr(idx_out, "idx_out"), _dev_ptr(buf, "ws"), buf.numel(),
+                                   _stream(q, stream))
+    _check(st, "adamas_decode_step")
+    return out

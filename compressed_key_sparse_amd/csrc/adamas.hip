@@ -1,0 +1,329 @@
+// adamas.hip -- C ABI of the MI355X ADAMAS decode path (declared in
+// include/adamas.h): host-side argument checks, workspace layout and kernel
+// launches.  Citations refer to the ADAMAS article
+// (www.lnwmold.com/news/826806) by its numbered sections.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "adamas.h"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace adm;
+
+constexpr int kMaxG = 8;                   // query heads per KV head
+constexpr int64_t kMaxGroups = 8192;       // B*Hq and B*Hkv (control-area slots)
+constexpr size_t kCtrlSelect = 0;          // u32 counters of select / decode groups
+constexpr size_t kCtrlAttend = 32768;      // u32 counters of attention rows
+constexpr int kMaxBudget = 1 << 20;
+constexpr size_t kLdsLimit = 48 * 1024;
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+bool valid_dtype(int dt) { return dt == ADAMAS_F32 || dt == ADAMAS_BF16; }
+bool valid_dim(int d) { return d == 64 || d == 128; }
+
+// LDS bytes of the fused selection kernel for a chunk of c tokens.
+size_t decode_lds(int D, int G, int c) {
+  const size_t nbp = (size_t)((3 * D + 1 + 3) & ~3);
+  return 64 + (size_t)G * (D / 16) * 4 + (size_t)G * nbp * 4 + (size_t)G * c * 2;
+}
+
+// Chunk of tokens per selection workgroup: large against the budget (the
+// candidates a chunk forwards are min(budget, chunk)), within the LDS limit,
+// and no larger than the context needs.
+int choose_chunk(int64_t n_ctx, int budget, int G, int D) {
+  int c = 4096;
+  while (c < 16384 && c < 8 * budget && decode_lds(D, G, 2 * c) <= kLdsLimit) c *= 2;
+  while (c > 512 && decode_lds(D, G, c) > kLdsLimit) c /= 2;
+  while (c > 512 && (int64_t)(c / 2) >= n_ctx) c /= 2;
+  return c;
+}
+
+int attend_splits(int rows) { return (rows + kAttnRows - 1) / kAttnRows; }
+
+struct SelectPlan {
+  int chunk = 0, n_chunks = 0, kmax = 0;
+  size_t cand_off = 0, end = 0;
+};
+
+SelectPlan plan_select(int64_t rows, int64_t n_ctx, int budget, int G, int D, size_t start) {
+  SelectPlan p;
+  p.chunk = choose_chunk(n_ctx, budget, G, D);
+  p.n_chunks = (int)((n_ctx + p.chunk - 1) / p.chunk);
+  p.kmax = budget < p.chunk ? budget : p.chunk;
+  p.cand_off = round_up(start, 256);
+  p.end = p.cand_off + (size_t)rows * p.n_chunks * p.kmax * sizeof(uint32_t);
+  return p;
+}
+
+struct AttendPlan {
+  int splits = 0;
+  size_t part_off = 0, end = 0;
+};
+
+AttendPlan plan_attend(int64_t rows, int sel_rows, int D, size_t start) {
+  AttendPlan p;
+  p.splits = attend_splits(sel_rows);
+  p.part_off = round_up(start, 256);
+  p.end = p.part_off + (p.splits > 1 ? (size_t)rows * p.splits * (2 + D) * sizeof(float) : 0);
+  return p;
+}
+
+struct DecodePlan {
+  SelectPlan sel;
+  size_t idx_off = 0;
+  AttendPlan att;
+  size_t total = 0;
+};
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D) {
+  DecodePlan p;
+  const int64_t rows = (int64_t)B * Hq;
+  p.sel = plan_select(rows, n_ctx, budget, Hq / Hkv, D, ADAMAS_WS_CTRL_BYTES);
+  p.idx_off = round_up(p.sel.end, 256);
+  const size_t idx_end = p.idx_off + (size_t)rows * budget * sizeof(int32_t);
+  const int sel_rows = (int)(n_ctx < budget ? n_ctx : budget);
+  p.att = plan_attend(rows, sel_rows, D, idx_end);
+  p.total = round_up(p.att.end, 256);
+  return p;
+}
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------- kernel tables
+template <int D, int G>
+void launch_score_t(dim3 grid, hipStream_t s, const uint8_t* qc, const uint8_t* kc, int Hq,
+                    int Hkv, int64_t cap, int64_t n_ctx, int chunk, uint16_t* dist) {
+  k_score<D, G><<<grid, kBlock, 0, s>>>(qc, kc, Hq, Hkv, cap, n_ctx, chunk, dist);
+}
+
+template <int D, int G>
+void launch_decode_select_t(dim3 grid, size_t lds, hipStream_t s, const void* q, int bf,
+                            const uint8_t* kc, int Hq, int Hkv, int64_t cap, int64_t n_ctx,
+                            int chunk, int n_chunks, int budget, uint32_t* cand, uint32_t* ctr,
+                            int32_t* idx) {
+  k_decode_select<D, G><<<grid, kBlock, lds, s>>>(q, bf, kc, Hq, Hkv, cap, n_ctx, chunk,
+                                                  n_chunks, budget, cand, ctr, idx);
+}
+
+template <int D>
+bool dispatch_score(int G, dim3 grid, hipStream_t s, const uint8_t* qc, const uint8_t* kc,
+                    int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk, uint16_t* dist) {
+  switch (G) {
+#define ADM_CASE(g) \
+  case g: launch_score_t<D, g>(grid, s, qc, kc, Hq, Hkv, cap, n_ctx, chunk, dist); return true;
+    ADM_CASE(1) ADM_CASE(2) ADM_CASE(3) ADM_CASE(4) ADM_CASE(5) ADM_CASE(6) ADM_CASE(7)
+    ADM_CASE(8)
+#undef ADM_CASE
+    default: return false;
+  }
+}
+
+template <int D>
+bool dispatch_decode_select(int G, dim3 grid, size_t lds, hipStream_t s, const void* q, int bf,
+                            const uint8_t* kc, int Hq, int Hkv, int64_t cap, int64_t n_ctx,
+                            int chunk, int n_chunks, int budget, uint32_t* cand, uint32_t* ctr,
+                            int32_t* idx) {
+  switch (G) {
+#define ADM_CASE(g)                                                                      \
+  case g:                                                                                \
+    launch_decode_select_t<D, g>(grid, lds, s, q, bf, kc, Hq, Hkv, cap, n_ctx, chunk,    \
+                                 n_chunks, budget, cand, ctr, idx);                      \
+    return true;
+    ADM_CASE(1) ADM_CASE(2) ADM_CASE(3) ADM_CASE(4) ADM_CASE(5) ADM_CASE(6) ADM_CASE(7)
+    ADM_CASE(8)
+#undef ADM_CASE
+    default: return false;
+  }
+}
+
+void launch_attend(int D, dim3 grid, hipStream_t s, const void* q, const void* k, const void* v,
+                   int bf, const int32_t* idx, int Hq, int Hkv, int64_t cap, int budget,
+                   float qscale, float* part, uint32_t* ctr, void* out) {
+  if (D == 128)
+    k_attend<128><<<grid, kBlock, 0, s>>>(q, k, v, bf, idx, Hq, Hkv, cap, budget, qscale, part,
+                                          ctr, out);
+  else
+    k_attend<64><<<grid, kBlock, 0, s>>>(q, k, v, bf, idx, Hq, Hkv, cap, budget, qscale, part,
+                                         ctr, out);
+}
+
+// Score scale in the log2 domain: s2 = (q . k) * scale * log2(e).
+float attend_qscale(float scale, int D) {
+  const float sc = (scale == 0.0f) ? 1.0f / sqrtf((float)D) : scale;
+  return sc * 1.4426950408889634f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int adamas_version(void) { return ADAMAS_VERSION; }
+
+const char* adamas_status_string(int status) {
+  switch (status) {
+    case ADAMAS_OK: return "ok";
+    case ADAMAS_ERR_INVALID: return "invalid argument (null/misaligned pointer, size or range)";
+    case ADAMAS_ERR_UNSUPPORTED: return "unsupported (head_dim, dtype or a size limit)";
+    case ADAMAS_ERR_WORKSPACE: return "workspace missing or too small";
+    case ADAMAS_ERR_DEVICE: return "device launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx, int budget,
+                              int head_dim) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_ctx < 1 || budget < 1 ||
+      budget > kMaxBudget || !valid_dim(head_dim))
+    return 0;
+  if (op == ADAMAS_OP_DECODE_STEP && Hq / Hkv > kMaxG) return 0;
+  const int64_t rows = (int64_t)B * Hq;
+  switch (op) {
+    case ADAMAS_OP_SELECT_TOPK:
+      return round_up(plan_select(rows, n_ctx, budget, 1, head_dim, ADAMAS_WS_CTRL_BYTES).end,
+                      256);
+    case ADAMAS_OP_SPARSE_ATTEND:
+      return round_up(plan_attend(rows, budget, head_dim, ADAMAS_WS_CTRL_BYTES).end, 256);
+    case ADAMAS_OP_DECODE_STEP:
+      return plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).total;
+    default: return 0;
+  }
+}
+
+int adamas_encode_keys(const void* x, int dtype, int batch, int heads, int64_t n, int head_dim,
+                       uint8_t* codes, int64_t cap, int64_t pos, void* x_copy_dst,
+                       hipStream_t stream) {
+  if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
+  if (batch < 1 || heads < 1 || n < 0 || pos < 0 || cap < 1 || pos + n > cap)
+    return ADAMAS_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(codes)) return ADAMAS_ERR_INVALID;
+  if (x_copy_dst != nullptr && !aligned16(x_copy_dst)) return ADAMAS_ERR_INVALID;
+  if (n == 0) return ADAMAS_OK;
+  const int64_t nvec = (int64_t)batch * heads * n;
+  const int64_t blocks64 = (nvec + 3) / 4;
+  const unsigned blocks = (unsigned)(blocks64 < 16384 ? blocks64 : 16384);
+  const int bf = dtype == ADAMAS_BF16;
+  if (head_dim == 128)
+    k_encode<128><<<blocks, kBlock, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst);
+  else
+    k_encode<64><<<blocks, kBlock, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst);
+  return launch_status();
+}
+
+int adamas_score(const uint8_t* q_codes, const uint8_t* k_codes, int B, int Hq, int Hkv,
+                 int head_dim, int64_t cap, int64_t n_ctx, uint16_t* dist, hipStream_t stream) {
+  if (!valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_ctx < 0 || cap < 1 || n_ctx > cap)
+    return ADAMAS_ERR_INVALID;
+  if (Hq / Hkv > kMaxG || Hkv > 65535 || B > 65535 || n_ctx > INT32_MAX)
+    return ADAMAS_ERR_UNSUPPORTED;
+  if (!aligned16(q_codes) || !aligned16(k_codes) || !aligned16(dist)) return ADAMAS_ERR_INVALID;
+  if (n_ctx == 0) return ADAMAS_OK;
+  const int chunk = 4096;
+  const dim3 grid((unsigned)((n_ctx + chunk - 1) / chunk), (unsigned)Hkv, (unsigned)B);
+  const int G = Hq / Hkv;
+  const bool ok = head_dim == 128
+                      ? dispatch_score<128>(G, grid, stream, q_codes, k_codes, Hq, Hkv, cap,
+                                            n_ctx, chunk, dist)
+                      : dispatch_score<64>(G, grid, stream, q_codes, k_codes, Hq, Hkv, cap,
+                                           n_ctx, chunk, dist);
+  if (!ok) return ADAMAS_ERR_UNSUPPORTED;
+  return launch_status();
+}
+
+int adamas_select_topk(const uint16_t* dist, int B, int Hq, int64_t n_ctx, int head_dim,
+                       int budget, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
+  if (B < 1 || Hq < 1 || n_ctx < 1 || budget < 1) return ADAMAS_ERR_INVALID;
+  if (budget > kMaxBudget || n_ctx > INT32_MAX || (int64_t)B * Hq > kMaxGroups || Hq > 65535 ||
+      B > 65535)
+    return ADAMAS_ERR_UNSUPPORTED;
+  if (!aligned16(dist) || !aligned16(idx)) return ADAMAS_ERR_INVALID;
+  if (ws == nullptr || !aligned16(ws)) return ADAMAS_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)B * Hq;
+  const SelectPlan p = plan_select(rows, n_ctx, budget, 1, head_dim, ADAMAS_WS_CTRL_BYTES);
+  if (ws_bytes < round_up(p.end, 256)) return ADAMAS_ERR_WORKSPACE;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const dim3 grid((unsigned)p.n_chunks, (unsigned)Hq, (unsigned)B);
+  const size_t nbp = (size_t)((3 * head_dim + 1 + 3) & ~3);
+  const size_t lds = 64 + nbp * 4 + (size_t)p.chunk * 2;
+  uint32_t* cand = reinterpret_cast<uint32_t*>(w + p.cand_off);
+  uint32_t* ctr = reinterpret_cast<uint32_t*>(w + kCtrlSelect);
+  if (head_dim == 128)
+    k_select<128><<<grid, kBlock, lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks, budget,
+                                                 cand, ctr, idx);
+  else
+    k_select<64><<<grid, kBlock, lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks, budget,
+                                                cand, ctr, idx);
+  return launch_status();
+}
+
+int adamas_sparse_attend(const void* q, const void* k, const void* v, int dtype,
+                         const int32_t* idx, int B, int Hq, int Hkv, int head_dim, int64_t cap,
+                         int budget, float scale, void* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || cap < 1 || budget < 1 || !isfinite(scale))
+    return ADAMAS_ERR_INVALID;
+  if (budget > kMaxBudget || (int64_t)B * Hq > kMaxGroups || Hq > 65535 || B > 65535)
+    return ADAMAS_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(idx) || !aligned16(out))
+    return ADAMAS_ERR_INVALID;
+  if (ws == nullptr || !aligned16(ws)) return ADAMAS_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)B * Hq;
+  const AttendPlan p = plan_attend(rows, budget, head_dim, ADAMAS_WS_CTRL_BYTES);
+  if (ws_bytes < round_up(p.end, 256)) return ADAMAS_ERR_WORKSPACE;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const dim3 grid((unsigned)p.splits, (unsigned)Hq, (unsigned)B);
+  launch_attend(head_dim, grid, stream, q, k, v, dtype == ADAMAS_BF16, idx, Hq, Hkv, cap, budget,
+                attend_qscale(scale, head_dim), reinterpret_cast<float*>(w + p.part_off),
+                reinterpret_cast<uint32_t*>(w + kCtrlAttend), out);
+  return launch_status();
+}
+
+int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_t* k_codes,
+                       int dtype, int B, int Hq, int Hkv, int head_dim, int64_t cap,
+                       int64_t n_ctx, int budget, float scale, void* out, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || cap < 1 || n_ctx < 1 || n_ctx > cap ||
+      budget < 1 || !isfinite(scale))
+    return ADAMAS_ERR_INVALID;
+  if (budget > kMaxBudget || n_ctx > INT32_MAX || Hq / Hkv > kMaxG ||
+      (int64_t)B * Hq > kMaxGroups || Hq > 65535 || B > 65535)
+    return ADAMAS_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_codes) || !aligned16(out))
+    return ADAMAS_ERR_INVALID;
+  if (idx_out != nullptr && !aligned16(idx_out)) return ADAMAS_ERR_INVALID;
+  if (ws == nullptr || !aligned16(ws)) return ADAMAS_ERR_WORKSPACE;
+  const DecodePlan p = plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim);
+  if (ws_bytes < p.total) return ADAMAS_ERR_WORKSPACE;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const int G = Hq / Hkv;
+  const int bf = dtype == ADAMAS_BF16;
+  int32_t* idx = idx_out != nullptr ? idx_out : reinterpret_cast<int32_t*>(w + p.idx_off);
+  const dim3 gsel((unsigned)p.sel.n_chunks, (unsigned)Hkv, (unsigned)B);
+  const size_t lds = decode_lds(head_dim, G, p.sel.chunk);
+  uint32_t* cand = reinterpret_cast<uint32_t*>(w + p.sel.cand_off);
+  uint32_t* ctr_sel = reinterpret_cast<uint32_t*>(w + kCtrlSelect);
+  const bool ok = head_dim == 128
+                      ? dispatch_decode_select<128>(G, gsel, lds, stream, q, bf, k_codes, Hq, Hkv,
+                                                    cap, n_ctx, p.sel.chunk, p.sel.n_chunks,
+                                                    budget, cand, ctr_sel, idx)
+                      : dispatch_decode_select<64>(G, gsel, lds, stream, q, bf, k_codes, Hq, Hkv,
+                                                   cap, n_ctx, p.sel.chunk, p.sel.n_chunks,
+                                                   budget, cand, ctr_sel, idx);
+  if (!ok) return ADAMAS_ERR_UNSUPPORTED;
+  const dim3 gatt((unsigned)p.att.splits, (unsigned)Hq, (unsigned)B);
+  launch_attend(head_dim, gatt, stream, q, k, v, bf, idx, Hq, Hkv, cap, budget,
+                attend_qscale(scale, head_dim), reinterpret_cast<float*>(w + p.att.part_off),
+                reinterpret_cast<uint32_t*>(w + kCtrlAttend), out);
+  return launch_status();
+}
+
+}  // extern "C"

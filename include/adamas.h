@@ -1,0 +1,167 @@
+/*
+ * adamas.h -- C ABI of the MI355X (gfx950) ADAMAS decode path.
+ *
+ * The method (ADAMAS article, www.lnwmold.com/news/826806): rotate queries
+ * and keys by a Hadamard matrix over the head dimension (§2.1), bucket each
+ * rotated vector into 2-bit codes at -0.5*absmax, 0, +0.5*absmax (§2.2), keep
+ * the keys' codes packed four per byte in a compact cache (§3.1), score a
+ * query against every cached key by Manhattan distance between codes (§2.3),
+ * keep a per-head token budget of the closest keys (§5.2), and run exact
+ * softmax attention over only those K/V rows (§6).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - All tensor arguments are DEVICE pointers, borrowed for the duration of
+ *    the enqueued work; the library never allocates, frees or retains them.
+ *    Tensors are dense, row-major, in the layouts given per call, and must be
+ *    16-byte aligned.
+ *  - Element types: ADAMAS_F32 (binary32) or ADAMAS_BF16 (bfloat16).
+ *  - head_dim must be 64 or 128.
+ *  - Calls enqueue work on `stream` (0 = the null stream) and return without
+ *    waiting; results are visible after a stream synchronisation or event.
+ *    No call synchronises the device, so calls may be captured into a graph.
+ *  - Errors: every argument is checked on the host BEFORE anything is
+ *    enqueued; on any non-zero status nothing was enqueued.  A launch failure
+ *    reported by the runtime after enqueueing returns ADAMAS_ERR_DEVICE.
+ *  - Workspace: calls that take (ws, ws_bytes) need a device buffer of at
+ *    least adamas_workspace_bytes(...) bytes whose first ADAMAS_WS_CTRL_BYTES
+ *    bytes are zero before the first call that uses it (allocate it zeroed).
+ *    Every call that completes leaves those bytes zero again, so one
+ *    workspace can be reused by any sequence of calls ON ONE STREAM; calls
+ *    that may overlap in time need separate workspaces.
+ *  - Codes: a row of d dims is d/4 bytes; code i sits in byte i/4 at bits
+ *    (7 - 2*(i%4)) .. (6 - 2*(i%4)), i.e. the first code of a byte in its top
+ *    two bits.  Code values: 0 if y < -a/2, 1 if y < 0, 2 if y < a/2, else 3,
+ *    with y the unnormalised Sylvester-order Hadamard transform of the vector
+ *    in binary32 and a = max|y_i| over the vector.
+ */
+#ifndef ADAMAS_H
+#define ADAMAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADAMAS_VERSION 100 /* 1.0.0 */
+
+/* Leading bytes of a workspace that must be zero before its first use. */
+#define ADAMAS_WS_CTRL_BYTES 65536
+
+typedef enum {
+    ADAMAS_OK = 0,
+    ADAMAS_ERR_INVALID = 1,     /* null/misaligned pointer, bad size or range */
+    ADAMAS_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, unknown dtype, limits */
+    ADAMAS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than needed */
+    ADAMAS_ERR_DEVICE = 4       /* the HIP runtime reported a launch error */
+} adamas_status;
+
+typedef enum { ADAMAS_F32 = 0, ADAMAS_BF16 = 1 } adamas_dtype;
+
+typedef enum {
+    ADAMAS_OP_SELECT_TOPK = 0,
+    ADAMAS_OP_SPARSE_ATTEND = 1,
+    ADAMAS_OP_DECODE_STEP = 2
+} adamas_op;
+
+/*
+ * Encode keys (or queries) into 2-bit codes: §2.1 rotation, §2.2 bucketing,
+ * §3.1 packing (the article's CompressedKVCache.update).
+ *
+ *   x          [batch][heads][n][head_dim] elements of `dtype`.
+ *   codes      [batch][heads][cap][head_dim/4] bytes; rows [pos, pos+n) of
+ *              each (batch, head) are written, no other byte is touched.
+ *   x_copy_dst nullable; if set, [batch][heads][cap][head_dim] elements of
+ *              `dtype` receiving a verbatim copy of x at rows [pos, pos+n)
+ *              (append the raw keys to a K cache in the same pass).
+ * A query vector is encoded with n = 1, cap = 1, pos = 0.
+ * Requires batch, heads >= 1, n >= 0, 0 <= pos, pos + n <= cap.
+ * n = 0 is a no-op that returns ADAMAS_OK.
+ */
+int adamas_encode_keys(const void *x, int dtype, int batch, int heads, int64_t n,
+                       int head_dim, uint8_t *codes, int64_t cap, int64_t pos,
+                       void *x_copy_dst, hipStream_t stream);
+
+/*
+ * Manhattan distance between query codes and the first n_ctx cached key
+ * codes (§2.3): dist[b][hq][t] = sum_i |qc_i - kc_i|, in 0 .. 3*head_dim.
+ * Query head hq reads KV head hq / (Hq / Hkv).
+ *
+ *   q_codes [B][Hq][head_dim/4] bytes.
+ *   k_codes [B][Hkv][cap][head_dim/4] bytes.
+ *   dist    [B][Hq][n_ctx] uint16.
+ * Requires Hq % Hkv == 0, 0 <= n_ctx <= cap; n_ctx = 0 is a no-op.
+ */
+int adamas_score(const uint8_t *q_codes, const uint8_t *k_codes, int B, int Hq,
+                 int Hkv, int head_dim, int64_t cap, int64_t n_ctx,
+                 uint16_t *dist, hipStream_t stream);
+
+/*
+ * Token budget (§5.2): per (b, hq) keep the min(budget, n_ctx) tokens with
+ * the smallest (distance, token index) -- the lowest index wins a tie --
+ * and write their indices in ascending order, padding with -1.
+ *
+ *   dist [B][Hq][n_ctx] uint16, values <= 3*head_dim.
+ *   idx  [B][Hq][budget] int32.
+ * Requires n_ctx >= 1, budget >= 1, workspace of
+ * adamas_workspace_bytes(ADAMAS_OP_SELECT_TOPK, ...).
+ */
+int adamas_select_topk(const uint16_t *dist, int B, int Hq, int64_t n_ctx,
+                       int head_dim, int budget, int32_t *idx, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Exact softmax attention over the selected rows only (§6):
+ * s_j = scale * q . k_j, p = softmax(s), out = sum_j p_j v_j, accumulated in
+ * binary32 and rounded to `dtype`.  Rows with idx < 0 are skipped; a head
+ * with no valid index gets zeros.  Uses the original (unrotated) q, K, V.
+ *
+ *   q    [B][Hq][head_dim]; k, v [B][Hkv][cap][head_dim]; out [B][Hq][head_dim]
+ *   idx  [B][Hq][budget] int32, every entry < cap.
+ *   scale: 0 selects 1/sqrt(head_dim); must be finite.
+ * Requires Hq % Hkv == 0, budget >= 1, workspace of
+ * adamas_workspace_bytes(ADAMAS_OP_SPARSE_ATTEND, ...).
+ */
+int adamas_sparse_attend(const void *q, const void *k, const void *v, int dtype,
+                         const int32_t *idx, int B, int Hq, int Hkv, int head_dim,
+                         int64_t cap, int budget, float scale, void *out, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One decode step of one layer, fused: encode each query head (§2.1-§2.2),
+ * score it against cached codes rows [0, n_ctx) (§2.3), keep the budget
+ * (§5.2) and attend over those K/V rows (§6).  Same results as
+ * adamas_encode_keys(q) -> adamas_score -> adamas_select_topk ->
+ * adamas_sparse_attend.
+ *
+ *   q [B][Hq][head_dim]; k, v [B][Hkv][cap][head_dim]; k_codes
+ *   [B][Hkv][cap][head_dim/4]; out [B][Hq][head_dim]; idx_out nullable
+ *   [B][Hq][budget] int32 (the selection, as adamas_select_topk writes it).
+ * Requires Hq % Hkv == 0, 1 <= n_ctx <= cap, budget >= 1, workspace of
+ * adamas_workspace_bytes(ADAMAS_OP_DECODE_STEP, ...).
+ */
+int adamas_decode_step(const void *q, const void *k, const void *v,
+                       const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
+                       int head_dim, int64_t cap, int64_t n_ctx, int budget,
+                       float scale, void *out, int32_t *idx_out, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by `op` for the given shape (0 for invalid shapes). */
+size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx,
+                              int budget, int head_dim);
+
+/* Static, human-readable text for a status code. */
+const char *adamas_status_string(int status);
+
+/* ADAMAS_VERSION of the built library. */
+int adamas_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAMAS_H */

@@ -1,0 +1,139 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before anything is enqueued.
+
+No call here reaches a kernel launch: each one fails host-side validation,
+which runs before any HIP call (fake, never-dereferenced pointer values)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_key_sparse_amd as adamas
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adamas.h")
+
+A = 0x10000     # a fake 16-byte-aligned device address (never dereferenced)
+MIS = 0x10001   # misaligned
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(adamas.library_path()):
+        from compressed_key_sparse_amd import _build
+        _build.build(force=False)
+    return adamas.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(adamas_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"adamas_encode_keys", "adamas_score", "adamas_select_topk",
+                          "adamas_sparse_attend", "adamas_decode_step", "adamas_workspace_bytes",
+                          "adamas_status_string", "adamas_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.adamas_version() == 100
+    for s in range(5):
+        assert lib.adamas_status_string(s)
+    assert lib.adamas_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    f = lib.adamas_workspace_bytes
+    assert f(2, 1, 32, 32, 131072, 256, 128) > 65536
+    assert f(2, 1, 32, 32, 131072, 256, 96) == 0      # head_dim
+    assert f(2, 1, 24, 7, 1000, 64, 128) == 0          # Hq % Hkv
+    assert f(2, 1, 32, 2, 1000, 64, 128) == 0          # group of 16 > 8
+    assert f(0, 1, 32, 1, 1000, 64, 128) > 0           # select ignores Hkv grouping
+    assert f(2, 1, 32, 32, 0, 64, 128) == 0
+    assert f(2, 1, 32, 32, 1000, 0, 128) == 0
+    assert f(7, 1, 32, 32, 1000, 64, 128) == 0         # unknown op
+    # grows with the context and the budget
+    assert f(2, 1, 32, 32, 262144, 256, 128) > f(2, 1, 32, 32, 131072, 256, 128)
+    assert f(1, 1, 32, 32, 1, 1024, 128) > f(1, 1, 32, 32, 1, 64, 128)
+
+
+def test_encode_validation(lib):
+    f = lib.adamas_encode_keys
+    assert f(A, 0, 1, 1, 4, 96, A, 8, 0, None, None) == UNSUPPORTED
+    assert f(A, 2, 1, 1, 4, 128, A, 8, 0, None, None) == UNSUPPORTED
+    assert f(A, 1, 1, 1, 4, 128, A, 8, 5, None, None) == INVALID     # pos + n > cap
+    assert f(A, 1, 1, 1, -1, 128, A, 8, 0, None, None) == INVALID
+    assert f(A, 1, 0, 1, 4, 128, A, 8, 0, None, None) == INVALID
+    assert f(MIS, 1, 1, 1, 4, 128, A, 8, 0, None, None) == INVALID
+    assert f(A, 1, 1, 1, 4, 128, None, 8, 0, None, None) == INVALID
+    assert f(A, 1, 1, 1, 4, 128, A, 8, 0, MIS, None) == INVALID
+    assert f(A, 1, 1, 1, 0, 128, A, 8, 0, None, None) == OK            # n = 0: no-op
+
+
+def test_score_validation(lib):
+    f = lib.adamas_score
+    assert f(A, A, 1, 6, 4, 128, 100, 10, A, None) == INVALID          # Hq % Hkv
+    assert f(A, A, 1, 4, 4, 128, 100, 101, A, None) == INVALID         # n_ctx > cap
+    assert f(A, A, 1, 4, 4, 80, 100, 10, A, None) == UNSUPPORTED
+    assert f(A, A, 1, 18, 2, 128, 100, 10, A, None) == UNSUPPORTED     # group of 9
+    assert f(A, MIS, 1, 4, 4, 128, 100, 10, A, None) == INVALID
+    assert f(A, A, 1, 4, 4, 128, 100, 0, A, None) == OK                # empty: no-op
+
+
+def test_select_validation(lib):
+    f = lib.adamas_select_topk
+    need = lib.adamas_workspace_bytes(0, 1, 4, 1, 1000, 64, 128)
+    assert f(A, 1, 4, 1000, 128, 0, A, A, need, None) == INVALID       # budget 0
+    assert f(A, 1, 4, 0, 128, 64, A, A, need, None) == INVALID         # empty context
+    assert f(A, 1, 4, 1000, 64 + 1, 64, A, A, need, None) == UNSUPPORTED
+    assert f(A, 1, 4, 1000, 128, 64, A, None, need, None) == WORKSPACE
+    assert f(A, 1, 4, 1000, 128, 64, A, A, need - 1, None) == WORKSPACE
+    assert f(A, 1, 4, 1000, 128, 64, MIS, A, need, None) == INVALID
+    assert f(A, 1, 8193, 1000, 128, 64, A, A, need, None) == UNSUPPORTED  # > 8192 rows
+
+
+def test_attend_validation(lib):
+    f = lib.adamas_sparse_attend
+    need = lib.adamas_workspace_bytes(1, 1, 4, 2, 1, 64, 128)
+    args = lambda **kw: [kw.get("q", A), A, A, kw.get("dt", 1), A, 1, kw.get("hq", 4), 2, 128,
+                         100, kw.get("budget", 64), ctypes.c_float(kw.get("scale", 0.0)), A, A,
+                         kw.get("ws", need), None]
+    assert f(*args(hq=5)) == INVALID
+    assert f(*args(dt=3)) == UNSUPPORTED
+    assert f(*args(q=MIS)) == INVALID
+    assert f(*args(budget=0)) == INVALID
+    assert f(*args(scale=float("nan"))) == INVALID
+    assert f(*args(ws=need - 1)) == WORKSPACE
+
+
+def test_decode_validation(lib):
+    f = lib.adamas_decode_step
+    need = lib.adamas_workspace_bytes(2, 1, 8, 4, 1000, 64, 128)
+    def call(**kw):
+        return f(A, A, A, kw.get("codes", A), kw.get("dt", 1), 1, kw.get("hq", 8),
+                 kw.get("hkv", 4), kw.get("d", 128), kw.get("cap", 1024), kw.get("n", 1000),
+                 kw.get("budget", 64), ctypes.c_float(0.0), A, kw.get("idx", None), A,
+                 kw.get("ws", need), None)
+    assert call(n=0) == INVALID
+    assert call(n=1025) == INVALID
+    assert call(hkv=3) == INVALID
+    assert call(hq=36, hkv=4) == UNSUPPORTED   # group of 9
+    assert call(d=96) == UNSUPPORTED
+    assert call(codes=MIS) == INVALID
+    assert call(idx=MIS) == INVALID
+    assert call(ws=need - 1) == WORKSPACE
+    assert call(budget=0) == INVALID
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(adamas, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(adamas, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        adamas.load()

@@ -1,0 +1,232 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle.
+
+Codes, distances and selected indices must be bit-exact; attention outputs
+must be within the relative error bound (2e-3 bf16, 1e-5 fp32) of the
+oracle's binary64 result rounded to the output type.  Inputs are seeded
+synthetic draws (synth.py); the oracle receives byte-identical host copies.
+"""
+import numpy as np
+import pytest
+import torch
+
+import compressed_key_sparse_amd as adamas
+import synth
+from gpu_helpers import TOL, host, log, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    adamas.load()
+
+
+def _dt(name):
+    return torch.float32 if name == "f32" else torch.bfloat16
+
+
+# ------------------------------------------------------------------ encode
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_encode_random(ora, d, dt):
+    log(f"encode random d={d} dt={dt}")
+    x = synth.random_values((2, 3, 777, d), _dt(dt), seed=d, device=DEV, scale=3.0)
+    codes = torch.full((2, 3, 1000, d // 4), 0x5A, dtype=torch.uint8, device=DEV)
+    copy = torch.zeros((2, 3, 1000, d), dtype=_dt(dt), device=DEV)
+    adamas.encode_keys(x, codes, pos=100, x_copy=copy)
+    ref = np.full((2, 3, 1000, d // 4), 0x5A, np.uint8)
+    ora.encode_keys(host(x), ref, cap=1000, pos=100)
+    assert np.array_equal(codes.cpu().numpy(), ref)
+    assert torch.equal(copy[:, :, 100:877], x) and not copy[:, :, :100].any()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_encode_edge_values(ora, d):
+    log(f"encode edge values d={d}")
+    n = 64
+    rows = [np.zeros(d, np.float32), -np.zeros(d, np.float32)]
+    rows += [np.eye(d, dtype=np.float32)[j] for j in (0, 1, d - 1)]
+    rows += list(synth.integer_values((20, d), -3, 3, seed=1))          # exact ties
+    rows += list(synth.integer_values((10, d), 0, 1, seed=2))
+    rows.append(np.full(d, 1e-42, np.float32))                           # denormals
+    rows.append(np.full(d, 3e36, np.float32) * np.sign(np.arange(d) - d / 2 + 0.5))
+    rows.append(np.where(np.arange(d) % 3 == 0, 1e-40, -2e-41).astype(np.float32))
+    while len(rows) < n:
+        rows.append(rows[len(rows) % 7] * np.float32(2.0 ** (len(rows) - 40)))
+    x = np.stack(rows[:n]).reshape(1, 1, n, d).astype(np.float32)
+    xt = torch.from_numpy(x).to(DEV)
+    codes = torch.zeros((1, 1, n, d // 4), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(xt, codes)
+    assert np.array_equal(codes.cpu().numpy(), ora.encode_keys(x))
+    xb = xt.to(torch.bfloat16)
+    adamas.encode_keys(xb, codes)
+    assert np.array_equal(codes.cpu().numpy(), ora.encode_keys(host(xb)))
+
+
+def test_encode_query_and_large_batch(ora):
+    log("encode: queries (n=1) and a 4096-token prefill chunk")
+    q = synth.random_values((16, 32, 128), torch.bfloat16, seed=3, device=DEV)
+    qc = adamas.encode_query(q)
+    assert np.array_equal(qc.cpu().numpy(), ora.encode_keys(host(q)[:, :, None, :])[:, :, 0])
+    w = synth.BATCH16_64K
+    chunk = synth.make_chunk(w, 0, DEV)
+    codes = torch.zeros((1, 32, 4096 + 16, 32), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(chunk, codes, pos=16)
+    ref = ora.encode_keys(host(chunk), np.zeros((1, 32, 4096 + 16, 32), np.uint8), 4096 + 16, 16)
+    assert np.array_equal(codes.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------- score
+@pytest.mark.parametrize("d,hq,hkv,n", [(128, 4, 4, 9000), (64, 6, 2, 4097), (128, 24, 8, 300),
+                                        (128, 8, 1, 5000), (64, 3, 3, 1), (128, 2, 1, 255)])
+def test_score(ora, d, hq, hkv, n):
+    log(f"score d={d} hq={hq} hkv={hkv} n={n}")
+    g = torch.Generator(device=DEV).manual_seed(n + hq)
+    cap = n + 37
+    kc = torch.randint(0, 256, (2, hkv, cap, d // 4), generator=g, device=DEV,
+                       dtype=torch.int32).to(torch.uint8)
+    qc = torch.randint(0, 256, (2, hq, d // 4), generator=g, device=DEV,
+                       dtype=torch.int32).to(torch.uint8)
+    dist = adamas.score(qc, kc, n_ctx=n)
+    ref = ora.score(qc.cpu().numpy(), kc.cpu().numpy(), n_ctx=n)
+    assert np.array_equal(dist.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ select
+@pytest.mark.parametrize("n,budget,hi", [(1, 1, 5), (100, 64, 3), (100, 200, 3), (4097, 64, 384),
+                                         (20000, 256, 40), (20000, 1000, 2), (70000, 256, 384),
+                                         (9000, 4096, 10), (33, 32, 0)])
+def test_select(ora, n, budget, hi):
+    log(f"select n={n} budget={budget} values<={hi}")
+    g = torch.Generator(device=DEV).manual_seed(n * 7 + budget)
+    dist = torch.randint(0, hi + 1, (2, 3, n), generator=g, device=DEV,
+                         dtype=torch.int32).to(torch.uint16)
+    idx = adamas.select_topk(dist, budget, head_dim=128)
+    ref = ora.select_topk(dist.cpu().numpy(), budget)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------ attend
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("budget", [1, 31, 256, 1000])
+def test_sparse_attend(ora, d, dt, budget):
+    log(f"attend d={d} dt={dt} budget={budget}")
+    B, Hq, Hkv, cap = 2, 6, 3, 3000
+    dtype = _dt(dt)
+    q = synth.random_values((B, Hq, d), dtype, seed=1, device=DEV)
+    k = synth.random_values((B, Hkv, cap, d), dtype, seed=2, device=DEV)
+    v = synth.random_values((B, Hkv, cap, d), dtype, seed=3, device=DEV, scale=2.0)
+    rng = np.random.default_rng(budget)
+    idx = np.full((B, Hq, budget), -1, np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            m = int(rng.integers(1, budget + 1)) if h else budget
+            idx[b, h, :m] = np.sort(rng.choice(cap, size=m, replace=False))
+    idx[0, 1, :] = -1                      # a head with nothing selected -> zeros
+    it = torch.from_numpy(idx).to(DEV)
+    out = adamas.sparse_attend(q, k, v, it)
+    ref, _ = ora.sparse_attend(host(q), host(k), host(v), idx)
+    e = rel_err(out, ref)
+    log(f"  rel err {e:.3e}")
+    assert e <= TOL[dtype]
+    assert not out[0, 1].any()
+
+
+def test_sparse_attend_single_row_exact(ora):
+    q = synth.random_values((1, 4, 128), torch.bfloat16, seed=4, device=DEV)
+    k = synth.random_values((1, 4, 50, 128), torch.bfloat16, seed=5, device=DEV)
+    v = synth.random_values((1, 4, 50, 128), torch.bfloat16, seed=6, device=DEV)
+    idx = torch.tensor([[[7], [0], [49], [23]]], dtype=torch.int32, device=DEV)
+    out = adamas.sparse_attend(q, k, v, idx)
+    for h, t in enumerate((7, 0, 49, 23)):
+        assert torch.equal(out[0, h], v[0, h, t])
+
+
+# ------------------------------------------------------------- decode step
+def _decode_case(ora, w, n_ctx=None, budget=None, layer=0):
+    n_ctx = w.n_ctx if n_ctx is None else n_ctx
+    budget = w.budget if budget is None else budget
+    lay = synth.make_layer(w, layer, DEV, n_ctx=n_ctx)
+    cap = lay["cap"]
+    codes = torch.zeros((w.batch, w.hkv, cap, w.head_dim // 4), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    idx = torch.empty((w.batch, w.hq, budget), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, n_ctx, budget, idx_out=idx)
+    torch.cuda.synchronize()
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    ocodes = ora.encode_keys(k)
+    assert np.array_equal(codes.cpu().numpy(), ocodes), "code cache differs"
+    oout, _, oidx = ora.decode_step(q, k, v, ocodes, n_ctx, budget)
+    assert np.array_equal(idx.cpu().numpy(), oidx), "selection differs"
+    e = rel_err(out, oout)
+    log(f"  {w.name} n={n_ctx} budget={budget}: rel err {e:.3e}")
+    assert e <= TOL[w.torch_dtype]
+    return lay, out, idx
+
+
+def test_decode_tiny_config(ora):
+    log("decode: tiny single-head fp32 config (full size)")
+    lay, out, idx = _decode_case(ora, synth.TINY)
+    p = int(lay["needles"][0, 0, 0, 0])
+    assert p in idx[0, 0].tolist()       # the planted key is selected
+
+
+@pytest.mark.parametrize("n,budget", [(1, 64), (63, 64), (64, 64), (700, 64), (5000, 256),
+                                      (20000, 1024), (4096, 2048)])
+def test_decode_small_mha(ora, n, budget):
+    log(f"decode small MHA n={n} budget={budget}")
+    w = synth.LLAMA2_32K.replace(hq=4, hkv=4, n_ctx=n, cap=n + 100, budget=budget)
+    _decode_case(ora, w)
+
+
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (24, 8), (8, 1), (5, 5)])
+def test_decode_small_gqa(ora, hq, hkv):
+    log(f"decode small GQA hq={hq} hkv={hkv}")
+    w = synth.LLAMA32_GQA_1M.replace(hq=hq, hkv=hkv, n_ctx=9001, cap=9001, budget=128)
+    _decode_case(ora, w)
+
+
+def test_decode_fp32_d64_batch(ora):
+    log("decode fp32 d=64 batch 3")
+    w = synth.TINY.replace(batch=3, hq=4, hkv=2, n_ctx=3000, cap=3000, budget=100)
+    _decode_case(ora, w)
+
+
+def test_decode_full_budget_equals_dense(ora):
+    log("decode: budget >= n equals dense attention over all n rows")
+    w = synth.LLAMA2_32K.replace(hq=2, hkv=2, n_ctx=500, cap=500, budget=512)
+    lay, out, idx = _decode_case(ora, w)
+    assert idx[..., :500].equal(torch.arange(500, device=DEV, dtype=torch.int32).expand(1, 2, 500))
+    assert (idx[..., 500:] == -1).all()
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    dense_idx = np.tile(np.arange(500, dtype=np.int32), (1, 2, 1))
+    ref, _ = ora.sparse_attend(q, k, v, dense_idx)
+    assert rel_err(out, ref) <= TOL[torch.bfloat16]
+
+
+def test_decode_deterministic_and_workspace_reuse(ora):
+    log("decode: run-twice bit determinism; one workspace across shapes")
+    ws = adamas.Workspace(DEV)
+    w = synth.LLAMA2_32K.replace(hq=8, hkv=8, n_ctx=12000, cap=12000, budget=256)
+    lay = synth.make_layer(w, 0, DEV)
+    codes = torch.zeros((1, 8, 12000, 32), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    outs = []
+    for n, bud in ((12000, 256), (5000, 64), (12000, 256), (777, 1024), (12000, 256)):
+        idx = torch.empty((1, 8, bud), dtype=torch.int32, device=DEV)
+        o = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, n, bud, idx_out=idx, ws=ws)
+        outs.append((n, bud, o.clone(), idx.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][2], outs[2][2]) and torch.equal(outs[0][2], outs[4][2])
+    assert torch.equal(outs[0][3], outs[2][3]) and torch.equal(outs[0][3], outs[4][3])
+    # control bytes back to zero after every call
+    assert not ws.buf[:adamas.WS_CTRL_BYTES].any()
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    oc = ora.encode_keys(k)
+    for n, bud, o, idx in outs[:4]:
+        _, _, oidx = ora.decode_step(q, k, v, oc, n, bud)
+        assert np.array_equal(idx.cpu().numpy(), oidx)
