@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the MI355X ADAMAS path (one GPU).
+
+Workload: batch 1, 32 heads (MHA), head_dim 128, 131072 cached tokens per
+layer, 32 layers, bf16 K/V, token budget 256 (Llama-2-7B-shaped 128K decode).
+A step runs the fused decode step of every layer in sequence: encode the
+query heads, scan the 2-bit code cache, select the budget, attend over the
+selected rows.  K/V and the code cache are resident in HBM before timing
+(the code cache is built once, untimed, by adamas_encode_keys, like a
+prefill).  Inputs are seeded synthetic draws (synth.py).
+
+Prints ONE JSON line with:
+  value        decode tokens/s (batch / step time), step timed as a replayed
+               HIP graph of the 32 layer calls;
+  roofline     algorithmic bytes of one decode-step launch (code cache +
+               gathered K/V rows + q/out) / its average duration, from HIP
+               events recorded on the launch stream around every launch of an
+               eager pass over the same steps, against 8 TB/s;
+  cpu_baseline the CPU oracle timed on a bounded sample of layers on the host
+               cores, scaled to tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-step tokens/s + achieved HBM GB/s at 128K ctx, budget 256, 1 GPU"
+
+
+def algorithmic_bytes(B, Hq, Hkv, d, n_ctx, budget, elem_bytes):
+    """Bytes one layer's decode step must move: every cached code once,
+    the selected K and V rows, the query in and the output out."""
+    codes = B * Hkv * n_ctx * d // 4
+    rows = B * Hq * min(budget, n_ctx) * d * 2 * elem_bytes
+    qo = B * Hq * d * elem_bytes * 2
+    return codes + rows + qo
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--budget", type=int, default=256)
+    ap.add_argument("--layers", type=int, default=None, help="override the 32-layer stack")
+    ap.add_argument("--n-ctx", type=int, default=None)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target oracle CPU time for the baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU by design: no collectives).", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: multi-rank launch is not supported (single-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import compressed_key_sparse_amd as adamas
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    adamas.load()
+    w = synth.LLAMA2_128K_32L
+    if args.n_ctx:
+        w = w.replace(n_ctx=args.n_ctx, cap=args.n_ctx)
+    L = args.layers or w.layers
+    B, Hq, Hkv, d, n, bud = w.batch, w.hq, w.hkv, w.head_dim, w.n_ctx, args.budget
+    print(f"[bench] setup: {L} layers x {Hq} heads x {n} tokens x d{d} {w.dtype}, budget {bud}",
+          file=sys.stderr, flush=True)
+    t_setup = time.time()
+    layers = []
+    for l in range(L):
+        lay = synth.make_layer(w, l, dev)
+        codes = torch.empty((B, Hkv, w.cap, d // 4), dtype=torch.uint8, device=dev)
+        adamas.encode_keys(lay["k"], codes)
+        layers.append({"q": lay["q"], "k": lay["k"], "v": lay["v"], "codes": codes,
+                       "out": torch.empty_like(lay["q"]), "needles": lay["needles"]})
+    torch.cuda.synchronize()
+    print(f"[bench] setup done in {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.Stream(dev)
+    ws = adamas.Workspace(dev)
+    ws.get(adamas.workspace_bytes(adamas.OP_DECODE_STEP, B, Hq, Hkv, n, bud, d))
+
+    def run_step():
+        for lay in layers:
+            adamas.decode_step(lay["q"], lay["k"], lay["v"], lay["codes"], n, bud, out=lay["out"],
+                               ws=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            run_step()
+    torch.cuda.synchronize()
+
+    # -- eager pass: HIP events around every launch, on the launch stream
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(L)] for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(K):
+        for l, lay in enumerate(layers):
+            ev[s][l][0].record(stream)
+            adamas.decode_step(lay["q"], lay["k"], lay["v"], lay["codes"], n, bud, out=lay["out"],
+                               ws=ws, stream=stream)
+            ev[s][l][1].record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / K
+    launch_us = float(np.mean([a.elapsed_time(b) for row in ev for a, b in row]) * 1e3)
+
+    # -- graph pass: the 32-layer step captured once and replayed K times
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                run_step()
+            for _ in range(args.warmup):
+                g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(K):
+                g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+    ms = graph_ms if graph_ms is not None else eager_ms
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+
+    per_layer = algorithmic_bytes(B, Hq, Hkv, d, n, bud, 2)
+    step_bytes = per_layer * L
+    achieved = per_layer / (launch_us * 1e-6) / 1e9
+
+    # recall of planted needles in the last step's selection (sanity signal)
+    idx = torch.empty((B, Hq, bud), dtype=torch.int32, device=dev)
+    lay = layers[0]
+    adamas.decode_step(lay["q"], lay["k"], lay["v"], lay["codes"], n, bud, idx_out=idx, ws=ws)
+    torch.cuda.synchronize()
+    sel = idx.cpu().numpy()
+    found = sum(len(set(lay["needles"][0, h, 0].tolist()) & set(sel[0, h].tolist()))
+                for h in range(Hq))
+    recall = found / (Hq * w.needles)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(layers, w, n, bud, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(B / (ms * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": d, "n_ctx": n, "layers": L, "budget": bud,
+                   "timing": "hip-graph replay" if graph_ms is not None else "eager"},
+        "hbm_gbs_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "roofline": {"bound": "hbm", "kernel": "adamas_decode_step (one layer)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": per_layer, "launch_us": round(launch_us, 3)},
+        "needle_recall": round(recall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(layers, w, n, bud, seconds):
+    """Time the CPU oracle's decode step on whole layers of the same workload
+    until about `seconds` of oracle time has accumulated (at least one layer);
+    scale to tokens/s for the full stack."""
+    import numpy as np
+    import oracle
+    import synth
+
+    oracle.build(force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    spent, done = 0.0, 0
+    for lay in layers:
+        q, k, v = (synth.to_numpy_bits(lay[x]) for x in ("q", "k", "v"))
+        codes = oracle.encode_keys(k)               # prefill state, untimed
+        t = time.perf_counter()
+        oracle.decode_step(q, k, v, codes, n, bud)
+        spent += time.perf_counter() - t
+        done += 1
+        print(f"[bench] oracle layer {done}: {spent:.1f}s", file=sys.stderr, flush=True)
+        del q, k, v, codes
+        if spent >= seconds:
+            break
+    per_layer = spent / done
+    step = per_layer * w.layers
+    return {"value": round(w.batch / step, 4), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {w.layers} layers ({w.hq} heads x {n} tokens each, budget {bud}),"
+                      f" {spent:.1f}s of oracle time, scaled to the {w.layers}-layer step"}
+
+
+if __name__ == "__main__":
+    main()

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "adamas.h"
 #include "kernels.hpp"
 
@@ -18,45 +20,54 @@ constexpr int64_t kMaxGroups = 8192;       // B*Hq and B*Hkv (control-area slots
 constexpr size_t kCtrlSelect = 0;          // u32 counters of select / decode groups
 constexpr size_t kCtrlAttend = 32768;      // u32 counters of attention rows
 constexpr int kMaxBudget = 1 << 20;
-constexpr size_t kLdsLimit = 48 * 1024;
+constexpr size_t kLdsLimit = 64 * 1024;    // per-workgroup LDS used by any kernel here
+constexpr int kMaxCandTile = 8192;         // candidate entries staged in LDS at once
 
 bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool valid_dtype(int dt) { return dt == ADAMAS_F32 || dt == ADAMAS_BF16; }
 bool valid_dim(int d) { return d == 64 || d == 128; }
+size_t nbins_padded(int D) { return (size_t)((3 * D + 1 + 3) & ~3); }
 
-// LDS bytes of the fused selection kernel for a chunk of c tokens.
-size_t decode_lds(int D, int G, int c) {
-  const size_t nbp = (size_t)((3 * D + 1 + 3) & ~3);
-  return 64 + (size_t)G * (D / 16) * 4 + (size_t)G * nbp * 4 + (size_t)G * c * 2;
-}
-
-// Chunk of tokens per selection workgroup: large against the budget (the
-// candidates a chunk forwards are min(budget, chunk)), within the LDS limit,
-// and no larger than the context needs.
-int choose_chunk(int64_t n_ctx, int budget, int G, int D) {
-  int c = 4096;
-  while (c < 16384 && c < 8 * budget && decode_lds(D, G, 2 * c) <= kLdsLimit) c *= 2;
-  while (c > 512 && decode_lds(D, G, c) > kLdsLimit) c /= 2;
-  while (c > 512 && (int64_t)(c / 2) >= n_ctx) c /= 2;
-  return c;
-}
-
-int attend_splits(int rows) { return (rows + kAttnRows - 1) / kAttnRows; }
-
+// Candidate layout shared by the selection kernels: per head, n_chunks slots
+// of kpad = round_up(min(budget, chunk), 4) u32 entries.
 struct SelectPlan {
-  int chunk = 0, n_chunks = 0, kmax = 0;
-  size_t cand_off = 0, end = 0;
+  int chunk = 0, n_chunks = 0, kpad = 0, mcap = 0;
+  size_t cand_off = 0, end = 0, lds = 0;
 };
 
-SelectPlan plan_select(int64_t rows, int64_t n_ctx, int budget, int G, int D, size_t start) {
-  SelectPlan p;
-  p.chunk = choose_chunk(n_ctx, budget, G, D);
+void finish_select_plan(SelectPlan& p, int64_t rows, int64_t n_ctx, int budget, size_t start) {
   p.n_chunks = (int)((n_ctx + p.chunk - 1) / p.chunk);
-  p.kmax = budget < p.chunk ? budget : p.chunk;
+  const int kmax = budget < p.chunk ? budget : p.chunk;
+  p.kpad = (kmax + 3) & ~3;
+  const int64_t m = (int64_t)p.n_chunks * p.kpad;
+  p.mcap = (int)(m < kMaxCandTile ? m : kMaxCandTile);
   p.cand_off = round_up(start, 256);
-  p.end = p.cand_off + (size_t)rows * p.n_chunks * p.kmax * sizeof(uint32_t);
+  p.end = p.cand_off + (size_t)rows * (size_t)m * sizeof(uint32_t);
+}
+
+// adamas_select_topk: 1024-thread workgroups over chunks of the distances.
+SelectPlan plan_select(int64_t rows, int64_t n_ctx, int budget, int D, size_t start) {
+  SelectPlan p;
+  int c = 4096;
+  while (c < 16384 && c < 8 * budget) c *= 2;
+  while (c > kSelectThreads && (int64_t)(c / 2) >= n_ctx) c /= 2;
+  p.chunk = c;
+  finish_select_plan(p, rows, n_ctx, budget, start);
+  const size_t region = std::max((size_t)p.chunk * 2, (size_t)p.mcap * 4);
+  p.lds = kTmpWords * 4 + nbins_padded(D) * 4 + region;
   return p;
+}
+
+// Decode kernel LDS: scan phase (query words, histograms, distances) and the
+// aliasing final phase (histogram, attention partials, indices, candidates).
+size_t decode_lds_scan(int D, int G, int c) {
+  return (size_t)G * (D / 16) * 4 + (size_t)G * nbins_padded(D) * 4 + (size_t)G * c * 2;
+}
+size_t decode_lds_final(int D, int budget, int mcap) {
+  const int nw = kDecodeThreads / kWave;
+  return nbins_padded(D) * 4 + (size_t)(nw + 1) * (2 + D) * 4 +
+         (size_t)((budget + 3) & ~3) * 4 + (size_t)mcap * 4;
 }
 
 struct AttendPlan {
@@ -66,7 +77,7 @@ struct AttendPlan {
 
 AttendPlan plan_attend(int64_t rows, int sel_rows, int D, size_t start) {
   AttendPlan p;
-  p.splits = attend_splits(sel_rows);
+  p.splits = (sel_rows + kAttendRowsPerBatch - 1) / kAttendRowsPerBatch;
   p.part_off = round_up(start, 256);
   p.end = p.part_off + (p.splits > 1 ? (size_t)rows * p.splits * (2 + D) * sizeof(float) : 0);
   return p;
@@ -74,19 +85,36 @@ AttendPlan plan_attend(int64_t rows, int sel_rows, int D, size_t start) {
 
 struct DecodePlan {
   SelectPlan sel;
+  bool fuse = false;
   size_t idx_off = 0;
   AttendPlan att;
   size_t total = 0;
 };
 
+// adamas_decode_step: 1024-thread workgroups, chunks as large as LDS allows
+// (fewer candidates to merge), attention fused into the selecting workgroup
+// when the selection is small (at most two 256-row batches for the group).
 DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D) {
   DecodePlan p;
+  const int G = Hq / Hkv;
   const int64_t rows = (int64_t)B * Hq;
-  p.sel = plan_select(rows, n_ctx, budget, Hq / Hkv, D, ADAMAS_WS_CTRL_BYTES);
+  int c = 16384;
+  while (c > 1024 && kTmpWords * 4 + decode_lds_scan(D, G, c) > kLdsLimit) c /= 2;
+  while (c > 1024 && (int64_t)(c / 2) >= n_ctx) c /= 2;
+  p.sel.chunk = c;
+  finish_select_plan(p.sel, rows, n_ctx, budget, ADAMAS_WS_CTRL_BYTES);
+  const int bsel = (int)(n_ctx < budget ? n_ctx : budget);
+  const int batches = G * ((bsel + kAttendRowsPerBatch - 1) / kAttendRowsPerBatch);
+  p.fuse = batches <= 2;
+  // shrink the LDS candidate tile if the final phase would not fit
+  while (p.sel.mcap > 256 &&
+         kTmpWords * 4 + decode_lds_final(D, budget, p.sel.mcap) > kLdsLimit)
+    p.sel.mcap = (p.sel.mcap / 2 + 3) & ~3;
+  p.sel.lds = kTmpWords * 4 + std::max(decode_lds_scan(D, G, c),
+                                       decode_lds_final(D, budget, p.sel.mcap));
   p.idx_off = round_up(p.sel.end, 256);
   const size_t idx_end = p.idx_off + (size_t)rows * budget * sizeof(int32_t);
-  const int sel_rows = (int)(n_ctx < budget ? n_ctx : budget);
-  p.att = plan_attend(rows, sel_rows, D, idx_end);
+  p.att = plan_attend(rows, bsel, D, idx_end);
   p.total = round_up(p.att.end, 256);
   return p;
 }
@@ -99,16 +127,7 @@ int launch_status() {
 template <int D, int G>
 void launch_score_t(dim3 grid, hipStream_t s, const uint8_t* qc, const uint8_t* kc, int Hq,
                     int Hkv, int64_t cap, int64_t n_ctx, int chunk, uint16_t* dist) {
-  k_score<D, G><<<grid, kBlock, 0, s>>>(qc, kc, Hq, Hkv, cap, n_ctx, chunk, dist);
-}
-
-template <int D, int G>
-void launch_decode_select_t(dim3 grid, size_t lds, hipStream_t s, const void* q, int bf,
-                            const uint8_t* kc, int Hq, int Hkv, int64_t cap, int64_t n_ctx,
-                            int chunk, int n_chunks, int budget, uint32_t* cand, uint32_t* ctr,
-                            int32_t* idx) {
-  k_decode_select<D, G><<<grid, kBlock, lds, s>>>(q, bf, kc, Hq, Hkv, cap, n_ctx, chunk,
-                                                  n_chunks, budget, cand, ctr, idx);
+  k_score<D, G><<<grid, kScoreThreads, 0, s>>>(qc, kc, Hq, Hkv, cap, n_ctx, chunk, dist);
 }
 
 template <int D>
@@ -124,17 +143,30 @@ bool dispatch_score(int G, dim3 grid, hipStream_t s, const uint8_t* qc, const ui
   }
 }
 
-template <int D>
-bool dispatch_decode_select(int G, dim3 grid, size_t lds, hipStream_t s, const void* q, int bf,
-                            const uint8_t* kc, int Hq, int Hkv, int64_t cap, int64_t n_ctx,
-                            int chunk, int n_chunks, int budget, uint32_t* cand, uint32_t* ctr,
-                            int32_t* idx) {
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const uint8_t* kc;
+  int Hq, Hkv;
+  int64_t cap, n_ctx;
+  int budget;
+  float qscale;
+  uint32_t *cand, *ctr;
+  int32_t* idx;
+  void* out;
+};
+
+template <int D, int G, bool BF>
+void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  k_decode<D, G, BF><<<grid, kDecodeThreads, p.sel.lds, s>>>(
+      a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
+      p.sel.kpad, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx, a.out);
+}
+
+template <int D, bool BF>
+bool dispatch_decode(int G, const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
   switch (G) {
-#define ADM_CASE(g)                                                                      \
-  case g:                                                                                \
-    launch_decode_select_t<D, g>(grid, lds, s, q, bf, kc, Hq, Hkv, cap, n_ctx, chunk,    \
-                                 n_chunks, budget, cand, ctr, idx);                      \
-    return true;
+#define ADM_CASE(g) \
+  case g: launch_decode_t<D, g, BF>(p, grid, s, a); return true;
     ADM_CASE(1) ADM_CASE(2) ADM_CASE(3) ADM_CASE(4) ADM_CASE(5) ADM_CASE(6) ADM_CASE(7)
     ADM_CASE(8)
 #undef ADM_CASE
@@ -142,15 +174,24 @@ bool dispatch_decode_select(int G, dim3 grid, size_t lds, hipStream_t s, const v
   }
 }
 
-void launch_attend(int D, dim3 grid, hipStream_t s, const void* q, const void* k, const void* v,
-                   int bf, const int32_t* idx, int Hq, int Hkv, int64_t cap, int budget,
+void launch_attend(int D, bool bf, dim3 grid, hipStream_t s, const void* q, const void* k,
+                   const void* v, const int32_t* idx, int Hq, int Hkv, int64_t cap, int budget,
                    float qscale, float* part, uint32_t* ctr, void* out) {
-  if (D == 128)
-    k_attend<128><<<grid, kBlock, 0, s>>>(q, k, v, bf, idx, Hq, Hkv, cap, budget, qscale, part,
-                                          ctr, out);
-  else
-    k_attend<64><<<grid, kBlock, 0, s>>>(q, k, v, bf, idx, Hq, Hkv, cap, budget, qscale, part,
-                                         ctr, out);
+  if (D == 128) {
+    if (bf)
+      k_attend<128, true><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
+                                                          qscale, part, ctr, out);
+    else
+      k_attend<128, false><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
+                                                           qscale, part, ctr, out);
+  } else {
+    if (bf)
+      k_attend<64, true><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
+                                                         qscale, part, ctr, out);
+    else
+      k_attend<64, false><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
+                                                          qscale, part, ctr, out);
+  }
 }
 
 // Score scale in the log2 domain: s2 = (q . k) * scale * log2(e).
@@ -185,7 +226,7 @@ size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx, int
   const int64_t rows = (int64_t)B * Hq;
   switch (op) {
     case ADAMAS_OP_SELECT_TOPK:
-      return round_up(plan_select(rows, n_ctx, budget, 1, head_dim, ADAMAS_WS_CTRL_BYTES).end,
+      return round_up(plan_select(rows, n_ctx, budget, head_dim, ADAMAS_WS_CTRL_BYTES).end,
                       256);
     case ADAMAS_OP_SPARSE_ATTEND:
       return round_up(plan_attend(rows, budget, head_dim, ADAMAS_WS_CTRL_BYTES).end, 256);
@@ -209,9 +250,9 @@ int adamas_encode_keys(const void* x, int dtype, int batch, int heads, int64_t n
   const unsigned blocks = (unsigned)(blocks64 < 16384 ? blocks64 : 16384);
   const int bf = dtype == ADAMAS_BF16;
   if (head_dim == 128)
-    k_encode<128><<<blocks, kBlock, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst);
+    k_encode<128><<<blocks, kEncodeThreads, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst);
   else
-    k_encode<64><<<blocks, kBlock, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst);
+    k_encode<64><<<blocks, kEncodeThreads, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst);
   return launch_status();
 }
 
@@ -246,20 +287,18 @@ int adamas_select_topk(const uint16_t* dist, int B, int Hq, int64_t n_ctx, int h
   if (!aligned16(dist) || !aligned16(idx)) return ADAMAS_ERR_INVALID;
   if (ws == nullptr || !aligned16(ws)) return ADAMAS_ERR_WORKSPACE;
   const int64_t rows = (int64_t)B * Hq;
-  const SelectPlan p = plan_select(rows, n_ctx, budget, 1, head_dim, ADAMAS_WS_CTRL_BYTES);
+  const SelectPlan p = plan_select(rows, n_ctx, budget, head_dim, ADAMAS_WS_CTRL_BYTES);
   if (ws_bytes < round_up(p.end, 256)) return ADAMAS_ERR_WORKSPACE;
   uint8_t* w = static_cast<uint8_t*>(ws);
   const dim3 grid((unsigned)p.n_chunks, (unsigned)Hq, (unsigned)B);
-  const size_t nbp = (size_t)((3 * head_dim + 1 + 3) & ~3);
-  const size_t lds = 64 + nbp * 4 + (size_t)p.chunk * 2;
   uint32_t* cand = reinterpret_cast<uint32_t*>(w + p.cand_off);
   uint32_t* ctr = reinterpret_cast<uint32_t*>(w + kCtrlSelect);
   if (head_dim == 128)
-    k_select<128><<<grid, kBlock, lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks, budget,
-                                                 cand, ctr, idx);
+    k_select<128><<<grid, kSelectThreads, p.lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks,
+                                                           budget, p.kpad, p.mcap, cand, ctr, idx);
   else
-    k_select<64><<<grid, kBlock, lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks, budget,
-                                                cand, ctr, idx);
+    k_select<64><<<grid, kSelectThreads, p.lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks,
+                                                          budget, p.kpad, p.mcap, cand, ctr, idx);
   return launch_status();
 }
 
@@ -280,7 +319,7 @@ int adamas_sparse_attend(const void* q, const void* k, const void* v, int dtype,
   if (ws_bytes < round_up(p.end, 256)) return ADAMAS_ERR_WORKSPACE;
   uint8_t* w = static_cast<uint8_t*>(ws);
   const dim3 grid((unsigned)p.splits, (unsigned)Hq, (unsigned)B);
-  launch_attend(head_dim, grid, stream, q, k, v, dtype == ADAMAS_BF16, idx, Hq, Hkv, cap, budget,
+  launch_attend(head_dim, dtype == ADAMAS_BF16, grid, stream, q, k, v, idx, Hq, Hkv, cap, budget,
                 attend_qscale(scale, head_dim), reinterpret_cast<float*>(w + p.part_off),
                 reinterpret_cast<uint32_t*>(w + kCtrlAttend), out);
   return launch_status();
@@ -305,24 +344,28 @@ int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_
   if (ws_bytes < p.total) return ADAMAS_ERR_WORKSPACE;
   uint8_t* w = static_cast<uint8_t*>(ws);
   const int G = Hq / Hkv;
-  const int bf = dtype == ADAMAS_BF16;
-  int32_t* idx = idx_out != nullptr ? idx_out : reinterpret_cast<int32_t*>(w + p.idx_off);
-  const dim3 gsel((unsigned)p.sel.n_chunks, (unsigned)Hkv, (unsigned)B);
-  const size_t lds = decode_lds(head_dim, G, p.sel.chunk);
-  uint32_t* cand = reinterpret_cast<uint32_t*>(w + p.sel.cand_off);
-  uint32_t* ctr_sel = reinterpret_cast<uint32_t*>(w + kCtrlSelect);
-  const bool ok = head_dim == 128
-                      ? dispatch_decode_select<128>(G, gsel, lds, stream, q, bf, k_codes, Hq, Hkv,
-                                                    cap, n_ctx, p.sel.chunk, p.sel.n_chunks,
-                                                    budget, cand, ctr_sel, idx)
-                      : dispatch_decode_select<64>(G, gsel, lds, stream, q, bf, k_codes, Hq, Hkv,
-                                                   cap, n_ctx, p.sel.chunk, p.sel.n_chunks,
-                                                   budget, cand, ctr_sel, idx);
+  const bool bf = dtype == ADAMAS_BF16;
+  int32_t* idx = idx_out != nullptr ? idx_out
+                 : p.fuse       ? nullptr
+                                : reinterpret_cast<int32_t*>(w + p.idx_off);
+  DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
+               reinterpret_cast<uint32_t*>(w + p.sel.cand_off),
+               reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out};
+  const dim3 grid((unsigned)p.sel.n_chunks, (unsigned)Hkv, (unsigned)B);
+  bool ok;
+  if (head_dim == 128)
+    ok = bf ? dispatch_decode<128, true>(G, p, grid, stream, a)
+            : dispatch_decode<128, false>(G, p, grid, stream, a);
+  else
+    ok = bf ? dispatch_decode<64, true>(G, p, grid, stream, a)
+            : dispatch_decode<64, false>(G, p, grid, stream, a);
   if (!ok) return ADAMAS_ERR_UNSUPPORTED;
-  const dim3 gatt((unsigned)p.att.splits, (unsigned)Hq, (unsigned)B);
-  launch_attend(head_dim, gatt, stream, q, k, v, bf, idx, Hq, Hkv, cap, budget,
-                attend_qscale(scale, head_dim), reinterpret_cast<float*>(w + p.att.part_off),
-                reinterpret_cast<uint32_t*>(w + kCtrlAttend), out);
+  if (!p.fuse) {
+    const dim3 gatt((unsigned)p.att.splits, (unsigned)Hq, (unsigned)B);
+    launch_attend(head_dim, bf, gatt, stream, q, k, v, idx, Hq, Hkv, cap, budget, a.qscale,
+                  reinterpret_cast<float*>(w + p.att.part_off),
+                  reinterpret_cast<uint32_t*>(w + kCtrlAttend), out);
+  }
   return launch_status();
 }
 

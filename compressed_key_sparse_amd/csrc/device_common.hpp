@@ -14,7 +14,13 @@
 namespace adm {
 
 constexpr int kWave = 64;
-constexpr int kBlock = 256;  // every kernel here runs 4 waves per workgroup
+
+// LDS scratch words used by the block-level helpers (s_tmp[0..31]).
+constexpr int kTmpWaveSums = 0;   // [0, 16): per-wave partial sums
+constexpr int kTmpThrT = 16;      // threshold bin
+constexpr int kTmpThrLt = 17;     // count below the threshold
+constexpr int kTmpFlag = 20;      // "last arrival" flag
+constexpr int kTmpWords = 32;
 
 // ---------------------------------------------------------------- elements
 ADM_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -49,6 +55,31 @@ ADM_DEV void load_elems(const void* base, bool is_bf16, int64_t i, float (&out)[
       out[0] = *p;
     }
   }
+}
+
+// Data handed from one workgroup to another within a launch (candidate
+// lists, attention partials) is written and read with device-scope atomic
+// stores and loads.  Those are coherent across the XCDs' separate L2 caches
+// by themselves, so the hand-off needs no L2 write-back or invalidation: the
+// writer only waits for its stores to complete before counting its arrival.
+ADM_DEV void store_shared(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+ADM_DEV uint32_t load_shared(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+ADM_DEV void store_shared_f32(float* p, float v) {
+  store_shared(reinterpret_cast<uint32_t*>(p), __float_as_uint(v));
+}
+ADM_DEV float load_shared_f32(const float* p) {
+  return __uint_as_float(load_shared(reinterpret_cast<const uint32_t*>(p)));
+}
+
+// Streaming 16-byte load that is not expected to be reused (non-temporal).
+ADM_DEV uint4 load_stream(const uint4* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
 }
 
 // ---------------------------------------------------------- §2.1 + §2.2
@@ -103,7 +134,7 @@ ADM_DEV uint32_t wave_encode(float (&y)[D / 64]) {
   for (int e = 0; e < E; ++e) {
     const float v = y[e];
     const uint32_t c = (v < t0) ? 0u : (v < 0.0f) ? 1u : (v < t2) ? 2u : 3u;
-    const int i = lane * E + e;                       // dimension index
+    const int i = lane * E + e;                            // dimension index
     const int pos = 8 * ((i >> 2) & 3) + 6 - 2 * (i & 3);  // bit position in its word
     bits |= c << pos;
   }
@@ -152,22 +183,57 @@ ADM_DEV uint32_t swap_pair(uint32_t v) {
 }
 
 // ----------------------------------------------------------- block scans
-// Inclusive prefix sum of one u32 per thread over the 256-thread block.
-// Uses s_tmp[0..3]; contains two barriers.
+// DPP controls (GFX9 data-parallel primitives on 16-lane rows).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;
+
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+ADM_DEV uint32_t dpp_u32(uint32_t v) {
+  // lanes whose source is outside the row, or whose row is masked off, get 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+template <int CTRL>
+ADM_DEV float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront: shifts of 1, 2, 4, 8
+// inside each 16-lane row, then row broadcasts of lanes 15 and 31 carry the
+// row totals into the following rows.
+ADM_DEV uint32_t wave_scan_incl(uint32_t v) {
+  v += dpp_u32<kDppRowShr1>(v);
+  v += dpp_u32<kDppRowShr2>(v);
+  v += dpp_u32<kDppRowShr4>(v);
+  v += dpp_u32<kDppRowShr8>(v);
+  v += dpp_u32<kDppRowBcast15, 0xA>(v);
+  v += dpp_u32<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
+// Sum over each 16-lane row, returned on every lane of the row.
+ADM_DEV float row16_sum(float x) {
+  x += dpp_f32<kDppQuadXor1>(x);
+  x += dpp_f32<kDppQuadXor2>(x);
+  x += dpp_f32<kDppRowRor4>(x);
+  x += dpp_f32<kDppRowRor8>(x);
+  return x;
+}
+
+// Inclusive prefix sum of one u32 per thread over an NT-thread block.
+// Uses s_tmp[0 .. NT/64); contains two barriers.
+template <int NT>
 ADM_DEV uint32_t block_scan_incl(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
+  constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t n = __shfl_up(v, o);
-    if (lane >= o) v += n;
-  }
-  if (lane == kWave - 1) s_tmp[wid] = v;
+  v = wave_scan_incl(v);
+  if (lane == kWave - 1) s_tmp[kTmpWaveSums + wid] = v;
   __syncthreads();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kBlock / kWave; ++w) {
-    uint32_t x = s_tmp[w];
+  for (int w = 0; w < NW; ++w) {
+    uint32_t x = s_tmp[kTmpWaveSums + w];
     pre += (w < wid) ? x : 0u;
     tot += x;
   }
@@ -183,118 +249,215 @@ struct Threshold {
   int t;
   uint32_t lt;
 };
+template <int NT>
 ADM_DEV Threshold find_threshold(const uint32_t* hist, int nbins, uint32_t K, uint32_t* s_tmp) {
-  const int bpt = (nbins + kBlock - 1) / kBlock;
+  const int bpt = (nbins + NT - 1) / NT;
   const int b0 = threadIdx.x * bpt;
   uint32_t sum = 0;
   for (int i = 0; i < bpt; ++i)
     if (b0 + i < nbins) sum += hist[b0 + i];
   uint32_t tot;
-  const uint32_t incl = block_scan_incl(sum, s_tmp, &tot);
+  const uint32_t incl = block_scan_incl<NT>(sum, s_tmp, &tot);
   const uint32_t excl = incl - sum;
   if (excl < K && K <= incl) {
     uint32_t c = excl;
     for (int i = 0; i < bpt; ++i) {
       const uint32_t h = hist[b0 + i];
       if (c + h >= K) {
-        s_tmp[8] = (uint32_t)(b0 + i);
-        s_tmp[9] = c;
+        s_tmp[kTmpThrT] = (uint32_t)(b0 + i);
+        s_tmp[kTmpThrLt] = c;
         break;
       }
       c += h;
     }
   }
   __syncthreads();
-  Threshold r{(int)s_tmp[8], s_tmp[9]};
+  Threshold r{(int)s_tmp[kTmpThrT], s_tmp[kTmpThrLt]};
   __syncthreads();
   return r;
 }
 
 // Ordered selection inside one chunk held in LDS.  Keeps every token with
 // D < t and the first `quota` tokens (lowest index) with D == t, and writes
-// them in token order as (D << 16) | token to out[].  Token i is kept at
-// position (#kept-lt before i) + min(#eq before i, quota).
-ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, int tpt, Threshold thr,
-                           uint32_t quota, uint32_t* out, uint32_t* s_tmp) {
-  const int t0 = threadIdx.x * tpt;
-  uint32_t lt = 0, eq = 0;
-  for (int i = 0; i < tpt; ++i) {
-    const int t = t0 + i;
-    if (t < valid) {
-      const int d = sdist[t];
-      lt += d < thr.t;
-      eq += d == thr.t;
+// them in token order as (D << 16) | token to out[]; entries [kept, pad_to)
+// of out[] get the sentinel 0xFFFFFFFF.  Token i is kept at position
+// (#lt before i) + min(#eq before i, quota).  Thread j owns tokens
+// [j*TPT, (j+1)*TPT), read once with 16-byte LDS loads (TPT in {1,2,4,8,16};
+// distances past `valid` must be >= 3*D+1 or never read: they are masked).
+template <int NT, int TPT>
+ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint32_t quota,
+                           uint32_t* out, int kept, int pad_to, uint32_t* s_tmp) {
+  const int t0 = threadIdx.x * TPT;
+  uint32_t d[TPT];
+  if constexpr (TPT >= 8) {
+#pragma unroll
+    for (int v8 = 0; v8 < TPT / 8; ++v8) {
+      const uint4 w = *reinterpret_cast<const uint4*>(sdist + t0 + 8 * v8);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d[8 * v8 + 2 * i] = ws[i] & 0xffffu;
+        d[8 * v8 + 2 * i + 1] = ws[i] >> 16;
+      }
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) d[i] = sdist[t0 + i];
+  }
+  uint32_t lt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    if (t0 + i >= valid) d[i] = 0xffffu;  // masked: neither below nor at the threshold
+    lt += (int)d[i] < thr.t;
+    eq += (int)d[i] == thr.t;
   }
   uint32_t tot;
   const uint32_t mine = lt | (eq << 16);
-  const uint32_t ex = block_scan_incl(mine, s_tmp, &tot) - mine;
+  const uint32_t ex = block_scan_incl<NT>(mine, s_tmp, &tot) - mine;
   uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
-  for (int i = 0; i < tpt; ++i) {
-    const int t = t0 + i;
-    if (t < valid) {
-      const uint32_t d = sdist[t];
-      if ((int)d < thr.t) {
-        out[ltb + (eqb < quota ? eqb : quota)] = (d << 16) | (uint32_t)t;
-        ++ltb;
-      } else if ((int)d == thr.t) {
-        if (eqb < quota) out[ltb + eqb] = (d << 16) | (uint32_t)t;
-        ++eqb;
-      }
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    if ((int)d[i] < thr.t) {
+      store_shared(&out[ltb + (eqb < quota ? eqb : quota)], (d[i] << 16) | (uint32_t)(t0 + i));
+      ++ltb;
+    } else if ((int)d[i] == thr.t) {
+      if (eqb < quota) store_shared(&out[ltb + eqb], (d[i] << 16) | (uint32_t)(t0 + i));
+      ++eqb;
+    }
+  }
+  for (int j = kept + (int)threadIdx.x; j < pad_to; j += NT) store_shared(&out[j], 0xFFFFFFFFu);
+}
+
+// Dispatch on tokens per thread (chunk / NT, a power of two up to 16).
+template <int NT>
+ADM_DEV void chunk_compact_any(int tpt, const uint16_t* sdist, int valid, Threshold thr,
+                               uint32_t quota, uint32_t* out, int kept, int pad_to,
+                               uint32_t* s_tmp) {
+  switch (tpt) {
+    case 1: chunk_compact<NT, 1>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
+    case 2: chunk_compact<NT, 2>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
+    case 4: chunk_compact<NT, 4>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
+    case 8: chunk_compact<NT, 8>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
+    default: chunk_compact<NT, 16>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
+  }
+}
+
+// Copy n u32 written by other workgroups of this launch from global memory
+// to LDS, with up to 16 outstanding coherent loads per thread.  The barrier
+// between the loads and the LDS stores keeps the compiler from sinking each
+// load into its store (which would serialize them).  Contains one barrier per
+// 16*NT elements.
+template <int NT>
+ADM_DEV void bulk_load_shared(uint32_t* dst, const uint32_t* src, int n) {
+  constexpr int UL = 16;
+  for (int base = 0; base < n; base += NT * UL) {
+    uint32_t r[UL];
+#pragma unroll
+    for (int j = 0; j < UL; ++j) {
+      const int i = base + j * NT + (int)threadIdx.x;
+      if (base + j * NT < n) r[j] = load_shared(src + (i < n ? i : n - 1));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < UL; ++j) {
+      const int i = base + j * NT + (int)threadIdx.x;
+      if (base + j * NT < n && i < n) dst[i] = r[j];
     }
   }
 }
 
-// Final selection of one head from its chunk candidates.  cand[] holds, per
-// chunk c, Kmax entries (D << 16 | token-in-chunk) in token order (the last
-// chunk holds k_last), so the array is in global token order.  Keeps the
-// bsel smallest (D, token) and writes the tokens, ascending, to idx[0..bsel),
-// then -1 up to budget.  shist must hold nbins words of LDS.
-ADM_DEV void final_select(const uint32_t* cand, int n_chunks, int kmax, int k_last, int chunk,
-                          int bsel, int budget, int32_t* idx, uint32_t* shist, int nbins,
-                          uint32_t* s_tmp) {
-  const int M = (n_chunks - 1) * kmax + k_last;
-  for (int i = threadIdx.x; i < nbins; i += kBlock) shist[i] = 0;
+// Final selection of one head from its chunk candidates.  cand[] (global,
+// written by store_shared) holds n_chunks slots of kpad entries (D << 16 | token in
+// chunk) in token order, unused entries 0xFFFFFFFF, so the array is in global
+// token order.  Keeps the bsel smallest (D, token), writes the tokens,
+// ascending, to sidx[0..bsel) (LDS, if non-null) and idx[0..bsel) (global, if
+// non-null) followed by -1 up to budget.  Candidates pass through LDS scand[]
+// (capacity mcap) in tiles; one tile when M <= mcap.
+template <int NT>
+ADM_DEV void final_select(const uint32_t* cand, int M, int kpad, int chunk, int nbins, int bsel,
+                          int budget, int32_t* sidx, int32_t* idx, uint32_t* scand, int mcap,
+                          uint32_t* shist, uint32_t* s_tmp) {
+  const bool resident = M <= mcap;
+  for (int i = threadIdx.x; i < nbins; i += NT) shist[i] = 0;
+  for (int base = 0; base < M; base += mcap) {
+    const int n = min(mcap, M - base);
+    __syncthreads();
+    bulk_load_shared<NT>(scand, cand + base, n);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const uint32_t d = scand[i] >> 16;
+      if ((int)d < nbins) atomicAdd(&shist[d], 1u);
+    }
+  }
   __syncthreads();
-  for (int i = threadIdx.x; i < M; i += kBlock) atomicAdd(&shist[cand[i] >> 16], 1u);
-  __syncthreads();
-  const Threshold thr = find_threshold(shist, nbins, (uint32_t)bsel, s_tmp);
+  const Threshold thr = find_threshold<NT>(shist, nbins, (uint32_t)bsel, s_tmp);
   const uint32_t quota = (uint32_t)bsel - thr.lt;
-  constexpr int kTpt = 16;
   uint32_t carry_lt = 0, carry_eq = 0;
-  for (int base = 0; base < M; base += kBlock * kTpt) {
-    const int i0 = base + threadIdx.x * kTpt;
+  for (int base = 0; base < M; base += mcap) {
+    const int n = min(mcap, M - base);
+    if (!resident) {
+      __syncthreads();
+      bulk_load_shared<NT>(scand, cand + base, n);
+      __syncthreads();
+    }
+    const int tpt = (n + NT - 1) / NT;
+    const int i0 = threadIdx.x * tpt;
     uint32_t lt = 0, eq = 0;
-    for (int i = 0; i < kTpt; ++i) {
-      if (i0 + i < M) {
-        const int d = (int)(cand[i0 + i] >> 16);
+    for (int i = 0; i < tpt; ++i) {
+      if (i0 + i < n) {
+        const int d = (int)(scand[i0 + i] >> 16);
         lt += d < thr.t;
         eq += d == thr.t;
       }
     }
     uint32_t tot;
     const uint32_t mine = lt | (eq << 16);
-    const uint32_t ex = block_scan_incl(mine, s_tmp, &tot) - mine;
+    const uint32_t ex = block_scan_incl<NT>(mine, s_tmp, &tot) - mine;
     uint32_t ltb = carry_lt + (ex & 0xffffu), eqb = carry_eq + (ex >> 16);
-    for (int i = 0; i < kTpt; ++i) {
+    for (int i = 0; i < tpt; ++i) {
       const int j = i0 + i;
-      if (j < M) {
-        const uint32_t v = cand[j];
+      if (j < n) {
+        const uint32_t v = scand[j];
         const int d = (int)(v >> 16);
-        const int32_t tok = (j / kmax) * chunk + (int32_t)(v & 0xffffu);
+        int pos = -1;
         if (d < thr.t) {
-          idx[ltb + (eqb < quota ? eqb : quota)] = tok;
+          pos = (int)(ltb + (eqb < quota ? eqb : quota));
           ++ltb;
         } else if (d == thr.t) {
-          if (eqb < quota) idx[ltb + eqb] = tok;
+          if (eqb < quota) pos = (int)(ltb + eqb);
           ++eqb;
+        }
+        if (pos >= 0) {
+          const int32_t tok = ((base + j) / kpad) * chunk + (int32_t)(v & 0xffffu);
+          if (sidx) sidx[pos] = tok;
+          if (idx) idx[pos] = tok;
         }
       }
     }
     carry_lt += tot & 0xffffu;
     carry_eq += tot >> 16;
   }
-  for (int j = bsel + threadIdx.x; j < budget; j += kBlock) idx[j] = -1;
+  if (idx)
+    for (int j = bsel + threadIdx.x; j < budget; j += NT) idx[j] = -1;
+  __syncthreads();
+}
+
+// Count this workgroup's arrival after its store_shared writes completed;
+// returns true on the last of n_arrivals workgroups, whose load_shared reads
+// then see every earlier workgroup's writes.  Each thread waits for its own
+// stores (workgroup-scope release), the barrier orders the whole workgroup
+// before the count, and the count itself is a device-scope atomic.
+template <int NT>
+ADM_DEV bool arrive_last(uint32_t* counter, int n_arrivals, uint32_t* s_tmp) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_tmp[kTmpFlag] = (prev == (uint32_t)(n_arrivals - 1)) ? 1u : 0u;
+  }
+  __syncthreads();
+  return s_tmp[kTmpFlag] != 0;
 }
 
 }  // namespace adm

@@ -12,19 +12,29 @@ namespace adm {
 constexpr int kNbins(int D) { return 3 * D + 1; }
 constexpr int kNbinsPadded(int D) { return (3 * D + 1 + 3) & ~3; }
 
+constexpr int kEncodeThreads = 256;
+constexpr int kScoreThreads = 256;
+constexpr int kSelectThreads = 1024;
+constexpr int kDecodeThreads = 1024;  // one workgroup of 16 wavefronts per CU
+constexpr int kAttendThreads = 1024;
+constexpr int kAttendRowsPerSlot = 4;  // rows a 16-lane slot holds in flight
+constexpr int kAttendRowsPerBatch = (kAttendThreads / 16) * kAttendRowsPerSlot;  // 256
+
 // ------------------------------------------------------------------ encode
 // §2.1 + §2.2 + §3.1 for keys (or queries): one wavefront per vector,
 // grid-stride over the batch*heads*n vectors of x[batch*heads][n][D].
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_encode(const void* __restrict__ x, int is_bf16,
-                                                   int64_t n, int64_t nvec,
-                                                   uint8_t* __restrict__ codes, int64_t cap,
-                                                   int64_t pos, void* __restrict__ copy) {
+__global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restrict__ x,
+                                                           int is_bf16, int64_t n, int64_t nvec,
+                                                           uint8_t* __restrict__ codes,
+                                                           int64_t cap, int64_t pos,
+                                                           void* __restrict__ copy) {
   constexpr int E = D / 64;
   constexpr int kLanesPerWord = 16 / E;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t nwaves = (int64_t)gridDim.x * (kBlock / kWave);
-  for (int64_t v = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; v < nvec; v += nwaves) {
+  const int64_t nwaves = (int64_t)gridDim.x * (kEncodeThreads / kWave);
+  for (int64_t v = ((int64_t)blockIdx.x * kEncodeThreads + threadIdx.x) / kWave; v < nvec;
+       v += nwaves) {
     const int64_t bh = v / n;
     const int64_t row = bh * cap + pos + (v - bh * n);
     const int64_t src = v * D + lane * E;
@@ -55,25 +65,25 @@ __global__ __launch_bounds__(kBlock) void k_encode(const void* __restrict__ x, i
 // -------------------------------------------------------------------- scan
 // §2.3: stream one chunk of packed key codes and produce, for each of the G
 // query heads sharing this KV head, the Manhattan distance of every token.
-// Codes are read as 16-byte units (64 codes); at D = 128 a token is two units
-// held by a lane pair whose partial sums are added with a DPP swap.  Loads of
-// U units per thread are issued before any of them is used.
-template <int D, int G, int U, class Sink>
+// Codes are read as 16-byte units (64 codes) with non-temporal loads, U per
+// thread in flight; at D = 128 a token is two units held by a lane pair whose
+// partial sums are added with a DPP swap.
+template <int D, int G, int NT, int U, class Sink>
 ADM_DEV void scan_chunk(const uint8_t* __restrict__ kbase, int valid, const QPlanes (&qp)[G],
                         Sink&& sink) {
   constexpr int kUnitsPerToken = D / 64;
   const int units = valid * kUnitsPerToken;
   const uint4* __restrict__ src = reinterpret_cast<const uint4*>(kbase);
-  for (int base = 0; base < units; base += kBlock * U) {
+  for (int base = 0; base < units; base += NT * U) {
     uint4 w[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int u = base + j * kBlock + (int)threadIdx.x;
-      w[j] = (u < units) ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+      const int u = base + j * NT + (int)threadIdx.x;
+      w[j] = load_stream(src + (u < units ? u : units - 1));  // clamped: always in bounds
     }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int u = base + j * kBlock + (int)threadIdx.x;
+      const int u = base + j * NT + (int)threadIdx.x;
       const uint32_t p0 = therm_p(w[j].x), p1 = therm_p(w[j].y);
       const uint32_t p2 = therm_p(w[j].z), p3 = therm_p(w[j].w);
       const uint32_t t0 = therm_t(w[j].x, w[j].y), t1 = therm_t(w[j].z, w[j].w);
@@ -113,14 +123,15 @@ ADM_DEV void load_qplanes(const uint32_t* sq, QPlanes (&qp)[G]) {
 // ------------------------------------------------------------------- score
 // adamas_score: grid (chunks, Hkv, B); query codes already encoded.
 template <int D, int G>
-__global__ __launch_bounds__(kBlock) void k_score(const uint8_t* __restrict__ q_codes,
-                                                  const uint8_t* __restrict__ k_codes, int Hq,
-                                                  int Hkv, int64_t cap, int64_t n_ctx, int chunk,
-                                                  uint16_t* __restrict__ dist) {
+__global__ __launch_bounds__(kScoreThreads) void k_score(const uint8_t* __restrict__ q_codes,
+                                                         const uint8_t* __restrict__ k_codes,
+                                                         int Hq, int Hkv, int64_t cap,
+                                                         int64_t n_ctx, int chunk,
+                                                         uint16_t* __restrict__ dist) {
   constexpr int W = D / 16;
   __shared__ uint32_t sq[G * W];
   const int c = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  for (int i = threadIdx.x; i < G * W; i += kBlock)
+  for (int i = threadIdx.x; i < G * W; i += kScoreThreads)
     sq[i] = reinterpret_cast<const uint32_t*>(
         q_codes + ((int64_t)b * Hq + (int64_t)hkv * G) * (D / 4))[i];
   __syncthreads();
@@ -130,172 +141,21 @@ __global__ __launch_bounds__(kBlock) void k_score(const uint8_t* __restrict__ q_
   const int valid = (int)min((int64_t)chunk, n_ctx - t0);
   const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
   uint16_t* drow = dist + ((int64_t)b * Hq + (int64_t)hkv * G) * n_ctx + t0;
-  scan_chunk<D, G, 4>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
+  scan_chunk<D, G, kScoreThreads, 8>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
     drow[(int64_t)g * n_ctx + tok] = (uint16_t)d;
   });
 }
 
-// --------------------------------------------------------- §5.2 selection
-// Per chunk: keep the chunk's min(budget, valid) best (D, token) as
-// candidates; a token in the global top-budget is always in its chunk's
-// top-budget, so the union of the chunk candidates contains the answer.  The
-// last workgroup of a group (atomic arrival count) selects from the union.
-ADM_DEV bool arrive_last(uint32_t* counter, int n_arrivals, uint32_t* s_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(counter, 1u);
-    *s_flag = (prev == (uint32_t)(n_arrivals - 1)) ? 1u : 0u;
-  }
-  __syncthreads();
-  const bool last = *s_flag != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-// adamas_select_topk: grid (chunks, Hq, B) over uint16 distances.
-template <int D>
-__global__ __launch_bounds__(kBlock) void k_select(const uint16_t* __restrict__ dist, int Hq,
-                                                   int64_t n_ctx, int chunk, int n_chunks,
-                                                   int budget, uint32_t* __restrict__ cand,
-                                                   uint32_t* __restrict__ counters,
-                                                   int32_t* __restrict__ idx) {
-  constexpr int NB = kNbins(D), NBP = kNbinsPadded(D);
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
-  uint32_t* shist = s_tmp + 16;
-  uint16_t* sdist = reinterpret_cast<uint16_t*>(shist + NBP);
-  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-  const int64_t row = (int64_t)b * Hq + hq;
-  for (int i = threadIdx.x; i < NBP; i += kBlock) shist[i] = 0;
-  __syncthreads();
-  const int64_t t0 = (int64_t)c * chunk;
-  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
-  const uint16_t* drow = dist + row * n_ctx + t0;
-  for (int t = threadIdx.x; t < valid; t += kBlock) {
-    // values above 3*D break the caller's contract; clamp so LDS stays in bounds
-    const uint16_t d = drow[t] < NB ? drow[t] : (uint16_t)(NB - 1);
-    sdist[t] = d;
-    atomicAdd(&shist[d], 1u);
-  }
-  __syncthreads();
-  const int kmax = min(budget, chunk);
-  const int kc = min(budget, valid);
-  const Threshold thr = find_threshold(shist, NB, (uint32_t)kc, s_tmp);
-  chunk_compact(sdist, valid, chunk / kBlock, thr, (uint32_t)kc - thr.lt,
-                cand + (row * n_chunks + c) * kmax, s_tmp);
-  if (!arrive_last(&counters[row], n_chunks, &s_tmp[12])) return;
-  const int valid_last = (int)(n_ctx - (int64_t)(n_chunks - 1) * chunk);
-  final_select(cand + row * n_chunks * kmax, n_chunks, kmax, min(budget, valid_last), chunk,
-               (int)min((int64_t)budget, n_ctx), budget, idx + row * budget, shist, NB, s_tmp);
-  if (threadIdx.x == 0) counters[row] = 0;
-}
-
-// ------------------------------------------------------- fused decode step
-// adamas_decode_step, selection half: grid (chunks, Hkv, B).  Each workgroup
-// encodes the G query heads of its KV head (§2.1-§2.2, one wavefront per
-// head), scans one chunk of codes (§2.3) keeping distances and a histogram in
-// LDS, writes the chunk's candidates, and the last workgroup of the KV head
-// selects the budget for its G query heads (§5.2).
-template <int D, int G>
-__global__ __launch_bounds__(kBlock) void k_decode_select(
-    const void* __restrict__ q, int q_bf16, const uint8_t* __restrict__ k_codes, int Hq, int Hkv,
-    int64_t cap, int64_t n_ctx, int chunk, int n_chunks, int budget, uint32_t* __restrict__ cand,
-    uint32_t* __restrict__ counters, int32_t* __restrict__ idx) {
-  constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), W = D / 16;
-  constexpr int E = D / 64, kLanesPerWord = 16 / E;
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
-  uint32_t* sq = s_tmp + 16;
-  uint32_t* shist = sq + G * W;
-  uint16_t* sdist = reinterpret_cast<uint16_t*>(shist + G * NBP);
-  const int c = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  for (int i = threadIdx.x; i < G * NBP; i += kBlock) shist[i] = 0;
-  for (int g = wid; g < G; g += kBlock / kWave) {
-    float y[E];
-    load_elems<E>(q, q_bf16 != 0, ((int64_t)b * Hq + (int64_t)hkv * G + g) * D + lane * E, y);
-    const uint32_t word = wave_encode<D>(y);
-    if (lane % kLanesPerWord == 0) sq[g * W + lane / kLanesPerWord] = word;
-  }
-  __syncthreads();
-  QPlanes qp[G];
-  load_qplanes<D, G>(sq, qp);
-  const int64_t t0 = (int64_t)c * chunk;
-  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
-  const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
-  scan_chunk<D, G, 4>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
-    sdist[g * chunk + tok] = (uint16_t)d;
-    atomicAdd(&shist[g * NBP + d], 1u);
-  });
-  __syncthreads();
-  const int kmax = min(budget, chunk);
-  const int kc = min(budget, valid);
-  for (int g = 0; g < G; ++g) {
-    const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-    const Threshold thr = find_threshold(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
-    chunk_compact(sdist + g * chunk, valid, chunk / kBlock, thr, (uint32_t)kc - thr.lt,
-                  cand + (row * n_chunks + c) * kmax, s_tmp);
-  }
-  if (!arrive_last(&counters[b * Hkv + hkv], n_chunks, &s_tmp[12])) return;
-  const int valid_last = (int)(n_ctx - (int64_t)(n_chunks - 1) * chunk);
-  const int bsel = (int)min((int64_t)budget, n_ctx);
-  for (int g = 0; g < G; ++g) {
-    const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-    final_select(cand + row * n_chunks * kmax, n_chunks, kmax, min(budget, valid_last), chunk,
-                 bsel, budget, idx + row * budget, shist, NB, s_tmp);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) counters[b * Hkv + hkv] = 0;
-}
-
 // ---------------------------------------------------------------- §6 attend
-// Split-K gather attention: grid (splits, Hq, B).  A workgroup takes up to
-// 32 selected rows; each 16-lane slot owns two rows and every lane D/16
-// dimensions.  K and V rows of a slot are loaded before any is used.  Scores
-// are kept in the log2 domain (q pre-multiplied by scale*log2(e)); partial
-// (m, l, o) triples merge by log-sum-exp, first across slots, then across
-// splits by the last-arriving workgroup of the head.
-constexpr int kAttnRowsPerSlot = 2;
-constexpr int kAttnRows = 16 * kAttnRowsPerSlot;
-
-template <int EL>
-ADM_DEV void load_row_slice(const void* base, bool is_bf16, int64_t elem, float (&out)[EL]) {
-  if (is_bf16) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + elem;
-    if constexpr (EL == 8) {
-      const uint4 w = *reinterpret_cast<const uint4*>(p);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        out[2 * i] = bf16_to_f32(ws[i] & 0xffffu);
-        out[2 * i + 1] = bf16_to_f32(ws[i] >> 16);
-      }
-    } else {
-      const uint2 w = *reinterpret_cast<const uint2*>(p);
-      out[0] = bf16_to_f32(w.x & 0xffffu);
-      out[1] = bf16_to_f32(w.x >> 16);
-      out[2] = bf16_to_f32(w.y & 0xffffu);
-      out[3] = bf16_to_f32(w.y >> 16);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-#pragma unroll
-    for (int i = 0; i < EL / 4; ++i) {
-      const float4 w = p[i];
-      out[4 * i] = w.x;
-      out[4 * i + 1] = w.y;
-      out[4 * i + 2] = w.z;
-      out[4 * i + 3] = w.w;
-    }
-  }
-}
-
+// Gather attention over a list of selected rows of one head.  A 16-lane slot
+// owns a row at a time and every lane D/16 dimensions; each slot keeps
+// kAttendRowsPerSlot rows' K and V in flight.  Scores stay in the log2 domain
+// (q pre-multiplied by scale*log2(e)) and the slots' (m, l, o) merge by
+// log-sum-exp.  On return s_res[0] = m, s_res[1] = l, s_res[2 + t] = o_t.
 struct Softmax {
   float m, l;
 };
 
-// Merge (m2, l2, o2) into (m1, l1, o1); m = -inf marks an empty partial.
 template <int EL>
 ADM_DEV void merge_partial(Softmax& a, float (&oa)[EL], Softmax bpart, const float (&ob)[EL]) {
   const float M = fmaxf(a.m, bpart.m);
@@ -308,65 +168,91 @@ ADM_DEV void merge_partial(Softmax& a, float (&oa)[EL], Softmax bpart, const flo
   a.m = M;
 }
 
-template <int D>
-__global__ __launch_bounds__(kBlock) void k_attend(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    int is_bf16, const int32_t* __restrict__ idx, int Hq, int Hkv, int64_t cap, int budget,
-    float qscale, float* __restrict__ part, uint32_t* __restrict__ counters,
-    void* __restrict__ out) {
-  constexpr int EL = D / 16;
-  constexpr int RS = kAttnRowsPerSlot;
-  __shared__ float s_part[kBlock / kWave][2 + D];
-  __shared__ uint32_t s_flag[1];
-  const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, S = gridDim.x;
-  const int G = Hq / Hkv;
-  const int64_t row = (int64_t)b * Hq + hq;
-  const int64_t kvrow0 = ((int64_t)b * Hkv + hq / G) * cap;
-  const int l16 = threadIdx.x & 15, slot = threadIdx.x >> 4;
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const bool bf = is_bf16 != 0;
-
-  float qv[EL];
-  load_row_slice<EL>(q, bf, row * D + l16 * EL, qv);
+// Raw element words of one lane's slice of a row (D/16 elements).
+template <int D, bool BF>
+struct RowRaw {
+  static constexpr int EL = D / 16;
+  static constexpr int WORDS = BF ? EL / 2 : EL;
+  uint32_t w[WORDS];
+  ADM_DEV void load(const void* base, int64_t elem) {
+    if constexpr (BF) {
+      const uint16_t* p = static_cast<const uint16_t*>(base) + elem;
+      if constexpr (WORDS == 4) {
+        const uint4 t = *reinterpret_cast<const uint4*>(p);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+      } else {
+        const uint2 t = *reinterpret_cast<const uint2*>(p);
+        w[0] = t.x; w[1] = t.y;
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
 #pragma unroll
-  for (int e = 0; e < EL; ++e) qv[e] *= qscale;
-
-  const int r0 = s * kAttnRows;
-  const int r1 = min(r0 + kAttnRows, budget);
-  int32_t tok[RS];
-#pragma unroll
-  for (int j = 0; j < RS; ++j) {
-    const int r = r0 + slot + 16 * j;
-    int32_t t = (r < r1) ? idx[row * budget + r] : -1;
-    tok[j] = (t >= 0 && (int64_t)t < cap) ? t : -1;
-  }
-  float kf[RS][EL], vf[RS][EL];
-#pragma unroll
-  for (int j = 0; j < RS; ++j) {
-    if (tok[j] >= 0) {
-      load_row_slice<EL>(k, bf, (kvrow0 + tok[j]) * D + l16 * EL, kf[j]);
-      load_row_slice<EL>(v, bf, (kvrow0 + tok[j]) * D + l16 * EL, vf[j]);
+      for (int i = 0; i < WORDS / 4; ++i) {
+        const uint4 t = p[i];
+        w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
+      }
     }
+  }
+  ADM_DEV float at(int e) const {
+    if constexpr (BF)
+      return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : bf16_to_f32(w[e >> 1] & 0xffffu);
+    else
+      return __uint_as_float(w[e]);
+  }
+};
+
+template <int D, bool BF, int NT>
+ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
+                         const void* __restrict__ v, int64_t qoff, int64_t kvrow0, int64_t cap,
+                         const int32_t* rows, int nrows, float qscale, float* s_part,
+                         float* s_res) {
+  // fp32 rows are twice the bytes: half the rows per batch keeps registers in budget
+  constexpr int EL = D / 16, NS = NT / 16, NW = NT / kWave;
+  constexpr int RB = BF ? kAttendRowsPerSlot : kAttendRowsPerSlot / 2;
+  const int l16 = threadIdx.x & 15, slot = threadIdx.x >> 4;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  float qv[EL];
+  {
+    RowRaw<D, BF> qr;
+    qr.load(q, qoff + l16 * EL);
+#pragma unroll
+    for (int e = 0; e < EL; ++e) qv[e] = qr.at(e) * qscale;
   }
   Softmax st{-INFINITY, 0.0f};
   float o[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) o[e] = 0.0f;
+  for (int r0 = 0; r0 < nrows; r0 += NS * RB) {
+    int32_t tok[RB];
 #pragma unroll
-  for (int j = 0; j < RS; ++j) {
-    if (tok[j] >= 0) {  // uniform across the 16 lanes of a slot
-      float dot = 0.0f;
+    for (int j = 0; j < RB; ++j) {
+      const int r = r0 + slot + NS * j;
+      const int32_t t = (r < nrows) ? rows[r] : -1;
+      tok[j] = (t >= 0 && (int64_t)t < cap) ? t : -1;
+    }
+    RowRaw<D, BF> kr[RB], vr[RB];
+    // unselected slots load row 0 of the head (in bounds) and are skipped below
 #pragma unroll
-      for (int e = 0; e < EL; ++e) dot += qv[e] * kf[j][e];
+    for (int j = 0; j < RB; ++j) {
+      const int64_t r = kvrow0 + (tok[j] >= 0 ? tok[j] : 0);
+      kr[j].load(k, r * D + l16 * EL);
+      vr[j].load(v, r * D + l16 * EL);
+    }
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1) dot += __shfl_xor(dot, m);
-      const float M = fmaxf(st.m, dot);
-      const float corr = (st.m == -INFINITY) ? 0.0f : exp2f(st.m - M);
-      const float p = exp2f(dot - M);
-      st.l = st.l * corr + p;
+    for (int j = 0; j < RB; ++j) {
+      if (tok[j] >= 0) {  // uniform across the 16 lanes of a slot
+        float dot = 0.0f;
 #pragma unroll
-      for (int e = 0; e < EL; ++e) o[e] = o[e] * corr + p * vf[j][e];
-      st.m = M;
+        for (int e = 0; e < EL; ++e) dot += qv[e] * kr[j].at(e);
+        dot = row16_sum(dot);
+        const float M = fmaxf(st.m, dot);
+        const float corr = (st.m == -INFINITY) ? 0.0f : exp2f(st.m - M);
+        const float p = exp2f(dot - M);
+        st.l = st.l * corr + p;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) o[e] = o[e] * corr + p * vr[j].at(e);
+        st.m = M;
+      }
     }
   }
   // merge the four slots of each wavefront (lanes ^16, ^32), then the waves
@@ -378,64 +264,224 @@ __global__ __launch_bounds__(kBlock) void k_attend(
     for (int e = 0; e < EL; ++e) oo[e] = __shfl_xor(o[e], m);
     merge_partial<EL>(st, o, other, oo);
   }
+  float* mine = s_part + wid * (2 + D);
   if (lane < 16) {
     if (lane == 0) {
-      s_part[wid][0] = st.m;
-      s_part[wid][1] = st.l;
+      mine[0] = st.m;
+      mine[1] = st.l;
     }
 #pragma unroll
-    for (int e = 0; e < EL; ++e) s_part[wid][2 + l16 * EL + e] = o[e];
+    for (int e = 0; e < EL; ++e) mine[2 + l16 * EL + e] = o[e];
   }
   __syncthreads();
-  // thread t < D combines the waves for dimension t
-  float m_all = -INFINITY, l_all = 0.0f, o_all = 0.0f;
   if (threadIdx.x < D) {
     const int dd = threadIdx.x;
-    for (int w = 0; w < kBlock / kWave; ++w) m_all = fmaxf(m_all, s_part[w][0]);
-    if (m_all != -INFINITY) {
-      for (int w = 0; w < kBlock / kWave; ++w) {
-        const float mw = s_part[w][0];
-        const float a = (mw == -INFINITY) ? 0.0f : exp2f(mw - m_all);
-        l_all += s_part[w][1] * a;
-        o_all += s_part[w][2 + dd] * a;
-      }
-    }
-  }
-  auto store_out = [&](int dd, float val) {
-    if (bf)
-      static_cast<uint16_t*>(out)[row * D + dd] = f32_to_bf16(val);
-    else
-      static_cast<float*>(out)[row * D + dd] = val;
-  };
-  if (S == 1) {
-    if (threadIdx.x < D) store_out(threadIdx.x, l_all > 0.0f ? o_all / l_all : 0.0f);
-    return;
-  }
-  float* my = part + (row * S + s) * (2 + D);
-  if (threadIdx.x < D) {
-    my[2 + threadIdx.x] = o_all;
-    if (threadIdx.x == 0) {
-      my[0] = m_all;
-      my[1] = l_all;
-    }
-  }
-  if (!arrive_last(&counters[row], S, &s_flag[0])) return;
-  if (threadIdx.x < D) {
-    const float* ps = part + row * S * (2 + D);
     float M = -INFINITY;
-    for (int i = 0; i < S; ++i) M = fmaxf(M, ps[i * (2 + D)]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_part[w * (2 + D)]);
     float L = 0.0f, O = 0.0f;
     if (M != -INFINITY) {
-      for (int i = 0; i < S; ++i) {
-        const float mi = ps[i * (2 + D)];
-        const float a = (mi == -INFINITY) ? 0.0f : exp2f(mi - M);
-        L += ps[i * (2 + D) + 1] * a;
-        O += ps[i * (2 + D) + 2 + threadIdx.x] * a;
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_part[w * (2 + D)];
+        const float a = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+        L += s_part[w * (2 + D) + 1] * a;
+        O += s_part[w * (2 + D) + 2 + dd] * a;
       }
     }
-    store_out(threadIdx.x, L > 0.0f ? O / L : 0.0f);
+    s_res[2 + dd] = O;
+    if (dd == 0) {
+      s_res[0] = M;
+      s_res[1] = L;
+    }
   }
+  __syncthreads();
+}
+
+template <bool BF>
+ADM_DEV void store_out(void* out, int64_t i, float val) {
+  if constexpr (BF)
+    static_cast<uint16_t*>(out)[i] = f32_to_bf16(val);
+  else
+    static_cast<float*>(out)[i] = val;
+}
+
+// adamas_sparse_attend (and the large-selection half of a decode step):
+// grid (splits, Hq, B), up to kAttendRowsPerBatch rows per workgroup.  With
+// more than one split, partial (m, l, o) triples are merged by the last
+// workgroup of the head.
+template <int D, bool BF>
+__global__ __launch_bounds__(kAttendThreads) void k_attend(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const int32_t* __restrict__ idx, int Hq, int Hkv, int64_t cap, int budget, float qscale,
+    float* __restrict__ part, uint32_t* __restrict__ counters, void* __restrict__ out) {
+  constexpr int NT = kAttendThreads, NW = NT / kWave, PW = 2 + D;
+  constexpr int kMergeTile = 32;
+  __shared__ uint32_t s_tmp[kTmpWords];
+  __shared__ float s_part[NW * PW];
+  __shared__ float s_res[PW];
+  __shared__ float s_tile[kMergeTile * PW];
+  const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, S = gridDim.x;
+  const int G = Hq / Hkv;
+  const int64_t row = (int64_t)b * Hq + hq;
+  const int64_t kvrow0 = ((int64_t)b * Hkv + hq / G) * cap;
+  const int r0 = s * kAttendRowsPerBatch;
+  const int nrows = min(kAttendRowsPerBatch, budget - r0);
+  attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, idx + row * budget + r0, nrows, qscale,
+                         s_part, s_res);
+  if (S == 1) {
+    if (threadIdx.x < D) {
+      const float L = s_res[1];
+      store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? s_res[2 + threadIdx.x] / L : 0.0f);
+    }
+    return;
+  }
+  float* mine = part + (row * S + s) * PW;
+  for (int i = threadIdx.x; i < PW; i += NT) store_shared_f32(&mine[i], s_res[i]);
+  if (!arrive_last<NT>(&counters[row], S, s_tmp)) return;
+  const float* ps = part + row * S * PW;
+  float M = -INFINITY, L = 0.0f, O = 0.0f;
+  for (int t0 = 0; t0 < S; t0 += kMergeTile) {
+    const int nt = min(kMergeTile, S - t0);
+    __syncthreads();
+    bulk_load_shared<NT>(reinterpret_cast<uint32_t*>(s_tile),
+                         reinterpret_cast<const uint32_t*>(ps + t0 * PW), nt * PW);
+    __syncthreads();
+    if (threadIdx.x < D) {
+      for (int i = 0; i < nt; ++i) {
+        const float mi = s_tile[i * PW];
+        if (mi == -INFINITY) continue;
+        const float Mn = fmaxf(M, mi);
+        const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+        const float bb = exp2f(mi - Mn);
+        L = L * a + s_tile[i * PW + 1] * bb;
+        O = O * a + s_tile[i * PW + 2 + threadIdx.x] * bb;
+        M = Mn;
+      }
+    }
+  }
+  if (threadIdx.x < D) store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? O / L : 0.0f);
   if (threadIdx.x == 0) counters[row] = 0;
+}
+
+// --------------------------------------------------------- §5.2 selection
+// Per chunk: keep the chunk's min(budget, valid) best (D, token) as
+// candidates; a token in the global top-budget is always in its chunk's
+// top-budget, so the union of the chunk candidates contains the answer.  The
+// last workgroup of a group (atomic arrival count) selects from the union.
+
+// adamas_select_topk: grid (chunks, Hq, B) over uint16 distances.
+template <int D>
+__global__ __launch_bounds__(kSelectThreads) void k_select(
+    const uint16_t* __restrict__ dist, int Hq, int64_t n_ctx, int chunk, int n_chunks,
+    int budget, int kpad, int mcap, uint32_t* __restrict__ cand, uint32_t* __restrict__ counters,
+    int32_t* __restrict__ idx) {
+  constexpr int NT = kSelectThreads, NB = kNbins(D), NBP = kNbinsPadded(D);
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* shist = s_tmp + kTmpWords;
+  uint8_t* region = reinterpret_cast<uint8_t*>(shist + NBP);
+  uint16_t* sdist = reinterpret_cast<uint16_t*>(region);   // phase 1
+  uint32_t* scand = reinterpret_cast<uint32_t*>(region);   // phase 2
+  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int64_t row = (int64_t)b * Hq + hq;
+  for (int i = threadIdx.x; i < NBP; i += NT) shist[i] = 0;
+  __syncthreads();
+  const int64_t t0 = (int64_t)c * chunk;
+  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
+  const uint16_t* drow = dist + row * n_ctx + t0;
+  for (int t = threadIdx.x; t < valid; t += NT) {
+    // values above 3*D break the caller's contract; clamp so LDS stays in bounds
+    const uint16_t d = drow[t] < NB ? drow[t] : (uint16_t)(NB - 1);
+    sdist[t] = d;
+    atomicAdd(&shist[d], 1u);
+  }
+  __syncthreads();
+  const int kc = min(budget, valid);
+  const Threshold thr = find_threshold<NT>(shist, NB, (uint32_t)kc, s_tmp);
+  chunk_compact_any<NT>(chunk / NT, sdist, valid, thr, (uint32_t)kc - thr.lt,
+                        cand + (row * n_chunks + c) * kpad, kc, kpad, s_tmp);
+  if (!arrive_last<NT>(&counters[row], n_chunks, s_tmp)) return;
+  final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad, chunk, NB,
+                   (int)min((int64_t)budget, n_ctx), budget, nullptr, idx + row * budget, scand,
+                   mcap, shist, s_tmp);
+  if (threadIdx.x == 0) counters[row] = 0;
+}
+
+// ------------------------------------------------------- fused decode step
+// adamas_decode_step: grid (chunks, Hkv, B) of 1024-thread workgroups.  Each
+// workgroup encodes the G query heads of its KV head (§2.1-§2.2, one
+// wavefront per head), scans one chunk of codes (§2.3) keeping distances and
+// a histogram in LDS, and writes the chunk's candidates.  The last workgroup
+// of the KV head selects the budget for its G query heads (§5.2) and, when
+// fuse_attend is set, attends over the selected rows (§6) and writes out.
+template <int D, int G, bool BF>
+__global__ __launch_bounds__(kDecodeThreads) void k_decode(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
+    int n_chunks, int budget, int kpad, int mcap, int fuse_attend, float qscale,
+    uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
+    void* __restrict__ out) {
+  constexpr int NT = kDecodeThreads, NW = NT / kWave;
+  constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), W = D / 16;
+  constexpr int E = D / 64, kLanesPerWord = 16 / E, PW = 2 + D;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
+  uint8_t* region = smem + kTmpWords * 4;
+  // phase 1 (scan) layout
+  uint32_t* sq = reinterpret_cast<uint32_t*>(region);
+  uint32_t* shist = sq + G * W;
+  uint16_t* sdist = reinterpret_cast<uint16_t*>(shist + G * NBP);
+  // phase 2 (final selection + attention) layout, aliasing phase 1
+  uint32_t* fhist = reinterpret_cast<uint32_t*>(region);
+  float* s_part = reinterpret_cast<float*>(fhist + NBP);
+  float* s_res = s_part + NW * PW;
+  int32_t* sidx = reinterpret_cast<int32_t*>(s_res + PW);
+  uint32_t* scand = reinterpret_cast<uint32_t*>(sidx + ((budget + 3) & ~3));
+
+  const int c = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  for (int i = threadIdx.x; i < G * NBP; i += NT) shist[i] = 0;
+  for (int g = wid; g < G; g += NW) {
+    float y[E];
+    load_elems<E>(q, BF, ((int64_t)b * Hq + (int64_t)hkv * G + g) * D + lane * E, y);
+    const uint32_t word = wave_encode<D>(y);
+    if (lane % kLanesPerWord == 0) sq[g * W + lane / kLanesPerWord] = word;
+  }
+  __syncthreads();
+  QPlanes qp[G];
+  load_qplanes<D, G>(sq, qp);
+  const int64_t t0 = (int64_t)c * chunk;
+  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
+  const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
+  scan_chunk<D, G, NT, 8>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
+    sdist[g * chunk + tok] = (uint16_t)d;
+    atomicAdd(&shist[g * NBP + d], 1u);
+  });
+  __syncthreads();
+  const int kc = min(budget, valid);
+  for (int g = 0; g < G; ++g) {
+    const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
+    const Threshold thr = find_threshold<NT>(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
+    chunk_compact_any<NT>(chunk / NT, sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt,
+                          cand + (row * n_chunks + c) * kpad, kc, kpad, s_tmp);
+  }
+  if (!arrive_last<NT>(&counters[b * Hkv + hkv], n_chunks, s_tmp)) return;
+  const int bsel = (int)min((int64_t)budget, n_ctx);
+  for (int g = 0; g < G; ++g) {
+    const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
+    final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad, chunk, NB, bsel, budget,
+                     fuse_attend ? sidx : nullptr, idx ? idx + row * budget : nullptr, scand,
+                     mcap, fhist, s_tmp);
+    if (fuse_attend) {
+      attend_rows<D, BF, NT>(q, k, v, row * D, ((int64_t)b * Hkv + hkv) * cap, cap, sidx, bsel,
+                             qscale, s_part, s_res);
+      if (threadIdx.x < D) {
+        const float L = s_res[1];
+        store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? s_res[2 + threadIdx.x] / L : 0.0f);
+      }
+      __syncthreads();
+    }
+  }
+  if (threadIdx.x == 0) counters[b * Hkv + hkv] = 0;
 }
 
 }  // namespace adm
