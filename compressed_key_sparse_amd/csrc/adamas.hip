@@ -30,16 +30,18 @@ bool valid_dim(int d) { return d == 64 || d == 128; }
 size_t nbins_padded(int D) { return (size_t)((3 * D + 1 + 3) & ~3); }
 
 // Candidate layout shared by the selection kernels: per head, n_chunks slots
-// of kpad = round_up(min(budget, chunk), 4) u32 entries.
+// of kpad u32 entries, kpad the power of two >= max(4, min(budget, chunk)).
 struct SelectPlan {
-  int chunk = 0, n_chunks = 0, kpad = 0, mcap = 0;
+  int chunk = 0, n_chunks = 0, kpad = 0, kpad_log2 = 0, mcap = 0;
   size_t cand_off = 0, end = 0, lds = 0;
 };
 
 void finish_select_plan(SelectPlan& p, int64_t rows, int64_t n_ctx, int budget, size_t start) {
   p.n_chunks = (int)((n_ctx + p.chunk - 1) / p.chunk);
   const int kmax = budget < p.chunk ? budget : p.chunk;
-  p.kpad = (kmax + 3) & ~3;
+  p.kpad_log2 = 2;
+  while ((1 << p.kpad_log2) < kmax) ++p.kpad_log2;
+  p.kpad = 1 << p.kpad_log2;
   const int64_t m = (int64_t)p.n_chunks * p.kpad;
   p.mcap = (int)(m < kMaxCandTile ? m : kMaxCandTile);
   p.cand_off = round_up(start, 256);
@@ -159,7 +161,7 @@ template <int D, int G, bool BF>
 void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
   k_decode<D, G, BF><<<grid, kDecodeThreads, p.sel.lds, s>>>(
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
-      p.sel.kpad, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx, a.out);
+      p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx, a.out);
 }
 
 template <int D, bool BF>
@@ -295,10 +297,10 @@ int adamas_select_topk(const uint16_t* dist, int B, int Hq, int64_t n_ctx, int h
   uint32_t* ctr = reinterpret_cast<uint32_t*>(w + kCtrlSelect);
   if (head_dim == 128)
     k_select<128><<<grid, kSelectThreads, p.lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks,
-                                                           budget, p.kpad, p.mcap, cand, ctr, idx);
+                                                           budget, p.kpad_log2, p.mcap, cand, ctr, idx);
   else
     k_select<64><<<grid, kSelectThreads, p.lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks,
-                                                          budget, p.kpad, p.mcap, cand, ctr, idx);
+                                                          budget, p.kpad_log2, p.mcap, cand, ctr, idx);
   return launch_status();
 }
 

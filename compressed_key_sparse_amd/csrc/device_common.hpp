@@ -277,6 +277,15 @@ ADM_DEV Threshold find_threshold(const uint32_t* hist, int nbins, uint32_t K, ui
   return r;
 }
 
+// d[i] for a runtime i over a small register array (select chain, no scratch).
+template <int N>
+ADM_DEV uint32_t sdist_at(const uint32_t (&d)[N], int i) {
+  uint32_t r = d[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) r = (i == k) ? d[k] : r;
+  return r;
+}
+
 // Ordered selection inside one chunk held in LDS.  Keeps every token with
 // D < t and the first `quota` tokens (lowest index) with D == t, and writes
 // them in token order as (D << 16) | token to out[]; entries [kept, pad_to)
@@ -304,24 +313,27 @@ ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint
 #pragma unroll
     for (int i = 0; i < TPT; ++i) d[i] = sdist[t0 + i];
   }
-  uint32_t lt = 0, eq = 0;
+  uint32_t ltm = 0, eqm = 0;  // bit i: token t0+i is below / at the threshold
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
-    if (t0 + i >= valid) d[i] = 0xffffu;  // masked: neither below nor at the threshold
-    lt += (int)d[i] < thr.t;
-    eq += (int)d[i] == thr.t;
+    const int di = (t0 + i < valid) ? (int)d[i] : 0xffff;  // past `valid`: neither
+    ltm |= (uint32_t)(di < thr.t) << i;
+    eqm |= (uint32_t)(di == thr.t) << i;
   }
   uint32_t tot;
-  const uint32_t mine = lt | (eq << 16);
+  const uint32_t mine = (uint32_t)__popc(ltm) | ((uint32_t)__popc(eqm) << 16);
   const uint32_t ex = block_scan_incl<NT>(mine, s_tmp, &tot) - mine;
   uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
-#pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    if ((int)d[i] < thr.t) {
-      store_shared(&out[ltb + (eqb < quota ? eqb : quota)], (d[i] << 16) | (uint32_t)(t0 + i));
+  // visit only the flagged tokens, in order (a small fraction of the chunk)
+  for (uint32_t m = ltm | eqm; m != 0; m &= m - 1) {
+    const int i = __ffs(m) - 1;
+    const uint32_t v = ((uint32_t)thr.t << 16) | (uint32_t)(t0 + i);
+    if ((ltm >> i) & 1u) {
+      const uint32_t dv = (uint32_t)(t0 + i) | (sdist_at(d, i) << 16);
+      store_shared(&out[ltb + (eqb < quota ? eqb : quota)], dv);
       ++ltb;
-    } else if ((int)d[i] == thr.t) {
-      if (eqb < quota) store_shared(&out[ltb + eqb], (d[i] << 16) | (uint32_t)(t0 + i));
+    } else {
+      if (eqb < quota) store_shared(&out[ltb + eqb], v);
       ++eqb;
     }
   }
@@ -367,14 +379,14 @@ ADM_DEV void bulk_load_shared(uint32_t* dst, const uint32_t* src, int n) {
 }
 
 // Final selection of one head from its chunk candidates.  cand[] (global,
-// written by store_shared) holds n_chunks slots of kpad entries (D << 16 | token in
+// written by store_shared) holds n_chunks slots of 2^kpad_log2 entries (D << 16 | token in
 // chunk) in token order, unused entries 0xFFFFFFFF, so the array is in global
 // token order.  Keeps the bsel smallest (D, token), writes the tokens,
 // ascending, to sidx[0..bsel) (LDS, if non-null) and idx[0..bsel) (global, if
 // non-null) followed by -1 up to budget.  Candidates pass through LDS scand[]
 // (capacity mcap) in tiles; one tile when M <= mcap.
 template <int NT>
-ADM_DEV void final_select(const uint32_t* cand, int M, int kpad, int chunk, int nbins, int bsel,
+ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk, int nbins, int bsel,
                           int budget, int32_t* sidx, int32_t* idx, uint32_t* scand, int mcap,
                           uint32_t* shist, uint32_t* s_tmp) {
   const bool resident = M <= mcap;
@@ -428,7 +440,7 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad, int chunk, int 
           ++eqb;
         }
         if (pos >= 0) {
-          const int32_t tok = ((base + j) / kpad) * chunk + (int32_t)(v & 0xffffu);
+          const int32_t tok = ((base + j) >> kpad_log2) * chunk + (int32_t)(v & 0xffffu);
           if (sidx) sidx[pos] = tok;
           if (idx) idx[pos] = tok;
         }

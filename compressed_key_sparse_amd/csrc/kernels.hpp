@@ -372,8 +372,8 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
 template <int D>
 __global__ __launch_bounds__(kSelectThreads) void k_select(
     const uint16_t* __restrict__ dist, int Hq, int64_t n_ctx, int chunk, int n_chunks,
-    int budget, int kpad, int mcap, uint32_t* __restrict__ cand, uint32_t* __restrict__ counters,
-    int32_t* __restrict__ idx) {
+    int budget, int kpad_log2, int mcap, uint32_t* __restrict__ cand,
+    uint32_t* __restrict__ counters, int32_t* __restrict__ idx) {
   constexpr int NT = kSelectThreads, NB = kNbins(D), NBP = kNbinsPadded(D);
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
@@ -396,11 +396,12 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
   }
   __syncthreads();
   const int kc = min(budget, valid);
+  const int kpad = 1 << kpad_log2;
   const Threshold thr = find_threshold<NT>(shist, NB, (uint32_t)kc, s_tmp);
   chunk_compact_any<NT>(chunk / NT, sdist, valid, thr, (uint32_t)kc - thr.lt,
                         cand + (row * n_chunks + c) * kpad, kc, kpad, s_tmp);
   if (!arrive_last<NT>(&counters[row], n_chunks, s_tmp)) return;
-  final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad, chunk, NB,
+  final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad_log2, chunk, NB,
                    (int)min((int64_t)budget, n_ctx), budget, nullptr, idx + row * budget, scand,
                    mcap, shist, s_tmp);
   if (threadIdx.x == 0) counters[row] = 0;
@@ -417,7 +418,7 @@ template <int D, int G, bool BF>
 __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
-    int n_chunks, int budget, int kpad, int mcap, int fuse_attend, float qscale,
+    int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
     void* __restrict__ out) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
@@ -437,7 +438,13 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   int32_t* sidx = reinterpret_cast<int32_t*>(s_res + PW);
   uint32_t* scand = reinterpret_cast<uint32_t*>(sidx + ((budget + 3) & ~3));
 
-  const int c = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id; rotating the
+  // chunk index with the KV head spreads every chunk offset of the code cache
+  // over all XCDs (a fixed offset per XCD loads some XCDs' memory paths more).
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int c = (lin % n_chunks + lin / n_chunks) % n_chunks;
+  const int hkv = blockIdx.y, b = blockIdx.z;
+  const int kpad = 1 << kpad_log2;
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   for (int i = threadIdx.x; i < G * NBP; i += NT) shist[i] = 0;
   for (int g = wid; g < G; g += NW) {
@@ -468,7 +475,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   const int bsel = (int)min((int64_t)budget, n_ctx);
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-    final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad, chunk, NB, bsel, budget,
+    final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad_log2, chunk, NB, bsel, budget,
                      fuse_attend ? sidx : nullptr, idx ? idx + row * budget : nullptr, scand,
                      mcap, fhist, s_tmp);
     if (fuse_attend) {
