@@ -56,11 +56,77 @@ def parse():
                     help="target oracle CPU time for the baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="print a compact summary of rocprofv3 CSV output under DIR and exit")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------- profiles
+KERNEL_SOURCES = ("compressed_key_sparse_amd/csrc/adamas.hip",
+                  "compressed_key_sparse_amd/csrc/kernels.hpp",
+                  "compressed_key_sparse_amd/csrc/device_common.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_llama2-128k_hbm_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed PMC summary, or None if
+    the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def summarize(dirpath: str):
+    """Compact text summary of rocprofv3 --stats / --pmc CSV files."""
+    import csv
+    import glob
+    from collections import defaultdict
+    for f in sorted(glob.glob(os.path.join(dirpath, "**", "*kernel_stats.csv"), recursive=True)):
+        print(f"# kernel stats ({os.path.basename(f)})")
+        print("calls  avg_us    min_us    max_us    total_%  kernel")
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Name"]
+                if "adm::" not in name and "copy" not in name.lower():
+                    continue
+                print(f"{int(r['Calls']):5d} {float(r['AverageNs'])/1e3:8.2f} "
+                      f"{float(r['MinNs'])/1e3:8.2f} {float(r['MaxNs'])/1e3:8.2f} "
+                      f"{float(r['Percentage']):8.2f}  {name[:110]}")
+    for f in sorted(glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"),
+                              recursive=True)):
+        acc = defaultdict(list)
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name", "")
+                if "adm::" not in name and "copy" not in name.lower():
+                    continue
+                acc[(name, r["Counter_Name"], r.get("Grid_Size", ""))].append(
+                    float(r["Counter_Value"]))
+        print(f"# counters ({os.path.basename(f)}): mean per dispatch")
+        print("dispatches  counter      mean_value  grid  kernel")
+        for (name, cn, grid), vals in sorted(acc.items()):
+            print(f"{len(vals):10d}  {cn:11s} {sum(vals)/len(vals):12.1f}  {grid}  {name[:100]}")
 
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path is single-GPU by design: no collectives).", file=sys.stderr)
@@ -193,7 +259,7 @@ def main():
         "eager_ms_per_step": round(eager_ms, 4),
         "roofline": {"bound": "hbm", "kernel": "adamas_decode_step (one layer)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": per_layer, "launch_us": round(launch_us, 3)},
         "needle_recall": round(recall, 4),
         "cpu_baseline": cpu,

@@ -54,22 +54,34 @@ SelectPlan plan_select(int64_t rows, int64_t n_ctx, int budget, int D, size_t st
   int c = 4096;
   while (c < 16384 && c < 8 * budget) c *= 2;
   while (c > kSelectThreads && (int64_t)(c / 2) >= n_ctx) c /= 2;
-  p.chunk = c;
-  finish_select_plan(p, rows, n_ctx, budget, start);
-  const size_t region = std::max((size_t)p.chunk * 2, (size_t)p.mcap * 4);
-  p.lds = kTmpWords * 4 + nbins_padded(D) * 4 + region;
+  for (;;) {
+    p.chunk = c;
+    finish_select_plan(p, rows, n_ctx, budget, start);
+    const size_t region = std::max((size_t)p.chunk * 2, (size_t)p.mcap * 4);
+    p.lds = kTmpWords * 4 + nbins_padded(D) * 4 + (size_t)p.kpad * 4 + region;
+    if (p.lds <= kLdsLimit || c <= kSelectThreads) break;
+    c /= 2;
+  }
   return p;
 }
 
 // Decode kernel LDS: scan phase (query words, histograms, distances) and the
 // aliasing final phase (histogram, attention partials, indices, candidates).
-size_t decode_lds_scan(int D, int G, int c) {
-  return (size_t)G * (D / 16) * 4 + (size_t)G * nbins_padded(D) * 4 + (size_t)G * c * 2;
+int cand_slot(int budget, int chunk) {
+  const int kmax = budget < chunk ? budget : chunk;
+  int k = 4;
+  while (k < kmax) k *= 2;
+  return k;
 }
-size_t decode_lds_final(int D, int budget, int mcap) {
+size_t decode_lds_scan(int D, int G, int c, int budget) {
+  return (size_t)G * (D / 16) * 4 + (size_t)G * nbins_padded(D) * 4 +
+         (size_t)cand_slot(budget, c) * 4 + (size_t)G * c * 2;
+}
+// sel_rows = min(budget, n_ctx) indices are kept in LDS only when attention is fused.
+size_t decode_lds_final(int D, int sel_rows_lds, int mcap) {
   const int nw = kDecodeThreads / kWave;
-  return nbins_padded(D) * 4 + (size_t)(nw + 1) * (2 + D) * 4 +
-         (size_t)((budget + 3) & ~3) * 4 + (size_t)mcap * 4;
+  return nbins_padded(D) * 4 + (size_t)(nw + 1) * (2 + D) * 4 + (size_t)kAttendThreads / 16 * 4 +
+         (size_t)((sel_rows_lds + 3) & ~3) * 4 + (size_t)mcap * 4;
 }
 
 struct AttendPlan {
@@ -81,13 +93,15 @@ AttendPlan plan_attend(int64_t rows, int sel_rows, int D, size_t start) {
   AttendPlan p;
   p.splits = (sel_rows + kAttendRowsPerBatch - 1) / kAttendRowsPerBatch;
   p.part_off = round_up(start, 256);
-  p.end = p.part_off + (p.splits > 1 ? (size_t)rows * p.splits * (2 + D) * sizeof(float) : 0);
+  const size_t pwp = (size_t)((2 + D + 3) & ~3);
+  p.end = p.part_off + (p.splits > 1 ? (size_t)rows * p.splits * pwp * sizeof(float) : 0);
   return p;
 }
 
 struct DecodePlan {
   SelectPlan sel;
   bool fuse = false;
+  int pf_rows = 0;
   size_t idx_off = 0;
   AttendPlan att;
   size_t total = 0;
@@ -101,19 +115,22 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D)
   const int G = Hq / Hkv;
   const int64_t rows = (int64_t)B * Hq;
   int c = 16384;
-  while (c > 1024 && kTmpWords * 4 + decode_lds_scan(D, G, c) > kLdsLimit) c /= 2;
+  while (c > 1024 && kTmpWords * 4 + decode_lds_scan(D, G, c, budget) > kLdsLimit) c /= 2;
   while (c > 1024 && (int64_t)(c / 2) >= n_ctx) c /= 2;
   p.sel.chunk = c;
   finish_select_plan(p.sel, rows, n_ctx, budget, ADAMAS_WS_CTRL_BYTES);
   const int bsel = (int)(n_ctx < budget ? n_ctx : budget);
   const int batches = G * ((bsel + kAttendRowsPerBatch - 1) / kAttendRowsPerBatch);
   p.fuse = batches <= 2;
+  // rows each chunk prefetches: 1.5x its expected share of the selection
+  p.pf_rows = G == 1 ? (3 * bsel + 2 * p.sel.n_chunks - 1) / (2 * p.sel.n_chunks) : 0;
+  const int sidx_rows = p.fuse ? bsel : 0;
   // shrink the LDS candidate tile if the final phase would not fit
   while (p.sel.mcap > 256 &&
-         kTmpWords * 4 + decode_lds_final(D, budget, p.sel.mcap) > kLdsLimit)
+         kTmpWords * 4 + decode_lds_final(D, sidx_rows, p.sel.mcap) > kLdsLimit)
     p.sel.mcap = (p.sel.mcap / 2 + 3) & ~3;
-  p.sel.lds = kTmpWords * 4 + std::max(decode_lds_scan(D, G, c),
-                                       decode_lds_final(D, budget, p.sel.mcap));
+  p.sel.lds = kTmpWords * 4 + std::max(decode_lds_scan(D, G, c, budget),
+                                       decode_lds_final(D, sidx_rows, p.sel.mcap));
   p.idx_off = round_up(p.sel.end, 256);
   const size_t idx_end = p.idx_off + (size_t)rows * budget * sizeof(int32_t);
   p.att = plan_attend(rows, bsel, D, idx_end);
@@ -161,7 +178,8 @@ template <int D, int G, bool BF>
 void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
   k_decode<D, G, BF><<<grid, kDecodeThreads, p.sel.lds, s>>>(
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
-      p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx, a.out);
+      p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, p.pf_rows, a.qscale, a.cand, a.ctr, a.idx,
+      a.out);
 }
 
 template <int D, bool BF>

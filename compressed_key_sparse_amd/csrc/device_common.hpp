@@ -58,21 +58,65 @@ ADM_DEV void load_elems(const void* base, bool is_bf16, int64_t i, float (&out)[
 }
 
 // Data handed from one workgroup to another within a launch (candidate
-// lists, attention partials) is written and read with device-scope atomic
-// stores and loads.  Those are coherent across the XCDs' separate L2 caches
-// by themselves, so the hand-off needs no L2 write-back or invalidation: the
-// writer only waits for its stores to complete before counting its arrival.
+// lists, attention partials) is written and read with device-scope coherent
+// accesses (the sc1 cache policy): they are coherent across the XCDs'
+// separate L2 caches by themselves, so the hand-off needs no L2 write-back or
+// invalidation; the writer only waits for its stores to complete before
+// counting its arrival.  Whole 16-byte rows are moved through buffer
+// instructions (a 4-byte coherent store costs a full line of write traffic).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCachePolicyCoherent = 16;       // sc1: device-scope coherence
+constexpr int kBufferDword3 = 0x00020000;      // raw 32-bit buffer (GFX9 layout)
+
+ADM_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                           kBufferDword3);
+}
+ADM_DEV void store_shared_x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, kCachePolicyCoherent);
+}
+ADM_DEV u32x4 load_shared_x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCachePolicyCoherent);
+}
 ADM_DEV void store_shared(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-ADM_DEV uint32_t load_shared(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// Copy n u32 (n % 4 == 0) between LDS and a coherent global buffer (16-byte
+// rows; the global side is 16-byte aligned).
+template <int NT>
+ADM_DEV void lds_to_shared(uint32_t* dst_global, const uint32_t* src_lds, int n) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(dst_global, (uint32_t)n * 4u);
+  for (int i = threadIdx.x; i < n / 4; i += NT) {
+    const uint4 v = reinterpret_cast<const uint4*>(src_lds)[i];
+    store_shared_x4(r, (uint32_t)i * 16u, u32x4{v.x, v.y, v.z, v.w});
+  }
 }
-ADM_DEV void store_shared_f32(float* p, float v) {
-  store_shared(reinterpret_cast<uint32_t*>(p), __float_as_uint(v));
-}
-ADM_DEV float load_shared_f32(const float* p) {
-  return __uint_as_float(load_shared(reinterpret_cast<const uint32_t*>(p)));
+
+// Copy n u32 (n % 4 == 0) written by other workgroups of this launch into LDS,
+// up to 8 outstanding 16-byte coherent loads per thread.  The barrier between
+// the loads and the LDS stores keeps the compiler from sinking each load into
+// its store (which would serialize them).  One barrier per 32*NT elements.
+template <int NT>
+ADM_DEV void shared_to_lds(uint32_t* dst_lds, const uint32_t* src_global, int n) {
+  constexpr int UL = 8;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src_global, (uint32_t)n * 4u);
+  const int n4 = n / 4;
+  for (int base = 0; base < n4; base += NT * UL) {
+    u32x4 v[UL];
+#pragma unroll
+    for (int j = 0; j < UL; ++j) {
+      const int i = base + j * NT + (int)threadIdx.x;
+      if (base + j * NT < n4) v[j] = load_shared_x4(r, (uint32_t)i * 16u);  // past n: reads 0
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < UL; ++j) {
+      const int i = base + j * NT + (int)threadIdx.x;
+      if (base + j * NT < n4 && i < n4)
+        reinterpret_cast<uint4*>(dst_lds)[i] = make_uint4(v[j].x, v[j].y, v[j].z, v[j].w);
+    }
+  }
 }
 
 // Streaming 16-byte load that is not expected to be reused (non-temporal).
@@ -245,80 +289,86 @@ ADM_DEV uint32_t block_scan_incl(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
 // ------------------------------------------------------------------ §5.2
 // Threshold of a budget over a distance histogram: the smallest t with
 // count(D <= t) >= K, and lt = count(D < t).  Requires 1 <= K <= total count.
+// Wavefront 0 does the search (one DPP scan over 64 lanes of consecutive
+// bins); the result reaches every thread through LDS after one barrier.
+// Two budgets K0, K1 are searched in the same pass (pass K1 = K0 for one).
 struct Threshold {
   int t;
   uint32_t lt;
 };
-template <int NT>
-ADM_DEV Threshold find_threshold(const uint32_t* hist, int nbins, uint32_t K, uint32_t* s_tmp) {
-  const int bpt = (nbins + NT - 1) / NT;
-  const int b0 = threadIdx.x * bpt;
-  uint32_t sum = 0;
-  for (int i = 0; i < bpt; ++i)
-    if (b0 + i < nbins) sum += hist[b0 + i];
-  uint32_t tot;
-  const uint32_t incl = block_scan_incl<NT>(sum, s_tmp, &tot);
-  const uint32_t excl = incl - sum;
-  if (excl < K && K <= incl) {
-    uint32_t c = excl;
-    for (int i = 0; i < bpt; ++i) {
-      const uint32_t h = hist[b0 + i];
-      if (c + h >= K) {
-        s_tmp[kTmpThrT] = (uint32_t)(b0 + i);
-        s_tmp[kTmpThrLt] = c;
-        break;
+constexpr int kTmpThr1T = 18, kTmpThr1Lt = 19;
+
+ADM_DEV void find_threshold_pair(const uint32_t* hist, int nbins, uint32_t K0, uint32_t K1,
+                                 uint32_t* s_tmp, Threshold* r0, Threshold* r1) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int bpl = (nbins + kWave - 1) / kWave;
+    const int b0 = lane * bpl;
+    uint32_t sum = 0;
+    for (int i = 0; i < bpl; ++i)
+      if (b0 + i < nbins) sum += hist[b0 + i];
+    const uint32_t incl = wave_scan_incl(sum);
+    const uint32_t excl = incl - sum;
+    const uint32_t Ks[2] = {K0, K1};
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t K = Ks[w];
+      if (excl < K && K <= incl) {
+        uint32_t c = excl;
+        for (int i = 0; i < bpl; ++i) {
+          const uint32_t h = hist[b0 + i];
+          if (c + h >= K) {
+            s_tmp[w ? kTmpThr1T : kTmpThrT] = (uint32_t)(b0 + i);
+            s_tmp[w ? kTmpThr1Lt : kTmpThrLt] = c;
+            break;
+          }
+          c += h;
+        }
       }
-      c += h;
     }
   }
   __syncthreads();
-  Threshold r{(int)s_tmp[kTmpThrT], s_tmp[kTmpThrLt]};
+  *r0 = Threshold{(int)s_tmp[kTmpThrT], s_tmp[kTmpThrLt]};
+  *r1 = Threshold{(int)s_tmp[kTmpThr1T], s_tmp[kTmpThr1Lt]};
   __syncthreads();
-  return r;
 }
 
-// d[i] for a runtime i over a small register array (select chain, no scratch).
-template <int N>
-ADM_DEV uint32_t sdist_at(const uint32_t (&d)[N], int i) {
-  uint32_t r = d[0];
-#pragma unroll
-  for (int k = 1; k < N; ++k) r = (i == k) ? d[k] : r;
-  return r;
+template <int NT>
+ADM_DEV Threshold find_threshold(const uint32_t* hist, int nbins, uint32_t K, uint32_t* s_tmp) {
+  Threshold a, b;
+  find_threshold_pair(hist, nbins, K, K, s_tmp, &a, &b);
+  return a;
 }
 
 // Ordered selection inside one chunk held in LDS.  Keeps every token with
 // D < t and the first `quota` tokens (lowest index) with D == t, and writes
-// them in token order as (D << 16) | token to out[]; entries [kept, pad_to)
-// of out[] get the sentinel 0xFFFFFFFF.  Token i is kept at position
-// (#lt before i) + min(#eq before i, quota).  Thread j owns tokens
-// [j*TPT, (j+1)*TPT), read once with 16-byte LDS loads (TPT in {1,2,4,8,16};
-// distances past `valid` must be >= 3*D+1 or never read: they are masked).
-template <int NT, int TPT>
+// them in token order as (D << 16) | token to out[] (LDS); entries
+// [kept, pad_to) of out[] get the sentinel 0xFFFFFFFF.  Token i is kept at
+// position (#lt before i) + min(#eq before i, quota).  Thread j owns tokens
+// [16j, 16j+16), read once with 16-byte LDS loads (threads past the chunk
+// own nothing).  on_kept(token, D) is called for every kept token.
+constexpr int kCompactTpt = 16;
+template <int NT, class OnKept>
 ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint32_t quota,
-                           uint32_t* out, int kept, int pad_to, uint32_t* s_tmp) {
+                           uint32_t* out, int kept, int pad_to, uint32_t* s_tmp,
+                           OnKept&& on_kept) {
+  constexpr int TPT = kCompactTpt;
   const int t0 = threadIdx.x * TPT;
-  uint32_t d[TPT];
-  if constexpr (TPT >= 8) {
+  uint32_t ltm = 0, eqm = 0;  // bit i: token t0+i is below / at the threshold
+  if (t0 < valid) {
 #pragma unroll
     for (int v8 = 0; v8 < TPT / 8; ++v8) {
       const uint4 w = *reinterpret_cast<const uint4*>(sdist + t0 + 8 * v8);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        d[8 * v8 + 2 * i] = ws[i] & 0xffffu;
-        d[8 * v8 + 2 * i + 1] = ws[i] >> 16;
+      for (int i = 0; i < 8; ++i) {
+        const int k = 8 * v8 + i;
+        const int di = (t0 + k < valid) ? (int)((ws[i >> 1] >> (16 * (i & 1))) & 0xffffu)
+                                        : 0xffff;  // past `valid`: neither
+        ltm |= (uint32_t)(di < thr.t) << k;
+        eqm |= (uint32_t)(di == thr.t) << k;
       }
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) d[i] = sdist[t0 + i];
-  }
-  uint32_t ltm = 0, eqm = 0;  // bit i: token t0+i is below / at the threshold
-#pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int di = (t0 + i < valid) ? (int)d[i] : 0xffff;  // past `valid`: neither
-    ltm |= (uint32_t)(di < thr.t) << i;
-    eqm |= (uint32_t)(di == thr.t) << i;
   }
   uint32_t tot;
   const uint32_t mine = (uint32_t)__popc(ltm) | ((uint32_t)__popc(eqm) << 16);
@@ -327,59 +377,25 @@ ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint
   // visit only the flagged tokens, in order (a small fraction of the chunk)
   for (uint32_t m = ltm | eqm; m != 0; m &= m - 1) {
     const int i = __ffs(m) - 1;
-    const uint32_t v = ((uint32_t)thr.t << 16) | (uint32_t)(t0 + i);
+    const uint32_t t = (uint32_t)(t0 + i);
     if ((ltm >> i) & 1u) {
-      const uint32_t dv = (uint32_t)(t0 + i) | (sdist_at(d, i) << 16);
-      store_shared(&out[ltb + (eqb < quota ? eqb : quota)], dv);
+      const uint32_t d = sdist[t];
+      out[ltb + (eqb < quota ? eqb : quota)] = (d << 16) | t;
+      on_kept(t, d);
       ++ltb;
     } else {
-      if (eqb < quota) store_shared(&out[ltb + eqb], v);
+      if (eqb < quota) {
+        out[ltb + eqb] = ((uint32_t)thr.t << 16) | t;
+        on_kept(t, (uint32_t)thr.t);
+      }
       ++eqb;
     }
   }
-  for (int j = kept + (int)threadIdx.x; j < pad_to; j += NT) store_shared(&out[j], 0xFFFFFFFFu);
-}
-
-// Dispatch on tokens per thread (chunk / NT, a power of two up to 16).
-template <int NT>
-ADM_DEV void chunk_compact_any(int tpt, const uint16_t* sdist, int valid, Threshold thr,
-                               uint32_t quota, uint32_t* out, int kept, int pad_to,
-                               uint32_t* s_tmp) {
-  switch (tpt) {
-    case 1: chunk_compact<NT, 1>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
-    case 2: chunk_compact<NT, 2>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
-    case 4: chunk_compact<NT, 4>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
-    case 8: chunk_compact<NT, 8>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
-    default: chunk_compact<NT, 16>(sdist, valid, thr, quota, out, kept, pad_to, s_tmp); break;
-  }
-}
-
-// Copy n u32 written by other workgroups of this launch from global memory
-// to LDS, with up to 16 outstanding coherent loads per thread.  The barrier
-// between the loads and the LDS stores keeps the compiler from sinking each
-// load into its store (which would serialize them).  Contains one barrier per
-// 16*NT elements.
-template <int NT>
-ADM_DEV void bulk_load_shared(uint32_t* dst, const uint32_t* src, int n) {
-  constexpr int UL = 16;
-  for (int base = 0; base < n; base += NT * UL) {
-    uint32_t r[UL];
-#pragma unroll
-    for (int j = 0; j < UL; ++j) {
-      const int i = base + j * NT + (int)threadIdx.x;
-      if (base + j * NT < n) r[j] = load_shared(src + (i < n ? i : n - 1));
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < UL; ++j) {
-      const int i = base + j * NT + (int)threadIdx.x;
-      if (base + j * NT < n && i < n) dst[i] = r[j];
-    }
-  }
+  for (int j = kept + (int)threadIdx.x; j < pad_to; j += NT) out[j] = 0xFFFFFFFFu;
 }
 
 // Final selection of one head from its chunk candidates.  cand[] (global,
-// written by store_shared) holds n_chunks slots of 2^kpad_log2 entries (D << 16 | token in
+// written by lds_to_shared) holds n_chunks slots of 2^kpad_log2 entries (D << 16 | token in
 // chunk) in token order, unused entries 0xFFFFFFFF, so the array is in global
 // token order.  Keeps the bsel smallest (D, token), writes the tokens,
 // ascending, to sidx[0..bsel) (LDS, if non-null) and idx[0..bsel) (global, if
@@ -394,7 +410,7 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
   for (int base = 0; base < M; base += mcap) {
     const int n = min(mcap, M - base);
     __syncthreads();
-    bulk_load_shared<NT>(scand, cand + base, n);
+    shared_to_lds<NT>(scand, cand + base, n);
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += NT) {
       const uint32_t d = scand[i] >> 16;
@@ -409,7 +425,7 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
     const int n = min(mcap, M - base);
     if (!resident) {
       __syncthreads();
-      bulk_load_shared<NT>(scand, cand + base, n);
+      shared_to_lds<NT>(scand, cand + base, n);
       __syncthreads();
     }
     const int tpt = (n + NT - 1) / NT;

@@ -201,24 +201,44 @@ struct RowRaw {
   }
 };
 
+// Dot product of one lane's q and k slices (EL elements): bf16 pairs go
+// through the packed bf16 dot instruction (exact products, binary32 sums).
+template <int D, bool BF>
+ADM_DEV float slice_dot(const RowRaw<D, BF>& q, const RowRaw<D, BF>& k) {
+  float acc = 0.0f;
+  if constexpr (BF) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < RowRaw<D, BF>::WORDS; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q.w[i]),
+                                            __builtin_bit_cast(bf2, k.w[i]), acc, false);
+  } else {
+#pragma unroll
+    for (int e = 0; e < RowRaw<D, BF>::EL; ++e) acc += q.at(e) * k.at(e);
+  }
+  return acc;
+}
+
+// Gather attention over nrows selected rows of one head.  Rows go in
+// batches of NS*RB (a 16-lane slot holds RB rows' K and V, every lane D/16
+// dimensions).  Per batch: scores (log2 domain) to LDS, one batch maximum,
+// then weights and the weighted V sum without per-row rescaling; batches
+// merge by log-sum-exp.  On return s_res[0] = m, s_res[1] = l,
+// s_res[2 + t] = o_t.  s_part holds NW*(2+D) floats plus NS*RB scores.
 template <int D, bool BF, int NT>
 ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
                          const void* __restrict__ v, int64_t qoff, int64_t kvrow0, int64_t cap,
                          const int32_t* rows, int nrows, float qscale, float* s_part,
                          float* s_res) {
+  constexpr int EL = D / 16, NS = NT / 16, NW = NT / kWave, PW = 2 + D;
   // fp32 rows are twice the bytes: half the rows per batch keeps registers in budget
-  constexpr int EL = D / 16, NS = NT / 16, NW = NT / kWave;
   constexpr int RB = BF ? kAttendRowsPerSlot : kAttendRowsPerSlot / 2;
   const int l16 = threadIdx.x & 15, slot = threadIdx.x >> 4;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-  float qv[EL];
-  {
-    RowRaw<D, BF> qr;
-    qr.load(q, qoff + l16 * EL);
-#pragma unroll
-    for (int e = 0; e < EL; ++e) qv[e] = qr.at(e) * qscale;
-  }
-  Softmax st{-INFINITY, 0.0f};
+  float* s_score = s_part + NW * PW;  // NS*RB scores of the current batch
+  RowRaw<D, BF> qr;
+  qr.load(q, qoff + l16 * EL);
+  float m_run = -INFINITY, l_run = 0.0f;
   float o[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) o[e] = 0.0f;
@@ -238,58 +258,58 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
       kr[j].load(k, r * D + l16 * EL);
       vr[j].load(v, r * D + l16 * EL);
     }
+    float sc[RB];
+    float mloc = -INFINITY;
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
-      if (tok[j] >= 0) {  // uniform across the 16 lanes of a slot
-        float dot = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EL; ++e) dot += qv[e] * kr[j].at(e);
-        dot = row16_sum(dot);
-        const float M = fmaxf(st.m, dot);
-        const float corr = (st.m == -INFINITY) ? 0.0f : exp2f(st.m - M);
-        const float p = exp2f(dot - M);
-        st.l = st.l * corr + p;
-#pragma unroll
-        for (int e = 0; e < EL; ++e) o[e] = o[e] * corr + p * vr[j].at(e);
-        st.m = M;
-      }
+      sc[j] = row16_sum(slice_dot<D, BF>(qr, kr[j])) * qscale;
+      if (tok[j] < 0) sc[j] = -INFINITY;
+      mloc = fmaxf(mloc, sc[j]);
     }
+    // batch maximum: slot maxima through LDS, reduced by every thread
+    if (l16 == 0) s_score[slot] = mloc;
+    __syncthreads();
+    float mb = -INFINITY;
+    for (int i = 0; i < NS; ++i) mb = fmaxf(mb, s_score[i]);
+    __syncthreads();
+    if (mb == -INFINITY) continue;  // nothing valid in this batch (uniform)
+    const float mn = fmaxf(m_run, mb);
+    const float corr = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - mn);
+    l_run *= corr;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) o[e] *= corr;
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const float p = (tok[j] >= 0) ? exp2f(sc[j] - mn) : 0.0f;
+      l_run += p;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) o[e] += p * vr[j].at(e);
+    }
+    m_run = mn;
   }
-  // merge the four slots of each wavefront (lanes ^16, ^32), then the waves
+  // every slot shares m_run: sum l and o over slots (lanes ^16, ^32), then waves
 #pragma unroll
   for (int m = 16; m < kWave; m <<= 1) {
-    Softmax other{__shfl_xor(st.m, m), __shfl_xor(st.l, m)};
-    float oo[EL];
+    l_run += __shfl_xor(l_run, m);
 #pragma unroll
-    for (int e = 0; e < EL; ++e) oo[e] = __shfl_xor(o[e], m);
-    merge_partial<EL>(st, o, other, oo);
+    for (int e = 0; e < EL; ++e) o[e] += __shfl_xor(o[e], m);
   }
-  float* mine = s_part + wid * (2 + D);
+  float* mine = s_part + wid * PW;
   if (lane < 16) {
-    if (lane == 0) {
-      mine[0] = st.m;
-      mine[1] = st.l;
-    }
+    if (lane == 0) mine[1] = l_run;
 #pragma unroll
     for (int e = 0; e < EL; ++e) mine[2 + l16 * EL + e] = o[e];
   }
   __syncthreads();
   if (threadIdx.x < D) {
-    const int dd = threadIdx.x;
-    float M = -INFINITY;
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_part[w * (2 + D)]);
     float L = 0.0f, O = 0.0f;
-    if (M != -INFINITY) {
-      for (int w = 0; w < NW; ++w) {
-        const float mw = s_part[w * (2 + D)];
-        const float a = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-        L += s_part[w * (2 + D) + 1] * a;
-        O += s_part[w * (2 + D) + 2 + dd] * a;
-      }
+    for (int w = 0; w < NW; ++w) {
+      L += s_part[w * PW + 1];
+      O += s_part[w * PW + 2 + threadIdx.x];
     }
-    s_res[2 + dd] = O;
-    if (dd == 0) {
-      s_res[0] = M;
+    s_res[2 + threadIdx.x] = O;
+    if (threadIdx.x == 0) {
+      s_res[0] = m_run;
       s_res[1] = L;
     }
   }
@@ -314,11 +334,12 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
     const int32_t* __restrict__ idx, int Hq, int Hkv, int64_t cap, int budget, float qscale,
     float* __restrict__ part, uint32_t* __restrict__ counters, void* __restrict__ out) {
   constexpr int NT = kAttendThreads, NW = NT / kWave, PW = 2 + D;
+  constexpr int PWP = (PW + 3) & ~3;  // partial rows padded to 16 bytes
   constexpr int kMergeTile = 32;
   __shared__ uint32_t s_tmp[kTmpWords];
-  __shared__ float s_part[NW * PW];
-  __shared__ float s_res[PW];
-  __shared__ float s_tile[kMergeTile * PW];
+  __shared__ float s_part[NW * PW + kAttendRowsPerBatch];
+  __shared__ __align__(16) float s_res[PWP];
+  __shared__ __align__(16) float s_tile[kMergeTile * PWP];
   const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, S = gridDim.x;
   const int G = Hq / Hkv;
   const int64_t row = (int64_t)b * Hq + hq;
@@ -334,26 +355,27 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
     }
     return;
   }
-  float* mine = part + (row * S + s) * PW;
-  for (int i = threadIdx.x; i < PW; i += NT) store_shared_f32(&mine[i], s_res[i]);
+  float* mine = part + (row * S + s) * PWP;
+  lds_to_shared<NT>(reinterpret_cast<uint32_t*>(mine), reinterpret_cast<const uint32_t*>(s_res),
+                    PWP);
   if (!arrive_last<NT>(&counters[row], S, s_tmp)) return;
-  const float* ps = part + row * S * PW;
+  const float* ps = part + row * S * PWP;
   float M = -INFINITY, L = 0.0f, O = 0.0f;
   for (int t0 = 0; t0 < S; t0 += kMergeTile) {
     const int nt = min(kMergeTile, S - t0);
     __syncthreads();
-    bulk_load_shared<NT>(reinterpret_cast<uint32_t*>(s_tile),
-                         reinterpret_cast<const uint32_t*>(ps + t0 * PW), nt * PW);
+    shared_to_lds<NT>(reinterpret_cast<uint32_t*>(s_tile),
+                      reinterpret_cast<const uint32_t*>(ps + t0 * PWP), nt * PWP);
     __syncthreads();
     if (threadIdx.x < D) {
       for (int i = 0; i < nt; ++i) {
-        const float mi = s_tile[i * PW];
+        const float mi = s_tile[i * PWP];
         if (mi == -INFINITY) continue;
         const float Mn = fmaxf(M, mi);
         const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
         const float bb = exp2f(mi - Mn);
-        L = L * a + s_tile[i * PW + 1] * bb;
-        O = O * a + s_tile[i * PW + 2 + threadIdx.x] * bb;
+        L = L * a + s_tile[i * PWP + 1] * bb;
+        O = O * a + s_tile[i * PWP + 2 + threadIdx.x] * bb;
         M = Mn;
       }
     }
@@ -378,7 +400,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
   uint32_t* shist = s_tmp + kTmpWords;
-  uint8_t* region = reinterpret_cast<uint8_t*>(shist + NBP);
+  uint32_t* sstage = shist + NBP;                           // chunk candidates
+  uint8_t* region = reinterpret_cast<uint8_t*>(sstage + (1 << kpad_log2));
   uint16_t* sdist = reinterpret_cast<uint16_t*>(region);   // phase 1
   uint32_t* scand = reinterpret_cast<uint32_t*>(region);   // phase 2
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
@@ -398,8 +421,10 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
   const int kc = min(budget, valid);
   const int kpad = 1 << kpad_log2;
   const Threshold thr = find_threshold<NT>(shist, NB, (uint32_t)kc, s_tmp);
-  chunk_compact_any<NT>(chunk / NT, sdist, valid, thr, (uint32_t)kc - thr.lt,
-                        cand + (row * n_chunks + c) * kpad, kc, kpad, s_tmp);
+  chunk_compact<NT>(sdist, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad, s_tmp,
+                    [](uint32_t, uint32_t) {});
+  __syncthreads();
+  lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
   if (!arrive_last<NT>(&counters[row], n_chunks, s_tmp)) return;
   final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad_log2, chunk, NB,
                    (int)min((int64_t)budget, n_ctx), budget, nullptr, idx + row * budget, scand,
@@ -418,7 +443,7 @@ template <int D, int G, bool BF>
 __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
-    int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,
+    int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, int pf_rows, float qscale,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
     void* __restrict__ out) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
@@ -430,13 +455,15 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   // phase 1 (scan) layout
   uint32_t* sq = reinterpret_cast<uint32_t*>(region);
   uint32_t* shist = sq + G * W;
-  uint16_t* sdist = reinterpret_cast<uint16_t*>(shist + G * NBP);
+  uint32_t* sstage = shist + G * NBP;  // one head's chunk candidates
+  uint16_t* sdist = reinterpret_cast<uint16_t*>(sstage + (1 << kpad_log2));
   // phase 2 (final selection + attention) layout, aliasing phase 1
   uint32_t* fhist = reinterpret_cast<uint32_t*>(region);
   float* s_part = reinterpret_cast<float*>(fhist + NBP);
-  float* s_res = s_part + NW * PW;
-  int32_t* sidx = reinterpret_cast<int32_t*>(s_res + PW);
-  uint32_t* scand = reinterpret_cast<uint32_t*>(sidx + ((budget + 3) & ~3));
+  float* s_res = s_part + NW * PW + NT / 16;  // after attend_rows' per-slot scratch
+  int32_t* sidx = reinterpret_cast<int32_t*>(s_res + PW);  // fused attention only
+  const int bsel = (int)min((int64_t)budget, n_ctx);
+  uint32_t* scand = reinterpret_cast<uint32_t*>(sidx + (fuse_attend ? ((bsel + 3) & ~3) : 0));
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id; rotating the
   // chunk index with the KV head spreads every chunk offset of the code cache
@@ -465,14 +492,44 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   });
   __syncthreads();
   const int kc = min(budget, valid);
+  Threshold thr_pf{-1, 0};
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-    const Threshold thr = find_threshold<NT>(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
-    chunk_compact_any<NT>(chunk / NT, sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt,
-                          cand + (row * n_chunks + c) * kpad, kc, kpad, s_tmp);
+    Threshold thr;
+    find_threshold_pair(shist + g * NBP, NB, (uint32_t)kc,
+                        (uint32_t)max(1, min(kc, pf_rows)), s_tmp, &thr, &thr_pf);
+    chunk_compact<NT>(sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad,
+                      s_tmp, [](uint32_t, uint32_t) {});
+    __syncthreads();
+    lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
   }
-  if (!arrive_last<NT>(&counters[b * Hkv + hkv], n_chunks, s_tmp)) return;
-  const int bsel = (int)min((int64_t)budget, n_ctx);
+  const bool last = arrive_last<NT>(&counters[b * Hkv + hkv], n_chunks, s_tmp);
+  // Speculative prefetch (single query head per KV head): touch the K/V rows
+  // of this chunk's best candidates, which are likely to survive the final
+  // selection, so the selecting workgroup's gather finds them in the device
+  // cache.  Issued after the arrival so that no wait delays the count.
+  uint32_t pf_acc = 0;
+  if (G == 1 && pf_rows > 0) {
+    const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap + t0;
+    constexpr int kRowBytes = D * (BF ? 2 : 4);
+    for (int j = threadIdx.x; j < kc; j += NT) {
+      const uint32_t e = sstage[j];
+      if ((int)(e >> 16) <= thr_pf.t) {
+        const int64_t r = kvrow0 + (e & 0xffffu);
+        const uint8_t* kr = static_cast<const uint8_t*>(k) + r * kRowBytes;
+        const uint8_t* vr = static_cast<const uint8_t*>(v) + r * kRowBytes;
+#pragma unroll
+        for (int off = 0; off < kRowBytes; off += 128)
+          pf_acc ^= *reinterpret_cast<const uint32_t*>(kr + off) ^
+                    *reinterpret_cast<const uint32_t*>(vr + off);
+      }
+    }
+  }
+  if (!last) {
+    asm volatile("" ::"v"(pf_acc));  // keep the prefetch loads
+    return;
+  }
+  __syncthreads();  // sstage (phase-1 LDS) is reused by the final phase below
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
     final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad_log2, chunk, NB, bsel, budget,
@@ -489,6 +546,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     }
   }
   if (threadIdx.x == 0) counters[b * Hkv + hkv] = 0;
+  asm volatile("" ::"v"(pf_acc));
 }
 
 }  // namespace adm

@@ -176,7 +176,8 @@ def test_decode_tiny_config(ora):
 
 
 @pytest.mark.parametrize("n,budget", [(1, 64), (63, 64), (64, 64), (700, 64), (5000, 256),
-                                      (20000, 1024), (4096, 2048)])
+                                      (20000, 1024), (4096, 2048), (30000, 20000),
+                                      (70000, 512), (1000, 100000)])
 def test_decode_small_mha(ora, n, budget):
     log(f"decode small MHA n={n} budget={budget}")
     w = synth.LLAMA2_32K.replace(hq=4, hkv=4, n_ctx=n, cap=n + 100, budget=budget)
