@@ -101,7 +101,6 @@ AttendPlan plan_attend(int64_t rows, int sel_rows, int D, size_t start) {
 struct DecodePlan {
   SelectPlan sel;
   bool fuse = false;
-  int pf_rows = 0;
   size_t idx_off = 0;
   AttendPlan att;
   size_t total = 0;
@@ -122,8 +121,6 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D)
   const int bsel = (int)(n_ctx < budget ? n_ctx : budget);
   const int batches = G * ((bsel + kAttendRowsPerBatch - 1) / kAttendRowsPerBatch);
   p.fuse = batches <= 2;
-  // rows each chunk prefetches: 1.5x its expected share of the selection
-  p.pf_rows = G == 1 ? (3 * bsel + 2 * p.sel.n_chunks - 1) / (2 * p.sel.n_chunks) : 0;
   const int sidx_rows = p.fuse ? bsel : 0;
   // shrink the LDS candidate tile if the final phase would not fit
   while (p.sel.mcap > 256 &&
@@ -178,7 +175,7 @@ template <int D, int G, bool BF>
 void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
   k_decode<D, G, BF><<<grid, kDecodeThreads, p.sel.lds, s>>>(
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
-      p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, p.pf_rows, a.qscale, a.cand, a.ctr, a.idx,
+      p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
       a.out);
 }
 

@@ -443,7 +443,7 @@ template <int D, int G, bool BF>
 __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
-    int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, int pf_rows, float qscale,
+    int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
     void* __restrict__ out) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
@@ -492,44 +492,15 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   });
   __syncthreads();
   const int kc = min(budget, valid);
-  Threshold thr_pf{-1, 0};
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-    Threshold thr;
-    find_threshold_pair(shist + g * NBP, NB, (uint32_t)kc,
-                        (uint32_t)max(1, min(kc, pf_rows)), s_tmp, &thr, &thr_pf);
+    const Threshold thr = find_threshold<NT>(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
     chunk_compact<NT>(sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad,
                       s_tmp, [](uint32_t, uint32_t) {});
     __syncthreads();
     lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
   }
-  const bool last = arrive_last<NT>(&counters[b * Hkv + hkv], n_chunks, s_tmp);
-  // Speculative prefetch (single query head per KV head): touch the K/V rows
-  // of this chunk's best candidates, which are likely to survive the final
-  // selection, so the selecting workgroup's gather finds them in the device
-  // cache.  Issued after the arrival so that no wait delays the count.
-  uint32_t pf_acc = 0;
-  if (G == 1 && pf_rows > 0) {
-    const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap + t0;
-    constexpr int kRowBytes = D * (BF ? 2 : 4);
-    for (int j = threadIdx.x; j < kc; j += NT) {
-      const uint32_t e = sstage[j];
-      if ((int)(e >> 16) <= thr_pf.t) {
-        const int64_t r = kvrow0 + (e & 0xffffu);
-        const uint8_t* kr = static_cast<const uint8_t*>(k) + r * kRowBytes;
-        const uint8_t* vr = static_cast<const uint8_t*>(v) + r * kRowBytes;
-#pragma unroll
-        for (int off = 0; off < kRowBytes; off += 128)
-          pf_acc ^= *reinterpret_cast<const uint32_t*>(kr + off) ^
-                    *reinterpret_cast<const uint32_t*>(vr + off);
-      }
-    }
-  }
-  if (!last) {
-    asm volatile("" ::"v"(pf_acc));  // keep the prefetch loads
-    return;
-  }
-  __syncthreads();  // sstage (phase-1 LDS) is reused by the final phase below
+  if (!arrive_last<NT>(&counters[b * Hkv + hkv], n_chunks, s_tmp)) return;
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
     final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad_log2, chunk, NB, bsel, budget,
@@ -546,7 +517,6 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     }
   }
   if (threadIdx.x == 0) counters[b * Hkv + hkv] = 0;
-  asm volatile("" ::"v"(pf_acc));
 }
 
 }  // namespace adm
