@@ -333,11 +333,30 @@ ADM_DEV void find_threshold_pair(const uint32_t* hist, int nbins, uint32_t K0, u
   __syncthreads();
 }
 
+// One bin per thread (nbins <= NT): DPP scan inside each wavefront, then the
+// wavefront totals through LDS; the thread whose bin crosses K publishes it.
 template <int NT>
 ADM_DEV Threshold find_threshold(const uint32_t* hist, int nbins, uint32_t K, uint32_t* s_tmp) {
-  Threshold a, b;
-  find_threshold_pair(hist, nbins, K, K, s_tmp, &a, &b);
-  return a;
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  const int nwb = (nbins + kWave - 1) / kWave;  // wavefronts that hold bins
+  const uint32_t h = (int)threadIdx.x < nbins ? hist[threadIdx.x] : 0u;
+  const uint32_t incl_w = wave_scan_incl(h);
+  if (lane == kWave - 1 && wid < nwb) s_tmp[kTmpWaveSums + wid] = incl_w;
+  __syncthreads();
+  if (wid < nwb) {
+    uint32_t pre = 0;
+    for (int w = 0; w < wid; ++w) pre += s_tmp[kTmpWaveSums + w];
+    const uint32_t incl = pre + incl_w, excl = incl - h;
+    if (excl < K && K <= incl) {
+      s_tmp[kTmpThrT] = threadIdx.x;
+      s_tmp[kTmpThrLt] = excl;
+    }
+  }
+  __syncthreads();
+  const Threshold r{(int)s_tmp[kTmpThrT], s_tmp[kTmpThrLt]};
+  static_assert(NW <= 16, "wave sums live in s_tmp[0..16)");
+  return r;
 }
 
 // Ordered selection inside one chunk held in LDS.  Keeps every token with
@@ -356,19 +375,30 @@ ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint
   const int t0 = threadIdx.x * TPT;
   uint32_t ltm = 0, eqm = 0;  // bit i: token t0+i is below / at the threshold
   if (t0 < valid) {
+    // two distances per 32-bit word (both <= 3*D < 2^15): with packed 16-bit
+    // subtractions, bit 15 of (t-1-d) is set iff d >= t and of (t-d) iff d > t
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 tm1 = {(short)(thr.t - 1), (short)(thr.t - 1)};
+    const s16x2 tt = {(short)thr.t, (short)thr.t};
+    uint32_t ge = 0, gt = 0;
 #pragma unroll
     for (int v8 = 0; v8 < TPT / 8; ++v8) {
       const uint4 w = *reinterpret_cast<const uint4*>(sdist + t0 + 8 * v8);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = 8 * v8 + i;
-        const int di = (t0 + k < valid) ? (int)((ws[i >> 1] >> (16 * (i & 1))) & 0xffffu)
-                                        : 0xffff;  // past `valid`: neither
-        ltm |= (uint32_t)(di < thr.t) << k;
-        eqm |= (uint32_t)(di == thr.t) << k;
+      for (int i = 0; i < 4; ++i) {
+        const s16x2 dv = __builtin_bit_cast(s16x2, ws[i]);
+        const uint32_t a = __builtin_bit_cast(uint32_t, (s16x2)(tm1 - dv));
+        const uint32_t b = __builtin_bit_cast(uint32_t, (s16x2)(tt - dv));
+        const int k = 8 * v8 + 2 * i;
+        ge |= (((a >> 15) & 1u) | ((a >> 30) & 2u)) << k;
+        gt |= (((b >> 15) & 1u) | ((b >> 30) & 2u)) << k;
       }
     }
+    const int nv = valid - t0;  // tokens of this thread inside the chunk
+    const uint32_t vmask = nv >= TPT ? 0xffffu : ((1u << nv) - 1u);
+    ltm = ~ge & vmask;
+    eqm = ge & ~gt & vmask;
   }
   uint32_t tot;
   const uint32_t mine = (uint32_t)__popc(ltm) | ((uint32_t)__popc(eqm) << 16);
@@ -402,9 +432,74 @@ ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint
 // non-null) followed by -1 up to budget.  Candidates pass through LDS scand[]
 // (capacity mcap) in tiles; one tile when M <= mcap.
 template <int NT>
+ADM_DEV void final_select_tiled(const uint32_t* cand, int M, int kpad_log2, int chunk, int nbins,
+                                int bsel, int budget, int32_t* sidx, int32_t* idx,
+                                uint32_t* scand, int mcap, uint32_t* shist, uint32_t* s_tmp);
+
+// Up to 4*NT candidates: each thread keeps four consecutive entries in
+// registers from one 16-byte coherent load; histogram, threshold and ordered
+// compaction run on them directly.
+template <int NT>
 ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk, int nbins, int bsel,
                           int budget, int32_t* sidx, int32_t* idx, uint32_t* scand, int mcap,
                           uint32_t* shist, uint32_t* s_tmp) {
+  if (M > 4 * NT) {
+    final_select_tiled<NT>(cand, M, kpad_log2, chunk, nbins, bsel, budget, sidx, idx, scand,
+                           mcap, shist, s_tmp);
+    return;
+  }
+  const int i0 = 4 * (int)threadIdx.x;
+  u32x4 e = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  if (i0 < M) e = load_shared_x4(make_rsrc(cand, (uint32_t)M * 4u), (uint32_t)i0 * 4u);
+  if ((int)threadIdx.x < nbins) shist[threadIdx.x] = 0;
+  __syncthreads();
+  uint32_t v[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (i0 + j >= M) v[j] = 0xFFFFFFFFu;  // sentinel: no bin, never selected
+    const uint32_t d = v[j] >> 16;
+    if ((int)d < nbins) atomicAdd(&shist[d], 1u);
+  }
+  __syncthreads();
+  const Threshold thr = find_threshold<NT>(shist, nbins, (uint32_t)bsel, s_tmp);
+  const uint32_t quota = (uint32_t)bsel - thr.lt;
+  uint32_t lt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = (int)(v[j] >> 16);
+    lt += d < thr.t;
+    eq += d == thr.t;
+  }
+  uint32_t tot;
+  const uint32_t mine = lt | (eq << 16);
+  const uint32_t ex = block_scan_incl<NT>(mine, s_tmp, &tot) - mine;
+  uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = (int)(v[j] >> 16);
+    int pos = -1;
+    if (d < thr.t) {
+      pos = (int)(ltb + (eqb < quota ? eqb : quota));
+      ++ltb;
+    } else if (d == thr.t) {
+      if (eqb < quota) pos = (int)(ltb + eqb);
+      ++eqb;
+    }
+    if (pos >= 0) {
+      const int32_t tok = ((i0 + j) >> kpad_log2) * chunk + (int32_t)(v[j] & 0xffffu);
+      if (sidx) sidx[pos] = tok;
+      if (idx) idx[pos] = tok;
+    }
+  }
+  if (idx)
+    for (int j = bsel + threadIdx.x; j < budget; j += NT) idx[j] = -1;
+  __syncthreads();
+}
+
+template <int NT>
+ADM_DEV void final_select_tiled(const uint32_t* cand, int M, int kpad_log2, int chunk, int nbins,
+                                int bsel, int budget, int32_t* sidx, int32_t* idx,
+                                uint32_t* scand, int mcap, uint32_t* shist, uint32_t* s_tmp) {
   const bool resident = M <= mcap;
   for (int i = threadIdx.x; i < nbins; i += NT) shist[i] = 0;
   for (int base = 0; base < M; base += mcap) {

@@ -266,11 +266,15 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
       if (tok[j] < 0) sc[j] = -INFINITY;
       mloc = fmaxf(mloc, sc[j]);
     }
-    // batch maximum: slot maxima through LDS, reduced by every thread
-    if (l16 == 0) s_score[slot] = mloc;
+    // batch maximum: over the wavefront's 4 slots (lanes ^16, ^32), then the
+    // wavefront maxima through LDS
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    if (lane == 0) s_score[wid] = mloc;
     __syncthreads();
     float mb = -INFINITY;
-    for (int i = 0; i < NS; ++i) mb = fmaxf(mb, s_score[i]);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) mb = fmaxf(mb, s_score[i]);
     __syncthreads();
     if (mb == -INFINITY) continue;  // nothing valid in this batch (uniform)
     const float mn = fmaxf(m_run, mb);
