@@ -22,6 +22,16 @@ constexpr int kTmpThrLt = 17;     // count below the threshold
 constexpr int kTmpFlag = 20;      // "last arrival" flag
 constexpr int kTmpWords = 32;
 
+// Workgroup barrier for LDS exchanges only.  __syncthreads() also orders
+// global memory, which on this target waits for every outstanding vector
+// load and store; tail phases keep global loads in flight across their LDS
+// barriers, so they synchronise LDS alone.
+ADM_DEV void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- elements
 ADM_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -109,7 +119,7 @@ ADM_DEV void shared_to_lds(uint32_t* dst_lds, const uint32_t* src_global, int n)
       const int i = base + j * NT + (int)threadIdx.x;
       if (base + j * NT < n4) v[j] = load_shared_x4(r, (uint32_t)i * 16u);  // past n: reads 0
     }
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int j = 0; j < UL; ++j) {
       const int i = base + j * NT + (int)threadIdx.x;
@@ -273,7 +283,7 @@ ADM_DEV uint32_t block_scan_incl(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
   const int wid = threadIdx.x >> 6;
   v = wave_scan_incl(v);
   if (lane == kWave - 1) s_tmp[kTmpWaveSums + wid] = v;
-  __syncthreads();
+  lds_sync();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -281,7 +291,7 @@ ADM_DEV uint32_t block_scan_incl(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
     pre += (w < wid) ? x : 0u;
     tot += x;
   }
-  __syncthreads();
+  lds_sync();
   *total = tot;
   return v + pre;
 }
@@ -327,10 +337,10 @@ ADM_DEV void find_threshold_pair(const uint32_t* hist, int nbins, uint32_t K0, u
       }
     }
   }
-  __syncthreads();
+  lds_sync();
   *r0 = Threshold{(int)s_tmp[kTmpThrT], s_tmp[kTmpThrLt]};
   *r1 = Threshold{(int)s_tmp[kTmpThr1T], s_tmp[kTmpThr1Lt]};
-  __syncthreads();
+  lds_sync();
 }
 
 // One bin per thread (nbins <= NT): DPP scan inside each wavefront, then the
@@ -343,7 +353,7 @@ ADM_DEV Threshold find_threshold(const uint32_t* hist, int nbins, uint32_t K, ui
   const uint32_t h = (int)threadIdx.x < nbins ? hist[threadIdx.x] : 0u;
   const uint32_t incl_w = wave_scan_incl(h);
   if (lane == kWave - 1 && wid < nwb) s_tmp[kTmpWaveSums + wid] = incl_w;
-  __syncthreads();
+  lds_sync();
   if (wid < nwb) {
     uint32_t pre = 0;
     for (int w = 0; w < wid; ++w) pre += s_tmp[kTmpWaveSums + w];
@@ -353,7 +363,7 @@ ADM_DEV Threshold find_threshold(const uint32_t* hist, int nbins, uint32_t K, ui
       s_tmp[kTmpThrLt] = excl;
     }
   }
-  __syncthreads();
+  lds_sync();
   const Threshold r{(int)s_tmp[kTmpThrT], s_tmp[kTmpThrLt]};
   static_assert(NW <= 16, "wave sums live in s_tmp[0..16)");
   return r;
@@ -452,7 +462,7 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
   u32x4 e = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
   if (i0 < M) e = load_shared_x4(make_rsrc(cand, (uint32_t)M * 4u), (uint32_t)i0 * 4u);
   if ((int)threadIdx.x < nbins) shist[threadIdx.x] = 0;
-  __syncthreads();
+  lds_sync();
   uint32_t v[4] = {e.x, e.y, e.z, e.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -460,7 +470,7 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
     const uint32_t d = v[j] >> 16;
     if ((int)d < nbins) atomicAdd(&shist[d], 1u);
   }
-  __syncthreads();
+  lds_sync();
   const Threshold thr = find_threshold<NT>(shist, nbins, (uint32_t)bsel, s_tmp);
   const uint32_t quota = (uint32_t)bsel - thr.lt;
   uint32_t lt = 0, eq = 0;
@@ -493,7 +503,7 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
   }
   if (idx)
     for (int j = bsel + threadIdx.x; j < budget; j += NT) idx[j] = -1;
-  __syncthreads();
+  lds_sync();
 }
 
 template <int NT>
@@ -504,24 +514,24 @@ ADM_DEV void final_select_tiled(const uint32_t* cand, int M, int kpad_log2, int 
   for (int i = threadIdx.x; i < nbins; i += NT) shist[i] = 0;
   for (int base = 0; base < M; base += mcap) {
     const int n = min(mcap, M - base);
-    __syncthreads();
+    lds_sync();
     shared_to_lds<NT>(scand, cand + base, n);
-    __syncthreads();
+    lds_sync();
     for (int i = threadIdx.x; i < n; i += NT) {
       const uint32_t d = scand[i] >> 16;
       if ((int)d < nbins) atomicAdd(&shist[d], 1u);
     }
   }
-  __syncthreads();
+  lds_sync();
   const Threshold thr = find_threshold<NT>(shist, nbins, (uint32_t)bsel, s_tmp);
   const uint32_t quota = (uint32_t)bsel - thr.lt;
   uint32_t carry_lt = 0, carry_eq = 0;
   for (int base = 0; base < M; base += mcap) {
     const int n = min(mcap, M - base);
     if (!resident) {
-      __syncthreads();
+      lds_sync();
       shared_to_lds<NT>(scand, cand + base, n);
-      __syncthreads();
+      lds_sync();
     }
     const int tpt = (n + NT - 1) / NT;
     const int i0 = threadIdx.x * tpt;
@@ -562,7 +572,7 @@ ADM_DEV void final_select_tiled(const uint32_t* cand, int M, int kpad_log2, int 
   }
   if (idx)
     for (int j = bsel + threadIdx.x; j < budget; j += NT) idx[j] = -1;
-  __syncthreads();
+  lds_sync();
 }
 
 // Count this workgroup's arrival after its store_shared writes completed;

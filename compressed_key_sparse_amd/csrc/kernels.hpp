@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(const uint8_t* __restri
   for (int i = threadIdx.x; i < G * W; i += kScoreThreads)
     sq[i] = reinterpret_cast<const uint32_t*>(
         q_codes + ((int64_t)b * Hq + (int64_t)hkv * G) * (D / 4))[i];
-  __syncthreads();
+  lds_sync();
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
   const int64_t t0 = (int64_t)c * chunk;
@@ -271,11 +271,11 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     if (lane == 0) s_score[wid] = mloc;
-    __syncthreads();
+    lds_sync();
     float mb = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NW; ++i) mb = fmaxf(mb, s_score[i]);
-    __syncthreads();
+    lds_sync();
     if (mb == -INFINITY) continue;  // nothing valid in this batch (uniform)
     const float mn = fmaxf(m_run, mb);
     const float corr = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - mn);
@@ -304,7 +304,7 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
     for (int e = 0; e < EL; ++e) mine[2 + l16 * EL + e] = o[e];
   }
-  __syncthreads();
+  lds_sync();
   if (threadIdx.x < D) {
     float L = 0.0f, O = 0.0f;
     for (int w = 0; w < NW; ++w) {
@@ -317,7 +317,7 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
       s_res[1] = L;
     }
   }
-  __syncthreads();
+  lds_sync();
 }
 
 template <bool BF>
@@ -367,10 +367,10 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
   float M = -INFINITY, L = 0.0f, O = 0.0f;
   for (int t0 = 0; t0 < S; t0 += kMergeTile) {
     const int nt = min(kMergeTile, S - t0);
-    __syncthreads();
+    lds_sync();
     shared_to_lds<NT>(reinterpret_cast<uint32_t*>(s_tile),
                       reinterpret_cast<const uint32_t*>(ps + t0 * PWP), nt * PWP);
-    __syncthreads();
+    lds_sync();
     if (threadIdx.x < D) {
       for (int i = 0; i < nt; ++i) {
         const float mi = s_tile[i * PWP];
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int64_t row = (int64_t)b * Hq + hq;
   for (int i = threadIdx.x; i < NBP; i += NT) shist[i] = 0;
-  __syncthreads();
+  lds_sync();
   const int64_t t0 = (int64_t)c * chunk;
   const int valid = (int)min((int64_t)chunk, n_ctx - t0);
   const uint16_t* drow = dist + row * n_ctx + t0;
@@ -421,13 +421,13 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     sdist[t] = d;
     atomicAdd(&shist[d], 1u);
   }
-  __syncthreads();
+  lds_sync();
   const int kc = min(budget, valid);
   const int kpad = 1 << kpad_log2;
   const Threshold thr = find_threshold<NT>(shist, NB, (uint32_t)kc, s_tmp);
   chunk_compact<NT>(sdist, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad, s_tmp,
                     [](uint32_t, uint32_t) {});
-  __syncthreads();
+  lds_sync();
   lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
   if (!arrive_last<NT>(&counters[row], n_chunks, s_tmp)) return;
   final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad_log2, chunk, NB,
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     const uint32_t word = wave_encode<D>(y);
     if (lane % kLanesPerWord == 0) sq[g * W + lane / kLanesPerWord] = word;
   }
-  __syncthreads();
+  lds_sync();
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
   const int64_t t0 = (int64_t)c * chunk;
@@ -494,30 +494,31 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     sdist[g * chunk + tok] = (uint16_t)d;
     atomicAdd(&shist[g * NBP + d], 1u);
   });
-  __syncthreads();
+  lds_sync();
   const int kc = min(budget, valid);
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
     const Threshold thr = find_threshold<NT>(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
     chunk_compact<NT>(sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad,
                       s_tmp, [](uint32_t, uint32_t) {});
-    __syncthreads();
+    lds_sync();
     lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
   }
   if (!arrive_last<NT>(&counters[b * Hkv + hkv], n_chunks, s_tmp)) return;
+  const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap;
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-    final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad_log2, chunk, NB, bsel, budget,
-                     fuse_attend ? sidx : nullptr, idx ? idx + row * budget : nullptr, scand,
-                     mcap, fhist, s_tmp);
+    final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad_log2, chunk, NB, bsel,
+                     budget, fuse_attend ? sidx : nullptr, idx ? idx + row * budget : nullptr,
+                     scand, mcap, fhist, s_tmp);
     if (fuse_attend) {
-      attend_rows<D, BF, NT>(q, k, v, row * D, ((int64_t)b * Hkv + hkv) * cap, cap, sidx, bsel,
+      attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx, bsel,
                              qscale, s_part, s_res);
       if (threadIdx.x < D) {
         const float L = s_res[1];
         store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? s_res[2 + threadIdx.x] / L : 0.0f);
       }
-      __syncthreads();
+      lds_sync();
     }
   }
   if (threadIdx.x == 0) counters[b * Hkv + hkv] = 0;
