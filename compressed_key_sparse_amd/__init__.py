@@ -29,7 +29,9 @@ _LIB_PATH = os.path.join(_HERE, "libadamas.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = range(5)
 F32, BF16 = 0, 1
 OP_SELECT_TOPK, OP_SPARSE_ATTEND, OP_DECODE_STEP = 0, 1, 2
-WS_CTRL_BYTES = 65536
+WS_CTRL_BYTES = 65792          # ADAMAS_WS_CTRL_BYTES
+WS_STATUS_OFFSET = 65536       # ADAMAS_WS_STATUS_OFFSET
+DECODE_AUTO, DECODE_LAST_ARRIVAL, DECODE_GROUP_WAIT = 0, 1, 2
 
 _lib = None
 
@@ -69,6 +71,10 @@ def load():
     lib.adamas_status_string.argtypes = [i32]
     lib.adamas_status_string.restype = ctypes.c_char_p
     lib.adamas_version.restype = i32
+    lib.adamas_set_decode_mode.argtypes = [i32]
+    lib.adamas_decode_path.argtypes = [i32, i32, i32, i64, i32, i32]
+    for fn in ("adamas_set_decode_mode", "adamas_decode_path"):
+        getattr(lib, fn).restype = i32
     for fn in ("adamas_encode_keys", "adamas_score", "adamas_select_topk", "adamas_sparse_attend",
                "adamas_decode_step"):
         getattr(lib, fn).restype = i32
@@ -218,6 +224,20 @@ def sparse_attend(q, k, v, idx, scale: float = 0.0, out=None, ws: Workspace | No
                                      _dev_ptr(buf, "ws"), buf.numel(), _stream(q, stream))
     _check(st, "adamas_sparse_attend")
     return out
+
+
+def set_decode_mode(mode: int) -> None:
+    """Process-wide schedule of decode_step: DECODE_AUTO, DECODE_LAST_ARRIVAL or
+    DECODE_GROUP_WAIT (adamas_set_decode_mode)."""
+    _check(load().adamas_set_decode_mode(int(mode)), "adamas_set_decode_mode")
+
+
+def decode_path(B: int, Hq: int, Hkv: int, n_ctx: int, budget: int, head_dim: int) -> int:
+    """The schedule decode_step would use for this shape on the current device."""
+    r = load().adamas_decode_path(B, Hq, Hkv, n_ctx, budget, head_dim)
+    if r < 0:
+        raise AdamasError(-r, "adamas_decode_path")
+    return r
 
 
 def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0, out=None,

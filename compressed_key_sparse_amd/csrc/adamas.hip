@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "adamas.h"
 #include "kernels.hpp"
@@ -135,6 +136,74 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D)
   return p;
 }
 
+// adamas_decode_step with group waits (k_decode_gs): every workgroup of the
+// launch must be resident at once, so the grid is kept within one
+// 1024-thread workgroup per compute unit (always resident: at most 128 VGPRs
+// and 64 KiB of LDS per workgroup).  Chunks are as small as that allows
+// (more compute units streaming), and no smaller than 1024 tokens.
+struct GroupPlan {
+  bool ok = false;
+  int chunk = 0, n_chunks = 0, cmax = 0;
+  size_t lds = 0, hist_off = 0, part_off = 0, total = 0;
+};
+
+size_t decode_gs_lds(int D, int G, int c, int cmax) {
+  const int nw = kDecodeThreads / kWave;
+  const size_t pwp = (size_t)((2 + D + 3) & ~3);
+  const size_t attend = ((size_t)nw * (2 + D) + kDecodeThreads / 16 + pwp) * 4;
+  const size_t merge = (size_t)kGsMergeTile * pwp * 4;
+  return (size_t)kTmpWords * 4 + 32 * 4 + (size_t)G * (D / 16) * 4 +
+         (size_t)(G + 2) * nbins_padded(D) * 4 + (size_t)G * cmax * 4 +
+         std::max({(size_t)G * c * 2, attend, merge});
+}
+
+GroupPlan plan_decode_gs(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D,
+                         int64_t capacity) {
+  GroupPlan p;
+  const int G = Hq / Hkv;
+  const int64_t groups = (int64_t)B * Hkv, rows = (int64_t)B * Hq;
+  const int64_t bsel = n_ctx < budget ? n_ctx : budget;
+  auto cmax_of = [&](int c) { return (int)((std::min<int64_t>(bsel, c) + 3) & ~3); };
+  auto chunks_of = [&](int c) { return (n_ctx + c - 1) / c; };
+  int c = 16384;
+  while (c > 1024 && decode_gs_lds(D, G, c, cmax_of(c)) > kLdsLimit) c /= 2;
+  while (c > 1024 && groups * chunks_of(c / 2) <= capacity &&
+         decode_gs_lds(D, G, c / 2, cmax_of(c / 2)) <= kLdsLimit)
+    c /= 2;
+  p.chunk = c;
+  p.n_chunks = (int)chunks_of(c);
+  p.cmax = cmax_of(c);
+  p.lds = decode_gs_lds(D, G, c, p.cmax);
+  const size_t nbh = (size_t)((3 * D + 1 + 7) & ~7), pwp = (size_t)((2 + D + 3) & ~3);
+  p.hist_off = round_up(ADAMAS_WS_CTRL_BYTES, 256);
+  p.part_off = round_up(p.hist_off + (size_t)rows * p.n_chunks * nbh * 2, 256);
+  p.total = round_up(p.part_off + (size_t)rows * p.n_chunks * pwp * 4, 256);
+  p.ok = p.lds <= kLdsLimit && groups * p.n_chunks <= capacity && groups <= kMaxGroups;
+  return p;
+}
+
+// Workgroups of one launch that are resident together: one per compute unit.
+int64_t device_capacity() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Sizing a workspace does not know the device: size for a capacity no device
+// here exceeds, which gives the most chunks.
+constexpr int64_t kSizingCapacity = 1024;
+
+std::atomic<int> g_decode_mode{ADAMAS_DECODE_AUTO};
+
 int launch_status() {
   return hipGetLastError() == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_DEVICE;
 }
@@ -177,6 +246,30 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
       p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
       a.out);
+}
+
+template <int D, int G, bool BF>
+void launch_decode_gs_t(const GroupPlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a,
+                        uint8_t* w) {
+  k_decode_gs<D, G, BF><<<grid, kDecodeThreads, p.lds, s>>>(
+      a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.chunk, p.n_chunks, a.budget, p.cmax,
+      a.qscale, reinterpret_cast<uint16_t*>(w + p.hist_off),
+      reinterpret_cast<float*>(w + p.part_off), reinterpret_cast<uint32_t*>(w + kCtrlSelect),
+      reinterpret_cast<uint32_t*>(w + kCtrlAttend),
+      reinterpret_cast<uint32_t*>(w + ADAMAS_WS_STATUS_OFFSET), a.idx, a.out);
+}
+
+template <int D, bool BF>
+bool dispatch_decode_gs(int G, const GroupPlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a,
+                        uint8_t* w) {
+  switch (G) {
+#define ADM_CASE(g) \
+  case g: launch_decode_gs_t<D, g, BF>(p, grid, s, a, w); return true;
+    ADM_CASE(1) ADM_CASE(2) ADM_CASE(3) ADM_CASE(4) ADM_CASE(5) ADM_CASE(6) ADM_CASE(7)
+    ADM_CASE(8)
+#undef ADM_CASE
+    default: return false;
+  }
 }
 
 template <int D, bool BF>
@@ -248,7 +341,9 @@ size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx, int
     case ADAMAS_OP_SPARSE_ATTEND:
       return round_up(plan_attend(rows, budget, head_dim, ADAMAS_WS_CTRL_BYTES).end, 256);
     case ADAMAS_OP_DECODE_STEP:
-      return plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).total;
+      return std::max(
+          plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).total,
+          plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, kSizingCapacity).total);
     default: return 0;
   }
 }
@@ -357,11 +452,35 @@ int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_
     return ADAMAS_ERR_INVALID;
   if (idx_out != nullptr && !aligned16(idx_out)) return ADAMAS_ERR_INVALID;
   if (ws == nullptr || !aligned16(ws)) return ADAMAS_ERR_WORKSPACE;
-  const DecodePlan p = plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim);
-  if (ws_bytes < p.total) return ADAMAS_ERR_WORKSPACE;
+  // the documented requirement covers both schedules, whichever runs
+  if (ws_bytes < adamas_workspace_bytes(ADAMAS_OP_DECODE_STEP, B, Hq, Hkv, n_ctx, budget,
+                                        head_dim))
+    return ADAMAS_ERR_WORKSPACE;
+  const int mode = g_decode_mode.load(std::memory_order_relaxed);
   uint8_t* w = static_cast<uint8_t*>(ws);
   const int G = Hq / Hkv;
   const bool bf = dtype == ADAMAS_BF16;
+  const DecodePlan p = plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim);
+  // AUTO takes group waits where the last-arrival schedule could not fuse
+  // the attention (it would need a second launch)
+  if (mode == ADAMAS_DECODE_GROUP_WAIT || (mode == ADAMAS_DECODE_AUTO && !p.fuse)) {
+    const GroupPlan gp = plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, device_capacity());
+    if (gp.ok) {
+      if (ws_bytes < gp.total) return ADAMAS_ERR_WORKSPACE;
+      DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
+                   nullptr, nullptr, idx_out, out};
+      const dim3 grid((unsigned)gp.n_chunks, (unsigned)Hkv, (unsigned)B);
+      const bool ok = head_dim == 128
+                          ? (bf ? dispatch_decode_gs<128, true>(G, gp, grid, stream, a, w)
+                                : dispatch_decode_gs<128, false>(G, gp, grid, stream, a, w))
+                          : (bf ? dispatch_decode_gs<64, true>(G, gp, grid, stream, a, w)
+                                : dispatch_decode_gs<64, false>(G, gp, grid, stream, a, w));
+      if (!ok) return ADAMAS_ERR_UNSUPPORTED;
+      return launch_status();
+    }
+    if (mode == ADAMAS_DECODE_GROUP_WAIT) return ADAMAS_ERR_UNSUPPORTED;
+  }
+  if (ws_bytes < p.total) return ADAMAS_ERR_WORKSPACE;
   int32_t* idx = idx_out != nullptr ? idx_out
                  : p.fuse       ? nullptr
                                 : reinterpret_cast<int32_t*>(w + p.idx_off);
@@ -384,6 +503,29 @@ int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_
                   reinterpret_cast<uint32_t*>(w + kCtrlAttend), out);
   }
   return launch_status();
+}
+
+int adamas_set_decode_mode(int mode) {
+  if (mode != ADAMAS_DECODE_AUTO && mode != ADAMAS_DECODE_LAST_ARRIVAL &&
+      mode != ADAMAS_DECODE_GROUP_WAIT)
+    return ADAMAS_ERR_INVALID;
+  g_decode_mode.store(mode, std::memory_order_relaxed);
+  return ADAMAS_OK;
+}
+
+int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_ctx < 1 || budget < 1 ||
+      budget > kMaxBudget || !valid_dim(head_dim) || Hq / Hkv > kMaxG)
+    return -ADAMAS_ERR_INVALID;
+  const int mode = g_decode_mode.load(std::memory_order_relaxed);
+  if (mode == ADAMAS_DECODE_LAST_ARRIVAL) return ADAMAS_DECODE_LAST_ARRIVAL;
+  if (mode == ADAMAS_DECODE_AUTO && plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).fuse)
+    return ADAMAS_DECODE_LAST_ARRIVAL;
+  const int64_t capacity = device_capacity();
+  if (capacity <= 0) return -ADAMAS_ERR_DEVICE;
+  if (plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, capacity).ok)
+    return ADAMAS_DECODE_GROUP_WAIT;
+  return mode == ADAMAS_DECODE_GROUP_WAIT ? -ADAMAS_ERR_UNSUPPORTED : ADAMAS_DECODE_LAST_ARRIVAL;
 }
 
 }  // extern "C"

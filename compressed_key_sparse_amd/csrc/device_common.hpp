@@ -88,6 +88,12 @@ ADM_DEV void store_shared_x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 
 ADM_DEV u32x4 load_shared_x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCachePolicyCoherent);
 }
+ADM_DEV uint32_t load_shared_b32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kCachePolicyCoherent);
+}
+ADM_DEV uint32_t load_shared_b16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)byte_off, 0, kCachePolicyCoherent);
+}
 ADM_DEV void store_shared(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -369,18 +375,59 @@ ADM_DEV Threshold find_threshold(const uint32_t* hist, int nbins, uint32_t K, ui
   return r;
 }
 
+// Threshold of a budget over a group of chunks scanned by different
+// workgroups.  Thread b < nbins holds tot = the group's count of distance b
+// and bef = the count of distance b in the chunks before this workgroup's.
+// Returns the group threshold t and lt = count(D < t) as find_threshold
+// does, and for the chunks before this one lt_before = their count of D < t
+// and ties_before = their count of D == t.  s_sums holds 32 words.
+struct GroupThreshold {
+  int t;
+  uint32_t lt, lt_before, ties_before;
+};
+constexpr int kTmpGrpLtBefore = 21, kTmpGrpTiesBefore = 22, kTmpGroupCounts = 24;
+
+template <int NT>
+ADM_DEV GroupThreshold find_group_threshold(uint32_t tot, uint32_t bef, int nbins, uint32_t K,
+                                            uint32_t* s_sums, uint32_t* s_tmp) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  const int nwb = (nbins + kWave - 1) / kWave;
+  if ((int)threadIdx.x >= nbins) tot = bef = 0;
+  const uint32_t it = wave_scan_incl(tot), ib = wave_scan_incl(bef);
+  if (lane == kWave - 1 && wid < nwb) {
+    s_sums[wid] = it;
+    s_sums[16 + wid] = ib;
+  }
+  lds_sync();
+  if (wid < nwb) {
+    uint32_t pt = 0, pb = 0;
+    for (int w = 0; w < wid; ++w) {
+      pt += s_sums[w];
+      pb += s_sums[16 + w];
+    }
+    const uint32_t incl = pt + it, excl = incl - tot;
+    if (excl < K && K <= incl) {
+      s_tmp[kTmpThrT] = threadIdx.x;
+      s_tmp[kTmpThrLt] = excl;
+      s_tmp[kTmpGrpLtBefore] = pb + ib - bef;
+      s_tmp[kTmpGrpTiesBefore] = bef;
+    }
+  }
+  lds_sync();
+  return GroupThreshold{(int)s_tmp[kTmpThrT], s_tmp[kTmpThrLt], s_tmp[kTmpGrpLtBefore],
+                        s_tmp[kTmpGrpTiesBefore]};
+}
+
 // Ordered selection inside one chunk held in LDS.  Keeps every token with
-// D < t and the first `quota` tokens (lowest index) with D == t, and writes
-// them in token order as (D << 16) | token to out[] (LDS); entries
-// [kept, pad_to) of out[] get the sentinel 0xFFFFFFFF.  Token i is kept at
-// position (#lt before i) + min(#eq before i, quota).  Thread j owns tokens
-// [16j, 16j+16), read once with 16-byte LDS loads (threads past the chunk
-// own nothing).  on_kept(token, D) is called for every kept token.
+// D < t and the first `quota` tokens (lowest index) with D == t, and calls
+// emit(pos, token, D) for each, pos being its rank in token order among the
+// kept: (#lt before it) + min(#eq before it, quota).  Returns the number
+// kept.  Thread j owns tokens [16j, 16j+16), read once with 16-byte LDS loads
+// (threads past the chunk own nothing).
 constexpr int kCompactTpt = 16;
-template <int NT, class OnKept>
-ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint32_t quota,
-                           uint32_t* out, int kept, int pad_to, uint32_t* s_tmp,
-                           OnKept&& on_kept) {
+template <int NT, class Emit>
+ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t quota,
+                               uint32_t* s_tmp, Emit&& emit) {
   constexpr int TPT = kCompactTpt;
   const int t0 = threadIdx.x * TPT;
   uint32_t ltm = 0, eqm = 0;  // bit i: token t0+i is below / at the threshold
@@ -388,8 +435,8 @@ ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint
     // two distances per 32-bit word (both <= 3*D < 2^15): with packed 16-bit
     // subtractions, bit 15 of (t-1-d) is set iff d >= t and of (t-d) iff d > t
     typedef short s16x2 __attribute__((ext_vector_type(2)));
-    const s16x2 tm1 = {(short)(thr.t - 1), (short)(thr.t - 1)};
-    const s16x2 tt = {(short)thr.t, (short)thr.t};
+    const s16x2 tm1 = {(short)(t - 1), (short)(t - 1)};
+    const s16x2 tt = {(short)t, (short)t};
     uint32_t ge = 0, gt = 0;
 #pragma unroll
     for (int v8 = 0; v8 < TPT / 8; ++v8) {
@@ -417,20 +464,30 @@ ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint
   // visit only the flagged tokens, in order (a small fraction of the chunk)
   for (uint32_t m = ltm | eqm; m != 0; m &= m - 1) {
     const int i = __ffs(m) - 1;
-    const uint32_t t = (uint32_t)(t0 + i);
+    const uint32_t tok = (uint32_t)(t0 + i);
     if ((ltm >> i) & 1u) {
-      const uint32_t d = sdist[t];
-      out[ltb + (eqb < quota ? eqb : quota)] = (d << 16) | t;
-      on_kept(t, d);
+      emit(ltb + (eqb < quota ? eqb : quota), tok, (uint32_t)sdist[tok]);
       ++ltb;
     } else {
-      if (eqb < quota) {
-        out[ltb + eqb] = ((uint32_t)thr.t << 16) | t;
-        on_kept(t, (uint32_t)thr.t);
-      }
+      if (eqb < quota) emit(ltb + eqb, tok, (uint32_t)t);
       ++eqb;
     }
   }
+  const uint32_t eq_all = tot >> 16;
+  return (tot & 0xffffu) + (eq_all < quota ? eq_all : quota);
+}
+
+// chunk_collect into out[] (LDS) as (D << 16) | token; entries [kept, pad_to)
+// get the sentinel 0xFFFFFFFF.  on_kept(token, D) is called for every kept
+// token.
+template <int NT, class OnKept>
+ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint32_t quota,
+                           uint32_t* out, int kept, int pad_to, uint32_t* s_tmp,
+                           OnKept&& on_kept) {
+  chunk_collect<NT>(sdist, valid, thr.t, quota, s_tmp, [&](uint32_t pos, uint32_t t, uint32_t d) {
+    out[pos] = (d << 16) | t;
+    on_kept(t, d);
+  });
   for (int j = kept + (int)threadIdx.x; j < pad_to; j += NT) out[j] = 0xFFFFFFFFu;
 }
 
@@ -591,6 +648,32 @@ ADM_DEV bool arrive_last(uint32_t* counter, int n_arrivals, uint32_t* s_tmp) {
   }
   __syncthreads();
   return s_tmp[kTmpFlag] != 0;
+}
+
+// Count this workgroup's arrival as arrive_last does, then wait until all
+// n_arrivals workgroups of the group have arrived.  Only for launches whose
+// workgroups are all resident on the device together (the caller checks the
+// grid against the device), so every awaited workgroup is running.  The wait
+// is bounded: past kGroupWaitPolls polls it gives up and sets *status to 1,
+// and the results of that launch are invalid.
+constexpr uint32_t kGroupWaitPolls = 1u << 20;
+template <int NT>
+ADM_DEV void arrive_and_wait(uint32_t* counter, int n_arrivals, uint32_t* status) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t seen =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    for (uint32_t polls = 0; seen < (uint32_t)n_arrivals; ++polls) {
+      if (polls == kGroupWaitPolls) {
+        __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      seen = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
 }
 
 }  // namespace adm

@@ -11,6 +11,8 @@ namespace adm {
 
 constexpr int kNbins(int D) { return 3 * D + 1; }
 constexpr int kNbinsPadded(int D) { return (3 * D + 1 + 3) & ~3; }
+constexpr int kNbinsHist(int D) { return (3 * D + 1 + 7) & ~7; }  // u16 bins, 16-byte rows
+constexpr int kGsMergeTile = 16;  // partials merged per LDS tile (k_decode_gs)
 
 constexpr int kEncodeThreads = 256;
 constexpr int kScoreThreads = 256;
@@ -522,6 +524,175 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     }
   }
   if (threadIdx.x == 0) counters[b * Hkv + hkv] = 0;
+}
+
+// ------------------------------------------ fused decode step, group wait
+// adamas_decode_step when all workgroups of the launch are resident on the
+// device together: grid (chunks, Hkv, B) as k_decode, the chunk workgroups
+// of one KV head forming a group.  Each workgroup encodes its query heads
+// and scans its chunk (§2.1-§2.3) into LDS as k_decode does, then publishes
+// only the chunk's distance histograms and waits for its group.  The summed
+// histograms give every workgroup each query head's budget threshold (§5.2)
+// and, from the chunks before its own, how many of the threshold ties fall
+// to its chunk and where its tokens go in the ascending selection; so each
+// workgroup keeps its own share of the budget without exchanging candidates,
+// attends over those rows (§6) and publishes a partial (m, l, o).  The last
+// workgroup of the group merges the partials by log-sum-exp.
+//   ghist  [B*Hq][n_chunks][NBH] u16   part [B*Hq][n_chunks][PWP] f32
+//   cmax   >= min(budget, n_ctx, chunk), a multiple of 4 (LDS index rows)
+template <int D, int G, bool BF>
+__global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
+    int n_chunks, int budget, int cmax, float qscale, uint16_t* __restrict__ ghist,
+    float* __restrict__ part, uint32_t* __restrict__ arrive_hist,
+    uint32_t* __restrict__ arrive_part, uint32_t* __restrict__ status, int32_t* __restrict__ idx,
+    void* __restrict__ out) {
+  constexpr int NT = kDecodeThreads, NW = NT / kWave;
+  constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), NBH = kNbinsHist(D), W = D / 16;
+  static_assert(G <= kTmpWords - kTmpGroupCounts, "per-head counts live in s_tmp");
+  constexpr int E = D / 64, kLanesPerWord = 16 / E, PW = 2 + D, PWP = (PW + 3) & ~3;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* s_sums = s_tmp + kTmpWords;
+  uint32_t* sq = s_sums + 32;
+  uint32_t* shist = sq + G * W;
+  uint32_t* s_tot = shist + G * NBP;  // group counts per bin: all chunks, chunks before
+  uint32_t* s_bef = s_tot + NBP;
+  int32_t* sidx = reinterpret_cast<int32_t*>(s_bef + NBP);
+  uint8_t* region = reinterpret_cast<uint8_t*>(sidx + G * cmax);
+  uint16_t* sdist = reinterpret_cast<uint16_t*>(region);  // scan and selection
+  float* s_part = reinterpret_cast<float*>(region);       // attention, after selection
+  float* s_res = s_part + NW * PW + NT / 16;
+  float* s_merge = reinterpret_cast<float*>(region);      // merge, last workgroup
+
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int c = (lin % n_chunks + lin / n_chunks) % n_chunks;
+  const int hkv = blockIdx.y, b = blockIdx.z;
+  const int grp = b * Hkv + hkv;
+  const int64_t row0 = (int64_t)b * Hq + (int64_t)hkv * G;
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  for (int i = threadIdx.x; i < G * NBP; i += NT) shist[i] = 0;
+  for (int g = wid; g < G; g += NW) {
+    float y[E];
+    load_elems<E>(q, BF, (row0 + g) * D + lane * E, y);
+    const uint32_t word = wave_encode<D>(y);
+    if (lane % kLanesPerWord == 0) sq[g * W + lane / kLanesPerWord] = word;
+  }
+  lds_sync();
+  QPlanes qp[G];
+  load_qplanes<D, G>(sq, qp);
+  const int64_t t0 = (int64_t)c * chunk;
+  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
+  const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
+  scan_chunk<D, G, NT, 8>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
+    sdist[g * chunk + tok] = (uint16_t)d;
+    atomicAdd(&shist[g * NBP + d], 1u);
+  });
+  lds_sync();
+
+  // publish this chunk's histograms as u16 rows (counts <= chunk < 2^16)
+  for (int i = threadIdx.x; i < G * (NBH / 8); i += NT) {
+    const int g = i / (NBH / 8), b0 = (i % (NBH / 8)) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int lo = b0 + 2 * j, hi = lo + 1;
+      w[j] = (lo < NB ? shist[g * NBP + lo] : 0u) | ((hi < NB ? shist[g * NBP + hi] : 0u) << 16);
+    }
+    uint16_t* dst = ghist + ((row0 + g) * n_chunks + c) * NBH;
+    store_shared_x4(make_rsrc(dst, NBH * 2), (uint32_t)b0 * 2u, u32x4{w[0], w[1], w[2], w[3]});
+  }
+  arrive_and_wait<NT>(&arrive_hist[grp], n_chunks, status);
+
+  // group thresholds; this chunk's share of each query head's selection
+  const int bsel = (int)min((int64_t)budget, n_ctx);
+  uint32_t* s_cnt = s_tmp + kTmpGroupCounts;  // rows kept per query head
+  for (int g = 0; g < G; ++g) {
+    const int64_t row = row0 + g;
+    // the group's histograms: one 16-byte row segment (8 bins of one chunk)
+    // per thread, summed into LDS
+    for (int i = threadIdx.x; i < 2 * NBP; i += NT) s_tot[i] = 0;
+    lds_sync();
+    {
+      constexpr int SEG = NBH / 8;
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(ghist + row * n_chunks * NBH, (uint32_t)(n_chunks * NBH * 2));
+      for (int i0 = 0; i0 < n_chunks * SEG; i0 += NT) {
+        const int i = i0 + (int)threadIdx.x;
+        const int cc = i / SEG, b0 = (i % SEG) * 8;
+        u32x4 h = {0u, 0u, 0u, 0u};
+        if (i < n_chunks * SEG) h = load_shared_x4(r, (uint32_t)(cc * NBH + b0) * 2u);
+        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t x = (hw[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+          if (x != 0u && b0 + j < NB) {
+            atomicAdd(&s_tot[b0 + j], x);
+            if (cc < c) atomicAdd(&s_bef[b0 + j], x);
+          }
+        }
+      }
+    }
+    lds_sync();
+    const uint32_t tot = (int)threadIdx.x < NB ? s_tot[threadIdx.x] : 0u;
+    const uint32_t bef = (int)threadIdx.x < NB ? s_bef[threadIdx.x] : 0u;
+    const GroupThreshold gt = find_group_threshold<NT>(tot, bef, NB, (uint32_t)bsel, s_sums, s_tmp);
+    const uint32_t quota = (uint32_t)bsel - gt.lt;  // ties at t the whole group keeps
+    const uint32_t mine_q = quota > gt.ties_before ? quota - gt.ties_before : 0u;
+    const uint32_t off = gt.lt_before + min(gt.ties_before, quota);
+    int32_t* sg = sidx + g * cmax;
+    int32_t* ig = idx ? idx + row * budget + off : nullptr;
+    const uint32_t kept = chunk_collect<NT>(sdist + g * chunk, valid, gt.t, mine_q, s_tmp,
+                               [&](uint32_t pos, uint32_t t, uint32_t) {
+                                 const int32_t tok = (int32_t)(t0 + t);
+                                 sg[pos] = tok;
+                                 if (ig) ig[pos] = tok;
+                               });
+    if (threadIdx.x == 0) s_cnt[g] = kept;
+    if (idx && c == 0)
+      for (int j = bsel + (int)threadIdx.x; j < budget; j += NT) idx[row * budget + j] = -1;
+  }
+  lds_sync();  // index rows complete; the distances are no longer needed
+
+  const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap;
+  for (int g = 0; g < G; ++g) {
+    const int64_t row = row0 + g;
+    attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx + g * cmax, (int)s_cnt[g], qscale,
+                           s_part, s_res);
+    lds_to_shared<NT>(reinterpret_cast<uint32_t*>(part + (row * n_chunks + c) * PWP),
+                      reinterpret_cast<const uint32_t*>(s_res), PWP);
+  }
+  if (!arrive_last<NT>(&arrive_part[grp], n_chunks, s_tmp)) return;
+  for (int g = 0; g < G; ++g) {
+    const int64_t row = row0 + g;
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    for (int c0 = 0; c0 < n_chunks; c0 += kGsMergeTile) {
+      const int nt = min(kGsMergeTile, n_chunks - c0);
+      lds_sync();
+      shared_to_lds<NT>(reinterpret_cast<uint32_t*>(s_merge),
+                        reinterpret_cast<const uint32_t*>(part + (row * n_chunks + c0) * PWP),
+                        nt * PWP);
+      lds_sync();
+      if ((int)threadIdx.x < D) {
+        for (int i = 0; i < nt; ++i) {
+          const float mi = s_merge[i * PWP];
+          if (mi == -INFINITY) continue;
+          const float Mn = fmaxf(M, mi);
+          const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+          const float bb = exp2f(mi - Mn);
+          L = L * a + s_merge[i * PWP + 1] * bb;
+          O = O * a + s_merge[i * PWP + 2 + threadIdx.x] * bb;
+          M = Mn;
+        }
+      }
+    }
+    if ((int)threadIdx.x < D) store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? O / L : 0.0f);
+  }
+  if (threadIdx.x == 0) {
+    arrive_hist[grp] = 0;
+    arrive_part[grp] = 0;
+  }
 }
 
 }  // namespace adm

@@ -49,8 +49,15 @@ extern "C" {
 
 #define ADAMAS_VERSION 100 /* 1.0.0 */
 
-/* Leading bytes of a workspace that must be zero before its first use. */
-#define ADAMAS_WS_CTRL_BYTES 65536
+/* Leading bytes of a workspace that must be zero before its first use:
+ * arrival counters, then the status word. */
+#define ADAMAS_WS_CTRL_BYTES 65792
+
+/* Byte offset in a workspace of a u32 status word.  A decode step that ran
+ * with group waits (ADAMAS_DECODE_GROUP_WAIT) and found a wait exceeding its
+ * bound sets it to a nonzero value; that call's outputs are then invalid.
+ * The library never clears it. */
+#define ADAMAS_WS_STATUS_OFFSET 65536
 
 typedef enum {
     ADAMAS_OK = 0,
@@ -61,6 +68,14 @@ typedef enum {
 } adamas_status;
 
 typedef enum { ADAMAS_F32 = 0, ADAMAS_BF16 = 1 } adamas_dtype;
+
+/* How adamas_decode_step coordinates the workgroups that scan the chunks of
+ * one KV head (see adamas_set_decode_mode). */
+typedef enum {
+    ADAMAS_DECODE_AUTO = 0,
+    ADAMAS_DECODE_LAST_ARRIVAL = 1,
+    ADAMAS_DECODE_GROUP_WAIT = 2
+} adamas_decode_mode;
 
 typedef enum {
     ADAMAS_OP_SELECT_TOPK = 0,
@@ -149,6 +164,38 @@ int adamas_decode_step(const void *q, const void *k, const void *v,
                        int head_dim, int64_t cap, int64_t n_ctx, int budget,
                        float scale, void *out, int32_t *idx_out, void *ws,
                        size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Process-wide choice of how adamas_decode_step splits the work of one KV
+ * head (results are identical; only the schedule differs):
+ *  - ADAMAS_DECODE_LAST_ARRIVAL: each chunk workgroup hands its chunk's
+ *    min(budget, chunk) best candidates to the last workgroup to finish, which
+ *    selects the budget (§5.2) and attends (§6) alone.
+ *  - ADAMAS_DECODE_GROUP_WAIT: each chunk workgroup publishes its chunk's
+ *    distance histogram and waits for the others of its KV head; from the sum
+ *    it selects its own share of the budget and attends over it, and the last
+ *    one merges the partial results.  Needs every workgroup of the launch
+ *    resident at once, i.e. B*Hkv*chunks <= the device's compute units;
+ *    adamas_decode_step returns ADAMAS_ERR_UNSUPPORTED when it is forced and
+ *    the shape does not fit.  Launches of this kind on several streams of one
+ *    device at once rely on the hardware starting a launch's workgroups in
+ *    order; each wait is bounded (see ADAMAS_WS_STATUS_OFFSET).
+ *  - ADAMAS_DECODE_AUTO (default): LAST_ARRIVAL while its last workgroup can
+ *    attend over the whole selection itself (G * ceil(min(budget, n_ctx) /
+ *    256) <= 2), else GROUP_WAIT where the shape fits, else LAST_ARRIVAL with
+ *    a separate attention launch.
+ * Returns ADAMAS_OK, or ADAMAS_ERR_INVALID for an unknown mode.
+ */
+int adamas_set_decode_mode(int mode);
+
+/*
+ * The schedule adamas_decode_step would use for this shape on the current
+ * device under the current mode: ADAMAS_DECODE_LAST_ARRIVAL or
+ * ADAMAS_DECODE_GROUP_WAIT, or a negated status (-ADAMAS_ERR_INVALID for a
+ * bad shape, -ADAMAS_ERR_UNSUPPORTED if GROUP_WAIT is forced and does not
+ * fit, -ADAMAS_ERR_DEVICE if no device can be queried).
+ */
+int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim);
 
 /* Workspace bytes needed by `op` for the given shape (0 for invalid shapes). */
 size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx,

@@ -59,8 +59,8 @@ def test_workspace_bytes(lib):
     assert f(2, 1, 32, 32, 0, 64, 128) == 0
     assert f(2, 1, 32, 32, 1000, 0, 128) == 0
     assert f(7, 1, 32, 32, 1000, 64, 128) == 0         # unknown op
-    # grows with the context and the budget
-    assert f(2, 1, 32, 32, 262144, 256, 128) > f(2, 1, 32, 32, 131072, 256, 128)
+    # never shrinks with the context; grows with the budget
+    assert f(2, 1, 32, 32, 262144, 256, 128) >= f(2, 1, 32, 32, 131072, 256, 128)
     assert f(1, 1, 32, 32, 1, 1024, 128) > f(1, 1, 32, 32, 1, 64, 128)
 
 
@@ -137,3 +137,24 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(adamas, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         adamas.load()
+
+
+def test_decode_mode_validation(lib):
+    assert lib.adamas_set_decode_mode(3) == INVALID
+    assert lib.adamas_set_decode_mode(-1) == INVALID
+    for m in (2, 1, 0):                     # GROUP_WAIT, LAST_ARRIVAL, back to AUTO
+        assert lib.adamas_set_decode_mode(m) == OK
+    # shape checks come before any device query
+    f = lib.adamas_decode_path
+    assert f(1, 32, 32, 0, 256, 128) == -INVALID
+    assert f(1, 32, 7, 1000, 256, 128) == -INVALID
+    assert f(1, 32, 32, 1000, 256, 96) == -INVALID
+    assert f(1, 32, 2, 1000, 256, 128) == -INVALID     # 16 query heads per KV head
+    assert f(1, 32, 32, 1000, 0, 128) == -INVALID
+
+
+def test_status_word_inside_control_bytes():
+    assert adamas.WS_STATUS_OFFSET + 4 <= adamas.WS_CTRL_BYTES
+    text = open(HEADER).read()
+    assert f"#define ADAMAS_WS_CTRL_BYTES {adamas.WS_CTRL_BYTES}" in text
+    assert f"#define ADAMAS_WS_STATUS_OFFSET {adamas.WS_STATUS_OFFSET}" in text

@@ -231,3 +231,63 @@ def test_decode_deterministic_and_workspace_reuse(ora):
     for n, bud, o, idx in outs[:4]:
         _, _, oidx = ora.decode_step(q, k, v, oc, n, bud)
         assert np.array_equal(idx.cpu().numpy(), oidx)
+
+
+# ------------------------------------------- decode schedules, both forced
+_SCHED_CASES = {
+    "mha-5000-b256": synth.LLAMA2_32K.replace(hq=4, hkv=4, n_ctx=5000, cap=5100, budget=256),
+    "mha-70000-b512": synth.LLAMA2_32K.replace(hq=4, hkv=4, n_ctx=70000, cap=70000, budget=512),
+    "mha-30000-b20000": synth.LLAMA2_32K.replace(hq=2, hkv=2, n_ctx=30000, cap=30000,
+                                                 budget=20000),
+    "mha-1-b64": synth.LLAMA2_32K.replace(hq=4, hkv=4, n_ctx=1, cap=16, budget=64),
+    "gqa-24-8-9001": synth.LLAMA32_GQA_1M.replace(hq=24, hkv=8, n_ctx=9001, cap=9001, budget=128),
+    "gqa-8-1-9001": synth.LLAMA32_GQA_1M.replace(hq=8, hkv=1, n_ctx=9001, cap=9001, budget=300),
+    "f32-d64-batch3": synth.TINY.replace(batch=3, hq=4, hkv=2, n_ctx=3000, cap=3000, budget=100),
+}
+
+
+@pytest.fixture
+def restore_mode():
+    yield
+    adamas.set_decode_mode(adamas.DECODE_AUTO)
+
+
+@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT])
+@pytest.mark.parametrize("case", sorted(_SCHED_CASES))
+def test_decode_schedules(ora, restore_mode, mode, case):
+    w = _SCHED_CASES[case]
+    log(f"decode schedule {mode} {case}")
+    adamas.set_decode_mode(mode)
+    assert adamas.decode_path(w.batch, w.hq, w.hkv, w.n_ctx, w.budget, w.head_dim) == mode
+    lay = synth.make_layer(w, 0, DEV)
+    codes = torch.zeros((w.batch, w.hkv, w.cap, w.head_dim // 4), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    ws = adamas.Workspace(DEV)
+    idx = torch.empty((w.batch, w.hq, w.budget), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, w.n_ctx, w.budget,
+                             idx_out=idx, ws=ws)
+    out_noidx = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, w.n_ctx, w.budget, ws=ws)
+    torch.cuda.synchronize()
+    assert not ws.buf[:adamas.WS_CTRL_BYTES].any(), "control bytes or status word left set"
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    oout, _, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), w.n_ctx, w.budget)
+    assert np.array_equal(idx.cpu().numpy(), oidx), "selection differs"
+    e = rel_err(out, oout)
+    log(f"  rel err {e:.3e}")
+    assert e <= TOL[w.torch_dtype]
+    assert torch.equal(out, out_noidx)
+
+
+def test_decode_schedule_choice(restore_mode):
+    adamas.set_decode_mode(adamas.DECODE_AUTO)
+    # one 256-row batch per head: the last workgroup attends alone
+    assert adamas.decode_path(1, 32, 32, 131072, 256, 128) == adamas.DECODE_LAST_ARRIVAL
+    # 1024 rows per head would need a second launch; 256 workgroups fit the device
+    assert adamas.decode_path(1, 32, 32, 131072, 1024, 128) == adamas.DECODE_GROUP_WAIT
+    # 512 KV heads of chunks do not fit: the last-arrival schedule takes them
+    assert adamas.decode_path(16, 32, 32, 65536, 512, 128) == adamas.DECODE_LAST_ARRIVAL
+    adamas.set_decode_mode(adamas.DECODE_GROUP_WAIT)
+    assert adamas.decode_path(1, 32, 32, 131072, 256, 128) == adamas.DECODE_GROUP_WAIT
+    adamas.set_decode_mode(adamas.DECODE_GROUP_WAIT)
+    with pytest.raises(adamas.AdamasError):
+        adamas.decode_path(16, 32, 32, 65536, 512, 128)
