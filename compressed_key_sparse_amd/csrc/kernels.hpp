@@ -18,6 +18,10 @@ constexpr int kEncodeThreads = 256;
 constexpr int kScoreThreads = 256;
 constexpr int kSelectThreads = 1024;
 constexpr int kDecodeThreads = 1024;  // one workgroup of 16 wavefronts per CU
+// 16-byte code loads per thread in flight in the decode scans: 64 KiB per
+// workgroup per batch streams faster than 128 or 256 KiB (fewer requests
+// queued per CU at the same delivered bandwidth)
+constexpr int kDecodeScanDepth = 4;
 constexpr int kAttendThreads = 1024;
 constexpr int kAttendRowsPerSlot = 4;  // rows a 16-lane slot holds in flight
 constexpr int kAttendRowsPerBatch = (kAttendThreads / 16) * kAttendRowsPerSlot;  // 256
@@ -492,7 +496,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   const int64_t t0 = (int64_t)c * chunk;
   const int valid = (int)min((int64_t)chunk, n_ctx - t0);
   const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
-  scan_chunk<D, G, NT, 8>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
+  scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
     sdist[g * chunk + tok] = (uint16_t)d;
     atomicAdd(&shist[g * NBP + d], 1u);
   });
@@ -585,7 +589,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   const int64_t t0 = (int64_t)c * chunk;
   const int valid = (int)min((int64_t)chunk, n_ctx - t0);
   const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
-  scan_chunk<D, G, NT, 8>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
+  scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
     sdist[g * chunk + tok] = (uint16_t)d;
     atomicAdd(&shist[g * NBP + d], 1u);
   });
