@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #define ADM_DEV __device__ __forceinline__
 
 namespace adm {
@@ -142,6 +144,56 @@ ADM_DEV uint4 load_stream(const uint4* p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// ------------------------------------------------------- lane exchanges
+// x from lane (lane ^ M) of the wavefront, without the LDS crossbar:
+//   M = 1, 2: DPP quad permutations [1,0,3,2], [2,3,0,1];
+//   M = 4:    DPP half-row mirror (l ^ 7 within 8 lanes), then quad [3,2,1,0] (l ^ 3);
+//   M = 8:    DPP rotation by 8 within the 16-lane row;
+//   M = 16, 32: v_permlane16_swap / v_permlane32_swap of x with itself, which
+//   leaves x in one result and the partner lane's x in the other.
+template <int CTRL>
+ADM_DEV uint32_t dpp_move(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int M>
+ADM_DEV uint32_t lane_xor_u32(uint32_t v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane mask");
+  if constexpr (M == 1) return dpp_move<0xB1>(v);
+  if constexpr (M == 2) return dpp_move<0x4E>(v);
+  if constexpr (M == 4) return dpp_move<0x1B>(dpp_move<0x141>(v));
+  if constexpr (M == 8) return dpp_move<0x128>(v);
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return r[0] == v ? r[1] : r[0];
+  }
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] == v ? r[1] : r[0];
+  }
+}
+template <int M>
+ADM_DEV float lane_xor(float x) {
+  return __uint_as_float(lane_xor_u32<M>(__float_as_uint(x)));
+}
+// x + x(lane ^ M) and max(x, x(lane ^ M)) for M = 16, 32: the two swap
+// results are x and the partner's x in some order, which neither needs.
+template <int M>
+ADM_DEV float xor_sum(float x) {
+  static_assert(M == 16 || M == 32, "row exchanges only");
+  const uint32_t v = __float_as_uint(x);
+  const auto r = (M == 16) ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                           : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int M>
+ADM_DEV float xor_max(float x) {
+  static_assert(M == 16 || M == 32, "row exchanges only");
+  const uint32_t v = __float_as_uint(x);
+  const auto r = (M == 16) ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                           : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---------------------------------------------------------- §2.1 + §2.2
 // One wavefront rotates, buckets and packs one vector of D dims.
 // Lane l holds elements l*E .. l*E+E-1 (E = D/64).  The fast Walsh-Hadamard
@@ -173,20 +225,32 @@ ADM_DEV uint32_t wave_encode(float (&y)[D / 64]) {
       }
     }
   }
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
+  // butterflies across lanes: the lane with bit m clear keeps a + b, the
+  // other a - b (a = the lower lane's value)
+  auto stage = [&](auto mtag) {
+    constexpr int m = decltype(mtag)::value;
     const bool upper = (lane & m) != 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      float p = __shfl_xor(y[e], m);
+      const float p = lane_xor<m>(y[e]);
       y[e] = upper ? (p - y[e]) : (y[e] + p);
     }
-  }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
+  stage(std::integral_constant<int, 16>{});
+  stage(std::integral_constant<int, 32>{});
   float a = fabsf(y[0]);
 #pragma unroll
   for (int e = 1; e < E; ++e) a = fmaxf(a, fabsf(y[e]));
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) a = fmaxf(a, __shfl_xor(a, m));
+  a = fmaxf(a, lane_xor<1>(a));
+  a = fmaxf(a, lane_xor<2>(a));
+  a = fmaxf(a, lane_xor<4>(a));
+  a = fmaxf(a, lane_xor<8>(a));
+  a = xor_max<16>(a);
+  a = xor_max<32>(a);
   const float t0 = -0.5f * a;
   const float t2 = 0.5f * a;
   uint32_t bits = 0;
@@ -199,8 +263,10 @@ ADM_DEV uint32_t wave_encode(float (&y)[D / 64]) {
     bits |= c << pos;
   }
   constexpr int kLanesPerWord = 16 / E;
-#pragma unroll
-  for (int m = 1; m < kLanesPerWord; m <<= 1) bits |= __shfl_xor(bits, m);
+  bits |= lane_xor_u32<1>(bits);
+  bits |= lane_xor_u32<2>(bits);
+  bits |= lane_xor_u32<4>(bits);
+  if constexpr (kLanesPerWord == 16) bits |= lane_xor_u32<8>(bits);
   return (lane % kLanesPerWord) == 0 ? bits : 0u;
 }
 

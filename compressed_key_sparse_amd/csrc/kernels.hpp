@@ -274,8 +274,8 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
     }
     // batch maximum: over the wavefront's 4 slots (lanes ^16, ^32), then the
     // wavefront maxima through LDS
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = xor_max<16>(mloc);
+    mloc = xor_max<32>(mloc);
     if (lane == 0) s_score[wid] = mloc;
     lds_sync();
     float mb = -INFINITY;
@@ -298,12 +298,9 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
     m_run = mn;
   }
   // every slot shares m_run: sum l and o over slots (lanes ^16, ^32), then waves
+  l_run = xor_sum<32>(xor_sum<16>(l_run));
 #pragma unroll
-  for (int m = 16; m < kWave; m <<= 1) {
-    l_run += __shfl_xor(l_run, m);
-#pragma unroll
-    for (int e = 0; e < EL; ++e) o[e] += __shfl_xor(o[e], m);
-  }
+  for (int e = 0; e < EL; ++e) o[e] = xor_sum<32>(xor_sum<16>(o[e]));
   float* mine = s_part + wid * PW;
   if (lane < 16) {
     if (lane == 0) mine[1] = l_run;
