@@ -12,6 +12,7 @@
 #include <type_traits>
 
 #define ADM_DEV __device__ __forceinline__
+#define ADM_HOST_DEV __host__ __device__
 
 namespace adm {
 
@@ -427,8 +428,12 @@ ADM_DEV Threshold find_threshold(const uint32_t* hist, int nbins, uint32_t K, ui
   if (lane == kWave - 1 && wid < nwb) s_tmp[kTmpWaveSums + wid] = incl_w;
   lds_sync();
   if (wid < nwb) {
-    uint32_t pre = 0;
-    for (int w = 0; w < wid; ++w) pre += s_tmp[kTmpWaveSums + w];
+    uint32_t pre = 0;  // all wave sums read at once, the earlier ones added
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = s_tmp[kTmpWaveSums + w];
+      pre += w < wid ? x : 0u;
+    }
     const uint32_t incl = pre + incl_w, excl = incl - h;
     if (excl < K && K <= incl) {
       s_tmp[kTmpThrT] = threadIdx.x;
@@ -467,9 +472,11 @@ ADM_DEV GroupThreshold find_group_threshold(uint32_t tot, uint32_t bef, int nbin
   lds_sync();
   if (wid < nwb) {
     uint32_t pt = 0, pb = 0;
-    for (int w = 0; w < wid; ++w) {
-      pt += s_sums[w];
-      pb += s_sums[16 + w];
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+      const uint32_t xt = s_sums[w], xb = s_sums[16 + w];
+      pt += w < wid ? xt : 0u;
+      pb += w < wid ? xb : 0u;
     }
     const uint32_t incl = pt + it, excl = incl - tot;
     if (excl < K && K <= incl) {
@@ -491,12 +498,13 @@ ADM_DEV GroupThreshold find_group_threshold(uint32_t tot, uint32_t bef, int nbin
 // kept.  Thread j owns tokens [16j, 16j+16), read once with 16-byte LDS loads
 // (threads past the chunk own nothing).
 constexpr int kCompactTpt = 16;
-template <int NT, class Emit>
+template <int NT, class Emit, int TPT = kCompactTpt>
 ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t quota,
                                uint32_t* s_tmp, Emit&& emit) {
-  constexpr int TPT = kCompactTpt;
+  static_assert(TPT % 8 == 0 && TPT <= 32, "whole 16-byte reads, one 32-bit mask");
   const int t0 = threadIdx.x * TPT;
   uint32_t ltm = 0, eqm = 0;  // bit i: token t0+i is below / at the threshold
+  uint32_t dw[TPT / 2] = {};  // the thread's distances, two per word
   if (t0 < valid) {
     // two distances per 32-bit word (both <= 3*D < 2^15): with packed 16-bit
     // subtractions, bit 15 of (t-1-d) is set iff d >= t and of (t-d) iff d > t
@@ -510,6 +518,7 @@ ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        dw[4 * v8 + i] = ws[i];
         const s16x2 dv = __builtin_bit_cast(s16x2, ws[i]);
         const uint32_t a = __builtin_bit_cast(uint32_t, (s16x2)(tm1 - dv));
         const uint32_t b = __builtin_bit_cast(uint32_t, (s16x2)(tt - dv));
@@ -519,7 +528,8 @@ ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t
       }
     }
     const int nv = valid - t0;  // tokens of this thread inside the chunk
-    const uint32_t vmask = nv >= TPT ? 0xffffu : ((1u << nv) - 1u);
+    constexpr uint32_t kAll = TPT == 32 ? 0xffffffffu : ((1u << TPT) - 1u);
+    const uint32_t vmask = nv >= TPT ? kAll : ((1u << nv) - 1u);
     ltm = ~ge & vmask;
     eqm = ge & ~gt & vmask;
   }
@@ -532,7 +542,10 @@ ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t
     const int i = __ffs(m) - 1;
     const uint32_t tok = (uint32_t)(t0 + i);
     if ((ltm >> i) & 1u) {
-      emit(ltb + (eqb < quota ? eqb : quota), tok, (uint32_t)sdist[tok]);
+      uint32_t word = dw[0];
+#pragma unroll
+      for (int k = 1; k < TPT / 2; ++k) word = (i >> 1) == k ? dw[k] : word;
+      emit(ltb + (eqb < quota ? eqb : quota), tok, (word >> (16 * (i & 1))) & 0xffffu);
       ++ltb;
     } else {
       if (eqb < quota) emit(ltb + eqb, tok, (uint32_t)t);
@@ -546,14 +559,15 @@ ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t
 // chunk_collect into out[] (LDS) as (D << 16) | token; entries [kept, pad_to)
 // get the sentinel 0xFFFFFFFF.  on_kept(token, D) is called for every kept
 // token.
-template <int NT, class OnKept>
+template <int NT, int TPT = kCompactTpt, class OnKept>
 ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint32_t quota,
                            uint32_t* out, int kept, int pad_to, uint32_t* s_tmp,
                            OnKept&& on_kept) {
-  chunk_collect<NT>(sdist, valid, thr.t, quota, s_tmp, [&](uint32_t pos, uint32_t t, uint32_t d) {
+  auto emit = [&](uint32_t pos, uint32_t t, uint32_t d) {
     out[pos] = (d << 16) | t;
     on_kept(t, d);
-  });
+  };
+  chunk_collect<NT, decltype(emit)&, TPT>(sdist, valid, thr.t, quota, s_tmp, emit);
   for (int j = kept + (int)threadIdx.x; j < pad_to; j += NT) out[j] = 0xFFFFFFFFu;
 }
 
@@ -567,7 +581,14 @@ ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint
 template <int NT>
 ADM_DEV void final_select_tiled(const uint32_t* cand, int M, int kpad_log2, int chunk, int nbins,
                                 int bsel, int budget, int32_t* sidx, int32_t* idx,
-                                uint32_t* scand, int mcap, uint32_t* shist, uint32_t* s_tmp);
+                                uint32_t* scand, int mcap, uint32_t* shist, uint32_t* s_tmp,
+                                const int32_t* slot_start);
+
+// First token of candidate slot `slot`: slot * chunk for fixed chunks, else
+// from slot_start[] (LDS) when the slots cover intervals of varying length.
+ADM_DEV int32_t slot_token0(const int32_t* slot_start, int slot, int chunk) {
+  return slot_start ? slot_start[slot] : slot * chunk;
+}
 
 // Up to 4*NT candidates: each thread keeps four consecutive entries in
 // registers from one 16-byte coherent load; histogram, threshold and ordered
@@ -575,10 +596,10 @@ ADM_DEV void final_select_tiled(const uint32_t* cand, int M, int kpad_log2, int 
 template <int NT>
 ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk, int nbins, int bsel,
                           int budget, int32_t* sidx, int32_t* idx, uint32_t* scand, int mcap,
-                          uint32_t* shist, uint32_t* s_tmp) {
+                          uint32_t* shist, uint32_t* s_tmp, const int32_t* slot_start = nullptr) {
   if (M > 4 * NT) {
     final_select_tiled<NT>(cand, M, kpad_log2, chunk, nbins, bsel, budget, sidx, idx, scand,
-                           mcap, shist, s_tmp);
+                           mcap, shist, s_tmp, slot_start);
     return;
   }
   const int i0 = 4 * (int)threadIdx.x;
@@ -619,7 +640,8 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
       ++eqb;
     }
     if (pos >= 0) {
-      const int32_t tok = ((i0 + j) >> kpad_log2) * chunk + (int32_t)(v[j] & 0xffffu);
+      const int32_t tok =
+          slot_token0(slot_start, (i0 + j) >> kpad_log2, chunk) + (int32_t)(v[j] & 0xffffu);
       if (sidx) sidx[pos] = tok;
       if (idx) idx[pos] = tok;
     }
@@ -632,7 +654,8 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
 template <int NT>
 ADM_DEV void final_select_tiled(const uint32_t* cand, int M, int kpad_log2, int chunk, int nbins,
                                 int bsel, int budget, int32_t* sidx, int32_t* idx,
-                                uint32_t* scand, int mcap, uint32_t* shist, uint32_t* s_tmp) {
+                                uint32_t* scand, int mcap, uint32_t* shist, uint32_t* s_tmp,
+                                const int32_t* slot_start) {
   const bool resident = M <= mcap;
   for (int i = threadIdx.x; i < nbins; i += NT) shist[i] = 0;
   for (int base = 0; base < M; base += mcap) {
@@ -684,7 +707,8 @@ ADM_DEV void final_select_tiled(const uint32_t* cand, int M, int kpad_log2, int 
           ++eqb;
         }
         if (pos >= 0) {
-          const int32_t tok = ((base + j) >> kpad_log2) * chunk + (int32_t)(v & 0xffffu);
+          const int32_t tok =
+              slot_token0(slot_start, (base + j) >> kpad_log2, chunk) + (int32_t)(v & 0xffffu);
           if (sidx) sidx[pos] = tok;
           if (idx) idx[pos] = tok;
         }
