@@ -196,6 +196,7 @@ def main():
 
     # -- graph pass: the 32-layer step captured once and replayed K times
     graph_ms = None
+    step_times = []
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
@@ -205,14 +206,32 @@ def main():
                 g.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
         g0.record(stream)
         with torch.cuda.stream(stream):
-            for _ in range(K):
+            gev[0].record(stream)
+            for i in range(K):
                 g.replay()
+                gev[i + 1].record(stream)
         g1.record(stream)
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / K
+        step_times = [gev[i].elapsed_time(gev[i + 1]) for i in range(K)]
     ms = graph_ms if graph_ms is not None else eager_ms
+
+    # what plain streaming reads reach on this device (4 GiB, beyond the
+    # last-level cache), with the decode scan's own load instructions
+    sr = torch.ones(1 << 30, dtype=torch.int32, device=dev)
+    sink = adamas.stream_read(sr)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(5):
+        adamas.stream_read(sr, sink)
+    s1.record()
+    torch.cuda.synchronize()
+    stream_gbs = sr.numel() * 4 * 5 / (s0.elapsed_time(s1) * 1e-3) / 1e9
+    del sr, sink
 
     if args.copy_calibration:
         # a plain conversion kernel of known traffic (reads 1 GiB of fp32,
@@ -267,6 +286,13 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": per_layer, "launch_us": round(avg_launch_us, 3),
                      "eager_event_launch_us": round(launch_us, 3)},
+        "step_ms": ({"p10": round(float(np.percentile(step_times, 10)), 4),
+                     "p50": round(float(np.percentile(step_times, 50)), 4),
+                     "p90": round(float(np.percentile(step_times, 90)), 4)}
+                    if step_times else None),
+        "stream_read": {"kernel": "adamas_stream_read over 4 GiB", "gbs": round(stream_gbs, 1),
+                        "frac_of_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
+                        "decode_over_stream": round(achieved / stream_gbs, 4)},
         "needle_recall": round(recall, 4),
         "cpu_baseline": cpu,
     }

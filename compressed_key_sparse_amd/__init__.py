@@ -71,6 +71,10 @@ def load():
     lib.adamas_status_string.argtypes = [i32]
     lib.adamas_status_string.restype = ctypes.c_char_p
     lib.adamas_version.restype = i32
+    lib.adamas_stream_read.argtypes = [P, sz, P, P]
+    lib.adamas_stream_read.restype = i32
+    lib.adamas_stream_read_blocks.argtypes = [sz]
+    lib.adamas_stream_read_blocks.restype = sz
     lib.adamas_set_decode_mode.argtypes = [i32]
     lib.adamas_decode_path.argtypes = [i32, i32, i32, i64, i32, i32]
     for fn in ("adamas_set_decode_mode", "adamas_decode_path"):
@@ -224,6 +228,17 @@ def sparse_attend(q, k, v, idx, scale: float = 0.0, out=None, ws: Workspace | No
                                      _dev_ptr(buf, "ws"), buf.numel(), _stream(q, stream))
     _check(st, "adamas_sparse_attend")
     return out
+
+
+def stream_read(x: torch.Tensor, sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Reference streaming read of x's bytes (adamas_stream_read); returns the sink."""
+    nbytes = x.numel() * x.element_size()
+    nblk = int(load().adamas_stream_read_blocks(nbytes))
+    if sink is None:
+        sink = torch.empty(nblk, dtype=torch.int32, device=x.device)
+    _check(load().adamas_stream_read(_dev_ptr(x, "x"), nbytes, _dev_ptr(sink, "sink"),
+                                     _stream(x, stream)), "adamas_stream_read")
+    return sink
 
 
 def set_decode_mode(mode: int) -> None:

@@ -23,6 +23,7 @@ constexpr size_t kCtrlAttend = 32768;      // u32 counters of attention rows
 constexpr int kMaxBudget = 1 << 20;
 constexpr size_t kLdsLimit = 64 * 1024;    // per-workgroup LDS used by any kernel here
 constexpr int kMaxCandTile = 8192;         // candidate entries staged in LDS at once
+constexpr size_t kStreamBlocks = 1024;     // adamas_stream_read: four slices per compute unit
 
 bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -526,6 +527,24 @@ int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int he
   if (plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, capacity).ok)
     return ADAMAS_DECODE_GROUP_WAIT;
   return mode == ADAMAS_DECODE_GROUP_WAIT ? -ADAMAS_ERR_UNSUPPORTED : ADAMAS_DECODE_LAST_ARRIVAL;
+}
+
+size_t adamas_stream_read_blocks(size_t bytes) {
+  const size_t units = bytes / 16;
+  const size_t per = (size_t)kStreamThreads * kDecodeScanDepth;
+  const size_t want = (units + per - 1) / per;
+  return want < kStreamBlocks ? want : kStreamBlocks;
+}
+
+int adamas_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!aligned16(src) || sink == nullptr || bytes == 0 || bytes % 16 != 0)
+    return ADAMAS_ERR_INVALID;
+  const int64_t units = (int64_t)(bytes / 16);
+  const int64_t blocks = (int64_t)adamas_stream_read_blocks(bytes);
+  const int64_t per_block = (units + blocks - 1) / blocks;
+  k_stream_read<<<(unsigned)blocks, kStreamThreads, 0, stream>>>(
+      static_cast<const uint4*>(src), units, per_block, sink);
+  return launch_status();
 }
 
 }  // extern "C"

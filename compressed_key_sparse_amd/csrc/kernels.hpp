@@ -696,4 +696,41 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   }
 }
 
+// ---------------------------------------------------------- reference read
+// adamas_stream_read: each workgroup streams one contiguous slice of the
+// buffer with the decode scan's loads (16 bytes per thread, kDecodeScanDepth
+// in flight, non-temporal) and writes the XOR of what it read, so the reads
+// cannot be dropped.
+constexpr int kStreamThreads = 1024;
+__global__ __launch_bounds__(kStreamThreads) void k_stream_read(const uint4* __restrict__ src,
+                                                                int64_t units, int64_t per_block,
+                                                                uint32_t* __restrict__ sink) {
+  constexpr int U = kDecodeScanDepth;
+  const int64_t u0 = (int64_t)blockIdx.x * per_block;
+  const int64_t u1 = min(u0 + per_block, units);
+  uint32_t acc = 0;
+  for (int64_t base = u0; base < u1; base += (int64_t)kStreamThreads * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t u = base + (int64_t)j * kStreamThreads + threadIdx.x;
+      w[j] = load_stream(src + (u < u1 ? u : u1 - 1));
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t u = base + (int64_t)j * kStreamThreads + threadIdx.x;
+      if (u < u1) acc ^= w[j].x ^ w[j].y ^ w[j].z ^ w[j].w;  // clamped loads repeat a unit
+    }
+  }
+  __shared__ uint32_t s_acc[kStreamThreads / kWave];
+  for (int m = 1; m < kWave; m <<= 1) acc ^= __shfl_xor(acc, m);
+  if ((threadIdx.x & (kWave - 1)) == 0) s_acc[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t x = 0;
+    for (int i = 0; i < kStreamThreads / kWave; ++i) x ^= s_acc[i];
+    sink[blockIdx.x] = x;
+  }
+}
+
 }  // namespace adm

@@ -201,6 +201,21 @@ int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int he
 size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx,
                               int budget, int head_dim);
 
+/*
+ * Reference streaming read, not a step of the method: reads `bytes` (a
+ * multiple of 16) at `src` (16-byte aligned) once, with the 16-byte
+ * non-temporal loads of the decode scan, each of
+ * adamas_stream_read_blocks(bytes) workgroups taking one contiguous slice,
+ * and writes one XOR word per workgroup to sink[] so the reads stay.  Timing
+ * it gives the bandwidth plain reads reach on the device, the figure the
+ * decode step's achieved bandwidth is read against.  Returns
+ * ADAMAS_ERR_INVALID for a null sink, misaligned src or a bad size.
+ */
+int adamas_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
+/* Workgroups (sink words) adamas_stream_read uses for `bytes`. */
+size_t adamas_stream_read_blocks(size_t bytes);
+
 /* Static, human-readable text for a status code. */
 const char *adamas_status_string(int status);
 

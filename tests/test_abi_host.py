@@ -158,3 +158,13 @@ def test_status_word_inside_control_bytes():
     text = open(HEADER).read()
     assert f"#define ADAMAS_WS_CTRL_BYTES {adamas.WS_CTRL_BYTES}" in text
     assert f"#define ADAMAS_WS_STATUS_OFFSET {adamas.WS_STATUS_OFFSET}" in text
+
+
+def test_stream_read_validation(lib):
+    f = lib.adamas_stream_read
+    assert f(MIS, 64, A, None) == INVALID
+    assert f(A, 0, A, None) == INVALID
+    assert f(A, 40, A, None) == INVALID          # not a multiple of 16
+    assert f(A, 64, None, None) == INVALID
+    assert lib.adamas_stream_read_blocks(16) == 1
+    assert lib.adamas_stream_read_blocks(1 << 40) == 1024

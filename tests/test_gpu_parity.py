@@ -291,3 +291,15 @@ def test_decode_schedule_choice(restore_mode):
     adamas.set_decode_mode(adamas.DECODE_GROUP_WAIT)
     with pytest.raises(adamas.AdamasError):
         adamas.decode_path(16, 32, 32, 65536, 512, 128)
+
+
+def test_stream_read_reads_every_byte():
+    # the reference read's sink words XOR to the XOR of the whole buffer
+    g = torch.Generator(device=DEV).manual_seed(7)
+    for n in (4, 1000, (1 << 22) + 12):
+        x = torch.randint(-2**31, 2**31 - 1, (n,), generator=g, device=DEV, dtype=torch.int32)
+        sink = adamas.stream_read(x)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(x.cpu().numpy().view(np.uint32))
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == want, n
