@@ -70,6 +70,31 @@ ADM_DEV void load_elems(const void* base, bool is_bf16, int64_t i, float (&out)[
   }
 }
 
+// The same elements as raw bits (issue the load now, widen later with
+// widen_elems): E * 2 or E * 4 bytes in a uint2.
+template <int E, bool BF>
+ADM_DEV uint2 load_elems_raw(const void* base, int64_t i) {
+  if constexpr (BF) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + i;
+    if constexpr (E == 2) return make_uint2(*reinterpret_cast<const uint32_t*>(p), 0u);
+    else return make_uint2(*p, 0u);
+  } else {
+    const float* p = static_cast<const float*>(base) + i;
+    if constexpr (E == 2) return *reinterpret_cast<const uint2*>(p);
+    else return make_uint2(__float_as_uint(*p), 0u);
+  }
+}
+template <int E, bool BF>
+ADM_DEV void widen_elems(uint2 raw, float (&out)[E]) {
+  if constexpr (BF) {
+    out[0] = bf16_to_f32(raw.x & 0xffffu);
+    if constexpr (E == 2) out[1] = bf16_to_f32(raw.x >> 16);
+  } else {
+    out[0] = __uint_as_float(raw.x);
+    if constexpr (E == 2) out[1] = __uint_as_float(raw.y);
+  }
+}
+
 // Data handed from one workgroup to another within a launch (candidate
 // lists, attention partials) is written and read with device-scope coherent
 // accesses (the sc1 cache policy): they are coherent across the XCDs'

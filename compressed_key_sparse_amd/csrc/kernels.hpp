@@ -74,42 +74,61 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
 // Codes are read as 16-byte units (64 codes) with non-temporal loads, U per
 // thread in flight; at D = 128 a token is two units held by a lane pair whose
 // partial sums are added with a DPP swap.
+template <int NT, int U>
+ADM_DEV void scan_load(const uint4* __restrict__ src, int units, int base, uint4 (&w)[U]) {
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int u = base + j * NT + (int)threadIdx.x;
+    w[j] = load_stream(src + (u < units ? u : units - 1));  // clamped: always in bounds
+  }
+}
+
+template <int D, int G, int NT, int U, class Sink>
+ADM_DEV void scan_units(const uint4 (&w)[U], int base, int units, const QPlanes (&qp)[G],
+                        Sink&& sink) {
+  constexpr int kUnitsPerToken = D / 64;
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int u = base + j * NT + (int)threadIdx.x;
+    const uint32_t p0 = therm_p(w[j].x), p1 = therm_p(w[j].y);
+    const uint32_t p2 = therm_p(w[j].z), p3 = therm_p(w[j].w);
+    const uint32_t t0 = therm_t(w[j].x, w[j].y), t1 = therm_t(w[j].z, w[j].w);
+    uint32_t dg[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      uint32_t s = __popc(p0 ^ qp[g].p[0]);
+      s += __popc(p1 ^ qp[g].p[1]);
+      s += __popc(p2 ^ qp[g].p[2]);
+      s += __popc(p3 ^ qp[g].p[3]);
+      s += __popc(t0 ^ qp[g].t[0]);
+      s += __popc(t1 ^ qp[g].t[1]);
+      if constexpr (kUnitsPerToken == 2) s += swap_pair(s);
+      dg[g] = s;
+    }
+    if (u < units && (kUnitsPerToken == 1 || (threadIdx.x & 1) == 0)) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) sink(g, u / kUnitsPerToken, dg[g]);
+    }
+  }
+}
+
+// Whole chunk; with `first` the caller has already issued the loads of the
+// first batch (units [0, NT*U)) into it.
 template <int D, int G, int NT, int U, class Sink>
 ADM_DEV void scan_chunk(const uint8_t* __restrict__ kbase, int valid, const QPlanes (&qp)[G],
-                        Sink&& sink) {
+                        Sink&& sink, const uint4 (*first)[U] = nullptr) {
   constexpr int kUnitsPerToken = D / 64;
   const int units = valid * kUnitsPerToken;
   const uint4* __restrict__ src = reinterpret_cast<const uint4*>(kbase);
-  for (int base = 0; base < units; base += NT * U) {
+  int base = 0;
+  if (first != nullptr) {
+    scan_units<D, G, NT, U>(*first, 0, units, qp, sink);
+    base = NT * U;
+  }
+  for (; base < units; base += NT * U) {
     uint4 w[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int u = base + j * NT + (int)threadIdx.x;
-      w[j] = load_stream(src + (u < units ? u : units - 1));  // clamped: always in bounds
-    }
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int u = base + j * NT + (int)threadIdx.x;
-      const uint32_t p0 = therm_p(w[j].x), p1 = therm_p(w[j].y);
-      const uint32_t p2 = therm_p(w[j].z), p3 = therm_p(w[j].w);
-      const uint32_t t0 = therm_t(w[j].x, w[j].y), t1 = therm_t(w[j].z, w[j].w);
-      uint32_t dg[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        uint32_t s = __popc(p0 ^ qp[g].p[0]);
-        s += __popc(p1 ^ qp[g].p[1]);
-        s += __popc(p2 ^ qp[g].p[2]);
-        s += __popc(p3 ^ qp[g].p[3]);
-        s += __popc(t0 ^ qp[g].t[0]);
-        s += __popc(t1 ^ qp[g].t[1]);
-        if constexpr (kUnitsPerToken == 2) s += swap_pair(s);
-        dg[g] = s;
-      }
-      if (u < units && (kUnitsPerToken == 1 || (threadIdx.x & 1) == 0)) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) sink(g, u / kUnitsPerToken, dg[g]);
-      }
-    }
+    scan_load<NT, U>(src, units, base, w);
+    scan_units<D, G, NT, U>(w, base, units, qp, sink);
   }
 }
 
@@ -481,22 +500,32 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   const int kpad = 1 << kpad_log2;
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   for (int i = threadIdx.x; i < G * NBP; i += NT) shist[i] = 0;
-  for (int g = wid; g < G; g += NW) {
+  // the query (wavefront g holds head g, G <= NW), then the first batch of
+  // codes, then the query's encoding while the codes are in flight
+  static_assert(G <= NW, "one wavefront per query head");
+  const int gq = wid < G ? wid : G - 1;  // spare wavefronts load a copy: no branch
+  const uint2 qraw =
+      load_elems_raw<E, BF>(q, ((int64_t)b * Hq + (int64_t)hkv * G + gq) * D + lane * E);
+  const int64_t t0 = (int64_t)c * chunk;
+  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
+  const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
+  uint4 first[kDecodeScanDepth];
+  scan_load<NT, kDecodeScanDepth>(reinterpret_cast<const uint4*>(kbase), valid * (D / 64), 0,
+                                  first);
+  __builtin_amdgcn_sched_barrier(0);  // keep the code loads ahead of the wait for q
+  if (wid < G) {
     float y[E];
-    load_elems<E>(q, BF, ((int64_t)b * Hq + (int64_t)hkv * G + g) * D + lane * E, y);
+    widen_elems<E, BF>(qraw, y);
     const uint32_t word = wave_encode<D>(y);
-    if (lane % kLanesPerWord == 0) sq[g * W + lane / kLanesPerWord] = word;
+    if (lane % kLanesPerWord == 0) sq[wid * W + lane / kLanesPerWord] = word;
   }
   lds_sync();
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
-  const int64_t t0 = (int64_t)c * chunk;
-  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
-  const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
   scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
     sdist[g * chunk + tok] = (uint16_t)d;
     atomicAdd(&shist[g * NBP + d], 1u);
-  });
+  }, &first);
   lds_sync();
   const int kc = min(budget, valid);
   for (int g = 0; g < G; ++g) {
@@ -574,22 +603,30 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   const int64_t row0 = (int64_t)b * Hq + (int64_t)hkv * G;
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   for (int i = threadIdx.x; i < G * NBP; i += NT) shist[i] = 0;
-  for (int g = wid; g < G; g += NW) {
+  // as k_decode: query, first batch of codes, then the query's encoding
+  static_assert(G <= NW, "one wavefront per query head");
+  const int gq = wid < G ? wid : G - 1;
+  const uint2 qraw = load_elems_raw<E, BF>(q, (row0 + gq) * D + lane * E);
+  const int64_t t0 = (int64_t)c * chunk;
+  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
+  const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
+  uint4 first[kDecodeScanDepth];
+  scan_load<NT, kDecodeScanDepth>(reinterpret_cast<const uint4*>(kbase), valid * (D / 64), 0,
+                                  first);
+  __builtin_amdgcn_sched_barrier(0);
+  if (wid < G) {
     float y[E];
-    load_elems<E>(q, BF, (row0 + g) * D + lane * E, y);
+    widen_elems<E, BF>(qraw, y);
     const uint32_t word = wave_encode<D>(y);
-    if (lane % kLanesPerWord == 0) sq[g * W + lane / kLanesPerWord] = word;
+    if (lane % kLanesPerWord == 0) sq[wid * W + lane / kLanesPerWord] = word;
   }
   lds_sync();
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
-  const int64_t t0 = (int64_t)c * chunk;
-  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
-  const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
   scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
     sdist[g * chunk + tok] = (uint16_t)d;
     atomicAdd(&shist[g * NBP + d], 1u);
-  });
+  }, &first);
   lds_sync();
 
   // publish this chunk's histograms as u16 rows (counts <= chunk < 2^16)
