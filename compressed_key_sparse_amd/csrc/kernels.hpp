@@ -246,10 +246,11 @@ ADM_DEV float slice_dot(const RowRaw<D, BF>& q, const RowRaw<D, BF>& k) {
 
 // Gather attention over nrows selected rows of one head.  Rows go in
 // batches of NS*RB (a 16-lane slot holds RB rows' K and V, every lane D/16
-// dimensions).  Per batch: scores (log2 domain) to LDS, one batch maximum,
-// then weights and the weighted V sum without per-row rescaling; batches
-// merge by log-sum-exp.  On return s_res[0] = m, s_res[1] = l,
-// s_res[2 + t] = o_t.  s_part holds NW*(2+D) floats plus NS*RB scores.
+// dimensions).  Each wavefront keeps its own running maximum (shared by its
+// 4 slots through lane exchanges, no workgroup barrier per batch), weights
+// and a weighted V sum; at the end the NW wavefront partials (m, l, o) are
+// merged by log-sum-exp.  On return s_res[0] = m, s_res[1] = l,
+// s_res[2 + t] = o_t.  s_part holds NW*(2+D) floats plus NT/16 spare.
 template <int D, bool BF, int NT>
 ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
                          const void* __restrict__ v, int64_t qoff, int64_t kvrow0, int64_t cap,
@@ -260,7 +261,6 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
   constexpr int RB = BF ? kAttendRowsPerSlot : kAttendRowsPerSlot / 2;
   const int l16 = threadIdx.x & 15, slot = threadIdx.x >> 4;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-  float* s_score = s_part + NW * PW;  // NS*RB scores of the current batch
   RowRaw<D, BF> qr;
   qr.load(q, qoff + l16 * EL);
   float m_run = -INFINITY, l_run = 0.0f;
@@ -291,17 +291,9 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
       if (tok[j] < 0) sc[j] = -INFINITY;
       mloc = fmaxf(mloc, sc[j]);
     }
-    // batch maximum: over the wavefront's 4 slots (lanes ^16, ^32), then the
-    // wavefront maxima through LDS
-    mloc = xor_max<16>(mloc);
-    mloc = xor_max<32>(mloc);
-    if (lane == 0) s_score[wid] = mloc;
-    lds_sync();
-    float mb = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) mb = fmaxf(mb, s_score[i]);
-    lds_sync();
-    if (mb == -INFINITY) continue;  // nothing valid in this batch (uniform)
+    // the wavefront's maximum over its 4 slots (lanes ^16, ^32)
+    const float mb = xor_max<32>(xor_max<16>(mloc));
+    if (mb == -INFINITY) continue;  // nothing valid for this wavefront (uniform in it)
     const float mn = fmaxf(m_run, mb);
     const float corr = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - mn);
     l_run *= corr;
@@ -322,20 +314,29 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
   for (int e = 0; e < EL; ++e) o[e] = xor_sum<32>(xor_sum<16>(o[e]));
   float* mine = s_part + wid * PW;
   if (lane < 16) {
-    if (lane == 0) mine[1] = l_run;
+    if (lane == 0) {
+      mine[0] = m_run;
+      mine[1] = l_run;
+    }
 #pragma unroll
     for (int e = 0; e < EL; ++e) mine[2 + l16 * EL + e] = o[e];
   }
   lds_sync();
   if (threadIdx.x < D) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_part[w * PW]);
     float L = 0.0f, O = 0.0f;
+#pragma unroll
     for (int w = 0; w < NW; ++w) {
-      L += s_part[w * PW + 1];
-      O += s_part[w * PW + 2 + threadIdx.x];
+      const float mw = s_part[w * PW];
+      const float a = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+      L += a * s_part[w * PW + 1];
+      O += a * s_part[w * PW + 2 + threadIdx.x];
     }
     s_res[2 + threadIdx.x] = O;
     if (threadIdx.x == 0) {
-      s_res[0] = m_run;
+      s_res[0] = M;
       s_res[1] = L;
     }
   }
