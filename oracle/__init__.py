@@ -14,7 +14,8 @@ refer to the ADAMAS article (www.lnwmold.com/news/826806) by section:
 Parity status per function (what pins it is listed in the test-suite):
   fwht / encode            pinned (closed forms, hand-worked codes)
   manhattan / score        pinned (brute force, closed-form GEMM identity)
-  select_topk              pinned (exhaustive brute force on tiny inputs)
+  select_topk              pinned (exhaustive brute force on tiny inputs; with a forced
+                           set: reduces to the plain selection on the other tokens)
   sparse_attend            pinned (dense attention at budget = n, budget = 1)
   decode_step              pinned by composition of the above
 """
@@ -63,6 +64,10 @@ def _load():
     lib.ora_score.argtypes = [P, P, i32, i32, i32, i32, i64, i64, P]
     lib.ora_select_row.argtypes = [P, i64, i32, P]
     lib.ora_select_topk.argtypes = [P, i32, i32, i64, i32, P]
+    lib.ora_select_row_keep.argtypes = [P, i64, i32, i64, i64, P]
+    lib.ora_select_topk_keep.argtypes = [P, i32, i32, i64, i32, i64, i64, P]
+    lib.ora_decode_step_keep.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, i64,
+                                         i64, f64, P, P, P]
     lib.ora_sparse_attend.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f64, P, P]
     lib.ora_decode_step.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, f64, P, P, P]
     lib.ora_f64_to_bf16.argtypes = [f64]
@@ -145,12 +150,16 @@ def score(q_codes: np.ndarray, k_codes: np.ndarray, n_ctx: int | None = None) ->
     return dist
 
 
-def select_topk(dist: np.ndarray, budget: int) -> np.ndarray:
-    """dist[B][Hq][n] -> idx[B][Hq][budget] int32, ascending, -1 padded (§5.2)."""
+def select_topk(dist: np.ndarray, budget: int, n_sink: int = 0, n_recent: int = 0) -> np.ndarray:
+    """dist[B][Hq][n] -> idx[B][Hq][budget] int32, ascending, -1 padded (§5.2);
+    the first n_sink and last n_recent tokens rank ahead of all others."""
     dist = np.ascontiguousarray(dist, np.uint16)
     B, Hq, n = dist.shape
     idx = np.empty((B, Hq, budget), np.int32)
-    _load().ora_select_topk(_ptr(dist), B, Hq, n, budget, _ptr(idx))
+    if n_sink == 0 and n_recent == 0:
+        _load().ora_select_topk(_ptr(dist), B, Hq, n, budget, _ptr(idx))
+    else:
+        _load().ora_select_topk_keep(_ptr(dist), B, Hq, n, budget, n_sink, n_recent, _ptr(idx))
     return idx
 
 
@@ -171,7 +180,8 @@ def sparse_attend(q, k, v, idx, scale: float = 0.0):
     return out, out64
 
 
-def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0):
+def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,
+                n_sink: int = 0, n_recent: int = 0):
     """Full step for one layer -> (out, out64, idx)."""
     q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
     k_codes = np.ascontiguousarray(k_codes, np.uint8)
@@ -181,8 +191,13 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0):
     out = np.empty((B, Hq, d), q.dtype)
     out64 = np.empty((B, Hq, d), np.float64)
     idx = np.empty((B, Hq, budget), np.int32)
-    _load().ora_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d, cap,
-                            n_ctx, budget, float(scale), _ptr(out), _ptr(out64), _ptr(idx))
+    if n_sink == 0 and n_recent == 0:
+        _load().ora_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d, cap,
+                                n_ctx, budget, float(scale), _ptr(out), _ptr(out64), _ptr(idx))
+    else:
+        _load().ora_decode_step_keep(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d,
+                                     cap, n_ctx, budget, n_sink, n_recent, float(scale),
+                                     _ptr(out), _ptr(out64), _ptr(idx))
     return out, out64, idx
 
 

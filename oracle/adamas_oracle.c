@@ -255,14 +255,23 @@ static int ora_cmp_i64(const void *pa, const void *pb)
     return a < b ? -1 : (a > b ? 1 : 0);
 }
 
-/* §5.2 -- token budget.  For one head: order tokens by (distance, index)
- * (reading: the lowest index wins a tie), keep the first min(budget, n),
- * report them in ascending token order and pad the rest of the row with -1. */
-void ora_select_row(const uint16_t *drow, int64_t n, int budget, int32_t *out)
+/* §5.2 -- token budget, with a set of tokens that is always kept.
+ * The article keeps full attention for special tokens such as [CLS] (§3.2,
+ * §6); the page on sparse long-context architectures pairs a sliding window
+ * with attention sinks.  Reading: the first n_sink and the last n_recent of
+ * the n tokens form a forced set F that ranks ahead of every other token
+ * inside the budget.  For one head: order tokens by the key (0, t) for t in
+ * F and (D_t + 1, t) otherwise (reading: the lowest index wins a tie), keep
+ * the first min(budget, n), report them in ascending token order and pad the
+ * rest of the row with -1.  With F empty this is the plain (distance, index)
+ * order. */
+void ora_select_row_keep(const uint16_t *drow, int64_t n, int budget, int64_t n_sink,
+                         int64_t n_recent, int32_t *out)
 {
     ora_key *keys = (ora_key *)malloc(sizeof(ora_key) * (size_t)(n > 0 ? n : 1));
     for (int64_t t = 0; t < n; t++) {
-        keys[t].d = drow[t];
+        int forced = t < n_sink || t >= n - n_recent;
+        keys[t].d = forced ? 0u : (uint32_t)drow[t] + 1u;
         keys[t].t = t;
     }
     qsort(keys, (size_t)n, sizeof(ora_key), ora_cmp_key);
@@ -277,16 +286,28 @@ void ora_select_row(const uint16_t *drow, int64_t n, int budget, int32_t *out)
     free(keys);
 }
 
-void ora_select_topk(const uint16_t *dist, int B, int Hq, int64_t n_ctx,
-                     int budget, int32_t *idx)
+/* The plain §5.2 budget: no forced tokens. */
+void ora_select_row(const uint16_t *drow, int64_t n, int budget, int32_t *out)
+{
+    ora_select_row_keep(drow, n, budget, 0, 0, out);
+}
+
+void ora_select_topk_keep(const uint16_t *dist, int B, int Hq, int64_t n_ctx,
+                          int budget, int64_t n_sink, int64_t n_recent, int32_t *idx)
 {
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; b++)
         for (int hq = 0; hq < Hq; hq++) {
             int64_t r = (int64_t)b * Hq + hq;
-            ora_select_row(dist + r * n_ctx, n_ctx, budget,
-                           idx + r * (int64_t)budget);
+            ora_select_row_keep(dist + r * n_ctx, n_ctx, budget, n_sink, n_recent,
+                                idx + r * (int64_t)budget);
         }
+}
+
+void ora_select_topk(const uint16_t *dist, int B, int Hq, int64_t n_ctx,
+                     int budget, int32_t *idx)
+{
+    ora_select_topk_keep(dist, B, Hq, n_ctx, budget, 0, 0, idx);
 }
 
 /* §6 -- exact softmax attention over the selected rows only, in binary64.
@@ -355,12 +376,14 @@ void ora_sparse_attend(const void *q, const void *k, const void *v, int dtype,
 }
 
 /* One decode step for one layer: encode each query head (§2.1-§3.1), score
- * it against the first n_ctx cached codes (§2.3), keep the budget (§5.2) and
- * attend over those rows (§6).  idx_out may be null. */
-void ora_decode_step(const void *q, const void *k, const void *v,
-                     const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
-                     int d, int64_t cap, int64_t n_ctx, int budget,
-                     double scale, void *out, double *out64, int32_t *idx_out)
+ * it against the first n_ctx cached codes (§2.3), keep the budget (§5.2,
+ * with the forced set of ora_select_row_keep) and attend over those rows
+ * (§6).  idx_out may be null. */
+void ora_decode_step_keep(const void *q, const void *k, const void *v,
+                          const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
+                          int d, int64_t cap, int64_t n_ctx, int budget, int64_t n_sink,
+                          int64_t n_recent, double scale, void *out, double *out64,
+                          int32_t *idx_out)
 {
     int rb = d / 4;
     uint8_t *qc = (uint8_t *)malloc((size_t)B * Hq * rb);
@@ -371,11 +394,20 @@ void ora_decode_step(const void *q, const void *k, const void *v,
     int32_t *idx = idx_out ? idx_out
                            : (int32_t *)malloc(sizeof(int32_t) * (size_t)B * Hq *
                                                (size_t)budget);
-    ora_select_topk(dist, B, Hq, n_ctx, budget, idx);
+    ora_select_topk_keep(dist, B, Hq, n_ctx, budget, n_sink, n_recent, idx);
     ora_sparse_attend(q, k, v, dtype, idx, B, Hq, Hkv, d, cap, budget, scale,
                       out, out64);
     if (!idx_out)
         free(idx);
     free(dist);
     free(qc);
+}
+
+void ora_decode_step(const void *q, const void *k, const void *v,
+                     const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
+                     int d, int64_t cap, int64_t n_ctx, int budget,
+                     double scale, void *out, double *out64, int32_t *idx_out)
+{
+    ora_decode_step_keep(q, k, v, k_codes, dtype, B, Hq, Hkv, d, cap, n_ctx, budget, 0, 0,
+                         scale, out, out64, idx_out);
 }

@@ -266,6 +266,62 @@ def test_select_random_against_brute(ora):
                     assert got[b, h].tolist() == brute_select(d[b, h].tolist(), budget)
 
 
+def test_select_forced_set_reduces_to_plain_selection(ora):
+    """A forced set F (first n_sink, last n_recent tokens) ranks first inside
+    the budget.  Characterised against the plain selection, pinned above: if
+    |F| >= budget the budget's lowest-index members of F are kept; otherwise
+    all of F plus the plain selection of budget - |F| among the other tokens."""
+    for n in range(1, 6):
+        vecs = np.array(list(itertools.product(range(4), repeat=n)), np.uint16)
+        for n_sink in range(0, n + 1):
+            for n_recent in range(0, n + 1):
+                forced = [t for t in range(n) if t < n_sink or t >= n - n_recent]
+                others = [t for t in range(n) if t not in forced]
+                for budget in range(1, n + 2):
+                    got = ora.select_topk(vecs.reshape(1, -1, n), budget, n_sink, n_recent)[0]
+                    if len(forced) >= budget:
+                        want_one = forced[:budget]
+                    for row, dv in zip(got, vecs):
+                        if len(forced) < budget:
+                            rest = []
+                            if others:
+                                sub = dv[others].reshape(1, 1, -1)
+                                pick = ora.select_topk(sub, budget - len(forced))[0, 0]
+                                rest = [others[i] for i in pick if i >= 0]
+                            want_one = sorted(forced + rest)
+                        want = want_one + [-1] * (budget - len(want_one))
+                        assert row.tolist() == want, (n, n_sink, n_recent, budget, dv)
+
+
+def test_select_forced_set_special_cases(ora):
+    rng = np.random.default_rng(4)
+    d = rng.integers(0, 385, size=(1, 2, 3000)).astype(np.uint16)
+    # no forced tokens: the plain selection
+    assert np.array_equal(ora.select_topk(d, 256, 0, 0), ora.select_topk(d, 256))
+    # sink and window cover everything: the first budget tokens
+    assert ora.select_topk(d, 100, 2000, 1000)[0, 0].tolist() == list(range(100))
+    # budget exactly the window: the last tokens, whatever their distances
+    assert ora.select_topk(d, 64, 0, 64)[0, 1].tolist() == list(range(2936, 3000))
+    # a sink of 4 and a window of 60 inside a budget of 256: all 64 kept
+    got = ora.select_topk(d, 256, 4, 60)[0, 0].tolist()
+    assert set(range(4)) <= set(got) and set(range(2940, 3000)) <= set(got)
+    assert got == sorted(got) and len(set(got)) == 256
+
+
+def test_decode_step_with_forced_set_composes(ora):
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((1, 2, 64)).astype(np.float32)
+    k = rng.standard_normal((1, 2, 700, 64)).astype(np.float32)
+    v = rng.standard_normal((1, 2, 700, 64)).astype(np.float32)
+    codes = ora.encode_keys(k)
+    out, out64, idx = ora.decode_step(q, k, v, codes, 650, 40, 0.0, 3, 20)
+    qc = np.ascontiguousarray(ora.encode_keys(q.reshape(1, 2, 1, 64))[:, :, 0, :])
+    dist = ora.score(qc, codes, 650)
+    assert np.array_equal(idx, ora.select_topk(dist, 40, 3, 20))
+    ref, ref64 = ora.sparse_attend(q, k, v, idx)
+    assert np.array_equal(out64, ref64)
+
+
 # --------------------------------------------------------------------------
 # §6 attention over the selected rows
 def dense_attention(q, k, v, scale):
