@@ -66,6 +66,9 @@ def load():
                                          sz, P]
     lib.adamas_decode_step.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, f32, P,
                                        P, P, sz, P]
+    lib.adamas_select_topk_keep.argtypes = [P, i32, i32, i64, i32, i32, i32, i32, P, P, sz, P]
+    lib.adamas_decode_step_keep.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32,
+                                            i32, i32, f32, P, P, P, sz, P]
     lib.adamas_workspace_bytes.argtypes = [i32, i32, i32, i32, i64, i32, i32]
     lib.adamas_workspace_bytes.restype = sz
     lib.adamas_status_string.argtypes = [i32]
@@ -80,7 +83,7 @@ def load():
     for fn in ("adamas_set_decode_mode", "adamas_decode_path"):
         getattr(lib, fn).restype = i32
     for fn in ("adamas_encode_keys", "adamas_score", "adamas_select_topk", "adamas_sparse_attend",
-               "adamas_decode_step"):
+               "adamas_decode_step", "adamas_select_topk_keep", "adamas_decode_step_keep"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -196,16 +199,21 @@ def score(q_codes: torch.Tensor, k_codes: torch.Tensor, n_ctx: int | None = None
 
 
 def select_topk(dist: torch.Tensor, budget: int, head_dim: int, idx: torch.Tensor | None = None,
-                ws: Workspace | None = None, stream=None) -> torch.Tensor:
-    """dist [B][Hq][n] uint16 -> idx [B][Hq][budget] int32 (ascending, -1 padded)."""
+                ws: Workspace | None = None, stream=None, n_sink: int = 0,
+                n_recent: int = 0) -> torch.Tensor:
+    """dist [B][Hq][n] uint16 -> idx [B][Hq][budget] int32 (ascending, -1 padded).
+    The first n_sink and last n_recent tokens are always kept (adamas_select_topk_keep)."""
     B, Hq, n = dist.shape
     if idx is None:
         idx = torch.empty((B, Hq, budget), dtype=torch.int32, device=dist.device)
     nb = load().adamas_workspace_bytes(OP_SELECT_TOPK, B, Hq, 1, n, budget, head_dim)
     buf = _ws_for(dist.device, ws).get(nb)
-    st = load().adamas_select_topk(_dev_ptr(dist, "dist"), B, Hq, n, head_dim, budget,
-                                   _dev_ptr(idx, "idx"), _dev_ptr(buf, "ws"), buf.numel(),
-                                   _stream(dist, stream))
+    args = (_dev_ptr(dist, "dist"), B, Hq, n, head_dim, budget)
+    tail = (_dev_ptr(idx, "idx"), _dev_ptr(buf, "ws"), buf.numel(), _stream(dist, stream))
+    if n_sink == 0 and n_recent == 0:
+        st = load().adamas_select_topk(*args, *tail)
+    else:
+        st = load().adamas_select_topk_keep(*args, int(n_sink), int(n_recent), *tail)
     _check(st, "adamas_select_topk")
     return idx
 
@@ -256,8 +264,10 @@ def decode_path(B: int, Hq: int, Hkv: int, n_ctx: int, budget: int, head_dim: in
 
 
 def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0, out=None,
-                idx_out=None, ws: Workspace | None = None, stream=None) -> torch.Tensor:
-    """One fused decode step of one layer -> out [B][Hq][d] (idx_out optional)."""
+                idx_out=None, ws: Workspace | None = None, stream=None, n_sink: int = 0,
+                n_recent: int = 0) -> torch.Tensor:
+    """One fused decode step of one layer -> out [B][Hq][d] (idx_out optional).
+    The first n_sink and last n_recent tokens are always kept (adamas_decode_step_keep)."""
     B, Hq, d = q.shape
     _, Hkv, cap, _ = k.shape
     if k.dtype != q.dtype or v.dtype != q.dtype or tuple(v.shape) != tuple(k.shape):
@@ -268,10 +278,13 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0, o
         out = torch.empty_like(q)
     nb = load().adamas_workspace_bytes(OP_DECODE_STEP, B, Hq, Hkv, n_ctx, budget, d)
     buf = _ws_for(q.device, ws).get(nb)
-    st = load().adamas_decode_step(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                                   _dev_ptr(k_codes, "k_codes"), _dtype_code(q), B, Hq, Hkv, d,
-                                   cap, n_ctx, budget, float(scale), _dev_ptr(out, "out"),
-                                   _dev_ptr(idx_out, "idx_out"), _dev_ptr(buf, "ws"), buf.numel(),
-                                   _stream(q, stream))
+    head = (_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(k_codes, "k_codes"),
+            _dtype_code(q), B, Hq, Hkv, d, cap, n_ctx, budget)
+    tail = (float(scale), _dev_ptr(out, "out"), _dev_ptr(idx_out, "idx_out"), _dev_ptr(buf, "ws"),
+            buf.numel(), _stream(q, stream))
+    if n_sink == 0 and n_recent == 0:
+        st = load().adamas_decode_step(*head, *tail)
+    else:
+        st = load().adamas_decode_step_keep(*head, int(n_sink), int(n_recent), *tail)
     _check(st, "adamas_decode_step")
     return out

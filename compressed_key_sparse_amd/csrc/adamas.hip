@@ -29,7 +29,7 @@ bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool valid_dtype(int dt) { return dt == ADAMAS_F32 || dt == ADAMAS_BF16; }
 bool valid_dim(int d) { return d == 64 || d == 128; }
-size_t nbins_padded(int D) { return (size_t)((3 * D + 1 + 3) & ~3); }
+size_t nbins_padded(int D) { return D == 128 ? (size_t)kNbinsPadded(128) : (size_t)kNbinsPadded(64); }
 
 // Candidate layout shared by the selection kernels: per head, n_chunks slots
 // of kpad u32 entries, kpad the power of two >= max(4, min(budget, chunk)).
@@ -239,6 +239,7 @@ struct DecodeArgs {
   uint32_t *cand, *ctr;
   int32_t* idx;
   void* out;
+  int n_sink, n_recent;
 };
 
 template <int D, int G, bool BF>
@@ -246,7 +247,7 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
   k_decode<D, G, BF><<<grid, kDecodeThreads, p.sel.lds, s>>>(
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
       p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
-      a.out);
+      a.out, a.n_sink, a.n_recent);
 }
 
 template <int D, int G, bool BF>
@@ -257,7 +258,8 @@ void launch_decode_gs_t(const GroupPlan& p, dim3 grid, hipStream_t s, const Deco
       a.qscale, reinterpret_cast<uint16_t*>(w + p.hist_off),
       reinterpret_cast<float*>(w + p.part_off), reinterpret_cast<uint32_t*>(w + kCtrlSelect),
       reinterpret_cast<uint32_t*>(w + kCtrlAttend),
-      reinterpret_cast<uint32_t*>(w + ADAMAS_WS_STATUS_OFFSET), a.idx, a.out);
+      reinterpret_cast<uint32_t*>(w + ADAMAS_WS_STATUS_OFFSET), a.idx, a.out, a.n_sink,
+      a.n_recent);
 }
 
 template <int D, bool BF>
@@ -390,10 +392,12 @@ int adamas_score(const uint8_t* q_codes, const uint8_t* k_codes, int B, int Hq, 
   return launch_status();
 }
 
-int adamas_select_topk(const uint16_t* dist, int B, int Hq, int64_t n_ctx, int head_dim,
-                       int budget, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+int adamas_select_topk_keep(const uint16_t* dist, int B, int Hq, int64_t n_ctx, int head_dim,
+                            int budget, int n_sink, int n_recent, int32_t* idx, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
   if (!valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
-  if (B < 1 || Hq < 1 || n_ctx < 1 || budget < 1) return ADAMAS_ERR_INVALID;
+  if (B < 1 || Hq < 1 || n_ctx < 1 || budget < 1 || n_sink < 0 || n_recent < 0)
+    return ADAMAS_ERR_INVALID;
   if (budget > kMaxBudget || n_ctx > INT32_MAX || (int64_t)B * Hq > kMaxGroups || Hq > 65535 ||
       B > 65535)
     return ADAMAS_ERR_UNSUPPORTED;
@@ -408,11 +412,19 @@ int adamas_select_topk(const uint16_t* dist, int B, int Hq, int64_t n_ctx, int h
   uint32_t* ctr = reinterpret_cast<uint32_t*>(w + kCtrlSelect);
   if (head_dim == 128)
     k_select<128><<<grid, kSelectThreads, p.lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks,
-                                                           budget, p.kpad_log2, p.mcap, cand, ctr, idx);
+                                                           budget, p.kpad_log2, p.mcap, cand, ctr, idx,
+                                                           n_sink, n_recent);
   else
     k_select<64><<<grid, kSelectThreads, p.lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks,
-                                                          budget, p.kpad_log2, p.mcap, cand, ctr, idx);
+                                                          budget, p.kpad_log2, p.mcap, cand, ctr, idx,
+                                                          n_sink, n_recent);
   return launch_status();
+}
+
+int adamas_select_topk(const uint16_t* dist, int B, int Hq, int64_t n_ctx, int head_dim,
+                       int budget, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return adamas_select_topk_keep(dist, B, Hq, n_ctx, head_dim, budget, 0, 0, idx, ws, ws_bytes,
+                                 stream);
 }
 
 int adamas_sparse_attend(const void* q, const void* k, const void* v, int dtype,
@@ -438,13 +450,14 @@ int adamas_sparse_attend(const void* q, const void* k, const void* v, int dtype,
   return launch_status();
 }
 
-int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_t* k_codes,
-                       int dtype, int B, int Hq, int Hkv, int head_dim, int64_t cap,
-                       int64_t n_ctx, int budget, float scale, void* out, int32_t* idx_out,
-                       void* ws, size_t ws_bytes, hipStream_t stream) {
+int adamas_decode_step_keep(const void* q, const void* k, const void* v, const uint8_t* k_codes,
+                            int dtype, int B, int Hq, int Hkv, int head_dim, int64_t cap,
+                            int64_t n_ctx, int budget, int n_sink, int n_recent, float scale,
+                            void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
   if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || cap < 1 || n_ctx < 1 || n_ctx > cap ||
-      budget < 1 || !isfinite(scale))
+      budget < 1 || !isfinite(scale) || n_sink < 0 || n_recent < 0)
     return ADAMAS_ERR_INVALID;
   if (budget > kMaxBudget || n_ctx > INT32_MAX || Hq / Hkv > kMaxG ||
       (int64_t)B * Hq > kMaxGroups || Hq > 65535 || B > 65535)
@@ -469,7 +482,7 @@ int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_
     if (gp.ok) {
       if (ws_bytes < gp.total) return ADAMAS_ERR_WORKSPACE;
       DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
-                   nullptr, nullptr, idx_out, out};
+                   nullptr, nullptr, idx_out, out, n_sink, n_recent};
       const dim3 grid((unsigned)gp.n_chunks, (unsigned)Hkv, (unsigned)B);
       const bool ok = head_dim == 128
                           ? (bf ? dispatch_decode_gs<128, true>(G, gp, grid, stream, a, w)
@@ -487,7 +500,7 @@ int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_
                                 : reinterpret_cast<int32_t*>(w + p.idx_off);
   DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
                reinterpret_cast<uint32_t*>(w + p.sel.cand_off),
-               reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out};
+               reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent};
   const dim3 grid((unsigned)p.sel.n_chunks, (unsigned)Hkv, (unsigned)B);
   bool ok;
   if (head_dim == 128)
@@ -504,6 +517,14 @@ int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_
                   reinterpret_cast<uint32_t*>(w + kCtrlAttend), out);
   }
   return launch_status();
+}
+
+int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_t* k_codes,
+                       int dtype, int B, int Hq, int Hkv, int head_dim, int64_t cap,
+                       int64_t n_ctx, int budget, float scale, void* out, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  return adamas_decode_step_keep(q, k, v, k_codes, dtype, B, Hq, Hkv, head_dim, cap, n_ctx,
+                                 budget, 0, 0, scale, out, idx_out, ws, ws_bytes, stream);
 }
 
 int adamas_set_decode_mode(int mode) {

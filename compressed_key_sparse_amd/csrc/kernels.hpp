@@ -9,9 +9,29 @@
 
 namespace adm {
 
-constexpr int kNbins(int D) { return 3 * D + 1; }
-constexpr int kNbinsPadded(int D) { return (3 * D + 1 + 3) & ~3; }
-constexpr int kNbinsHist(int D) { return (3 * D + 1 + 7) & ~7; }  // u16 bins, 16-byte rows
+// Selection keys: bin 0 holds the tokens that are always kept (the first
+// n_sink and the last n_recent of the context), bin 1 + d the others at
+// Manhattan distance d (0 <= d <= 3*D).
+constexpr int kNbins(int D) { return 3 * D + 2; }
+constexpr int kNbinsPadded(int D) { return (kNbins(D) + 3) & ~3; }
+constexpr int kNbinsHist(int D) { return (kNbins(D) + 7) & ~7; }  // u16 bins, 16-byte rows
+
+// Key of token t: 0 if it is always kept, else 1 + its distance.
+ADM_DEV uint32_t select_key(int64_t t, uint32_t d, int64_t n_sink, int64_t keep_from) {
+  return (t < n_sink || t >= keep_from) ? 0u : d + 1u;
+}
+
+// The always-kept tokens of a run [t0, t0 + valid) as run-local bounds: token
+// i is kept iff i < lo or i >= hi (0 <= lo, hi <= valid).
+struct KeepRange {
+  int lo, hi;
+  ADM_DEV KeepRange(int64_t t0, int valid, int64_t n_sink, int64_t keep_from) {
+    const int64_t a = n_sink - t0, z = keep_from - t0;
+    lo = (int)(a < 0 ? 0 : (a > valid ? valid : a));
+    hi = (int)(z < 0 ? 0 : (z > valid ? valid : z));
+  }
+  ADM_DEV uint32_t key(int i, uint32_t d) const { return (i < lo || i >= hi) ? 0u : d + 1u; }
+};
 constexpr int kGsMergeTile = 16;  // partials merged per LDS tile (k_decode_gs)
 
 constexpr int kEncodeThreads = 256;
@@ -422,7 +442,7 @@ template <int D>
 __global__ __launch_bounds__(kSelectThreads) void k_select(
     const uint16_t* __restrict__ dist, int Hq, int64_t n_ctx, int chunk, int n_chunks,
     int budget, int kpad_log2, int mcap, uint32_t* __restrict__ cand,
-    uint32_t* __restrict__ counters, int32_t* __restrict__ idx) {
+    uint32_t* __restrict__ counters, int32_t* __restrict__ idx, int n_sink, int n_recent) {
   constexpr int NT = kSelectThreads, NB = kNbins(D), NBP = kNbinsPadded(D);
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
@@ -438,11 +458,13 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
   const int64_t t0 = (int64_t)c * chunk;
   const int valid = (int)min((int64_t)chunk, n_ctx - t0);
   const uint16_t* drow = dist + row * n_ctx + t0;
+  const int64_t keep_from = n_ctx - n_recent;
   for (int t = threadIdx.x; t < valid; t += NT) {
     // values above 3*D break the caller's contract; clamp so LDS stays in bounds
-    const uint16_t d = drow[t] < NB ? drow[t] : (uint16_t)(NB - 1);
-    sdist[t] = d;
-    atomicAdd(&shist[d], 1u);
+    const uint32_t d = drow[t] < NB - 1 ? drow[t] : (uint32_t)(NB - 2);
+    const uint32_t key = select_key(t0 + t, d, n_sink, keep_from);
+    sdist[t] = (uint16_t)key;
+    atomicAdd(&shist[key], 1u);
   }
   lds_sync();
   const int kc = min(budget, valid);
@@ -472,7 +494,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
     int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
-    void* __restrict__ out) {
+    void* __restrict__ out, int n_sink, int n_recent) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), W = D / 16;
   constexpr int E = D / 64, kLanesPerWord = 16 / E, PW = 2 + D;
@@ -523,9 +545,11 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   lds_sync();
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
+  const KeepRange keep(t0, valid, n_sink, n_ctx - n_recent);
   scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
-    sdist[g * chunk + tok] = (uint16_t)d;
-    atomicAdd(&shist[g * NBP + d], 1u);
+    const uint32_t key = keep.key(tok, d);
+    sdist[g * chunk + tok] = (uint16_t)key;
+    atomicAdd(&shist[g * NBP + key], 1u);
   }, &first);
   lds_sync();
   const int kc = min(budget, valid);
@@ -578,7 +602,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     int n_chunks, int budget, int cmax, float qscale, uint16_t* __restrict__ ghist,
     float* __restrict__ part, uint32_t* __restrict__ arrive_hist,
     uint32_t* __restrict__ arrive_part, uint32_t* __restrict__ status, int32_t* __restrict__ idx,
-    void* __restrict__ out) {
+    void* __restrict__ out, int n_sink, int n_recent) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), NBH = kNbinsHist(D), W = D / 16;
   static_assert(G <= kTmpWords - kTmpGroupCounts, "per-head counts live in s_tmp");
@@ -624,9 +648,11 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   lds_sync();
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
+  const KeepRange keep(t0, valid, n_sink, n_ctx - n_recent);
   scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
-    sdist[g * chunk + tok] = (uint16_t)d;
-    atomicAdd(&shist[g * NBP + d], 1u);
+    const uint32_t key = keep.key(tok, d);
+    sdist[g * chunk + tok] = (uint16_t)key;
+    atomicAdd(&shist[g * NBP + key], 1u);
   }, &first);
   lds_sync();
 

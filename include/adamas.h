@@ -197,6 +197,27 @@ int adamas_set_decode_mode(int mode);
  */
 int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim);
 
+/*
+ * adamas_select_topk and adamas_decode_step with a set of tokens that is
+ * always kept: the first n_sink and the last n_recent of the n_ctx tokens
+ * (attention sinks such as [CLS]/BOS positions, and a recent window; the
+ * article keeps full attention for special tokens, §3.2 and §6).  They rank
+ * ahead of every other token inside the budget: with F that set, the kept
+ * tokens are all of F plus the plain selection of budget - |F| among the
+ * others, or the budget's lowest-index members of F when |F| >= budget.
+ * n_sink = n_recent = 0 gives the plain calls.  Requires n_sink, n_recent
+ * >= 0; same workspace as the plain calls.
+ */
+int adamas_select_topk_keep(const uint16_t *dist, int B, int Hq, int64_t n_ctx,
+                            int head_dim, int budget, int n_sink, int n_recent,
+                            int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
+int adamas_decode_step_keep(const void *q, const void *k, const void *v,
+                            const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
+                            int head_dim, int64_t cap, int64_t n_ctx, int budget,
+                            int n_sink, int n_recent, float scale, void *out,
+                            int32_t *idx_out, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* Workspace bytes needed by `op` for the given shape (0 for invalid shapes). */
 size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx,
                               int budget, int head_dim);

@@ -168,3 +168,16 @@ def test_stream_read_validation(lib):
     assert f(A, 64, None, None) == INVALID
     assert lib.adamas_stream_read_blocks(16) == 1
     assert lib.adamas_stream_read_blocks(1 << 40) == 1024
+
+
+def test_keep_validation(lib):
+    f = lib.adamas_select_topk_keep
+    need = lib.adamas_workspace_bytes(0, 1, 4, 1, 1000, 64, 128)
+    assert f(A, 1, 4, 1000, 128, 64, -1, 0, A, A, need, None) == INVALID
+    assert f(A, 1, 4, 1000, 128, 64, 0, -5, A, A, need, None) == INVALID
+    g = lib.adamas_decode_step_keep
+    need = lib.adamas_workspace_bytes(2, 1, 8, 4, 1000, 64, 128)
+    args = lambda s, r: [A, A, A, A, 1, 1, 8, 4, 128, 1024, 1000, 64, s, r, ctypes.c_float(0.0),
+                         A, None, A, need, None]
+    assert g(*args(-1, 0)) == INVALID
+    assert g(*args(0, -1)) == INVALID

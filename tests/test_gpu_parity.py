@@ -303,3 +303,39 @@ def test_stream_read_reads_every_byte():
         want = np.bitwise_xor.reduce(x.cpu().numpy().view(np.uint32))
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         assert got == want, n
+
+
+# -------------------------------------------- always-kept sinks and window
+@pytest.mark.parametrize("n,budget,n_sink,n_recent,hi", [
+    (3000, 64, 4, 60, 6), (3000, 64, 64, 0, 6), (3000, 64, 0, 100, 6), (3000, 50, 40, 40, 2),
+    (20000, 256, 1, 32, 384), (777, 1000, 5, 5, 3), (70000, 512, 16, 256, 40)])
+def test_select_keep(ora, n, budget, n_sink, n_recent, hi):
+    log(f"select keep n={n} budget={budget} sink={n_sink} recent={n_recent}")
+    g = torch.Generator(device=DEV).manual_seed(n + budget + n_sink)
+    dist = torch.randint(0, hi + 1, (2, 3, n), generator=g, device=DEV,
+                         dtype=torch.int32).to(torch.uint16)
+    idx = adamas.select_topk(dist, budget, head_dim=128, n_sink=n_sink, n_recent=n_recent)
+    ref = ora.select_topk(dist.cpu().numpy(), budget, n_sink, n_recent)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT])
+@pytest.mark.parametrize("n,budget,n_sink,n_recent", [
+    (5000, 256, 4, 64), (70000, 512, 1, 128), (9001, 128, 128, 0), (30000, 1024, 8, 1000)])
+def test_decode_keep(ora, restore_mode, mode, n, budget, n_sink, n_recent):
+    log(f"decode keep mode {mode} n={n} budget={budget} sink={n_sink} recent={n_recent}")
+    adamas.set_decode_mode(mode)
+    w = synth.LLAMA2_32K.replace(hq=4, hkv=4, n_ctx=n, cap=n, budget=budget)
+    lay = synth.make_layer(w, 1, DEV)
+    codes = torch.zeros((1, 4, n, 32), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    idx = torch.empty((1, 4, budget), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, n, budget, idx_out=idx,
+                             n_sink=n_sink, n_recent=n_recent)
+    torch.cuda.synchronize()
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    oout, _, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), n, budget, 0.0, n_sink, n_recent)
+    assert np.array_equal(idx.cpu().numpy(), oidx), "selection differs"
+    e = rel_err(out, oout)
+    log(f"  rel err {e:.3e}")
+    assert e <= TOL[torch.bfloat16]
