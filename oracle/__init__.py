@@ -68,6 +68,10 @@ def _load():
     lib.ora_select_topk_keep.argtypes = [P, i32, i32, i64, i32, i64, i64, P]
     lib.ora_decode_step_keep.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, i64,
                                          i64, f64, P, P, P]
+    lib.ora_decode_step_ex.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, i64,
+                                       i64, i32, f64, P, P, P]
+    lib.ora_encode_vec_f32_rot.argtypes = [P, i32, i32, P, P, P]
+    lib.ora_encode_keys_rot.argtypes = [P, i32, i32, i32, i64, i32, P, i64, i64, i32]
     lib.ora_sparse_attend.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f64, P, P]
     lib.ora_decode_step.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, f64, P, P, P]
     lib.ora_f64_to_bf16.argtypes = [f64]
@@ -106,19 +110,23 @@ def hadamard_orthonormal_f64(x: np.ndarray) -> np.ndarray:
     return y
 
 
-def encode_vec(x: np.ndarray):
-    """One fp32 vector -> (packed bytes, rotated values, codes)."""
+def encode_vec(x: np.ndarray, rotate: bool = True):
+    """One fp32 vector -> (packed bytes, rotated values, codes); rotate=False
+    buckets the vector as it is."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     d = x.shape[-1]
     packed = np.empty(d // 4, np.uint8)
     y = np.empty(d, np.float32)
     codes = np.empty(d, np.int32)
-    _load().ora_encode_vec_f32(_ptr(x), d, _ptr(packed), _ptr(y), _ptr(codes))
+    if rotate:
+        _load().ora_encode_vec_f32(_ptr(x), d, _ptr(packed), _ptr(y), _ptr(codes))
+    else:
+        _load().ora_encode_vec_f32_rot(_ptr(x), d, 0, _ptr(packed), _ptr(y), _ptr(codes))
     return packed, y, codes
 
 
 def encode_keys(x: np.ndarray, codes: np.ndarray | None = None, cap: int | None = None,
-                pos: int = 0) -> np.ndarray:
+                pos: int = 0, rotate: bool = True) -> np.ndarray:
     """x[batch][heads][n][d] -> codes[batch][heads][cap][d/4], rows [pos, pos+n)."""
     x = np.ascontiguousarray(x)
     batch, heads, n, d = x.shape
@@ -127,7 +135,11 @@ def encode_keys(x: np.ndarray, codes: np.ndarray | None = None, cap: int | None 
     if codes is None:
         codes = np.zeros((batch, heads, cap, d // 4), np.uint8)
     assert codes.shape == (batch, heads, cap, d // 4) and codes.dtype == np.uint8
-    _load().ora_encode_keys(_ptr(x), _dtype_tag(x), batch, heads, n, d, _ptr(codes), cap, pos)
+    if rotate:
+        _load().ora_encode_keys(_ptr(x), _dtype_tag(x), batch, heads, n, d, _ptr(codes), cap, pos)
+    else:
+        _load().ora_encode_keys_rot(_ptr(x), _dtype_tag(x), batch, heads, n, d, _ptr(codes), cap,
+                                    pos, 0)
     return codes
 
 
@@ -181,7 +193,7 @@ def sparse_attend(q, k, v, idx, scale: float = 0.0):
 
 
 def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,
-                n_sink: int = 0, n_recent: int = 0):
+                n_sink: int = 0, n_recent: int = 0, rotate: bool = True):
     """Full step for one layer -> (out, out64, idx)."""
     q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
     k_codes = np.ascontiguousarray(k_codes, np.uint8)
@@ -191,7 +203,11 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,
     out = np.empty((B, Hq, d), q.dtype)
     out64 = np.empty((B, Hq, d), np.float64)
     idx = np.empty((B, Hq, budget), np.int32)
-    if n_sink == 0 and n_recent == 0:
+    if not rotate:
+        _load().ora_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d,
+                                   cap, n_ctx, budget, n_sink, n_recent, 0, float(scale),
+                                   _ptr(out), _ptr(out64), _ptr(idx))
+    elif n_sink == 0 and n_recent == 0:
         _load().ora_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d, cap,
                                 n_ctx, budget, float(scale), _ptr(out), _ptr(out64), _ptr(idx))
     else:

@@ -153,14 +153,17 @@ static void ora_pack(const int *codes, int d, uint8_t *out)
 
 /* Rotate, bucket and pack one vector given as fp32 values.  Also returns the
  * rotated values and codes when the pointers are non-null (for tests). */
-void ora_encode_vec_f32(const float *x, int d, uint8_t *packed, float *y_out,
-                        int *codes_out)
+/* rotate == 0 skips §2.1: the vector is bucketed as it is (the ablation row
+ * "2-bit quantisation only" of the article's §3.2 table). */
+void ora_encode_vec_f32_rot(const float *x, int d, int rotate, uint8_t *packed, float *y_out,
+                            int *codes_out)
 {
     float y[ORA_MAX_D];
     int c[ORA_MAX_D];
     for (int i = 0; i < d; i++)
         y[i] = x[i];
-    ora_fwht_f32(y, d);
+    if (rotate)
+        ora_fwht_f32(y, d);
     float a = 0.0f;
     for (int i = 0; i < d; i++) {
         float m = fabsf(y[i]);
@@ -182,8 +185,14 @@ void ora_encode_vec_f32(const float *x, int d, uint8_t *packed, float *y_out,
 
 /* Encode keys x[batch][heads][n][d] into the code cache
  * codes[batch][heads][cap][d/4] at token rows [pos, pos+n). */
-void ora_encode_keys(const void *x, int dtype, int batch, int heads, int64_t n,
-                     int d, uint8_t *codes, int64_t cap, int64_t pos)
+void ora_encode_vec_f32(const float *x, int d, uint8_t *packed, float *y_out,
+                        int *codes_out)
+{
+    ora_encode_vec_f32_rot(x, d, 1, packed, y_out, codes_out);
+}
+
+void ora_encode_keys_rot(const void *x, int dtype, int batch, int heads, int64_t n,
+                         int d, uint8_t *codes, int64_t cap, int64_t pos, int rotate)
 {
     int64_t total = (int64_t)batch * heads * n;
 #pragma omp parallel for schedule(static)
@@ -192,8 +201,14 @@ void ora_encode_keys(const void *x, int dtype, int batch, int heads, int64_t n,
         float xv[ORA_MAX_D];
         for (int i = 0; i < d; i++)
             xv[i] = ora_widen(x, dtype, v * d + i);
-        ora_encode_vec_f32(xv, d, codes + (bh * cap + pos + t) * (d / 4), 0, 0);
+        ora_encode_vec_f32_rot(xv, d, rotate, codes + (bh * cap + pos + t) * (d / 4), 0, 0);
     }
+}
+
+void ora_encode_keys(const void *x, int dtype, int batch, int heads, int64_t n,
+                     int d, uint8_t *codes, int64_t cap, int64_t pos)
+{
+    ora_encode_keys_rot(x, dtype, batch, heads, n, d, codes, cap, pos, 1);
 }
 
 /* Code i of a packed row (inverse of ora_pack). */
@@ -379,15 +394,15 @@ void ora_sparse_attend(const void *q, const void *k, const void *v, int dtype,
  * it against the first n_ctx cached codes (§2.3), keep the budget (§5.2,
  * with the forced set of ora_select_row_keep) and attend over those rows
  * (§6).  idx_out may be null. */
-void ora_decode_step_keep(const void *q, const void *k, const void *v,
-                          const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
-                          int d, int64_t cap, int64_t n_ctx, int budget, int64_t n_sink,
-                          int64_t n_recent, double scale, void *out, double *out64,
-                          int32_t *idx_out)
+void ora_decode_step_ex(const void *q, const void *k, const void *v,
+                        const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
+                        int d, int64_t cap, int64_t n_ctx, int budget, int64_t n_sink,
+                        int64_t n_recent, int rotate, double scale, void *out, double *out64,
+                        int32_t *idx_out)
 {
     int rb = d / 4;
     uint8_t *qc = (uint8_t *)malloc((size_t)B * Hq * rb);
-    ora_encode_keys(q, dtype, B, Hq, 1, d, qc, 1, 0);
+    ora_encode_keys_rot(q, dtype, B, Hq, 1, d, qc, 1, 0, rotate);
     uint16_t *dist = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)B * Hq *
                                         (size_t)(n_ctx > 0 ? n_ctx : 1));
     ora_score(qc, k_codes, B, Hq, Hkv, d, cap, n_ctx, dist);
@@ -403,11 +418,21 @@ void ora_decode_step_keep(const void *q, const void *k, const void *v,
     free(qc);
 }
 
+void ora_decode_step_keep(const void *q, const void *k, const void *v,
+                          const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
+                          int d, int64_t cap, int64_t n_ctx, int budget, int64_t n_sink,
+                          int64_t n_recent, double scale, void *out, double *out64,
+                          int32_t *idx_out)
+{
+    ora_decode_step_ex(q, k, v, k_codes, dtype, B, Hq, Hkv, d, cap, n_ctx, budget, n_sink,
+                       n_recent, 1, scale, out, out64, idx_out);
+}
+
 void ora_decode_step(const void *q, const void *k, const void *v,
                      const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
                      int d, int64_t cap, int64_t n_ctx, int budget,
                      double scale, void *out, double *out64, int32_t *idx_out)
 {
-    ora_decode_step_keep(q, k, v, k_codes, dtype, B, Hq, Hkv, d, cap, n_ctx, budget, 0, 0,
-                         scale, out, out64, idx_out);
+    ora_decode_step_ex(q, k, v, k_codes, dtype, B, Hq, Hkv, d, cap, n_ctx, budget, 0, 0, 1,
+                       scale, out, out64, idx_out);
 }

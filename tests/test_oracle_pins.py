@@ -322,6 +322,44 @@ def test_decode_step_with_forced_set_composes(ora):
     assert np.array_equal(out64, ref64)
 
 
+def _golden_no_rotation_cases():
+    out = []
+    with open(os.path.join(GOLDEN, "encode_no_rotation_hand_worked.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            d, x, codes, packed = (p.strip() for p in line.split("|"))
+            out.append((int(d), [float(v) for v in x.split(",")],
+                        [int(c) for c in codes.split(",")], bytes.fromhex(packed)))
+    return out
+
+
+@pytest.mark.parametrize("case", _golden_no_rotation_cases(), ids=lambda c: c[3].hex())
+def test_encode_without_rotation_hand_worked(ora, case):
+    d, x, codes, packed = case
+    got_packed, y, got_codes = ora.encode_vec(np.array(x, np.float32), rotate=False)
+    assert got_codes.tolist() == codes
+    assert bytes(got_packed) == packed
+    assert np.array_equal(y, np.array(x, np.float32))   # nothing rotated
+
+
+def test_encode_rotation_off_is_rotation_of_rotated_input(ora):
+    # H (H x) = d x for the unnormalised Sylvester H, and codes are invariant
+    # to a positive scale: encoding H x without the rotation equals encoding x
+    # with it, whenever H x is exact in fp32 (integer inputs here)
+    rng = np.random.default_rng(21)
+    for d in (64, 128):
+        x = rng.integers(-50, 50, size=(5, d)).astype(np.float32)
+        for row in x:
+            _, y, _ = ora.encode_vec(row)                 # y = H x, exact
+            with_rot, _, _ = ora.encode_vec(row)
+            without, _, _ = ora.encode_vec(y, rotate=False)
+            assert bytes(with_rot) == bytes(without)
+        k = x.reshape(1, 1, 5, d)
+        yk = np.stack([ora.encode_vec(r)[1] for r in x]).reshape(1, 1, 5, d)
+        assert np.array_equal(ora.encode_keys(k), ora.encode_keys(yk, rotate=False))
+
+
 # --------------------------------------------------------------------------
 # §6 attention over the selected rows
 def dense_attention(q, k, v, scale):
