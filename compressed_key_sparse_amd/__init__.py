@@ -79,6 +79,8 @@ def load():
     lib.adamas_stream_read_blocks.argtypes = [sz]
     lib.adamas_stream_read_blocks.restype = sz
     lib.adamas_set_decode_mode.argtypes = [i32]
+    lib.adamas_set_rotation.argtypes = [i32]
+    lib.adamas_set_rotation.restype = i32
     lib.adamas_decode_path.argtypes = [i32, i32, i32, i64, i32, i32]
     for fn in ("adamas_set_decode_mode", "adamas_decode_path"):
         getattr(lib, fn).restype = i32
@@ -247,6 +249,11 @@ def stream_read(x: torch.Tensor, sink: torch.Tensor | None = None, stream=None) 
     _check(load().adamas_stream_read(_dev_ptr(x, "x"), nbytes, _dev_ptr(sink, "sink"),
                                      _stream(x, stream)), "adamas_stream_read")
     return sink
+
+
+def set_rotation(on: bool) -> None:
+    """Process-wide: rotate vectors before bucketing (default) or not (adamas_set_rotation)."""
+    _check(load().adamas_set_rotation(1 if on else 0), "adamas_set_rotation")
 
 
 def set_decode_mode(mode: int) -> None:

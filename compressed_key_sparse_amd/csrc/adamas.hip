@@ -204,6 +204,8 @@ int64_t device_capacity() {
 constexpr int64_t kSizingCapacity = 1024;
 
 std::atomic<int> g_decode_mode{ADAMAS_DECODE_AUTO};
+std::atomic<int> g_rotation{1};
+int rotation_on() { return g_rotation.load(std::memory_order_relaxed); }
 
 int launch_status() {
   return hipGetLastError() == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_DEVICE;
@@ -247,7 +249,7 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
   k_decode<D, G, BF><<<grid, kDecodeThreads, p.sel.lds, s>>>(
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
       p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
-      a.out, a.n_sink, a.n_recent);
+      a.out, a.n_sink, a.n_recent, rotation_on());
 }
 
 template <int D, int G, bool BF>
@@ -259,7 +261,7 @@ void launch_decode_gs_t(const GroupPlan& p, dim3 grid, hipStream_t s, const Deco
       reinterpret_cast<float*>(w + p.part_off), reinterpret_cast<uint32_t*>(w + kCtrlSelect),
       reinterpret_cast<uint32_t*>(w + kCtrlAttend),
       reinterpret_cast<uint32_t*>(w + ADAMAS_WS_STATUS_OFFSET), a.idx, a.out, a.n_sink,
-      a.n_recent);
+      a.n_recent, rotation_on());
 }
 
 template <int D, bool BF>
@@ -365,9 +367,11 @@ int adamas_encode_keys(const void* x, int dtype, int batch, int heads, int64_t n
   const unsigned blocks = (unsigned)(blocks64 < 16384 ? blocks64 : 16384);
   const int bf = dtype == ADAMAS_BF16;
   if (head_dim == 128)
-    k_encode<128><<<blocks, kEncodeThreads, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst);
+    k_encode<128><<<blocks, kEncodeThreads, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst,
+                                                         rotation_on());
   else
-    k_encode<64><<<blocks, kEncodeThreads, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst);
+    k_encode<64><<<blocks, kEncodeThreads, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst,
+                                                        rotation_on());
   return launch_status();
 }
 
@@ -525,6 +529,12 @@ int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_
                        void* ws, size_t ws_bytes, hipStream_t stream) {
   return adamas_decode_step_keep(q, k, v, k_codes, dtype, B, Hq, Hkv, head_dim, cap, n_ctx,
                                  budget, 0, 0, scale, out, idx_out, ws, ws_bytes, stream);
+}
+
+int adamas_set_rotation(int on) {
+  if (on != 0 && on != 1) return ADAMAS_ERR_INVALID;
+  g_rotation.store(on, std::memory_order_relaxed);
+  return ADAMAS_OK;
 }
 
 int adamas_set_decode_mode(int mode) {

@@ -236,10 +236,12 @@ ADM_DEV float xor_max(float x) {
 // Packing (§3.1): four codes per byte, first code in bits 7..6; returns, on
 // the lanes with (lane % (16/E)) == 0, the little-endian 32-bit word
 // lane / (16/E) of the packed row (16 codes per word); other lanes return 0.
+// rotate == false buckets the vector as it is (no §2.1; for the ablation).
 template <int D>
-ADM_DEV uint32_t wave_encode(float (&y)[D / 64]) {
+ADM_DEV uint32_t wave_encode(float (&y)[D / 64], bool rotate = true) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & (kWave - 1);
+  if (rotate) {
 #pragma unroll
   for (int h = 1; h < E; h <<= 1) {
 #pragma unroll
@@ -268,6 +270,7 @@ ADM_DEV uint32_t wave_encode(float (&y)[D / 64]) {
   stage(std::integral_constant<int, 8>{});
   stage(std::integral_constant<int, 16>{});
   stage(std::integral_constant<int, 32>{});
+  }
   float a = fabsf(y[0]);
 #pragma unroll
   for (int e = 1; e < E; ++e) a = fmaxf(a, fabsf(y[e]));

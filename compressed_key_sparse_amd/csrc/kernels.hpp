@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
                                                            int is_bf16, int64_t n, int64_t nvec,
                                                            uint8_t* __restrict__ codes,
                                                            int64_t cap, int64_t pos,
-                                                           void* __restrict__ copy) {
+                                                           void* __restrict__ copy, int rotate) {
   constexpr int E = D / 64;
   constexpr int kLanesPerWord = 16 / E;
   const int lane = threadIdx.x & (kWave - 1);
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
     }
     float y[E];
     load_elems<E>(x, is_bf16 != 0, src, y);
-    const uint32_t word = wave_encode<D>(y);
+    const uint32_t word = wave_encode<D>(y, rotate != 0);
     if (lane % kLanesPerWord == 0)
       reinterpret_cast<uint32_t*>(codes + row * (D / 4))[lane / kLanesPerWord] = word;
   }
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
     int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
-    void* __restrict__ out, int n_sink, int n_recent) {
+    void* __restrict__ out, int n_sink, int n_recent, int rotate) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), W = D / 16;
   constexpr int E = D / 64, kLanesPerWord = 16 / E, PW = 2 + D;
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   if (wid < G) {
     float y[E];
     widen_elems<E, BF>(qraw, y);
-    const uint32_t word = wave_encode<D>(y);
+    const uint32_t word = wave_encode<D>(y, rotate != 0);
     if (lane % kLanesPerWord == 0) sq[wid * W + lane / kLanesPerWord] = word;
   }
   lds_sync();
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     int n_chunks, int budget, int cmax, float qscale, uint16_t* __restrict__ ghist,
     float* __restrict__ part, uint32_t* __restrict__ arrive_hist,
     uint32_t* __restrict__ arrive_part, uint32_t* __restrict__ status, int32_t* __restrict__ idx,
-    void* __restrict__ out, int n_sink, int n_recent) {
+    void* __restrict__ out, int n_sink, int n_recent, int rotate) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), NBH = kNbinsHist(D), W = D / 16;
   static_assert(G <= kTmpWords - kTmpGroupCounts, "per-head counts live in s_tmp");
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   if (wid < G) {
     float y[E];
     widen_elems<E, BF>(qraw, y);
-    const uint32_t word = wave_encode<D>(y);
+    const uint32_t word = wave_encode<D>(y, rotate != 0);
     if (lane % kLanesPerWord == 0) sq[wid * W + lane / kLanesPerWord] = word;
   }
   lds_sync();

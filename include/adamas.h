@@ -189,6 +189,15 @@ int adamas_decode_step(const void *q, const void *k, const void *v,
 int adamas_set_decode_mode(int mode);
 
 /*
+ * Process-wide switch of the §2.1 rotation for every later adamas_encode_keys
+ * and decode step (1, the default: rotate; 0: bucket vectors as they are, the
+ * "2-bit quantisation only" row of the article's §3.2 ablation).  Codes made
+ * with one setting must only be scored against queries encoded with the same
+ * one.  Returns ADAMAS_OK, or ADAMAS_ERR_INVALID unless on is 0 or 1.
+ */
+int adamas_set_rotation(int on);
+
+/*
  * The schedule adamas_decode_step would use for this shape on the current
  * device under the current mode: ADAMAS_DECODE_LAST_ARRIVAL or
  * ADAMAS_DECODE_GROUP_WAIT, or a negated status (-ADAMAS_ERR_INVALID for a

@@ -181,3 +181,10 @@ def test_keep_validation(lib):
                          A, None, A, need, None]
     assert g(*args(-1, 0)) == INVALID
     assert g(*args(0, -1)) == INVALID
+
+
+def test_rotation_switch_validation(lib):
+    assert lib.adamas_set_rotation(2) == INVALID
+    assert lib.adamas_set_rotation(-1) == INVALID
+    assert lib.adamas_set_rotation(0) == OK
+    assert lib.adamas_set_rotation(1) == OK

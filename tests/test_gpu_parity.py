@@ -339,3 +339,40 @@ def test_decode_keep(ora, restore_mode, mode, n, budget, n_sink, n_recent):
     e = rel_err(out, oout)
     log(f"  rel err {e:.3e}")
     assert e <= TOL[torch.bfloat16]
+
+
+# --------------------------------------- rotation switched off (ablation)
+@pytest.fixture
+def restore_rotation():
+    yield
+    adamas.set_rotation(True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_encode_without_rotation(ora, restore_rotation, d, dt):
+    adamas.set_rotation(False)
+    x = synth.random_values((2, 3, 777, d), _dt(dt), seed=31, device=DEV)
+    codes = torch.zeros((2, 3, 777, d // 4), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(x, codes)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), ora.encode_keys(host(x), rotate=False))
+
+
+@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT])
+def test_decode_without_rotation(ora, restore_rotation, restore_mode, mode):
+    adamas.set_rotation(False)
+    adamas.set_decode_mode(mode)
+    w = synth.LLAMA2_32K.replace(hq=4, hkv=4, n_ctx=20000, cap=20000, budget=256)
+    lay = synth.make_layer(w, 2, DEV)
+    codes = torch.zeros((1, 4, 20000, 32), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    idx = torch.empty((1, 4, 256), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, 20000, 256, idx_out=idx)
+    torch.cuda.synchronize()
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    ocodes = ora.encode_keys(k, rotate=False)
+    assert np.array_equal(codes.cpu().numpy(), ocodes)
+    oout, _, oidx = ora.decode_step(q, k, v, ocodes, 20000, 256, rotate=False)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert rel_err(out, oout) <= TOL[torch.bfloat16]
