@@ -376,3 +376,16 @@ def test_decode_without_rotation(ora, restore_rotation, restore_mode, mode):
     oout, _, oidx = ora.decode_step(q, k, v, ocodes, 20000, 256, rotate=False)
     assert np.array_equal(idx.cpu().numpy(), oidx)
     assert rel_err(out, oout) <= TOL[torch.bfloat16]
+
+
+def test_quality_dense_reference_matches_oracle(ora):
+    # the sweep's dense reference is exact attention over every row
+    from compressed_key_sparse_amd.quality import dense_attention
+    w = synth.LLAMA32_GQA_1M.replace(hq=6, hkv=2, n_ctx=2000, cap=2000)
+    lay = synth.make_layer(w, 0, DEV)
+    got = dense_attention(lay["q"], lay["k"], lay["v"])
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    idx = np.tile(np.arange(2000, dtype=np.int32), (1, 6, 1))
+    _, ref64 = ora.sparse_attend(q, k, v, idx)
+    e = float(np.linalg.norm(got.cpu().double().numpy() - ref64) / np.linalg.norm(ref64))
+    assert e < 1e-5
