@@ -69,6 +69,8 @@ def load():
     lib.adamas_select_topk_keep.argtypes = [P, i32, i32, i64, i32, i32, i32, i32, P, P, sz, P]
     lib.adamas_decode_step_keep.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32,
                                             i32, i32, f32, P, P, P, sz, P]
+    lib.adamas_decode_append_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i64,
+                                              i64, i32, i32, i32, f32, P, P, P, sz, P]
     lib.adamas_workspace_bytes.argtypes = [i32, i32, i32, i32, i64, i32, i32]
     lib.adamas_workspace_bytes.restype = sz
     lib.adamas_status_string.argtypes = [i32]
@@ -85,7 +87,8 @@ def load():
     for fn in ("adamas_set_decode_mode", "adamas_decode_path"):
         getattr(lib, fn).restype = i32
     for fn in ("adamas_encode_keys", "adamas_score", "adamas_select_topk", "adamas_sparse_attend",
-               "adamas_decode_step", "adamas_select_topk_keep", "adamas_decode_step_keep"):
+               "adamas_decode_step", "adamas_select_topk_keep", "adamas_decode_step_keep",
+               "adamas_decode_append_step"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -294,4 +297,39 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0, o
     else:
         st = load().adamas_decode_step_keep(*head, int(n_sink), int(n_recent), *tail)
     _check(st, "adamas_decode_step")
+    return out
+
+
+def decode_append_step(q, k, v, k_codes, lens, max_len: int, budget: int, k_new=None,
+                       v_new=None, scale: float = 0.0, out=None, idx_out=None,
+                       ws: Workspace | None = None, stream=None, n_sink: int = 0,
+                       n_recent: int = 0) -> torch.Tensor:
+    """One decode step over sequences of lengths lens (int32 [B], on the device),
+    appending k_new / v_new [B][Hkv][d] at row lens[b] of the caches when given
+    (adamas_decode_append_step).  lens is not advanced."""
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    if k.dtype != q.dtype or v.dtype != q.dtype or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q, k, v must share dtype; k and v share shape")
+    if tuple(k_codes.shape) != (B, Hkv, cap, d // 4) or k_codes.dtype != torch.uint8:
+        raise ValueError("k_codes must be uint8 [B][Hkv][cap][d/4]")
+    if lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
+        raise ValueError("lens must be int32 [B]")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        for t in (k_new, v_new):
+            if t.dtype != q.dtype or tuple(t.shape) != (B, Hkv, d):
+                raise ValueError("k_new, v_new must be [B][Hkv][d] of q's dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    nb = load().adamas_workspace_bytes(OP_DECODE_STEP, B, Hq, Hkv, max_len, budget, d)
+    buf = _ws_for(q.device, ws).get(nb)
+    st = load().adamas_decode_append_step(
+        _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"), _dev_ptr(k, "k"),
+        _dev_ptr(v, "v"), _dev_ptr(k_codes, "k_codes"), _dev_ptr(lens, "lens"), _dtype_code(q), B,
+        Hq, Hkv, d, cap, max_len, budget, int(n_sink), int(n_recent), float(scale),
+        _dev_ptr(out, "out"), _dev_ptr(idx_out, "idx_out"), _dev_ptr(buf, "ws"), buf.numel(),
+        _stream(q, stream))
+    _check(st, "adamas_decode_append_step")
     return out

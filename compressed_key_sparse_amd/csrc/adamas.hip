@@ -242,14 +242,21 @@ struct DecodeArgs {
   int32_t* idx;
   void* out;
   int n_sink, n_recent;
+  RaggedArgs rg;  // lens == nullptr: every sequence holds n_ctx rows
 };
 
 template <int D, int G, bool BF>
 void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
-  k_decode<D, G, BF><<<grid, kDecodeThreads, p.sel.lds, s>>>(
-      a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
-      p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
-      a.out, a.n_sink, a.n_recent, rotation_on());
+  if (a.rg.lens != nullptr)
+    k_decode<D, G, BF, true><<<grid, kDecodeThreads, p.sel.lds, s>>>(
+        a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
+        p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx, a.out,
+        a.n_sink, a.n_recent, rotation_on(), a.rg);
+  else
+    k_decode<D, G, BF, false><<<grid, kDecodeThreads, p.sel.lds, s>>>(
+        a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
+        p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx, a.out,
+        a.n_sink, a.n_recent, rotation_on(), a.rg);
 }
 
 template <int D, int G, bool BF>
@@ -454,6 +461,38 @@ int adamas_sparse_attend(const void* q, const void* k, const void* v, int dtype,
   return launch_status();
 }
 
+}  // extern "C"
+
+namespace {
+
+// The last-arrival schedule: the fused decode kernel, then (when the
+// selection is too large to attend inside it) the attention kernel over the
+// selected rows.
+int launch_last_arrival(const DecodePlan& p, const DecodeArgs& a, int B, int head_dim, bool bf,
+                        uint8_t* w, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const dim3 grid((unsigned)p.sel.n_chunks, (unsigned)a.Hkv, (unsigned)B);
+  bool ok;
+  if (head_dim == 128)
+    ok = bf ? dispatch_decode<128, true>(G, p, grid, stream, a)
+            : dispatch_decode<128, false>(G, p, grid, stream, a);
+  else
+    ok = bf ? dispatch_decode<64, true>(G, p, grid, stream, a)
+            : dispatch_decode<64, false>(G, p, grid, stream, a);
+  if (!ok) return ADAMAS_ERR_UNSUPPORTED;
+  if (!p.fuse) {
+    const dim3 gatt((unsigned)p.att.splits, (unsigned)a.Hq, (unsigned)B);
+    launch_attend(head_dim, bf, gatt, stream, a.q, a.k, a.v, a.idx, a.Hq, a.Hkv, a.cap, a.budget,
+                  a.qscale, reinterpret_cast<float*>(w + p.att.part_off),
+                  reinterpret_cast<uint32_t*>(w + kCtrlAttend), a.out);
+  }
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
 int adamas_decode_step_keep(const void* q, const void* k, const void* v, const uint8_t* k_codes,
                             int dtype, int B, int Hq, int Hkv, int head_dim, int64_t cap,
                             int64_t n_ctx, int budget, int n_sink, int n_recent, float scale,
@@ -486,7 +525,7 @@ int adamas_decode_step_keep(const void* q, const void* k, const void* v, const u
     if (gp.ok) {
       if (ws_bytes < gp.total) return ADAMAS_ERR_WORKSPACE;
       DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
-                   nullptr, nullptr, idx_out, out, n_sink, n_recent};
+                   nullptr, nullptr, idx_out, out, n_sink, n_recent, {}};
       const dim3 grid((unsigned)gp.n_chunks, (unsigned)Hkv, (unsigned)B);
       const bool ok = head_dim == 128
                           ? (bf ? dispatch_decode_gs<128, true>(G, gp, grid, stream, a, w)
@@ -504,23 +543,8 @@ int adamas_decode_step_keep(const void* q, const void* k, const void* v, const u
                                 : reinterpret_cast<int32_t*>(w + p.idx_off);
   DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
                reinterpret_cast<uint32_t*>(w + p.sel.cand_off),
-               reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent};
-  const dim3 grid((unsigned)p.sel.n_chunks, (unsigned)Hkv, (unsigned)B);
-  bool ok;
-  if (head_dim == 128)
-    ok = bf ? dispatch_decode<128, true>(G, p, grid, stream, a)
-            : dispatch_decode<128, false>(G, p, grid, stream, a);
-  else
-    ok = bf ? dispatch_decode<64, true>(G, p, grid, stream, a)
-            : dispatch_decode<64, false>(G, p, grid, stream, a);
-  if (!ok) return ADAMAS_ERR_UNSUPPORTED;
-  if (!p.fuse) {
-    const dim3 gatt((unsigned)p.att.splits, (unsigned)Hq, (unsigned)B);
-    launch_attend(head_dim, bf, gatt, stream, q, k, v, idx, Hq, Hkv, cap, budget, a.qscale,
-                  reinterpret_cast<float*>(w + p.att.part_off),
-                  reinterpret_cast<uint32_t*>(w + kCtrlAttend), out);
-  }
-  return launch_status();
+               reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent, {}};
+  return launch_last_arrival(p, a, B, head_dim, bf, w, stream);
 }
 
 int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_t* k_codes,
@@ -529,6 +553,41 @@ int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_
                        void* ws, size_t ws_bytes, hipStream_t stream) {
   return adamas_decode_step_keep(q, k, v, k_codes, dtype, B, Hq, Hkv, head_dim, cap, n_ctx,
                                  budget, 0, 0, scale, out, idx_out, ws, ws_bytes, stream);
+}
+
+int adamas_decode_append_step(const void* q, const void* k_new, const void* v_new, void* k,
+                              void* v, uint8_t* k_codes, const int32_t* lens, int dtype, int B,
+                              int Hq, int Hkv, int head_dim, int64_t cap, int64_t max_len,
+                              int budget, int n_sink, int n_recent, float scale, void* out,
+                              int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
+  const bool app = k_new != nullptr;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || cap < 1 || max_len < 1 || max_len > cap ||
+      budget < 1 || !isfinite(scale) || n_sink < 0 || n_recent < 0 || (v_new != nullptr) != app)
+    return ADAMAS_ERR_INVALID;
+  if (budget > kMaxBudget || max_len > INT32_MAX || Hq / Hkv > kMaxG ||
+      (int64_t)B * Hq > kMaxGroups || Hq > 65535 || B > 65535)
+    return ADAMAS_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_codes) ||
+      !aligned16(out) || lens == nullptr || reinterpret_cast<uintptr_t>(lens) % 4 != 0)
+    return ADAMAS_ERR_INVALID;
+  if (app && (!aligned16(k_new) || !aligned16(v_new))) return ADAMAS_ERR_INVALID;
+  if (idx_out != nullptr && !aligned16(idx_out)) return ADAMAS_ERR_INVALID;
+  if (ws == nullptr || !aligned16(ws)) return ADAMAS_ERR_WORKSPACE;
+  if (ws_bytes < adamas_workspace_bytes(ADAMAS_OP_DECODE_STEP, B, Hq, Hkv, max_len, budget,
+                                        head_dim))
+    return ADAMAS_ERR_WORKSPACE;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const DecodePlan p = plan_decode(B, Hq, Hkv, max_len, budget, head_dim);
+  if (ws_bytes < p.total) return ADAMAS_ERR_WORKSPACE;
+  int32_t* idx = idx_out != nullptr ? idx_out
+                 : p.fuse       ? nullptr
+                                : reinterpret_cast<int32_t*>(w + p.idx_off);
+  DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, max_len, budget, attend_qscale(scale, head_dim),
+               reinterpret_cast<uint32_t*>(w + p.sel.cand_off),
+               reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent,
+               RaggedArgs{lens, k_new, v_new, k, v, k_codes}};
+  return launch_last_arrival(p, a, B, head_dim, dtype == ADAMAS_BF16, w, stream);
 }
 
 int adamas_set_rotation(int on) {

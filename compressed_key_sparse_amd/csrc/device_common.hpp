@@ -332,6 +332,22 @@ ADM_DEV QPlanes make_qplanes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3)
   return r;
 }
 
+// Manhattan distance between two packed code rows of D dims (D/16 words),
+// with the plane formulas of the scan (one 16-byte unit of 4 words at a time).
+template <int D>
+ADM_DEV uint32_t code_distance(const uint32_t* a, const uint32_t* b) {
+  uint32_t s = 0;
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) {
+    const QPlanes qa = make_qplanes(a[4 * u], a[4 * u + 1], a[4 * u + 2], a[4 * u + 3]);
+    const uint32_t* w = b + 4 * u;
+    s += __popc(therm_p(w[0]) ^ qa.p[0]) + __popc(therm_p(w[1]) ^ qa.p[1]) +
+         __popc(therm_p(w[2]) ^ qa.p[2]) + __popc(therm_p(w[3]) ^ qa.p[3]) +
+         __popc(therm_t(w[0], w[1]) ^ qa.t[0]) + __popc(therm_t(w[2], w[3]) ^ qa.t[1]);
+  }
+  return s;
+}
+
 // Swap values between lane pairs (l, l^1) with a DPP quad permutation.
 ADM_DEV uint32_t swap_pair(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);

@@ -271,11 +271,21 @@ ADM_DEV float slice_dot(const RowRaw<D, BF>& q, const RowRaw<D, BF>& k) {
 // and a weighted V sum; at the end the NW wavefront partials (m, l, o) are
 // merged by log-sum-exp.  On return s_res[0] = m, s_res[1] = l,
 // s_res[2 + t] = o_t.  s_part holds NW*(2+D) floats plus NT/16 spare.
-template <int D, bool BF, int NT>
+// With OVR, row ovr.tok (when >= 0) is read from ovr.k / ovr.v at element
+// offset ovr.off instead of the cache (a row appended in the same launch).
+// Unselected slots carry token -1 and never match.
+struct RowOverride {
+  const void* k;
+  const void* v;
+  int64_t tok;
+  int64_t off;
+};
+
+template <int D, bool BF, int NT, bool OVR = false>
 ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
                          const void* __restrict__ v, int64_t qoff, int64_t kvrow0, int64_t cap,
                          const int32_t* rows, int nrows, float qscale, float* s_part,
-                         float* s_res) {
+                         float* s_res, RowOverride ovr = {}) {
   constexpr int EL = D / 16, NS = NT / 16, NW = NT / kWave, PW = 2 + D;
   // fp32 rows are twice the bytes: half the rows per batch keeps registers in budget
   constexpr int RB = BF ? kAttendRowsPerSlot : kAttendRowsPerSlot / 2;
@@ -300,8 +310,13 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const int64_t r = kvrow0 + (tok[j] >= 0 ? tok[j] : 0);
-      kr[j].load(k, r * D + l16 * EL);
-      vr[j].load(v, r * D + l16 * EL);
+      if (OVR && tok[j] >= 0 && tok[j] == ovr.tok) {
+        kr[j].load(ovr.k, ovr.off + l16 * EL);
+        vr[j].load(ovr.v, ovr.off + l16 * EL);
+      } else {
+        kr[j].load(k, r * D + l16 * EL);
+        vr[j].load(v, r * D + l16 * EL);
+      }
     }
     float sc[RB];
     float mloc = -INFINITY;
@@ -488,13 +503,28 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
 // a histogram in LDS, and writes the chunk's candidates.  The last workgroup
 // of the KV head selects the budget for its G query heads (§5.2) and, when
 // fuse_attend is set, attends over the selected rows (§6) and writes out.
-template <int D, int G, bool BF>
+// Ragged batches with the decoded token appended in the same launch
+// (adamas_decode_append_step): sequence b holds lens[b] cached rows; when
+// k_new is set its row lens[b] receives the step's key (codes, K) and value
+// and the step attends over lens[b] + 1 rows.  n_ctx is then the host's
+// bound on those lengths (the grid is planned for it); lens are clamped to
+// it and to the cache.
+struct RaggedArgs {
+  const int32_t* lens;         // [B]
+  const void* k_new;           // [B][Hkv][D] elements, or null: nothing appended
+  const void* v_new;           // [B][Hkv][D]
+  void* k_cache;               // the K, V and code caches again, written at row lens[b]
+  void* v_cache;
+  uint8_t* code_cache;
+};
+
+template <int D, int G, bool BF, bool RAG>
 __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
     int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
-    void* __restrict__ out, int n_sink, int n_recent, int rotate) {
+    void* __restrict__ out, int n_sink, int n_recent, int rotate, RaggedArgs rg) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), W = D / 16;
   constexpr int E = D / 64, kLanesPerWord = 16 / E, PW = 2 + D;
@@ -511,8 +541,10 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   float* s_part = reinterpret_cast<float*>(fhist + NBP);
   float* s_res = s_part + NW * PW + NT / 16;  // after attend_rows' per-slot scratch
   int32_t* sidx = reinterpret_cast<int32_t*>(s_res + PW);  // fused attention only
-  const int bsel = (int)min((int64_t)budget, n_ctx);
-  uint32_t* scand = reinterpret_cast<uint32_t*>(sidx + (fuse_attend ? ((bsel + 3) & ~3) : 0));
+  const int bsel_max = (int)min((int64_t)budget, n_ctx);
+  uint32_t* scand =
+      reinterpret_cast<uint32_t*>(sidx + (fuse_attend ? ((bsel_max + 3) & ~3) : 0));
+  uint32_t* s_knew = s_tmp + 24;  // ragged: the appended key's code row (W <= 8 words)
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id; rotating the
   // chunk index with the KV head spreads every chunk offset of the code cache
@@ -522,6 +554,19 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   const int hkv = blockIdx.y, b = blockIdx.z;
   const int kpad = 1 << kpad_log2;
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  static_assert(W <= 8, "the appended code row lives in s_tmp[24..32)");
+  // this sequence's rows and, when appending, the new token's position
+  int64_t n_b = n_ctx, pos_new = -1;
+  if constexpr (RAG) {
+    const bool app = rg.k_new != nullptr;
+    const int64_t lim = (cap < n_ctx ? cap : n_ctx) - (app ? 1 : 0);
+    int64_t L = rg.lens[b];
+    L = L < 0 ? 0 : (L > lim ? lim : L);
+    n_b = L + (app ? 1 : 0);
+    pos_new = app ? L : -1;
+  }
+  const int bsel = (int)min((int64_t)budget, n_b);
+  const int active = (int)((n_b + chunk - 1) / chunk);  // chunks holding rows of this sequence
   for (int i = threadIdx.x; i < G * NBP; i += NT) shist[i] = 0;
   // the query (wavefront g holds head g, G <= NW), then the first batch of
   // codes, then the query's encoding while the codes are in flight
@@ -530,12 +575,56 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   const uint2 qraw =
       load_elems_raw<E, BF>(q, ((int64_t)b * Hq + (int64_t)hkv * G + gq) * D + lane * E);
   const int64_t t0 = (int64_t)c * chunk;
-  const int valid = (int)min((int64_t)chunk, n_ctx - t0);
+  // rows of the grid's chunk (the planned bound), then of this sequence
+  const int valid_grid = (int)min((int64_t)chunk, n_ctx - t0);
   const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
   uint4 first[kDecodeScanDepth];
-  scan_load<NT, kDecodeScanDepth>(reinterpret_cast<const uint4*>(kbase), valid * (D / 64), 0,
+  scan_load<NT, kDecodeScanDepth>(reinterpret_cast<const uint4*>(kbase), valid_grid * (D / 64), 0,
                                   first);
   __builtin_amdgcn_sched_barrier(0);  // keep the code loads ahead of the wait for q
+  if constexpr (RAG) {
+    if (c >= active) {
+      if (n_b == 0 && c == 0) {  // an empty sequence: zeros, nothing selected
+        for (int g = 0; g < G; ++g) {
+          const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
+          if (threadIdx.x < D) store_out<BF>(out, row * D + threadIdx.x, 0.0f);
+          if (idx)
+            for (int j = threadIdx.x; j < budget; j += NT) idx[row * budget + j] = -1;
+        }
+      }
+      return;  // no rows of this sequence in this chunk
+    }
+  }
+  const int valid = (int)min((int64_t)chunk, n_b - t0);
+  const bool has_new = RAG && pos_new >= t0 && pos_new < t0 + valid;
+  const int valid_mem = valid - (has_new ? 1 : 0);  // rows read from the code cache
+  if constexpr (RAG) {
+    if (has_new && wid == NW - 1) {
+      // the appended token: encode its key, write its code row and its K and
+      // V rows for later steps.  Within this launch its distance comes from
+      // s_knew and its K, V from k_new, v_new (the final workgroup may sit on
+      // another XCD, whose L2 does not see these stores before the launch ends)
+      const int64_t src = ((int64_t)b * Hkv + hkv) * D;
+      const uint2 kraw = load_elems_raw<E, BF>(rg.k_new, src + lane * E);
+      float y[E];
+      widen_elems<E, BF>(kraw, y);
+      const uint32_t word = wave_encode<D>(y, rotate != 0);
+      const int64_t crow = ((int64_t)b * Hkv + hkv) * cap + pos_new;
+      if (lane % kLanesPerWord == 0) {
+        s_knew[lane / kLanesPerWord] = word;
+        reinterpret_cast<uint32_t*>(rg.code_cache + crow * (D / 4))[lane / kLanesPerWord] = word;
+      }
+      constexpr int kRowBytes = D * (BF ? 2 : 4);
+      if (lane < kRowBytes / 16) {
+        const uint4 kv = reinterpret_cast<const uint4*>(
+            static_cast<const uint8_t*>(rg.k_new) + src * (BF ? 2 : 4))[lane];
+        const uint4 vv = reinterpret_cast<const uint4*>(
+            static_cast<const uint8_t*>(rg.v_new) + src * (BF ? 2 : 4))[lane];
+        reinterpret_cast<uint4*>(static_cast<uint8_t*>(rg.k_cache) + crow * kRowBytes)[lane] = kv;
+        reinterpret_cast<uint4*>(static_cast<uint8_t*>(rg.v_cache) + crow * kRowBytes)[lane] = vv;
+      }
+    }
+  }
   if (wid < G) {
     float y[E];
     widen_elems<E, BF>(qraw, y);
@@ -545,12 +634,20 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
   lds_sync();
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
-  const KeepRange keep(t0, valid, n_sink, n_ctx - n_recent);
-  scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
+  const KeepRange keep(t0, valid, n_sink, n_b - n_recent);
+  scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid_mem, qp, [&](int g, int tok, uint32_t d) {
     const uint32_t key = keep.key(tok, d);
     sdist[g * chunk + tok] = (uint16_t)key;
     atomicAdd(&shist[g * NBP + key], 1u);
   }, &first);
+  if constexpr (RAG) {
+    if (has_new && (int)threadIdx.x < G) {
+      const int g = threadIdx.x, tok = valid_mem;
+      const uint32_t key = keep.key(tok, code_distance<D>(sq + g * W, s_knew));
+      sdist[g * chunk + tok] = (uint16_t)key;
+      atomicAdd(&shist[g * NBP + key], 1u);
+    }
+  }
   lds_sync();
   const int kc = min(budget, valid);
   for (int g = 0; g < G; ++g) {
@@ -561,16 +658,21 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     lds_sync();
     lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
   }
-  if (!arrive_last<NT>(&counters[b * Hkv + hkv], n_chunks, s_tmp)) return;
+  if (!arrive_last<NT>(&counters[b * Hkv + hkv], active, s_tmp)) return;
   const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap;
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-    final_select<NT>(cand + row * n_chunks * kpad, n_chunks * kpad, kpad_log2, chunk, NB, bsel,
+    final_select<NT>(cand + row * n_chunks * kpad, active * kpad, kpad_log2, chunk, NB, bsel,
                      budget, fuse_attend ? sidx : nullptr, idx ? idx + row * budget : nullptr,
                      scand, mcap, fhist, s_tmp);
     if (fuse_attend) {
-      attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx, bsel,
-                             qscale, s_part, s_res);
+      if constexpr (RAG)
+        attend_rows<D, BF, NT, true>(q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part,
+                                     s_res, RowOverride{rg.k_new, rg.v_new,
+                                                        rg.k_new != nullptr ? pos_new : -2,
+                                                        ((int64_t)b * Hkv + hkv) * D});
+      else
+        attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part, s_res);
       if (threadIdx.x < D) {
         const float L = s_res[1];
         store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? s_res[2 + threadIdx.x] / L : 0.0f);

@@ -227,6 +227,46 @@ int adamas_decode_step_keep(const void *q, const void *k, const void *v,
                             int32_t *idx_out, void *ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/*
+ * One decode step of a batch whose sequences differ in length, with the
+ * step's new token written into the caches in the same launch.  The
+ * article's compressed cache (§3.1) takes each new token's packed key code at
+ * its position as it is generated; here that key is rotated and bucketed
+ * (§2.1-§2.2) inside the step, scored with the rest (§2.3), and can be
+ * selected (§5.2) and attended (§6) in the step that adds it.  The step never
+ * allocates or reads host state that changes between steps, so it can be
+ * replayed from a HIP graph (graph launch is the article's small-batch
+ * latency measure, §5.1).
+ *   lens   [B] int32 device memory: rows already cached per sequence (L_b).
+ *          Read only; the caller advances it between steps (the library never
+ *          writes it), so the call can be captured in a HIP graph and replayed.
+ *   k_new, v_new  [B][Hkv][head_dim] of dtype, or both NULL.  When set, row
+ *          L_b of k, v and k_codes (for every KV head) receives the new key,
+ *          value and key code, and sequence b attends over its L_b + 1 rows,
+ *          the new one included.  When NULL nothing is written and sequence b
+ *          attends over its L_b rows.
+ *   k, v, k_codes  the caches of adamas_decode_step ([B][Hkv][cap][...]),
+ *          written only at row L_b and only when k_new is set.
+ *   max_len  host bound on the rows any sequence attends over (L_b + 1 with
+ *          k_new, L_b without); 1 <= max_len <= cap.  The launch is planned
+ *          for it: L_b is clamped to [0, max_len - 1] with k_new, to
+ *          [0, max_len] without.  The workspace is adamas_workspace_bytes(
+ *          ADAMAS_OP_DECODE_STEP, B, Hq, Hkv, max_len, budget, head_dim).
+ * Everything else is as adamas_decode_step_keep, with n_ctx = each
+ * sequence's own row count (so the recent window ends at its last row, and
+ * each sequence keeps min(budget, rows) tokens).  A sequence with no rows
+ * gets a zero output and idx_out rows of -1.  Always the LAST_ARRIVAL
+ * schedule, whatever adamas_set_decode_mode chose.  Errors are returned
+ * before anything is enqueued: ADAMAS_ERR_INVALID for bad sizes, a NULL or
+ * misaligned pointer (lens needs 4 bytes, the rest 16), or only one of
+ * k_new, v_new; ADAMAS_ERR_WORKSPACE for a short workspace.
+ */
+int adamas_decode_append_step(const void *q, const void *k_new, const void *v_new, void *k,
+                              void *v, uint8_t *k_codes, const int32_t *lens, int dtype, int B,
+                              int Hq, int Hkv, int head_dim, int64_t cap, int64_t max_len,
+                              int budget, int n_sink, int n_recent, float scale, void *out,
+                              int32_t *idx_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes needed by `op` for the given shape (0 for invalid shapes). */
 size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx,
                               int budget, int head_dim);

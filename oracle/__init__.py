@@ -217,5 +217,40 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,
     return out, out64, idx
 
 
+def decode_append_step(q, k, v, k_codes, lens, max_len: int, budget: int, k_new=None,
+                       v_new=None, scale: float = 0.0, n_sink: int = 0, n_recent: int = 0,
+                       rotate: bool = True):
+    """A decode step over sequences of their own lengths, each first taking the
+    step's new key and value at its next row (the compressed cache of §3.1
+    stores each new token's code at its position; the step itself is §2-§6 on
+    that sequence's rows).  Works on copies -> (out, out64, idx, k, v, k_codes)
+    with the caches as the step leaves them.
+
+    Sequence b holds L_b = lens[b] rows, clamped to [0, max_len - 1] when a
+    token is appended and to [0, max_len] otherwise; it is decoded on its own
+    with n_ctx = L_b (+1 with the new token), so its recent window ends at its
+    own last row.  No rows: a zero output and an all -1 selection."""
+    k, v, k_codes = (np.array(a, copy=True) for a in (k, v, k_codes))
+    B, Hq, d = q.shape
+    app = k_new is not None
+    out = np.zeros((B, Hq, d), q.dtype)
+    out64 = np.zeros((B, Hq, d), np.float64)
+    idx = np.full((B, Hq, budget), -1, np.int32)
+    for b in range(B):
+        L = min(max(int(lens[b]), 0), max_len - (1 if app else 0))
+        if app:
+            k[b, :, L] = k_new[b]
+            v[b, :, L] = v_new[b]
+            row = encode_keys(np.ascontiguousarray(k_new[b][None, :, None, :]), rotate=rotate)
+            k_codes[b, :, L] = row[0, :, 0]
+        n = L + (1 if app else 0)
+        if n == 0:
+            continue
+        o, o64, ix = decode_step(q[b:b + 1], k[b:b + 1], v[b:b + 1], k_codes[b:b + 1], n, budget,
+                                 scale, n_sink, n_recent, rotate)
+        out[b], out64[b], idx[b] = o[0], o64[0], ix[0]
+    return out, out64, idx, k, v, k_codes
+
+
 def f64_to_bf16_bits(x: float) -> int:
     return int(_load().ora_f64_to_bf16(float(x)))

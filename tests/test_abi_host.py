@@ -188,3 +188,31 @@ def test_rotation_switch_validation(lib):
     assert lib.adamas_set_rotation(-1) == INVALID
     assert lib.adamas_set_rotation(0) == OK
     assert lib.adamas_set_rotation(1) == OK
+
+
+def test_append_step_validation(lib):
+    f = lib.adamas_decode_append_step
+    need = lib.adamas_workspace_bytes(2, 2, 8, 4, 1000, 64, 128)
+
+    def call(**kw):
+        return f(A, kw.get("kn", A), kw.get("vn", A), A, A, kw.get("codes", A),
+                 kw.get("lens", A), kw.get("dt", 1), 2, kw.get("hq", 8), kw.get("hkv", 4),
+                 kw.get("d", 128), kw.get("cap", 1024), kw.get("max_len", 1000),
+                 kw.get("budget", 64), kw.get("sink", 0), kw.get("recent", 0),
+                 ctypes.c_float(0.0), A, kw.get("idx", None), A, kw.get("ws", need), None)
+    assert call(max_len=0) == INVALID
+    assert call(max_len=1025) == INVALID           # beyond the cache
+    assert call(kn=None) == INVALID                # only one of k_new, v_new
+    assert call(vn=None) == INVALID
+    assert call(lens=None) == INVALID
+    assert call(lens=A + 2) == INVALID             # lens needs 4-byte alignment
+    assert call(kn=MIS) == INVALID
+    assert call(codes=MIS) == INVALID
+    assert call(idx=MIS) == INVALID
+    assert call(hkv=3) == INVALID
+    assert call(hq=36, hkv=4) == UNSUPPORTED
+    assert call(d=96) == UNSUPPORTED
+    assert call(dt=3) == UNSUPPORTED
+    assert call(budget=0) == INVALID
+    assert call(sink=-1) == INVALID
+    assert call(ws=need - 1) == WORKSPACE

@@ -465,3 +465,72 @@ def test_decode_step_finds_planted_needles(ora):
     _, _, idx = ora.decode_step(q, k, v, codes, n_ctx=8192, budget=256)
     found = sum(len(set(lay["needles"][0, h, 0]) & set(idx[0, h].tolist())) for h in range(4))
     assert found >= 0.75 * 4 * w.needles
+
+
+# --------------------------------------------------------------------------
+# ragged decode step with the new token appended (§3.1 cache, §2-§6 per sequence)
+def _append_case(dtype, seed, B=4, Hq=4, Hkv=2, cap=40, d=64):
+    import torch
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = synth.random_values((B, Hq, d), dt, seed)
+    k = synth.random_values((B, Hkv, cap, d), dt, seed + 1)
+    v = synth.random_values((B, Hkv, cap, d), dt, seed + 2)
+    kn = synth.random_values((B, Hkv, d), dt, seed + 3)
+    vn = synth.random_values((B, Hkv, d), dt, seed + 4)
+    return [synth.to_numpy_bits(t) for t in (q, k, v, kn, vn)], dt
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_step_full_budget_is_dense_attention(ora, dtype):
+    # budget >= every sequence's rows: the step is exact softmax attention over
+    # the sequence's first L_b cached rows plus the appended one, whatever the codes
+    (q, k, v, kn, vn), dt = _append_case(dtype, 40)
+    codes = ora.encode_keys(k)
+    lens = np.array([0, 7, 39, 25], np.int32)
+    out, out64, idx, k2, v2, c2 = ora.decode_append_step(q, k, v, codes, lens, 40, 64, kn, vn)
+    f64 = lambda a: synth.bits_to_torch(a, dt).double().numpy()
+    qd, kd, vd, knd, vnd = (f64(a) for a in (q, k, v, kn, vn))
+    for b in range(4):
+        L = int(lens[b])
+        for h in range(4):
+            kk = np.concatenate([kd[b, h // 2, :L], knd[b, h // 2][None]])
+            vv = np.concatenate([vd[b, h // 2, :L], vnd[b, h // 2][None]])
+            want = dense_attention(qd[b, h], kk, vv, 1 / math.sqrt(64))
+            assert np.allclose(out64[b, h], want, rtol=1e-12, atol=1e-12)
+            assert list(idx[b, h, :L + 1]) == list(range(L + 1))
+            assert (idx[b, h, L + 1:] == -1).all()
+
+
+def test_append_step_writes_only_the_next_row(ora):
+    (q, k, v, kn, vn), _ = _append_case("bf16", 50)
+    codes = ora.encode_keys(k)
+    lens = np.array([3, 0, 39, 100], np.int32)   # the last one clamps to max_len - 1 = 39
+    _, _, _, k2, v2, c2 = ora.decode_append_step(q, k, v, codes, lens, 40, 8, kn, vn)
+    want_codes = ora.encode_keys(kn[:, :, None, :])[:, :, 0]
+    for b, L in enumerate([3, 0, 39, 39]):
+        assert np.array_equal(k2[b, :, L], kn[b]) and np.array_equal(v2[b, :, L], vn[b])
+        assert np.array_equal(c2[b, :, L], want_codes[b])
+        others = [t for t in range(40) if t != L]
+        assert np.array_equal(k2[b][:, others], k[b][:, others])
+        assert np.array_equal(v2[b][:, others], v[b][:, others])
+        assert np.array_equal(c2[b][:, others], codes[b][:, others])
+
+
+def test_append_step_recent_window_and_empty_sequences(ora):
+    (q, k, v, kn, vn), _ = _append_case("f32", 60)
+    codes = ora.encode_keys(k)
+    lens = np.array([30, 12, 0, 5], np.int32)
+    # a recent window of one always keeps the appended token
+    _, _, idx, *_ = ora.decode_append_step(q, k, v, codes, lens, 40, 4, kn, vn, n_recent=1)
+    for b, L in enumerate(lens):
+        assert (idx[b] == L).any(axis=-1).all()
+    # nothing appended: an empty sequence gives zeros and no selection, the
+    # others match the plain step over their own rows
+    out, out64, idx, k2, _, _ = ora.decode_append_step(q, k, v, codes, lens, 40, 4)
+    assert np.array_equal(k2, k)
+    assert not out64[2].any() and (idx[2] == -1).all()
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        o, o64, ix = ora.decode_step(q[b:b + 1], k[b:b + 1], v[b:b + 1], codes[b:b + 1], int(L), 4)
+        assert np.array_equal(ix[0], idx[b]) and np.array_equal(o64[0], out64[b])
