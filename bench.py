@@ -18,6 +18,16 @@ Prints ONE JSON line with:
                eager pass over the same steps, against 8 TB/s;
   cpu_baseline the CPU oracle timed on a bounded sample of layers on the host
                cores, scaled to tokens/s.
+
+--workload selects one of two further measurements (same JSON fields):
+  llama3.2-3b-gqa-1m        one GQA layer (24 query / 8 KV heads) over 1,048,576
+                            tokens, budget 1024; four layers' caches are cycled
+                            so the code cache never sits in the last-level cache;
+  batch16-mha-64k-append4k  16 sequences x 32 heads x 65536 rows, budget 512: the
+                            ragged decode step that appends each sequence's new
+                            token (adamas_decode_append_step) on one stream while
+                            a 4096-token prefill chunk for one sequence is
+                            encoded and copied on a second stream.
 """
 from __future__ import annotations
 
@@ -31,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+HEADLINE = "llama2-mha-128k-32layers"
 METRIC = "decode-step tokens/s + achieved HBM GB/s at 128K ctx, budget 256, 1 GPU"
 
 
@@ -56,6 +67,8 @@ def parse():
                     help="target oracle CPU time for the baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a conversion kernel of known traffic (HBM counter scaling)")
+    ap.add_argument("--workload", default=HEADLINE,
+                    choices=(HEADLINE, "llama3.2-3b-gqa-1m", "batch16-mha-64k-append4k"))
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="print a compact summary of rocprofv3 CSV output under DIR and exit")
     return ap.parse_args()
@@ -144,6 +157,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     adamas.load()
+    if args.workload == "llama3.2-3b-gqa-1m":
+        return bench_gqa(args, dev)
+    if args.workload == "batch16-mha-64k-append4k":
+        return bench_batch_append(args, dev)
     w = synth.LLAMA2_128K_32L
     if args.n_ctx:
         w = w.replace(n_ctx=args.n_ctx, cap=args.n_ctx)
@@ -297,6 +314,253 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def stream_read_gbs(dev):
+    """What plain streaming reads reach on this device (4 GiB, beyond the
+    last-level cache), with the decode scan's own load instructions."""
+    import torch
+
+    import compressed_key_sparse_amd as adamas
+    sr = torch.ones(1 << 30, dtype=torch.int32, device=dev)
+    sink = adamas.stream_read(sr)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(5):
+        adamas.stream_read(sr, sink)
+    s1.record()
+    torch.cuda.synchronize()
+    return sr.numel() * 4 * 5 / (s0.elapsed_time(s1) * 1e-3) / 1e9
+
+
+def timed_launches(launch, n_launch, stream, K):
+    """Call launch(i) for i in [0, n_launch) K times, HIP events around each
+    call on `stream` -> (ms per pass of n_launch calls, mean launch us)."""
+    import numpy as np
+    import torch
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_launch)] for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(K):
+        for i in range(n_launch):
+            ev[s][i][0].record(stream)
+            launch(i)
+            ev[s][i][1].record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return (e0.elapsed_time(e1) / K,
+            float(np.mean([a.elapsed_time(b) for row in ev for a, b in row]) * 1e3))
+
+
+def result_line(metric, w, B, ms, K, warmup, cfg, kernel, per_launch, launch_us, stream_gbs,
+                extra, cpu):
+    achieved = per_launch / (launch_us * 1e-6) / 1e9
+    res = {
+        "metric": metric, "value": round(B / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": cfg,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": per_launch,
+                     "launch_us": round(launch_us, 3)},
+        "stream_read": {"kernel": "adamas_stream_read over 4 GiB", "gbs": round(stream_gbs, 1),
+                        "frac_of_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
+                        "decode_over_stream": round(achieved / stream_gbs, 4)},
+        "cpu_baseline": cpu,
+    }
+    res.update(extra)
+    print(json.dumps(res), flush=True)
+
+
+def bench_gqa(args, dev):
+    """One 1M-token GQA layer per step; four layers' caches cycled (1 GiB of
+    codes, beyond the 256 MB last-level cache).  Timed as a replayed HIP graph
+    of four steps."""
+    import torch
+
+    import compressed_key_sparse_amd as adamas
+    import synth
+    w = synth.LLAMA32_GQA_1M
+    B, Hq, Hkv, d, n = w.batch, w.hq, w.hkv, w.head_dim, w.n_ctx
+    bud = w.budget if args.budget == 256 else args.budget
+    print(f"[bench] setup: 4 x GQA {Hq}/{Hkv} heads x {n} tokens, budget {bud}", file=sys.stderr,
+          flush=True)
+    layers = []
+    for l in range(4):
+        lay = synth.make_layer(w, l, dev)
+        codes = torch.empty((B, Hkv, w.cap, d // 4), dtype=torch.uint8, device=dev)
+        adamas.encode_keys(lay["k"], codes)
+        layers.append((lay, codes, torch.empty_like(lay["q"])))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(dev)
+    ws = adamas.Workspace(dev)
+    ws.get(adamas.workspace_bytes(adamas.OP_DECODE_STEP, B, Hq, Hkv, n, bud, d))
+
+    def launch(i):
+        lay, codes, out = layers[i]
+        adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, n, bud, out=out, ws=ws,
+                           stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            for i in range(4):
+                launch(i)
+    K = args.steps
+    eager_ms, launch_us = timed_launches(launch, 4, stream, K)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(4):
+                launch(i)
+        for _ in range(args.warmup):
+            g.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(K):
+            g.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms = g0.elapsed_time(g1) / (4 * K)
+    per_launch = algorithmic_bytes(B, Hq, Hkv, d, n, bud, 2)
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline([layers[0][0]], w.replace(layers=1), n, bud, args.cpu_seconds)
+    result_line(
+        f"decode-step tokens/s + achieved HBM GB/s, GQA 24/8 heads at 1M ctx, budget {bud}, 1 GPU",
+        w, B, ms, K, args.warmup,
+        {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+         "n_ctx": n, "budget": bud, "layers_cycled": 4, "timing": "hip-graph replay"},
+        "adamas_decode_step (one layer)", per_launch, ms * 1e3, stream_read_gbs(dev),
+        {"eager_ms_per_step": round(eager_ms / 4, 4),
+         "eager_event_launch_us": round(launch_us, 3),
+         "decode_path": adamas.decode_path(B, Hq, Hkv, n, bud, d)}, cpu)
+
+
+def bench_batch_append(args, dev):
+    """16 sequences of 65536 rows: each step appends one token per sequence
+    and decodes (one launch on stream 1) while a 4096-token chunk for sequence
+    (step mod 16) is encoded and its K rows copied into the reserved tail rows
+    [65536, 69632) on stream 2.  Timed eagerly (the chunk's sequence changes
+    every step): step = both streams done."""
+    import numpy as np
+    import torch
+
+    import compressed_key_sparse_amd as adamas
+    import synth
+    w = synth.BATCH16_64K
+    B, Hq, Hkv, d, n = w.batch, w.hq, w.hkv, w.head_dim, w.n_ctx
+    bud = w.budget if args.budget == 256 else args.budget
+    print(f"[bench] setup: batch {B} x {Hq} heads x {n} rows, budget {bud}, append", file=sys.stderr,
+          flush=True)
+    lay = synth.make_layer(w, 0, dev)
+    codes = torch.empty((B, Hkv, w.cap, d // 4), dtype=torch.uint8, device=dev)
+    for b in range(B):
+        adamas.encode_keys(lay["k"][b:b + 1], codes[b:b + 1])
+    # every sequence holds n - 1 rows; the step appends row n - 1 and attends n
+    lens = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
+    kn = synth.random_values((B, Hkv, d), w.torch_dtype, 77, device=dev)
+    vn = synth.random_values((B, Hkv, d), w.torch_dtype, 78, device=dev)
+    chunks = [synth.make_chunk(w, s, dev) for s in range(4)]
+    out = torch.empty_like(lay["q"])
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    ws = adamas.Workspace(dev)
+    ws.get(adamas.workspace_bytes(adamas.OP_DECODE_STEP, B, Hq, Hkv, n, bud, d))
+    ev = {}
+
+    def decode():
+        adamas.decode_append_step(lay["q"], lay["k"], lay["v"], codes, lens, n, bud, k_new=kn,
+                                  v_new=vn, out=out, ws=ws, stream=s1)
+
+    def step(i, timed=None):
+        b = i % B
+        s2.wait_stream(s1)
+        with torch.cuda.stream(s2):
+            adamas.encode_keys(chunks[i % len(chunks)], codes[b:b + 1], pos=n,
+                               x_copy=lay["k"][b:b + 1], stream=s2)
+        if timed is not None:
+            timed[0].record(s1)
+        decode()
+        if timed is not None:
+            timed[1].record(s1)
+        s1.wait_stream(s2)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(K)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    marks[0].record(s1)
+    for i in range(K):
+        step(i, pairs[i])
+        marks[i + 1].record(s1)
+    torch.cuda.synchronize()
+    step_times = [marks[i].elapsed_time(marks[i + 1]) for i in range(K)]
+    ms = marks[0].elapsed_time(marks[K]) / K
+    launch_us = float(np.mean([a.elapsed_time(b) for a, b in pairs]) * 1e3)
+    # decode alone (no chunk on stream 2), for the launch's uncontended rate
+    alone_ms, alone_us = timed_launches(lambda i: decode(), 1, s1, K)
+    # plus the new rows: k_new, v_new read, K, V and code rows written
+    per_launch = algorithmic_bytes(B, Hq, Hkv, d, n, bud, 2) + B * Hkv * (4 * d * 2 + d // 4)
+    chunk_bytes = Hkv * w.chunk * (2 * d * 2 + d // 4)   # read K, copy K, write codes
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline_append(lay, codes, lens, kn, vn, w, n, bud, args.cpu_seconds)
+    result_line(
+        f"batched decode+append tokens/s + achieved HBM GB/s, 16 x 64K ctx, budget {bud}, 1 GPU",
+        w, B, ms, K, args.warmup,
+        {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+         "n_ctx": n, "budget": bud, "prefill_chunk": w.chunk,
+         "timing": "eager, two streams, step = both done"},
+        "adamas_decode_append_step (16 sequences, 4096-token chunk encoding beside it)",
+        per_launch, launch_us, stream_read_gbs(dev),
+        {"step_ms": {"p10": round(float(np.percentile(step_times, 10)), 4),
+                     "p50": round(float(np.percentile(step_times, 50)), 4),
+                     "p90": round(float(np.percentile(step_times, 90)), 4)},
+         "hbm_gbs_step": round((per_launch + chunk_bytes) / (ms * 1e-3) / 1e9, 1),
+         "decode_alone_us": round(alone_us, 3),
+         "decode_alone_gbs": round(per_launch / (alone_us * 1e-6) / 1e9, 1)}, cpu)
+
+
+def cpu_baseline_append(lay, codes, lens, kn, vn, w, n, bud, seconds):
+    """The oracle's append step on single sequences of the batch (cycled) until
+    about `seconds` of oracle time; scaled to the 16-sequence step."""
+    import numpy as np
+
+    import oracle
+    import synth
+    oracle.build(force=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    staged = []
+    for b in (0, 5, 10):
+        sl = slice(b, b + 1)
+        k = synth.to_numpy_bits(lay["k"][sl, :, :n])
+        staged.append((synth.to_numpy_bits(lay["q"][sl]), k, synth.to_numpy_bits(lay["v"][sl, :, :n]),
+                       oracle.encode_keys(k), synth.to_numpy_bits(kn[sl]),
+                       synth.to_numpy_bits(vn[sl])))
+    spent, done = 0.0, 0
+    while spent < seconds or done == 0:
+        q, k, v, c, a, bvals = staged[done % len(staged)]
+        t = time.perf_counter()
+        oracle.decode_append_step(q, k, v, c, np.array([n - 1]), n, bud, a, bvals)
+        spent += time.perf_counter() - t
+        done += 1
+    print(f"[bench] oracle: {done} single-sequence append steps in {spent:.1f}s", file=sys.stderr,
+          flush=True)
+    step = spent / done * w.batch
+    return {"value": round(w.batch / step, 4), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} single-sequence append+decode steps cycling over 3 sequences "
+                      f"({w.hq} heads x {n} rows, budget {bud}), {spent:.1f}s of oracle time, "
+                      f"scaled to the {w.batch}-sequence step"}
 
 
 def cpu_baseline(layers, w, n, bud, seconds):

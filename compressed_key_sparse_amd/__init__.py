@@ -19,8 +19,10 @@ import torch
 
 __all__ = [
     "AdamasError", "load", "library_path", "encode_keys", "encode_query", "score", "select_topk",
-    "sparse_attend", "decode_step", "workspace_bytes", "Workspace", "OP_SELECT_TOPK",
-    "OP_SPARSE_ATTEND", "OP_DECODE_STEP",
+    "sparse_attend", "decode_step", "decode_append_step", "workspace_bytes", "Workspace",
+    "set_decode_mode", "decode_path", "set_rotation", "stream_read", "OP_SELECT_TOPK",
+    "OP_SPARSE_ATTEND", "OP_DECODE_STEP", "DECODE_AUTO", "DECODE_LAST_ARRIVAL",
+    "DECODE_GROUP_WAIT", "DECODE_SPLIT", "WS_CTRL_BYTES", "WS_STATUS_OFFSET",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +33,7 @@ F32, BF16 = 0, 1
 OP_SELECT_TOPK, OP_SPARSE_ATTEND, OP_DECODE_STEP = 0, 1, 2
 WS_CTRL_BYTES = 65792          # ADAMAS_WS_CTRL_BYTES
 WS_STATUS_OFFSET = 65536       # ADAMAS_WS_STATUS_OFFSET
-DECODE_AUTO, DECODE_LAST_ARRIVAL, DECODE_GROUP_WAIT = 0, 1, 2
+DECODE_AUTO, DECODE_LAST_ARRIVAL, DECODE_GROUP_WAIT, DECODE_SPLIT = 0, 1, 2, 3
 
 _lib = None
 
@@ -260,8 +262,8 @@ def set_rotation(on: bool) -> None:
 
 
 def set_decode_mode(mode: int) -> None:
-    """Process-wide schedule of decode_step: DECODE_AUTO, DECODE_LAST_ARRIVAL or
-    DECODE_GROUP_WAIT (adamas_set_decode_mode)."""
+    """Process-wide schedule of decode_step: DECODE_AUTO, DECODE_LAST_ARRIVAL,
+    DECODE_GROUP_WAIT or DECODE_SPLIT (adamas_set_decode_mode)."""
     _check(load().adamas_set_decode_mode(int(mode)), "adamas_set_decode_mode")
 
 

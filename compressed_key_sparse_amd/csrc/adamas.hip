@@ -105,8 +105,13 @@ struct DecodePlan {
   bool fuse = false;
   size_t idx_off = 0;
   AttendPlan att;
+  // SPLIT schedule: per-chunk key counts [B*Hq][nbins][ncp] u16 at chist_off
+  bool split_ok = false;
+  int ncp = 0, seg_chunks = 0, segs = 0;
+  size_t chist_off = 0;
   size_t total = 0;
 };
+constexpr int kSplitSegChunks = 32;  // chunks per k_split_select workgroup
 
 // adamas_decode_step: 1024-thread workgroups, chunks as large as LDS allows
 // (fewer candidates to merge), attention fused into the selecting workgroup
@@ -133,8 +138,21 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D)
   p.idx_off = round_up(p.sel.end, 256);
   const size_t idx_end = p.idx_off + (size_t)rows * budget * sizeof(int32_t);
   p.att = plan_attend(rows, bsel, D, idx_end);
-  p.total = round_up(p.att.end, 256);
+  p.ncp = (p.sel.n_chunks + 7) & ~7;
+  p.split_ok = p.sel.n_chunks <= kSplitMaxChunks;
+  p.seg_chunks = kSplitSegChunks;
+  p.segs = (p.sel.n_chunks + kSplitSegChunks - 1) / kSplitSegChunks;
+  p.chist_off = round_up(p.att.end, 256);
+  const size_t chist_end =
+      p.split_ok ? p.chist_off + (size_t)rows * (size_t)(3 * D + 2) * (size_t)p.ncp * 2 : p.att.end;
+  p.total = round_up(chist_end, 256);
   return p;
+}
+
+// More chunk candidates per head than one LDS tile holds: one workgroup
+// selecting from them all would take several passes over global memory.
+bool many_candidates(const DecodePlan& p) {
+  return (int64_t)p.sel.n_chunks * p.sel.kpad > kMaxCandTile;
 }
 
 // adamas_decode_step with group waits (k_decode_gs): every workgroup of the
@@ -243,6 +261,8 @@ struct DecodeArgs {
   void* out;
   int n_sink, n_recent;
   RaggedArgs rg;  // lens == nullptr: every sequence holds n_ctx rows
+  uint16_t* chist = nullptr;  // SPLIT: per-chunk key counts, selection left to k_split_select
+  int ncp = 0;
 };
 
 template <int D, int G, bool BF>
@@ -251,12 +271,12 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
     k_decode<D, G, BF, true><<<grid, kDecodeThreads, p.sel.lds, s>>>(
         a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
         p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx, a.out,
-        a.n_sink, a.n_recent, rotation_on(), a.rg);
+        a.n_sink, a.n_recent, rotation_on(), a.rg, nullptr, 0);
   else
     k_decode<D, G, BF, false><<<grid, kDecodeThreads, p.sel.lds, s>>>(
         a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
-        p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx, a.out,
-        a.n_sink, a.n_recent, rotation_on(), a.rg);
+        p.sel.kpad_log2, p.sel.mcap, (p.fuse && !a.chist) ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
+        a.out, a.n_sink, a.n_recent, rotation_on(), a.rg, a.chist, a.ncp);
 }
 
 template <int D, int G, bool BF>
@@ -480,7 +500,14 @@ int launch_last_arrival(const DecodePlan& p, const DecodeArgs& a, int B, int hea
     ok = bf ? dispatch_decode<64, true>(G, p, grid, stream, a)
             : dispatch_decode<64, false>(G, p, grid, stream, a);
   if (!ok) return ADAMAS_ERR_UNSUPPORTED;
-  if (!p.fuse) {
+  if (a.chist != nullptr) {
+    const int bsel = (int)(a.n_ctx < a.budget ? a.n_ctx : a.budget);
+    const dim3 gsel((unsigned)p.segs, (unsigned)((int64_t)B * a.Hq));
+    k_split_select<kSplitThreads><<<gsel, kSplitThreads, 0, stream>>>(
+        a.cand, a.chist, p.sel.n_chunks, p.ncp, p.seg_chunks, p.sel.kpad_log2, p.sel.chunk,
+        3 * head_dim + 2, bsel, a.budget, a.idx);
+  }
+  if (!p.fuse || a.chist != nullptr) {
     const dim3 gatt((unsigned)p.att.splits, (unsigned)a.Hq, (unsigned)B);
     launch_attend(head_dim, bf, gatt, stream, a.q, a.k, a.v, a.idx, a.Hq, a.Hkv, a.cap, a.budget,
                   a.qscale, reinterpret_cast<float*>(w + p.att.part_off),
@@ -518,9 +545,12 @@ int adamas_decode_step_keep(const void* q, const void* k, const void* v, const u
   const int G = Hq / Hkv;
   const bool bf = dtype == ADAMAS_BF16;
   const DecodePlan p = plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim);
+  const bool many = many_candidates(p);
   // AUTO takes group waits where the last-arrival schedule could not fuse
-  // the attention (it would need a second launch)
-  if (mode == ADAMAS_DECODE_GROUP_WAIT || (mode == ADAMAS_DECODE_AUTO && !p.fuse)) {
+  // the attention (it would need a second launch) or would select from too
+  // many candidates in one workgroup; failing that, the separate selection
+  // for the latter
+  if (mode == ADAMAS_DECODE_GROUP_WAIT || (mode == ADAMAS_DECODE_AUTO && (!p.fuse || many))) {
     const GroupPlan gp = plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, device_capacity());
     if (gp.ok) {
       if (ws_bytes < gp.total) return ADAMAS_ERR_WORKSPACE;
@@ -537,13 +567,19 @@ int adamas_decode_step_keep(const void* q, const void* k, const void* v, const u
     }
     if (mode == ADAMAS_DECODE_GROUP_WAIT) return ADAMAS_ERR_UNSUPPORTED;
   }
+  if (mode == ADAMAS_DECODE_SPLIT && !p.split_ok) return ADAMAS_ERR_UNSUPPORTED;
+  const bool split = mode == ADAMAS_DECODE_SPLIT || (mode == ADAMAS_DECODE_AUTO && many && p.split_ok);
   if (ws_bytes < p.total) return ADAMAS_ERR_WORKSPACE;
-  int32_t* idx = idx_out != nullptr ? idx_out
-                 : p.fuse       ? nullptr
-                                : reinterpret_cast<int32_t*>(w + p.idx_off);
+  int32_t* idx = idx_out != nullptr       ? idx_out
+                 : (p.fuse && !split) ? nullptr
+                                      : reinterpret_cast<int32_t*>(w + p.idx_off);
   DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
                reinterpret_cast<uint32_t*>(w + p.sel.cand_off),
                reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent, {}};
+  if (split) {
+    a.chist = reinterpret_cast<uint16_t*>(w + p.chist_off);
+    a.ncp = p.ncp;
+  }
   return launch_last_arrival(p, a, B, head_dim, bf, w, stream);
 }
 
@@ -598,7 +634,7 @@ int adamas_set_rotation(int on) {
 
 int adamas_set_decode_mode(int mode) {
   if (mode != ADAMAS_DECODE_AUTO && mode != ADAMAS_DECODE_LAST_ARRIVAL &&
-      mode != ADAMAS_DECODE_GROUP_WAIT)
+      mode != ADAMAS_DECODE_GROUP_WAIT && mode != ADAMAS_DECODE_SPLIT)
     return ADAMAS_ERR_INVALID;
   g_decode_mode.store(mode, std::memory_order_relaxed);
   return ADAMAS_OK;
@@ -609,14 +645,18 @@ int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int he
       budget > kMaxBudget || !valid_dim(head_dim) || Hq / Hkv > kMaxG)
     return -ADAMAS_ERR_INVALID;
   const int mode = g_decode_mode.load(std::memory_order_relaxed);
+  const DecodePlan p = plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim);
+  const bool many = many_candidates(p);
   if (mode == ADAMAS_DECODE_LAST_ARRIVAL) return ADAMAS_DECODE_LAST_ARRIVAL;
-  if (mode == ADAMAS_DECODE_AUTO && plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).fuse)
-    return ADAMAS_DECODE_LAST_ARRIVAL;
+  if (mode == ADAMAS_DECODE_SPLIT)
+    return p.split_ok ? ADAMAS_DECODE_SPLIT : -ADAMAS_ERR_UNSUPPORTED;
+  if (mode == ADAMAS_DECODE_AUTO && p.fuse && !many) return ADAMAS_DECODE_LAST_ARRIVAL;
   const int64_t capacity = device_capacity();
   if (capacity <= 0) return -ADAMAS_ERR_DEVICE;
   if (plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, capacity).ok)
     return ADAMAS_DECODE_GROUP_WAIT;
-  return mode == ADAMAS_DECODE_GROUP_WAIT ? -ADAMAS_ERR_UNSUPPORTED : ADAMAS_DECODE_LAST_ARRIVAL;
+  if (mode == ADAMAS_DECODE_GROUP_WAIT) return -ADAMAS_ERR_UNSUPPORTED;
+  return many && p.split_ok ? ADAMAS_DECODE_SPLIT : ADAMAS_DECODE_LAST_ARRIVAL;
 }
 
 size_t adamas_stream_read_blocks(size_t bytes) {

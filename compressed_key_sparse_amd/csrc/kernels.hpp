@@ -524,7 +524,8 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
     int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
-    void* __restrict__ out, int n_sink, int n_recent, int rotate, RaggedArgs rg) {
+    void* __restrict__ out, int n_sink, int n_recent, int rotate, RaggedArgs rg,
+    uint16_t* __restrict__ chist, int ncp) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), W = D / 16;
   constexpr int E = D / 64, kLanesPerWord = 16 / E, PW = 2 + D;
@@ -649,6 +650,14 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     }
   }
   lds_sync();
+  if (chist != nullptr) {
+    // separate selection (k_split_select): this chunk's key counts per head
+    for (int i = threadIdx.x; i < G * NB; i += NT) {
+      const int g = i / NB, kb = i - g * NB;
+      const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
+      chist[(row * NB + kb) * ncp + c] = (uint16_t)shist[g * NBP + kb];
+    }
+  }
   const int kc = min(budget, valid);
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
@@ -658,6 +667,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     lds_sync();
     lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
   }
+  if (chist != nullptr) return;  // k_split_select takes it from here
   if (!arrive_last<NT>(&counters[b * Hkv + hkv], active, s_tmp)) return;
   const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap;
   for (int g = 0; g < G; ++g) {
@@ -681,6 +691,153 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(
     }
   }
   if (threadIdx.x == 0) counters[b * Hkv + hkv] = 0;
+}
+
+// ------------------------------------- decode step, selection on its own
+// When a head has too many chunk candidates for one workgroup to select
+// from quickly (n_chunks * kpad well beyond what fits in LDS at once),
+// k_decode publishes each chunk's candidates and its key counts per query
+// head and stops, and this kernel selects.  Grid (segments, B*Hq).  Each
+// workgroup sums the head's counts over the chunks (§5.2 threshold t and
+// quota of ties), derives for every chunk how many of its keys lie below t
+// and how many of its ties it contributes, and from their prefix sums where
+// its kept tokens start in the ascending selection; its wavefronts then copy
+// the kept tokens of the segment's chunks there, one chunk at a time.  Ties
+// at t go to the lowest token indices: chunks are in token order, and each
+// chunk's candidates are too.
+//   chist [B*Hq][nbins][ncp] u16, ncp >= n_chunks a multiple of 8
+//   cand  [B*Hq][n_chunks][kpad] as k_decode leaves it (token order, 0xFFFFFFFF unused)
+constexpr int kSplitThreads = 1024;
+constexpr int kSplitMaxChunks = 2048;
+constexpr int kSplitEntriesPerLane = 16;  // a wavefront loads 1024 candidates at once
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_split_select(
+    const uint32_t* __restrict__ cand, const uint16_t* __restrict__ chist, int n_chunks, int ncp,
+    int chunks_per_seg, int kpad_log2, int chunk, int nbins, int bsel, int budget,
+    int32_t* __restrict__ idx) {
+  constexpr int NW = NT / kWave, EPL = kSplitEntriesPerLane;
+  __shared__ uint32_t s_tmp[kTmpWords];
+  __shared__ uint32_t s_hist[kNbinsPadded(128)];
+  __shared__ uint32_t s_first[kSplitMaxChunks];  // first output position of the chunk's tokens
+  __shared__ uint32_t s_take[kSplitMaxChunks];   // (count below t) << 16 | ties taken
+  const int64_t row = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+  const uint16_t* h = chist + row * nbins * ncp;
+  for (int i = threadIdx.x; i < nbins; i += NT) s_hist[i] = 0;
+  for (int i = threadIdx.x; i < n_chunks; i += NT) s_first[i] = 0;
+  lds_sync();
+  {  // the head's counts: P threads per key, each over every P-th group of 8 chunks
+    const int P = max(1, NT / nbins), g8 = (n_chunks + 7) / 8;
+    for (int it = threadIdx.x; it < nbins * P; it += NT) {
+      const int kb = it / P, p = it - kb * P;
+      const uint4* src = reinterpret_cast<const uint4*>(h + (int64_t)kb * ncp);
+      uint32_t sum = 0;
+      for (int j = p; j < g8; j += P) {
+        const uint4 w = src[j];
+        const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+        const int rem = n_chunks - 8 * j;  // counts past the last chunk are not written
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          sum += (2 * u < rem ? (x[u] & 0xffffu) : 0u) + (2 * u + 1 < rem ? (x[u] >> 16) : 0u);
+      }
+      if (sum) atomicAdd(&s_hist[kb], sum);
+    }
+  }
+  lds_sync();
+  const Threshold thr = find_threshold<NT>(s_hist, nbins, (uint32_t)bsel, s_tmp);
+  const uint32_t quota = (uint32_t)bsel - thr.lt;
+  {  // per chunk: keys below t (P2 threads per chunk, every P2-th key) and ties at t
+    const int P2 = max(1, NT / n_chunks);
+    for (int it = threadIdx.x; it < n_chunks * P2; it += NT) {
+      const int c = it % n_chunks, p = it / n_chunks;
+      uint32_t sum = 0;
+#pragma unroll 4
+      for (int kb = p; kb < thr.t; kb += P2) sum += h[(int64_t)kb * ncp + c];
+      if (sum) atomicAdd(&s_first[c], sum);
+      if (p == 0) s_take[c] = h[(int64_t)thr.t * ncp + c];
+    }
+  }
+  lds_sync();
+  {  // prefix sums over chunks: where each chunk's tokens start, and its share of ties
+    const int tpt = (n_chunks + NT - 1) / NT, c0 = threadIdx.x * tpt;
+    uint32_t lts = 0, eqs = 0;
+    for (int j = 0; j < tpt; ++j)
+      if (c0 + j < n_chunks) {
+        lts += s_first[c0 + j];
+        eqs += s_take[c0 + j];
+      }
+    uint32_t tot;
+    uint32_t lt_ex = block_scan_incl<NT>(lts, s_tmp, &tot) - lts;
+    uint32_t eq_ex = block_scan_incl<NT>(eqs, s_tmp, &tot) - eqs;
+    for (int j = 0; j < tpt; ++j) {
+      const int c = c0 + j;
+      if (c >= n_chunks) break;
+      const uint32_t lt = s_first[c], eq = s_take[c];
+      // ties taken by earlier chunks, then this chunk's share.  Written so
+      // that no subtraction can wrap: with `eq_ex >= quota ? 0 : min(eq,
+      // quota - eq_ex)` the compiler (ROCm 7.2 clang) also folded a separate
+      // min(eq_ex, quota) to eq_ex
+      const uint32_t before = eq_ex < quota ? eq_ex : quota;
+      const uint32_t q = min(eq, quota - before);
+      s_first[c] = lt_ex + before;
+      s_take[c] = (lt << 16) | q;
+      lt_ex += lt;
+      eq_ex += eq;
+    }
+  }
+  lds_sync();
+  int32_t* out = idx + row * budget;
+  if (blockIdx.x == 0)
+    for (int j = bsel + threadIdx.x; j < budget; j += NT) out[j] = -1;
+  const uint32_t t = (uint32_t)thr.t;
+  const int kpad = 1 << kpad_log2;
+  const int c_lo = blockIdx.x * chunks_per_seg, c_hi = min(n_chunks, c_lo + chunks_per_seg);
+  for (int c = c_lo + wid; c < c_hi; c += NW) {
+    const uint32_t tk = s_take[c], q = tk & 0xffffu, need = (tk >> 16) + q;
+    if (need == 0) continue;
+    uint32_t pos = s_first[c], ties = 0, got = 0;
+    const uint32_t end = min(pos + need, (uint32_t)bsel);  // this chunk's slots in the selection
+    const uint32_t* list = cand + ((row * n_chunks + c) << kpad_log2);
+    const int32_t tok0 = c * chunk;
+    for (int base = 0; base < kpad && got < need; base += EPL * kWave) {
+      // EPL consecutive candidates per lane, in token order across lanes
+      uint32_t v[EPL];
+#pragma unroll
+      for (int u = 0; u < EPL / 4; ++u) {
+        const int i = base + lane * EPL + 4 * u;
+        uint4 e = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+        if (i < kpad) e = *reinterpret_cast<const uint4*>(list + i);
+        v[4 * u] = e.x;
+        v[4 * u + 1] = e.y;
+        v[4 * u + 2] = e.z;
+        v[4 * u + 3] = e.w;
+      }
+      uint32_t neq = 0;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) neq += (v[j] >> 16) == t;
+      const uint32_t eq_incl = wave_scan_incl(neq);
+      uint32_t rank = ties + eq_incl - neq;  // ties of this chunk before this lane's
+      uint32_t flags = 0, ntake = 0;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const uint32_t d = v[j] >> 16;
+        const bool take = d < t || (d == t && rank < q);
+        rank += d == t;
+        flags |= (take ? 1u : 0u) << j;
+        ntake += take;
+      }
+      const uint32_t take_incl = wave_scan_incl(ntake);
+      uint32_t o = pos + take_incl - ntake;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if ((flags >> j & 1u) && o < end) out[o++] = tok0 + (int32_t)(v[j] & 0xffffu);
+      const uint32_t took = __builtin_amdgcn_readlane(take_incl, kWave - 1);
+      ties += __builtin_amdgcn_readlane(eq_incl, kWave - 1);
+      got += took;
+      pos += took;
+    }
+  }
 }
 
 // ------------------------------------------ fused decode step, group wait
@@ -806,8 +963,10 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     const uint32_t bef = (int)threadIdx.x < NB ? s_bef[threadIdx.x] : 0u;
     const GroupThreshold gt = find_group_threshold<NT>(tot, bef, NB, (uint32_t)bsel, s_sums, s_tmp);
     const uint32_t quota = (uint32_t)bsel - gt.lt;  // ties at t the whole group keeps
-    const uint32_t mine_q = quota > gt.ties_before ? quota - gt.ties_before : 0u;
-    const uint32_t off = gt.lt_before + min(gt.ties_before, quota);
+    // ties kept by the chunks before, then this chunk's share (no subtraction wraps)
+    const uint32_t before = gt.ties_before < quota ? gt.ties_before : quota;
+    const uint32_t mine_q = quota - before;
+    const uint32_t off = gt.lt_before + before;
     int32_t* sg = sidx + g * cmax;
     int32_t* ig = idx ? idx + row * budget + off : nullptr;
     const uint32_t kept = chunk_collect<NT>(sdist + g * chunk, valid, gt.t, mine_q, s_tmp,

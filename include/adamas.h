@@ -74,7 +74,8 @@ typedef enum { ADAMAS_F32 = 0, ADAMAS_BF16 = 1 } adamas_dtype;
 typedef enum {
     ADAMAS_DECODE_AUTO = 0,
     ADAMAS_DECODE_LAST_ARRIVAL = 1,
-    ADAMAS_DECODE_GROUP_WAIT = 2
+    ADAMAS_DECODE_GROUP_WAIT = 2,
+    ADAMAS_DECODE_SPLIT = 3
 } adamas_decode_mode;
 
 typedef enum {
@@ -180,10 +181,19 @@ int adamas_decode_step(const void *q, const void *k, const void *v,
  *    the shape does not fit.  Launches of this kind on several streams of one
  *    device at once rely on the hardware starting a launch's workgroups in
  *    order; each wait is bounded (see ADAMAS_WS_STATUS_OFFSET).
+ *  - ADAMAS_DECODE_SPLIT: each chunk workgroup publishes its chunk's
+ *    candidates and its key counts per query head; a second launch, a few
+ *    workgroups per query head, sums the counts to the head's threshold,
+ *    places every chunk's share of the budget in the ascending selection and
+ *    copies it there; a third launch attends.  For heads with many chunks
+ *    (long contexts with large budgets), where one workgroup selecting from
+ *    all chunk candidates would be slow.  Needs at most 2048 chunks per head
+ *    (ADAMAS_ERR_UNSUPPORTED when forced beyond).
  *  - ADAMAS_DECODE_AUTO (default): LAST_ARRIVAL while its last workgroup can
  *    attend over the whole selection itself (G * ceil(min(budget, n_ctx) /
- *    256) <= 2), else GROUP_WAIT where the shape fits, else LAST_ARRIVAL with
- *    a separate attention launch.
+ *    256) <= 2) from at most 8192 chunk candidates per head; otherwise
+ *    GROUP_WAIT where the shape fits, else SPLIT beyond 8192 candidates, else
+ *    LAST_ARRIVAL with a separate attention launch.
  * Returns ADAMAS_OK, or ADAMAS_ERR_INVALID for an unknown mode.
  */
 int adamas_set_decode_mode(int mode);
@@ -199,10 +209,11 @@ int adamas_set_rotation(int on);
 
 /*
  * The schedule adamas_decode_step would use for this shape on the current
- * device under the current mode: ADAMAS_DECODE_LAST_ARRIVAL or
- * ADAMAS_DECODE_GROUP_WAIT, or a negated status (-ADAMAS_ERR_INVALID for a
- * bad shape, -ADAMAS_ERR_UNSUPPORTED if GROUP_WAIT is forced and does not
- * fit, -ADAMAS_ERR_DEVICE if no device can be queried).
+ * device under the current mode: ADAMAS_DECODE_LAST_ARRIVAL,
+ * ADAMAS_DECODE_GROUP_WAIT or ADAMAS_DECODE_SPLIT, or a negated status
+ * (-ADAMAS_ERR_INVALID for a bad shape, -ADAMAS_ERR_UNSUPPORTED if
+ * GROUP_WAIT or SPLIT is forced and does not fit, -ADAMAS_ERR_DEVICE if no
+ * device can be queried).
  */
 int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim);
 

@@ -140,9 +140,9 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
 
 
 def test_decode_mode_validation(lib):
-    assert lib.adamas_set_decode_mode(3) == INVALID
+    assert lib.adamas_set_decode_mode(4) == INVALID
     assert lib.adamas_set_decode_mode(-1) == INVALID
-    for m in (2, 1, 0):                     # GROUP_WAIT, LAST_ARRIVAL, back to AUTO
+    for m in (3, 2, 1, 0):                  # SPLIT, GROUP_WAIT, LAST_ARRIVAL, back to AUTO
         assert lib.adamas_set_decode_mode(m) == OK
     # shape checks come before any device query
     f = lib.adamas_decode_path

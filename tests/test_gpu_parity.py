@@ -243,6 +243,8 @@ _SCHED_CASES = {
     "gqa-24-8-9001": synth.LLAMA32_GQA_1M.replace(hq=24, hkv=8, n_ctx=9001, cap=9001, budget=128),
     "gqa-8-1-9001": synth.LLAMA32_GQA_1M.replace(hq=8, hkv=1, n_ctx=9001, cap=9001, budget=300),
     "f32-d64-batch3": synth.TINY.replace(batch=3, hq=4, hkv=2, n_ctx=3000, cap=3000, budget=100),
+    "gqa-6-2-300000-b1024": synth.LLAMA32_GQA_1M.replace(hq=6, hkv=2, n_ctx=300000, cap=300000,
+                                                         budget=1024),
 }
 
 
@@ -252,7 +254,8 @@ def restore_mode():
     adamas.set_decode_mode(adamas.DECODE_AUTO)
 
 
-@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT])
+@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT,
+                                  adamas.DECODE_SPLIT])
 @pytest.mark.parametrize("case", sorted(_SCHED_CASES))
 def test_decode_schedules(ora, restore_mode, mode, case):
     w = _SCHED_CASES[case]
@@ -286,6 +289,9 @@ def test_decode_schedule_choice(restore_mode):
     assert adamas.decode_path(1, 32, 32, 131072, 1024, 128) == adamas.DECODE_GROUP_WAIT
     # 512 KV heads of chunks do not fit: the last-arrival schedule takes them
     assert adamas.decode_path(16, 32, 32, 65536, 512, 128) == adamas.DECODE_LAST_ARRIVAL
+    # 128 chunks of 1024 candidates per head at 1M tokens: selection on its own
+    assert adamas.decode_path(1, 24, 8, 1048576, 1024, 128) == adamas.DECODE_SPLIT
+    assert adamas.decode_path(1, 32, 32, 1048576, 256, 128) == adamas.DECODE_SPLIT
     adamas.set_decode_mode(adamas.DECODE_GROUP_WAIT)
     assert adamas.decode_path(1, 32, 32, 131072, 256, 128) == adamas.DECODE_GROUP_WAIT
     adamas.set_decode_mode(adamas.DECODE_GROUP_WAIT)
@@ -319,7 +325,8 @@ def test_select_keep(ora, n, budget, n_sink, n_recent, hi):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT])
+@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT,
+                                  adamas.DECODE_SPLIT])
 @pytest.mark.parametrize("n,budget,n_sink,n_recent", [
     (5000, 256, 4, 64), (70000, 512, 1, 128), (9001, 128, 128, 0), (30000, 1024, 8, 1000)])
 def test_decode_keep(ora, restore_mode, mode, n, budget, n_sink, n_recent):
@@ -359,7 +366,8 @@ def test_encode_without_rotation(ora, restore_rotation, d, dt):
     assert np.array_equal(codes.cpu().numpy(), ora.encode_keys(host(x), rotate=False))
 
 
-@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT])
+@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT,
+                                  adamas.DECODE_SPLIT])
 def test_decode_without_rotation(ora, restore_rotation, restore_mode, mode):
     adamas.set_rotation(False)
     adamas.set_decode_mode(mode)
