@@ -22,6 +22,11 @@ constexpr size_t kCtrlSelect = 0;          // u32 counters of select / decode gr
 constexpr size_t kCtrlAttend = 32768;      // u32 counters of attention rows
 constexpr int kMaxBudget = 1 << 20;
 constexpr size_t kLdsLimit = 64 * 1024;    // per-workgroup LDS used by any kernel here
+// ... except the decode chunk scan, which keeps G * chunk u16 distances: up
+// to the 160 KiB a gfx950 workgroup may hold (one 1024-thread workgroup per
+// compute unit either way), so grouped heads scan chunks as long as MHA ones
+constexpr size_t kLdsDecodeLimit = 160 * 1024;
+constexpr int64_t kComputeUnits = 256;     // MI355X; workgroups of one decode round
 constexpr int kMaxCandTile = 8192;         // candidate entries staged in LDS at once
 constexpr size_t kStreamBlocks = 1024;     // adamas_stream_read: four slices per compute unit
 
@@ -121,8 +126,11 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D)
   const int G = Hq / Hkv;
   const int64_t rows = (int64_t)B * Hq;
   int c = 16384;
-  while (c > 1024 && kTmpWords * 4 + decode_lds_scan(D, G, c, budget) > kLdsLimit) c /= 2;
+  while (c > 1024 && kTmpWords * 4 + decode_lds_scan(D, G, c, budget) > kLdsDecodeLimit) c /= 2;
   while (c > 1024 && (int64_t)(c / 2) >= n_ctx) c /= 2;
+  // shorter chunks while the whole launch still fits one workgroup per
+  // compute unit: more of the device streams the code cache
+  while (c > 1024 && (int64_t)B * Hkv * ((n_ctx + c / 2 - 1) / (c / 2)) <= kComputeUnits) c /= 2;
   p.sel.chunk = c;
   finish_select_plan(p.sel, rows, n_ctx, budget, ADAMAS_WS_CTRL_BYTES);
   const int bsel = (int)(n_ctx < budget ? n_ctx : budget);
@@ -131,7 +139,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D)
   const int sidx_rows = p.fuse ? bsel : 0;
   // shrink the LDS candidate tile if the final phase would not fit
   while (p.sel.mcap > 256 &&
-         kTmpWords * 4 + decode_lds_final(D, sidx_rows, p.sel.mcap) > kLdsLimit)
+         kTmpWords * 4 + decode_lds_final(D, sidx_rows, p.sel.mcap) > kLdsDecodeLimit)
     p.sel.mcap = (p.sel.mcap / 2 + 3) & ~3;
   p.sel.lds = kTmpWords * 4 + std::max(decode_lds_scan(D, G, c, budget),
                                        decode_lds_final(D, sidx_rows, p.sel.mcap));
@@ -265,8 +273,18 @@ struct DecodeArgs {
   int ncp = 0;
 };
 
+// Dynamic LDS beyond 64 KiB must be allowed per kernel before its launch.
+template <class K>
+void allow_lds(K kernel, size_t lds) {
+  if (lds > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
 template <int D, int G, bool BF>
 void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  allow_lds(a.rg.lens != nullptr ? &k_decode<D, G, BF, true> : &k_decode<D, G, BF, false>,
+            p.sel.lds);
   if (a.rg.lens != nullptr)
     k_decode<D, G, BF, true><<<grid, kDecodeThreads, p.sel.lds, s>>>(
         a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
