@@ -281,20 +281,35 @@ void allow_lds(K kernel, size_t lds) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
+template <int D, int G, bool BF, bool RAG, bool OCC>
+void launch_decode_k(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
+  allow_lds(&k_decode<D, G, BF, RAG, OCC>, p.sel.lds);
+  k_decode<D, G, BF, RAG, OCC><<<grid, kDecodeThreads, p.sel.lds, s>>>(
+      a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
+      p.sel.kpad_log2, p.sel.mcap, (p.fuse && !a.chist) ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
+      a.out, a.n_sink, a.n_recent, rotation_on(), a.rg, RAG ? nullptr : a.chist,
+      RAG ? 0 : a.ncp);
+}
+
 template <int D, int G, bool BF>
 void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
-  allow_lds(a.rg.lens != nullptr ? &k_decode<D, G, BF, true> : &k_decode<D, G, BF, false>,
-            p.sel.lds);
+  // MHA launches of several rounds run two workgroups per compute unit
+  // when their LDS allows it
+  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+  const bool occ = G == 1 && wgs > kComputeUnits && 2 * p.sel.lds <= kLdsDecodeLimit;
+  if constexpr (G == 1) {
+    if (occ) {
+      if (a.rg.lens != nullptr)
+        launch_decode_k<D, G, BF, true, true>(p, grid, s, a);
+      else
+        launch_decode_k<D, G, BF, false, true>(p, grid, s, a);
+      return;
+    }
+  }
   if (a.rg.lens != nullptr)
-    k_decode<D, G, BF, true><<<grid, kDecodeThreads, p.sel.lds, s>>>(
-        a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
-        p.sel.kpad_log2, p.sel.mcap, p.fuse ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx, a.out,
-        a.n_sink, a.n_recent, rotation_on(), a.rg, nullptr, 0);
+    launch_decode_k<D, G, BF, true, false>(p, grid, s, a);
   else
-    k_decode<D, G, BF, false><<<grid, kDecodeThreads, p.sel.lds, s>>>(
-        a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
-        p.sel.kpad_log2, p.sel.mcap, (p.fuse && !a.chist) ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
-        a.out, a.n_sink, a.n_recent, rotation_on(), a.rg, a.chist, a.ncp);
+    launch_decode_k<D, G, BF, false, false>(p, grid, s, a);
 }
 
 template <int D, int G, bool BF>

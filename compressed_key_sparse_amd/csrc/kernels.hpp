@@ -518,8 +518,12 @@ struct RaggedArgs {
   uint8_t* code_cache;
 };
 
-template <int D, int G, bool BF, bool RAG>
-__global__ __launch_bounds__(kDecodeThreads) void k_decode(
+// OCC: compiled for two resident workgroups per compute unit (at most 64
+// VGPRs), for launches of several rounds, where one workgroup's chunk tail
+// then overlaps the other's scan.
+template <int D, int G, bool BF, bool RAG, bool OCC = false>
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(OCC ? 8 : 1)))
+void k_decode(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
     int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,

@@ -172,3 +172,9 @@ def test_graph_replay_advances_lengths(ora):
             lens_d.add_(1)
         torch.cuda.synchronize()
     assert not ws.buf[:adamas.WS_CTRL_BYTES].any()
+
+
+def test_append_many_rounds(ora):
+    log("append step over 256 KV heads x 2 chunks (two workgroups per compute unit)")
+    w = synth.LLAMA2_32K.replace(batch=8, hq=32, hkv=32, n_ctx=20001, cap=20001, budget=256)
+    _run(ora, w, [20000, 9000, 16384, 1, 0, 12345, 16383, 19999], 20001, 256)
