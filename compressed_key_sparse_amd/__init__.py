@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "AdamasError", "load", "library_path", "encode_keys", "encode_query", "score", "select_topk",
-    "sparse_attend", "decode_step", "decode_append_step", "workspace_bytes", "Workspace",
+    "sparse_attend", "decode_step", "decode_append_step", "decode_paged_step", "workspace_bytes",
+    "Workspace",
     "set_decode_mode", "decode_path", "set_rotation", "stream_read", "OP_SELECT_TOPK",
     "OP_SPARSE_ATTEND", "OP_DECODE_STEP", "DECODE_AUTO", "DECODE_LAST_ARRIVAL",
     "DECODE_GROUP_WAIT", "DECODE_SPLIT", "WS_CTRL_BYTES", "WS_STATUS_OFFSET",
@@ -73,6 +74,8 @@ def load():
                                             i32, i32, f32, P, P, P, sz, P]
     lib.adamas_decode_append_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i64,
                                               i64, i32, i32, i32, f32, P, P, P, sz, P]
+    lib.adamas_decode_paged_step.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                             i32, i32, i64, i32, i32, i32, f32, P, P, P, sz, P]
     lib.adamas_workspace_bytes.argtypes = [i32, i32, i32, i32, i64, i32, i32]
     lib.adamas_workspace_bytes.restype = sz
     lib.adamas_status_string.argtypes = [i32]
@@ -90,7 +93,7 @@ def load():
         getattr(lib, fn).restype = i32
     for fn in ("adamas_encode_keys", "adamas_score", "adamas_select_topk", "adamas_sparse_attend",
                "adamas_decode_step", "adamas_select_topk_keep", "adamas_decode_step_keep",
-               "adamas_decode_append_step"):
+               "adamas_decode_append_step", "adamas_decode_paged_step"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -334,4 +337,42 @@ def decode_append_step(q, k, v, k_codes, lens, max_len: int, budget: int, k_new=
         _dev_ptr(out, "out"), _dev_ptr(idx_out, "idx_out"), _dev_ptr(buf, "ws"), buf.numel(),
         _stream(q, stream))
     _check(st, "adamas_decode_append_step")
+    return out
+
+
+def decode_paged_step(q, k_pool, v_pool, code_pool, page_table, lens, max_len: int, budget: int,
+                      k_new=None, v_new=None, scale: float = 0.0, out=None, idx_out=None,
+                      ws: Workspace | None = None, stream=None, n_sink: int = 0,
+                      n_recent: int = 0) -> torch.Tensor:
+    """decode_append_step over paged pools (adamas_decode_paged_step):
+    k_pool / v_pool [n_pages][Hkv][page_size][d], code_pool [n_pages][Hkv][page_size][d/4],
+    page_table int32 [B][max_pages], lens int32 [B]."""
+    B, Hq, d = q.shape
+    n_pages, Hkv, page, _ = k_pool.shape
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("q and the pools must share dtype; k and v pools share shape")
+    if tuple(code_pool.shape) != (n_pages, Hkv, page, d // 4) or code_pool.dtype != torch.uint8:
+        raise ValueError("code_pool must be uint8 [n_pages][Hkv][page_size][d/4]")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be int32 [B][max_pages]")
+    if lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
+        raise ValueError("lens must be int32 [B]")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        for t in (k_new, v_new):
+            if t.dtype != q.dtype or tuple(t.shape) != (B, Hkv, d):
+                raise ValueError("k_new, v_new must be [B][Hkv][d] of q's dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    nb = load().adamas_workspace_bytes(OP_DECODE_STEP, B, Hq, Hkv, max_len, budget, d)
+    buf = _ws_for(q.device, ws).get(nb)
+    st = load().adamas_decode_paged_step(
+        _dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
+        _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), _dev_ptr(code_pool, "code_pool"),
+        _dev_ptr(page_table, "page_table"), _dev_ptr(lens, "lens"), _dtype_code(q), B, Hq, Hkv, d,
+        page, n_pages, page_table.shape[1], max_len, budget, int(n_sink), int(n_recent),
+        float(scale), _dev_ptr(out, "out"), _dev_ptr(idx_out, "idx_out"), _dev_ptr(buf, "ws"),
+        buf.numel(), _stream(q, stream))
+    _check(st, "adamas_decode_paged_step")
     return out

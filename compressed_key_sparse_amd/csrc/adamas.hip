@@ -27,6 +27,8 @@ constexpr size_t kLdsLimit = 64 * 1024;    // per-workgroup LDS used by any kern
 // compute unit either way), so grouped heads scan chunks as long as MHA ones
 constexpr size_t kLdsDecodeLimit = 160 * 1024;
 constexpr int64_t kComputeUnits = 256;     // MI355X; workgroups of one decode round
+// Paged caches: a page holds at least one scan load of a wavefront per KV head
+constexpr int kMinPageTokens = 1024, kMaxPageTokens = 16384;
 constexpr int kMaxCandTile = 8192;         // candidate entries staged in LDS at once
 constexpr size_t kStreamBlocks = 1024;     // adamas_stream_read: four slices per compute unit
 
@@ -281,7 +283,7 @@ void allow_lds(K kernel, size_t lds) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-template <int D, int G, bool BF, bool RAG, bool OCC>
+template <int D, int G, bool BF, int RAG, bool OCC>
 void launch_decode_k(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
   allow_lds(&k_decode<D, G, BF, RAG, OCC>, p.sel.lds);
   k_decode<D, G, BF, RAG, OCC><<<grid, kDecodeThreads, p.sel.lds, s>>>(
@@ -297,19 +299,24 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
   // when their LDS allows it
   const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
   const bool occ = G == 1 && wgs > kComputeUnits && 2 * p.sel.lds <= kLdsDecodeLimit;
+  const int rag = a.rg.lens == nullptr ? 0 : (a.rg.pages == nullptr ? 1 : 2);
   if constexpr (G == 1) {
     if (occ) {
-      if (a.rg.lens != nullptr)
-        launch_decode_k<D, G, BF, true, true>(p, grid, s, a);
+      if (rag == 2)
+        launch_decode_k<D, G, BF, 2, true>(p, grid, s, a);
+      else if (rag == 1)
+        launch_decode_k<D, G, BF, 1, true>(p, grid, s, a);
       else
-        launch_decode_k<D, G, BF, false, true>(p, grid, s, a);
+        launch_decode_k<D, G, BF, 0, true>(p, grid, s, a);
       return;
     }
   }
-  if (a.rg.lens != nullptr)
-    launch_decode_k<D, G, BF, true, false>(p, grid, s, a);
+  if (rag == 2)
+    launch_decode_k<D, G, BF, 2, false>(p, grid, s, a);
+  else if (rag == 1)
+    launch_decode_k<D, G, BF, 1, false>(p, grid, s, a);
   else
-    launch_decode_k<D, G, BF, false, false>(p, grid, s, a);
+    launch_decode_k<D, G, BF, 0, false>(p, grid, s, a);
 }
 
 template <int D, int G, bool BF>
@@ -349,23 +356,37 @@ bool dispatch_decode(int G, const DecodePlan& p, dim3 grid, hipStream_t s, const
   }
 }
 
+template <int D, bool BF>
+void launch_attend_t(dim3 grid, hipStream_t s, const void* q, const void* k, const void* v,
+                     const int32_t* idx, int Hq, int Hkv, int64_t cap, int budget, float qscale,
+                     float* part, uint32_t* ctr, void* out, const PageArgs* pa) {
+  if (pa != nullptr)
+    k_attend<D, BF, true><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
+                                                          qscale, part, ctr, out, *pa);
+  else
+    k_attend<D, BF, false><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
+                                                           qscale, part, ctr, out, PageArgs{});
+}
+
+// pa: the page table of paged K/V pools, or null for [B][Hkv][cap][D] caches
 void launch_attend(int D, bool bf, dim3 grid, hipStream_t s, const void* q, const void* k,
                    const void* v, const int32_t* idx, int Hq, int Hkv, int64_t cap, int budget,
-                   float qscale, float* part, uint32_t* ctr, void* out) {
+                   float qscale, float* part, uint32_t* ctr, void* out,
+                   const PageArgs* pa = nullptr) {
   if (D == 128) {
     if (bf)
-      k_attend<128, true><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
-                                                          qscale, part, ctr, out);
+      launch_attend_t<128, true>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
+                                 out, pa);
     else
-      k_attend<128, false><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
-                                                           qscale, part, ctr, out);
+      launch_attend_t<128, false>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
+                                  out, pa);
   } else {
     if (bf)
-      k_attend<64, true><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
-                                                         qscale, part, ctr, out);
+      launch_attend_t<64, true>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
+                                out, pa);
     else
-      k_attend<64, false><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
-                                                          qscale, part, ctr, out);
+      launch_attend_t<64, false>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
+                                 out, pa);
   }
 }
 
@@ -542,9 +563,11 @@ int launch_last_arrival(const DecodePlan& p, const DecodeArgs& a, int B, int hea
   }
   if (!p.fuse || a.chist != nullptr) {
     const dim3 gatt((unsigned)p.att.splits, (unsigned)a.Hq, (unsigned)B);
+    const PageArgs pa{a.rg.pages, a.rg.max_pages, a.rg.page_log2, a.rg.n_pages};
     launch_attend(head_dim, bf, gatt, stream, a.q, a.k, a.v, a.idx, a.Hq, a.Hkv, a.cap, a.budget,
                   a.qscale, reinterpret_cast<float*>(w + p.att.part_off),
-                  reinterpret_cast<uint32_t*>(w + kCtrlAttend), a.out);
+                  reinterpret_cast<uint32_t*>(w + kCtrlAttend), a.out,
+                  a.rg.pages != nullptr ? &pa : nullptr);
   }
   return launch_status();
 }
@@ -624,11 +647,19 @@ int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_
                                  budget, 0, 0, scale, out, idx_out, ws, ws_bytes, stream);
 }
 
-int adamas_decode_append_step(const void* q, const void* k_new, const void* v_new, void* k,
-                              void* v, uint8_t* k_codes, const int32_t* lens, int dtype, int B,
-                              int Hq, int Hkv, int head_dim, int64_t cap, int64_t max_len,
-                              int budget, int n_sink, int n_recent, float scale, void* out,
-                              int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// adamas_decode_append_step and adamas_decode_paged_step: validation shared
+// by both, then one last-arrival launch (plus the attention launch when the
+// selection is large).  pages == nullptr: contiguous [B][Hkv][cap] caches.
+int ragged_step(const void* q, const void* k_new, const void* v_new, void* k, void* v,
+                uint8_t* k_codes, const int32_t* lens, int dtype, int B, int Hq, int Hkv,
+                int head_dim, int64_t cap, int64_t max_len, int budget, int n_sink, int n_recent,
+                float scale, void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                hipStream_t stream, const int32_t* pages, int max_pages, int page_log2,
+                int n_pages) {
   if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
   const bool app = k_new != nullptr;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || cap < 1 || max_len < 1 || max_len > cap ||
@@ -655,8 +686,42 @@ int adamas_decode_append_step(const void* q, const void* k_new, const void* v_ne
   DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, max_len, budget, attend_qscale(scale, head_dim),
                reinterpret_cast<uint32_t*>(w + p.sel.cand_off),
                reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent,
-               RaggedArgs{lens, k_new, v_new, k, v, k_codes}};
+               RaggedArgs{lens, k_new, v_new, k, v, k_codes, pages, max_pages, page_log2,
+                          n_pages}};
   return launch_last_arrival(p, a, B, head_dim, dtype == ADAMAS_BF16, w, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int adamas_decode_append_step(const void* q, const void* k_new, const void* v_new, void* k,
+                              void* v, uint8_t* k_codes, const int32_t* lens, int dtype, int B,
+                              int Hq, int Hkv, int head_dim, int64_t cap, int64_t max_len,
+                              int budget, int n_sink, int n_recent, float scale, void* out,
+                              int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return ragged_step(q, k_new, v_new, k, v, k_codes, lens, dtype, B, Hq, Hkv, head_dim, cap,
+                     max_len, budget, n_sink, n_recent, scale, out, idx_out, ws, ws_bytes, stream,
+                     nullptr, 0, 0, 0);
+}
+
+int adamas_decode_paged_step(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                             void* v_pool, uint8_t* code_pool, const int32_t* page_table,
+                             const int32_t* lens, int dtype, int B, int Hq, int Hkv, int head_dim,
+                             int page_size, int n_pages, int max_pages, int64_t max_len,
+                             int budget, int n_sink, int n_recent, float scale, void* out,
+                             int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int page_log2 = 0;
+  while (page_log2 < 30 && (1 << page_log2) < page_size) ++page_log2;
+  if (page_size < kMinPageTokens || page_size > kMaxPageTokens || (1 << page_log2) != page_size)
+    return ADAMAS_ERR_UNSUPPORTED;
+  if (n_pages < 1 || max_pages < 1 || page_table == nullptr ||
+      reinterpret_cast<uintptr_t>(page_table) % 4 != 0)
+    return ADAMAS_ERR_INVALID;
+  return ragged_step(q, k_new, v_new, k_pool, v_pool, code_pool, lens, dtype, B, Hq, Hkv,
+                     head_dim, (int64_t)max_pages * page_size, max_len, budget, n_sink, n_recent,
+                     scale, out, idx_out, ws, ws_bytes, stream, page_table, max_pages, page_log2,
+                     n_pages);
 }
 
 int adamas_set_rotation(int on) {

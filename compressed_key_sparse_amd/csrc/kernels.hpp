@@ -94,12 +94,47 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
 // Codes are read as 16-byte units (64 codes) with non-temporal loads, U per
 // thread in flight; at D = 128 a token is two units held by a lane pair whose
 // partial sums are added with a DPP swap.
-template <int NT, int U>
-ADM_DEV void scan_load(const uint4* __restrict__ src, int units, int base, uint4 (&w)[U]) {
+//
+// Where a head's code units are: one contiguous stream, or pages of a pool.
+// load(bj, u, units) reads unit u = bj + threadIdx.x of the scan (bj is the
+// same on every lane: the batch base plus j * NT); units past `units` read an
+// in-bounds unit whose value is not used.
+struct ContigCodes {
+  const uint4* p;
+  ADM_DEV uint4 load(int, int u, int units) const {
+    return load_stream(p + (u < units ? u : units - 1));
+  }
+};
+
+// Paged code cache: the sequence's page table row `pt` maps its logical page
+// i (2^page_log2 tokens, 2^upp_log2 units per KV head) to a pool page;
+// pool page p holds the units of KV head h at ((p * Hkv + h) << upp_log2).
+// u0 is the chunk's first unit in the sequence.  Pages hold >= NT units and
+// chunks start on multiples of NT units, so the NT units of one load share a
+// page, whose table entry is read once per wavefront (scalar).  Entries
+// outside [0, n_pages) and pages past the table are clamped in bounds.
+struct PagedCodes {
+  const uint4* pool;
+  const int32_t* pt;
+  int64_t u0;
+  int upp_log2, hkv, Hkv, n_pages, max_pages;
+  ADM_DEV uint4 load(int bj, int u, int units) const {
+    const int64_t ab = u0 + bj;
+    int pg = (int)(ab >> upp_log2);
+    pg = __builtin_amdgcn_readfirstlane(pg < max_pages - 1 ? pg : max_pages - 1);
+    int id = pt[pg];
+    id = __builtin_amdgcn_readfirstlane(id < 0 ? 0 : (id < n_pages ? id : n_pages - 1));
+    const int64_t off = u < units ? (ab & ((1 << upp_log2) - 1)) + (u - bj) : 0;
+    return load_stream(pool + ((((int64_t)id * Hkv + hkv) << upp_log2) + off));
+  }
+};
+
+template <int NT, int U, class Src>
+ADM_DEV void scan_load(const Src& src, int units, int base, uint4 (&w)[U]) {
 #pragma unroll
   for (int j = 0; j < U; ++j) {
-    const int u = base + j * NT + (int)threadIdx.x;
-    w[j] = load_stream(src + (u < units ? u : units - 1));  // clamped: always in bounds
+    const int bj = base + j * NT;
+    w[j] = src.load(bj, bj + (int)threadIdx.x, units);
   }
 }
 
@@ -134,12 +169,11 @@ ADM_DEV void scan_units(const uint4 (&w)[U], int base, int units, const QPlanes 
 
 // Whole chunk; with `first` the caller has already issued the loads of the
 // first batch (units [0, NT*U)) into it.
-template <int D, int G, int NT, int U, class Sink>
-ADM_DEV void scan_chunk(const uint8_t* __restrict__ kbase, int valid, const QPlanes (&qp)[G],
-                        Sink&& sink, const uint4 (*first)[U] = nullptr) {
+template <int D, int G, int NT, int U, class Src, class Sink>
+ADM_DEV void scan_chunk(const Src& src, int valid, const QPlanes (&qp)[G], Sink&& sink,
+                        const uint4 (*first)[U] = nullptr) {
   constexpr int kUnitsPerToken = D / 64;
   const int units = valid * kUnitsPerToken;
-  const uint4* __restrict__ src = reinterpret_cast<const uint4*>(kbase);
   int base = 0;
   if (first != nullptr) {
     scan_units<D, G, NT, U>(*first, 0, units, qp, sink);
@@ -186,7 +220,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(const uint8_t* __restri
   const int valid = (int)min((int64_t)chunk, n_ctx - t0);
   const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
   uint16_t* drow = dist + ((int64_t)b * Hq + (int64_t)hkv * G) * n_ctx + t0;
-  scan_chunk<D, G, kScoreThreads, 8>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
+  scan_chunk<D, G, kScoreThreads, 8>(ContigCodes{reinterpret_cast<const uint4*>(kbase)}, valid,
+                                     qp, [&](int g, int tok, uint32_t d) {
     drow[(int64_t)g * n_ctx + tok] = (uint16_t)d;
   });
 }
@@ -281,11 +316,34 @@ struct RowOverride {
   int64_t off;
 };
 
-template <int D, bool BF, int NT, bool OVR = false>
+// Rows of a paged K/V (or code) pool for one (sequence, KV head): the
+// sequence's page table row pt maps its logical page t >> page_log2 to a pool
+// page, and token t sits in pool row ((page * Hkv + hkv) << page_log2) plus
+// its offset in the page.  Entries outside [0, n_pages) and pages past the
+// table are clamped in bounds (such rows hold whatever that page holds).
+struct PageMap {
+  const int32_t* pt;
+  int page_log2, n_pages, max_pages, hkv, Hkv;
+  ADM_DEV int32_t entry(int64_t t) const {
+    const int64_t pg = t >> page_log2;
+    return pt[pg < max_pages - 1 ? pg : max_pages - 1];
+  }
+  ADM_DEV bool valid(int64_t t) const {
+    const int32_t id = entry(t);
+    return (t >> page_log2) < max_pages && id >= 0 && id < n_pages;
+  }
+  ADM_DEV int64_t row(int64_t t) const {
+    int32_t id = entry(t);
+    id = id < 0 ? 0 : (id < n_pages ? id : n_pages - 1);
+    return (((int64_t)id * Hkv + hkv) << page_log2) + (t & ((1 << page_log2) - 1));
+  }
+};
+
+template <int D, bool BF, int NT, bool OVR = false, bool PG = false>
 ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
                          const void* __restrict__ v, int64_t qoff, int64_t kvrow0, int64_t cap,
                          const int32_t* rows, int nrows, float qscale, float* s_part,
-                         float* s_res, RowOverride ovr = {}) {
+                         float* s_res, RowOverride ovr = {}, PageMap pm = {}) {
   constexpr int EL = D / 16, NS = NT / 16, NW = NT / kWave, PW = 2 + D;
   // fp32 rows are twice the bytes: half the rows per batch keeps registers in budget
   constexpr int RB = BF ? kAttendRowsPerSlot : kAttendRowsPerSlot / 2;
@@ -309,7 +367,8 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
     // unselected slots load row 0 of the head (in bounds) and are skipped below
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
-      const int64_t r = kvrow0 + (tok[j] >= 0 ? tok[j] : 0);
+      const int64_t t = tok[j] >= 0 ? tok[j] : 0;
+      const int64_t r = PG ? pm.row(t) : kvrow0 + t;
       if (OVR && tok[j] >= 0 && tok[j] == ovr.tok) {
         kr[j].load(ovr.k, ovr.off + l16 * EL);
         vr[j].load(ovr.v, ovr.off + l16 * EL);
@@ -389,12 +448,19 @@ ADM_DEV void store_out(void* out, int64_t i, float val) {
 // adamas_sparse_attend (and the large-selection half of a decode step):
 // grid (splits, Hq, B), up to kAttendRowsPerBatch rows per workgroup.  With
 // more than one split, partial (m, l, o) triples are merged by the last
-// workgroup of the head.
-template <int D, bool BF>
+// workgroup of the head.  With PG, k and v are paged pools and `pages` the
+// page table (PageMap; cap is then its logical capacity).
+struct PageArgs {
+  const int32_t* pages;  // [B][max_pages]
+  int max_pages, page_log2, n_pages;
+};
+
+template <int D, bool BF, bool PG = false>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ idx, int Hq, int Hkv, int64_t cap, int budget, float qscale,
-    float* __restrict__ part, uint32_t* __restrict__ counters, void* __restrict__ out) {
+    float* __restrict__ part, uint32_t* __restrict__ counters, void* __restrict__ out,
+    PageArgs pa = {}) {
   constexpr int NT = kAttendThreads, NW = NT / kWave, PW = 2 + D;
   constexpr int PWP = (PW + 3) & ~3;  // partial rows padded to 16 bytes
   constexpr int kMergeTile = 32;
@@ -408,8 +474,10 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
   const int64_t kvrow0 = ((int64_t)b * Hkv + hq / G) * cap;
   const int r0 = s * kAttendRowsPerBatch;
   const int nrows = min(kAttendRowsPerBatch, budget - r0);
-  attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, idx + row * budget + r0, nrows, qscale,
-                         s_part, s_res);
+  const PageMap pm{PG ? pa.pages + (int64_t)b * pa.max_pages : nullptr, pa.page_log2, pa.n_pages,
+                   pa.max_pages, hq / G, Hkv};
+  attend_rows<D, BF, NT, false, PG>(q, k, v, row * D, kvrow0, cap, idx + row * budget + r0, nrows,
+                                    qscale, s_part, s_res, RowOverride{}, pm);
   if (S == 1) {
     if (threadIdx.x < D) {
       const float L = s_res[1];
@@ -509,6 +577,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
 // and the step attends over lens[b] + 1 rows.  n_ctx is then the host's
 // bound on those lengths (the grid is planned for it); lens are clamped to
 // it and to the cache.
+// With a page table (the paged variant, RAG == 2) k, v and k_codes are pools
+// of pages as PageMap describes, and cap is the table's logical capacity.
 struct RaggedArgs {
   const int32_t* lens;         // [B]
   const void* k_new;           // [B][Hkv][D] elements, or null: nothing appended
@@ -516,12 +586,16 @@ struct RaggedArgs {
   void* k_cache;               // the K, V and code caches again, written at row lens[b]
   void* v_cache;
   uint8_t* code_cache;
+  const int32_t* pages;        // [B][max_pages] pool page of each logical page (RAG == 2)
+  int max_pages, page_log2, n_pages;
 };
 
 // OCC: compiled for two resident workgroups per compute unit (at most 64
 // VGPRs), for launches of several rounds, where one workgroup's chunk tail
 // then overlaps the other's scan.
-template <int D, int G, bool BF, bool RAG, bool OCC = false>
+// RAG: 0 every sequence holds n_ctx rows; 1 ragged (RaggedArgs); 2 ragged
+// over paged pools.
+template <int D, int G, bool BF, int RAG, bool OCC = false>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(OCC ? 8 : 1)))
 void k_decode(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -582,10 +656,18 @@ void k_decode(
   const int64_t t0 = (int64_t)c * chunk;
   // rows of the grid's chunk (the planned bound), then of this sequence
   const int valid_grid = (int)min((int64_t)chunk, n_ctx - t0);
-  const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
+  [[maybe_unused]] const PageMap pmap{rg.pages + (int64_t)b * rg.max_pages, rg.page_log2,
+                                      rg.n_pages, rg.max_pages, hkv, Hkv};
+  const auto src = [&] {
+    if constexpr (RAG == 2)
+      return PagedCodes{reinterpret_cast<const uint4*>(k_codes), pmap.pt, t0 * (D / 64),
+                        rg.page_log2 + (D == 128 ? 1 : 0), hkv, Hkv, rg.n_pages, rg.max_pages};
+    else
+      return ContigCodes{reinterpret_cast<const uint4*>(
+          k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4))};
+  }();
   uint4 first[kDecodeScanDepth];
-  scan_load<NT, kDecodeScanDepth>(reinterpret_cast<const uint4*>(kbase), valid_grid * (D / 64), 0,
-                                  first);
+  scan_load<NT, kDecodeScanDepth>(src, valid_grid * (D / 64), 0, first);
   __builtin_amdgcn_sched_barrier(0);  // keep the code loads ahead of the wait for q
   if constexpr (RAG) {
     if (c >= active) {
@@ -614,13 +696,17 @@ void k_decode(
       float y[E];
       widen_elems<E, BF>(kraw, y);
       const uint32_t word = wave_encode<D>(y, rotate != 0);
-      const int64_t crow = ((int64_t)b * Hkv + hkv) * cap + pos_new;
+      const int64_t crow =
+          RAG == 2 ? pmap.row(pos_new) : ((int64_t)b * Hkv + hkv) * cap + pos_new;
+      // a paged row whose table entry is out of range is scored but not stored
+      const bool store = RAG != 2 || pmap.valid(pos_new);
       if (lane % kLanesPerWord == 0) {
         s_knew[lane / kLanesPerWord] = word;
-        reinterpret_cast<uint32_t*>(rg.code_cache + crow * (D / 4))[lane / kLanesPerWord] = word;
+        if (store)
+          reinterpret_cast<uint32_t*>(rg.code_cache + crow * (D / 4))[lane / kLanesPerWord] = word;
       }
       constexpr int kRowBytes = D * (BF ? 2 : 4);
-      if (lane < kRowBytes / 16) {
+      if (store && lane < kRowBytes / 16) {
         const uint4 kv = reinterpret_cast<const uint4*>(
             static_cast<const uint8_t*>(rg.k_new) + src * (BF ? 2 : 4))[lane];
         const uint4 vv = reinterpret_cast<const uint4*>(
@@ -640,7 +726,7 @@ void k_decode(
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
   const KeepRange keep(t0, valid, n_sink, n_b - n_recent);
-  scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid_mem, qp, [&](int g, int tok, uint32_t d) {
+  scan_chunk<D, G, NT, kDecodeScanDepth>(src, valid_mem, qp, [&](int g, int tok, uint32_t d) {
     const uint32_t key = keep.key(tok, d);
     sdist[g * chunk + tok] = (uint16_t)key;
     atomicAdd(&shist[g * NBP + key], 1u);
@@ -681,10 +767,11 @@ void k_decode(
                      scand, mcap, fhist, s_tmp);
     if (fuse_attend) {
       if constexpr (RAG)
-        attend_rows<D, BF, NT, true>(q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part,
-                                     s_res, RowOverride{rg.k_new, rg.v_new,
-                                                        rg.k_new != nullptr ? pos_new : -2,
-                                                        ((int64_t)b * Hkv + hkv) * D});
+        attend_rows<D, BF, NT, true, RAG == 2>(
+            q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part, s_res,
+            RowOverride{rg.k_new, rg.v_new, rg.k_new != nullptr ? pos_new : -2,
+                        ((int64_t)b * Hkv + hkv) * D},
+            pmap);
       else
         attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part, s_res);
       if (threadIdx.x < D) {
@@ -898,9 +985,9 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   const int64_t t0 = (int64_t)c * chunk;
   const int valid = (int)min((int64_t)chunk, n_ctx - t0);
   const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);
+  const ContigCodes src{reinterpret_cast<const uint4*>(kbase)};
   uint4 first[kDecodeScanDepth];
-  scan_load<NT, kDecodeScanDepth>(reinterpret_cast<const uint4*>(kbase), valid * (D / 64), 0,
-                                  first);
+  scan_load<NT, kDecodeScanDepth>(src, valid * (D / 64), 0, first);
   __builtin_amdgcn_sched_barrier(0);
   if (wid < G) {
     float y[E];
@@ -912,7 +999,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
   const KeepRange keep(t0, valid, n_sink, n_ctx - n_recent);
-  scan_chunk<D, G, NT, kDecodeScanDepth>(kbase, valid, qp, [&](int g, int tok, uint32_t d) {
+  scan_chunk<D, G, NT, kDecodeScanDepth>(src, valid, qp, [&](int g, int tok, uint32_t d) {
     const uint32_t key = keep.key(tok, d);
     sdist[g * chunk + tok] = (uint16_t)key;
     atomicAdd(&shist[g * NBP + key], 1u);

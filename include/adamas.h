@@ -278,6 +278,40 @@ int adamas_decode_append_step(const void *q, const void *k_new, const void *v_ne
                               int budget, int n_sink, int n_recent, float scale, void *out,
                               int32_t *idx_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * adamas_decode_append_step over paged caches.  The article's compressed
+ * cache is built in chunks of a fixed number of tokens (§3.1, chunk_size
+ * 1024); here every cache is a pool of such pages shared by all sequences,
+ * and a page table maps each sequence's logical pages to pool pages, so a
+ * sequence grows one page at a time without moving its rows.
+ *   k_pool, v_pool  [n_pages][Hkv][page_size][head_dim] of dtype
+ *   code_pool       [n_pages][Hkv][page_size][head_dim/4] u8
+ *          (one pool page holds page_size consecutive tokens of every KV head;
+ *          a page of one head is contiguous, so adamas_encode_keys with
+ *          batch 1, heads Hkv, cap page_size fills it, x_copy_dst the K page)
+ *   page_table [B][max_pages] int32 device memory: pool page of logical page
+ *          i of sequence b, i.e. of its tokens [i*page_size, (i+1)*page_size).
+ *          Entries for pages a sequence does not reach are not read.
+ *   page_size  a power of two in [1024, 16384].
+ *   max_len    <= max_pages * page_size (the logical capacity).
+ * Token t of sequence b, KV head h, is pool row
+ * (page_table[b][t / page_size] * Hkv + h) * page_size + t % page_size.
+ * Everything else (lens, k_new/v_new and the row they are written to,
+ * clamping, outputs, workspace, errors) is as adamas_decode_append_step, with
+ * the logical capacity in place of cap.  Page table entries outside
+ * [0, n_pages) give undefined results for the rows they map (reads stay
+ * inside the pools; a new token whose entry is out of range is not stored).
+ * ADAMAS_ERR_UNSUPPORTED for a page_size outside the range above,
+ * ADAMAS_ERR_INVALID for n_pages or max_pages < 1 or a NULL or misaligned
+ * page table (4 bytes).
+ */
+int adamas_decode_paged_step(const void *q, const void *k_new, const void *v_new, void *k_pool,
+                             void *v_pool, uint8_t *code_pool, const int32_t *page_table,
+                             const int32_t *lens, int dtype, int B, int Hq, int Hkv, int head_dim,
+                             int page_size, int n_pages, int max_pages, int64_t max_len,
+                             int budget, int n_sink, int n_recent, float scale, void *out,
+                             int32_t *idx_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes needed by `op` for the given shape (0 for invalid shapes). */
 size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx,
                               int budget, int head_dim);

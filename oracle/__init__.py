@@ -252,5 +252,42 @@ def decode_append_step(q, k, v, k_codes, lens, max_len: int, budget: int, k_new=
     return out, out64, idx, k, v, k_codes
 
 
+def decode_paged_step(q, k_pool, v_pool, code_pool, page_table, lens, max_len: int, budget: int,
+                      k_new=None, v_new=None, scale: float = 0.0, n_sink: int = 0,
+                      n_recent: int = 0, rotate: bool = True):
+    """decode_append_step over paged pools (the §3.1 cache kept in fixed-size
+    chunks): pool page p holds tokens of every KV head, k_pool[p][h][j] is
+    token j of the page; sequence b's logical page i is pool page
+    page_table[b][i].  Each sequence's cache is gathered into one contiguous
+    array, stepped as decode_append_step does, and its new row (if any) put
+    back into copies of the pools -> (out, out64, idx, k_pool, v_pool, code_pool)."""
+    k_pool, v_pool, code_pool = (np.array(a, copy=True) for a in (k_pool, v_pool, code_pool))
+    B = q.shape[0]
+    n_pages, Hkv, P, d = k_pool.shape
+    max_pages = page_table.shape[1]
+    outs, out64s, idxs = [], [], []
+    for b in range(B):
+        pages = [int(x) for x in page_table[b]]
+        # only the pages the sequence reaches are looked up
+        need = (min(max(int(lens[b]), 0), max_len - (1 if k_new is not None else 0))
+                + (1 if k_new is not None else 0) + P - 1) // P
+        ids = [pages[i] if i < need else 0 for i in range(max_pages)]
+        gather = lambda pool: np.ascontiguousarray(
+            np.concatenate([pool[i] for i in ids], axis=1)[None])   # [1][Hkv][max_pages*P][...]
+        kb, vb, cb = gather(k_pool), gather(v_pool), gather(code_pool)
+        o, o64, ix, k2, v2, c2 = decode_append_step(
+            q[b:b + 1], kb, vb, cb, np.asarray(lens)[b:b + 1], max_len, budget,
+            None if k_new is None else k_new[b:b + 1], None if v_new is None else v_new[b:b + 1],
+            scale, n_sink, n_recent, rotate)
+        if k_new is not None:
+            L = min(max(int(lens[b]), 0), max_len - 1)
+            pg, off = ids[L // P], L % P
+            k_pool[pg][:, off] = k2[0][:, L]
+            v_pool[pg][:, off] = v2[0][:, L]
+            code_pool[pg][:, off] = c2[0][:, L]
+        outs.append(o[0]); out64s.append(o64[0]); idxs.append(ix[0])
+    return np.stack(outs), np.stack(out64s), np.stack(idxs), k_pool, v_pool, code_pool
+
+
 def f64_to_bf16_bits(x: float) -> int:
     return int(_load().ora_f64_to_bf16(float(x)))

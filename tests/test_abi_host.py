@@ -216,3 +216,23 @@ def test_append_step_validation(lib):
     assert call(budget=0) == INVALID
     assert call(sink=-1) == INVALID
     assert call(ws=need - 1) == WORKSPACE
+
+
+def test_paged_step_validation(lib):
+    f = lib.adamas_decode_paged_step
+    need = lib.adamas_workspace_bytes(2, 2, 8, 4, 4096, 64, 128)
+
+    def call(**kw):
+        return f(A, A, A, A, A, A, kw.get("table", A), A, 1, 2, 8, 4, 128,
+                 kw.get("page", 1024), kw.get("n_pages", 16), kw.get("max_pages", 4),
+                 kw.get("max_len", 4096), 64, 0, 0, ctypes.c_float(0.0), A, None, A,
+                 kw.get("ws", need), None)
+    assert call(page=1000) == UNSUPPORTED           # not a power of two
+    assert call(page=512) == UNSUPPORTED            # below one wavefront load per head
+    assert call(page=32768) == UNSUPPORTED
+    assert call(n_pages=0) == INVALID
+    assert call(max_pages=0) == INVALID
+    assert call(table=None) == INVALID
+    assert call(table=A + 2) == INVALID
+    assert call(max_len=4097) == INVALID            # beyond max_pages * page_size
+    assert call(ws=need - 1) == WORKSPACE

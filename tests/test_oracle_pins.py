@@ -534,3 +534,43 @@ def test_append_step_recent_window_and_empty_sequences(ora):
             continue
         o, o64, ix = ora.decode_step(q[b:b + 1], k[b:b + 1], v[b:b + 1], codes[b:b + 1], int(L), 4)
         assert np.array_equal(ix[0], idx[b]) and np.array_equal(o64[0], out64[b])
+
+
+def test_paged_step_matches_contiguous_layout(ora):
+    # the paged oracle over a shuffled pool equals the contiguous append step
+    # on the caches the page tables describe, and writes the new row into the
+    # pool page the table names
+    import torch
+    B, Hq, Hkv, d, P = 2, 4, 2, 64, 1024
+    pages_per_seq = 3
+    rng = np.random.default_rng(3)
+    q = synth.to_numpy_bits(synth.random_values((B, Hq, d), torch.bfloat16, 70))
+    kc = synth.to_numpy_bits(synth.random_values((B, Hkv, pages_per_seq * P, d), torch.bfloat16, 71))
+    vc = synth.to_numpy_bits(synth.random_values((B, Hkv, pages_per_seq * P, d), torch.bfloat16, 72))
+    kn = synth.to_numpy_bits(synth.random_values((B, Hkv, d), torch.bfloat16, 73))
+    vn = synth.to_numpy_bits(synth.random_values((B, Hkv, d), torch.bfloat16, 74))
+    cc = ora.encode_keys(kc)
+    n_pages = B * pages_per_seq + 2
+    perm = rng.permutation(n_pages)[:B * pages_per_seq].reshape(B, pages_per_seq)
+    kp = np.zeros((n_pages, Hkv, P, d), np.uint16)
+    vp = np.zeros_like(kp)
+    cp = np.zeros((n_pages, Hkv, P, d // 4), np.uint8)
+    for b in range(B):
+        for i in range(pages_per_seq):
+            kp[perm[b, i]] = kc[b][:, i * P:(i + 1) * P]
+            vp[perm[b, i]] = vc[b][:, i * P:(i + 1) * P]
+            cp[perm[b, i]] = cc[b][:, i * P:(i + 1) * P]
+    lens = np.array([2047, 1500], np.int32)       # the first appends at a page boundary
+    out, out64, idx, kp2, vp2, cp2 = ora.decode_paged_step(q, kp, vp, cp, perm.astype(np.int32),
+                                                           lens, 3 * P, 96, kn, vn)
+    o_ref, o64_ref, idx_ref, k2, v2, c2 = ora.decode_append_step(q, kc, vc, cc, lens, 3 * P, 96,
+                                                                 kn, vn)
+    assert np.array_equal(idx, idx_ref) and np.array_equal(out64, o64_ref)
+    for b in range(B):
+        L = int(lens[b])
+        pg, off = perm[b, L // P], L % P
+        assert np.array_equal(kp2[pg][:, off], kn[b]) and np.array_equal(vp2[pg][:, off], vn[b])
+        assert np.array_equal(cp2[pg][:, off], c2[b][:, L])
+    changed = [(p, h, j) for p, h, j in zip(*np.nonzero((kp2 != kp).any(-1)))]
+    assert sorted(changed) == sorted((perm[b, int(lens[b]) // P], h, int(lens[b]) % P)
+                                     for b in range(B) for h in range(Hkv))
