@@ -27,7 +27,10 @@ Prints ONE JSON line with:
                             ragged decode step that appends each sequence's new
                             token (adamas_decode_append_step) on one stream while
                             a 4096-token prefill chunk for one sequence is
-                            encoded and copied on a second stream.
+                            encoded and copied on a second stream.  With
+                            --paged the caches are a shuffled pool of
+                            1024-token pages (adamas_decode_paged_step) and
+                            the chunk fills four spare pool pages.
 """
 from __future__ import annotations
 
@@ -69,6 +72,8 @@ def parse():
                     help="also run a conversion kernel of known traffic (HBM counter scaling)")
     ap.add_argument("--workload", default=HEADLINE,
                     choices=(HEADLINE, "llama3.2-3b-gqa-1m", "batch16-mha-64k-append4k"))
+    ap.add_argument("--paged", action="store_true",
+                    help="batch16 workload: caches in a shuffled pool of 1024-token pages")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="print a compact summary of rocprofv3 CSV output under DIR and exit")
     return ap.parse_args()
@@ -462,6 +467,25 @@ def bench_batch_append(args, dev):
     codes = torch.empty((B, Hkv, w.cap, d // 4), dtype=torch.uint8, device=dev)
     for b in range(B):
         adamas.encode_keys(lay["k"][b:b + 1], codes[b:b + 1])
+    P = 1024
+    if args.paged:
+        # the same rows moved into a shuffled pool of pages (+4 for the chunk)
+        per = n // P
+        n_pages = B * per + 4
+        perm = np.random.default_rng(5).permutation(n_pages)
+        table = torch.from_numpy(perm[:B * per].reshape(B, per).astype(np.int32)).to(dev)
+        spare = [int(x) for x in perm[B * per:]]
+        kp = torch.empty((n_pages, Hkv, P, d), dtype=w.torch_dtype, device=dev)
+        vp = torch.empty_like(kp)
+        cp = torch.empty((n_pages, Hkv, P, d // 4), dtype=torch.uint8, device=dev)
+        for b in range(B):
+            for i in range(per):
+                pg = int(perm[b * per + i])
+                kp[pg] = lay["k"][b, :, i * P:(i + 1) * P]
+                vp[pg] = lay["v"][b, :, i * P:(i + 1) * P]
+                cp[pg] = codes[b, :, i * P:(i + 1) * P]
+        del lay["k"], lay["v"], codes
+        torch.cuda.empty_cache()
     # every sequence holds n - 1 rows; the step appends row n - 1 and attends n
     lens = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
     kn = synth.random_values((B, Hkv, d), w.torch_dtype, 77, device=dev)
@@ -475,15 +499,25 @@ def bench_batch_append(args, dev):
     ev = {}
 
     def decode():
-        adamas.decode_append_step(lay["q"], lay["k"], lay["v"], codes, lens, n, bud, k_new=kn,
-                                  v_new=vn, out=out, ws=ws, stream=s1)
+        if args.paged:
+            adamas.decode_paged_step(lay["q"], kp, vp, cp, table, lens, n, bud, k_new=kn,
+                                     v_new=vn, out=out, ws=ws, stream=s1)
+        else:
+            adamas.decode_append_step(lay["q"], lay["k"], lay["v"], codes, lens, n, bud, k_new=kn,
+                                      v_new=vn, out=out, ws=ws, stream=s1)
 
     def step(i, timed=None):
         b = i % B
         s2.wait_stream(s1)
         with torch.cuda.stream(s2):
-            adamas.encode_keys(chunks[i % len(chunks)], codes[b:b + 1], pos=n,
-                               x_copy=lay["k"][b:b + 1], stream=s2)
+            ch = chunks[i % len(chunks)]
+            if args.paged:   # the chunk's four pages, one encode call each
+                for j, pg in enumerate(spare):
+                    adamas.encode_keys(ch[:, :, j * P:(j + 1) * P].contiguous(),
+                                       cp[pg:pg + 1], x_copy=kp[pg:pg + 1], stream=s2)
+            else:
+                adamas.encode_keys(ch, codes[b:b + 1], pos=n, x_copy=lay["k"][b:b + 1],
+                                   stream=s2)
         if timed is not None:
             timed[0].record(s1)
         decode()
@@ -512,15 +546,17 @@ def bench_batch_append(args, dev):
     per_launch = algorithmic_bytes(B, Hq, Hkv, d, n, bud, 2) + B * Hkv * (4 * d * 2 + d // 4)
     chunk_bytes = Hkv * w.chunk * (2 * d * 2 + d // 4)   # read K, copy K, write codes
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.paged:
         cpu = cpu_baseline_append(lay, codes, lens, kn, vn, w, n, bud, args.cpu_seconds)
     result_line(
         f"batched decode+append tokens/s + achieved HBM GB/s, 16 x 64K ctx, budget {bud}, 1 GPU",
         w, B, ms, K, args.warmup,
         {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
          "n_ctx": n, "budget": bud, "prefill_chunk": w.chunk,
+         "layout": "paged, 1024-token pages, shuffled" if args.paged else "contiguous",
          "timing": "eager, two streams, step = both done"},
-        "adamas_decode_append_step (16 sequences, 4096-token chunk encoding beside it)",
+        ("adamas_decode_paged_step" if args.paged else "adamas_decode_append_step")
+        + " (16 sequences, 4096-token chunk encoding beside it)",
         per_launch, launch_us, stream_read_gbs(dev),
         {"step_ms": {"p10": round(float(np.percentile(step_times, 10)), 4),
                      "p50": round(float(np.percentile(step_times, 50)), 4),

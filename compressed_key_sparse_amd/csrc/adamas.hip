@@ -678,8 +678,21 @@ int ragged_step(const void* q, const void* k_new, const void* v_new, void* k, vo
                                         head_dim))
     return ADAMAS_ERR_WORKSPACE;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const DecodePlan p = plan_decode(B, Hq, Hkv, max_len, budget, head_dim);
+  DecodePlan p = plan_decode(B, Hq, Hkv, max_len, budget, head_dim);
   if (ws_bytes < p.total) return ADAMAS_ERR_WORKSPACE;
+  // paged with fused attention: the final workgroup keeps the page table row
+  // in LDS after the candidate tile, when it is short and fits
+  int pt_lds = 0;
+  if (pages != nullptr && p.fuse && max_pages <= kDecodeThreads) {
+    const size_t need = (size_t)kTmpWords * 4 +
+                        decode_lds_final(head_dim, (int)std::min<int64_t>(budget, max_len),
+                                         p.sel.mcap) +
+                        (size_t)max_pages * 4;
+    if (need <= kLdsDecodeLimit) {
+      p.sel.lds = std::max(p.sel.lds, need);
+      pt_lds = 1;
+    }
+  }
   int32_t* idx = idx_out != nullptr ? idx_out
                  : p.fuse       ? nullptr
                                 : reinterpret_cast<int32_t*>(w + p.idx_off);
@@ -687,7 +700,7 @@ int ragged_step(const void* q, const void* k_new, const void* v_new, void* k, vo
                reinterpret_cast<uint32_t*>(w + p.sel.cand_off),
                reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent,
                RaggedArgs{lens, k_new, v_new, k, v, k_codes, pages, max_pages, page_log2,
-                          n_pages}};
+                          n_pages, pt_lds}};
   return launch_last_arrival(p, a, B, head_dim, dtype == ADAMAS_BF16, w, stream);
 }
 

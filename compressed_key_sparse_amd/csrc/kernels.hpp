@@ -95,56 +95,63 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
 // thread in flight; at D = 128 a token is two units held by a lane pair whose
 // partial sums are added with a DPP swap.
 //
-// Where a head's code units are: one contiguous stream, or pages of a pool.
-// load(bj, u, units) reads unit u = bj + threadIdx.x of the scan (bj is the
-// same on every lane: the batch base plus j * NT); units past `units` read an
-// in-bounds unit whose value is not used.
+// Where a head's code units are, and which of them each lane takes: one
+// contiguous stream, or pages of a pool.  A scan walks batches at `base` in
+// [0, limit(units)) by step<NT, U>(); load j of a batch reads this lane's
+// unit(base, j), and units from bound(units) on are read in bounds but not
+// used.
 struct ContigCodes {
   const uint4* p;
-  ADM_DEV uint4 load(int, int u, int units) const {
+  template <int NT>
+  ADM_DEV int unit(int base, int j) const { return base + j * NT + (int)threadIdx.x; }
+  template <int NT, int U>
+  static constexpr int step() { return NT * U; }
+  ADM_DEV int limit(int units) const { return units; }
+  ADM_DEV int bound(int units) const { return units; }
+  ADM_DEV uint4 load(int u, int units) const {
     return load_stream(p + (u < units ? u : units - 1));
   }
 };
 
-// Paged code cache: the sequence's page table row `pt` maps its logical page
-// i (2^page_log2 tokens, 2^upp_log2 units per KV head) to a pool page;
-// pool page p holds the units of KV head h at ((p * Hkv + h) << upp_log2).
-// u0 is the chunk's first unit in the sequence.  Pages hold >= NT units and
-// chunks start on multiples of NT units, so the NT units of one load share a
-// page, whose table entry is read once per wavefront (scalar).  Entries
-// outside [0, n_pages) and pages past the table are clamped in bounds.
+// Paged code cache: each wavefront of the chunk's workgroup scans its own
+// stretch of `upw` consecutive units, [w0, w0 + upw), which lies inside one
+// page (pages hold >= 16 stretches and stretches start on multiples of upw),
+// so the page table is read once per wavefront and every load is a plain
+// offset from `page` (the pool units of this KV head in that page; poff is
+// the page offset of unit w0).
 struct PagedCodes {
-  const uint4* pool;
-  const int32_t* pt;
-  int64_t u0;
-  int upp_log2, hkv, Hkv, n_pages, max_pages;
-  ADM_DEV uint4 load(int bj, int u, int units) const {
-    const int64_t ab = u0 + bj;
-    int pg = (int)(ab >> upp_log2);
-    pg = __builtin_amdgcn_readfirstlane(pg < max_pages - 1 ? pg : max_pages - 1);
-    int id = pt[pg];
-    id = __builtin_amdgcn_readfirstlane(id < 0 ? 0 : (id < n_pages ? id : n_pages - 1));
-    const int64_t off = u < units ? (ab & ((1 << upp_log2) - 1)) + (u - bj) : 0;
-    return load_stream(pool + ((((int64_t)id * Hkv + hkv) << upp_log2) + off));
+  const uint4* page;
+  int w0, upw, poff;
+  template <int NT>
+  ADM_DEV int unit(int base, int j) const {
+    return w0 + base + j * kWave + (int)(threadIdx.x & (kWave - 1));
+  }
+  template <int NT, int U>
+  static constexpr int step() { return kWave * U; }
+  ADM_DEV int limit(int units) const {
+    const int r = units - w0;
+    return r < 0 ? 0 : (r < upw ? r : upw);
+  }
+  ADM_DEV int bound(int units) const { return units < w0 + upw ? units : w0 + upw; }
+  ADM_DEV uint4 load(int u, int units) const {
+    return load_stream(page + poff + ((u < bound(units) ? u : w0) - w0));
   }
 };
 
 template <int NT, int U, class Src>
 ADM_DEV void scan_load(const Src& src, int units, int base, uint4 (&w)[U]) {
 #pragma unroll
-  for (int j = 0; j < U; ++j) {
-    const int bj = base + j * NT;
-    w[j] = src.load(bj, bj + (int)threadIdx.x, units);
-  }
+  for (int j = 0; j < U; ++j) w[j] = src.load(src.template unit<NT>(base, j), units);
 }
 
-template <int D, int G, int NT, int U, class Sink>
-ADM_DEV void scan_units(const uint4 (&w)[U], int base, int units, const QPlanes (&qp)[G],
-                        Sink&& sink) {
+template <int D, int G, int NT, int U, class Src, class Sink>
+ADM_DEV void scan_units(const Src& src, const uint4 (&w)[U], int base, int units,
+                        const QPlanes (&qp)[G], Sink&& sink) {
   constexpr int kUnitsPerToken = D / 64;
+  const int bnd = src.bound(units);
 #pragma unroll
   for (int j = 0; j < U; ++j) {
-    const int u = base + j * NT + (int)threadIdx.x;
+    const int u = src.template unit<NT>(base, j);
     const uint32_t p0 = therm_p(w[j].x), p1 = therm_p(w[j].y);
     const uint32_t p2 = therm_p(w[j].z), p3 = therm_p(w[j].w);
     const uint32_t t0 = therm_t(w[j].x, w[j].y), t1 = therm_t(w[j].z, w[j].w);
@@ -160,7 +167,7 @@ ADM_DEV void scan_units(const uint4 (&w)[U], int base, int units, const QPlanes 
       if constexpr (kUnitsPerToken == 2) s += swap_pair(s);
       dg[g] = s;
     }
-    if (u < units && (kUnitsPerToken == 1 || (threadIdx.x & 1) == 0)) {
+    if (u < bnd && (kUnitsPerToken == 1 || (threadIdx.x & 1) == 0)) {
 #pragma unroll
       for (int g = 0; g < G; ++g) sink(g, u / kUnitsPerToken, dg[g]);
     }
@@ -168,21 +175,21 @@ ADM_DEV void scan_units(const uint4 (&w)[U], int base, int units, const QPlanes 
 }
 
 // Whole chunk; with `first` the caller has already issued the loads of the
-// first batch (units [0, NT*U)) into it.
+// first batch (base 0) into it.
 template <int D, int G, int NT, int U, class Src, class Sink>
 ADM_DEV void scan_chunk(const Src& src, int valid, const QPlanes (&qp)[G], Sink&& sink,
                         const uint4 (*first)[U] = nullptr) {
-  constexpr int kUnitsPerToken = D / 64;
-  const int units = valid * kUnitsPerToken;
+  constexpr int kUnitsPerToken = D / 64, kStep = Src::template step<NT, U>();
+  const int units = valid * kUnitsPerToken, lim = src.limit(units);
   int base = 0;
   if (first != nullptr) {
-    scan_units<D, G, NT, U>(*first, 0, units, qp, sink);
-    base = NT * U;
+    if (lim > 0) scan_units<D, G, NT, U>(src, *first, 0, units, qp, sink);
+    base = kStep;
   }
-  for (; base < units; base += NT * U) {
+  for (; base < lim; base += kStep) {
     uint4 w[U];
     scan_load<NT, U>(src, units, base, w);
-    scan_units<D, G, NT, U>(w, base, units, qp, sink);
+    scan_units<D, G, NT, U>(src, w, base, units, qp, sink);
   }
 }
 
@@ -588,6 +595,8 @@ struct RaggedArgs {
   uint8_t* code_cache;
   const int32_t* pages;        // [B][max_pages] pool page of each logical page (RAG == 2)
   int max_pages, page_log2, n_pages;
+  int pt_lds;                  // 1: the final workgroup copies the table row to LDS after
+                               // the candidate tile (max_pages <= kDecodeThreads)
 };
 
 // OCC: compiled for two resident workgroups per compute unit (at most 64
@@ -659,10 +668,19 @@ void k_decode(
   [[maybe_unused]] const PageMap pmap{rg.pages + (int64_t)b * rg.max_pages, rg.page_log2,
                                       rg.n_pages, rg.max_pages, hkv, Hkv};
   const auto src = [&] {
-    if constexpr (RAG == 2)
-      return PagedCodes{reinterpret_cast<const uint4*>(k_codes), pmap.pt, t0 * (D / 64),
-                        rg.page_log2 + (D == 128 ? 1 : 0), hkv, Hkv, rg.n_pages, rg.max_pages};
-    else
+    if constexpr (RAG == 2) {
+      // this wavefront's stretch of the chunk and the pool page holding it
+      constexpr int kUpt = D / 64;
+      const int upp_log2 = rg.page_log2 + (kUpt == 2 ? 1 : 0);
+      const int upw = chunk * kUpt / NW, w0 = wid * upw;
+      const int64_t a = t0 * kUpt + w0;
+      const int64_t pg = a >> upp_log2;
+      int id = pmap.pt[pg < rg.max_pages - 1 ? pg : rg.max_pages - 1];
+      id = __builtin_amdgcn_readfirstlane(id < 0 ? 0 : (id < rg.n_pages ? id : rg.n_pages - 1));
+      return PagedCodes{reinterpret_cast<const uint4*>(k_codes) +
+                            (((int64_t)id * Hkv + hkv) << upp_log2),
+                        w0, upw, (int)(a & ((1 << upp_log2) - 1))};
+    } else
       return ContigCodes{reinterpret_cast<const uint4*>(
           k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4))};
   }();
@@ -760,18 +778,34 @@ void k_decode(
   if (chist != nullptr) return;  // k_split_select takes it from here
   if (!arrive_last<NT>(&counters[b * Hkv + hkv], active, s_tmp)) return;
   const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap;
+  // paged: the gathers below look up the sequence's page table; its row is
+  // loaded now (in flight during the selection) and kept in LDS
+  [[maybe_unused]] PageMap amap = pmap;
+  [[maybe_unused]] int32_t pt_entry = 0;
+  if constexpr (RAG == 2) {
+    if (rg.pt_lds && fuse_attend && (int)threadIdx.x < rg.max_pages)
+      pt_entry = pmap.pt[threadIdx.x];
+  }
   for (int g = 0; g < G; ++g) {
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
     final_select<NT>(cand + row * n_chunks * kpad, active * kpad, kpad_log2, chunk, NB, bsel,
                      budget, fuse_attend ? sidx : nullptr, idx ? idx + row * budget : nullptr,
                      scand, mcap, fhist, s_tmp);
+    if constexpr (RAG == 2) {
+      if (g == 0 && rg.pt_lds && fuse_attend) {
+        int32_t* s_pt = reinterpret_cast<int32_t*>(scand + mcap);
+        if ((int)threadIdx.x < rg.max_pages) s_pt[threadIdx.x] = pt_entry;
+        lds_sync();
+        amap.pt = s_pt;
+      }
+    }
     if (fuse_attend) {
       if constexpr (RAG)
         attend_rows<D, BF, NT, true, RAG == 2>(
             q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part, s_res,
             RowOverride{rg.k_new, rg.v_new, rg.k_new != nullptr ? pos_new : -2,
                         ((int64_t)b * Hkv + hkv) * D},
-            pmap);
+            amap);
       else
         attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part, s_res);
       if (threadIdx.x < D) {
