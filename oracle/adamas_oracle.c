@@ -29,6 +29,7 @@
 #include <string.h>
 
 #define ORA_MAX_D 4096
+#define ORA_GROUP 128 /* dimensions per absmax group (§2.2 grouped quantization) */
 
 /* Element type tags shared with the Python wrapper (not with the library). */
 enum { ORA_F32 = 0, ORA_BF16 = 1 };
@@ -121,10 +122,11 @@ void ora_hadamard_orthonormal_f64(const double *x, double *y, int d)
 /* ------------------------------------------------------------------------
  * §2.2 -- three-threshold dynamic bucketing of one rotated vector.
  *
- * absmax a = max_i |y_i| over the vector (reading: one absmax per vector,
- * i.e. per token and KV head or per query head; at head_dim <= 128 this is
- * also the article's 128-dimension group).  Thresholds t0 = -0.5a, t1 = 0,
- * t2 = +0.5a.  The comparison operator was lost in the article's text; the
+ * absmax a = max_i |y_i| over a group of dimensions (reading: the article's
+ * grouped quantization, one absmax per 128 consecutive rotated dimensions of
+ * one vector, i.e. per token and KV head or per query head; at head_dim <=
+ * 128 the group is the whole vector).  Thresholds t0 = -0.5a, t1 = 0,
+ * t2 = +0.5a, per group.  The comparison operator was lost in the article's text; the
  * reading is strict "less than":
  *     code = 0 if y < t0;  1 if y < 0;  2 if y < t2;  3 otherwise.
  * ---------------------------------------------------------------------- */
@@ -164,16 +166,19 @@ void ora_encode_vec_f32_rot(const float *x, int d, int rotate, uint8_t *packed, 
         y[i] = x[i];
     if (rotate)
         ora_fwht_f32(y, d);
-    float a = 0.0f;
-    for (int i = 0; i < d; i++) {
-        float m = fabsf(y[i]);
-        if (m > a)
-            a = m;
+    const int group = d < ORA_GROUP ? d : ORA_GROUP;
+    for (int g0 = 0; g0 < d; g0 += group) {
+        float a = 0.0f;
+        for (int i = g0; i < g0 + group; i++) {
+            float m = fabsf(y[i]);
+            if (m > a)
+                a = m;
+        }
+        float t0 = -0.5f * a;
+        float t2 = 0.5f * a;
+        for (int i = g0; i < g0 + group; i++)
+            c[i] = ora_bucket(y[i], t0, t2);
     }
-    float t0 = -0.5f * a;
-    float t2 = 0.5f * a;
-    for (int i = 0; i < d; i++)
-        c[i] = ora_bucket(y[i], t0, t2);
     ora_pack(c, d, packed);
     if (y_out)
         for (int i = 0; i < d; i++)

@@ -60,7 +60,7 @@ def test_fwht_columns_are_sylvester_hadamard(ora, d):
     assert np.array_equal(H @ H.T, d * np.eye(d, dtype=np.int64))
 
 
-@pytest.mark.parametrize("d", [4, 64, 128])
+@pytest.mark.parametrize("d", [4, 64, 128, 256])
 def test_fwht_exact_on_integers(ora, d):
     # |x| * d < 2^24 keeps every partial sum exact in binary32
     x = synth.integer_values((50, d), -1000, 1000, seed=d)
@@ -121,7 +121,7 @@ def test_encode_hand_worked(ora, case):
     assert unpack_codes(p).tolist() == codes
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_encode_unit_vectors_closed_form(ora, d):
     # H e_j is column j of H (entries +-1, absmax 1): +1 -> code 3, -1 -> code 0
     H = sylvester(d)
@@ -574,3 +574,38 @@ def test_paged_step_matches_contiguous_layout(ora):
     changed = [(p, h, j) for p, h, j in zip(*np.nonzero((kp2 != kp).any(-1)))]
     assert sorted(changed) == sorted((perm[b, int(lens[b]) // P], h, int(lens[b]) % P)
                                      for b in range(B) for h in range(Hkv))
+
+
+# --------------------------------------------------------------------------
+# §2.2 grouped quantization: one absmax per 128 rotated dimensions
+def test_encode_groups_of_128_hand_worked(ora):
+    # Choose the rotated vector y directly and encode x = H y / 256 (exact:
+    # H H = 256 I and every intermediate is a small multiple of 1/256).
+    # y = [100, 1 x 127 | 2, -2, 2, -2, ...]: group 0 has absmax 100, so its
+    # 1s (0 <= 1 < 50) code to 2 and the 100 to 3; group 1 has absmax 2, so
+    # 2 >= 1 codes to 3 and -2 < -1 to 0.  Packed MSB-first: 3,2,2,2 -> 0xEA,
+    # then 0xAA x 31, then 3,0,3,0 -> 0xCC x 32.  One absmax over the whole
+    # vector would code group 1 as 2, 1 (0xA6...) instead.
+    d = 256
+    y = np.array([100] + [1] * 127 + [2, -2] * 64, np.int64)
+    x = (sylvester(d) @ y).astype(np.float64) / d
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    p, yr, c = ora.encode_vec(x.astype(np.float32))
+    assert np.array_equal(yr, y.astype(np.float32))
+    assert bytes(p) == bytes([0xEA] + [0xAA] * 31 + [0xCC] * 32)
+
+
+def test_encode_groups_are_independent(ora):
+    # each 128-dim group of a 256-dim code depends only on its own rotated
+    # values: scaling one group's rotated values leaves every code unchanged
+    rng = np.random.default_rng(5)
+    H = sylvester(256)
+    for _ in range(50):
+        y = rng.integers(-40, 41, 256)
+        x1 = (H @ y).astype(np.float32) / 256
+        y2 = y.copy()
+        y2[128:] *= 3
+        x2 = (H @ y2).astype(np.float32) / 256
+        p1, _, c1 = ora.encode_vec(x1)
+        p2, _, c2 = ora.encode_vec(x2)
+        assert np.array_equal(c1, c2) and bytes(p1) == bytes(p2)
