@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "adamas.h"
 #include "kernels.hpp"
@@ -35,8 +36,19 @@ constexpr size_t kStreamBlocks = 1024;     // adamas_stream_read: four slices pe
 bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool valid_dtype(int dt) { return dt == ADAMAS_F32 || dt == ADAMAS_BF16; }
-bool valid_dim(int d) { return d == 64 || d == 128; }
-size_t nbins_padded(int D) { return D == 128 ? (size_t)kNbinsPadded(128) : (size_t)kNbinsPadded(64); }
+bool valid_dim(int d) { return d == 64 || d == 128 || d == 256; }
+size_t nbins_padded(int D) { return (size_t)kNbinsPadded(D); }
+
+// Calls f(std::integral_constant<int, D>{}) for a supported head_dim D.
+template <class F>
+void with_dim(int d, F&& f) {
+  if (d == 256)
+    f(std::integral_constant<int, 256>{});
+  else if (d == 128)
+    f(std::integral_constant<int, 128>{});
+  else
+    f(std::integral_constant<int, 64>{});
+}
 
 // Candidate layout shared by the selection kernels: per head, n_chunks slots
 // of kpad u32 entries, kpad the power of two >= max(4, min(budget, chunk)).
@@ -83,7 +95,7 @@ int cand_slot(int budget, int chunk) {
   return k;
 }
 size_t decode_lds_scan(int D, int G, int c, int budget) {
-  return (size_t)G * (D / 16) * 4 + (size_t)G * nbins_padded(D) * 4 +
+  return (size_t)(G + 1) * (D / 16) * 4 + (size_t)G * nbins_padded(D) * 4 +
          (size_t)cand_slot(budget, c) * 4 + (size_t)G * c * 2;
 }
 // sel_rows = min(budget, n_ctx) indices are kept in LDS only when attention is fused.
@@ -373,21 +385,15 @@ void launch_attend(int D, bool bf, dim3 grid, hipStream_t s, const void* q, cons
                    const void* v, const int32_t* idx, int Hq, int Hkv, int64_t cap, int budget,
                    float qscale, float* part, uint32_t* ctr, void* out,
                    const PageArgs* pa = nullptr) {
-  if (D == 128) {
+  with_dim(D, [&](auto dc) {
+    constexpr int DD = decltype(dc)::value;
     if (bf)
-      launch_attend_t<128, true>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
-                                 out, pa);
-    else
-      launch_attend_t<128, false>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
-                                  out, pa);
-  } else {
-    if (bf)
-      launch_attend_t<64, true>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
+      launch_attend_t<DD, true>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
                                 out, pa);
     else
-      launch_attend_t<64, false>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
+      launch_attend_t<DD, false>(grid, s, q, k, v, idx, Hq, Hkv, cap, budget, qscale, part, ctr,
                                  out, pa);
-  }
+  });
 }
 
 // Score scale in the log2 domain: s2 = (q . k) * scale * log2(e).
@@ -447,12 +453,10 @@ int adamas_encode_keys(const void* x, int dtype, int batch, int heads, int64_t n
   const int64_t blocks64 = (nvec + 3) / 4;
   const unsigned blocks = (unsigned)(blocks64 < 16384 ? blocks64 : 16384);
   const int bf = dtype == ADAMAS_BF16;
-  if (head_dim == 128)
-    k_encode<128><<<blocks, kEncodeThreads, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst,
-                                                         rotation_on());
-  else
-    k_encode<64><<<blocks, kEncodeThreads, 0, stream>>>(x, bf, n, nvec, codes, cap, pos, x_copy_dst,
-                                                        rotation_on());
+  with_dim(head_dim, [&](auto dc) {
+    k_encode<decltype(dc)::value><<<blocks, kEncodeThreads, 0, stream>>>(
+        x, bf, n, nvec, codes, cap, pos, x_copy_dst, rotation_on());
+  });
   return launch_status();
 }
 
@@ -468,11 +472,11 @@ int adamas_score(const uint8_t* q_codes, const uint8_t* k_codes, int B, int Hq, 
   const int chunk = 4096;
   const dim3 grid((unsigned)((n_ctx + chunk - 1) / chunk), (unsigned)Hkv, (unsigned)B);
   const int G = Hq / Hkv;
-  const bool ok = head_dim == 128
-                      ? dispatch_score<128>(G, grid, stream, q_codes, k_codes, Hq, Hkv, cap,
-                                            n_ctx, chunk, dist)
-                      : dispatch_score<64>(G, grid, stream, q_codes, k_codes, Hq, Hkv, cap,
-                                           n_ctx, chunk, dist);
+  bool ok = false;
+  with_dim(head_dim, [&](auto dc) {
+    ok = dispatch_score<decltype(dc)::value>(G, grid, stream, q_codes, k_codes, Hq, Hkv, cap,
+                                             n_ctx, chunk, dist);
+  });
   if (!ok) return ADAMAS_ERR_UNSUPPORTED;
   return launch_status();
 }
@@ -495,14 +499,11 @@ int adamas_select_topk_keep(const uint16_t* dist, int B, int Hq, int64_t n_ctx, 
   const dim3 grid((unsigned)p.n_chunks, (unsigned)Hq, (unsigned)B);
   uint32_t* cand = reinterpret_cast<uint32_t*>(w + p.cand_off);
   uint32_t* ctr = reinterpret_cast<uint32_t*>(w + kCtrlSelect);
-  if (head_dim == 128)
-    k_select<128><<<grid, kSelectThreads, p.lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks,
-                                                           budget, p.kpad_log2, p.mcap, cand, ctr, idx,
-                                                           n_sink, n_recent);
-  else
-    k_select<64><<<grid, kSelectThreads, p.lds, stream>>>(dist, Hq, n_ctx, p.chunk, p.n_chunks,
-                                                          budget, p.kpad_log2, p.mcap, cand, ctr, idx,
-                                                          n_sink, n_recent);
+  with_dim(head_dim, [&](auto dc) {
+    k_select<decltype(dc)::value><<<grid, kSelectThreads, p.lds, stream>>>(
+        dist, Hq, n_ctx, p.chunk, p.n_chunks, budget, p.kpad_log2, p.mcap, cand, ctr, idx,
+        n_sink, n_recent);
+  });
   return launch_status();
 }
 
@@ -546,13 +547,12 @@ int launch_last_arrival(const DecodePlan& p, const DecodeArgs& a, int B, int hea
                         uint8_t* w, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const dim3 grid((unsigned)p.sel.n_chunks, (unsigned)a.Hkv, (unsigned)B);
-  bool ok;
-  if (head_dim == 128)
-    ok = bf ? dispatch_decode<128, true>(G, p, grid, stream, a)
-            : dispatch_decode<128, false>(G, p, grid, stream, a);
-  else
-    ok = bf ? dispatch_decode<64, true>(G, p, grid, stream, a)
-            : dispatch_decode<64, false>(G, p, grid, stream, a);
+  bool ok = false;
+  with_dim(head_dim, [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    ok = bf ? dispatch_decode<D, true>(G, p, grid, stream, a)
+            : dispatch_decode<D, false>(G, p, grid, stream, a);
+  });
   if (!ok) return ADAMAS_ERR_UNSUPPORTED;
   if (a.chist != nullptr) {
     const int bsel = (int)(a.n_ctx < a.budget ? a.n_ctx : a.budget);
@@ -613,11 +613,12 @@ int adamas_decode_step_keep(const void* q, const void* k, const void* v, const u
       DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
                    nullptr, nullptr, idx_out, out, n_sink, n_recent, {}};
       const dim3 grid((unsigned)gp.n_chunks, (unsigned)Hkv, (unsigned)B);
-      const bool ok = head_dim == 128
-                          ? (bf ? dispatch_decode_gs<128, true>(G, gp, grid, stream, a, w)
-                                : dispatch_decode_gs<128, false>(G, gp, grid, stream, a, w))
-                          : (bf ? dispatch_decode_gs<64, true>(G, gp, grid, stream, a, w)
-                                : dispatch_decode_gs<64, false>(G, gp, grid, stream, a, w));
+      bool ok = false;
+      with_dim(head_dim, [&](auto dc) {
+        constexpr int D = decltype(dc)::value;
+        ok = bf ? dispatch_decode_gs<D, true>(G, gp, grid, stream, a, w)
+                : dispatch_decode_gs<D, false>(G, gp, grid, stream, a, w);
+      });
       if (!ok) return ADAMAS_ERR_UNSUPPORTED;
       return launch_status();
     }

@@ -46,12 +46,18 @@ ADM_DEV uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Load `E` consecutive elements starting at element `i` (E in {1, 2}).
+// Load `E` consecutive elements starting at element `i` (E in {1, 2, 4}).
 template <int E>
 ADM_DEV void load_elems(const void* base, bool is_bf16, int64_t i, float (&out)[E]) {
   if (is_bf16) {
     const uint16_t* p = static_cast<const uint16_t*>(base) + i;
-    if constexpr (E == 2) {
+    if constexpr (E == 4) {
+      const uint2 w = *reinterpret_cast<const uint2*>(p);
+      out[0] = bf16_to_f32(w.x & 0xffffu);
+      out[1] = bf16_to_f32(w.x >> 16);
+      out[2] = bf16_to_f32(w.y & 0xffffu);
+      out[3] = bf16_to_f32(w.y >> 16);
+    } else if constexpr (E == 2) {
       uint32_t w = *reinterpret_cast<const uint32_t*>(p);
       out[0] = bf16_to_f32(w & 0xffffu);
       out[1] = bf16_to_f32(w >> 16);
@@ -60,7 +66,13 @@ ADM_DEV void load_elems(const void* base, bool is_bf16, int64_t i, float (&out)[
     }
   } else {
     const float* p = static_cast<const float*>(base) + i;
-    if constexpr (E == 2) {
+    if constexpr (E == 4) {
+      const float4 w = *reinterpret_cast<const float4*>(p);
+      out[0] = w.x;
+      out[1] = w.y;
+      out[2] = w.z;
+      out[3] = w.w;
+    } else if constexpr (E == 2) {
       float2 w = *reinterpret_cast<const float2*>(p);
       out[0] = w.x;
       out[1] = w.y;
@@ -71,27 +83,41 @@ ADM_DEV void load_elems(const void* base, bool is_bf16, int64_t i, float (&out)[
 }
 
 // The same elements as raw bits (issue the load now, widen later with
-// widen_elems): E * 2 or E * 4 bytes in a uint2.
+// widen_elems): E * 2 or E * 4 bytes in a uint4 (only the bytes loaded are
+// set; the rest are zero).
 template <int E, bool BF>
-ADM_DEV uint2 load_elems_raw(const void* base, int64_t i) {
+ADM_DEV uint4 load_elems_raw(const void* base, int64_t i) {
   if constexpr (BF) {
     const uint16_t* p = static_cast<const uint16_t*>(base) + i;
-    if constexpr (E == 2) return make_uint2(*reinterpret_cast<const uint32_t*>(p), 0u);
-    else return make_uint2(*p, 0u);
+    if constexpr (E == 4) {
+      const uint2 w = *reinterpret_cast<const uint2*>(p);
+      return make_uint4(w.x, w.y, 0u, 0u);
+    } else if constexpr (E == 2) {
+      return make_uint4(*reinterpret_cast<const uint32_t*>(p), 0u, 0u, 0u);
+    } else {
+      return make_uint4(*p, 0u, 0u, 0u);
+    }
   } else {
     const float* p = static_cast<const float*>(base) + i;
-    if constexpr (E == 2) return *reinterpret_cast<const uint2*>(p);
-    else return make_uint2(__float_as_uint(*p), 0u);
+    if constexpr (E == 4) {
+      return *reinterpret_cast<const uint4*>(p);
+    } else if constexpr (E == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(p);
+      return make_uint4(w.x, w.y, 0u, 0u);
+    } else {
+      return make_uint4(__float_as_uint(*p), 0u, 0u, 0u);
+    }
   }
 }
 template <int E, bool BF>
-ADM_DEV void widen_elems(uint2 raw, float (&out)[E]) {
-  if constexpr (BF) {
-    out[0] = bf16_to_f32(raw.x & 0xffffu);
-    if constexpr (E == 2) out[1] = bf16_to_f32(raw.x >> 16);
-  } else {
-    out[0] = __uint_as_float(raw.x);
-    if constexpr (E == 2) out[1] = __uint_as_float(raw.y);
+ADM_DEV void widen_elems(uint4 raw, float (&out)[E]) {
+  const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if constexpr (BF)
+      out[e] = bf16_to_f32((e & 1) ? (r[e >> 1] >> 16) : (r[e >> 1] & 0xffffu));
+    else
+      out[e] = __uint_as_float(r[e]);
   }
 }
 
@@ -230,8 +256,10 @@ ADM_DEV float xor_max(float x) {
 // order (addition is commutative and round-to-nearest is sign-symmetric).
 // Stages below E are inside a lane; the rest exchange with lane ^ (h / E).
 //
-// Bucketing: a = max|y| over the vector, thresholds -0.5a, 0, +0.5a, codes
-// 0 if y < -a/2, 1 if y < 0, 2 if y < a/2, else 3 (strict comparisons).
+// Bucketing: a = max|y| over a group of 128 dimensions (the whole vector
+// when D <= 128; at D = 256 lanes 0-31 and 32-63 hold the two groups),
+// thresholds -0.5a, 0, +0.5a, codes 0 if y < -a/2, 1 if y < 0, 2 if
+// y < a/2, else 3 (strict comparisons).
 //
 // Packing (§3.1): four codes per byte, first code in bits 7..6; returns, on
 // the lanes with (lane % (16/E)) == 0, the little-endian 32-bit word
@@ -279,7 +307,7 @@ ADM_DEV uint32_t wave_encode(float (&y)[D / 64], bool rotate = true) {
   a = fmaxf(a, lane_xor<4>(a));
   a = fmaxf(a, lane_xor<8>(a));
   a = xor_max<16>(a);
-  a = xor_max<32>(a);
+  if constexpr (D <= 128) a = xor_max<32>(a);  // else one absmax per 32-lane half
   const float t0 = -0.5f * a;
   const float t2 = 0.5f * a;
   uint32_t bits = 0;
@@ -294,7 +322,7 @@ ADM_DEV uint32_t wave_encode(float (&y)[D / 64], bool rotate = true) {
   constexpr int kLanesPerWord = 16 / E;
   bits |= lane_xor_u32<1>(bits);
   bits |= lane_xor_u32<2>(bits);
-  bits |= lane_xor_u32<4>(bits);
+  if constexpr (kLanesPerWord >= 8) bits |= lane_xor_u32<4>(bits);
   if constexpr (kLanesPerWord == 16) bits |= lane_xor_u32<8>(bits);
   return (lane % kLanesPerWord) == 0 ? bits : 0u;
 }

@@ -67,13 +67,19 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
     if (copy != nullptr) {
       const int64_t dst = row * D + lane * E;
       if (is_bf16) {
-        if constexpr (E == 2)
+        if constexpr (E == 4)
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(copy) + dst) =
+              *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + src);
+        else if constexpr (E == 2)
           *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(copy) + dst) =
               *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + src);
         else
           static_cast<uint16_t*>(copy)[dst] = static_cast<const uint16_t*>(x)[src];
       } else {
-        if constexpr (E == 2)
+        if constexpr (E == 4)
+          *reinterpret_cast<uint4*>(static_cast<float*>(copy) + dst) =
+              *reinterpret_cast<const uint4*>(static_cast<const float*>(x) + src);
+        else if constexpr (E == 2)
           *reinterpret_cast<uint2*>(static_cast<float*>(copy) + dst) =
               *reinterpret_cast<const uint2*>(static_cast<const float*>(x) + src);
         else
@@ -165,9 +171,13 @@ ADM_DEV void scan_units(const Src& src, const uint4 (&w)[U], int base, int units
       s += __popc(t0 ^ qp[g].t[0]);
       s += __popc(t1 ^ qp[g].t[1]);
       if constexpr (kUnitsPerToken == 2) s += swap_pair(s);
+      if constexpr (kUnitsPerToken == 4) {  // a quad of lanes holds one token
+        s += lane_xor_u32<1>(s);
+        s += lane_xor_u32<2>(s);
+      }
       dg[g] = s;
     }
-    if (u < bnd && (kUnitsPerToken == 1 || (threadIdx.x & 1) == 0)) {
+    if (u < bnd && (threadIdx.x & (kUnitsPerToken - 1)) == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g) sink(g, u / kUnitsPerToken, dg[g]);
     }
@@ -193,15 +203,16 @@ ADM_DEV void scan_chunk(const Src& src, int valid, const QPlanes (&qp)[G], Sink&
   }
 }
 
-// Query planes for this thread's half of the row (D = 128: lane parity picks
-// words 0-3 or 4-7; D = 64: the whole row) from packed words in LDS.
+// Query planes for this thread's part of the row (D/64 consecutive lanes hold
+// one token's units; lane t of them takes words 4t..4t+3) from packed words in
+// LDS.
 template <int D, int G>
 ADM_DEV void load_qplanes(const uint32_t* sq, QPlanes (&qp)[G]) {
   constexpr int W = D / 16;
-  const int half = (D == 128) ? (int)(threadIdx.x & 1) : 0;
+  const int part = (int)(threadIdx.x & (D / 64 - 1));
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const uint32_t* r = sq + g * W + half * 4;
+    const uint32_t* r = sq + g * W + part * 4;
     qp[g] = make_qplanes(r[0], r[1], r[2], r[3]);
   }
 }
@@ -264,9 +275,12 @@ struct RowRaw {
   ADM_DEV void load(const void* base, int64_t elem) {
     if constexpr (BF) {
       const uint16_t* p = static_cast<const uint16_t*>(base) + elem;
-      if constexpr (WORDS == 4) {
-        const uint4 t = *reinterpret_cast<const uint4*>(p);
-        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+      if constexpr (WORDS >= 4) {
+#pragma unroll
+        for (int i = 0; i < WORDS / 4; ++i) {
+          const uint4 t = reinterpret_cast<const uint4*>(p)[i];
+          w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
+        }
       } else {
         const uint2 t = *reinterpret_cast<const uint2*>(p);
         w[0] = t.x; w[1] = t.y;
@@ -353,7 +367,8 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
                          float* s_res, RowOverride ovr = {}, PageMap pm = {}) {
   constexpr int EL = D / 16, NS = NT / 16, NW = NT / kWave, PW = 2 + D;
   // fp32 rows are twice the bytes: half the rows per batch keeps registers in budget
-  constexpr int RB = BF ? kAttendRowsPerSlot : kAttendRowsPerSlot / 2;
+  // (and D = 256 rows twice those of D = 128)
+  constexpr int RB = (BF ? kAttendRowsPerSlot : kAttendRowsPerSlot / 2) / (D > 128 ? 2 : 1);
   const int l16 = threadIdx.x & 15, slot = threadIdx.x >> 4;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
   RowRaw<D, BF> qr;
@@ -620,8 +635,8 @@ void k_decode(
   uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
   uint8_t* region = smem + kTmpWords * 4;
   // phase 1 (scan) layout
-  uint32_t* sq = reinterpret_cast<uint32_t*>(region);
-  uint32_t* shist = sq + G * W;
+  uint32_t* sq = reinterpret_cast<uint32_t*>(region);  // G query rows, then the appended key
+  uint32_t* shist = sq + (G + 1) * W;
   uint32_t* sstage = shist + G * NBP;  // one head's chunk candidates
   uint16_t* sdist = reinterpret_cast<uint16_t*>(sstage + (1 << kpad_log2));
   // phase 2 (final selection + attention) layout, aliasing phase 1
@@ -632,7 +647,7 @@ void k_decode(
   const int bsel_max = (int)min((int64_t)budget, n_ctx);
   uint32_t* scand =
       reinterpret_cast<uint32_t*>(sidx + (fuse_attend ? ((bsel_max + 3) & ~3) : 0));
-  uint32_t* s_knew = s_tmp + 24;  // ragged: the appended key's code row (W <= 8 words)
+  uint32_t* s_knew = sq + G * W;  // ragged: the appended key's code row
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id; rotating the
   // chunk index with the KV head spreads every chunk offset of the code cache
@@ -642,7 +657,6 @@ void k_decode(
   const int hkv = blockIdx.y, b = blockIdx.z;
   const int kpad = 1 << kpad_log2;
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  static_assert(W <= 8, "the appended code row lives in s_tmp[24..32)");
   // this sequence's rows and, when appending, the new token's position
   int64_t n_b = n_ctx, pos_new = -1;
   if constexpr (RAG) {
@@ -660,7 +674,7 @@ void k_decode(
   // codes, then the query's encoding while the codes are in flight
   static_assert(G <= NW, "one wavefront per query head");
   const int gq = wid < G ? wid : G - 1;  // spare wavefronts load a copy: no branch
-  const uint2 qraw =
+  const uint4 qraw =
       load_elems_raw<E, BF>(q, ((int64_t)b * Hq + (int64_t)hkv * G + gq) * D + lane * E);
   const int64_t t0 = (int64_t)c * chunk;
   // rows of the grid's chunk (the planned bound), then of this sequence
@@ -671,7 +685,7 @@ void k_decode(
     if constexpr (RAG == 2) {
       // this wavefront's stretch of the chunk and the pool page holding it
       constexpr int kUpt = D / 64;
-      const int upp_log2 = rg.page_log2 + (kUpt == 2 ? 1 : 0);
+      const int upp_log2 = rg.page_log2 + (kUpt == 4 ? 2 : kUpt == 2 ? 1 : 0);
       const int upw = chunk * kUpt / NW, w0 = wid * upw;
       const int64_t a = t0 * kUpt + w0;
       const int64_t pg = a >> upp_log2;
@@ -710,7 +724,7 @@ void k_decode(
       // s_knew and its K, V from k_new, v_new (the final workgroup may sit on
       // another XCD, whose L2 does not see these stores before the launch ends)
       const int64_t src = ((int64_t)b * Hkv + hkv) * D;
-      const uint2 kraw = load_elems_raw<E, BF>(rg.k_new, src + lane * E);
+      const uint4 kraw = load_elems_raw<E, BF>(rg.k_new, src + lane * E);
       float y[E];
       widen_elems<E, BF>(kraw, y);
       const uint32_t word = wave_encode<D>(y, rotate != 0);
@@ -843,7 +857,7 @@ __global__ __launch_bounds__(NT) void k_split_select(
     int32_t* __restrict__ idx) {
   constexpr int NW = NT / kWave, EPL = kSplitEntriesPerLane;
   __shared__ uint32_t s_tmp[kTmpWords];
-  __shared__ uint32_t s_hist[kNbinsPadded(128)];
+  __shared__ uint32_t s_hist[kNbinsPadded(256)];
   __shared__ uint32_t s_first[kSplitMaxChunks];  // first output position of the chunk's tokens
   __shared__ uint32_t s_take[kSplitMaxChunks];   // (count below t) << 16 | ties taken
   const int64_t row = blockIdx.y;
@@ -1015,7 +1029,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   // as k_decode: query, first batch of codes, then the query's encoding
   static_assert(G <= NW, "one wavefront per query head");
   const int gq = wid < G ? wid : G - 1;
-  const uint2 qraw = load_elems_raw<E, BF>(q, (row0 + gq) * D + lane * E);
+  const uint4 qraw = load_elems_raw<E, BF>(q, (row0 + gq) * D + lane * E);
   const int64_t t0 = (int64_t)c * chunk;
   const int valid = (int)min((int64_t)chunk, n_ctx - t0);
   const uint8_t* kbase = k_codes + (((int64_t)b * Hkv + hkv) * cap + t0) * (D / 4);

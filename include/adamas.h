@@ -16,7 +16,7 @@
  *    Tensors are dense, row-major, in the layouts given per call, and must be
  *    16-byte aligned.
  *  - Element types: ADAMAS_F32 (binary32) or ADAMAS_BF16 (bfloat16).
- *  - head_dim must be 64 or 128.
+ *  - head_dim must be 64, 128 or 256.
  *  - Calls enqueue work on `stream` (0 = the null stream) and return without
  *    waiting; results are visible after a stream synchronisation or event.
  *    No call synchronises the device, so calls may be captured into a graph.
@@ -33,7 +33,9 @@
  *    (7 - 2*(i%4)) .. (6 - 2*(i%4)), i.e. the first code of a byte in its top
  *    two bits.  Code values: 0 if y < -a/2, 1 if y < 0, 2 if y < a/2, else 3,
  *    with y the unnormalised Sylvester-order Hadamard transform of the vector
- *    in binary32 and a = max|y_i| over the vector.
+ *    in binary32 and a = max|y_i| over the vector's group of 128 dimensions
+ *    (the article's grouped quantization, §2.2): the whole vector at
+ *    head_dim <= 128, each half separately at head_dim 256.
  */
 #ifndef ADAMAS_H
 #define ADAMAS_H
@@ -62,7 +64,7 @@ extern "C" {
 typedef enum {
     ADAMAS_OK = 0,
     ADAMAS_ERR_INVALID = 1,     /* null/misaligned pointer, bad size or range */
-    ADAMAS_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, unknown dtype, limits */
+    ADAMAS_ERR_UNSUPPORTED = 2, /* head_dim not 64/128/256, unknown dtype, limits */
     ADAMAS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than needed */
     ADAMAS_ERR_DEVICE = 4       /* the HIP runtime reported a launch error */
 } adamas_status;

@@ -236,3 +236,11 @@ def test_paged_step_validation(lib):
     assert call(table=A + 2) == INVALID
     assert call(max_len=4097) == INVALID            # beyond max_pages * page_size
     assert call(ws=need - 1) == WORKSPACE
+
+
+def test_head_dim_256_accepted_512_not(lib):
+    assert lib.adamas_workspace_bytes(2, 1, 32, 32, 131072, 256, 256) > 0
+    assert lib.adamas_workspace_bytes(2, 1, 32, 32, 131072, 256, 512) == 0
+    assert lib.adamas_encode_keys(A, 1, 1, 1, 0, 256, A, 8, 0, None, None) == OK
+    assert lib.adamas_encode_keys(A, 1, 1, 1, 4, 512, A, 8, 0, None, None) == UNSUPPORTED
+    assert lib.adamas_decode_path(1, 32, 32, 1000, 256, 512) == -INVALID

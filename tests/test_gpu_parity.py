@@ -29,7 +29,7 @@ def _dt(name):
 
 
 # ------------------------------------------------------------------ encode
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_encode_random(ora, d, dt):
     log(f"encode random d={d} dt={dt}")
@@ -43,7 +43,7 @@ def test_encode_random(ora, d, dt):
     assert torch.equal(copy[:, :, 100:877], x) and not copy[:, :, :100].any()
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_encode_edge_values(ora, d):
     log(f"encode edge values d={d}")
     n = 64
@@ -81,7 +81,8 @@ def test_encode_query_and_large_batch(ora):
 
 # ------------------------------------------------------------------- score
 @pytest.mark.parametrize("d,hq,hkv,n", [(128, 4, 4, 9000), (64, 6, 2, 4097), (128, 24, 8, 300),
-                                        (128, 8, 1, 5000), (64, 3, 3, 1), (128, 2, 1, 255)])
+                                        (128, 8, 1, 5000), (64, 3, 3, 1), (128, 2, 1, 255),
+                                        (256, 4, 2, 5000), (256, 8, 1, 3000)])
 def test_score(ora, d, hq, hkv, n):
     log(f"score d={d} hq={hq} hkv={hkv} n={n}")
     g = torch.Generator(device=DEV).manual_seed(n + hq)
@@ -109,8 +110,18 @@ def test_select(ora, n, budget, hi):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("n,budget", [(5000, 128), (70000, 1024)])
+def test_select_d256_distances(ora, n, budget):
+    log(f"select with head_dim 256 distances (0..768) n={n} budget={budget}")
+    g = torch.Generator(device=DEV).manual_seed(n + 256)
+    dist = torch.randint(0, 769, (1, 4, n), generator=g, device=DEV,
+                         dtype=torch.int32).to(torch.uint16)
+    idx = adamas.select_topk(dist, budget, head_dim=256)
+    assert np.array_equal(idx.cpu().numpy(), ora.select_topk(dist.cpu().numpy(), budget))
+
+
 # ------------------------------------------------------------------ attend
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("budget", [1, 31, 256, 1000])
 def test_sparse_attend(ora, d, dt, budget):
