@@ -23,7 +23,8 @@ __all__ = [
     "Workspace",
     "set_decode_mode", "decode_path", "set_rotation", "stream_read", "OP_SELECT_TOPK",
     "OP_SPARSE_ATTEND", "OP_DECODE_STEP", "DECODE_AUTO", "DECODE_LAST_ARRIVAL",
-    "DECODE_GROUP_WAIT", "DECODE_SPLIT", "WS_CTRL_BYTES", "WS_STATUS_OFFSET",
+    "DECODE_GROUP_WAIT", "DECODE_SPLIT", "WS_CTRL_BYTES", "WS_STATUS_OFFSET", "ROTATE_OFF",
+    "ROTATE_F32", "ROTATE_F16",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -259,9 +260,15 @@ def stream_read(x: torch.Tensor, sink: torch.Tensor | None = None, stream=None) 
     return sink
 
 
-def set_rotation(on: bool) -> None:
-    """Process-wide: rotate vectors before bucketing (default) or not (adamas_set_rotation)."""
-    _check(load().adamas_set_rotation(1 if on else 0), "adamas_set_rotation")
+ROTATE_OFF, ROTATE_F32, ROTATE_F16 = 0, 1, 2
+
+
+def set_rotation(on) -> None:
+    """Process-wide: rotate vectors before bucketing in binary32 (True / ROTATE_F32, the
+    default), not at all (False / ROTATE_OFF) or in binary16 (ROTATE_F16)
+    (adamas_set_rotation)."""
+    mode = int(on) if not isinstance(on, bool) else (1 if on else 0)
+    _check(load().adamas_set_rotation(mode), "adamas_set_rotation")
 
 
 def set_decode_mode(mode: int) -> None:

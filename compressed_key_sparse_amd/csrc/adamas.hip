@@ -739,7 +739,7 @@ int adamas_decode_paged_step(const void* q, const void* k_new, const void* v_new
 }
 
 int adamas_set_rotation(int on) {
-  if (on != 0 && on != 1) return ADAMAS_ERR_INVALID;
+  if (on != 0 && on != 1 && on != 2) return ADAMAS_ERR_INVALID;
   g_rotation.store(on, std::memory_order_relaxed);
   return ADAMAS_OK;
 }

@@ -264,20 +264,32 @@ ADM_DEV float xor_max(float x) {
 // Packing (§3.1): four codes per byte, first code in bits 7..6; returns, on
 // the lanes with (lane % (16/E)) == 0, the little-endian 32-bit word
 // lane / (16/E) of the packed row (16 codes per word); other lanes return 0.
-// rotate == false buckets the vector as it is (no §2.1; for the ablation).
-template <int D>
-ADM_DEV uint32_t wave_encode(float (&y)[D / 64], bool rotate = true) {
+// The §2.1 butterflies over one wavefront's vector (H16: every sum and
+// difference one binary16 operation on binary16 inputs).
+template <int D, bool H16>
+ADM_DEV void wave_fwht(float (&y)[D / 64]) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & (kWave - 1);
-  if (rotate) {
+  auto add = [](float a, float b) -> float {
+    if constexpr (H16) return (float)(_Float16)((_Float16)a + (_Float16)b);
+    else return a + b;
+  };
+  auto sub = [](float a, float b) -> float {
+    if constexpr (H16) return (float)(_Float16)((_Float16)a - (_Float16)b);
+    else return a - b;
+  };
+  if constexpr (H16) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = (float)(_Float16)y[e];
+  }
 #pragma unroll
   for (int h = 1; h < E; h <<= 1) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if ((e & h) == 0) {
         float a = y[e], b = y[e + h];
-        y[e] = a + b;
-        y[e + h] = a - b;
+        y[e] = add(a, b);
+        y[e + h] = sub(a, b);
       }
     }
   }
@@ -289,7 +301,7 @@ ADM_DEV uint32_t wave_encode(float (&y)[D / 64], bool rotate = true) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const float p = lane_xor<m>(y[e]);
-      y[e] = upper ? (p - y[e]) : (y[e] + p);
+      y[e] = upper ? sub(p, y[e]) : add(y[e], p);
     }
   };
   stage(std::integral_constant<int, 1>{});
@@ -298,7 +310,20 @@ ADM_DEV uint32_t wave_encode(float (&y)[D / 64], bool rotate = true) {
   stage(std::integral_constant<int, 8>{});
   stage(std::integral_constant<int, 16>{});
   stage(std::integral_constant<int, 32>{});
-  }
+}
+
+// mode: 1 rotates in binary32; 0 buckets the vector as it is (no §2.1; for
+// the ablation); 2 rotates in binary16 (the article's FP16 advice, §6): the
+// inputs are rounded to binary16 and every sum and difference is one
+// binary16 operation, carried between lanes as the equal binary32 value.
+template <int D>
+ADM_DEV uint32_t wave_encode(float (&y)[D / 64], int mode = 1) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (mode == 1)
+    wave_fwht<D, false>(y);
+  else if (mode == 2)
+    wave_fwht<D, true>(y);
   float a = fabsf(y[0]);
 #pragma unroll
   for (int e = 1; e < E; ++e) a = fmaxf(a, fabsf(y[e]));

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
     }
     float y[E];
     load_elems<E>(x, is_bf16 != 0, src, y);
-    const uint32_t word = wave_encode<D>(y, rotate != 0);
+    const uint32_t word = wave_encode<D>(y, rotate);
     if (lane % kLanesPerWord == 0)
       reinterpret_cast<uint32_t*>(codes + row * (D / 4))[lane / kLanesPerWord] = word;
   }
@@ -727,7 +727,7 @@ void k_decode(
       const uint4 kraw = load_elems_raw<E, BF>(rg.k_new, src + lane * E);
       float y[E];
       widen_elems<E, BF>(kraw, y);
-      const uint32_t word = wave_encode<D>(y, rotate != 0);
+      const uint32_t word = wave_encode<D>(y, rotate);
       const int64_t crow =
           RAG == 2 ? pmap.row(pos_new) : ((int64_t)b * Hkv + hkv) * cap + pos_new;
       // a paged row whose table entry is out of range is scored but not stored
@@ -751,7 +751,7 @@ void k_decode(
   if (wid < G) {
     float y[E];
     widen_elems<E, BF>(qraw, y);
-    const uint32_t word = wave_encode<D>(y, rotate != 0);
+    const uint32_t word = wave_encode<D>(y, rotate);
     if (lane % kLanesPerWord == 0) sq[wid * W + lane / kLanesPerWord] = word;
   }
   lds_sync();
@@ -1040,7 +1040,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   if (wid < G) {
     float y[E];
     widen_elems<E, BF>(qraw, y);
-    const uint32_t word = wave_encode<D>(y, rotate != 0);
+    const uint32_t word = wave_encode<D>(y, rotate);
     if (lane % kLanesPerWord == 0) sq[wid * W + lane / kLanesPerWord] = word;
   }
   lds_sync();

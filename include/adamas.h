@@ -202,10 +202,16 @@ int adamas_set_decode_mode(int mode);
 
 /*
  * Process-wide switch of the §2.1 rotation for every later adamas_encode_keys
- * and decode step (1, the default: rotate; 0: bucket vectors as they are, the
- * "2-bit quantisation only" row of the article's §3.2 ablation).  Codes made
- * with one setting must only be scored against queries encoded with the same
- * one.  Returns ADAMAS_OK, or ADAMAS_ERR_INVALID unless on is 0 or 1.
+ * and decode step (1, the default: rotate in binary32; 0: bucket vectors as
+ * they are, the "2-bit quantisation only" row of the article's §3.2
+ * ablation; 2: rotate in binary16, the article's advice to keep the Hadamard
+ * transform in FP16 (§6): inputs rounded to binary16, every butterfly sum and
+ * difference one binary16 operation; values beyond 65504 overflow to
+ * infinities, so this is for inputs known to stay in range).  The distances
+ * are integers whatever the setting (the article's INT8 similarity is exact
+ * here already).  Codes made with one setting must only be scored against
+ * queries encoded with the same one.  Returns ADAMAS_OK, or
+ * ADAMAS_ERR_INVALID unless on is 0, 1 or 2.
  */
 int adamas_set_rotation(int on);
 

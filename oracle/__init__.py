@@ -74,6 +74,8 @@ def _load():
     lib.ora_encode_keys_rot.argtypes = [P, i32, i32, i32, i64, i32, P, i64, i64, i32]
     lib.ora_sparse_attend.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f64, P, P]
     lib.ora_decode_step.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, f64, P, P, P]
+    lib.ora_f64_to_f16_value.argtypes = [f64]
+    lib.ora_f64_to_f16_value.restype = ctypes.c_float
     lib.ora_f64_to_bf16.argtypes = [f64]
     lib.ora_f64_to_bf16.restype = ctypes.c_uint16
     _lib = lib
@@ -110,19 +112,25 @@ def hadamard_orthonormal_f64(x: np.ndarray) -> np.ndarray:
     return y
 
 
-def encode_vec(x: np.ndarray, rotate: bool = True):
+def encode_vec(x: np.ndarray, rotate: int = True):
     """One fp32 vector -> (packed bytes, rotated values, codes); rotate=False
-    buckets the vector as it is."""
+    buckets the vector as it is, rotate=2 rotates in binary16."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     d = x.shape[-1]
     packed = np.empty(d // 4, np.uint8)
     y = np.empty(d, np.float32)
     codes = np.empty(d, np.int32)
-    if rotate:
+    if rotate is True or rotate == 1:
         _load().ora_encode_vec_f32(_ptr(x), d, _ptr(packed), _ptr(y), _ptr(codes))
     else:
-        _load().ora_encode_vec_f32_rot(_ptr(x), d, 0, _ptr(packed), _ptr(y), _ptr(codes))
+        _load().ora_encode_vec_f32_rot(_ptr(x), d, int(rotate), _ptr(packed), _ptr(y),
+                                       _ptr(codes))
     return packed, y, codes
+
+
+def f64_to_f16_value(x: float) -> float:
+    """Correctly rounded binary64 -> binary16, as a float."""
+    return float(_load().ora_f64_to_f16_value(float(x)))
 
 
 def encode_keys(x: np.ndarray, codes: np.ndarray | None = None, cap: int | None = None,
@@ -135,11 +143,11 @@ def encode_keys(x: np.ndarray, codes: np.ndarray | None = None, cap: int | None 
     if codes is None:
         codes = np.zeros((batch, heads, cap, d // 4), np.uint8)
     assert codes.shape == (batch, heads, cap, d // 4) and codes.dtype == np.uint8
-    if rotate:
+    if rotate is True or rotate == 1:
         _load().ora_encode_keys(_ptr(x), _dtype_tag(x), batch, heads, n, d, _ptr(codes), cap, pos)
     else:
         _load().ora_encode_keys_rot(_ptr(x), _dtype_tag(x), batch, heads, n, d, _ptr(codes), cap,
-                                    pos, 0)
+                                    pos, int(rotate))
     return codes
 
 
@@ -203,10 +211,10 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,
     out = np.empty((B, Hq, d), q.dtype)
     out64 = np.empty((B, Hq, d), np.float64)
     idx = np.empty((B, Hq, budget), np.int32)
-    if not rotate:
+    if not (rotate is True or rotate == 1):
         _load().ora_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d,
-                                   cap, n_ctx, budget, n_sink, n_recent, 0, float(scale),
-                                   _ptr(out), _ptr(out64), _ptr(idx))
+                                   cap, n_ctx, budget, n_sink, n_recent, int(rotate),
+                                   float(scale), _ptr(out), _ptr(out64), _ptr(idx))
     elif n_sink == 0 and n_recent == 0:
         _load().ora_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d, cap,
                                 n_ctx, budget, float(scale), _ptr(out), _ptr(out64), _ptr(idx))

@@ -101,6 +101,47 @@ void ora_fwht_f32(float *y, int d)
     }
 }
 
+/* Correctly rounded (round-to-nearest-even) binary64 -> binary16, returned
+ * as the float of equal value (exact).  Written from the definition: 11
+ * significant bits for normal results, spacing 2^-24 below 2^-14, and any
+ * result above 65504 (the largest finite binary16) becomes an infinity. */
+float ora_f64_to_f16_value(double x)
+{
+    if (isnan(x))
+        return NAN;
+    double ax = fabs(x), r;
+    if (ax < ldexp(1.0, -14)) {
+        r = rint(ax * ldexp(1.0, 24)) * ldexp(1.0, -24);
+    } else {
+        int e;
+        double m = frexp(ax, &e);               /* ax = m * 2^e, m in [0.5, 1) */
+        r = ldexp(rint(m * 2048.0), e - 11);    /* 11 significant bits */
+    }
+    if (r > 65504.0)
+        r = INFINITY;
+    return (float)copysign(r, x);
+}
+
+/* The same transform with every value in binary16 (the article's advice to
+ * keep the Hadamard transform in FP16, §6): the inputs are rounded to
+ * binary16, and each sum and difference is formed exactly (in binary64) and
+ * rounded once to binary16. */
+void ora_fwht_f16(float *y, int d)
+{
+    for (int i = 0; i < d; i++)
+        y[i] = ora_f64_to_f16_value(y[i]);
+    for (int h = 1; h < d; h <<= 1) {
+        for (int i = 0; i < d; i++) {
+            if ((i & h) == 0) {
+                double a = y[i];
+                double b = y[i + h];
+                y[i] = ora_f64_to_f16_value(a + b);
+                y[i + h] = ora_f64_to_f16_value(a - b);
+            }
+        }
+    }
+}
+
 /* Same transform in binary64, divided by sqrt(d): the orthonormal H of §2.1.
  * Used only by tests of the rotation's invariants. */
 void ora_hadamard_orthonormal_f64(const double *x, double *y, int d)
@@ -156,7 +197,8 @@ static void ora_pack(const int *codes, int d, uint8_t *out)
 /* Rotate, bucket and pack one vector given as fp32 values.  Also returns the
  * rotated values and codes when the pointers are non-null (for tests). */
 /* rotate == 0 skips §2.1: the vector is bucketed as it is (the ablation row
- * "2-bit quantisation only" of the article's §3.2 table). */
+ * "2-bit quantisation only" of the article's §3.2 table); rotate == 2 runs
+ * the transform in binary16 (ora_fwht_f16). */
 void ora_encode_vec_f32_rot(const float *x, int d, int rotate, uint8_t *packed, float *y_out,
                             int *codes_out)
 {
@@ -164,7 +206,9 @@ void ora_encode_vec_f32_rot(const float *x, int d, int rotate, uint8_t *packed, 
     int c[ORA_MAX_D];
     for (int i = 0; i < d; i++)
         y[i] = x[i];
-    if (rotate)
+    if (rotate == 2)
+        ora_fwht_f16(y, d);
+    else if (rotate)
         ora_fwht_f32(y, d);
     const int group = d < ORA_GROUP ? d : ORA_GROUP;
     for (int g0 = 0; g0 < d; g0 += group) {

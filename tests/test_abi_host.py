@@ -184,7 +184,8 @@ def test_keep_validation(lib):
 
 
 def test_rotation_switch_validation(lib):
-    assert lib.adamas_set_rotation(2) == INVALID
+    assert lib.adamas_set_rotation(3) == INVALID
+    assert lib.adamas_set_rotation(2) == OK
     assert lib.adamas_set_rotation(-1) == INVALID
     assert lib.adamas_set_rotation(0) == OK
     assert lib.adamas_set_rotation(1) == OK

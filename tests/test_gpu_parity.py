@@ -397,6 +397,44 @@ def test_decode_without_rotation(ora, restore_rotation, restore_mode, mode):
     assert rel_err(out, oout) <= TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_encode_f16_rotation(ora, restore_rotation, d, dt):
+    adamas.set_rotation(adamas.ROTATE_F16)
+    rows = [synth.random_values((1, 2, 500, d), _dt(dt), seed=41, device=DEV, scale=4.0)]
+    # exact ties and sums that round in binary16
+    ints = synth.integer_values((1, 2, 100, d), -9, 9, seed=3)
+    rows.append(torch.from_numpy(ints.astype(np.float32) * np.float32(7.0)).to(DEV).to(_dt(dt)))
+    x = torch.cat(rows, dim=2).contiguous()
+    codes = torch.zeros((1, 2, 600, d // 4), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(x, codes)
+    torch.cuda.synchronize()
+    ref = ora.encode_keys(host(x), rotate=2)
+    assert np.array_equal(codes.cpu().numpy(), ref)
+    # and the binary16 codes do differ from the binary32 ones somewhere
+    assert not np.array_equal(ref, ora.encode_keys(host(x)))
+
+
+@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_GROUP_WAIT,
+                                  adamas.DECODE_SPLIT])
+def test_decode_f16_rotation(ora, restore_rotation, restore_mode, mode):
+    adamas.set_rotation(adamas.ROTATE_F16)
+    adamas.set_decode_mode(mode)
+    w = synth.LLAMA2_32K.replace(hq=8, hkv=4, n_ctx=20000, cap=20000, budget=256)
+    lay = synth.make_layer(w, 3, DEV)
+    codes = torch.zeros((1, 4, 20000, 32), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    idx = torch.empty((1, 8, 256), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, 20000, 256, idx_out=idx)
+    torch.cuda.synchronize()
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    ocodes = ora.encode_keys(k, rotate=2)
+    assert np.array_equal(codes.cpu().numpy(), ocodes)
+    oout, _, oidx = ora.decode_step(q, k, v, ocodes, 20000, 256, rotate=2)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert rel_err(out, oout) <= TOL[torch.bfloat16]
+
+
 def test_quality_dense_reference_matches_oracle(ora):
     # the sweep's dense reference is exact attention over every row
     from compressed_key_sparse_amd.quality import dense_attention

@@ -609,3 +609,51 @@ def test_encode_groups_are_independent(ora):
         p1, _, c1 = ora.encode_vec(x1)
         p2, _, c2 = ora.encode_vec(x2)
         assert np.array_equal(c1, c2) and bytes(p1) == bytes(p2)
+
+
+# --------------------------------------------------------------------------
+# binary16 rotation variant (the article's "Hadamard in FP16" advice)
+def test_f64_to_f16_matches_numpy(ora):
+    # numpy's double -> half conversion is an independent correctly rounded
+    # implementation: ties, subnormals, the overflow edge, signs
+    rng = np.random.default_rng(2)
+    vals = [0.0, -0.0, 1.0, 2049.0, 2051.0, 4097.0, 65504.0, 65519.99, 65520.0, 1e6,
+            2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25, 2.0 ** -14 - 2.0 ** -26, 1.0 / 3]
+    vals += list(rng.standard_normal(3000) * np.exp(rng.uniform(-18, 12, 3000)))
+    for x in vals + [-v for v in vals]:
+        got = ora.f64_to_f16_value(x)
+        want = float(np.float16(x))
+        assert got == want or (np.isinf(got) and np.isinf(want) and np.sign(got) == np.sign(want)), x
+
+
+def test_fwht_f16_exact_on_small_integers(ora):
+    # integers with |H x| <= 2048 stay exact in binary16: the binary16 rotation
+    # gives the integer transform itself, and the codes of the fp32 rotation
+    rng = np.random.default_rng(4)
+    for d in (16, 64, 128):
+        H = sylvester(d)
+        for _ in range(20):
+            x = rng.integers(-2048 // d, 2048 // d + 1, d).astype(np.float32)
+            p16, y16, c16 = ora.encode_vec(x, rotate=2)
+            p32, _, _ = ora.encode_vec(x)
+            assert np.array_equal(y16, (H @ x.astype(np.int64)).astype(np.float32))
+            assert bytes(p16) == bytes(p32)
+
+
+def test_fwht_f16_rounding_hand_worked(ora):
+    # d = 2, x = (3072, 1025), both exact binary16: the sum 4097 rounds to
+    # 4096 (spacing 4 above 4096), the difference 2047 is exact.  x = (1025,
+    # 0.5): the sum 1025.5 is a tie between 1025 and 1026 (spacing 1) and goes
+    # to the even 1026; the difference 1024.5 ties to 1024.  x = (3072.625,
+    # 1024.375) is first rounded to (3072, 1024) (spacings 2 and 1), so the
+    # rotated pair is (4096, 2048) and both code to 3 (2048 >= 4096 / 2),
+    # where the binary32 rotation gives (4097, 2048.25): codes 3 and 2.
+    _, y, _ = ora.encode_vec(np.array([3072, 1025], np.float32), rotate=2)
+    assert y.tolist() == [4096.0, 2047.0]
+    _, y, _ = ora.encode_vec(np.array([1025, 0.5], np.float32), rotate=2)
+    assert y.tolist() == [1026.0, 1024.0]
+    x = np.array([3072.625, 1024.375, 0, 0], np.float32)
+    _, y16, c16 = ora.encode_vec(x, rotate=2)
+    _, y32, c32 = ora.encode_vec(x)
+    assert y16.tolist() == [4096.0, 2048.0, 4096.0, 2048.0]
+    assert c16.tolist() == [3, 3, 3, 3] and c32.tolist() == [3, 2, 3, 2]
