@@ -95,8 +95,10 @@ int cand_slot(int budget, int chunk) {
   return k;
 }
 size_t decode_lds_scan(int D, int G, int c, int budget) {
+  const int kpad = cand_slot(budget, c);
   return (size_t)(G + 1) * (D / 16) * 4 + (size_t)G * nbins_padded(D) * 4 +
-         (size_t)cand_slot(budget, c) * 4 + (size_t)G * c * 2;
+         (size_t)stage_heads(G, kpad) * kpad * 4 + (size_t)G * c * 2 +
+         (size_t)(2 + kDecodeThreads / kWave) * G * 4;
 }
 // sel_rows = min(budget, n_ctx) indices are kept in LDS only when attention is fused.
 size_t decode_lds_final(int D, int sel_rows_lds, int mcap) {

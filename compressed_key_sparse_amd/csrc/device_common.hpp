@@ -653,6 +653,123 @@ ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t
   return (tot & 0xffffu) + (eq_all < quota ? eq_all : quota);
 }
 
+// The chunk phase for G query heads at once (G >= 2): thresholds of all
+// heads from their histograms, then the ordered selection of each head's kc
+// best tokens into its own staging row, with three workgroup barriers in all
+// (the per-head helpers above take about five per head).
+//   hist  [G][nbp] key counts     sdist [G][chunk] keys     out [G][kpad]
+// Head g keeps every token with key < t_g and the first kc - lt_g (lowest
+// index) with key == t_g, in token order, as (key << 16) | token; entries
+// past its kc are 0xFFFFFFFF.  s_thr holds 2G words, s_sums NW*G words.
+template <int NT, int NB, int G, int TPT = kCompactTpt>
+ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* sdist, int chunk,
+                                 int valid, uint32_t kc, uint32_t* out, int kpad,
+                                 uint32_t* s_thr, uint32_t* s_sums) {
+  constexpr int NW = NT / kWave, BPL = (NB + kWave - 1) / kWave;
+  static_assert(G <= NW, "one wavefront per head finds its threshold");
+  static_assert(TPT % 8 == 0 && TPT <= 32, "whole 16-byte reads, one 32-bit mask");
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  // (1) thresholds: wavefront g scans head g's histogram, BPL bins per lane
+  if (wid < G) {
+    const uint32_t* h = hist + wid * nbp;
+    uint32_t v[BPL], sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int bin = lane * BPL + j;
+      v[j] = bin < NB ? h[bin] : 0u;
+      sum += v[j];
+    }
+    const uint32_t incl = wave_scan_incl(sum), excl = incl - sum;
+    if (excl < kc && kc <= incl) {  // the lane holding the kc-th smallest key
+      uint32_t acc = excl, lt = 0;
+      int t = 0;
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {  // the bin where the count reaches kc
+        if (acc < kc && kc <= acc + v[j]) {
+          t = lane * BPL + j;
+          lt = acc;
+        }
+        acc += v[j];
+      }
+      s_thr[2 * wid] = (uint32_t)t;
+      s_thr[2 * wid + 1] = lt;
+    }
+  }
+  // zero the staging rows' tails while the thresholds settle
+  for (int i = threadIdx.x; i < G * kpad; i += NT) {
+    const int g = i / kpad, j = i - g * kpad;
+    if ((uint32_t)j >= kc) out[i] = 0xFFFFFFFFu;
+  }
+  lds_sync();
+  // (2) this thread's TPT tokens: per head, masks of keys below / at t_g,
+  // from two keys per 32-bit word with packed 16-bit subtractions (keys are
+  // below 2^15): bit 15 of (t-1-d) is set iff d >= t, of (t-d) iff d > t
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const int t0 = threadIdx.x * TPT;
+  const int nv = valid - t0;
+  constexpr uint32_t kAll = TPT == 32 ? 0xffffffffu : ((1u << TPT) - 1u);
+  const uint32_t vmask = nv >= TPT ? kAll : (nv > 0 ? ((1u << nv) - 1u) : 0u);
+  uint32_t ltm[G], eqm[G], mine[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = (int)s_thr[2 * g];
+    const s16x2 tm1 = {(short)(t - 1), (short)(t - 1)};
+    const s16x2 tt = {(short)t, (short)t};
+    uint32_t ge = 0, gt = 0;
+    if (t0 < valid) {
+#pragma unroll
+      for (int v8 = 0; v8 < TPT / 8; ++v8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(sdist + g * chunk + t0 + 8 * v8);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const s16x2 dv = __builtin_bit_cast(s16x2, ws[i]);
+          const uint32_t a = __builtin_bit_cast(uint32_t, (s16x2)(tm1 - dv));
+          const uint32_t b = __builtin_bit_cast(uint32_t, (s16x2)(tt - dv));
+          const int k = 8 * v8 + 2 * i;
+          ge |= (((a >> 15) & 1u) | ((a >> 30) & 2u)) << k;
+          gt |= (((b >> 15) & 1u) | ((b >> 30) & 2u)) << k;
+        }
+      }
+    }
+    ltm[g] = ~ge & vmask;
+    eqm[g] = ge & ~gt & vmask;
+    mine[g] = (uint32_t)__popc(ltm[g]) | ((uint32_t)__popc(eqm[g]) << 16);
+  }
+  // (3) prefix counts over the workgroup for every head with one barrier
+  uint32_t incl[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    incl[g] = wave_scan_incl(mine[g]);
+    if (lane == kWave - 1) s_sums[wid * G + g] = incl[g];
+  }
+  lds_sync();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint32_t pre = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) pre += w < wid ? s_sums[w * G + g] : 0u;
+    const uint32_t ex = pre + incl[g] - mine[g];
+    uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
+    const uint32_t quota = kc - s_thr[2 * g + 1];
+    const uint32_t t = s_thr[2 * g];
+    uint32_t* o = out + g * kpad;
+    for (uint32_t m = ltm[g] | eqm[g]; m != 0; m &= m - 1) {
+      const int i = __ffs(m) - 1;
+      const uint32_t tok = (uint32_t)(t0 + i);
+      if ((ltm[g] >> i) & 1u) {
+        const uint32_t d = sdist[g * chunk + tok];
+        o[ltb + (eqb < quota ? eqb : quota)] = (d << 16) | tok;
+        ++ltb;
+      } else {
+        if (eqb < quota) o[ltb + eqb] = (t << 16) | tok;
+        ++eqb;
+      }
+    }
+  }
+  lds_sync();
+}
+
 // chunk_collect into out[] (LDS) as (D << 16) | token; entries [kept, pad_to)
 // get the sentinel 0xFFFFFFFF.  on_kept(token, D) is called for every kept
 // token.

@@ -38,6 +38,12 @@ constexpr int kEncodeThreads = 256;
 constexpr int kScoreThreads = 256;
 constexpr int kSelectThreads = 1024;
 constexpr int kDecodeThreads = 1024;  // one workgroup of 16 wavefronts per CU
+// Grouped heads stage all G heads' chunk candidates at once when G * kpad
+// entries fit this many (chunk_compact_heads); else one head at a time.
+constexpr int kFusedStageEntries = 8192;
+ADM_HOST_DEV constexpr int stage_heads(int G, int kpad) {
+  return (G >= 2 && G * kpad <= kFusedStageEntries) ? G : 1;
+}
 // 16-byte code loads per thread in flight in the decode scans: 64 KiB per
 // workgroup per batch streams faster than 128 or 256 KiB (fewer requests
 // queued per CU at the same delivered bandwidth)
@@ -637,8 +643,10 @@ void k_decode(
   // phase 1 (scan) layout
   uint32_t* sq = reinterpret_cast<uint32_t*>(region);  // G query rows, then the appended key
   uint32_t* shist = sq + (G + 1) * W;
-  uint32_t* sstage = shist + G * NBP;  // one head's chunk candidates
-  uint16_t* sdist = reinterpret_cast<uint16_t*>(sstage + (1 << kpad_log2));
+  const int n_stage = stage_heads(G, 1 << kpad_log2);
+  uint32_t* sstage = shist + G * NBP;  // chunk candidates of n_stage heads
+  uint16_t* sdist = reinterpret_cast<uint16_t*>(sstage + n_stage * (1 << kpad_log2));
+  uint32_t* s_fused = reinterpret_cast<uint32_t*>(sdist + G * chunk);  // 2G + NW*G words
   // phase 2 (final selection + attention) layout, aliasing phase 1
   uint32_t* fhist = reinterpret_cast<uint32_t*>(region);
   float* s_part = reinterpret_cast<float*>(fhist + NBP);
@@ -781,13 +789,27 @@ void k_decode(
     }
   }
   const int kc = min(budget, valid);
-  for (int g = 0; g < G; ++g) {
-    const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-    const Threshold thr = find_threshold<NT>(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
-    chunk_compact<NT>(sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad,
-                      s_tmp, [](uint32_t, uint32_t) {});
-    lds_sync();
-    lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
+  bool staged = false;
+  if constexpr (G >= 2) {
+    if (n_stage == G) {
+      chunk_compact_heads<NT, NB, G>(shist, NBP, sdist, chunk, valid, (uint32_t)kc, sstage, kpad,
+                                     s_fused, s_fused + 2 * G);
+      for (int g = 0; g < G; ++g) {
+        const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
+        lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage + g * kpad, kpad);
+      }
+      staged = true;
+    }
+  }
+  if (!staged) {
+    for (int g = 0; g < G; ++g) {
+      const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
+      const Threshold thr = find_threshold<NT>(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
+      chunk_compact<NT>(sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad,
+                        s_tmp, [](uint32_t, uint32_t) {});
+      lds_sync();
+      lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
+    }
   }
   if (chist != nullptr) return;  // k_split_select takes it from here
   if (!arrive_last<NT>(&counters[b * Hkv + hkv], active, s_tmp)) return;
