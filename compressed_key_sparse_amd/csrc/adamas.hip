@@ -126,13 +126,23 @@ struct DecodePlan {
   bool fuse = false;
   size_t idx_off = 0;
   AttendPlan att;
-  // SPLIT schedule: per-chunk key counts [B*Hq][nbins][ncp] u16 at chist_off
+  // SPLIT schedule: per-chunk key counts [B*Hq][nbins][ncp] u16 at chist_off,
+  // attention partials [B*Hq][segs][2 + D padded to 4] f32 at spart_off
   bool split_ok = false;
   int ncp = 0, seg_chunks = 0, segs = 0;
-  size_t chist_off = 0;
+  size_t chist_off = 0, spart_off = 0;
   size_t total = 0;
 };
-constexpr int kSplitSegChunks = 32;  // chunks per k_split_select workgroup
+constexpr int kSplitSegChunks = 8;  // chunks per k_split_select workgroup
+
+// LDS of k_split_select: scratch, key counts, two per-chunk arrays, and when
+// the attention is fused the row list and the attention scratch.
+size_t split_select_lds(int D, int ncp, bool fused) {
+  const size_t nw = kSplitThreads / kWave, pw = 2 + D, pwp = (pw + 3) & ~3;
+  size_t b = (size_t)kTmpWords * 4 + (size_t)kNbinsPadded(D) * 4 + 2 * (size_t)ncp * 4;
+  if (fused) b += (size_t)kSplitFuseRows * 4 + (nw * pw + kSplitThreads / 16 + pwp) * 4;
+  return b;
+}
 
 // adamas_decode_step: 1024-thread workgroups, chunks as large as LDS allows
 // (fewer candidates to merge), attention fused into the selecting workgroup
@@ -167,9 +177,13 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D)
   p.seg_chunks = kSplitSegChunks;
   p.segs = (p.sel.n_chunks + kSplitSegChunks - 1) / kSplitSegChunks;
   p.chist_off = round_up(p.att.end, 256);
-  const size_t chist_end =
-      p.split_ok ? p.chist_off + (size_t)rows * (size_t)(3 * D + 2) * (size_t)p.ncp * 2 : p.att.end;
-  p.total = round_up(chist_end, 256);
+  size_t end = p.att.end;
+  if (p.split_ok) {
+    const size_t chist_end = p.chist_off + (size_t)rows * (size_t)(3 * D + 2) * (size_t)p.ncp * 2;
+    p.spart_off = round_up(chist_end, 256);
+    end = p.spart_off + (size_t)rows * p.segs * (size_t)((2 + D + 3) & ~3) * 4;
+  }
+  p.total = round_up(end, 256);
   return p;
 }
 
@@ -556,14 +570,33 @@ int launch_last_arrival(const DecodePlan& p, const DecodeArgs& a, int B, int hea
             : dispatch_decode<D, false>(G, p, grid, stream, a);
   });
   if (!ok) return ADAMAS_ERR_UNSUPPORTED;
+  bool attended = false;
   if (a.chist != nullptr) {
     const int bsel = (int)(a.n_ctx < a.budget ? a.n_ctx : a.budget);
     const dim3 gsel((unsigned)p.segs, (unsigned)((int64_t)B * a.Hq));
-    k_split_select<kSplitThreads><<<gsel, kSplitThreads, 0, stream>>>(
-        a.cand, a.chist, p.sel.n_chunks, p.ncp, p.seg_chunks, p.sel.kpad_log2, p.sel.chunk,
-        3 * head_dim + 2, bsel, a.budget, a.idx);
+    // attention inside the selection launch when a segment's rows fit in LDS
+    const bool fa = bsel <= kSplitFuseRows;
+    const SplitAttend sa{fa ? a.q : nullptr, a.k, a.v, a.Hq, a.Hkv, a.cap, a.qscale,
+                         reinterpret_cast<float*>(w + p.spart_off),
+                         reinterpret_cast<uint32_t*>(w + kCtrlAttend), a.out};
+    const size_t lds = split_select_lds(head_dim, p.ncp, fa);
+    with_dim(head_dim, [&](auto dc) {
+      constexpr int D = decltype(dc)::value;
+      if (bf) {
+        allow_lds(&k_split_select<D, true>, lds);
+        k_split_select<D, true><<<gsel, kSplitThreads, lds, stream>>>(
+            a.cand, a.chist, p.sel.n_chunks, p.ncp, p.seg_chunks, p.sel.kpad_log2, p.sel.chunk,
+            3 * D + 2, bsel, a.budget, a.idx, sa);
+      } else {
+        allow_lds(&k_split_select<D, false>, lds);
+        k_split_select<D, false><<<gsel, kSplitThreads, lds, stream>>>(
+            a.cand, a.chist, p.sel.n_chunks, p.ncp, p.seg_chunks, p.sel.kpad_log2, p.sel.chunk,
+            3 * D + 2, bsel, a.budget, a.idx, sa);
+      }
+    });
+    attended = fa;
   }
-  if (!p.fuse || a.chist != nullptr) {
+  if ((!p.fuse || a.chist != nullptr) && !attended) {
     const dim3 gatt((unsigned)p.att.splits, (unsigned)a.Hq, (unsigned)B);
     const PageArgs pa{a.rg.pages, a.rg.max_pages, a.rg.page_log2, a.rg.n_pages};
     launch_attend(head_dim, bf, gatt, stream, a.q, a.k, a.v, a.idx, a.Hq, a.Hkv, a.cap, a.budget,

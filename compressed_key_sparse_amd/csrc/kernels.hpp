@@ -872,16 +872,39 @@ constexpr int kSplitThreads = 1024;
 constexpr int kSplitMaxChunks = 2048;
 constexpr int kSplitEntriesPerLane = 16;  // a wavefront loads 1024 candidates at once
 
-template <int NT>
-__global__ __launch_bounds__(NT) void k_split_select(
+// With fa.q set, each workgroup also attends over the tokens it placed (its
+// segment's share of the selection, staged in LDS; at most kSplitFuseRows)
+// and publishes a partial (m, l, o); the last workgroup of the head merges
+// them by log-sum-exp and writes the output (no separate attention launch).
+// LDS (dynamic): split_select_lds(D, n_chunks, fused).
+struct SplitAttend {
+  const void* q;               // null: selection only
+  const void* k;
+  const void* v;
+  int Hq, Hkv;
+  int64_t cap;
+  float qscale;
+  float* part;                 // [B*Hq][segments][PWP] partials
+  uint32_t* counters;          // [B*Hq] arrival counters, left zero
+  void* out;
+};
+constexpr int kSplitFuseRows = 8192;
+
+template <int D, bool BF>
+__global__ __launch_bounds__(kSplitThreads) void k_split_select(
     const uint32_t* __restrict__ cand, const uint16_t* __restrict__ chist, int n_chunks, int ncp,
     int chunks_per_seg, int kpad_log2, int chunk, int nbins, int bsel, int budget,
-    int32_t* __restrict__ idx) {
-  constexpr int NW = NT / kWave, EPL = kSplitEntriesPerLane;
-  __shared__ uint32_t s_tmp[kTmpWords];
-  __shared__ uint32_t s_hist[kNbinsPadded(256)];
-  __shared__ uint32_t s_first[kSplitMaxChunks];  // first output position of the chunk's tokens
-  __shared__ uint32_t s_take[kSplitMaxChunks];   // (count below t) << 16 | ties taken
+    int32_t* __restrict__ idx, SplitAttend fa) {
+  constexpr int NT = kSplitThreads, NW = NT / kWave, EPL = kSplitEntriesPerLane;
+  constexpr int PW = 2 + D, PWP = (PW + 3) & ~3;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* s_hist = s_tmp + kTmpWords;
+  uint32_t* s_first = s_hist + kNbinsPadded(D);  // first output position of the chunk's tokens
+  uint32_t* s_take = s_first + ncp;               // (count below t) << 16 | ties taken
+  int32_t* s_rows = reinterpret_cast<int32_t*>(s_take + ncp);  // fused: this segment's tokens
+  float* s_part = reinterpret_cast<float*>(s_rows + kSplitFuseRows);
+  float* s_res = s_part + NW * PW + NT / 16;
   const int64_t row = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
   const uint16_t* h = chist + row * nbins * ncp;
@@ -954,6 +977,10 @@ __global__ __launch_bounds__(NT) void k_split_select(
   const uint32_t t = (uint32_t)thr.t;
   const int kpad = 1 << kpad_log2;
   const int c_lo = blockIdx.x * chunks_per_seg, c_hi = min(n_chunks, c_lo + chunks_per_seg);
+  // this segment's slots of the selection: [seg0, seg1)
+  const uint32_t seg0 = c_lo < n_chunks ? s_first[c_lo] : (uint32_t)bsel;
+  const uint32_t seg1 = c_hi < n_chunks ? s_first[c_hi] : (uint32_t)bsel;
+  const bool fused = fa.q != nullptr;
   for (int c = c_lo + wid; c < c_hi; c += NW) {
     const uint32_t tk = s_take[c], q = tk & 0xffffu, need = (tk >> 16) + q;
     if (need == 0) continue;
@@ -992,13 +1019,63 @@ __global__ __launch_bounds__(NT) void k_split_select(
       uint32_t o = pos + take_incl - ntake;
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
-        if ((flags >> j & 1u) && o < end) out[o++] = tok0 + (int32_t)(v[j] & 0xffffu);
+        if ((flags >> j & 1u) && o < end) {
+          const int32_t tok = tok0 + (int32_t)(v[j] & 0xffffu);
+          out[o] = tok;
+          if (fused) s_rows[o - seg0] = tok;
+          ++o;
+        }
       const uint32_t took = __builtin_amdgcn_readlane(take_incl, kWave - 1);
       ties += __builtin_amdgcn_readlane(eq_incl, kWave - 1);
       got += took;
       pos += took;
     }
   }
+  if (!fused) return;
+  // §6 over this segment's rows, then the log-sum-exp merge of the segments
+  lds_sync();
+  const int G = fa.Hq / fa.Hkv;
+  const int b = (int)(row / fa.Hq), hq = (int)(row % fa.Hq);
+  const int64_t kvrow0 = ((int64_t)b * fa.Hkv + hq / G) * fa.cap;
+  attend_rows<D, BF, NT>(fa.q, fa.k, fa.v, row * D, kvrow0, fa.cap, s_rows, (int)(seg1 - seg0),
+                         fa.qscale, s_part, s_res);
+  const int S = gridDim.x;
+  if (S == 1) {
+    if ((int)threadIdx.x < D) {
+      const float L = s_res[1];
+      store_out<BF>(fa.out, row * D + threadIdx.x, L > 0.0f ? s_res[2 + threadIdx.x] / L : 0.0f);
+    }
+    return;
+  }
+  lds_to_shared<NT>(reinterpret_cast<uint32_t*>(fa.part + (row * S + blockIdx.x) * PWP),
+                    reinterpret_cast<const uint32_t*>(s_res), PWP);
+  if (!arrive_last<NT>(&fa.counters[row], S, s_tmp)) return;
+  // merge: partials staged through LDS (the row list is free now)
+  float* s_tile = reinterpret_cast<float*>(s_rows);
+  constexpr int kTile = kSplitFuseRows / PWP;
+  const float* ps = fa.part + row * S * PWP;
+  float M = -INFINITY, L = 0.0f, O = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += kTile) {
+    const int nt = min(kTile, S - s0);
+    lds_sync();
+    shared_to_lds<NT>(reinterpret_cast<uint32_t*>(s_tile),
+                      reinterpret_cast<const uint32_t*>(ps + s0 * PWP), nt * PWP);
+    lds_sync();
+    if ((int)threadIdx.x < D) {
+      for (int i = 0; i < nt; ++i) {
+        const float mi = s_tile[i * PWP];
+        if (mi == -INFINITY) continue;
+        const float Mn = fmaxf(M, mi);
+        const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+        const float bb = exp2f(mi - Mn);
+        L = L * a + s_tile[i * PWP + 1] * bb;
+        O = O * a + s_tile[i * PWP + 2 + threadIdx.x] * bb;
+        M = Mn;
+      }
+    }
+  }
+  if ((int)threadIdx.x < D) store_out<BF>(fa.out, row * D + threadIdx.x, L > 0.0f ? O / L : 0.0f);
+  if (threadIdx.x == 0) fa.counters[row] = 0;
 }
 
 // ------------------------------------------ fused decode step, group wait
