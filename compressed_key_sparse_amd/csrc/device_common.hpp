@@ -588,6 +588,31 @@ ADM_DEV GroupThreshold find_group_threshold(uint32_t tot, uint32_t bef, int nbin
                         s_tmp[kTmpGrpTiesBefore]};
 }
 
+// Threshold masks of TPT keys held two per 32-bit word (key 2i in the low
+// half of word i, key 2i+1 in the high half; keys below 2^15): bit j of ge is
+// set iff key j >= t, of gt iff key j > t.  The packed 16-bit differences
+// (t-1-d) and (t-d) carry the answers in their sign bits; one shift and one
+// and-or move word i's two sign bits to bits 2i and 16+2i, and the two halves
+// are interleaved once at the end.
+template <int TPT>
+ADM_DEV void key_masks(const uint32_t* ws, int t, uint32_t& ge, uint32_t& gt) {
+  static_assert(TPT % 8 == 0 && TPT <= 16, "sign bits of TPT/2 words fit one 16-bit half");
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const s16x2 tm1 = {(short)(t - 1), (short)(t - 1)};
+  const s16x2 tt = {(short)t, (short)t};
+  uint32_t ga = 0, gb = 0;
+#pragma unroll
+  for (int i = 0; i < TPT / 2; ++i) {
+    const s16x2 dv = __builtin_bit_cast(s16x2, ws[i]);
+    const uint32_t a = __builtin_bit_cast(uint32_t, (s16x2)(tm1 - dv));
+    const uint32_t b = __builtin_bit_cast(uint32_t, (s16x2)(tt - dv));
+    ga |= (a >> (15 - 2 * i)) & (0x00010001u << (2 * i));
+    gb |= (b >> (15 - 2 * i)) & (0x00010001u << (2 * i));
+  }
+  ge = (ga & 0x5555u) | ((ga >> 15) & 0xAAAAu);
+  gt = (gb & 0x5555u) | ((gb >> 15) & 0xAAAAu);
+}
+
 // Ordered selection inside one chunk held in LDS.  Keeps every token with
 // D < t and the first `quota` tokens (lowest index) with D == t, and calls
 // emit(pos, token, D) for each, pos being its rank in token order among the
@@ -598,34 +623,20 @@ constexpr int kCompactTpt = 16;
 template <int NT, class Emit, int TPT = kCompactTpt>
 ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t quota,
                                uint32_t* s_tmp, Emit&& emit) {
-  static_assert(TPT % 8 == 0 && TPT <= 32, "whole 16-byte reads, one 32-bit mask");
+  static_assert(TPT % 8 == 0 && TPT <= 16, "whole 16-byte reads, one 16-bit mask");
   const int t0 = threadIdx.x * TPT;
   uint32_t ltm = 0, eqm = 0;  // bit i: token t0+i is below / at the threshold
-  uint32_t dw[TPT / 2] = {};  // the thread's distances, two per word
+  uint32_t dw[TPT / 2] = {};  // the thread's distances, two per word (all <= 3*D < 2^15)
   if (t0 < valid) {
-    // two distances per 32-bit word (both <= 3*D < 2^15): with packed 16-bit
-    // subtractions, bit 15 of (t-1-d) is set iff d >= t and of (t-d) iff d > t
-    typedef short s16x2 __attribute__((ext_vector_type(2)));
-    const s16x2 tm1 = {(short)(t - 1), (short)(t - 1)};
-    const s16x2 tt = {(short)t, (short)t};
-    uint32_t ge = 0, gt = 0;
 #pragma unroll
     for (int v8 = 0; v8 < TPT / 8; ++v8) {
       const uint4 w = *reinterpret_cast<const uint4*>(sdist + t0 + 8 * v8);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dw[4 * v8 + i] = ws[i];
-        const s16x2 dv = __builtin_bit_cast(s16x2, ws[i]);
-        const uint32_t a = __builtin_bit_cast(uint32_t, (s16x2)(tm1 - dv));
-        const uint32_t b = __builtin_bit_cast(uint32_t, (s16x2)(tt - dv));
-        const int k = 8 * v8 + 2 * i;
-        ge |= (((a >> 15) & 1u) | ((a >> 30) & 2u)) << k;
-        gt |= (((b >> 15) & 1u) | ((b >> 30) & 2u)) << k;
-      }
+      dw[4 * v8] = w.x; dw[4 * v8 + 1] = w.y; dw[4 * v8 + 2] = w.z; dw[4 * v8 + 3] = w.w;
     }
+    uint32_t ge, gt;
+    key_masks<TPT>(dw, t, ge, gt);
     const int nv = valid - t0;  // tokens of this thread inside the chunk
-    constexpr uint32_t kAll = TPT == 32 ? 0xffffffffu : ((1u << TPT) - 1u);
+    constexpr uint32_t kAll = (1u << TPT) - 1u;
     const uint32_t vmask = nv >= TPT ? kAll : ((1u << nv) - 1u);
     ltm = ~ge & vmask;
     eqm = ge & ~gt & vmask;
@@ -667,7 +678,7 @@ ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* 
                                  uint32_t* s_thr, uint32_t* s_sums) {
   constexpr int NW = NT / kWave, BPL = (NB + kWave - 1) / kWave;
   static_assert(G <= NW, "one wavefront per head finds its threshold");
-  static_assert(TPT % 8 == 0 && TPT <= 32, "whole 16-byte reads, one 32-bit mask");
+  static_assert(TPT % 8 == 0 && TPT <= 16, "whole 16-byte reads, one 16-bit mask");
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   // (1) thresholds: wavefront g scans head g's histogram, BPL bins per lane
   if (wid < G) {
@@ -701,36 +712,24 @@ ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* 
     if ((uint32_t)j >= kc) out[i] = 0xFFFFFFFFu;
   }
   lds_sync();
-  // (2) this thread's TPT tokens: per head, masks of keys below / at t_g,
-  // from two keys per 32-bit word with packed 16-bit subtractions (keys are
-  // below 2^15): bit 15 of (t-1-d) is set iff d >= t, of (t-d) iff d > t
-  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  // (2) this thread's TPT tokens: per head, masks of keys below / at t_g
   const int t0 = threadIdx.x * TPT;
   const int nv = valid - t0;
-  constexpr uint32_t kAll = TPT == 32 ? 0xffffffffu : ((1u << TPT) - 1u);
+  constexpr uint32_t kAll = (1u << TPT) - 1u;
   const uint32_t vmask = nv >= TPT ? kAll : (nv > 0 ? ((1u << nv) - 1u) : 0u);
   uint32_t ltm[G], eqm[G], mine[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int t = (int)s_thr[2 * g];
-    const s16x2 tm1 = {(short)(t - 1), (short)(t - 1)};
-    const s16x2 tt = {(short)t, (short)t};
     uint32_t ge = 0, gt = 0;
     if (t0 < valid) {
+      uint32_t ws[TPT / 2];
 #pragma unroll
       for (int v8 = 0; v8 < TPT / 8; ++v8) {
         const uint4 w = *reinterpret_cast<const uint4*>(sdist + g * chunk + t0 + 8 * v8);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const s16x2 dv = __builtin_bit_cast(s16x2, ws[i]);
-          const uint32_t a = __builtin_bit_cast(uint32_t, (s16x2)(tm1 - dv));
-          const uint32_t b = __builtin_bit_cast(uint32_t, (s16x2)(tt - dv));
-          const int k = 8 * v8 + 2 * i;
-          ge |= (((a >> 15) & 1u) | ((a >> 30) & 2u)) << k;
-          gt |= (((b >> 15) & 1u) | ((b >> 30) & 2u)) << k;
-        }
+        ws[4 * v8] = w.x; ws[4 * v8 + 1] = w.y; ws[4 * v8 + 2] = w.z; ws[4 * v8 + 3] = w.w;
       }
+      key_masks<TPT>(ws, t, ge, gt);
     }
     ltm[g] = ~ge & vmask;
     eqm[g] = ge & ~gt & vmask;
