@@ -369,6 +369,16 @@ ADM_DEV uint32_t therm_t(uint32_t w0, uint32_t w1) {
   return (w0 & 0xAAAAAAAAu) | ((w1 >> 1) & 0x55555555u);
 }
 
+// popc(x) + acc as one instruction.  Written out so that a sum of plane
+// popcounts stays a chain of accumulating counts (the compiler otherwise
+// re-associates it into separate counts joined by three-input adds, two more
+// VALU instructions per six counts in the scan's inner loop).
+ADM_DEV uint32_t popc_acc(uint32_t x, uint32_t acc) {
+  uint32_t r;
+  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(acc));
+  return r;
+}
+
 // Query-side planes for one 16-byte unit (4 words, 64 codes).
 struct QPlanes {
   uint32_t p[4];

@@ -31,6 +31,8 @@ struct KeepRange {
     hi = (int)(z < 0 ? 0 : (z > valid ? valid : z));
   }
   ADM_DEV uint32_t key(int i, uint32_t d) const { return (i < lo || i >= hi) ? 0u : d + 1u; }
+  // no token of [0, n) is always kept: every key there is d + 1
+  ADM_DEV bool keeps_none(int n) const { return lo == 0 && hi >= n; }
 };
 constexpr int kGsMergeTile = 16;  // partials merged per LDS tile (k_decode_gs)
 
@@ -171,11 +173,11 @@ ADM_DEV void scan_units(const Src& src, const uint4 (&w)[U], int base, int units
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       uint32_t s = __popc(p0 ^ qp[g].p[0]);
-      s += __popc(p1 ^ qp[g].p[1]);
-      s += __popc(p2 ^ qp[g].p[2]);
-      s += __popc(p3 ^ qp[g].p[3]);
-      s += __popc(t0 ^ qp[g].t[0]);
-      s += __popc(t1 ^ qp[g].t[1]);
+      s = popc_acc(p1 ^ qp[g].p[1], s);
+      s = popc_acc(p2 ^ qp[g].p[2], s);
+      s = popc_acc(p3 ^ qp[g].p[3], s);
+      s = popc_acc(t0 ^ qp[g].t[0], s);
+      s = popc_acc(t1 ^ qp[g].t[1], s);
       if constexpr (kUnitsPerToken == 2) s += swap_pair(s);
       if constexpr (kUnitsPerToken == 4) {  // a quad of lanes holds one token
         s += lane_xor_u32<1>(s);
@@ -766,11 +768,18 @@ void k_decode(
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
   const KeepRange keep(t0, valid, n_sink, n_b - n_recent);
-  scan_chunk<D, G, NT, kDecodeScanDepth>(src, valid_mem, qp, [&](int g, int tok, uint32_t d) {
-    const uint32_t key = keep.key(tok, d);
+  const auto sink = [&](int g, int tok, uint32_t key) {
     sdist[g * chunk + tok] = (uint16_t)key;
     atomicAdd(&shist[g * NBP + key], 1u);
-  }, &first);
+  };
+  // a chunk without always-kept tokens (the common case) skips the range test
+  if (keep.keeps_none(valid_mem))
+    scan_chunk<D, G, NT, kDecodeScanDepth>(
+        src, valid_mem, qp, [&](int g, int tok, uint32_t d) { sink(g, tok, d + 1u); }, &first);
+  else
+    scan_chunk<D, G, NT, kDecodeScanDepth>(
+        src, valid_mem, qp, [&](int g, int tok, uint32_t d) { sink(g, tok, keep.key(tok, d)); },
+        &first);
   if constexpr (RAG) {
     if (has_new && (int)threadIdx.x < G) {
       const int g = threadIdx.x, tok = valid_mem;
@@ -1146,11 +1155,17 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
   const KeepRange keep(t0, valid, n_sink, n_ctx - n_recent);
-  scan_chunk<D, G, NT, kDecodeScanDepth>(src, valid, qp, [&](int g, int tok, uint32_t d) {
-    const uint32_t key = keep.key(tok, d);
+  const auto sink = [&](int g, int tok, uint32_t key) {
     sdist[g * chunk + tok] = (uint16_t)key;
     atomicAdd(&shist[g * NBP + key], 1u);
-  }, &first);
+  };
+  if (keep.keeps_none(valid))
+    scan_chunk<D, G, NT, kDecodeScanDepth>(
+        src, valid, qp, [&](int g, int tok, uint32_t d) { sink(g, tok, d + 1u); }, &first);
+  else
+    scan_chunk<D, G, NT, kDecodeScanDepth>(
+        src, valid, qp, [&](int g, int tok, uint32_t d) { sink(g, tok, keep.key(tok, d)); },
+        &first);
   lds_sync();
 
   // publish this chunk's histograms as u16 rows (counts <= chunk < 2^16)
