@@ -415,9 +415,12 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
       if (tok[j] < 0) sc[j] = -INFINITY;
       mloc = fmaxf(mloc, sc[j]);
     }
-    // the wavefront's maximum over its 4 slots (lanes ^16, ^32)
+    // the wavefront's maximum over its 4 slots (lanes ^16, ^32).  No early
+    // exit for a batch with nothing valid: the update below leaves the state
+    // unchanged then (weights 0, correction 1 or 0 on an empty state), and a
+    // branch here would let the compiler sink the V loads behind the wait for
+    // K, a second memory round trip
     const float mb = xor_max<32>(xor_max<16>(mloc));
-    if (mb == -INFINITY) continue;  // nothing valid for this wavefront (uniform in it)
     const float mn = fmaxf(m_run, mb);
     const float corr = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - mn);
     l_run *= corr;
