@@ -126,7 +126,7 @@ struct DecodePlan {
   bool fuse = false;
   size_t idx_off = 0;
   AttendPlan att;
-  // SPLIT schedule: per-chunk key counts [B*Hq][nbins][ncp] u16 at chist_off,
+  // SPLIT schedule: per-chunk key counts [B*Hq][ncp][kNbinsHist(D)] u16 at chist_off,
   // attention partials [B*Hq][segs][2 + D padded to 4] f32 at spart_off
   bool split_ok = false;
   int ncp = 0, seg_chunks = 0, segs = 0;
@@ -179,7 +179,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D)
   p.chist_off = round_up(p.att.end, 256);
   size_t end = p.att.end;
   if (p.split_ok) {
-    const size_t chist_end = p.chist_off + (size_t)rows * (size_t)(3 * D + 2) * (size_t)p.ncp * 2;
+    const size_t chist_end = p.chist_off + (size_t)rows * (size_t)p.ncp * kNbinsHist(D) * 2;
     p.spart_off = round_up(chist_end, 256);
     end = p.spart_off + (size_t)rows * p.segs * (size_t)((2 + D + 3) & ~3) * 4;
   }

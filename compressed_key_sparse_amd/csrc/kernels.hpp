@@ -793,11 +793,22 @@ void k_decode(
   }
   lds_sync();
   if (chist != nullptr) {
-    // separate selection (k_split_select): this chunk's key counts per head
-    for (int i = threadIdx.x; i < G * NB; i += NT) {
-      const int g = i / NB, kb = i - g * NB;
+    // separate selection (k_split_select): this chunk's key counts per head,
+    // one row of kNbinsHist(D) u16 per (head, chunk), 8 counts per store
+    constexpr int CR = kNbinsHist(D), CQ = CR / 8;
+    for (int i = threadIdx.x; i < G * CQ; i += NT) {
+      const int g = i / CQ, b0 = (i - g * CQ) * 8;
       const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-      chist[(row * NB + kb) * ncp + c] = (uint16_t)shist[g * NBP + kb];
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int kb = b0 + 2 * k;
+        const uint32_t lo = kb < NB ? shist[g * NBP + kb] : 0u;
+        const uint32_t hi = kb + 1 < NB ? shist[g * NBP + kb + 1] : 0u;
+        w[k] = lo | (hi << 16);
+      }
+      reinterpret_cast<uint4*>(chist + (row * ncp + c) * CR)[b0 / 8] =
+          make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
   const int kc = min(budget, valid);
@@ -878,11 +889,13 @@ void k_decode(
 // the kept tokens of the segment's chunks there, one chunk at a time.  Ties
 // at t go to the lowest token indices: chunks are in token order, and each
 // chunk's candidates are too.
-//   chist [B*Hq][nbins][ncp] u16, ncp >= n_chunks a multiple of 8
+//   chist [B*Hq][ncp][kNbinsHist(D)] u16 (a row of key counts per chunk),
+//         ncp >= n_chunks
 //   cand  [B*Hq][n_chunks][kpad] as k_decode leaves it (token order, 0xFFFFFFFF unused)
 constexpr int kSplitThreads = 1024;
 constexpr int kSplitMaxChunks = 2048;
 constexpr int kSplitEntriesPerLane = 16;  // a wavefront loads 1024 candidates at once
+constexpr int kSplitRegChunks = 4;  // count rows a wavefront holds in registers (fast path)
 
 // With fa.q set, each workgroup also attends over the tokens it placed (its
 // segment's share of the selection, staged in LDS; at most kSplitFuseRows)
@@ -919,43 +932,101 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
   float* s_res = s_part + NW * PW + NT / 16;
   const int64_t row = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-  const uint16_t* h = chist + row * nbins * ncp;
+  constexpr int CR = kNbinsHist(D), CQ = CR / 8;
+  const uint16_t* h = chist + row * ncp * CR;
   for (int i = threadIdx.x; i < nbins; i += NT) s_hist[i] = 0;
   for (int i = threadIdx.x; i < n_chunks; i += NT) s_first[i] = 0;
   lds_sync();
-  {  // the head's counts: P threads per key, each over every P-th group of 8 chunks
-    const int P = max(1, NT / nbins), g8 = (n_chunks + 7) / 8;
-    for (int it = threadIdx.x; it < nbins * P; it += NT) {
-      const int kb = it / P, p = it - kb * P;
-      const uint4* src = reinterpret_cast<const uint4*>(h + (int64_t)kb * ncp);
-      uint32_t sum = 0;
-      for (int j = p; j < g8; j += P) {
-        const uint4 w = src[j];
-        const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-        const int rem = n_chunks - 8 * j;  // counts past the last chunk are not written
+  Threshold thr;
+  if (CQ <= kWave && n_chunks <= kSplitRegChunks * NW) {
+    // every count in registers after one round of loads: wavefront w holds
+    // the rows of chunks w, w + NW, ..., lane l their keys 8l..8l+7
+    uint4 e[kSplitRegChunks];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          sum += (2 * u < rem ? (x[u] & 0xffffu) : 0u) + (2 * u + 1 < rem ? (x[u] >> 16) : 0u);
+    for (int k = 0; k < kSplitRegChunks; ++k) {
+      const int c = wid + NW * k;
+      e[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (c < n_chunks && lane < CQ) e[k] = reinterpret_cast<const uint4*>(h + (int64_t)c * CR)[lane];
+    }
+    // count u (0..7) of a row slice: half u & 1 of word u >> 1
+    const auto count = [](const uint4& x, int u) {
+      const int wi = u >> 1;
+      const uint32_t w = wi < 2 ? (wi == 0 ? x.x : x.y) : (wi == 2 ? x.z : x.w);
+      return (w >> (16 * (u & 1))) & 0xffffu;
+    };
+    if (lane < CQ) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {  // this lane's key 8l+u summed over its chunks
+        uint32_t sum = 0;
+#pragma unroll
+        for (int k = 0; k < kSplitRegChunks; ++k) sum += count(e[k], u);
+        if (sum && lane * 8 + u < nbins) atomicAdd(&s_hist[lane * 8 + u], sum);
       }
-      if (sum) atomicAdd(&s_hist[kb], sum);
     }
-  }
-  lds_sync();
-  const Threshold thr = find_threshold<NT>(s_hist, nbins, (uint32_t)bsel, s_tmp);
-  const uint32_t quota = (uint32_t)bsel - thr.lt;
-  {  // per chunk: keys below t (P2 threads per chunk, every P2-th key) and ties at t
-    const int P2 = max(1, NT / n_chunks);
-    for (int it = threadIdx.x; it < n_chunks * P2; it += NT) {
-      const int c = it % n_chunks, p = it / n_chunks;
-      uint32_t sum = 0;
+    lds_sync();
+    thr = find_threshold<NT>(s_hist, nbins, (uint32_t)bsel, s_tmp);
+    // per chunk: keys below t and ties at t, one wavefront sum each
+#pragma unroll
+    for (int k = 0; k < kSplitRegChunks; ++k) {
+      const int c = wid + NW * k;
+      if (c >= n_chunks) break;  // uniform in the wavefront
+      uint32_t lt = 0, eq = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int kb = lane * 8 + u;
+        const uint32_t n = count(e[k], u);
+        lt += kb < thr.t ? n : 0u;
+        eq += kb == thr.t ? n : 0u;
+      }
+      lt = __builtin_amdgcn_readlane(wave_scan_incl(lt), kWave - 1);
+      eq = __builtin_amdgcn_readlane(wave_scan_incl(eq), kWave - 1);
+      if (lane == 0) {
+        s_first[c] = lt;
+        s_take[c] = eq;
+      }
+    }
+  } else {
+    {  // the head's counts: P threads per key, each over every P-th chunk
+      const int P = max(1, NT / nbins);
+      for (int it = threadIdx.x; it < nbins * P; it += NT) {
+        const int kb = it / P, p = it - kb * P;
+        uint32_t sum = 0;
+        for (int c = p; c < n_chunks; c += P) sum += h[(int64_t)c * CR + kb];
+        if (sum) atomicAdd(&s_hist[kb], sum);
+      }
+    }
+    lds_sync();
+    thr = find_threshold<NT>(s_hist, nbins, (uint32_t)bsel, s_tmp);
+    {  // per chunk: keys below t (P2 threads per chunk, every P2-th key) and ties at t
+      const int P2 = max(1, NT / n_chunks);
+      for (int it = threadIdx.x; it < n_chunks * P2; it += NT) {
+        const int c = it % n_chunks, p = it / n_chunks;
+        const uint16_t* hc = h + (int64_t)c * CR;
+        uint32_t sum = 0;
 #pragma unroll 4
-      for (int kb = p; kb < thr.t; kb += P2) sum += h[(int64_t)kb * ncp + c];
-      if (sum) atomicAdd(&s_first[c], sum);
-      if (p == 0) s_take[c] = h[(int64_t)thr.t * ncp + c];
+        for (int kb = p; kb < thr.t; kb += P2) sum += hc[kb];
+        if (sum) atomicAdd(&s_first[c], sum);
+        if (p == 0) s_take[c] = hc[thr.t];
+      }
     }
   }
+  const uint32_t quota = (uint32_t)bsel - thr.lt;
   lds_sync();
-  {  // prefix sums over chunks: where each chunk's tokens start, and its share of ties
+  if (n_chunks <= kWave) {
+    // prefix sums over chunks in one wavefront: where each chunk's tokens
+    // start, and its share of the ties (the same arithmetic as below)
+    if (wid == 0) {
+      const int c = lane;
+      const uint32_t lt = c < n_chunks ? s_first[c] : 0u, eq = c < n_chunks ? s_take[c] : 0u;
+      const uint32_t lt_ex = wave_scan_incl(lt) - lt, eq_ex = wave_scan_incl(eq) - eq;
+      const uint32_t before = eq_ex < quota ? eq_ex : quota;
+      const uint32_t q = min(eq, quota - before);
+      if (c < n_chunks) {
+        s_first[c] = lt_ex + before;
+        s_take[c] = (lt << 16) | q;
+      }
+    }
+  } else {  // prefix sums over chunks: where each chunk's tokens start, and its share of ties
     const int tpt = (n_chunks + NT - 1) / NT, c0 = threadIdx.x * tpt;
     uint32_t lts = 0, eqs = 0;
     for (int j = 0; j < tpt; ++j)

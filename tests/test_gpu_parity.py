@@ -269,7 +269,23 @@ def restore_mode():
                                   adamas.DECODE_SPLIT])
 @pytest.mark.parametrize("case", sorted(_SCHED_CASES))
 def test_decode_schedules(ora, restore_mode, mode, case):
-    w = _SCHED_CASES[case]
+    _check_schedule(ora, _SCHED_CASES[case], mode, case)
+
+
+# split schedule only: more chunks (74 of 4096 tokens) than the selection
+# kernel's register path takes, so its general count passes run at d = 128
+_SPLIT_CASES = {
+    "gqa-16-2-300000-b512": synth.LLAMA32_GQA_1M.replace(hq=16, hkv=2, n_ctx=300000,
+                                                         cap=300000, budget=512),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_SPLIT_CASES))
+def test_decode_split_many_chunks(ora, restore_mode, case):
+    _check_schedule(ora, _SPLIT_CASES[case], adamas.DECODE_SPLIT, case)
+
+
+def _check_schedule(ora, w, mode, case):
     log(f"decode schedule {mode} {case}")
     adamas.set_decode_mode(mode)
     assert adamas.decode_path(w.batch, w.hq, w.hkv, w.n_ctx, w.budget, w.head_dim) == mode
