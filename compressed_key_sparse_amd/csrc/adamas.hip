@@ -466,8 +466,9 @@ int adamas_encode_keys(const void* x, int dtype, int batch, int heads, int64_t n
   if (x_copy_dst != nullptr && !aligned16(x_copy_dst)) return ADAMAS_ERR_INVALID;
   if (n == 0) return ADAMAS_OK;
   const int64_t nvec = (int64_t)batch * heads * n;
-  const int64_t blocks64 = (nvec + 3) / 4;
-  const unsigned blocks = (unsigned)(blocks64 < 16384 ? blocks64 : 16384);
+  const int64_t slots = kEncodeThreads / 16;  // one vector per 16-lane slot
+  const int64_t blocks64 = (nvec + slots - 1) / slots;
+  const unsigned blocks = (unsigned)(blocks64 < 8192 ? blocks64 : 8192);
   const int bf = dtype == ADAMAS_BF16;
   with_dim(head_dim, [&](auto dc) {
     k_encode<decltype(dc)::value><<<blocks, kEncodeThreads, 0, stream>>>(

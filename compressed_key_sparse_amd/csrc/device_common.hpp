@@ -312,6 +312,52 @@ ADM_DEV void wave_fwht(float (&y)[D / 64]) {
   stage(std::integral_constant<int, 32>{});
 }
 
+// The same butterflies over one vector held by a 16-lane slot of the
+// wavefront, lane l16 holding the EL = D/16 consecutive dimensions
+// [l16*EL, l16*EL + EL): the stages below EL pair registers of one lane, the
+// stages EL, 2EL, 4EL and 8EL pair lanes l16 and l16 + h/EL inside the slot's
+// 16-lane row.  Stage order and every operation are those of wave_fwht.
+template <int D, bool H16>
+ADM_DEV void slot_fwht(float (&y)[D / 16], int l16) {
+  constexpr int EL = D / 16;
+  auto add = [](float a, float b) -> float {
+    if constexpr (H16) return (float)(_Float16)((_Float16)a + (_Float16)b);
+    else return a + b;
+  };
+  auto sub = [](float a, float b) -> float {
+    if constexpr (H16) return (float)(_Float16)((_Float16)a - (_Float16)b);
+    else return a - b;
+  };
+  if constexpr (H16) {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) y[e] = (float)(_Float16)y[e];
+  }
+#pragma unroll
+  for (int h = 1; h < EL; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      if ((e & h) == 0) {
+        const float a = y[e], b = y[e + h];
+        y[e] = add(a, b);
+        y[e + h] = sub(a, b);
+      }
+    }
+  }
+  auto stage = [&](auto mtag) {
+    constexpr int m = decltype(mtag)::value;
+    const bool upper = (l16 & m) != 0;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const float p = lane_xor<m>(y[e]);
+      y[e] = upper ? sub(p, y[e]) : add(y[e], p);
+    }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
+}
+
 // mode: 1 rotates in binary32; 0 buckets the vector as it is (no §2.1; for
 // the ablation); 2 rotates in binary16 (the article's FP16 advice, §6): the
 // inputs are rounded to binary16 and every sum and difference is one

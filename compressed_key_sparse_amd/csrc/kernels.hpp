@@ -63,42 +63,78 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
                                                            uint8_t* __restrict__ codes,
                                                            int64_t cap, int64_t pos,
                                                            void* __restrict__ copy, int rotate) {
-  constexpr int E = D / 64;
-  constexpr int kLanesPerWord = 16 / E;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t nwaves = (int64_t)gridDim.x * (kEncodeThreads / kWave);
-  for (int64_t v = ((int64_t)blockIdx.x * kEncodeThreads + threadIdx.x) / kWave; v < nvec;
-       v += nwaves) {
+  // a 16-lane slot per vector: lane l holds dimensions [l*EL, l*EL + EL), so
+  // the butterflies of distance below EL stay in registers and the others
+  // (EL, 2EL, 4EL, 8EL) are DPP exchanges inside the slot's row of 16 lanes;
+  // each lane moves 16 bytes or more of the vector per access
+  constexpr int EL = D / 16, SLOTS = kEncodeThreads / 16;
+  constexpr int kGroupLanes = (D > 128 ? 128 : D) / EL;  // lanes of one absmax group
+  const int l16 = threadIdx.x & 15;
+  const int64_t nslots = (int64_t)gridDim.x * SLOTS;
+  for (int64_t v = (int64_t)blockIdx.x * SLOTS + (threadIdx.x >> 4); v < nvec; v += nslots) {
     const int64_t bh = v / n;
     const int64_t row = bh * cap + pos + (v - bh * n);
-    const int64_t src = v * D + lane * E;
-    if (copy != nullptr) {
-      const int64_t dst = row * D + lane * E;
-      if (is_bf16) {
-        if constexpr (E == 4)
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(copy) + dst) =
-              *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + src);
-        else if constexpr (E == 2)
-          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(copy) + dst) =
-              *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + src);
-        else
-          static_cast<uint16_t*>(copy)[dst] = static_cast<const uint16_t*>(x)[src];
+    const int64_t src = v * D + l16 * EL;
+    float y[EL];
+    if (is_bf16) {
+      constexpr int NB = EL * 2;  // bytes per lane
+      const uint8_t* s8 = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(x) + src);
+      uint32_t w[EL / 2];
+      if constexpr (NB == 8) {
+        const uint2 t = *reinterpret_cast<const uint2*>(s8);
+        w[0] = t.x; w[1] = t.y;
+        if (copy != nullptr)
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(copy) + row * D + l16 * EL) = t;
       } else {
-        if constexpr (E == 4)
-          *reinterpret_cast<uint4*>(static_cast<float*>(copy) + dst) =
-              *reinterpret_cast<const uint4*>(static_cast<const float*>(x) + src);
-        else if constexpr (E == 2)
-          *reinterpret_cast<uint2*>(static_cast<float*>(copy) + dst) =
-              *reinterpret_cast<const uint2*>(static_cast<const float*>(x) + src);
-        else
-          static_cast<float*>(copy)[dst] = static_cast<const float*>(x)[src];
+#pragma unroll
+        for (int k = 0; k < NB / 16; ++k) {
+          const uint4 t = reinterpret_cast<const uint4*>(s8)[k];
+          w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
+          if (copy != nullptr)
+            reinterpret_cast<uint4*>(static_cast<uint16_t*>(copy) + row * D + l16 * EL)[k] = t;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EL; ++e)
+        y[e] = (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : bf16_to_f32(w[e >> 1] & 0xffffu);
+    } else {
+      const uint4* s4 = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + src);
+#pragma unroll
+      for (int k = 0; k < EL / 4; ++k) {
+        const uint4 t = s4[k];
+        y[4 * k] = __uint_as_float(t.x); y[4 * k + 1] = __uint_as_float(t.y);
+        y[4 * k + 2] = __uint_as_float(t.z); y[4 * k + 3] = __uint_as_float(t.w);
+        if (copy != nullptr)
+          reinterpret_cast<uint4*>(static_cast<float*>(copy) + row * D + l16 * EL)[k] = t;
       }
     }
-    float y[E];
-    load_elems<E>(x, is_bf16 != 0, src, y);
-    const uint32_t word = wave_encode<D>(y, rotate);
-    if (lane % kLanesPerWord == 0)
-      reinterpret_cast<uint32_t*>(codes + row * (D / 4))[lane / kLanesPerWord] = word;
+    if (rotate == 1)
+      slot_fwht<D, false>(y, l16);
+    else if (rotate == 2)
+      slot_fwht<D, true>(y, l16);
+    // §2.2: absmax of the vector's 128-dimension group, codes at -a/2, 0, a/2
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) a = fmaxf(a, fabsf(y[e]));
+    a = fmaxf(a, lane_xor<1>(a));
+    a = fmaxf(a, lane_xor<2>(a));
+    if constexpr (kGroupLanes >= 8) a = fmaxf(a, lane_xor<4>(a));
+    if constexpr (kGroupLanes >= 16) a = fmaxf(a, lane_xor<8>(a));
+    const float t0 = -0.5f * a, t2 = 0.5f * a;
+    // §3.1: 4 codes per byte, first code in the high bits; 16 dimensions per word
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const float val = y[e];
+      const uint32_t c = (val < t0) ? 0u : (val < 0.0f) ? 1u : (val < t2) ? 2u : 3u;
+      const int i = (l16 * EL + e) & 15;  // dimension index within its word
+      bits |= c << (8 * (i >> 2) + 6 - 2 * (i & 3));
+    }
+    constexpr int kLanesPerWord = 16 / EL;
+    if constexpr (kLanesPerWord >= 2) bits |= lane_xor_u32<1>(bits);
+    if constexpr (kLanesPerWord >= 4) bits |= lane_xor_u32<2>(bits);
+    if (l16 % kLanesPerWord == 0)
+      reinterpret_cast<uint32_t*>(codes + row * (D / 4))[l16 / kLanesPerWord] = bits;
   }
 }
 
