@@ -812,7 +812,9 @@ void k_decode(
     atomicAdd(&shist[g * NBP + key], 1u);
   };
   // a chunk without always-kept tokens (the common case) skips the range test
-  if (keep.keeps_none(valid_mem))
+  // (not in the paged two-per-CU build, where the second copy of the scan
+  // costs spills under its 64-register cap)
+  if (!(OCC && RAG == 2) && keep.keeps_none(valid_mem))
     scan_chunk<D, G, NT, kDecodeScanDepth>(
         src, valid_mem, qp, [&](int g, int tok, uint32_t d) { sink(g, tok, d + 1u); }, &first);
   else
