@@ -146,7 +146,7 @@ def main():
         summarize(args.summarize)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path is single-GPU by design: no collectives).", file=sys.stderr)
         sys.exit(2)
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -612,7 +612,7 @@ def test_encode_groups_are_independent(ora):
 
 
 # --------------------------------------------------------------------------
-# binary16 rotation variant (the article's "Hadamard in FP16" advice)
+# binary16 rotation variant (the article advises computing the rotation in FP16, §6)
 def test_f64_to_f16_matches_numpy(ora):
     # numpy's double -> half conversion is an independent correctly rounded
     # implementation: ties, subnormals, the overflow edge, signs
