@@ -78,7 +78,7 @@ uint16_t ora_f64_to_bf16(double x)
  * §2.1 -- fast Walsh-Hadamard transform, unnormalised, Sylvester order.
  *
  * H is built by the recursion H_1 = [1], H_{2m} = [[H_m, H_m], [H_m, -H_m]]
- * (the article's "recursive construction"), so H[i][j] = (-1)^popcount(i&j).
+ * (the article builds H recursively), so H[i][j] = (-1)^popcount(i&j).
  * The divide-and-conquer form applies log2(d) butterfly stages; stage h pairs
  * element i (bit h clear) with element i+h and replaces them by their sum and
  * difference.  Stages run h = 1, 2, 4, ..., d/2; each result is one binary32
