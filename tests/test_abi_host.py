@@ -245,3 +245,19 @@ def test_head_dim_256_accepted_512_not(lib):
     assert lib.adamas_encode_keys(A, 1, 1, 1, 0, 256, A, 8, 0, None, None) == OK
     assert lib.adamas_encode_keys(A, 1, 1, 1, 4, 512, A, 8, 0, None, None) == UNSUPPORTED
     assert lib.adamas_decode_path(1, 32, 32, 1000, 256, 512) == -INVALID
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU: --gpus N > 1 and a multi-rank launch
+    exit with a message before any GPU work."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ)
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+    env["WORLD_SIZE"] = "2"
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py")],
+                       capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 2 and "single-GPU" in r.stderr
