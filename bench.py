@@ -447,84 +447,118 @@ def bench_gqa(args, dev):
          "decode_path": adamas.decode_path(B, Hq, Hkv, n, bud, d)}, cpu)
 
 
+class BatchAppendState:
+    """The batch-16 append workload as the benchmark runs it: 16 sequences of
+    65536 rows, each holding n - 1 rows so that the step appends row n - 1 and
+    attends over n; one decode launch per step on stream s1 while a
+    4096-token chunk for sequence (step mod 16) is encoded and its K rows
+    copied into the reserved tail rows [65536, 69632) on stream s2.  With
+    paged=True the same rows sit in a shuffled pool of 1024-token pages and
+    the chunk fills four spare pool pages.  The parity tests build the same
+    state and check the same calls."""
+
+    PAGE = 1024
+
+    def __init__(self, w, dev, bud, paged=False):
+        import numpy as np
+        import torch
+
+        import compressed_key_sparse_amd as adamas
+        import synth
+        self.w, self.dev, self.bud, self.paged = w, dev, bud, paged
+        B, Hkv, d, n = w.batch, w.hkv, w.head_dim, w.n_ctx
+        lay = synth.make_layer(w, 0, dev)
+        codes = torch.empty((B, Hkv, w.cap, d // 4), dtype=torch.uint8, device=dev)
+        for b in range(B):
+            adamas.encode_keys(lay["k"][b:b + 1], codes[b:b + 1])
+        P = self.PAGE
+        self.q = lay["q"]
+        if paged:
+            per = n // P
+            n_pages = B * per + 4
+            perm = np.random.default_rng(5).permutation(n_pages)
+            self.table = torch.from_numpy(perm[:B * per].reshape(B, per).astype(np.int32)).to(dev)
+            self.spare = [int(x) for x in perm[B * per:]]
+            self.kp = torch.empty((n_pages, Hkv, P, d), dtype=w.torch_dtype, device=dev)
+            self.vp = torch.empty_like(self.kp)
+            self.cp = torch.empty((n_pages, Hkv, P, d // 4), dtype=torch.uint8, device=dev)
+            for b in range(B):
+                for i in range(per):
+                    pg = int(perm[b * per + i])
+                    self.kp[pg] = lay["k"][b, :, i * P:(i + 1) * P]
+                    self.vp[pg] = lay["v"][b, :, i * P:(i + 1) * P]
+                    self.cp[pg] = codes[b, :, i * P:(i + 1) * P]
+            del lay, codes
+            torch.cuda.empty_cache()
+        else:
+            self.k, self.v, self.codes = lay["k"], lay["v"], codes
+        self.lens = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
+        self.kn = synth.random_values((B, Hkv, d), w.torch_dtype, 77, device=dev)
+        self.vn = synth.random_values((B, Hkv, d), w.torch_dtype, 78, device=dev)
+        self.chunks = [synth.make_chunk(w, s, dev) for s in range(4)]
+        self.out = torch.empty_like(self.q)
+        torch.cuda.synchronize()
+        self.s1, self.s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+        self.ws = adamas.Workspace(dev)
+        self.ws.get(adamas.workspace_bytes(adamas.OP_DECODE_STEP, B, w.hq, Hkv, n, bud, d))
+
+    def decode(self, idx_out=None):
+        import compressed_key_sparse_amd as adamas
+        n = self.w.n_ctx
+        if self.paged:
+            adamas.decode_paged_step(self.q, self.kp, self.vp, self.cp, self.table, self.lens, n,
+                                     self.bud, k_new=self.kn, v_new=self.vn, out=self.out,
+                                     idx_out=idx_out, ws=self.ws, stream=self.s1)
+        else:
+            adamas.decode_append_step(self.q, self.k, self.v, self.codes, self.lens, n, self.bud,
+                                      k_new=self.kn, v_new=self.vn, out=self.out,
+                                      idx_out=idx_out, ws=self.ws, stream=self.s1)
+
+    def encode_chunk(self, i):
+        """Enqueue step i's prefill chunk on s2 (its sequence is i mod 16)."""
+        import torch
+
+        import compressed_key_sparse_amd as adamas
+        b, n, P = i % self.w.batch, self.w.n_ctx, self.PAGE
+        with torch.cuda.stream(self.s2):
+            ch = self.chunks[i % len(self.chunks)]
+            if self.paged:   # the chunk's four pages, one encode call each
+                for j, pg in enumerate(self.spare):
+                    adamas.encode_keys(ch[:, :, j * P:(j + 1) * P].contiguous(),
+                                       self.cp[pg:pg + 1], x_copy=self.kp[pg:pg + 1],
+                                       stream=self.s2)
+            else:
+                adamas.encode_keys(ch, self.codes[b:b + 1], pos=n, x_copy=self.k[b:b + 1],
+                                   stream=self.s2)
+
+    def step(self, i, timed=None, idx_out=None):
+        self.s2.wait_stream(self.s1)
+        self.encode_chunk(i)
+        if timed is not None:
+            timed[0].record(self.s1)
+        self.decode(idx_out)
+        if timed is not None:
+            timed[1].record(self.s1)
+        self.s1.wait_stream(self.s2)
+
+
 def bench_batch_append(args, dev):
     """16 sequences of 65536 rows: each step appends one token per sequence
     and decodes (one launch on stream 1) while a 4096-token chunk for sequence
     (step mod 16) is encoded and its K rows copied into the reserved tail rows
-    [65536, 69632) on stream 2.  Timed eagerly (the chunk's sequence changes
-    every step): step = both streams done."""
+    [65536, 69632) on stream 2 (BatchAppendState).  Timed eagerly (the
+    chunk's sequence changes every step): step = both streams done."""
     import numpy as np
     import torch
 
-    import compressed_key_sparse_amd as adamas
     import synth
     w = synth.BATCH16_64K
     B, Hq, Hkv, d, n = w.batch, w.hq, w.hkv, w.head_dim, w.n_ctx
     bud = w.budget if args.budget == 256 else args.budget
     print(f"[bench] setup: batch {B} x {Hq} heads x {n} rows, budget {bud}, append", file=sys.stderr,
           flush=True)
-    lay = synth.make_layer(w, 0, dev)
-    codes = torch.empty((B, Hkv, w.cap, d // 4), dtype=torch.uint8, device=dev)
-    for b in range(B):
-        adamas.encode_keys(lay["k"][b:b + 1], codes[b:b + 1])
-    P = 1024
-    if args.paged:
-        # the same rows moved into a shuffled pool of pages (+4 for the chunk)
-        per = n // P
-        n_pages = B * per + 4
-        perm = np.random.default_rng(5).permutation(n_pages)
-        table = torch.from_numpy(perm[:B * per].reshape(B, per).astype(np.int32)).to(dev)
-        spare = [int(x) for x in perm[B * per:]]
-        kp = torch.empty((n_pages, Hkv, P, d), dtype=w.torch_dtype, device=dev)
-        vp = torch.empty_like(kp)
-        cp = torch.empty((n_pages, Hkv, P, d // 4), dtype=torch.uint8, device=dev)
-        for b in range(B):
-            for i in range(per):
-                pg = int(perm[b * per + i])
-                kp[pg] = lay["k"][b, :, i * P:(i + 1) * P]
-                vp[pg] = lay["v"][b, :, i * P:(i + 1) * P]
-                cp[pg] = codes[b, :, i * P:(i + 1) * P]
-        del lay["k"], lay["v"], codes
-        torch.cuda.empty_cache()
-    # every sequence holds n - 1 rows; the step appends row n - 1 and attends n
-    lens = torch.full((B,), n - 1, dtype=torch.int32, device=dev)
-    kn = synth.random_values((B, Hkv, d), w.torch_dtype, 77, device=dev)
-    vn = synth.random_values((B, Hkv, d), w.torch_dtype, 78, device=dev)
-    chunks = [synth.make_chunk(w, s, dev) for s in range(4)]
-    out = torch.empty_like(lay["q"])
-    torch.cuda.synchronize()
-    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
-    ws = adamas.Workspace(dev)
-    ws.get(adamas.workspace_bytes(adamas.OP_DECODE_STEP, B, Hq, Hkv, n, bud, d))
-    ev = {}
-
-    def decode():
-        if args.paged:
-            adamas.decode_paged_step(lay["q"], kp, vp, cp, table, lens, n, bud, k_new=kn,
-                                     v_new=vn, out=out, ws=ws, stream=s1)
-        else:
-            adamas.decode_append_step(lay["q"], lay["k"], lay["v"], codes, lens, n, bud, k_new=kn,
-                                      v_new=vn, out=out, ws=ws, stream=s1)
-
-    def step(i, timed=None):
-        b = i % B
-        s2.wait_stream(s1)
-        with torch.cuda.stream(s2):
-            ch = chunks[i % len(chunks)]
-            if args.paged:   # the chunk's four pages, one encode call each
-                for j, pg in enumerate(spare):
-                    adamas.encode_keys(ch[:, :, j * P:(j + 1) * P].contiguous(),
-                                       cp[pg:pg + 1], x_copy=kp[pg:pg + 1], stream=s2)
-            else:
-                adamas.encode_keys(ch, codes[b:b + 1], pos=n, x_copy=lay["k"][b:b + 1],
-                                   stream=s2)
-        if timed is not None:
-            timed[0].record(s1)
-        decode()
-        if timed is not None:
-            timed[1].record(s1)
-        s1.wait_stream(s2)
-
+    st = BatchAppendState(w, dev, bud, paged=args.paged)
+    s1, step, decode = st.s1, st.step, st.decode
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -547,7 +581,7 @@ def bench_batch_append(args, dev):
     chunk_bytes = Hkv * w.chunk * (2 * d * 2 + d // 4)   # read K, copy K, write codes
     cpu = None
     if args.cpu_seconds > 0 and not args.paged:
-        cpu = cpu_baseline_append(lay, codes, lens, kn, vn, w, n, bud, args.cpu_seconds)
+        cpu = cpu_baseline_append(st, w, n, bud, args.cpu_seconds)
     result_line(
         f"batched decode+append tokens/s + achieved HBM GB/s, 16 x 64K ctx, budget {bud}, 1 GPU",
         w, B, ms, K, args.warmup,
@@ -566,7 +600,7 @@ def bench_batch_append(args, dev):
          "decode_alone_gbs": round(per_launch / (alone_us * 1e-6) / 1e9, 1)}, cpu)
 
 
-def cpu_baseline_append(lay, codes, lens, kn, vn, w, n, bud, seconds):
+def cpu_baseline_append(st, w, n, bud, seconds):
     """The oracle's append step on single sequences of the batch (cycled) until
     about `seconds` of oracle time; scaled to the 16-sequence step."""
     import numpy as np
@@ -578,10 +612,10 @@ def cpu_baseline_append(lay, codes, lens, kn, vn, w, n, bud, seconds):
     staged = []
     for b in (0, 5, 10):
         sl = slice(b, b + 1)
-        k = synth.to_numpy_bits(lay["k"][sl, :, :n])
-        staged.append((synth.to_numpy_bits(lay["q"][sl]), k, synth.to_numpy_bits(lay["v"][sl, :, :n]),
-                       oracle.encode_keys(k), synth.to_numpy_bits(kn[sl]),
-                       synth.to_numpy_bits(vn[sl])))
+        k = synth.to_numpy_bits(st.k[sl, :, :n])
+        staged.append((synth.to_numpy_bits(st.q[sl]), k, synth.to_numpy_bits(st.v[sl, :, :n]),
+                       oracle.encode_keys(k), synth.to_numpy_bits(st.kn[sl]),
+                       synth.to_numpy_bits(st.vn[sl])))
     spent, done = 0.0, 0
     while spent < seconds or done == 0:
         q, k, v, c, a, bvals = staged[done % len(staged)]

@@ -24,7 +24,8 @@ __all__ = [
     "set_decode_mode", "decode_path", "set_rotation", "stream_read", "OP_SELECT_TOPK",
     "OP_SPARSE_ATTEND", "OP_DECODE_STEP", "DECODE_AUTO", "DECODE_LAST_ARRIVAL",
     "DECODE_GROUP_WAIT", "DECODE_SPLIT", "WS_CTRL_BYTES", "WS_STATUS_OFFSET", "ROTATE_OFF",
-    "ROTATE_F32", "ROTATE_F16",
+    "ROTATE_F32", "ROTATE_F16", "GroupWaitGaveUp", "set_wait_polls", "wait_polls",
+    "DEFAULT_WAIT_POLLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +37,7 @@ OP_SELECT_TOPK, OP_SPARSE_ATTEND, OP_DECODE_STEP = 0, 1, 2
 WS_CTRL_BYTES = 65792          # ADAMAS_WS_CTRL_BYTES
 WS_STATUS_OFFSET = 65536       # ADAMAS_WS_STATUS_OFFSET
 DECODE_AUTO, DECODE_LAST_ARRIVAL, DECODE_GROUP_WAIT, DECODE_SPLIT = 0, 1, 2, 3
+DEFAULT_WAIT_POLLS = 1 << 20   # the library's initial group-wait bound
 
 _lib = None
 
@@ -45,6 +47,11 @@ class AdamasError(RuntimeError):
         self.status = status
         msg = load().adamas_status_string(status).decode() if _lib is not None else str(status)
         super().__init__(f"{what}: {msg} (status {status})")
+
+
+class GroupWaitGaveUp(RuntimeError):
+    """A group-wait decode step gave up waiting (workspace status word set):
+    the outputs of that call are invalid."""
 
 
 def library_path() -> str:
@@ -90,6 +97,10 @@ def load():
     lib.adamas_set_rotation.argtypes = [i32]
     lib.adamas_set_rotation.restype = i32
     lib.adamas_decode_path.argtypes = [i32, i32, i32, i64, i32, i32]
+    lib.adamas_set_wait_polls.argtypes = [ctypes.c_uint32]
+    lib.adamas_set_wait_polls.restype = i32
+    lib.adamas_wait_polls.argtypes = []
+    lib.adamas_wait_polls.restype = ctypes.c_uint32
     for fn in ("adamas_set_decode_mode", "adamas_decode_path"):
         getattr(lib, fn).restype = i32
     for fn in ("adamas_encode_keys", "adamas_score", "adamas_select_topk", "adamas_sparse_attend",
@@ -151,6 +162,39 @@ class Workspace:
             self.buf = torch.zeros(max(nbytes, WS_CTRL_BYTES), dtype=torch.uint8,
                                    device=self.device)
         return self.buf
+
+    def status(self) -> int:
+        """The workspace status word (ADAMAS_WS_STATUS_OFFSET), read after the work
+        enqueued so far on the current stream: nonzero once a group wait gave up
+        (that call's outputs are invalid).  The library never clears it."""
+        if self.buf.numel() < WS_CTRL_BYTES:
+            return 0
+        word = self.buf[WS_STATUS_OFFSET:WS_STATUS_OFFSET + 4]
+        return int(word.view(torch.int32).item())
+
+    def reset_status(self) -> None:
+        """Re-arm the status word (enqueued on the current stream)."""
+        if self.buf.numel() >= WS_CTRL_BYTES:
+            self.buf[WS_STATUS_OFFSET:WS_STATUS_OFFSET + 4].zero_()
+
+    def check(self) -> None:
+        """Raise GroupWaitGaveUp (and re-arm the word) if a call on this
+        workspace gave up a group wait since the last check."""
+        st = self.status()
+        if st != 0:
+            self.reset_status()
+            raise GroupWaitGaveUp(
+                f"a group-wait decode step gave up waiting (status word {st:#x}); "
+                "outputs since the last check are invalid")
+
+    def control_bytes_clear(self) -> bool:
+        """True when the arrival counters (the control bytes other than the
+        status word) are all zero, as every completed call leaves them."""
+        if self.buf.numel() < WS_CTRL_BYTES:
+            return True
+        ctrl = self.buf[:WS_CTRL_BYTES].clone()
+        ctrl[WS_STATUS_OFFSET:WS_STATUS_OFFSET + 4] = 0
+        return bool((ctrl == 0).all().item())
 
 
 _default_ws: dict = {}
@@ -271,6 +315,19 @@ def set_rotation(on) -> None:
     _check(load().adamas_set_rotation(mode), "adamas_set_rotation")
 
 
+def set_wait_polls(polls: int) -> None:
+    """Process-wide bound of each group wait, in polls (adamas_set_wait_polls);
+    DEFAULT_WAIT_POLLS restores the library's default."""
+    if not 0 <= int(polls) < 2 ** 32:
+        raise ValueError("polls must fit an unsigned 32-bit integer")
+    _check(load().adamas_set_wait_polls(int(polls)), "adamas_set_wait_polls")
+
+
+def wait_polls() -> int:
+    """The current group-wait bound (adamas_wait_polls)."""
+    return int(load().adamas_wait_polls())
+
+
 def set_decode_mode(mode: int) -> None:
     """Process-wide schedule of decode_step: DECODE_AUTO, DECODE_LAST_ARRIVAL,
     DECODE_GROUP_WAIT or DECODE_SPLIT (adamas_set_decode_mode)."""
@@ -287,9 +344,12 @@ def decode_path(B: int, Hq: int, Hkv: int, n_ctx: int, budget: int, head_dim: in
 
 def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0, out=None,
                 idx_out=None, ws: Workspace | None = None, stream=None, n_sink: int = 0,
-                n_recent: int = 0) -> torch.Tensor:
+                n_recent: int = 0, check: bool = False) -> torch.Tensor:
     """One fused decode step of one layer -> out [B][Hq][d] (idx_out optional).
-    The first n_sink and last n_recent tokens are always kept (adamas_decode_step_keep)."""
+    The first n_sink and last n_recent tokens are always kept (adamas_decode_step_keep).
+    With check=True the call waits for the step and raises GroupWaitGaveUp if a
+    group wait gave up (Workspace.check); otherwise the caller checks the
+    workspace when it synchronises."""
     B, Hq, d = q.shape
     _, Hkv, cap, _ = k.shape
     if k.dtype != q.dtype or v.dtype != q.dtype or tuple(v.shape) != tuple(k.shape):
@@ -309,6 +369,9 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0, o
     else:
         st = load().adamas_decode_step_keep(*head, int(n_sink), int(n_recent), *tail)
     _check(st, "adamas_decode_step")
+    if check:
+        (stream if stream is not None else torch.cuda.current_stream(q.device)).synchronize()
+        _ws_for(q.device, ws).check()
     return out
 
 

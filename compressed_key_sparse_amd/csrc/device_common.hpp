@@ -125,9 +125,11 @@ ADM_DEV void widen_elems(uint4 raw, float (&out)[E]) {
 // lists, attention partials) is written and read with device-scope coherent
 // accesses (the sc1 cache policy): they are coherent across the XCDs'
 // separate L2 caches by themselves, so the hand-off needs no L2 write-back or
-// invalidation; the writer only waits for its stores to complete before
-// counting its arrival.  Whole 16-byte rows are moved through buffer
-// instructions (a 4-byte coherent store costs a full line of write traffic).
+// invalidation.  Every wavefront of the writer waits for its own stores to be
+// acknowledged (wait_vmem, below) before the workgroup barrier that precedes
+// the arrival count, so the count is never visible before the data it
+// announces.  Whole 16-byte rows are moved through buffer instructions (a
+// 4-byte coherent store costs a full line of write traffic).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCachePolicyCoherent = 16;       // sc1: device-scope coherence
 constexpr int kBufferDword3 = 0x00020000;      // raw 32-bit buffer (GFX9 layout)
@@ -991,13 +993,25 @@ ADM_DEV void final_select_tiled(const uint32_t* cand, int M, int kpad_log2, int 
   lds_sync();
 }
 
-// Count this workgroup's arrival after its store_shared writes completed;
-// returns true on the last of n_arrivals workgroups, whose load_shared reads
-// then see every earlier workgroup's writes.  Each thread waits for its own
-// stores (workgroup-scope release), the barrier orders the whole workgroup
-// before the count, and the count itself is a device-scope atomic.
+// Wait until every vector memory access this wavefront has issued is
+// complete; on gfx9-family targets stores count in vmcnt too, and a
+// device-scope (sc1) store completes once it is written through to the level
+// every XCD reads.  s_waitcnt immediate: vmcnt[3:0] in bits 3:0, expcnt in
+// 6:4, lgkmcnt in 11:8, vmcnt[5:4] in 15:14; expcnt and lgkmcnt are left at
+// their maxima (not waited for).  A workgroup-scope release fence does not
+// wait for vmcnt on this target (all of a workgroup's wavefronts share one
+// compute unit), so the hand-offs below wait explicitly.
+constexpr int kWaitVmcnt0 = 0x0F70;
+ADM_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); }
+
+// Count this workgroup's arrival after its coherent (sc1) hand-off stores
+// completed; returns true on the last of n_arrivals workgroups, whose
+// coherent loads then see every earlier workgroup's writes.  Every wavefront
+// waits for its own stores (wait_vmem), the barrier orders the whole
+// workgroup before the count, and the count itself is a device-scope atomic.
 template <int NT>
 ADM_DEV bool arrive_last(uint32_t* counter, int n_arrivals, uint32_t* s_tmp) {
+  wait_vmem();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1013,26 +1027,32 @@ ADM_DEV bool arrive_last(uint32_t* counter, int n_arrivals, uint32_t* s_tmp) {
 // n_arrivals workgroups of the group have arrived.  Only for launches whose
 // workgroups are all resident on the device together (the caller checks the
 // grid against the device), so every awaited workgroup is running.  The wait
-// is bounded: past kGroupWaitPolls polls it gives up and sets *status to 1,
-// and the results of that launch are invalid.
-constexpr uint32_t kGroupWaitPolls = 1u << 20;
+// is bounded: after max_polls polls it gives up, sets *status to 1 and
+// returns false (on every thread of the workgroup); the caller must then not
+// use the group's data (it may be incomplete) and still run to its end, so
+// that every counter is left zero; that launch's results are invalid.
+// Returns true when all n_arrivals workgroups have arrived.
 template <int NT>
-ADM_DEV void arrive_and_wait(uint32_t* counter, int n_arrivals, uint32_t* status) {
+ADM_DEV bool arrive_and_wait(uint32_t* counter, int n_arrivals, uint32_t* status,
+                             uint32_t max_polls, uint32_t* s_tmp) {
+  wait_vmem();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t seen =
         __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     for (uint32_t polls = 0; seen < (uint32_t)n_arrivals; ++polls) {
-      if (polls == kGroupWaitPolls) {
+      if (polls >= max_polls) {
         __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
       seen = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    s_tmp[kTmpFlag] = seen >= (uint32_t)n_arrivals ? 1u : 0u;
   }
   __syncthreads();
+  return s_tmp[kTmpFlag] != 0;
 }
 
 }  // namespace adm

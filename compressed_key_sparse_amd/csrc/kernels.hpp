@@ -1219,8 +1219,8 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
     int n_chunks, int budget, int cmax, float qscale, uint16_t* __restrict__ ghist,
     float* __restrict__ part, uint32_t* __restrict__ arrive_hist,
-    uint32_t* __restrict__ arrive_part, uint32_t* __restrict__ status, int32_t* __restrict__ idx,
-    void* __restrict__ out, int n_sink, int n_recent, int rotate) {
+    uint32_t* __restrict__ arrive_part, uint32_t* __restrict__ status, uint32_t max_polls,
+    int32_t* __restrict__ idx, void* __restrict__ out, int n_sink, int n_recent, int rotate) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), NBH = kNbinsHist(D), W = D / 16;
   static_assert(G <= kTmpWords - kTmpGroupCounts, "per-head counts live in s_tmp");
@@ -1292,12 +1292,17 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     uint16_t* dst = ghist + ((row0 + g) * n_chunks + c) * NBH;
     store_shared_x4(make_rsrc(dst, NBH * 2), (uint32_t)b0 * 2u, u32x4{w[0], w[1], w[2], w[3]});
   }
-  arrive_and_wait<NT>(&arrive_hist[grp], n_chunks, status);
+  // a wait that gave up leaves the group's histograms possibly incomplete:
+  // this workgroup then keeps no rows (and writes no indices), publishes an
+  // empty partial and runs to its end, so the counters are still reset
+  const bool complete = arrive_and_wait<NT>(&arrive_hist[grp], n_chunks, status, max_polls,
+                                            s_tmp);
 
   // group thresholds; this chunk's share of each query head's selection
   const int bsel = (int)min((int64_t)budget, n_ctx);
   uint32_t* s_cnt = s_tmp + kTmpGroupCounts;  // rows kept per query head
-  for (int g = 0; g < G; ++g) {
+  if (!complete && (int)threadIdx.x < G) s_cnt[threadIdx.x] = 0;
+  for (int g = 0; g < (complete ? G : 0); ++g) {
     const int64_t row = row0 + g;
     // the group's histograms: one 16-byte row segment (8 bins of one chunk)
     // per thread, summed into LDS
@@ -1392,7 +1397,9 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
 // in flight, non-temporal) and writes the XOR of what it read, so the reads
 // cannot be dropped.
 constexpr int kStreamThreads = 1024;
-__global__ __launch_bounds__(kStreamThreads) void k_stream_read(const uint4* __restrict__ src,
+// (internal linkage: every translation unit that includes this header gets
+// its own copy; only the library's entry point launches it)
+static __global__ __launch_bounds__(kStreamThreads) void k_stream_read(const uint4* __restrict__ src,
                                                                 int64_t units, int64_t per_block,
                                                                 uint32_t* __restrict__ sink) {
   constexpr int U = kDecodeScanDepth;

@@ -57,8 +57,11 @@ extern "C" {
 
 /* Byte offset in a workspace of a u32 status word.  A decode step that ran
  * with group waits (ADAMAS_DECODE_GROUP_WAIT) and found a wait exceeding its
- * bound sets it to a nonzero value; that call's outputs are then invalid.
- * The library never clears it. */
+ * bound (adamas_set_wait_polls) sets it to a nonzero value; that call's
+ * outputs are then invalid, while its control bytes are still left zero, so
+ * the workspace stays usable.  The library never clears the word: a caller
+ * that may run group waits reads it after synchronising the stream (the
+ * Python binding's Workspace.status()) and writes zero to re-arm it. */
 #define ADAMAS_WS_STATUS_OFFSET 65536
 
 typedef enum {
@@ -201,6 +204,22 @@ int adamas_decode_step(const void *q, const void *k, const void *v,
 int adamas_set_decode_mode(int mode);
 
 /*
+ * Process-wide bound on each group wait of the ADAMAS_DECODE_GROUP_WAIT
+ * schedule, in polls of the arrival counter (each poll sleeps about 64
+ * cycles first).  A workgroup still waiting after `polls` polls gives up,
+ * sets the workspace status word (ADAMAS_WS_STATUS_OFFSET) and runs to its
+ * end with incomplete data: that call's outputs are invalid, and nothing
+ * hangs.  The default, 1 << 20 polls, is far above any wait of a launch
+ * whose workgroups are all resident; a small value (0 gives up at once)
+ * forces the give-up path, e.g. to test a caller's status check.  Affects
+ * launches enqueued after the call.  Returns ADAMAS_OK.
+ */
+int adamas_set_wait_polls(uint32_t polls);
+
+/* The current group-wait bound (adamas_set_wait_polls). */
+uint32_t adamas_wait_polls(void);
+
+/*
  * Process-wide switch of the §2.1 rotation for every later adamas_encode_keys
  * and decode step (1, the default: rotate in binary32; 0: bucket vectors as
  * they are, the "2-bit quantisation only" row of the article's §3.2
@@ -299,7 +318,11 @@ int adamas_decode_append_step(const void *q, const void *k_new, const void *v_ne
  *          batch 1, heads Hkv, cap page_size fills it, x_copy_dst the K page)
  *   page_table [B][max_pages] int32 device memory: pool page of logical page
  *          i of sequence b, i.e. of its tokens [i*page_size, (i+1)*page_size).
- *          Entries for pages a sequence does not reach are not read.
+ *          Every entry of a row up to the pages max_len spans may be read
+ *          (the scan issues its first loads before it knows a sequence's
+ *          length); entries a sequence does not reach only have to be
+ *          readable, their values are clamped into [0, n_pages) and the rows
+ *          they map are not used.
  *   page_size  a power of two in [1024, 16384].
  *   max_len    <= max_pages * page_size (the logical capacity).
  * Token t of sequence b, KV head h, is pool row

@@ -377,13 +377,17 @@ void ora_select_topk(const uint16_t *dist, int B, int Hq, int64_t n_ctx,
 /* §6 -- exact softmax attention over the selected rows only, in binary64.
  * s_j = scale * q . k_j; p = softmax(s); o = sum_j p_j v_j, using the
  * original (unrotated) q, K, V: by §2.1 the rotation leaves q.k unchanged.
- * scale == 0 means 1/sqrt(d) (reading: the usual attention scale).  Entries of idx below 0 are skipped; a row with
- * no valid entry yields zeros.  Writes o in binary64 to out64 (if non-null)
- * and rounded to the element type to out. */
-void ora_sparse_attend(const void *q, const void *k, const void *v, int dtype,
-                       const int32_t *idx, int B, int Hq, int Hkv, int d,
-                       int64_t cap, int budget, double scale, void *out,
-                       double *out64)
+ * scale == 0 means 1/sqrt(d) (reading: the usual attention scale).  Entries
+ * of idx below 0 are skipped; a row with no valid entry yields zeros.  Writes
+ * o in binary64 to out64 (if non-null) and rounded to the element type to
+ * out.  absmass64 (if non-null) receives, per output element, the sum of
+ * the magnitudes of its terms, sum_j p_j |v_j,i| (binary64): the scale that
+ * rounding errors in a floating-point evaluation of o_i are proportional to
+ * (tests bound a GPU result's error by it; it does not enter o). */
+void ora_sparse_attend_ex(const void *q, const void *k, const void *v, int dtype,
+                          const int32_t *idx, int B, int Hq, int Hkv, int d,
+                          int64_t cap, int budget, double scale, void *out,
+                          double *out64, double *absmass64)
 {
     int G = Hq / Hkv;
     if (scale == 0.0)
@@ -411,8 +415,11 @@ void ora_sparse_attend(const void *q, const void *k, const void *v, int dtype,
                     m = s[j];
                 any = 1;
             }
-            for (int i = 0; i < d; i++)
+            double am[ORA_MAX_D];
+            for (int i = 0; i < d; i++) {
                 o[i] = 0.0;
+                am[i] = 0.0;
+            }
             double l = 0.0;
             if (any) {
                 for (int j = 0; j < budget; j++) {
@@ -421,13 +428,20 @@ void ora_sparse_attend(const void *q, const void *k, const void *v, int dtype,
                     double p = exp(s[j] - m);
                     l += p;
                     int64_t row = (kvbase + sel[j]) * d;
-                    for (int i = 0; i < d; i++)
-                        o[i] += p * (double)ora_widen(v, dtype, row + i);
+                    for (int i = 0; i < d; i++) {
+                        double vi = (double)ora_widen(v, dtype, row + i);
+                        o[i] += p * vi;
+                        am[i] += p * fabs(vi);
+                    }
                 }
-                for (int i = 0; i < d; i++)
+                for (int i = 0; i < d; i++) {
                     o[i] /= l;
+                    am[i] /= l;
+                }
             }
             for (int i = 0; i < d; i++) {
+                if (absmass64)
+                    absmass64[r * d + i] = am[i];
                 if (out64)
                     out64[r * d + i] = o[i];
                 if (dtype == ORA_F32)
@@ -437,6 +451,15 @@ void ora_sparse_attend(const void *q, const void *k, const void *v, int dtype,
             }
             free(s);
         }
+}
+
+void ora_sparse_attend(const void *q, const void *k, const void *v, int dtype,
+                       const int32_t *idx, int B, int Hq, int Hkv, int d,
+                       int64_t cap, int budget, double scale, void *out,
+                       double *out64)
+{
+    ora_sparse_attend_ex(q, k, v, dtype, idx, B, Hq, Hkv, d, cap, budget, scale, out,
+                         out64, 0);
 }
 
 /* One decode step for one layer: encode each query head (§2.1-§3.1), score

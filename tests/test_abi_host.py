@@ -261,3 +261,19 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py")],
                        capture_output=True, text=True, env=env, timeout=120)
     assert r.returncode == 2 and "single-GPU" in r.stderr
+
+
+def test_wait_polls_setter(lib):
+    """The group-wait bound is process-wide and round-trips; the binding
+    restores the default."""
+    lib.adamas_set_wait_polls.argtypes = [ctypes.c_uint32]
+    lib.adamas_wait_polls.restype = ctypes.c_uint32
+    assert lib.adamas_wait_polls() == adamas.DEFAULT_WAIT_POLLS
+    assert lib.adamas_set_wait_polls(0) == OK
+    assert lib.adamas_wait_polls() == 0
+    adamas.set_wait_polls(12345)
+    assert adamas.wait_polls() == 12345
+    with pytest.raises(ValueError):
+        adamas.set_wait_polls(-1)
+    adamas.set_wait_polls(adamas.DEFAULT_WAIT_POLLS)
+    assert adamas.wait_polls() == adamas.DEFAULT_WAIT_POLLS

@@ -8,7 +8,7 @@ import torch
 
 import compressed_key_sparse_amd as adamas
 import synth
-from gpu_helpers import TOL, host, log, rel_err
+from gpu_helpers import check_out, check_out_paged, host, log
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -57,11 +57,9 @@ def test_decode_d256(ora, restore_mode, mode, case):
                              idx_out=idx, ws=ws)
     torch.cuda.synchronize()
     assert not ws.buf[:adamas.WS_CTRL_BYTES].any()
-    oout, _, oidx = ora.decode_step(q, k, v, oc, w.n_ctx, w.budget)
+    oout, o64, oidx = ora.decode_step(q, k, v, oc, w.n_ctx, w.budget)
     assert np.array_equal(idx.cpu().numpy(), oidx), "selection differs"
-    e = rel_err(out, oout)
-    log(f"  path {path} rel err {e:.3e}")
-    assert e <= TOL[w.torch_dtype]
+    check_out(ora, out, q, k, v, oidx, oout, o64, f"path {path}")
 
 
 def test_append_d256(ora):
@@ -82,11 +80,11 @@ def test_append_d256(ora):
                                     torch.tensor(lens, dtype=torch.int32, device=DEV), 5000, 128,
                                     k_new=kn, v_new=vn, idx_out=idx)
     torch.cuda.synchronize()
-    oout, _, oidx, ok, ov, ocd = ora.decode_append_step(q, k, v, oc, np.array(lens), 5000, 128,
-                                                        host(kn), host(vn))
+    oout, o64, oidx, ok, ov, ocd = ora.decode_append_step(q, k, v, oc, np.array(lens), 5000,
+                                                          128, host(kn), host(vn))
     assert np.array_equal(codes.cpu().numpy(), ocd) and np.array_equal(host(lay["k"]), ok)
     assert np.array_equal(idx.cpu().numpy(), oidx)
-    assert rel_err(out, oout) <= TOL[torch.bfloat16]
+    check_out(ora, out, q, ok, ov, oidx, oout, o64, "append d256")
     assert (idx[0, 0].cpu().numpy() == 4999).any()      # the near-query key is kept
 
 
@@ -117,9 +115,9 @@ def test_paged_d256(ora):
                                    torch.tensor(lens, dtype=torch.int32, device=DEV), per * P,
                                    256, k_new=kn, v_new=vn, idx_out=idx)
     torch.cuda.synchronize()
-    oout, _, oidx, okp, ovp, ocp = ora.decode_paged_step(host(lay["q"]), kp_h, vp_h, cp_h, table,
-                                                         np.array(lens), per * P, 256, host(kn),
-                                                         host(vn))
+    oout, o64, oidx, okp, ovp, ocp = ora.decode_paged_step(host(lay["q"]), kp_h, vp_h, cp_h,
+                                                           table, np.array(lens), per * P, 256,
+                                                           host(kn), host(vn))
     assert np.array_equal(host(kp), okp) and np.array_equal(cp.cpu().numpy(), ocp)
     assert np.array_equal(idx.cpu().numpy(), oidx)
-    assert rel_err(out, oout) <= TOL[torch.bfloat16]
+    check_out_paged(ora, out, host(lay["q"]), okp, ovp, table, oidx, oout, o64, "paged d256")

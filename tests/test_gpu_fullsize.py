@@ -13,7 +13,7 @@ import torch
 
 import compressed_key_sparse_amd as adamas
 import synth
-from gpu_helpers import TOL, host, log, rel_err
+from gpu_helpers import check_out, host, log
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -42,11 +42,9 @@ def _check(ora, w, lay, codes, idx, out, budget, batch_rows=None):
     q, k, v = (host(lay[x][sl]) for x in ("q", "k", "v"))
     ocodes = ora.encode_keys(k)
     assert np.array_equal(codes[sl].cpu().numpy(), ocodes), "code cache differs"
-    oout, _, oidx = ora.decode_step(q, k, v, ocodes, w.n_ctx, budget)
+    oout, o64, oidx = ora.decode_step(q, k, v, ocodes, w.n_ctx, budget)
     assert np.array_equal(idx[sl].cpu().numpy(), oidx), "selection differs"
-    e = rel_err(out[sl], oout)
-    log(f"  {w.name} budget {budget}: indices exact, rel err {e:.3e}")
-    assert e <= TOL[w.torch_dtype]
+    check_out(ora, out[sl], q, k, v, oidx, oout, o64, f"{w.name} budget {budget}")
 
 
 def test_llama2_32k_full(ora):
@@ -61,6 +59,22 @@ def test_llama2_128k_layer_budgets(ora, budget):
     log(f"full size: 128K-token layer {layer} of the 32-layer stack, budget {budget}")
     w = synth.LLAMA2_128K_32L
     _check(ora, w, *_run_layer(w, layer, budget), budget)
+
+
+@pytest.mark.parametrize("extra", [0, 1000])
+def test_llama2_128k_layer_dense_budget(ora, extra):
+    """The article's accuracy policy of dense attention in the last layers
+    (§3.2) is a call with a budget >= the context: every row is selected (in
+    order, -1 padded beyond the context) and the output is exact attention
+    over all 131072 rows."""
+    w = synth.LLAMA2_128K_32L
+    budget = w.n_ctx + extra
+    log(f"full size: 128K-token layer 29 with budget {budget} (dense)")
+    lay, codes, idx, out = _run_layer(w, 29, budget)
+    want = torch.arange(w.n_ctx, dtype=torch.int32, device=DEV)
+    assert torch.equal(idx[..., :w.n_ctx], want.expand(1, w.hq, w.n_ctx))
+    assert (idx[..., w.n_ctx:] == -1).all()
+    _check(ora, w, lay, codes, idx, out, budget)
 
 
 def test_llama32_gqa_1m(ora):

@@ -15,7 +15,7 @@ import torch
 
 import compressed_key_sparse_amd as adamas
 import synth
-from gpu_helpers import TOL, host, log, rel_err
+from gpu_helpers import check_out_paged, host, log
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -69,7 +69,7 @@ def _run(ora, w, P, pages_per_seq, lens, budget, append=True, n_sink=0, n_recent
                                    k_new=kn if append else None, v_new=vn if append else None,
                                    idx_out=idx, n_sink=n_sink, n_recent=n_recent)
     torch.cuda.synchronize()
-    oout, _, oidx, okp, ovp, ocp = ora.decode_paged_step(
+    oout, o64, oidx, okp, ovp, ocp = ora.decode_paged_step(
         q, kp_h, vp_h, cp_h, table, np.array(lens), max_len, budget,
         host(kn) if append else None, host(vn) if append else None, n_sink=n_sink,
         n_recent=n_recent)
@@ -79,9 +79,8 @@ def _run(ora, w, P, pages_per_seq, lens, budget, append=True, n_sink=0, n_recent
     got = idx.cpu().numpy()
     for b in range(B):
         assert np.array_equal(got[b], oidx[b]), f"selection of sequence {b} differs"
-    e = rel_err(out, oout)
-    log(f"  P={P} lens={lens} budget={budget} append={append}: rel err {e:.3e}")
-    assert e <= TOL[dt]
+    check_out_paged(ora, out, q, okp, ovp, table, oidx, oout, o64,
+                    f"P={P} lens={lens} budget={budget} append={append}")
     return got
 
 
@@ -158,10 +157,11 @@ def test_paged_graph_replay_across_page_boundary(ora):
         g.replay()
         torch.cuda.synchronize()
         lens = [L + rep for L in lens0]
-        oout, _, oidx, kp_h, vp_h, cp_h = ora.decode_paged_step(
+        oout, o64, oidx, kp_h, vp_h, cp_h = ora.decode_paged_step(
             host(q_new), kp_h, vp_h, cp_h, table, np.array(lens), 3 * P, 64, host(kn), host(vn))
         assert np.array_equal(idx.cpu().numpy(), oidx), f"replay {rep}: selection differs"
-        assert rel_err(out, oout) <= TOL[dt], f"replay {rep}: output differs"
+        check_out_paged(ora, out, host(q_new), kp_h, vp_h, table, oidx, oout, o64,
+                        f"replay {rep}")
         assert np.array_equal(host(kp), kp_h) and np.array_equal(cp.cpu().numpy(), cp_h)
         with torch.cuda.stream(s):
             lens_d.add_(1)

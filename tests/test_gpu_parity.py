@@ -11,7 +11,7 @@ import torch
 
 import compressed_key_sparse_amd as adamas
 import synth
-from gpu_helpers import TOL, host, log, rel_err
+from gpu_helpers import check_out, host, log
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -140,10 +140,8 @@ def test_sparse_attend(ora, d, dt, budget):
     idx[0, 1, :] = -1                      # a head with nothing selected -> zeros
     it = torch.from_numpy(idx).to(DEV)
     out = adamas.sparse_attend(q, k, v, it)
-    ref, _ = ora.sparse_attend(host(q), host(k), host(v), idx)
-    e = rel_err(out, ref)
-    log(f"  rel err {e:.3e}")
-    assert e <= TOL[dtype]
+    ref, ref64 = ora.sparse_attend(host(q), host(k), host(v), idx)
+    check_out(ora, out, host(q), host(k), host(v), idx, ref, ref64, f"attend d={d} {dt}")
     assert not out[0, 1].any()
 
 
@@ -171,11 +169,9 @@ def _decode_case(ora, w, n_ctx=None, budget=None, layer=0):
     q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
     ocodes = ora.encode_keys(k)
     assert np.array_equal(codes.cpu().numpy(), ocodes), "code cache differs"
-    oout, _, oidx = ora.decode_step(q, k, v, ocodes, n_ctx, budget)
+    oout, o64, oidx = ora.decode_step(q, k, v, ocodes, n_ctx, budget)
     assert np.array_equal(idx.cpu().numpy(), oidx), "selection differs"
-    e = rel_err(out, oout)
-    log(f"  {w.name} n={n_ctx} budget={budget}: rel err {e:.3e}")
-    assert e <= TOL[w.torch_dtype]
+    check_out(ora, out, q, k, v, oidx, oout, o64, f"{w.name} n={n_ctx} budget={budget}")
     return lay, out, idx
 
 
@@ -216,8 +212,8 @@ def test_decode_full_budget_equals_dense(ora):
     assert (idx[..., 500:] == -1).all()
     q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
     dense_idx = np.tile(np.arange(500, dtype=np.int32), (1, 2, 1))
-    ref, _ = ora.sparse_attend(q, k, v, dense_idx)
-    assert rel_err(out, ref) <= TOL[torch.bfloat16]
+    ref, ref64 = ora.sparse_attend(q, k, v, dense_idx)
+    check_out(ora, out, q, k, v, dense_idx, ref, ref64, "dense")
 
 
 def test_decode_deterministic_and_workspace_reuse(ora):
@@ -300,11 +296,9 @@ def _check_schedule(ora, w, mode, case):
     torch.cuda.synchronize()
     assert not ws.buf[:adamas.WS_CTRL_BYTES].any(), "control bytes or status word left set"
     q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
-    oout, _, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), w.n_ctx, w.budget)
+    oout, o64, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), w.n_ctx, w.budget)
     assert np.array_equal(idx.cpu().numpy(), oidx), "selection differs"
-    e = rel_err(out, oout)
-    log(f"  rel err {e:.3e}")
-    assert e <= TOL[w.torch_dtype]
+    check_out(ora, out, q, k, v, oidx, oout, o64, case)
     assert torch.equal(out, out_noidx)
 
 
@@ -368,11 +362,10 @@ def test_decode_keep(ora, restore_mode, mode, n, budget, n_sink, n_recent):
                              n_sink=n_sink, n_recent=n_recent)
     torch.cuda.synchronize()
     q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
-    oout, _, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), n, budget, 0.0, n_sink, n_recent)
+    oout, o64, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), n, budget, 0.0, n_sink,
+                                      n_recent)
     assert np.array_equal(idx.cpu().numpy(), oidx), "selection differs"
-    e = rel_err(out, oout)
-    log(f"  rel err {e:.3e}")
-    assert e <= TOL[torch.bfloat16]
+    check_out(ora, out, q, k, v, oidx, oout, o64, "keep")
 
 
 # --------------------------------------- rotation switched off (ablation)
@@ -408,9 +401,9 @@ def test_decode_without_rotation(ora, restore_rotation, restore_mode, mode):
     q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
     ocodes = ora.encode_keys(k, rotate=False)
     assert np.array_equal(codes.cpu().numpy(), ocodes)
-    oout, _, oidx = ora.decode_step(q, k, v, ocodes, 20000, 256, rotate=False)
+    oout, o64, oidx = ora.decode_step(q, k, v, ocodes, 20000, 256, rotate=False)
     assert np.array_equal(idx.cpu().numpy(), oidx)
-    assert rel_err(out, oout) <= TOL[torch.bfloat16]
+    check_out(ora, out, q, k, v, oidx, oout, o64, "no rotation")
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
@@ -446,9 +439,9 @@ def test_decode_f16_rotation(ora, restore_rotation, restore_mode, mode):
     q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
     ocodes = ora.encode_keys(k, rotate=2)
     assert np.array_equal(codes.cpu().numpy(), ocodes)
-    oout, _, oidx = ora.decode_step(q, k, v, ocodes, 20000, 256, rotate=2)
+    oout, o64, oidx = ora.decode_step(q, k, v, ocodes, 20000, 256, rotate=2)
     assert np.array_equal(idx.cpu().numpy(), oidx)
-    assert rel_err(out, oout) <= TOL[torch.bfloat16]
+    check_out(ora, out, q, k, v, oidx, oout, o64, "f16 rotation")
 
 
 def test_quality_dense_reference_matches_oracle(ora):
@@ -462,3 +455,39 @@ def test_quality_dense_reference_matches_oracle(ora):
     _, ref64 = ora.sparse_attend(q, k, v, idx)
     e = float(np.linalg.norm(got.cpu().double().numpy() - ref64) / np.linalg.norm(ref64))
     assert e < 1e-5
+
+
+# ------------------------------------------------ group-wait give-up path
+def test_group_wait_give_up_is_reported(ora, restore_mode):
+    """A group wait bounded at 0 polls gives up at once wherever its group is
+    not complete yet.  Forced from the host this way, every workgroup still
+    runs to its end: the call's status word is set, its arrival counters are
+    left zero, and after re-arming the word the next call (default bound) is
+    correct and reports nothing."""
+    w = synth.LLAMA2_32K.replace(hq=4, hkv=4, n_ctx=20000, cap=20000, budget=256)
+    adamas.set_decode_mode(adamas.DECODE_GROUP_WAIT)
+    assert adamas.decode_path(1, 4, 4, w.n_ctx, w.budget, 128) == adamas.DECODE_GROUP_WAIT
+    lay = synth.make_layer(w, 0, DEV)
+    codes = torch.zeros((1, 4, w.cap, 32), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    ws = adamas.Workspace(DEV)
+    try:
+        adamas.set_wait_polls(0)
+        log("group wait with a bound of 0 polls")
+        adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, w.n_ctx, w.budget, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        adamas.set_wait_polls(adamas.DEFAULT_WAIT_POLLS)
+    assert ws.status() != 0, "no give-up reported"
+    assert ws.control_bytes_clear(), "arrival counters left set after a give-up"
+    with pytest.raises(adamas.GroupWaitGaveUp):
+        ws.check()                                   # raises and re-arms
+    assert ws.status() == 0
+    idx = torch.empty((1, 4, w.budget), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, w.n_ctx, w.budget, idx_out=idx,
+                             ws=ws, check=True)
+    assert ws.status() == 0 and ws.control_bytes_clear()
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    oout, o64, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), w.n_ctx, w.budget)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    check_out(ora, out, q, k, v, oidx, oout, o64, "after a give-up")

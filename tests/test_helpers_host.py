@@ -1,0 +1,37 @@
+"""Host checks of the test helpers the GPU parity tests rely on: the output
+type's spacing used in the element-wise bound, and the oracle's error scale
+sum_j p_j |v_j| (equal to the output itself when every value is >= 0)."""
+import numpy as np
+import torch
+
+import synth
+from gpu_helpers import ulp
+
+
+def test_ulp_bf16_and_f32():
+    x = np.array([1.0, 1.5, 2.0, -3.0, 0.0, 2.0 ** -126, 2.0 ** -130, 1e30])
+    got = ulp(x, torch.bfloat16)
+    want = [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -133, 2.0 ** -133, 2.0 ** -133,
+            2.0 ** (int(np.floor(np.log2(1e30))) - 7)]
+    assert np.array_equal(got, np.array(want))
+    g32 = ulp(x, torch.float32)
+    assert np.array_equal(g32[:5], [2.0 ** -23, 2.0 ** -23, 2.0 ** -22, 2.0 ** -22, 2.0 ** -149])
+    # agrees with numpy's float32 spacing on normal numbers
+    r = np.random.default_rng(0).standard_normal(1000).astype(np.float32) * 100
+    assert np.array_equal(ulp(r.astype(np.float64), torch.float32),
+                          np.spacing(np.abs(r)).astype(np.float64))
+
+
+def test_error_scale_equals_output_for_nonnegative_values(ora):
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((2, 3, 64)).astype(np.float32)
+    k = rng.standard_normal((2, 3, 50, 64)).astype(np.float32)
+    v = np.abs(rng.standard_normal((2, 3, 50, 64))).astype(np.float32)
+    idx = np.sort(rng.choice(50, size=(2, 3, 20)), axis=-1).astype(np.int32)
+    _, o64 = ora.sparse_attend(q, k, v, idx)
+    assert np.array_equal(ora.attend_error_scale(q, k, v, idx), o64)
+    # with signed values it bounds |o| from above
+    v2 = (v * np.where(rng.random(v.shape) < 0.5, -1, 1)).astype(np.float32)
+    _, o64b = ora.sparse_attend(q, k, v2, idx)
+    a = ora.attend_error_scale(q, k, v2, idx)
+    assert np.all(a >= np.abs(o64b)) and np.array_equal(a, o64)

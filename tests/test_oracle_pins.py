@@ -440,6 +440,68 @@ def test_f64_to_bf16_correct_rounding(ora):
                 assert err_v < err_n or (err_v == err_n and bits % 2 == 0)
 
 
+def _bf16_bits_exact(x: float) -> int:
+    """bfloat16 round-to-nearest-even of x by exact rational arithmetic, from
+    the format's definition: sign, 8 exponent bits (bias 127), 7 fraction
+    bits; normal values (1 + f/128) * 2^(e-127), subnormal f/128 * 2^-126;
+    a result of 2^128 or more is an infinity."""
+    sign = 0x8000 if math.copysign(1.0, x) < 0 else 0
+    a = Fraction(abs(x))
+    if a == 0:
+        return sign
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                   # now 2^e <= a < 2^(e+1)
+    e = max(e, -126)                             # subnormals share the spacing of 2^-126
+    spacing = Fraction(2) ** (e - 7)
+    q = a / spacing
+    n = math.floor(q)
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = n * spacing                              # the rounded magnitude
+    if v >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    if v < Fraction(2) ** -126:                  # subnormal: fraction bits only
+        return sign | int(v / Fraction(2) ** -133)
+    ev = v.numerator.bit_length() - v.denominator.bit_length()
+    if Fraction(2) ** ev > v:
+        ev -= 1
+    frac = (v / Fraction(2) ** ev - 1) * 128
+    assert frac.denominator == 1 and 0 <= frac < 128
+    return sign | ((ev + 127) << 7) | int(frac)
+
+
+def test_f64_to_bf16_extremes_exact(ora):
+    """The binary64 -> bfloat16 rounding at the edges of the format, against
+    exact rational rounding: the overflow boundary (the largest finite value,
+    the tie above it, which rounds to infinity because its pattern is odd, and
+    the values just below that tie), the normal/subnormal boundary, the whole
+    subnormal range including ties at half the smallest subnormal, and
+    log-uniform draws over the entire binary64 range."""
+    maxf = (2 - 2.0 ** -7) * 2.0 ** 127                 # largest finite bfloat16
+    tie_inf = (2 - 2.0 ** -8) * 2.0 ** 127              # halfway to 2^128
+    edge = [maxf, np.nextafter(maxf, np.inf), np.nextafter(tie_inf, 0), tie_inf,
+            np.nextafter(tie_inf, np.inf), 2.0 ** 128, 1e300, float(np.finfo(np.float64).max),
+            (2 - 2.0 ** -7) * 2.0 ** 126 + 2.0 ** 118,    # a tie below the top binade
+            2.0 ** -126, np.nextafter(2.0 ** -126, 0), 2.0 ** -126 - 2.0 ** -134,
+            2.0 ** -133, 2.0 ** -134, np.nextafter(2.0 ** -134, 1), np.nextafter(2.0 ** -134, 0),
+            3 * 2.0 ** -134, 5 * 2.0 ** -134, 2.0 ** -140, 5e-324, 0.0, -0.0]
+    edge += [-x for x in edge]
+    rng = np.random.default_rng(17)
+    sub = list(rng.integers(0, 2 ** 20, 1500) * 2.0 ** -147)           # across the subnormals
+    sub += list((rng.integers(0, 2 ** 8, 500) * 2 + 1) * 2.0 ** -134)  # exact subnormal ties
+    wide = list(np.ldexp(rng.uniform(1, 2, 3000), rng.integers(-1074, 1024, 3000)))
+    wide = [x * (1 if s else -1) for x, s in zip(wide, rng.integers(0, 2, 3000))]
+    top = list(np.ldexp(rng.uniform(1, 2, 1000), 127))                 # the top binade
+    for x in edge + sub + wide + top:
+        x = float(x)
+        assert ora.f64_to_bf16_bits(x) == _bf16_bits_exact(x), x
+    assert _bf16_bits_exact(maxf) == 0x7F7F and _bf16_bits_exact(tie_inf) == 0x7F80
+    assert _bf16_bits_exact(np.nextafter(tie_inf, 0)) == 0x7F7F
+    assert _bf16_bits_exact(2.0 ** -134) == 0 and _bf16_bits_exact(3 * 2.0 ** -134) == 2
+
+
 # --------------------------------------------------------------------------
 # the composed step
 def test_decode_step_is_composition(ora):
