@@ -74,7 +74,7 @@ def _load():
     lib.ora_encode_keys_rot.argtypes = [P, i32, i32, i32, i64, i32, P, i64, i64, i32]
     lib.ora_sparse_attend.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f64, P, P]
     lib.ora_sparse_attend_ex.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f64, P,
-                                         P, P]
+                                         P, P, P]
     lib.ora_decode_step.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, f64, P, P, P]
     lib.ora_f64_to_f16_value.argtypes = [f64]
     lib.ora_f64_to_f16_value.restype = ctypes.c_float
@@ -202,10 +202,11 @@ def sparse_attend(q, k, v, idx, scale: float = 0.0):
     return out, out64
 
 
-def attend_error_scale(q, k, v, idx, scale: float = 0.0) -> np.ndarray:
-    """Per output element of sparse_attend, sum_j p_j |v_j,i| in binary64
-    ([B][Hq][d]): the magnitude a floating-point evaluation's rounding errors
-    scale with (test tolerance scale; not part of the result)."""
+def attend_error_scale(q, k, v, idx, scale: float = 0.0):
+    """Error scales of a floating-point evaluation of sparse_attend (test
+    tolerances; not part of the result), in binary64 -> (A, S):
+    A [B][Hq][d] per output element sum_j p_j |v_j,i|, and S [B][Hq] the
+    largest score magnitude |scale| * sum_i |q_i k_j,i| over the selected rows."""
     q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
     idx = np.ascontiguousarray(idx, np.int32)
     dt = _dtype_tag(q)
@@ -214,9 +215,11 @@ def attend_error_scale(q, k, v, idx, scale: float = 0.0) -> np.ndarray:
     out = np.empty((B, Hq, d), q.dtype)
     out64 = np.empty((B, Hq, d), np.float64)
     am = np.empty((B, Hq, d), np.float64)
+    sm = np.empty((B, Hq), np.float64)
     _load().ora_sparse_attend_ex(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(idx), B, Hq, Hkv, d, cap,
-                                 idx.shape[-1], float(scale), _ptr(out), _ptr(out64), _ptr(am))
-    return am
+                                 idx.shape[-1], float(scale), _ptr(out), _ptr(out64), _ptr(am),
+                                 _ptr(sm))
+    return am, sm
 
 
 def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,

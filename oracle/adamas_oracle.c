@@ -380,14 +380,16 @@ void ora_select_topk(const uint16_t *dist, int B, int Hq, int64_t n_ctx,
  * scale == 0 means 1/sqrt(d) (reading: the usual attention scale).  Entries
  * of idx below 0 are skipped; a row with no valid entry yields zeros.  Writes
  * o in binary64 to out64 (if non-null) and rounded to the element type to
- * out.  absmass64 (if non-null) receives, per output element, the sum of
- * the magnitudes of its terms, sum_j p_j |v_j,i| (binary64): the scale that
- * rounding errors in a floating-point evaluation of o_i are proportional to
- * (tests bound a GPU result's error by it; it does not enter o). */
+ * out.  Two error scales of a floating-point evaluation of the same
+ * attention (tests bound a GPU result's error by them; neither enters o):
+ * absmass64 (if non-null) receives, per output element, the sum of the
+ * magnitudes of its terms, sum_j p_j |v_j,i|; scoremag64 (if non-null), per
+ * (b, hq), the largest score magnitude |scale| * sum_i |q_i k_j,i| over the
+ * selected rows (0 when none is selected).  Both in binary64. */
 void ora_sparse_attend_ex(const void *q, const void *k, const void *v, int dtype,
                           const int32_t *idx, int B, int Hq, int Hkv, int d,
                           int64_t cap, int budget, double scale, void *out,
-                          double *out64, double *absmass64)
+                          double *out64, double *absmass64, double *scoremag64)
 {
     int G = Hq / Hkv;
     if (scale == 0.0)
@@ -400,21 +402,28 @@ void ora_sparse_attend_ex(const void *q, const void *k, const void *v, int dtype
             const int32_t *sel = idx + r * (int64_t)budget;
             double *s = (double *)malloc(sizeof(double) * (size_t)budget);
             double o[ORA_MAX_D];
-            double m = -INFINITY;
+            double m = -INFINITY, smag = 0.0;
             int any = 0;
             for (int j = 0; j < budget; j++) {
                 if (sel[j] < 0)
                     continue;
                 int64_t row = (kvbase + sel[j]) * d;
-                double acc = 0.0;
-                for (int i = 0; i < d; i++)
-                    acc += (double)ora_widen(q, dtype, r * d + i) *
-                           (double)ora_widen(k, dtype, row + i);
+                double acc = 0.0, mag = 0.0;
+                for (int i = 0; i < d; i++) {
+                    double prod = (double)ora_widen(q, dtype, r * d + i) *
+                                  (double)ora_widen(k, dtype, row + i);
+                    acc += prod;
+                    mag += fabs(prod);
+                }
                 s[j] = scale * acc;
                 if (s[j] > m)
                     m = s[j];
+                if (fabs(scale) * mag > smag)
+                    smag = fabs(scale) * mag;
                 any = 1;
             }
+            if (scoremag64)
+                scoremag64[r] = smag;
             double am[ORA_MAX_D];
             for (int i = 0; i < d; i++) {
                 o[i] = 0.0;
@@ -459,7 +468,7 @@ void ora_sparse_attend(const void *q, const void *k, const void *v, int dtype,
                        double *out64)
 {
     ora_sparse_attend_ex(q, k, v, dtype, idx, B, Hq, Hkv, d, cap, budget, scale, out,
-                         out64, 0);
+                         out64, 0, 0);
 }
 
 /* One decode step for one layer: encode each query head (§2.1-§3.1), score

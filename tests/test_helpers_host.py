@@ -2,6 +2,7 @@
 type's spacing used in the element-wise bound, and the oracle's error scale
 sum_j p_j |v_j| (equal to the output itself when every value is >= 0)."""
 import numpy as np
+import pytest
 import torch
 
 import synth
@@ -29,9 +30,16 @@ def test_error_scale_equals_output_for_nonnegative_values(ora):
     v = np.abs(rng.standard_normal((2, 3, 50, 64))).astype(np.float32)
     idx = np.sort(rng.choice(50, size=(2, 3, 20)), axis=-1).astype(np.int32)
     _, o64 = ora.sparse_attend(q, k, v, idx)
-    assert np.array_equal(ora.attend_error_scale(q, k, v, idx), o64)
+    a, s = ora.attend_error_scale(q, k, v, idx)
+    assert np.array_equal(a, o64)
+    # the score magnitude: the largest |scale| * sum_i |q_i k_j,i| over the selection
+    for b in range(2):
+        for h in range(3):
+            rows = k[b, h, idx[b, h]].astype(np.float64)
+            want = np.max(np.abs(rows) @ np.abs(q[b, h].astype(np.float64))) / 8.0
+            assert s[b, h] == pytest.approx(want, rel=1e-14)
     # with signed values it bounds |o| from above
     v2 = (v * np.where(rng.random(v.shape) < 0.5, -1, 1)).astype(np.float32)
     _, o64b = ora.sparse_attend(q, k, v2, idx)
-    a = ora.attend_error_scale(q, k, v2, idx)
-    assert np.all(a >= np.abs(o64b)) and np.array_equal(a, o64)
+    a, s2 = ora.attend_error_scale(q, k, v2, idx)
+    assert np.all(a >= np.abs(o64b)) and np.array_equal(a, o64) and np.array_equal(s2, s)
