@@ -76,6 +76,15 @@ def parse():
                     help="batch16 workload: caches in a shuffled pool of 1024-token pages")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="print a compact summary of rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--last", type=int, default=None,
+                    help="with --summarize: per-kernel statistics of the last N dispatches of a "
+                         "kernel trace (the timed graph replays of a --graph-only run)")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="skip the eager timed pass and the trailing recall launch, so the last "
+                         "steps*layers decode dispatches of a kernel trace are the timed replays")
+    ap.add_argument("--phases", action="store_true",
+                    help="per-phase timeline of the workload's decode launches from the "
+                         "measurement build (libadamas_phases.so); prints a table, no JSON line")
     return ap.parse_args()
 
 
@@ -106,6 +115,33 @@ def measured_traffic():
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+def summarize_trace(dirpath: str, last: int):
+    """Per-kernel durations of the last `last` dispatches in a rocprofv3
+    --kernel-trace CSV (End_Timestamp - Start_Timestamp, ns)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    import numpy as np
+    for f in sorted(glob.glob(os.path.join(dirpath, "**", "*kernel_trace.csv"), recursive=True)):
+        runs = defaultdict(list)
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if "adm::" not in name:
+                    continue
+                runs[name].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        print(f"# kernel trace ({os.path.basename(f)}): last {last} dispatches per kernel")
+        print("dispatches  avg_us   median_us  min_us   max_us   gap_avg_us  kernel")
+        for name, rs in sorted(runs.items()):
+            rs.sort()
+            sel = rs[-last:]
+            dur = np.array([(e - s) / 1e3 for s, e in sel])
+            gaps = np.array([(sel[i + 1][0] - sel[i][1]) / 1e3 for i in range(len(sel) - 1)])
+            print(f"{len(sel):10d} {dur.mean():8.3f} {np.median(dur):9.3f} {dur.min():8.3f} "
+                  f"{dur.max():8.3f} {gaps.mean() if gaps.size else 0.0:10.3f}  {name[:100]}")
 
 
 def summarize(dirpath: str):
@@ -143,7 +179,10 @@ def summarize(dirpath: str):
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize)
+        if args.last:
+            summarize_trace(args.summarize, args.last)
+        else:
+            summarize(args.summarize)
         return
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -161,7 +200,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    adamas.load()
+    adamas.load(variant="phases" if args.phases else None)
+    if args.phases:
+        return bench_phases(args, dev)
     if args.workload == "llama3.2-3b-gqa-1m":
         return bench_gqa(args, dev)
     if args.workload == "batch16-mha-64k-append4k":
@@ -200,21 +241,23 @@ def main():
 
     # -- eager pass: HIP events around every launch, on the launch stream
     K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(L)] for _ in range(K)]
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for s in range(K):
-        for l, lay in enumerate(layers):
-            ev[s][l][0].record(stream)
-            adamas.decode_step(lay["q"], lay["k"], lay["v"], lay["codes"], n, bud, out=lay["out"],
-                               ws=ws, stream=stream)
-            ev[s][l][1].record(stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / K
-    launch_us = float(np.mean([a.elapsed_time(b) for row in ev for a, b in row]) * 1e3)
+    eager_ms = launch_us = None
+    if not args.graph_only:
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(L)] for _ in range(K)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(K):
+            for l, lay in enumerate(layers):
+                ev[s][l][0].record(stream)
+                adamas.decode_step(lay["q"], lay["k"], lay["v"], lay["codes"], n, bud,
+                                   out=lay["out"], ws=ws, stream=stream)
+                ev[s][l][1].record(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / K
+        launch_us = float(np.mean([a.elapsed_time(b) for row in ev for a, b in row]) * 1e3)
 
     # -- graph pass: the 32-layer step captured once and replayed K times
     graph_ms = None
@@ -240,6 +283,11 @@ def main():
         graph_ms = g0.elapsed_time(g1) / K
         step_times = [gev[i].elapsed_time(gev[i + 1]) for i in range(K)]
     ms = graph_ms if graph_ms is not None else eager_ms
+    if ms is None:
+        raise SystemExit("bench.py: --graph-only with --no-graph times nothing")
+    if ws.status() != 0:
+        raise SystemExit("bench.py: a group-wait decode step gave up waiting (workspace status "
+                         "word set): the timed outputs are invalid")
 
     # what plain streaming reads reach on this device (4 GiB, beyond the
     # last-level cache), with the decode scan's own load instructions
@@ -272,14 +320,17 @@ def main():
     achieved = per_layer / (avg_launch_us * 1e-6) / 1e9
 
     # recall of planted needles in the last step's selection (sanity signal)
-    idx = torch.empty((B, Hq, bud), dtype=torch.int32, device=dev)
-    lay = layers[0]
-    adamas.decode_step(lay["q"], lay["k"], lay["v"], lay["codes"], n, bud, idx_out=idx, ws=ws)
-    torch.cuda.synchronize()
-    sel = idx.cpu().numpy()
-    found = sum(len(set(lay["needles"][0, h, 0].tolist()) & set(sel[0, h].tolist()))
-                for h in range(Hq))
-    recall = found / (Hq * w.needles)
+    recall = None
+    if not args.graph_only:
+        idx = torch.empty((B, Hq, bud), dtype=torch.int32, device=dev)
+        lay = layers[0]
+        adamas.decode_step(lay["q"], lay["k"], lay["v"], lay["codes"], n, bud, idx_out=idx,
+                           ws=ws)
+        torch.cuda.synchronize()
+        sel = idx.cpu().numpy()
+        found = sum(len(set(lay["needles"][0, h, 0].tolist()) & set(sel[0, h].tolist()))
+                    for h in range(Hq))
+        recall = round(found / (Hq * w.needles), 4)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -302,12 +353,12 @@ def main():
                    "head_dim": d, "n_ctx": n, "layers": L, "budget": bud,
                    "timing": "hip-graph replay" if graph_ms is not None else "eager"},
         "hbm_gbs_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-        "eager_ms_per_step": round(eager_ms, 4),
+        "eager_ms_per_step": round(eager_ms, 4) if eager_ms is not None else None,
         "roofline": {"bound": "hbm", "kernel": "adamas_decode_step (one layer)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": per_layer, "launch_us": round(avg_launch_us, 3),
-                     "eager_event_launch_us": round(launch_us, 3)},
+                     "eager_event_launch_us": round(launch_us, 3) if launch_us else None},
         "step_ms": ({"p10": round(float(np.percentile(step_times, 10)), 4),
                      "p50": round(float(np.percentile(step_times, 50)), 4),
                      "p90": round(float(np.percentile(step_times, 90)), 4)}
@@ -315,10 +366,125 @@ def main():
         "stream_read": {"kernel": "adamas_stream_read over 4 GiB", "gbs": round(stream_gbs, 1),
                         "frac_of_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
                         "decode_over_stream": round(achieved / stream_gbs, 4)},
-        "needle_recall": round(recall, 4),
+        "needle_recall": recall,
+        "decode_path": adamas.decode_path(B, Hq, Hkv, n, bud, d),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+PHASE_NAMES = {
+    "decode": {0: "entry", 1: "query encoded", 2: "scan end", 3: "chunk threshold",
+               4: "candidates staged", 5: "handed over / histograms published",
+               6: "final: candidates loaded", 7: "final: threshold", 8: "final: selected",
+               9: "rows gathered + weighted", 10: "partials merged", 11: "final: out stored",
+               12: "merged out stored", 13: "rows gathered, last wavefront",
+               14: "slot sums, last wavefront"},
+    "split": {0: "entry", 1: "threshold", 2: "placement", 3: "tokens copied",
+              9: "rows gathered + weighted", 10: "partials merged", 11: "partial handed over",
+              12: "merged out stored", 13: "rows gathered, last wavefront",
+              14: "slot sums, last wavefront"},
+    "attend": {0: "entry", 9: "rows gathered + weighted", 10: "partials merged",
+               11: "partial handed over", 12: "merged out stored",
+               13: "rows gathered, last wavefront", 14: "slot sums, last wavefront"},
+}
+
+
+def phase_table(samples, ticks_per_us):
+    """Per-phase times of the workgroups of each launch, relative to the
+    launch's first workgroup start (slot 0 of the decode region), in us:
+    medians over launches of the per-launch median, 90th percentile and
+    maximum over the workgroups that reached the slot."""
+    import numpy as np
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for st in samples:                      # [regions][workgroups][slots] per launch
+        starts = st[:, :, 0][st[:, :, 0] > 0]
+        if starts.size == 0:
+            continue
+        t0 = starts.min()
+        for ri, region in enumerate(("decode", "split", "attend")):
+            for slot in range(st.shape[2]):
+                v = st[ri, :, slot]
+                v = v[v > 0]
+                if v.size:
+                    us = (v - t0) / ticks_per_us
+                    acc[(ri, region, slot)].append(
+                        (np.median(us), np.percentile(us, 90), us.max(), v.size))
+    lines = ["region  slot  phase                                  wgs   median_us  p90_us   max_us"]
+    for (ri, region, slot), rows in sorted(acc.items()):
+        r = np.median(np.array(rows), axis=0)
+        name = PHASE_NAMES[region].get(slot, f"slot {slot}")
+        lines.append(f"{region:7s} {slot:4d}  {name:38s} {int(r[3]):5d} {r[0]:10.2f} {r[1]:8.2f} "
+                     f"{r[2]:8.2f}")
+    return "\n".join(lines)
+
+
+def bench_phases(args, dev):
+    """Per-phase timeline of decode launches, from the measurement build:
+    every launch runs alone (synchronised before and after) and its
+    workgroups' stamps are read back.  Workloads as in the timed runs: the
+    128K layer stack (cycling --layers, default 8, layers' caches so the
+    codes do not sit in the last-level cache), the GQA 1M layer (4 layers
+    cycled) or the batch-16 append step."""
+    import torch
+
+    import compressed_key_sparse_amd as adamas
+    import synth
+    rec = adamas.PhaseRecorder(dev)
+    launches = []
+    if args.workload == "batch16-mha-64k-append4k":
+        w = synth.BATCH16_64K
+        bud = w.budget if args.budget == 256 else args.budget
+        st = BatchAppendState(w, dev, bud, paged=args.paged)
+        launches = [lambda: st.decode()]
+        desc = f"{w.name}{' paged' if args.paged else ''}, budget {bud}"
+    else:
+        if args.workload == "llama3.2-3b-gqa-1m":
+            w, L = synth.LLAMA32_GQA_1M, 4
+            bud = w.budget if args.budget == 256 else args.budget
+        else:
+            w, L, bud = synth.LLAMA2_128K_32L, args.layers or 8, args.budget
+            if args.n_ctx:
+                w = w.replace(n_ctx=args.n_ctx, cap=args.n_ctx)
+        ws = adamas.Workspace(dev)
+        ws.get(adamas.workspace_bytes(adamas.OP_DECODE_STEP, w.batch, w.hq, w.hkv, w.n_ctx, bud,
+                                      w.head_dim))
+        stack = []
+        for l in range(L):
+            lay = synth.make_layer(w, l, dev)
+            codes = torch.empty((w.batch, w.hkv, w.cap, w.head_dim // 4), dtype=torch.uint8,
+                                device=dev)
+            adamas.encode_keys(lay["k"], codes)
+            stack.append((lay, codes, torch.empty_like(lay["q"])))
+        for lay, codes, out in stack:
+            launches.append(lambda lay=lay, codes=codes, out=out: adamas.decode_step(
+                lay["q"], lay["k"], lay["v"], codes, w.n_ctx, bud, out=out, ws=ws))
+        desc = (f"{w.name}, {w.hq}/{w.hkv} heads x {w.n_ctx} tokens, budget {bud}, "
+                f"path {adamas.decode_path(w.batch, w.hq, w.hkv, w.n_ctx, bud, w.head_dim)}")
+    torch.cuda.synchronize()
+    for f in launches:                      # warm-up
+        f()
+    samples = []
+    reps = max(1, args.steps // len(launches)) * len(launches)
+    for i in range(reps):
+        rec.clear()
+        torch.cuda.synchronize()
+        launches[i % len(launches)]()
+        samples.append(rec.read())
+    # the same launches back to back (as in a step), timed on the stream: the
+    # read-ahead of one launch feeds the next one only when they follow closely
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        launches[i % len(launches)]()
+    e1.record()
+    torch.cuda.synchronize()
+    print(f"# back to back: {e0.elapsed_time(e1) * 1e3 / reps:.2f} us per launch", flush=True)
+    rec.close()
+    print(f"# phase timeline: {desc}; {len(samples)} launches, wall clock "
+          f"{rec.ticks_per_us:.0f} ticks/us", flush=True)
+    print(phase_table(samples, rec.ticks_per_us), flush=True)
 
 
 def stream_read_gbs(dev):
@@ -432,6 +598,9 @@ def bench_gqa(args, dev):
     g1.record(stream)
     torch.cuda.synchronize()
     ms = g0.elapsed_time(g1) / (4 * K)
+    if ws.status() != 0:
+        raise SystemExit("bench.py: a group-wait decode step gave up waiting (workspace status "
+                         "word set): the timed outputs are invalid")
     per_launch = algorithmic_bytes(B, Hq, Hkv, d, n, bud, 2)
     cpu = None
     if args.cpu_seconds > 0:

@@ -25,11 +25,13 @@ __all__ = [
     "OP_SPARSE_ATTEND", "OP_DECODE_STEP", "DECODE_AUTO", "DECODE_LAST_ARRIVAL",
     "DECODE_GROUP_WAIT", "DECODE_SPLIT", "WS_CTRL_BYTES", "WS_STATUS_OFFSET", "ROTATE_OFF",
     "ROTATE_F32", "ROTATE_F16", "GroupWaitGaveUp", "set_wait_polls", "wait_polls",
-    "DEFAULT_WAIT_POLLS",
+    "DEFAULT_WAIT_POLLS", "PhaseRecorder",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libadamas.so")
+# the same library built with the phase timestamps compiled in (measurement only)
+_VARIANTS = {None: None, "phases": os.path.join(_HERE, "libadamas_phases.so")}
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = range(5)
 F32, BF16 = 0, 1
@@ -58,16 +60,27 @@ def library_path() -> str:
     return _LIB_PATH
 
 
-def load():
-    """dlopen libadamas.so (raises if it has not been built)."""
-    global _lib
+_variant = None
+
+
+def load(variant: str | None = None):
+    """dlopen libadamas.so (raises if it has not been built).  variant="phases"
+    loads the measurement build with phase timestamps instead; it must be the
+    first load of the process."""
+    global _lib, _variant
+    if variant not in _VARIANTS:
+        raise ValueError(f"unknown library variant {variant!r}")
     if _lib is not None:
+        if variant is not None and variant != _variant:
+            raise RuntimeError(f"library already loaded as variant {_variant!r}")
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    path = _LIB_PATH if variant is None else _VARIANTS[variant]
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{_LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; "
             "g.build()'` (hipcc --offload-arch=gfx950). There is no CPU fallback.")
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
+    _variant = variant
     P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)
     lib.adamas_encode_keys.argtypes = [P, i32, i32, i32, i64, i32, P, i64, i64, P, P]
@@ -101,6 +114,11 @@ def load():
     lib.adamas_set_wait_polls.restype = i32
     lib.adamas_wait_polls.argtypes = []
     lib.adamas_wait_polls.restype = ctypes.c_uint32
+    lib.adamas_phase_stamps_built.restype = i32
+    lib.adamas_phase_buffer_bytes.restype = sz
+    lib.adamas_set_phase_buffer.argtypes = [P, sz]
+    lib.adamas_set_phase_buffer.restype = i32
+    lib.adamas_wall_clock_khz.restype = i32
     for fn in ("adamas_set_decode_mode", "adamas_decode_path"):
         getattr(lib, fn).restype = i32
     for fn in ("adamas_encode_keys", "adamas_score", "adamas_select_topk", "adamas_sparse_attend",
@@ -313,6 +331,35 @@ def set_rotation(on) -> None:
     (adamas_set_rotation)."""
     mode = int(on) if not isinstance(on, bool) else (1 if on else 0)
     _check(load().adamas_set_rotation(mode), "adamas_set_rotation")
+
+
+class PhaseRecorder:
+    """Phase timestamps of the measurement build (load(variant="phases")):
+    a device buffer the kernels write the wall clock into at marked points.
+    read() -> numpy int64 [3 regions][8192 workgroups][16 slots] (0 = not
+    reached) after synchronising; clear() zeroes it; ticks_per_us the clock."""
+
+    REGIONS = ("decode", "split", "attend")
+
+    def __init__(self, device="cuda"):
+        lib = load()
+        if not lib.adamas_phase_stamps_built():
+            raise RuntimeError("the loaded library has no phase stamps (load(variant='phases'))")
+        n = int(lib.adamas_phase_buffer_bytes())
+        self.buf = torch.zeros(n // 8, dtype=torch.int64, device=device)
+        _check(lib.adamas_set_phase_buffer(ctypes.c_void_p(self.buf.data_ptr()), n),
+               "adamas_set_phase_buffer")
+        self.ticks_per_us = lib.adamas_wall_clock_khz() / 1000.0
+
+    def clear(self):
+        self.buf.zero_()
+
+    def read(self):
+        torch.cuda.synchronize(self.buf.device)
+        return self.buf.view(3, 8192, 16).cpu().numpy()
+
+    def close(self):
+        load().adamas_set_phase_buffer(None, 0)
 
 
 def set_wait_polls(polls: int) -> None:

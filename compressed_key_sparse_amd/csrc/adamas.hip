@@ -42,6 +42,8 @@ std::atomic<int> g_decode_mode{ADAMAS_DECODE_AUTO};
 std::atomic<int> g_rotation{1};
 int rotation_on() { return g_rotation.load(std::memory_order_relaxed); }
 std::atomic<uint32_t> g_wait_polls{kDefaultWaitPolls};
+std::atomic<uint64_t*> g_stamps{nullptr};  // phase stamps (measurement build)
+uint64_t* stamps_ptr() { return g_stamps.load(std::memory_order_relaxed); }
 
 int launch_status() {
   return hipGetLastError() == hipSuccess ? ADAMAS_OK : ADAMAS_ERR_DEVICE;
@@ -98,10 +100,12 @@ void launch_attend_t(dim3 grid, hipStream_t s, const void* q, const void* k, con
                      float* part, uint32_t* ctr, void* out, const PageArgs* pa) {
   if (pa != nullptr)
     k_attend<D, BF, true><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
-                                                          qscale, part, ctr, out, *pa);
+                                                          qscale, part, ctr, out, *pa,
+                                                          stamps_ptr());
   else
     k_attend<D, BF, false><<<grid, kAttendThreads, 0, s>>>(q, k, v, idx, Hq, Hkv, cap, budget,
-                                                           qscale, part, ctr, out, PageArgs{});
+                                                           qscale, part, ctr, out, PageArgs{},
+                                                           stamps_ptr());
 }
 
 // pa: the page table of paged K/V pools, or null for [B][Hkv][cap][D] caches
@@ -287,7 +291,7 @@ int launch_last_arrival(const DecodePlan& p, const DecodeArgs& a, int B, int hea
     const bool fa = bsel <= kSplitFuseRows;
     const SplitAttend sa{fa ? a.q : nullptr, a.k, a.v, a.Hq, a.Hkv, a.cap, a.qscale,
                          reinterpret_cast<float*>(w + p.spart_off),
-                         reinterpret_cast<uint32_t*>(w + kCtrlAttend), a.out};
+                         reinterpret_cast<uint32_t*>(w + kCtrlAttend), a.out, a.stamps};
     const size_t lds = split_select_lds(head_dim, p.ncp, fa);
     with_dim(head_dim, [&](auto dc) {
       constexpr int D = decltype(dc)::value;
@@ -320,11 +324,15 @@ int launch_last_arrival(const DecodePlan& p, const DecodeArgs& a, int B, int hea
 
 extern "C" {
 
-int adamas_decode_step_keep(const void* q, const void* k, const void* v, const uint8_t* k_codes,
-                            int dtype, int B, int Hq, int Hkv, int head_dim, int64_t cap,
-                            int64_t n_ctx, int budget, int n_sink, int n_recent, float scale,
-                            void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
-                            hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_step_impl(const void* q, const void* k, const void* v, const uint8_t* k_codes,
+                     int dtype, int B, int Hq, int Hkv, int head_dim,
+                     int64_t cap, int64_t n_ctx, int budget, int n_sink, int n_recent,
+                     float scale, void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
   if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || cap < 1 || n_ctx < 1 || n_ctx > cap ||
       budget < 1 || !isfinite(scale) || n_sink < 0 || n_recent < 0)
@@ -358,6 +366,7 @@ int adamas_decode_step_keep(const void* q, const void* k, const void* v, const u
                    nullptr, nullptr, idx_out, out, n_sink, n_recent, {}};
       a.rotate = rotation_on();
       a.wait_polls = g_wait_polls.load(std::memory_order_relaxed);
+      a.stamps = stamps_ptr();
       const dim3 grid((unsigned)gp.n_chunks, (unsigned)Hkv, (unsigned)B);
       bool ok = false;
       with_dim(head_dim, [&](auto dc) {
@@ -380,11 +389,25 @@ int adamas_decode_step_keep(const void* q, const void* k, const void* v, const u
                reinterpret_cast<uint32_t*>(w + p.sel.cand_off),
                reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent, {}};
   a.rotate = rotation_on();
+  a.stamps = stamps_ptr();
   if (split) {
     a.chist = reinterpret_cast<uint16_t*>(w + p.chist_off);
     a.ncp = p.ncp;
   }
   return launch_last_arrival(p, a, B, head_dim, bf, w, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int adamas_decode_step_keep(const void* q, const void* k, const void* v, const uint8_t* k_codes,
+                            int dtype, int B, int Hq, int Hkv, int head_dim, int64_t cap,
+                            int64_t n_ctx, int budget, int n_sink, int n_recent, float scale,
+                            void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  return decode_step_impl(q, k, v, k_codes, dtype, B, Hq, Hkv, head_dim, cap, n_ctx, budget,
+                          n_sink, n_recent, scale, out, idx_out, ws, ws_bytes, stream);
 }
 
 int adamas_decode_step(const void* q, const void* k, const void* v, const uint8_t* k_codes,
@@ -450,6 +473,7 @@ int ragged_step(const void* q, const void* k_new, const void* v_new, void* k, vo
                RaggedArgs{lens, k_new, v_new, k, v, k_codes, pages, max_pages, page_log2,
                           n_pages, pt_lds}};
   a.rotate = rotation_on();
+  a.stamps = stamps_ptr();
   return launch_last_arrival(p, a, B, head_dim, dtype == ADAMAS_BF16, w, stream);
 }
 
@@ -498,6 +522,27 @@ int adamas_set_wait_polls(uint32_t polls) {
 }
 
 uint32_t adamas_wait_polls(void) { return g_wait_polls.load(std::memory_order_relaxed); }
+
+int adamas_phase_stamps_built(void) { return kPhases ? 1 : 0; }
+
+size_t adamas_phase_buffer_bytes(void) {
+  return (size_t)kPhaseRegions * kPhaseMaxWorkgroups * kPhaseSlots * sizeof(uint64_t);
+}
+
+int adamas_set_phase_buffer(void* buf, size_t bytes) {
+  if (!kPhases) return ADAMAS_ERR_UNSUPPORTED;
+  if (buf != nullptr && (!aligned16(buf) || bytes < adamas_phase_buffer_bytes()))
+    return ADAMAS_ERR_INVALID;
+  g_stamps.store(static_cast<uint64_t*>(buf), std::memory_order_relaxed);
+  return ADAMAS_OK;
+}
+
+int adamas_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+  return khz;
+}
 
 int adamas_set_decode_mode(int mode) {
   if (mode != ADAMAS_DECODE_AUTO && mode != ADAMAS_DECODE_LAST_ARRIVAL &&

@@ -35,6 +35,45 @@ ADM_DEV void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ------------------------------------------------------------ phase stamps
+// A measurement build (compiled with -DADAMAS_PHASES=1, libadamas_phases.so)
+// records, per workgroup, the device's constant-rate wall clock at marked
+// points of a kernel: thread 0 stores the counter straight to a caller-given
+// buffer (no registers held, no barriers added), so the kernel's schedule is
+// the product's.  The product build compiles every mark away.  Layout:
+// [kernel region][workgroup][kPhaseSlots] u64, 0 = not reached.
+#if defined(ADAMAS_PHASES) && ADAMAS_PHASES
+constexpr bool kPhases = true;
+#else
+constexpr bool kPhases = false;
+#endif
+constexpr int kPhaseSlots = 16;
+constexpr int kPhaseMaxWorkgroups = 8192;  // per kernel region
+enum PhaseRegion { kPhaseDecode = 0, kPhaseSplit = 1, kPhaseAttend = 2, kPhaseRegions = 3 };
+struct PhaseStamps {
+  uint64_t* row;  // this workgroup's slots, or null
+  ADM_DEV PhaseStamps(uint64_t* buf, int region) : row(nullptr) {
+    if constexpr (kPhases) {
+      const int64_t wg = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+      if (buf != nullptr && wg < kPhaseMaxWorkgroups)
+        row = buf + ((int64_t)region * kPhaseMaxWorkgroups + wg) * kPhaseSlots;
+    }
+  }
+  ADM_DEV void mark(int slot) const {
+    if constexpr (kPhases) {
+      if (row != nullptr && threadIdx.x == 0) row[slot] = wall_clock64();
+    }
+  }
+  // the latest of the workgroup's wavefronts to reach this point
+  ADM_DEV void mark_last_wave(int slot) const {
+    if constexpr (kPhases) {
+      if (row != nullptr && (threadIdx.x & (kWave - 1)) == 0)
+        atomicMax(reinterpret_cast<unsigned long long*>(row + slot),
+                  (unsigned long long)wall_clock64());
+    }
+  }
+};
+
 // ---------------------------------------------------------------- elements
 ADM_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -867,7 +906,8 @@ ADM_DEV int32_t slot_token0(const int32_t* slot_start, int slot, int chunk) {
 template <int NT>
 ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk, int nbins, int bsel,
                           int budget, int32_t* sidx, int32_t* idx, uint32_t* scand, int mcap,
-                          uint32_t* shist, uint32_t* s_tmp, const int32_t* slot_start = nullptr) {
+                          uint32_t* shist, uint32_t* s_tmp, const int32_t* slot_start = nullptr,
+                          const PhaseStamps* ps = nullptr) {
   if (M > 4 * NT) {
     final_select_tiled<NT>(cand, M, kpad_log2, chunk, nbins, bsel, budget, sidx, idx, scand,
                            mcap, shist, s_tmp, slot_start);
@@ -886,7 +926,9 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
     if ((int)d < nbins) atomicAdd(&shist[d], 1u);
   }
   lds_sync();
+  if (ps) ps->mark(6);  // candidates loaded, histogram built
   const Threshold thr = find_threshold<NT>(shist, nbins, (uint32_t)bsel, s_tmp);
+  if (ps) ps->mark(7);  // threshold found
   const uint32_t quota = (uint32_t)bsel - thr.lt;
   uint32_t lt = 0, eq = 0;
 #pragma unroll

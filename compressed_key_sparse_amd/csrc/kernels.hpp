@@ -408,7 +408,8 @@ template <int D, bool BF, int NT, bool OVR = false, bool PG = false>
 ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
                          const void* __restrict__ v, int64_t qoff, int64_t kvrow0, int64_t cap,
                          const int32_t* rows, int nrows, float qscale, float* s_part,
-                         float* s_res, RowOverride ovr = {}, PageMap pm = {}) {
+                         float* s_res, RowOverride ovr = {}, PageMap pm = {},
+                         const PhaseStamps* ps = nullptr) {
   constexpr int EL = D / 16, NS = NT / 16, NW = NT / kWave, PW = 2 + D;
   // fp32 rows are twice the bytes: half the rows per batch keeps registers in budget
   // (and D = 256 rows twice those of D = 128)
@@ -471,10 +472,15 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
     }
     m_run = mn;
   }
+  if (ps) {
+    ps->mark(9);             // rows gathered, weighted (thread 0's wavefront)
+    ps->mark_last_wave(13);  // ... by every wavefront
+  }
   // every slot shares m_run: sum l and o over slots (lanes ^16, ^32), then waves
   l_run = xor_sum<32>(xor_sum<16>(l_run));
 #pragma unroll
   for (int e = 0; e < EL; ++e) o[e] = xor_sum<32>(xor_sum<16>(o[e]));
+  if (ps) ps->mark_last_wave(14);  // slot sums done by every wavefront
   float* mine = s_part + wid * PW;
   if (lane < 16) {
     if (lane == 0) {
@@ -504,6 +510,7 @@ ADM_DEV void attend_rows(const void* __restrict__ q, const void* __restrict__ k,
     }
   }
   lds_sync();
+  if (ps) ps->mark(10);  // partials of the wavefronts merged
 }
 
 template <bool BF>
@@ -529,8 +536,12 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ idx, int Hq, int Hkv, int64_t cap, int budget, float qscale,
     float* __restrict__ part, uint32_t* __restrict__ counters, void* __restrict__ out,
-    PageArgs pa = {}) {
+    PageArgs pa = {}, uint64_t* __restrict__ stamps = nullptr) {
   constexpr int NT = kAttendThreads, NW = NT / kWave, PW = 2 + D;
+  // phase stamps: 0 entry, 9-10 inside attend_rows, 11 partial handed over,
+  // 12 merged output stored
+  const PhaseStamps ps(stamps, kPhaseAttend);
+  ps.mark(0);
   constexpr int PWP = (PW + 3) & ~3;  // partial rows padded to 16 bytes
   constexpr int kMergeTile = 32;
   __shared__ uint32_t s_tmp[kTmpWords];
@@ -546,7 +557,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
   const PageMap pm{PG ? pa.pages + (int64_t)b * pa.max_pages : nullptr, pa.page_log2, pa.n_pages,
                    pa.max_pages, hq / G, Hkv};
   attend_rows<D, BF, NT, false, PG>(q, k, v, row * D, kvrow0, cap, idx + row * budget + r0, nrows,
-                                    qscale, s_part, s_res, RowOverride{}, pm);
+                                    qscale, s_part, s_res, RowOverride{}, pm, &ps);
   if (S == 1) {
     if (threadIdx.x < D) {
       const float L = s_res[1];
@@ -557,14 +568,16 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
   float* mine = part + (row * S + s) * PWP;
   lds_to_shared<NT>(reinterpret_cast<uint32_t*>(mine), reinterpret_cast<const uint32_t*>(s_res),
                     PWP);
-  if (!arrive_last<NT>(&counters[row], S, s_tmp)) return;
-  const float* ps = part + row * S * PWP;
+  const bool last = arrive_last<NT>(&counters[row], S, s_tmp);
+  ps.mark(11);
+  if (!last) return;
+  const float* pp = part + row * S * PWP;
   float M = -INFINITY, L = 0.0f, O = 0.0f;
   for (int t0 = 0; t0 < S; t0 += kMergeTile) {
     const int nt = min(kMergeTile, S - t0);
     lds_sync();
     shared_to_lds<NT>(reinterpret_cast<uint32_t*>(s_tile),
-                      reinterpret_cast<const uint32_t*>(ps + t0 * PWP), nt * PWP);
+                      reinterpret_cast<const uint32_t*>(pp + t0 * PWP), nt * PWP);
     lds_sync();
     if (threadIdx.x < D) {
       for (int i = 0; i < nt; ++i) {
@@ -581,6 +594,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
   }
   if (threadIdx.x < D) store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? O / L : 0.0f);
   if (threadIdx.x == 0) counters[row] = 0;
+  ps.mark(12);
 }
 
 // --------------------------------------------------------- §5.2 selection
@@ -674,10 +688,16 @@ void k_decode(
     int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
     void* __restrict__ out, int n_sink, int n_recent, int rotate, RaggedArgs rg,
-    uint16_t* __restrict__ chist, int ncp) {
+    uint16_t* __restrict__ chist, int ncp, uint64_t* __restrict__ stamps) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), W = D / 16;
   constexpr int E = D / 64, kLanesPerWord = 16 / E, PW = 2 + D;
+  // phase stamps (measurement build only): 0 entry, 1 query encoded, 2 scan
+  // end, 3 chunk threshold, 4 candidates staged, 5 handed over; final
+  // workgroup: 6-7 inside final_select, 8 selection done, 9-10 inside
+  // attend_rows, 11 output stored
+  const PhaseStamps ps(stamps, kPhaseDecode);
+  ps.mark(0);
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
   uint8_t* region = smem + kTmpWords * 4;
@@ -804,6 +824,7 @@ void k_decode(
     if (lane % kLanesPerWord == 0) sq[wid * W + lane / kLanesPerWord] = word;
   }
   lds_sync();
+  ps.mark(1);
   QPlanes qp[G];
   load_qplanes<D, G>(sq, qp);
   const KeepRange keep(t0, valid, n_sink, n_b - n_recent);
@@ -830,6 +851,7 @@ void k_decode(
     }
   }
   lds_sync();
+  ps.mark(2);
   if (chist != nullptr) {
     // separate selection (k_split_select): this chunk's key counts per head,
     // one row of kNbinsHist(D) u16 per (head, chunk), 8 counts per store
@@ -855,6 +877,7 @@ void k_decode(
     if (n_stage == G) {
       chunk_compact_heads<NT, NB, G>(shist, NBP, sdist, chunk, valid, (uint32_t)kc, sstage, kpad,
                                      s_fused, s_fused + 2 * G);
+      ps.mark(4);
       for (int g = 0; g < G; ++g) {
         const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
         lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage + g * kpad, kpad);
@@ -866,14 +889,21 @@ void k_decode(
     for (int g = 0; g < G; ++g) {
       const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
       const Threshold thr = find_threshold<NT>(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
+      ps.mark(3);
       chunk_compact<NT>(sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad,
                         s_tmp, [](uint32_t, uint32_t) {});
       lds_sync();
+      ps.mark(4);
       lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
     }
   }
-  if (chist != nullptr) return;  // k_split_select takes it from here
-  if (!arrive_last<NT>(&counters[b * Hkv + hkv], active, s_tmp)) return;
+  if (chist != nullptr) {  // k_split_select takes it from here
+    ps.mark(5);
+    return;
+  }
+  const bool last = arrive_last<NT>(&counters[b * Hkv + hkv], active, s_tmp);
+  ps.mark(5);
+  if (!last) return;
   const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap;
   // paged: the gathers below look up the sequence's page table; its row is
   // loaded now (in flight during the selection) and kept in LDS
@@ -887,7 +917,8 @@ void k_decode(
     const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
     final_select<NT>(cand + row * n_chunks * kpad, active * kpad, kpad_log2, chunk, NB, bsel,
                      budget, fuse_attend ? sidx : nullptr, idx ? idx + row * budget : nullptr,
-                     scand, mcap, fhist, s_tmp);
+                     scand, mcap, fhist, s_tmp, nullptr, &ps);
+    ps.mark(8);
     if constexpr (RAG == 2) {
       if (g == 0 && rg.pt_lds && fuse_attend) {
         int32_t* s_pt = reinterpret_cast<int32_t*>(scand + mcap);
@@ -902,9 +933,10 @@ void k_decode(
             q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part, s_res,
             RowOverride{rg.k_new, rg.v_new, rg.k_new != nullptr ? pos_new : -2,
                         ((int64_t)b * Hkv + hkv) * D},
-            amap);
+            amap, &ps);
       else
-        attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part, s_res);
+        attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part, s_res,
+                               RowOverride{}, PageMap{}, &ps);
       if (threadIdx.x < D) {
         const float L = s_res[1];
         store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? s_res[2 + threadIdx.x] / L : 0.0f);
@@ -913,6 +945,7 @@ void k_decode(
     }
   }
   if (threadIdx.x == 0) counters[b * Hkv + hkv] = 0;
+  ps.mark(11);
 }
 
 // ------------------------------------- decode step, selection on its own
@@ -950,6 +983,7 @@ struct SplitAttend {
   float* part;                 // [B*Hq][segments][PWP] partials
   uint32_t* counters;          // [B*Hq] arrival counters, left zero
   void* out;
+  uint64_t* stamps;            // phase stamps (measurement build), or null
 };
 constexpr int kSplitFuseRows = 8192;
 
@@ -960,6 +994,10 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
     int32_t* __restrict__ idx, SplitAttend fa) {
   constexpr int NT = kSplitThreads, NW = NT / kWave, EPL = kSplitEntriesPerLane;
   constexpr int PW = 2 + D, PWP = (PW + 3) & ~3;
+  // phase stamps: 0 entry, 1 threshold, 2 placement done, 3 tokens copied,
+  // 9-10 inside attend_rows, 11 partial handed over, 12 merged output stored
+  const PhaseStamps ps(fa.stamps, kPhaseSplit);
+  ps.mark(0);
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
   uint32_t* s_hist = s_tmp + kTmpWords;
@@ -1049,6 +1087,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
     }
   }
   const uint32_t quota = (uint32_t)bsel - thr.lt;
+  ps.mark(1);
   lds_sync();
   if (n_chunks <= kWave) {
     // prefix sums over chunks in one wavefront: where each chunk's tokens
@@ -1092,6 +1131,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
     }
   }
   lds_sync();
+  ps.mark(2);
   int32_t* out = idx + row * budget;
   if (blockIdx.x == 0)
     for (int j = bsel + threadIdx.x; j < budget; j += NT) out[j] = -1;
@@ -1155,11 +1195,12 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
   if (!fused) return;
   // §6 over this segment's rows, then the log-sum-exp merge of the segments
   lds_sync();
+  ps.mark(3);
   const int G = fa.Hq / fa.Hkv;
   const int b = (int)(row / fa.Hq), hq = (int)(row % fa.Hq);
   const int64_t kvrow0 = ((int64_t)b * fa.Hkv + hq / G) * fa.cap;
   attend_rows<D, BF, NT>(fa.q, fa.k, fa.v, row * D, kvrow0, fa.cap, s_rows, (int)(seg1 - seg0),
-                         fa.qscale, s_part, s_res);
+                         fa.qscale, s_part, s_res, RowOverride{}, PageMap{}, &ps);
   const int S = gridDim.x;
   if (S == 1) {
     if ((int)threadIdx.x < D) {
@@ -1170,17 +1211,19 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
   }
   lds_to_shared<NT>(reinterpret_cast<uint32_t*>(fa.part + (row * S + blockIdx.x) * PWP),
                     reinterpret_cast<const uint32_t*>(s_res), PWP);
-  if (!arrive_last<NT>(&fa.counters[row], S, s_tmp)) return;
+  const bool last = arrive_last<NT>(&fa.counters[row], S, s_tmp);
+  ps.mark(11);
+  if (!last) return;
   // merge: partials staged through LDS (the row list is free now)
   float* s_tile = reinterpret_cast<float*>(s_rows);
   constexpr int kTile = kSplitFuseRows / PWP;
-  const float* ps = fa.part + row * S * PWP;
+  const float* pp = fa.part + row * S * PWP;
   float M = -INFINITY, L = 0.0f, O = 0.0f;
   for (int s0 = 0; s0 < S; s0 += kTile) {
     const int nt = min(kTile, S - s0);
     lds_sync();
     shared_to_lds<NT>(reinterpret_cast<uint32_t*>(s_tile),
-                      reinterpret_cast<const uint32_t*>(ps + s0 * PWP), nt * PWP);
+                      reinterpret_cast<const uint32_t*>(pp + s0 * PWP), nt * PWP);
     lds_sync();
     if ((int)threadIdx.x < D) {
       for (int i = 0; i < nt; ++i) {
@@ -1197,6 +1240,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
   }
   if ((int)threadIdx.x < D) store_out<BF>(fa.out, row * D + threadIdx.x, L > 0.0f ? O / L : 0.0f);
   if (threadIdx.x == 0) fa.counters[row] = 0;
+  ps.mark(12);
 }
 
 // ------------------------------------------ fused decode step, group wait
@@ -1220,7 +1264,13 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     int n_chunks, int budget, int cmax, float qscale, uint16_t* __restrict__ ghist,
     float* __restrict__ part, uint32_t* __restrict__ arrive_hist,
     uint32_t* __restrict__ arrive_part, uint32_t* __restrict__ status, uint32_t max_polls,
-    int32_t* __restrict__ idx, void* __restrict__ out, int n_sink, int n_recent, int rotate) {
+    int32_t* __restrict__ idx, void* __restrict__ out, int n_sink, int n_recent, int rotate,
+    uint64_t* __restrict__ stamps) {
+  // phase stamps: 0 entry, 2 scan end, 3 histograms published, 4 group
+  // complete, 5 selection done, 9-10 inside attend_rows, 11 partial handed
+  // over, 12 merged output stored
+  const PhaseStamps ps(stamps, kPhaseDecode);
+  ps.mark(0);
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), NBH = kNbinsHist(D), W = D / 16;
   static_assert(G <= kTmpWords - kTmpGroupCounts, "per-head counts live in s_tmp");
@@ -1279,6 +1329,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
         src, valid, qp, [&](int g, int tok, uint32_t d) { sink(g, tok, keep.key(tok, d)); },
         &first);
   lds_sync();
+  ps.mark(2);
 
   // publish this chunk's histograms as u16 rows (counts <= chunk < 2^16)
   for (int i = threadIdx.x; i < G * (NBH / 8); i += NT) {
@@ -1295,8 +1346,10 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   // a wait that gave up leaves the group's histograms possibly incomplete:
   // this workgroup then keeps no rows (and writes no indices), publishes an
   // empty partial and runs to its end, so the counters are still reset
+  ps.mark(3);
   const bool complete = arrive_and_wait<NT>(&arrive_hist[grp], n_chunks, status, max_polls,
                                             s_tmp);
+  ps.mark(4);
 
   // group thresholds; this chunk's share of each query head's selection
   const int bsel = (int)min((int64_t)budget, n_ctx);
@@ -1350,16 +1403,19 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
       for (int j = bsel + (int)threadIdx.x; j < budget; j += NT) idx[row * budget + j] = -1;
   }
   lds_sync();  // index rows complete; the distances are no longer needed
+  ps.mark(5);
 
   const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap;
   for (int g = 0; g < G; ++g) {
     const int64_t row = row0 + g;
     attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx + g * cmax, (int)s_cnt[g], qscale,
-                           s_part, s_res);
+                           s_part, s_res, RowOverride{}, PageMap{}, &ps);
     lds_to_shared<NT>(reinterpret_cast<uint32_t*>(part + (row * n_chunks + c) * PWP),
                       reinterpret_cast<const uint32_t*>(s_res), PWP);
   }
-  if (!arrive_last<NT>(&arrive_part[grp], n_chunks, s_tmp)) return;
+  const bool last = arrive_last<NT>(&arrive_part[grp], n_chunks, s_tmp);
+  ps.mark(11);
+  if (!last) return;
   for (int g = 0; g < G; ++g) {
     const int64_t row = row0 + g;
     float M = -INFINITY, L = 0.0f, O = 0.0f;
@@ -1389,6 +1445,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     arrive_hist[grp] = 0;
     arrive_part[grp] = 0;
   }
+  ps.mark(12);
 }
 
 // ---------------------------------------------------------- reference read

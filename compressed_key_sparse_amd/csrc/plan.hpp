@@ -255,6 +255,7 @@ struct DecodeArgs {
   int ncp = 0;
   int rotate = 1;             // adamas_set_rotation mode
   uint32_t wait_polls = kDefaultWaitPolls;  // group-wait bound (adamas_set_wait_polls)
+  uint64_t* stamps = nullptr;  // phase stamps (measurement build), or null
 };
 
 // Dynamic LDS beyond 64 KiB must be allowed per kernel before its launch.

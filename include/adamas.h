@@ -343,6 +343,25 @@ int adamas_decode_paged_step(const void *q, const void *k_new, const void *v_new
                              int budget, int n_sink, int n_recent, float scale, void *out,
                              int32_t *idx_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Measurement hooks, not steps of the method.  A library built with
+ * -DADAMAS_PHASES=1 (libadamas_phases.so) records, for every workgroup of
+ * the decode, selection and attention kernels, the device's constant-rate
+ * wall clock (adamas_wall_clock_khz ticks per millisecond) at marked points,
+ * into a caller-owned device buffer of adamas_phase_buffer_bytes() bytes:
+ * u64 [3 kernel regions: decode, split selection, attention][8192
+ * workgroups][16 slots], 0 where a slot was not reached; each launch
+ * overwrites its region.  adamas_set_phase_buffer(NULL, 0) stops recording.
+ * In the product build adamas_phase_stamps_built() is 0 and
+ * adamas_set_phase_buffer returns ADAMAS_ERR_UNSUPPORTED; ADAMAS_ERR_INVALID
+ * for a misaligned or short buffer.  The buffer is borrowed until it is
+ * unset; launches that overlap in time overwrite each other's stamps.
+ */
+int adamas_phase_stamps_built(void);
+size_t adamas_phase_buffer_bytes(void);
+int adamas_set_phase_buffer(void *buf, size_t bytes);
+int adamas_wall_clock_khz(void);
+
 /* Workspace bytes needed by `op` for the given shape (0 for invalid shapes). */
 size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx,
                               int budget, int head_dim);
