@@ -71,7 +71,11 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a conversion kernel of known traffic (HBM counter scaling)")
     ap.add_argument("--workload", default=HEADLINE,
-                    choices=(HEADLINE, "llama3.2-3b-gqa-1m", "batch16-mha-64k-append4k"))
+                    choices=(HEADLINE, "llama3.2-3b-gqa-1m", "batch16-mha-64k-append4k",
+                             "llama2-mha-32k", "tiny-1h-d64-1k"))
+    ap.add_argument("--replicas", type=int, default=8,
+                    help="single-layer workloads: distinct copies of the layer cycled so that "
+                         "no launch finds its caches in the last-level cache")
     ap.add_argument("--paged", action="store_true",
                     help="batch16 workload: caches in a shuffled pool of 1024-token pages")
     ap.add_argument("--summarize", metavar="DIR", default=None,
@@ -207,6 +211,8 @@ def main():
         return bench_gqa(args, dev)
     if args.workload == "batch16-mha-64k-append4k":
         return bench_batch_append(args, dev)
+    if args.workload in ("llama2-mha-32k", "tiny-1h-d64-1k"):
+        return bench_single(args, dev, synth.WORKLOADS[args.workload])
     w = synth.LLAMA2_128K_32L
     if args.n_ctx:
         w = w.replace(n_ctx=args.n_ctx, cap=args.n_ctx)
@@ -545,6 +551,80 @@ def result_line(metric, w, B, ms, K, warmup, cfg, kernel, per_launch, launch_us,
     }
     res.update(extra)
     print(json.dumps(res), flush=True)
+
+
+def bench_single(args, dev, w):
+    """Latency of one decode-step launch of a single-layer workload (the
+    32K-token Llama-2-shaped layer, or the tiny single-head fp32 case):
+    --replicas distinct copies of the layer (caches and codes) are cycled in
+    a replayed HIP graph, so that each launch reads its codes from HBM rather
+    than from the last-level cache.  value = batch / launch time."""
+    import numpy as np
+    import torch
+
+    import compressed_key_sparse_amd as adamas
+    import synth
+    B, Hq, Hkv, d, n = w.batch, w.hq, w.hkv, w.head_dim, w.n_ctx
+    bud = w.budget if args.budget == 256 else args.budget
+    R = max(1, args.replicas)
+    print(f"[bench] setup: {R} replicas of {w.name}, budget {bud}", file=sys.stderr, flush=True)
+    reps = []
+    for r in range(R):
+        lay = synth.make_layer(w, r, dev)
+        codes = torch.empty((B, Hkv, w.cap, d // 4), dtype=torch.uint8, device=dev)
+        adamas.encode_keys(lay["k"], codes)
+        reps.append((lay, codes, torch.empty_like(lay["q"])))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(dev)
+    ws = adamas.Workspace(dev)
+    ws.get(adamas.workspace_bytes(adamas.OP_DECODE_STEP, B, Hq, Hkv, n, bud, d))
+
+    def launch(i):
+        lay, codes, out = reps[i]
+        adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, n, bud, out=out, ws=ws,
+                           stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            for i in range(R):
+                launch(i)
+    K = args.steps
+    eager_ms, launch_us = timed_launches(launch, R, stream, K)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(R):
+                launch(i)
+        for _ in range(args.warmup):
+            g.replay()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    marks[0].record(stream)
+    with torch.cuda.stream(stream):
+        for i in range(K):
+            g.replay()
+            marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [marks[i].elapsed_time(marks[i + 1]) * 1e3 / R for i in range(K)]
+    us = marks[0].elapsed_time(marks[K]) * 1e3 / (R * K)
+    if ws.status() != 0:
+        raise SystemExit("bench.py: a group-wait decode step gave up waiting")
+    per_launch = algorithmic_bytes(B, Hq, Hkv, d, n, bud, 4 if w.dtype == "f32" else 2)
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline([r[0] for r in reps[:4]], w.replace(layers=1), n, bud,
+                           args.cpu_seconds)
+    result_line(
+        f"decode-step latency + achieved HBM GB/s, {w.name}, budget {bud}, 1 GPU",
+        w, B, us * 1e-3, K, args.warmup,
+        {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+         "n_ctx": n, "budget": bud, "replicas_cycled": R, "timing": "hip-graph replay"},
+        "adamas_decode_step (one layer)", per_launch, us, stream_read_gbs(dev),
+        {"launch_us": {"mean": round(us, 3), "p10": round(float(np.percentile(per, 10)), 3),
+                       "p50": round(float(np.percentile(per, 50)), 3),
+                       "p90": round(float(np.percentile(per, 90)), 3)},
+         "eager_event_launch_us": round(launch_us, 3),
+         "decode_path": adamas.decode_path(B, Hq, Hkv, n, bud, d)}, cpu)
 
 
 def bench_gqa(args, dev):
