@@ -25,7 +25,7 @@ __all__ = [
     "OP_SPARSE_ATTEND", "OP_DECODE_STEP", "DECODE_AUTO", "DECODE_LAST_ARRIVAL",
     "DECODE_GROUP_WAIT", "DECODE_SPLIT", "WS_CTRL_BYTES", "WS_STATUS_OFFSET", "ROTATE_OFF",
     "ROTATE_F32", "ROTATE_F16", "GroupWaitGaveUp", "set_wait_polls", "wait_polls",
-    "DEFAULT_WAIT_POLLS", "PhaseRecorder",
+    "DEFAULT_WAIT_POLLS", "PhaseRecorder", "decode_step_static", "STATIC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -112,6 +112,11 @@ def load(variant: str | None = None):
     lib.adamas_decode_path.argtypes = [i32, i32, i32, i64, i32, i32]
     lib.adamas_set_wait_polls.argtypes = [ctypes.c_uint32]
     lib.adamas_set_wait_polls.restype = i32
+    lib.adamas_decode_step_static.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32,
+                                              f32, P, P, P]
+    lib.adamas_decode_step_static.restype = i32
+    lib.adamas_static_scratch_need.argtypes = [i32, i32, i32, i64, i32, i32]
+    lib.adamas_static_scratch_need.restype = sz
     lib.adamas_wait_polls.argtypes = []
     lib.adamas_wait_polls.restype = ctypes.c_uint32
     lib.adamas_phase_stamps_built.restype = i32
@@ -419,6 +424,30 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0, o
     if check:
         (stream if stream is not None else torch.cuda.current_stream(q.device)).synchronize()
         _ws_for(q.device, ws).check()
+    return out
+
+
+STATIC_SCRATCH_BYTES = 16 << 20   # ADAMAS_STATIC_SCRATCH_BYTES
+
+
+def decode_step_static(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,
+                       out=None, idx_out=None, stream=None) -> torch.Tensor:
+    """decode_step without a workspace (adamas_decode_step_static): the library's
+    static per-device scratch, for callers that cannot allocate.  Calls that
+    may overlap on one device race.  out / idx_out are the caller's."""
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    if k.dtype != q.dtype or v.dtype != q.dtype or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q, k, v must share dtype; k and v share shape")
+    if tuple(k_codes.shape) != (B, Hkv, cap, d // 4) or k_codes.dtype != torch.uint8:
+        raise ValueError("k_codes must be uint8 [B][Hkv][cap][d/4]")
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().adamas_decode_step_static(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(k_codes, "k_codes"),
+        _dtype_code(q), B, Hq, Hkv, d, cap, n_ctx, budget, float(scale), _dev_ptr(out, "out"),
+        _dev_ptr(idx_out, "idx_out"), _stream(q, stream))
+    _check(st, "adamas_decode_step_static")
     return out
 
 

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "adamas.h"
@@ -328,11 +329,11 @@ extern "C" {
 
 namespace {
 
-int decode_step_impl(const void* q, const void* k, const void* v, const uint8_t* k_codes,
-                     int dtype, int B, int Hq, int Hkv, int head_dim,
-                     int64_t cap, int64_t n_ctx, int budget, int n_sink, int n_recent,
-                     float scale, void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
+// Argument checks of a decode step (everything but the workspace).
+int check_decode_args(const void* q, const void* k, const void* v, const uint8_t* k_codes,
+                      int dtype, int B, int Hq, int Hkv, int head_dim, int64_t cap,
+                      int64_t n_ctx, int budget, int n_sink, int n_recent, float scale,
+                      const void* out, const int32_t* idx_out) {
   if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || cap < 1 || n_ctx < 1 || n_ctx > cap ||
       budget < 1 || !isfinite(scale) || n_sink < 0 || n_recent < 0)
@@ -343,12 +344,26 @@ int decode_step_impl(const void* q, const void* k, const void* v, const uint8_t*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_codes) || !aligned16(out))
     return ADAMAS_ERR_INVALID;
   if (idx_out != nullptr && !aligned16(idx_out)) return ADAMAS_ERR_INVALID;
+  return ADAMAS_OK;
+}
+
+// no_group_wait: never the group-wait schedule (the workspace then only has
+// to hold the last-arrival or split layout, DecodePlan::total).
+int decode_step_impl(const void* q, const void* k, const void* v, const uint8_t* k_codes,
+                     int dtype, int B, int Hq, int Hkv, int head_dim,
+                     int64_t cap, int64_t n_ctx, int budget, int n_sink, int n_recent,
+                     float scale, void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                     hipStream_t stream, bool no_group_wait = false) {
+  const int chk = check_decode_args(q, k, v, k_codes, dtype, B, Hq, Hkv, head_dim, cap, n_ctx,
+                                    budget, n_sink, n_recent, scale, out, idx_out);
+  if (chk != ADAMAS_OK) return chk;
   if (ws == nullptr || !aligned16(ws)) return ADAMAS_ERR_WORKSPACE;
   // the documented requirement covers both schedules, whichever runs
-  if (ws_bytes < adamas_workspace_bytes(ADAMAS_OP_DECODE_STEP, B, Hq, Hkv, n_ctx, budget,
-                                        head_dim))
+  if (!no_group_wait && ws_bytes < adamas_workspace_bytes(ADAMAS_OP_DECODE_STEP, B, Hq, Hkv,
+                                                          n_ctx, budget, head_dim))
     return ADAMAS_ERR_WORKSPACE;
-  const int mode = g_decode_mode.load(std::memory_order_relaxed);
+  int mode = g_decode_mode.load(std::memory_order_relaxed);
+  if (no_group_wait && mode == ADAMAS_DECODE_GROUP_WAIT) mode = ADAMAS_DECODE_AUTO;
   uint8_t* w = static_cast<uint8_t*>(ws);
   const int G = Hq / Hkv;
   const bool bf = dtype == ADAMAS_BF16;
@@ -358,7 +373,8 @@ int decode_step_impl(const void* q, const void* k, const void* v, const uint8_t*
   // the attention (it would need a second launch) or would select from too
   // many candidates in one workgroup; failing that, the separate selection
   // for the latter
-  if (mode == ADAMAS_DECODE_GROUP_WAIT || (mode == ADAMAS_DECODE_AUTO && (!p.fuse || many))) {
+  if (!no_group_wait &&
+      (mode == ADAMAS_DECODE_GROUP_WAIT || (mode == ADAMAS_DECODE_AUTO && (!p.fuse || many)))) {
     const GroupPlan gp = plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, device_capacity());
     if (gp.ok) {
       if (ws_bytes < gp.total) return ADAMAS_ERR_WORKSPACE;
@@ -569,6 +585,77 @@ int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int he
     return ADAMAS_DECODE_GROUP_WAIT;
   if (mode == ADAMAS_DECODE_GROUP_WAIT) return -ADAMAS_ERR_UNSUPPORTED;
   return many && p.split_ok ? ADAMAS_DECODE_SPLIT : ADAMAS_DECODE_LAST_ARRIVAL;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of adamas_decode_step_static: one copy per device, resident from
+// the library's load on that device until the process ends.  Host code never
+// uses this name as an address (in host code it is a stand-in for the
+// symbol); static_scratch() resolves the device address once per device.
+static __device__ __align__(256) uint8_t scratch[ADAMAS_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+__global__ void k_zero16(uint4* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The current device's scratch address, or null on a runtime error.  The
+// first call on a device resolves the symbol and enqueues on `stream` a
+// small kernel that zeroes the control bytes (the later calls rely on every
+// completed call leaving them zero).
+uint8_t* static_scratch(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  uint8_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p != nullptr) return p;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+    return nullptr;
+  k_zero16<<<16, 256, 0, stream>>>(static_cast<uint4*>(addr), ADAMAS_WS_CTRL_BYTES / 16);
+  if (hipGetLastError() != hipSuccess) return nullptr;
+  p = static_cast<uint8_t*>(addr);
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int adamas_decode_step_static(const void* q, const void* k, const void* v,
+                              const uint8_t* k_codes, int dtype, int B, int Hq, int Hkv,
+                              int head_dim, int64_t cap, int64_t n_ctx, int budget, float scale,
+                              void* out, int32_t* idx_out, hipStream_t stream) {
+  // every check before anything is resolved or enqueued: the arguments, then
+  // the shape's scratch against the static buffer
+  const int chk = check_decode_args(q, k, v, k_codes, dtype, B, Hq, Hkv, head_dim, cap, n_ctx,
+                                    budget, 0, 0, scale, out, idx_out);
+  if (chk != ADAMAS_OK) return chk;
+  if (plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).total > ADAMAS_STATIC_SCRATCH_BYTES)
+    return ADAMAS_ERR_WORKSPACE;
+  uint8_t* w = static_scratch(stream);
+  if (w == nullptr) return ADAMAS_ERR_DEVICE;
+  return decode_step_impl(q, k, v, k_codes, dtype, B, Hq, Hkv, head_dim, cap, n_ctx, budget, 0,
+                          0, scale, out, idx_out, w, ADAMAS_STATIC_SCRATCH_BYTES, stream, true);
+}
+
+size_t adamas_static_scratch_need(int B, int Hq, int Hkv, int64_t n_ctx, int budget,
+                                  int head_dim) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_ctx < 1 || budget < 1 ||
+      budget > kMaxBudget || !valid_dim(head_dim) || Hq / Hkv > kMaxG)
+    return 0;
+  return plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).total;
 }
 
 size_t adamas_stream_read_blocks(size_t bytes) {

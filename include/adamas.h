@@ -362,6 +362,34 @@ size_t adamas_phase_buffer_bytes(void);
 int adamas_set_phase_buffer(void *buf, size_t bytes);
 int adamas_wall_clock_khz(void);
 
+/*
+ * adamas_decode_step for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument; the call allocates nothing and calls no allocating
+ * routine.  Its scratch (candidate lists, arrival counters, partial results)
+ * is a static device buffer of ADAMAS_STATIC_SCRATCH_BYTES inside the
+ * library, one copy per device, held from the library's load until the
+ * process ends; the first call on a device resolves its address and enqueues
+ * a small kernel that zeroes its control bytes.  All calls on one device
+ * share that buffer: calls that may overlap in time on one device (several
+ * streams, several host threads) race and must not be made.  It never takes
+ * the group-wait schedule (adamas_set_decode_mode's GROUP_WAIT is read as
+ * AUTO), so there is no status word to check.  Arguments, layouts, results
+ * and errors are those of adamas_decode_step; a shape whose scratch
+ * (adamas_static_scratch_need) exceeds ADAMAS_STATIC_SCRATCH_BYTES returns
+ * ADAMAS_ERR_WORKSPACE before anything is enqueued, and a failure to resolve
+ * the buffer ADAMAS_ERR_DEVICE.
+ */
+#define ADAMAS_STATIC_SCRATCH_BYTES (16u << 20)
+int adamas_decode_step_static(const void *q, const void *k, const void *v,
+                              const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
+                              int head_dim, int64_t cap, int64_t n_ctx, int budget, float scale,
+                              void *out, int32_t *idx_out, hipStream_t stream);
+
+/* Scratch bytes adamas_decode_step_static needs for a shape (0 if invalid). */
+size_t adamas_static_scratch_need(int B, int Hq, int Hkv, int64_t n_ctx, int budget,
+                                  int head_dim);
+
 /* Workspace bytes needed by `op` for the given shape (0 for invalid shapes). */
 size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx,
                               int budget, int head_dim);
