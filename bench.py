@@ -385,7 +385,9 @@ PHASE_NAMES = {
                6: "final: candidates loaded", 7: "final: threshold", 8: "final: selected",
                9: "rows gathered + weighted", 10: "partials merged", 11: "final: out stored",
                12: "merged out stored", 13: "rows gathered, last wavefront",
-               14: "slot sums, last wavefront"},
+               14: "slot sums, last wavefront", 16: "chunk: thresholds (grouped heads)",
+               17: "chunk: masks, last wavefront", 18: "chunk: prefix over workgroup",
+               19: "chunk: tokens emitted, last wavefront"},
     "split": {0: "entry", 1: "threshold", 2: "placement", 3: "tokens copied",
               9: "rows gathered + weighted", 10: "partials merged", 11: "partial handed over",
               12: "merged out stored", 13: "rows gathered, last wavefront",

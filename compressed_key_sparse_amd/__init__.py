@@ -341,7 +341,7 @@ def set_rotation(on) -> None:
 class PhaseRecorder:
     """Phase timestamps of the measurement build (load(variant="phases")):
     a device buffer the kernels write the wall clock into at marked points.
-    read() -> numpy int64 [3 regions][8192 workgroups][16 slots] (0 = not
+    read() -> numpy int64 [3 regions][8192 workgroups][slots] (0 = not
     reached) after synchronising; clear() zeroes it; ticks_per_us the clock."""
 
     REGIONS = ("decode", "split", "attend")
@@ -361,7 +361,7 @@ class PhaseRecorder:
 
     def read(self):
         torch.cuda.synchronize(self.buf.device)
-        return self.buf.view(3, 8192, 16).cpu().numpy()
+        return self.buf.view(3, 8192, -1).cpu().numpy()
 
     def close(self):
         load().adamas_set_phase_buffer(None, 0)

@@ -47,7 +47,7 @@ constexpr bool kPhases = true;
 #else
 constexpr bool kPhases = false;
 #endif
-constexpr int kPhaseSlots = 16;
+constexpr int kPhaseSlots = 24;
 constexpr int kPhaseMaxWorkgroups = 8192;  // per kernel region
 enum PhaseRegion { kPhaseDecode = 0, kPhaseSplit = 1, kPhaseAttend = 2, kPhaseRegions = 3 };
 struct PhaseStamps {
@@ -719,7 +719,7 @@ ADM_DEV void key_masks(const uint32_t* ws, int t, uint32_t& ge, uint32_t& gt) {
 constexpr int kCompactTpt = 16;
 template <int NT, class Emit, int TPT = kCompactTpt>
 ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t quota,
-                               uint32_t* s_tmp, Emit&& emit) {
+                               uint32_t* s_tmp, Emit&& emit, const PhaseStamps* ps = nullptr) {
   static_assert(TPT % 8 == 0 && TPT <= 16, "whole 16-byte reads, one 16-bit mask");
   const int t0 = threadIdx.x * TPT;
   uint32_t ltm = 0, eqm = 0;  // bit i: token t0+i is below / at the threshold
@@ -740,7 +740,9 @@ ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t
   }
   uint32_t tot;
   const uint32_t mine = (uint32_t)__popc(ltm) | ((uint32_t)__popc(eqm) << 16);
+  if (ps) ps->mark_last_wave(17);  // masks done
   const uint32_t ex = block_scan_incl<NT>(mine, s_tmp, &tot) - mine;
+  if (ps) ps->mark(18);  // prefix over the workgroup
   uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
   // visit only the flagged tokens, in order (a small fraction of the chunk)
   for (uint32_t m = ltm | eqm; m != 0; m &= m - 1) {
@@ -757,6 +759,7 @@ ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t
       ++eqb;
     }
   }
+  if (ps) ps->mark_last_wave(19);  // tokens emitted
   const uint32_t eq_all = tot >> 16;
   return (tot & 0xffffu) + (eq_all < quota ? eq_all : quota);
 }
@@ -772,7 +775,8 @@ ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t
 template <int NT, int NB, int G, int TPT = kCompactTpt>
 ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* sdist, int chunk,
                                  int valid, uint32_t kc, uint32_t* out, int kpad,
-                                 uint32_t* s_thr, uint32_t* s_sums) {
+                                 uint32_t* s_thr, uint32_t* s_sums,
+                                 const PhaseStamps* ps = nullptr) {
   constexpr int NW = NT / kWave, BPL = (NB + kWave - 1) / kWave;
   static_assert(G <= NW, "one wavefront per head finds its threshold");
   static_assert(TPT % 8 == 0 && TPT <= 16, "whole 16-byte reads, one 16-bit mask");
@@ -809,6 +813,7 @@ ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* 
     if ((uint32_t)j >= kc) out[i] = 0xFFFFFFFFu;
   }
   lds_sync();
+  if (ps) ps->mark(16);  // thresholds found
   // (2) this thread's TPT tokens: per head, masks of keys below / at t_g
   const int t0 = threadIdx.x * TPT;
   const int nv = valid - t0;
@@ -832,6 +837,7 @@ ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* 
     eqm[g] = ge & ~gt & vmask;
     mine[g] = (uint32_t)__popc(ltm[g]) | ((uint32_t)__popc(eqm[g]) << 16);
   }
+  if (ps) ps->mark_last_wave(17);  // masks of every head done
   // (3) prefix counts over the workgroup for every head with one barrier
   uint32_t incl[G];
 #pragma unroll
@@ -840,6 +846,7 @@ ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* 
     if (lane == kWave - 1) s_sums[wid * G + g] = incl[g];
   }
   lds_sync();
+  if (ps) ps->mark(18);  // prefix over the workgroup
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     uint32_t pre = 0;
@@ -863,6 +870,7 @@ ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* 
       }
     }
   }
+  if (ps) ps->mark_last_wave(19);  // tokens emitted
   lds_sync();
 }
 
@@ -872,12 +880,12 @@ ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* 
 template <int NT, int TPT = kCompactTpt, class OnKept>
 ADM_DEV void chunk_compact(const uint16_t* sdist, int valid, Threshold thr, uint32_t quota,
                            uint32_t* out, int kept, int pad_to, uint32_t* s_tmp,
-                           OnKept&& on_kept) {
+                           OnKept&& on_kept, const PhaseStamps* ps = nullptr) {
   auto emit = [&](uint32_t pos, uint32_t t, uint32_t d) {
     out[pos] = (d << 16) | t;
     on_kept(t, d);
   };
-  chunk_collect<NT, decltype(emit)&, TPT>(sdist, valid, thr.t, quota, s_tmp, emit);
+  chunk_collect<NT, decltype(emit)&, TPT>(sdist, valid, thr.t, quota, s_tmp, emit, ps);
   for (int j = kept + (int)threadIdx.x; j < pad_to; j += NT) out[j] = 0xFFFFFFFFu;
 }
 

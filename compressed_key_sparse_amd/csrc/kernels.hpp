@@ -876,7 +876,7 @@ void k_decode(
   if constexpr (G >= 2) {
     if (n_stage == G) {
       chunk_compact_heads<NT, NB, G>(shist, NBP, sdist, chunk, valid, (uint32_t)kc, sstage, kpad,
-                                     s_fused, s_fused + 2 * G);
+                                     s_fused, s_fused + 2 * G, &ps);
       ps.mark(4);
       for (int g = 0; g < G; ++g) {
         const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
@@ -891,7 +891,7 @@ void k_decode(
       const Threshold thr = find_threshold<NT>(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
       ps.mark(3);
       chunk_compact<NT>(sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad,
-                        s_tmp, [](uint32_t, uint32_t) {});
+                        s_tmp, [](uint32_t, uint32_t) {}, &ps);
       lds_sync();
       ps.mark(4);
       lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);

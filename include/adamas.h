@@ -350,7 +350,7 @@ int adamas_decode_paged_step(const void *q, const void *k_new, const void *v_new
  * wall clock (adamas_wall_clock_khz ticks per millisecond) at marked points,
  * into a caller-owned device buffer of adamas_phase_buffer_bytes() bytes:
  * u64 [3 kernel regions: decode, split selection, attention][8192
- * workgroups][16 slots], 0 where a slot was not reached; each launch
+ * workgroups][24 slots], 0 where a slot was not reached; each launch
  * overwrites its region.  adamas_set_phase_buffer(NULL, 0) stops recording.
  * In the product build adamas_phase_stamps_built() is 0 and
  * adamas_set_phase_buffer returns ADAMAS_ERR_UNSUPPORTED; ADAMAS_ERR_INVALID
