@@ -23,7 +23,7 @@ constexpr int kTmpWaveSums = 0;   // [0, 16): per-wave partial sums
 constexpr int kTmpThrT = 16;      // threshold bin
 constexpr int kTmpThrLt = 17;     // count below the threshold
 constexpr int kTmpFlag = 20;      // "last arrival" flag
-constexpr int kTmpWords = 32;
+constexpr int kTmpStamps = 32;    // phase stamps (measurement build only)
 
 // Workgroup barrier for LDS exchanges only.  __syncthreads() also orders
 // global memory, which on this target waits for every outstanding vector
@@ -38,38 +38,54 @@ ADM_DEV void lds_sync() {
 // ------------------------------------------------------------ phase stamps
 // A measurement build (compiled with -DADAMAS_PHASES=1, libadamas_phases.so)
 // records, per workgroup, the device's constant-rate wall clock at marked
-// points of a kernel: thread 0 stores the counter straight to a caller-given
-// buffer (no registers held, no barriers added), so the kernel's schedule is
-// the product's.  The product build compiles every mark away.  Layout:
-// [kernel region][workgroup][kPhaseSlots] u64, 0 = not reached.
+// points of a kernel.  Thread 0 keeps the stamps in LDS (s_tmp[kTmpStamps,
+// +2*kPhaseSlots)) and copies them to the caller's buffer when the
+// workgroup exits (flush), so no global store is in flight when the kernel's
+// own code waits for its memory operations; the product build compiles every
+// mark away and reserves no LDS for them.  Buffer layout: [kernel
+// region][workgroup][kPhaseSlots] u64, 0 = not reached.
 #if defined(ADAMAS_PHASES) && ADAMAS_PHASES
 constexpr bool kPhases = true;
 #else
 constexpr bool kPhases = false;
 #endif
 constexpr int kPhaseSlots = 24;
+constexpr int kTmpWords = kTmpStamps + (kPhases ? 2 * kPhaseSlots : 0);
 constexpr int kPhaseMaxWorkgroups = 8192;  // per kernel region
 enum PhaseRegion { kPhaseDecode = 0, kPhaseSplit = 1, kPhaseAttend = 2, kPhaseRegions = 3 };
 struct PhaseStamps {
-  uint64_t* row;  // this workgroup's slots, or null
-  ADM_DEV PhaseStamps(uint64_t* buf, int region) : row(nullptr) {
+  uint64_t* row;  // this workgroup's slots in the caller's buffer, or null
+  uint64_t* lds;  // the stamps while the workgroup runs
+  ADM_DEV PhaseStamps(uint64_t* buf, int region, uint32_t* s_tmp) : row(nullptr), lds(nullptr) {
     if constexpr (kPhases) {
       const int64_t wg = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
-      if (buf != nullptr && wg < kPhaseMaxWorkgroups)
+      if (buf != nullptr && wg < kPhaseMaxWorkgroups) {
         row = buf + ((int64_t)region * kPhaseMaxWorkgroups + wg) * kPhaseSlots;
+        lds = reinterpret_cast<uint64_t*>(s_tmp + kTmpStamps);
+        if (threadIdx.x == 0)
+          for (int s = 0; s < kPhaseSlots; ++s) lds[s] = 0;
+      }
     }
   }
   ADM_DEV void mark(int slot) const {
     if constexpr (kPhases) {
-      if (row != nullptr && threadIdx.x == 0) row[slot] = wall_clock64();
+      if (lds != nullptr && threadIdx.x == 0) lds[slot] = wall_clock64();
     }
   }
-  // the latest of the workgroup's wavefronts to reach this point
+  // the latest of the workgroup's wavefronts to reach this point (slots
+  // marked this way must be followed by a workgroup barrier before flush)
   ADM_DEV void mark_last_wave(int slot) const {
     if constexpr (kPhases) {
-      if (row != nullptr && (threadIdx.x & (kWave - 1)) == 0)
-        atomicMax(reinterpret_cast<unsigned long long*>(row + slot),
+      if (lds != nullptr && (threadIdx.x & (kWave - 1)) == 0)
+        atomicMax(reinterpret_cast<unsigned long long*>(lds + slot),
                   (unsigned long long)wall_clock64());
+    }
+  }
+  // copy the stamps out; at every exit of the workgroup
+  ADM_DEV void flush() const {
+    if constexpr (kPhases) {
+      if (row != nullptr && threadIdx.x == 0)
+        for (int s = 0; s < kPhaseSlots; ++s) row[s] = lds[s];
     }
   }
 };

@@ -538,13 +538,13 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
     float* __restrict__ part, uint32_t* __restrict__ counters, void* __restrict__ out,
     PageArgs pa = {}, uint64_t* __restrict__ stamps = nullptr) {
   constexpr int NT = kAttendThreads, NW = NT / kWave, PW = 2 + D;
-  // phase stamps: 0 entry, 9-10 inside attend_rows, 11 partial handed over,
-  // 12 merged output stored
-  const PhaseStamps ps(stamps, kPhaseAttend);
-  ps.mark(0);
   constexpr int PWP = (PW + 3) & ~3;  // partial rows padded to 16 bytes
   constexpr int kMergeTile = 32;
   __shared__ uint32_t s_tmp[kTmpWords];
+  // phase stamps: 0 entry, 9-10 inside attend_rows, 11 partial handed over,
+  // 12 merged output stored
+  const PhaseStamps ps(stamps, kPhaseAttend, s_tmp);
+  ps.mark(0);
   __shared__ float s_part[NW * PW + kAttendRowsPerBatch];
   __shared__ __align__(16) float s_res[PWP];
   __shared__ __align__(16) float s_tile[kMergeTile * PWP];
@@ -563,6 +563,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
       const float L = s_res[1];
       store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? s_res[2 + threadIdx.x] / L : 0.0f);
     }
+    ps.flush();
     return;
   }
   float* mine = part + (row * S + s) * PWP;
@@ -570,7 +571,10 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
                     PWP);
   const bool last = arrive_last<NT>(&counters[row], S, s_tmp);
   ps.mark(11);
-  if (!last) return;
+  if (!last) {
+    ps.flush();
+    return;
+  }
   const float* pp = part + row * S * PWP;
   float M = -INFINITY, L = 0.0f, O = 0.0f;
   for (int t0 = 0; t0 < S; t0 += kMergeTile) {
@@ -595,6 +599,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(
   if (threadIdx.x < D) store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? O / L : 0.0f);
   if (threadIdx.x == 0) counters[row] = 0;
   ps.mark(12);
+  ps.flush();
 }
 
 // --------------------------------------------------------- §5.2 selection
@@ -692,14 +697,14 @@ void k_decode(
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), W = D / 16;
   constexpr int E = D / 64, kLanesPerWord = 16 / E, PW = 2 + D;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
   // phase stamps (measurement build only): 0 entry, 1 query encoded, 2 scan
   // end, 3 chunk threshold, 4 candidates staged, 5 handed over; final
   // workgroup: 6-7 inside final_select, 8 selection done, 9-10 inside
   // attend_rows, 11 output stored
-  const PhaseStamps ps(stamps, kPhaseDecode);
+  const PhaseStamps ps(stamps, kPhaseDecode, s_tmp);
   ps.mark(0);
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
   uint8_t* region = smem + kTmpWords * 4;
   // phase 1 (scan) layout
   uint32_t* sq = reinterpret_cast<uint32_t*>(region);  // G query rows, then the appended key
@@ -780,6 +785,7 @@ void k_decode(
             for (int j = threadIdx.x; j < budget; j += NT) idx[row * budget + j] = -1;
         }
       }
+      ps.flush();
       return;  // no rows of this sequence in this chunk
     }
   }
@@ -899,11 +905,15 @@ void k_decode(
   }
   if (chist != nullptr) {  // k_split_select takes it from here
     ps.mark(5);
+    ps.flush();
     return;
   }
   const bool last = arrive_last<NT>(&counters[b * Hkv + hkv], active, s_tmp);
   ps.mark(5);
-  if (!last) return;
+  if (!last) {
+    ps.flush();
+    return;
+  }
   const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap;
   // paged: the gathers below look up the sequence's page table; its row is
   // loaded now (in flight during the selection) and kept in LDS
@@ -946,6 +956,7 @@ void k_decode(
   }
   if (threadIdx.x == 0) counters[b * Hkv + hkv] = 0;
   ps.mark(11);
+  ps.flush();
 }
 
 // ------------------------------------- decode step, selection on its own
@@ -994,12 +1005,12 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
     int32_t* __restrict__ idx, SplitAttend fa) {
   constexpr int NT = kSplitThreads, NW = NT / kWave, EPL = kSplitEntriesPerLane;
   constexpr int PW = 2 + D, PWP = (PW + 3) & ~3;
-  // phase stamps: 0 entry, 1 threshold, 2 placement done, 3 tokens copied,
-  // 9-10 inside attend_rows, 11 partial handed over, 12 merged output stored
-  const PhaseStamps ps(fa.stamps, kPhaseSplit);
-  ps.mark(0);
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
+  // phase stamps: 0 entry, 1 threshold, 2 placement done, 3 tokens copied,
+  // 9-10 inside attend_rows, 11 partial handed over, 12 merged output stored
+  const PhaseStamps ps(fa.stamps, kPhaseSplit, s_tmp);
+  ps.mark(0);
   uint32_t* s_hist = s_tmp + kTmpWords;
   uint32_t* s_first = s_hist + kNbinsPadded(D);  // first output position of the chunk's tokens
   uint32_t* s_take = s_first + ncp;               // (count below t) << 16 | ties taken
@@ -1192,7 +1203,10 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
       pos += took;
     }
   }
-  if (!fused) return;
+  if (!fused) {
+    ps.flush();
+    return;
+  }
   // §6 over this segment's rows, then the log-sum-exp merge of the segments
   lds_sync();
   ps.mark(3);
@@ -1207,13 +1221,17 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
       const float L = s_res[1];
       store_out<BF>(fa.out, row * D + threadIdx.x, L > 0.0f ? s_res[2 + threadIdx.x] / L : 0.0f);
     }
+    ps.flush();
     return;
   }
   lds_to_shared<NT>(reinterpret_cast<uint32_t*>(fa.part + (row * S + blockIdx.x) * PWP),
                     reinterpret_cast<const uint32_t*>(s_res), PWP);
   const bool last = arrive_last<NT>(&fa.counters[row], S, s_tmp);
   ps.mark(11);
-  if (!last) return;
+  if (!last) {
+    ps.flush();
+    return;
+  }
   // merge: partials staged through LDS (the row list is free now)
   float* s_tile = reinterpret_cast<float*>(s_rows);
   constexpr int kTile = kSplitFuseRows / PWP;
@@ -1241,6 +1259,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
   if ((int)threadIdx.x < D) store_out<BF>(fa.out, row * D + threadIdx.x, L > 0.0f ? O / L : 0.0f);
   if (threadIdx.x == 0) fa.counters[row] = 0;
   ps.mark(12);
+  ps.flush();
 }
 
 // ------------------------------------------ fused decode step, group wait
@@ -1266,11 +1285,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     uint32_t* __restrict__ arrive_part, uint32_t* __restrict__ status, uint32_t max_polls,
     int32_t* __restrict__ idx, void* __restrict__ out, int n_sink, int n_recent, int rotate,
     uint64_t* __restrict__ stamps) {
-  // phase stamps: 0 entry, 2 scan end, 3 histograms published, 4 group
-  // complete, 5 selection done, 9-10 inside attend_rows, 11 partial handed
-  // over, 12 merged output stored
-  const PhaseStamps ps(stamps, kPhaseDecode);
-  ps.mark(0);
+
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), NBH = kNbinsHist(D), W = D / 16;
   static_assert(G <= kTmpWords - kTmpGroupCounts, "per-head counts live in s_tmp");
@@ -1278,6 +1293,11 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* s_tmp = reinterpret_cast<uint32_t*>(smem);
   uint32_t* s_sums = s_tmp + kTmpWords;
+  // phase stamps: 0 entry, 2 scan end, 3 histograms published, 4 group
+  // complete, 5 selection done, 9-10 inside attend_rows, 11 partial handed
+  // over, 12 merged output stored
+  const PhaseStamps ps(stamps, kPhaseDecode, s_tmp);
+  ps.mark(0);
   uint32_t* sq = s_sums + 32;
   uint32_t* shist = sq + G * W;
   uint32_t* s_tot = shist + G * NBP;  // group counts per bin: all chunks, chunks before
@@ -1415,7 +1435,10 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   }
   const bool last = arrive_last<NT>(&arrive_part[grp], n_chunks, s_tmp);
   ps.mark(11);
-  if (!last) return;
+  if (!last) {
+    ps.flush();
+    return;
+  }
   for (int g = 0; g < G; ++g) {
     const int64_t row = row0 + g;
     float M = -INFINITY, L = 0.0f, O = 0.0f;
@@ -1446,6 +1469,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     arrive_part[grp] = 0;
   }
   ps.mark(12);
+  ps.flush();
 }
 
 // ---------------------------------------------------------- reference read
