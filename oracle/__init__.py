@@ -71,6 +71,10 @@ def _load():
     lib.ora_decode_step_ex.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32, i64,
                                        i64, i32, f64, P, P, P]
     lib.ora_encode_vec_f32_rot.argtypes = [P, i32, i32, P, P, P]
+    lib.ora_encode_vec_f32_ex.argtypes = [P, i32, i32, ctypes.c_float, P, P, P]
+    lib.ora_encode_keys_ex.argtypes = [P, i32, i32, i32, i64, i32, P, i64, i64, i32, P, i32]
+    lib.ora_decode_step_alpha.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32,
+                                          i64, i64, i32, P, i32, f64, P, P, P]
     lib.ora_encode_keys_rot.argtypes = [P, i32, i32, i32, i64, i32, P, i64, i64, i32]
     lib.ora_sparse_attend.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f64, P, P]
     lib.ora_sparse_attend_ex.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f64, P,
@@ -114,15 +118,28 @@ def hadamard_orthonormal_f64(x: np.ndarray) -> np.ndarray:
     return y
 
 
-def encode_vec(x: np.ndarray, rotate: int = True):
+def _alpha_table(alpha):
+    """None -> (null, 0); a sequence of per-head-group bucketing fractions -> float32 array."""
+    if alpha is None:
+        return None, 0
+    a = np.ascontiguousarray(np.asarray(alpha, np.float32).reshape(-1))
+    assert a.size >= 1
+    return a, int(a.size)
+
+
+def encode_vec(x: np.ndarray, rotate: int = True, alpha: float | None = None):
     """One fp32 vector -> (packed bytes, rotated values, codes); rotate=False
-    buckets the vector as it is, rotate=2 rotates in binary16."""
+    buckets the vector as it is, rotate=2 rotates in binary16; alpha (default
+    0.5) places the outer thresholds at -alpha*a and +alpha*a."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     d = x.shape[-1]
     packed = np.empty(d // 4, np.uint8)
     y = np.empty(d, np.float32)
     codes = np.empty(d, np.int32)
-    if rotate is True or rotate == 1:
+    if alpha is not None:
+        _load().ora_encode_vec_f32_ex(_ptr(x), d, int(rotate), float(alpha), _ptr(packed), _ptr(y),
+                                      _ptr(codes))
+    elif rotate is True or rotate == 1:
         _load().ora_encode_vec_f32(_ptr(x), d, _ptr(packed), _ptr(y), _ptr(codes))
     else:
         _load().ora_encode_vec_f32_rot(_ptr(x), d, int(rotate), _ptr(packed), _ptr(y),
@@ -136,8 +153,9 @@ def f64_to_f16_value(x: float) -> float:
 
 
 def encode_keys(x: np.ndarray, codes: np.ndarray | None = None, cap: int | None = None,
-                pos: int = 0, rotate: bool = True) -> np.ndarray:
-    """x[batch][heads][n][d] -> codes[batch][heads][cap][d/4], rows [pos, pos+n)."""
+                pos: int = 0, rotate: bool = True, alpha=None) -> np.ndarray:
+    """x[batch][heads][n][d] -> codes[batch][heads][cap][d/4], rows [pos, pos+n).
+    alpha: per-head bucketing fractions, head h uses alpha[h % len(alpha)]."""
     x = np.ascontiguousarray(x)
     batch, heads, n, d = x.shape
     if cap is None:
@@ -145,7 +163,11 @@ def encode_keys(x: np.ndarray, codes: np.ndarray | None = None, cap: int | None 
     if codes is None:
         codes = np.zeros((batch, heads, cap, d // 4), np.uint8)
     assert codes.shape == (batch, heads, cap, d // 4) and codes.dtype == np.uint8
-    if rotate is True or rotate == 1:
+    if alpha is not None:
+        a, na = _alpha_table(alpha)
+        _load().ora_encode_keys_ex(_ptr(x), _dtype_tag(x), batch, heads, n, d, _ptr(codes), cap,
+                                   pos, int(rotate), _ptr(a), na)
+    elif rotate is True or rotate == 1:
         _load().ora_encode_keys(_ptr(x), _dtype_tag(x), batch, heads, n, d, _ptr(codes), cap, pos)
     else:
         _load().ora_encode_keys_rot(_ptr(x), _dtype_tag(x), batch, heads, n, d, _ptr(codes), cap,
@@ -223,8 +245,10 @@ def attend_error_scale(q, k, v, idx, scale: float = 0.0):
 
 
 def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,
-                n_sink: int = 0, n_recent: int = 0, rotate: bool = True):
-    """Full step for one layer -> (out, out64, idx)."""
+                n_sink: int = 0, n_recent: int = 0, rotate: bool = True, alpha=None):
+    """Full step for one layer -> (out, out64, idx).  alpha: the per-KV-head
+    bucketing table the keys were encoded with (query head hq uses its KV
+    head's entry)."""
     q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
     k_codes = np.ascontiguousarray(k_codes, np.uint8)
     dt = _dtype_tag(q)
@@ -233,7 +257,12 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,
     out = np.empty((B, Hq, d), q.dtype)
     out64 = np.empty((B, Hq, d), np.float64)
     idx = np.empty((B, Hq, budget), np.int32)
-    if not (rotate is True or rotate == 1):
+    if alpha is not None:
+        a, na = _alpha_table(alpha)
+        _load().ora_decode_step_alpha(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d,
+                                      cap, n_ctx, budget, n_sink, n_recent, int(rotate), _ptr(a),
+                                      na, float(scale), _ptr(out), _ptr(out64), _ptr(idx))
+    elif not (rotate is True or rotate == 1):
         _load().ora_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(k_codes), dt, B, Hq, Hkv, d,
                                    cap, n_ctx, budget, n_sink, n_recent, int(rotate),
                                    float(scale), _ptr(out), _ptr(out64), _ptr(idx))

@@ -198,9 +198,13 @@ static void ora_pack(const int *codes, int d, uint8_t *out)
  * rotated values and codes when the pointers are non-null (for tests). */
 /* rotate == 0 skips §2.1: the vector is bucketed as it is (the ablation row
  * "2-bit quantisation only" of the article's §3.2 table); rotate == 2 runs
- * the transform in binary16 (ora_fwht_f16). */
-void ora_encode_vec_f32_rot(const float *x, int d, int rotate, uint8_t *packed, float *y_out,
-                            int *codes_out)
+ * the transform in binary16 (ora_fwht_f16).
+ * alpha: the outer thresholds are -alpha*a and +alpha*a (one binary32
+ * product, the lower one its negation).  §2.2 fixes alpha = 0.5; the §3.2
+ * tuning list gives groups of attention heads their own bucketing thresholds,
+ * read here as a per-head-group alpha (0.5 unless the caller sets one). */
+void ora_encode_vec_f32_ex(const float *x, int d, int rotate, float alpha, uint8_t *packed,
+                           float *y_out, int *codes_out)
 {
     float y[ORA_MAX_D];
     int c[ORA_MAX_D];
@@ -218,8 +222,8 @@ void ora_encode_vec_f32_rot(const float *x, int d, int rotate, uint8_t *packed, 
             if (m > a)
                 a = m;
         }
-        float t0 = -0.5f * a;
-        float t2 = 0.5f * a;
+        float t2 = alpha * a;
+        float t0 = -t2;
         for (int i = g0; i < g0 + group; i++)
             c[i] = ora_bucket(y[i], t0, t2);
     }
@@ -232,26 +236,42 @@ void ora_encode_vec_f32_rot(const float *x, int d, int rotate, uint8_t *packed, 
             codes_out[i] = c[i];
 }
 
-/* Encode keys x[batch][heads][n][d] into the code cache
- * codes[batch][heads][cap][d/4] at token rows [pos, pos+n). */
+void ora_encode_vec_f32_rot(const float *x, int d, int rotate, uint8_t *packed, float *y_out,
+                            int *codes_out)
+{
+    ora_encode_vec_f32_ex(x, d, rotate, 0.5f, packed, y_out, codes_out);
+}
+
 void ora_encode_vec_f32(const float *x, int d, uint8_t *packed, float *y_out,
                         int *codes_out)
 {
     ora_encode_vec_f32_rot(x, d, 1, packed, y_out, codes_out);
 }
 
-void ora_encode_keys_rot(const void *x, int dtype, int batch, int heads, int64_t n,
-                         int d, uint8_t *codes, int64_t cap, int64_t pos, int rotate)
+/* Encode keys x[batch][heads][n][d] into the code cache
+ * codes[batch][heads][cap][d/4] at token rows [pos, pos+n).  Head h buckets
+ * with alpha[h % n_alpha] (0.5 for every head when n_alpha == 0). */
+void ora_encode_keys_ex(const void *x, int dtype, int batch, int heads, int64_t n,
+                        int d, uint8_t *codes, int64_t cap, int64_t pos, int rotate,
+                        const float *alpha, int n_alpha)
 {
     int64_t total = (int64_t)batch * heads * n;
 #pragma omp parallel for schedule(static)
     for (int64_t v = 0; v < total; v++) {
         int64_t bh = v / n, t = v % n;
+        int head = (int)(bh % heads);
+        float a = n_alpha > 0 ? alpha[head % n_alpha] : 0.5f;
         float xv[ORA_MAX_D];
         for (int i = 0; i < d; i++)
             xv[i] = ora_widen(x, dtype, v * d + i);
-        ora_encode_vec_f32_rot(xv, d, rotate, codes + (bh * cap + pos + t) * (d / 4), 0, 0);
+        ora_encode_vec_f32_ex(xv, d, rotate, a, codes + (bh * cap + pos + t) * (d / 4), 0, 0);
     }
+}
+
+void ora_encode_keys_rot(const void *x, int dtype, int batch, int heads, int64_t n,
+                         int d, uint8_t *codes, int64_t cap, int64_t pos, int rotate)
+{
+    ora_encode_keys_ex(x, dtype, batch, heads, n, d, codes, cap, pos, rotate, 0, 0);
 }
 
 void ora_encode_keys(const void *x, int dtype, int batch, int heads, int64_t n,
@@ -475,15 +495,23 @@ void ora_sparse_attend(const void *q, const void *k, const void *v, int dtype,
  * it against the first n_ctx cached codes (§2.3), keep the budget (§5.2,
  * with the forced set of ora_select_row_keep) and attend over those rows
  * (§6).  idx_out may be null. */
-void ora_decode_step_ex(const void *q, const void *k, const void *v,
-                        const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
-                        int d, int64_t cap, int64_t n_ctx, int budget, int64_t n_sink,
-                        int64_t n_recent, int rotate, double scale, void *out, double *out64,
-                        int32_t *idx_out)
+/* alpha / n_alpha: the per-KV-head bucketing table of ora_encode_keys_ex
+ * (the keys' codes were made with it); query head hq buckets with its KV
+ * head's entry, alpha[(hq / G) % n_alpha]. */
+void ora_decode_step_alpha(const void *q, const void *k, const void *v,
+                           const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
+                           int d, int64_t cap, int64_t n_ctx, int budget, int64_t n_sink,
+                           int64_t n_recent, int rotate, const float *alpha, int n_alpha,
+                           double scale, void *out, double *out64, int32_t *idx_out)
 {
     int rb = d / 4;
+    int G = Hq / Hkv;
     uint8_t *qc = (uint8_t *)malloc((size_t)B * Hq * rb);
-    ora_encode_keys_rot(q, dtype, B, Hq, 1, d, qc, 1, 0, rotate);
+    float *qalpha = (float *)malloc(sizeof(float) * (size_t)Hq);
+    for (int hq = 0; hq < Hq; hq++)
+        qalpha[hq] = n_alpha > 0 ? alpha[(hq / G) % n_alpha] : 0.5f;
+    ora_encode_keys_ex(q, dtype, B, Hq, 1, d, qc, 1, 0, rotate, qalpha, Hq);
+    free(qalpha);
     uint16_t *dist = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)B * Hq *
                                         (size_t)(n_ctx > 0 ? n_ctx : 1));
     ora_score(qc, k_codes, B, Hq, Hkv, d, cap, n_ctx, dist);
@@ -497,6 +525,16 @@ void ora_decode_step_ex(const void *q, const void *k, const void *v,
         free(idx);
     free(dist);
     free(qc);
+}
+
+void ora_decode_step_ex(const void *q, const void *k, const void *v,
+                        const uint8_t *k_codes, int dtype, int B, int Hq, int Hkv,
+                        int d, int64_t cap, int64_t n_ctx, int budget, int64_t n_sink,
+                        int64_t n_recent, int rotate, double scale, void *out, double *out64,
+                        int32_t *idx_out)
+{
+    ora_decode_step_alpha(q, k, v, k_codes, dtype, B, Hq, Hkv, d, cap, n_ctx, budget, n_sink,
+                          n_recent, rotate, 0, 0, scale, out, out64, idx_out);
 }
 
 void ora_decode_step_keep(const void *q, const void *k, const void *v,

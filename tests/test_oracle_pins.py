@@ -343,6 +343,92 @@ def test_encode_without_rotation_hand_worked(ora, case):
     assert np.array_equal(y, np.array(x, np.float32))   # nothing rotated
 
 
+def _golden_alpha_cases():
+    out = []
+    with open(os.path.join(GOLDEN, "encode_alpha_hand_worked.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            d, rot, alpha, x, y, codes, packed = (p.strip() for p in line.split("|"))
+            out.append((int(d), int(rot), float(alpha), [float(v) for v in x.split(",")],
+                        [float(v) for v in y.split(",")], [int(c) for c in codes.split(",")],
+                        bytes.fromhex(packed)))
+    return out
+
+
+@pytest.mark.parametrize("case", _golden_alpha_cases(),
+                         ids=lambda c: f"rot{c[1]}-a{c[2]}-{c[6].hex()}")
+def test_encode_alpha_hand_worked(ora, case):
+    d, rot, alpha, x, y, codes, packed = case
+    got_packed, got_y, got_codes = ora.encode_vec(np.array(x, np.float32), rotate=rot, alpha=alpha)
+    assert got_y.tolist() == y
+    assert got_codes.tolist() == codes
+    assert bytes(got_packed) == packed
+
+
+def test_encode_alpha_half_is_the_fixed_rule(ora):
+    # 0.5 * a is exact in binary32, so alpha = 0.5 gives the §2.2 codes bit for bit
+    rng = np.random.default_rng(21)
+    for d in (64, 128, 256):
+        for _ in range(50):
+            x = rng.standard_normal(d).astype(np.float32)
+            for rot in (0, 1):
+                assert np.array_equal(ora.encode_vec(x, rotate=rot, alpha=0.5)[0],
+                                      ora.encode_vec(x, rotate=rot)[0])
+
+
+def test_encode_alpha_definition_and_limits(ora):
+    rng = np.random.default_rng(22)
+    for d in (64, 256):
+        for alpha in (0.0, 0.1, 0.3, 0.7, 1.0, 1.5):
+            x = rng.standard_normal(d).astype(np.float32)
+            _, y, c = ora.encode_vec(x, rotate=1, alpha=alpha)
+            g = 128 if d > 128 else d
+            for g0 in range(0, d, g):
+                yy, cc = y[g0:g0 + g], c[g0:g0 + g]
+                t2 = np.float32(np.float32(alpha) * np.max(np.abs(yy)))
+                want = np.select([yy < -t2, yy < 0, yy < t2], [0, 1, 2], 3)
+                assert np.array_equal(cc, want)
+                if alpha == 0.0:       # sign codes: 3 for y >= 0, 0 below
+                    assert np.array_equal(cc, np.where(yy >= 0, 3, 0))
+                if alpha >= 1.0:       # only the maximum can reach code 3, nothing code 0
+                    assert not np.any(cc == 0)
+                    assert np.all((cc != 3) | (yy == np.max(np.abs(yy))))
+
+
+def test_encode_keys_alpha_per_head(ora):
+    x = synth.integer_values((2, 5, 7, 64), -9, 9, seed=3)
+    table = [0.25, 0.75, 0.4]
+    codes = ora.encode_keys(x, alpha=table)
+    for b, h, t in itertools.product(range(2), range(5), range(7)):
+        want = ora.encode_vec(x[b, h, t], alpha=table[h % 3])[0]
+        assert np.array_equal(codes[b, h, t], want)
+    assert np.array_equal(ora.encode_keys(x, alpha=[0.5]), ora.encode_keys(x))
+
+
+def test_decode_step_alpha_is_composition(ora):
+    # query head hq buckets with its KV head's alpha (hq // G)
+    w = synth.LLAMA2_32K.replace(hq=8, hkv=2, n_ctx=2000, cap=2100, budget=48)
+    lay = synth.make_layer(w, 0, "cpu")
+    q, k, v = (synth.to_numpy_bits(lay[x]) for x in ("q", "k", "v"))
+    table = [0.3, 0.7]
+    codes = ora.encode_keys(k, alpha=table)
+    out, out64, idx = ora.decode_step(q, k, v, codes, n_ctx=2000, budget=48, alpha=table)
+    qc = np.concatenate([ora.encode_keys(q[:, h:h + 1, None, :], alpha=[table[h // 4]])[:, :, 0]
+                         for h in range(8)], axis=1)
+    dist = ora.score(qc, codes, n_ctx=2000)
+    idx2 = ora.select_topk(dist, 48)
+    assert np.array_equal(idx, idx2)
+    o2, o64 = ora.sparse_attend(q, k, v, idx2)
+    assert np.array_equal(out, o2) and np.array_equal(out64, o64)
+    # a table of 0.5s is the fixed rule
+    c05 = ora.encode_keys(k, alpha=[0.5, 0.5])
+    assert np.array_equal(c05, ora.encode_keys(k))
+    r = ora.decode_step(q, k, v, c05, n_ctx=2000, budget=48, alpha=[0.5, 0.5])
+    r0 = ora.decode_step(q, k, v, c05, n_ctx=2000, budget=48)
+    assert all(np.array_equal(a, b) for a, b in zip(r, r0))
+
+
 def test_encode_rotation_off_is_rotation_of_rotated_input(ora):
     # H (H x) = d x for the unnormalised Sylvester H, and codes are invariant
     # to a positive scale: encoding H x without the rotation equals encoding x
