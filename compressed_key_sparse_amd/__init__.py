@@ -26,6 +26,7 @@ __all__ = [
     "DECODE_GROUP_WAIT", "DECODE_SPLIT", "WS_CTRL_BYTES", "WS_STATUS_OFFSET", "ROTATE_OFF",
     "ROTATE_F32", "ROTATE_F16", "GroupWaitGaveUp", "set_wait_polls", "wait_polls",
     "DEFAULT_WAIT_POLLS", "PhaseRecorder", "decode_step_static", "STATIC_SCRATCH_BYTES",
+    "set_bucket_alpha", "bucket_alpha", "MAX_ALPHA_GROUPS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -109,6 +110,10 @@ def load(variant: str | None = None):
     lib.adamas_set_decode_mode.argtypes = [i32]
     lib.adamas_set_rotation.argtypes = [i32]
     lib.adamas_set_rotation.restype = i32
+    lib.adamas_set_bucket_alpha.argtypes = [P, i32]
+    lib.adamas_set_bucket_alpha.restype = i32
+    lib.adamas_bucket_alpha.argtypes = [P, i32]
+    lib.adamas_bucket_alpha.restype = i32
     lib.adamas_decode_path.argtypes = [i32, i32, i32, i64, i32, i32]
     lib.adamas_set_wait_polls.argtypes = [ctypes.c_uint32]
     lib.adamas_set_wait_polls.restype = i32
@@ -336,6 +341,33 @@ def set_rotation(on) -> None:
     (adamas_set_rotation)."""
     mode = int(on) if not isinstance(on, bool) else (1 if on else 0)
     _check(load().adamas_set_rotation(mode), "adamas_set_rotation")
+
+
+MAX_ALPHA_GROUPS = 64
+
+
+def set_bucket_alpha(alpha=None) -> None:
+    """Process-wide per-head-group bucketing thresholds (adamas_set_bucket_alpha):
+    KV head h (and its query heads) buckets at -alpha[h % n]*a, 0 and
+    +alpha[h % n]*a; None or an empty sequence restores the fixed rule
+    (alpha 0.5)."""
+    if alpha is None:
+        _check(load().adamas_set_bucket_alpha(None, 0), "adamas_set_bucket_alpha")
+        return
+    a = (ctypes.c_float * MAX_ALPHA_GROUPS)()
+    vals = [float(x) for x in alpha]
+    if len(vals) > MAX_ALPHA_GROUPS:
+        raise ValueError(f"at most {MAX_ALPHA_GROUPS} alpha groups")
+    for i, x in enumerate(vals):
+        a[i] = x
+    _check(load().adamas_set_bucket_alpha(a, len(vals)), "adamas_set_bucket_alpha")
+
+
+def bucket_alpha() -> list:
+    """The current table (empty: the fixed rule, alpha 0.5)."""
+    a = (ctypes.c_float * MAX_ALPHA_GROUPS)()
+    n = load().adamas_bucket_alpha(a, MAX_ALPHA_GROUPS)
+    return [a[i] for i in range(n)]
 
 
 class PhaseRecorder:

@@ -42,6 +42,19 @@ constexpr int64_t kSizingCapacity = 1024;
 std::atomic<int> g_decode_mode{ADAMAS_DECODE_AUTO};
 std::atomic<int> g_rotation{1};
 int rotation_on() { return g_rotation.load(std::memory_order_relaxed); }
+// per-head-group bucketing alphas (adamas_set_bucket_alpha); n == 0: 0.5
+std::mutex g_alpha_mu;
+int g_alpha_n = 0;
+float g_alpha[kMaxAlphaGroups] = {};
+// the encoding rule a launch takes (by value, so a launch keeps the table it
+// was made with)
+EncodeRule encode_rule() {
+  EncodeRule r{rotation_on(), 0, {}};
+  std::lock_guard<std::mutex> lk(g_alpha_mu);
+  r.n_alpha = g_alpha_n;
+  for (int i = 0; i < g_alpha_n; ++i) r.alpha[i] = g_alpha[i];
+  return r;
+}
 std::atomic<uint32_t> g_wait_polls{kDefaultWaitPolls};
 std::atomic<uint64_t*> g_stamps{nullptr};  // phase stamps (measurement build)
 uint64_t* stamps_ptr() { return g_stamps.load(std::memory_order_relaxed); }
@@ -185,7 +198,7 @@ int adamas_encode_keys(const void* x, int dtype, int batch, int heads, int64_t n
   const int bf = dtype == ADAMAS_BF16;
   with_dim(head_dim, [&](auto dc) {
     k_encode<decltype(dc)::value><<<blocks, kEncodeThreads, 0, stream>>>(
-        x, bf, n, nvec, codes, cap, pos, x_copy_dst, rotation_on());
+        x, bf, n, nvec, codes, cap, pos, x_copy_dst, heads, encode_rule());
   });
   return launch_status();
 }
@@ -380,7 +393,7 @@ int decode_step_impl(const void* q, const void* k, const void* v, const uint8_t*
       if (ws_bytes < gp.total) return ADAMAS_ERR_WORKSPACE;
       DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
                    nullptr, nullptr, idx_out, out, n_sink, n_recent, {}};
-      a.rotate = rotation_on();
+      a.rule = encode_rule();
       a.wait_polls = g_wait_polls.load(std::memory_order_relaxed);
       a.stamps = stamps_ptr();
       const dim3 grid((unsigned)gp.n_chunks, (unsigned)Hkv, (unsigned)B);
@@ -404,7 +417,7 @@ int decode_step_impl(const void* q, const void* k, const void* v, const uint8_t*
   DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
                reinterpret_cast<uint32_t*>(w + p.sel.cand_off),
                reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent, {}};
-  a.rotate = rotation_on();
+  a.rule = encode_rule();
   a.stamps = stamps_ptr();
   if (split) {
     a.chist = reinterpret_cast<uint16_t*>(w + p.chist_off);
@@ -488,7 +501,7 @@ int ragged_step(const void* q, const void* k_new, const void* v_new, void* k, vo
                reinterpret_cast<uint32_t*>(w + kCtrlSelect), idx, out, n_sink, n_recent,
                RaggedArgs{lens, k_new, v_new, k, v, k_codes, pages, max_pages, page_log2,
                           n_pages, pt_lds}};
-  a.rotate = rotation_on();
+  a.rule = encode_rule();
   a.stamps = stamps_ptr();
   return launch_last_arrival(p, a, B, head_dim, dtype == ADAMAS_BF16, w, stream);
 }
@@ -530,6 +543,24 @@ int adamas_set_rotation(int on) {
   if (on != 0 && on != 1 && on != 2) return ADAMAS_ERR_INVALID;
   g_rotation.store(on, std::memory_order_relaxed);
   return ADAMAS_OK;
+}
+
+int adamas_set_bucket_alpha(const float* alpha, int n) {
+  static_assert(ADAMAS_MAX_ALPHA_GROUPS == kMaxAlphaGroups, "alpha table size");
+  if (n < 0 || n > kMaxAlphaGroups || (n > 0 && alpha == nullptr)) return ADAMAS_ERR_INVALID;
+  for (int i = 0; i < n; ++i)
+    if (!(alpha[i] >= 0.0f) || !std::isfinite(alpha[i])) return ADAMAS_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(g_alpha_mu);
+  for (int i = 0; i < n; ++i) g_alpha[i] = alpha[i];
+  g_alpha_n = n;
+  return ADAMAS_OK;
+}
+
+int adamas_bucket_alpha(float* alpha_out, int cap) {
+  std::lock_guard<std::mutex> lk(g_alpha_mu);
+  if (alpha_out != nullptr)
+    for (int i = 0; i < g_alpha_n && i < cap; ++i) alpha_out[i] = g_alpha[i];
+  return g_alpha_n;
 }
 
 int adamas_set_wait_polls(uint32_t polls) {

@@ -23,7 +23,7 @@ void launch_decode_k(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
   k_decode<D, G, BF, RAG, OCC><<<grid, kDecodeThreads, p.sel.lds, s>>>(
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
       p.sel.kpad_log2, p.sel.mcap, (p.fuse && !a.chist) ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
-      a.out, a.n_sink, a.n_recent, a.rotate, a.rg, RAG ? nullptr : a.chist,
+      a.out, a.n_sink, a.n_recent, a.rule, a.rg, RAG ? nullptr : a.chist,
       RAG ? 0 : a.ncp, a.stamps);
 }
 
@@ -62,7 +62,7 @@ void launch_decode_gs_t(const GroupPlan& p, dim3 grid, hipStream_t s, const Deco
       reinterpret_cast<float*>(w + p.part_off), reinterpret_cast<uint32_t*>(w + kCtrlSelect),
       reinterpret_cast<uint32_t*>(w + kCtrlAttend),
       reinterpret_cast<uint32_t*>(w + ADAMAS_WS_STATUS_OFFSET), a.wait_polls, a.idx, a.out,
-      a.n_sink, a.n_recent, a.rotate, a.stamps);
+      a.n_sink, a.n_recent, a.rule, a.stamps);
 }
 
 #define ADM_INST_G(g)                                                                        \

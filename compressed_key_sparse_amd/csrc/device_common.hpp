@@ -415,12 +415,28 @@ ADM_DEV void slot_fwht(float (&y)[D / 16], int l16) {
   stage(std::integral_constant<int, 8>{});
 }
 
-// mode: 1 rotates in binary32; 0 buckets the vector as it is (no §2.1; for
-// the ablation); 2 rotates in binary16 (the article's FP16 advice, §6): the
-// inputs are rounded to binary16 and every sum and difference is one
-// binary16 operation, carried between lanes as the equal binary32 value.
+// How vectors are encoded (§2.1, §2.2).  rotate: 1 rotates in binary32; 0
+// buckets the vector as it is (no §2.1; for the ablation); 2 rotates in
+// binary16 (the article's FP16 advice, §6).  The outer bucketing thresholds
+// of KV head h are -alpha*a and +alpha*a (one binary32 product), with
+// alpha = alpha[h % n_alpha], or 0.5 (the §2.2 rule) when n_alpha is 0: the
+// §3.2 tuning list lets groups of attention heads bucket with their own
+// thresholds.  A query head buckets with its KV head's alpha.
+constexpr int kMaxAlphaGroups = 64;
+struct EncodeRule {
+  int rotate;
+  int n_alpha;
+  float alpha[kMaxAlphaGroups];
+  __host__ __device__ __forceinline__ float alpha_of(int head) const {
+    return n_alpha > 0 ? alpha[head % n_alpha] : 0.5f;
+  }
+};
+
+// mode: EncodeRule::rotate.  In binary16 the inputs are rounded to binary16
+// and every sum and difference is one binary16 operation, carried between
+// lanes as the equal binary32 value.
 template <int D>
-ADM_DEV uint32_t wave_encode(float (&y)[D / 64], int mode = 1) {
+ADM_DEV uint32_t wave_encode(float (&y)[D / 64], int mode, float alpha) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & (kWave - 1);
   if (mode == 1)
@@ -436,8 +452,8 @@ ADM_DEV uint32_t wave_encode(float (&y)[D / 64], int mode = 1) {
   a = fmaxf(a, lane_xor<8>(a));
   a = xor_max<16>(a);
   if constexpr (D <= 128) a = xor_max<32>(a);  // else one absmax per 32-lane half
-  const float t0 = -0.5f * a;
-  const float t2 = 0.5f * a;
+  const float t2 = alpha * a;
+  const float t0 = -t2;
   uint32_t bits = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {

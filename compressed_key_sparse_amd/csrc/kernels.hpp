@@ -62,7 +62,8 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
                                                            int is_bf16, int64_t n, int64_t nvec,
                                                            uint8_t* __restrict__ codes,
                                                            int64_t cap, int64_t pos,
-                                                           void* __restrict__ copy, int rotate) {
+                                                           void* __restrict__ copy, int heads,
+                                                           EncodeRule rule) {
   // a 16-lane slot per vector: lane l holds dimensions [l*EL, l*EL + EL), so
   // the butterflies of distance below EL stay in registers and the others
   // (EL, 2EL, 4EL, 8EL) are DPP exchanges inside the slot's row of 16 lanes;
@@ -108,11 +109,12 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
           reinterpret_cast<uint4*>(static_cast<float*>(copy) + row * D + l16 * EL)[k] = t;
       }
     }
-    if (rotate == 1)
+    if (rule.rotate == 1)
       slot_fwht<D, false>(y, l16);
-    else if (rotate == 2)
+    else if (rule.rotate == 2)
       slot_fwht<D, true>(y, l16);
-    // §2.2: absmax of the vector's 128-dimension group, codes at -a/2, 0, a/2
+    // §2.2: absmax of the vector's 128-dimension group, codes at -alpha*a, 0,
+    // alpha*a (alpha of the vector's head; 0.5 unless set)
     float a = 0.0f;
 #pragma unroll
     for (int e = 0; e < EL; ++e) a = fmaxf(a, fabsf(y[e]));
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
     a = fmaxf(a, lane_xor<2>(a));
     if constexpr (kGroupLanes >= 8) a = fmaxf(a, lane_xor<4>(a));
     if constexpr (kGroupLanes >= 16) a = fmaxf(a, lane_xor<8>(a));
-    const float t0 = -0.5f * a, t2 = 0.5f * a;
+    const float t2 = rule.alpha_of((int)(bh % heads)) * a, t0 = -t2;
     // §3.1: 4 codes per byte, first code in the high bits; 16 dimensions per word
     uint32_t bits = 0;
 #pragma unroll
@@ -692,7 +694,7 @@ void k_decode(
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
     int n_chunks, int budget, int kpad_log2, int mcap, int fuse_attend, float qscale,
     uint32_t* __restrict__ cand, uint32_t* __restrict__ counters, int32_t* __restrict__ idx,
-    void* __restrict__ out, int n_sink, int n_recent, int rotate, RaggedArgs rg,
+    void* __restrict__ out, int n_sink, int n_recent, EncodeRule rule, RaggedArgs rg,
     uint16_t* __restrict__ chist, int ncp, uint64_t* __restrict__ stamps) {
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
   constexpr int NB = kNbins(D), NBP = kNbinsPadded(D), W = D / 16;
@@ -802,7 +804,7 @@ void k_decode(
       const uint4 kraw = load_elems_raw<E, BF>(rg.k_new, src + lane * E);
       float y[E];
       widen_elems<E, BF>(kraw, y);
-      const uint32_t word = wave_encode<D>(y, rotate);
+      const uint32_t word = wave_encode<D>(y, rule.rotate, rule.alpha_of(hkv));
       const int64_t crow =
           RAG == 2 ? pmap.row(pos_new) : ((int64_t)b * Hkv + hkv) * cap + pos_new;
       // a paged row whose table entry is out of range is scored but not stored
@@ -826,7 +828,7 @@ void k_decode(
   if (wid < G) {
     float y[E];
     widen_elems<E, BF>(qraw, y);
-    const uint32_t word = wave_encode<D>(y, rotate);
+    const uint32_t word = wave_encode<D>(y, rule.rotate, rule.alpha_of(hkv));
     if (lane % kLanesPerWord == 0) sq[wid * W + lane / kLanesPerWord] = word;
   }
   lds_sync();
@@ -1283,7 +1285,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     int n_chunks, int budget, int cmax, float qscale, uint16_t* __restrict__ ghist,
     float* __restrict__ part, uint32_t* __restrict__ arrive_hist,
     uint32_t* __restrict__ arrive_part, uint32_t* __restrict__ status, uint32_t max_polls,
-    int32_t* __restrict__ idx, void* __restrict__ out, int n_sink, int n_recent, int rotate,
+    int32_t* __restrict__ idx, void* __restrict__ out, int n_sink, int n_recent, EncodeRule rule,
     uint64_t* __restrict__ stamps) {
 
   constexpr int NT = kDecodeThreads, NW = NT / kWave;
@@ -1330,7 +1332,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   if (wid < G) {
     float y[E];
     widen_elems<E, BF>(qraw, y);
-    const uint32_t word = wave_encode<D>(y, rotate);
+    const uint32_t word = wave_encode<D>(y, rule.rotate, rule.alpha_of(hkv));
     if (lane % kLanesPerWord == 0) sq[wid * W + lane / kLanesPerWord] = word;
   }
   lds_sync();

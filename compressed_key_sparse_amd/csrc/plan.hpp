@@ -253,7 +253,7 @@ struct DecodeArgs {
   RaggedArgs rg;  // lens == nullptr: every sequence holds n_ctx rows
   uint16_t* chist = nullptr;  // SPLIT: per-chunk key counts, selection left to k_split_select
   int ncp = 0;
-  int rotate = 1;             // adamas_set_rotation mode
+  EncodeRule rule{1, 0, {}};  // rotation mode and bucketing alphas at launch
   uint32_t wait_polls = kDefaultWaitPolls;  // group-wait bound (adamas_set_wait_polls)
   uint64_t* stamps = nullptr;  // phase stamps (measurement build), or null
 };

@@ -235,6 +235,33 @@ uint32_t adamas_wait_polls(void);
 int adamas_set_rotation(int on);
 
 /*
+ * Per-head-group bucketing thresholds (article §2.2 with the §3.2 tuning
+ * list, which gives groups of attention heads their own thresholds).  §2.2
+ * buckets a rotated vector at -a/2, 0 and +a/2, a its absolute maximum (per
+ * 128-dimension group).  After this call the outer thresholds of KV head h
+ * are -t and +t with t = alpha[h % n] * a, one binary32 product (the middle
+ * one stays 0); every query head of that KV head's group buckets with the
+ * same alpha, so queries and keys of a head share one rule.  alpha: n host
+ * floats, each finite and >= 0 (0 gives sign codes; 1 and above leaves only
+ * the maximum in code 3), copied by the call.  n == 0 restores the §2.2 rule
+ * (alpha 0.5 for every head, which is also what a table of 0.5s gives, bit
+ * for bit).  Process-wide like adamas_set_rotation: it applies to launches
+ * enqueued after the call, each launch keeps the table it was made with, and
+ * codes made under one table must only be scored against queries encoded
+ * under the same one.  Returns ADAMAS_OK, or ADAMAS_ERR_INVALID if n is
+ * outside [0, ADAMAS_MAX_ALPHA_GROUPS], alpha is null with n > 0, or an
+ * entry is negative, infinite or NaN (the table is then left as it was).
+ */
+#define ADAMAS_MAX_ALPHA_GROUPS 64
+int adamas_set_bucket_alpha(const float* alpha, int n);
+
+/*
+ * The current table: copies min(n, cap) entries to alpha_out (when not
+ * null) and returns n (0: the §2.2 rule).
+ */
+int adamas_bucket_alpha(float* alpha_out, int cap);
+
+/*
  * The schedule adamas_decode_step would use for this shape on the current
  * device under the current mode: ADAMAS_DECODE_LAST_ARRIVAL,
  * ADAMAS_DECODE_GROUP_WAIT or ADAMAS_DECODE_SPLIT, or a negated status

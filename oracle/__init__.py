@@ -278,7 +278,7 @@ def decode_step(q, k, v, k_codes, n_ctx: int, budget: int, scale: float = 0.0,
 
 def decode_append_step(q, k, v, k_codes, lens, max_len: int, budget: int, k_new=None,
                        v_new=None, scale: float = 0.0, n_sink: int = 0, n_recent: int = 0,
-                       rotate: bool = True):
+                       rotate: bool = True, alpha=None):
     """A decode step over sequences of their own lengths, each first taking the
     step's new key and value at its next row (the compressed cache of §3.1
     stores each new token's code at its position; the step itself is §2-§6 on
@@ -288,7 +288,9 @@ def decode_append_step(q, k, v, k_codes, lens, max_len: int, budget: int, k_new=
     Sequence b holds L_b = lens[b] rows, clamped to [0, max_len - 1] when a
     token is appended and to [0, max_len] otherwise; it is decoded on its own
     with n_ctx = L_b (+1 with the new token), so its recent window ends at its
-    own last row.  No rows: a zero output and an all -1 selection."""
+    own last row.  No rows: a zero output and an all -1 selection.  alpha: the
+    per-KV-head bucketing table (the new key of KV head h buckets with
+    alpha[h % len(alpha)], as the cache's codes were made)."""
     k, v, k_codes = (np.array(a, copy=True) for a in (k, v, k_codes))
     B, Hq, d = q.shape
     app = k_new is not None
@@ -300,20 +302,21 @@ def decode_append_step(q, k, v, k_codes, lens, max_len: int, budget: int, k_new=
         if app:
             k[b, :, L] = k_new[b]
             v[b, :, L] = v_new[b]
-            row = encode_keys(np.ascontiguousarray(k_new[b][None, :, None, :]), rotate=rotate)
+            row = encode_keys(np.ascontiguousarray(k_new[b][None, :, None, :]), rotate=rotate,
+                              alpha=alpha)
             k_codes[b, :, L] = row[0, :, 0]
         n = L + (1 if app else 0)
         if n == 0:
             continue
         o, o64, ix = decode_step(q[b:b + 1], k[b:b + 1], v[b:b + 1], k_codes[b:b + 1], n, budget,
-                                 scale, n_sink, n_recent, rotate)
+                                 scale, n_sink, n_recent, rotate, alpha)
         out[b], out64[b], idx[b] = o[0], o64[0], ix[0]
     return out, out64, idx, k, v, k_codes
 
 
 def decode_paged_step(q, k_pool, v_pool, code_pool, page_table, lens, max_len: int, budget: int,
                       k_new=None, v_new=None, scale: float = 0.0, n_sink: int = 0,
-                      n_recent: int = 0, rotate: bool = True):
+                      n_recent: int = 0, rotate: bool = True, alpha=None):
     """decode_append_step over paged pools (the §3.1 cache kept in fixed-size
     chunks): pool page p holds tokens of every KV head, k_pool[p][h][j] is
     token j of the page; sequence b's logical page i is pool page
@@ -337,7 +340,7 @@ def decode_paged_step(q, k_pool, v_pool, code_pool, page_table, lens, max_len: i
         o, o64, ix, k2, v2, c2 = decode_append_step(
             q[b:b + 1], kb, vb, cb, np.asarray(lens)[b:b + 1], max_len, budget,
             None if k_new is None else k_new[b:b + 1], None if v_new is None else v_new[b:b + 1],
-            scale, n_sink, n_recent, rotate)
+            scale, n_sink, n_recent, rotate, alpha)
         if k_new is not None:
             L = min(max(int(lens[b]), 0), max_len - 1)
             pg, off = ids[L // P], L % P

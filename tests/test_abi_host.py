@@ -277,3 +277,27 @@ def test_wait_polls_setter(lib):
         adamas.set_wait_polls(-1)
     adamas.set_wait_polls(adamas.DEFAULT_WAIT_POLLS)
     assert adamas.wait_polls() == adamas.DEFAULT_WAIT_POLLS
+
+
+def test_bucket_alpha_setter(lib):
+    """The per-head-group bucketing table: validation leaves the table as it
+    was; the binding round-trips and restores the fixed rule."""
+    F = ctypes.c_float * 70
+    good = F(*([0.25, 0.75, 0.0, 1.5] + [0.5] * 66))
+    assert lib.adamas_bucket_alpha(None, 0) == 0
+    assert lib.adamas_set_bucket_alpha(good, 4) == OK
+    assert adamas.bucket_alpha() == [0.25, 0.75, 0.0, 1.5]
+    assert lib.adamas_set_bucket_alpha(good, 65) == INVALID
+    assert lib.adamas_set_bucket_alpha(good, -1) == INVALID
+    assert lib.adamas_set_bucket_alpha(None, 2) == INVALID
+    for bad in (-0.25, float("inf"), float("nan")):
+        assert lib.adamas_set_bucket_alpha(F(0.5, bad), 2) == INVALID
+    assert adamas.bucket_alpha() == [0.25, 0.75, 0.0, 1.5]
+    assert lib.adamas_set_bucket_alpha(good, 64) == OK
+    assert len(adamas.bucket_alpha()) == 64
+    with pytest.raises(ValueError):
+        adamas.set_bucket_alpha([0.5] * 65)
+    adamas.set_bucket_alpha([0.3])
+    assert adamas.bucket_alpha() == [pytest.approx(0.3)]
+    adamas.set_bucket_alpha(None)
+    assert adamas.bucket_alpha() == []

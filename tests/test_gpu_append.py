@@ -39,10 +39,18 @@ def _inputs(w, seed, near_query=True):
     return lay, codes, kn, vn
 
 
-def _run(ora, w, lens, max_len, budget, append=True, n_sink=0, n_recent=0, seed=500):
+def _run(ora, w, lens, max_len, budget, append=True, n_sink=0, n_recent=0, seed=500, alpha=None):
+    adamas.set_bucket_alpha(alpha)
+    try:
+        return _run_rule(ora, w, lens, max_len, budget, append, n_sink, n_recent, seed, alpha)
+    finally:
+        adamas.set_bucket_alpha(None)
+
+
+def _run_rule(ora, w, lens, max_len, budget, append, n_sink, n_recent, seed, alpha):
     lay, codes, kn, vn = _inputs(w, seed)
     q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
-    oc = ora.encode_keys(k)
+    oc = ora.encode_keys(k, alpha=alpha)
     assert np.array_equal(codes.cpu().numpy(), oc), "code cache differs before the step"
     lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
     idx = torch.full((w.batch, w.hq, budget), -7, dtype=torch.int32, device=DEV)
@@ -53,7 +61,7 @@ def _run(ora, w, lens, max_len, budget, append=True, n_sink=0, n_recent=0, seed=
     kn_h, vn_h = (host(t) for t in (kn, vn))
     oout, o64, oidx, ok, ov, ocd = ora.decode_append_step(
         q, k, v, oc, np.array(lens), max_len, budget, kn_h if append else None,
-        vn_h if append else None, n_sink=n_sink, n_recent=n_recent)
+        vn_h if append else None, n_sink=n_sink, n_recent=n_recent, alpha=alpha)
     assert torch.equal(lens_d.cpu(), torch.tensor(lens, dtype=torch.int32)), "lens written"
     assert np.array_equal(host(lay["k"]), ok), "K cache differs"
     assert np.array_equal(host(lay["v"]), ov), "V cache differs"
@@ -62,7 +70,7 @@ def _run(ora, w, lens, max_len, budget, append=True, n_sink=0, n_recent=0, seed=
     for b in range(w.batch):
         assert np.array_equal(got[b], oidx[b]), f"selection of sequence {b} differs"
     check_out(ora, out, q, ok, ov, oidx, oout, o64,
-              f"append={append} lens={lens} max_len={max_len} budget={budget}")
+              f"append={append} lens={lens} max_len={max_len} budget={budget} alpha={alpha}")
     return got, lay, kn
 
 
@@ -88,6 +96,12 @@ def test_append_gqa(ora, hq, hkv, dt, d):
     w = synth.LLAMA32_GQA_1M.replace(batch=3, hq=hq, hkv=hkv, head_dim=d, dtype=dt, n_ctx=5000,
                                      cap=5000, budget=128)
     _run(ora, w, [4999, 17, 2500], 5000, 128)
+
+
+def test_append_bucket_alpha(ora):
+    log("append with per-head-group bucketing thresholds")
+    w = synth.LLAMA32_GQA_1M.replace(batch=3, hq=8, hkv=4, n_ctx=5000, cap=5000, budget=128)
+    _run(ora, w, [4999, 17, 2500], 5000, 128, alpha=[0.25, 0.75, 0.4])
 
 
 @pytest.mark.parametrize("budget", [2048, 20000])

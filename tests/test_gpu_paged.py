@@ -52,7 +52,17 @@ def _pools(w, P, pages_per_seq, spare, seed):
     return lay, k_pool, v_pool, c_pool, table
 
 
-def _run(ora, w, P, pages_per_seq, lens, budget, append=True, n_sink=0, n_recent=0, seed=11):
+def _run(ora, w, P, pages_per_seq, lens, budget, append=True, n_sink=0, n_recent=0, seed=11,
+         alpha=None):
+    adamas.set_bucket_alpha(alpha)
+    try:
+        return _run_rule(ora, w, P, pages_per_seq, lens, budget, append, n_sink, n_recent, seed,
+                         alpha)
+    finally:
+        adamas.set_bucket_alpha(None)
+
+
+def _run_rule(ora, w, P, pages_per_seq, lens, budget, append, n_sink, n_recent, seed, alpha):
     lay, kp, vp, cp, table = _pools(w, P, pages_per_seq, 3, seed)
     B, Hkv, d, dt = w.batch, w.hkv, w.head_dim, w.torch_dtype
     max_len = pages_per_seq * P
@@ -61,7 +71,12 @@ def _run(ora, w, P, pages_per_seq, lens, budget, append=True, n_sink=0, n_recent
     for b in range(0, B, 2):                          # some new keys near a query head
         kn[b] = (lay["q"][b, ::w.hq // w.hkv].float() + 0.05 * kn[b].float()).to(dt)
     q = host(lay["q"])
-    kp_h, vp_h, cp_h = host(kp), host(vp), cp.cpu().numpy()
+    kp_h, vp_h = host(kp), host(vp)
+    # the oracle's own codes of the pages in use (spare pages stay zero)
+    cp_h = np.zeros(tuple(cp.shape), np.uint8)
+    used = np.unique(table[(table >= 0) & (table < cp.shape[0])])
+    cp_h[used] = ora.encode_keys(kp_h[used], alpha=alpha)
+    assert np.array_equal(cp.cpu().numpy(), cp_h), "code pool differs before the step"
     table_d = torch.from_numpy(table).to(DEV)
     lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
     idx = torch.full((B, w.hq, budget), -7, dtype=torch.int32, device=DEV)
@@ -72,7 +87,7 @@ def _run(ora, w, P, pages_per_seq, lens, budget, append=True, n_sink=0, n_recent
     oout, o64, oidx, okp, ovp, ocp = ora.decode_paged_step(
         q, kp_h, vp_h, cp_h, table, np.array(lens), max_len, budget,
         host(kn) if append else None, host(vn) if append else None, n_sink=n_sink,
-        n_recent=n_recent)
+        n_recent=n_recent, alpha=alpha)
     assert np.array_equal(host(kp), okp), "K pool differs"
     assert np.array_equal(host(vp), ovp), "V pool differs"
     assert np.array_equal(cp.cpu().numpy(), ocp), "code pool differs"
@@ -95,6 +110,12 @@ def test_paged_gqa_fp32_d64(ora):
     log("paged GQA 6/2 heads, fp32, d=64")
     w = synth.LLAMA32_GQA_1M.replace(batch=3, hq=6, hkv=2, head_dim=64, dtype="f32")
     _run(ora, w, 1024, 4, [4095, 2047, 100], 128)
+
+
+def test_paged_bucket_alpha(ora):
+    log("paged GQA with per-head-group bucketing thresholds")
+    w = synth.LLAMA32_GQA_1M.replace(batch=3, hq=6, hkv=2, head_dim=128, dtype="bf16")
+    _run(ora, w, 1024, 3, [3071, 1000, 5], 128, alpha=[0.3, 0.65])
 
 
 def test_paged_large_budget(ora):
@@ -133,7 +154,11 @@ def test_paged_graph_replay_across_page_boundary(ora):
     s = torch.cuda.Stream(DEV)
     ws = adamas.Workspace(DEV)
     ws.get(adamas.workspace_bytes(adamas.OP_DECODE_STEP, B, Hq, Hkv, 3 * P, 64, d))
-    kp_h, vp_h, cp_h = host(kp), host(vp), cp.cpu().numpy()
+    kp_h, vp_h = host(kp), host(vp)
+    cp_h = np.zeros(tuple(cp.shape), np.uint8)
+    used = np.unique(table[(table >= 0) & (table < cp.shape[0])])
+    cp_h[used] = ora.encode_keys(kp_h[used])
+    assert np.array_equal(cp.cpu().numpy(), cp_h), "code pool differs before the steps"
 
     def step():
         adamas.decode_paged_step(q_s, kp, vp, cp, table_d, lens_d, 3 * P, 64, k_new=kn_s,

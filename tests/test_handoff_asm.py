@@ -30,13 +30,13 @@ using namespace adm;
 void instantiate() {
   hipLaunchKernelGGL((k_decode<128, 1, true, 0, false>), dim3(1), dim3(1024), 0, 0, nullptr,
       nullptr, nullptr, nullptr, 0, 0, (int64_t)0, (int64_t)0, 0, 0, 0, 0, 0, 0, 0.f, nullptr,
-      nullptr, nullptr, nullptr, 0, 0, 0, RaggedArgs{}, nullptr, 0, nullptr);
+      nullptr, nullptr, nullptr, 0, 0, EncodeRule{}, RaggedArgs{}, nullptr, 0, nullptr);
   hipLaunchKernelGGL((k_decode<128, 3, true, 1, false>), dim3(1), dim3(1024), 0, 0, nullptr,
       nullptr, nullptr, nullptr, 0, 0, (int64_t)0, (int64_t)0, 0, 0, 0, 0, 0, 0, 0.f, nullptr,
-      nullptr, nullptr, nullptr, 0, 0, 0, RaggedArgs{}, nullptr, 0, nullptr);
+      nullptr, nullptr, nullptr, 0, 0, EncodeRule{}, RaggedArgs{}, nullptr, 0, nullptr);
   hipLaunchKernelGGL((k_decode_gs<128, 1, true>), dim3(1), dim3(1024), 0, 0, nullptr, nullptr,
       nullptr, nullptr, 0, 0, (int64_t)0, (int64_t)0, 0, 0, 0, 0, 0.f, nullptr, nullptr, nullptr,
-      nullptr, nullptr, 0u, nullptr, nullptr, 0, 0, 0, nullptr);
+      nullptr, nullptr, 0u, nullptr, nullptr, 0, 0, EncodeRule{}, nullptr);
   hipLaunchKernelGGL((k_attend<128, true, false>), dim3(1), dim3(1024), 0, 0, nullptr, nullptr,
       nullptr, nullptr, 0, 0, (int64_t)0, 0, 0.f, nullptr, nullptr, nullptr, PageArgs{});
   hipLaunchKernelGGL((k_select<128>), dim3(1), dim3(1024), 0, 0, nullptr, 0, (int64_t)0, 0, 0,

@@ -664,6 +664,22 @@ def test_append_step_writes_only_the_next_row(ora):
         assert np.array_equal(c2[b][:, others], codes[b][:, others])
 
 
+def test_append_step_alpha_encodes_the_new_key_per_head(ora):
+    (q, k, v, kn, vn), _ = _append_case("f32", 70, Hkv=2)
+    table = [0.2, 0.8]
+    codes = ora.encode_keys(k, alpha=table)
+    lens = np.array([5, 0, 39, 17], np.int32)
+    r = ora.decode_append_step(q, k, v, codes, lens, 40, 8, kn, vn, alpha=table)
+    c2 = r[5]
+    for b, L in enumerate(lens):
+        for h in range(2):
+            assert np.array_equal(c2[b, h, L], ora.encode_vec(kn[b, h], alpha=table[h])[0])
+        # the sequence's step is the alpha decode step over its own rows
+        o, o64, ix = ora.decode_step(q[b:b + 1], r[3][b:b + 1], r[4][b:b + 1], c2[b:b + 1],
+                                     int(L) + 1, 8, alpha=table)
+        assert np.array_equal(r[2][b], ix[0]) and np.array_equal(r[1][b], o64[0])
+
+
 def test_append_step_recent_window_and_empty_sequences(ora):
     (q, k, v, kn, vn), _ = _append_case("f32", 60)
     codes = ora.encode_keys(k)
