@@ -11,7 +11,13 @@ stand in for them with the same shapes:
     multiplied by 20, the outlier structure the ADAMAS article's §2.1 describes
     the rotation smoothing out;
   * queries correlated with planted "needle" keys, a synthetic analogue of the
-    needle-retrieval evaluations the pages mention.
+    needle-retrieval evaluations the pages mention;
+  * for the quality sweep only, three more stand-ins (QUALITY_STANDINS): graded
+    relevance with outlier channels in the keys alone (no planted keys; the
+    query scaled so that its softmax weight spreads over many rows), and
+    needles of increasing noise (equal expected scores, decreasing similarity
+    to the query) with milder outliers shared by queries and keys, or with
+    the x20 outliers in the keys alone.
 
 Bulk normal draws use a torch generator on the requested device (so large
 caches are produced on the GPU); structural choices (outlier channels, scales,
@@ -40,13 +46,16 @@ class Workload:
     dtype: str            # "f32" | "bf16"
     layers: int
     seed: int
-    kind: str             # "tiny" (single planted key) | "needles"
+    kind: str             # "tiny" (single planted key) | "needles" | "graded"
     outlier_channels: int
     outlier_gain: float = 20.0
     sigma: float = 0.5    # lognormal sigma of the per-channel scales
     needles: int = 8      # planted needle keys per query head
     noise: float = 0.3    # standard deviation of the needle / query noise
+    noise_max: float = 0.0  # > noise: needle i's noise grows geometrically up to this
     chunk: int = 0        # prefill chunk appended per step (0: none)
+    score_std: float = 3.3  # "graded": std of the scores q.k/sqrt(d) over the keys
+    q_outliers: bool = True   # the query shares the keys' channel scales (outlier gain too)
 
     @property
     def torch_dtype(self):
@@ -68,6 +77,23 @@ BATCH16_64K = Workload("batch16-mha-64k-append4k", 16, 32, 32, 128, 65536, 65536
                        "bf16", 1, 1005, "needles", 3, chunk=4096)
 
 WORKLOADS = {w.name: w for w in (TINY, LLAMA2_32K, LLAMA2_128K_32L, LLAMA32_GQA_1M, BATCH16_64K)}
+
+# Quality-sweep stand-in with graded relevance (not a benchmark workload): the
+# 128K-token shape, outlier channels in K only.  With scores of standard
+# deviation 3.3 over 131072 keys, the exact softmax puts about half its weight
+# on the top 64 rows and about 80 % on the top 1024 (the weight of a Gaussian
+# score tilts to N(3.3, 1)), so the budget has something to gain.
+LLAMA2_128K_GRADED = LLAMA2_128K_32L.replace(name="llama2-mha-128k-kout-graded", kind="graded",
+                                             seed=1006, q_outliers=False)
+# Needles whose noise ramps from 0.3 to 3 (so a larger budget reaches more of
+# them), with 6 outlier channels of gain 4 shared by queries and keys (the
+# planted keys then hold most of the softmax weight, not random keys aligned
+# with the outliers), or with the x20 outliers in the keys alone.
+LLAMA2_128K_RAMP = LLAMA2_128K_32L.replace(name="llama2-mha-128k-needle-ramp", seed=1009,
+                                           noise_max=3.0, outlier_gain=4.0, outlier_channels=6)
+LLAMA2_128K_RAMP_KOUT = LLAMA2_128K_32L.replace(name="llama2-mha-128k-needle-ramp-kout",
+                                                seed=1007, noise_max=3.0, q_outliers=False)
+QUALITY_STANDINS = (LLAMA2_128K_32L, LLAMA2_128K_RAMP, LLAMA2_128K_RAMP_KOUT, LLAMA2_128K_GRADED)
 HEADLINE_BUDGETS = (64, 128, 256, 1024)
 
 
@@ -85,8 +111,11 @@ def _torch_gen(device, *key: int) -> torch.Generator:
     return g
 
 
-def channel_scales(w: Workload, layer: int, b: int, hkv: int, tensor: int) -> np.ndarray:
-    """Per-channel scale vector (float32, head_dim) for one KV head and tensor (0=K, 1=V)."""
+def channel_scales(w: Workload, layer: int, b: int, hkv: int, tensor: int,
+                   gain: bool = True) -> np.ndarray:
+    """Per-channel scale vector (float32, head_dim) for one KV head and tensor
+    (0=K, 1=V, 2=the graded stand-in's query); gain=False leaves the outlier
+    channels unscaled."""
     r = _np_rng(w.seed, layer, b, hkv, tensor, 7)
     d = w.head_dim
     if w.kind == "tiny":
@@ -94,8 +123,18 @@ def channel_scales(w: Workload, layer: int, b: int, hkv: int, tensor: int) -> np
     else:
         s = np.exp(w.sigma * r.standard_normal(d))
     ch = r.choice(d, size=w.outlier_channels, replace=False)
-    s[ch] *= w.outlier_gain
+    if gain:
+        s[ch] *= w.outlier_gain
     return s.astype(np.float32)
+
+
+def needle_noise(w: Workload, i: int) -> float:
+    """Noise level of needle i: w.noise, or a geometric ramp from w.noise to
+    w.noise_max over the needles (equal expected scores, decreasing
+    similarity to the query)."""
+    if w.noise_max <= w.noise or w.needles < 2:
+        return w.noise
+    return w.noise * (w.noise_max / w.noise) ** (i / (w.needles - 1))
 
 
 def needle_positions(w: Workload, layer: int, b: int, hkv: int, n_ctx: int) -> np.ndarray:
@@ -103,7 +142,7 @@ def needle_positions(w: Workload, layer: int, b: int, hkv: int, n_ctx: int) -> n
     G = w.hq // w.hkv
     r = _np_rng(w.seed, layer, b, hkv, 11)
     per = 1 if w.kind == "tiny" else w.needles
-    k = min(G * per, n_ctx)
+    k = min(G * per, n_ctx) if w.kind != "graded" else 0
     pos = r.choice(n_ctx, size=k, replace=False)
     out = np.full(G * per, -1, np.int64)
     out[:k] = pos
@@ -140,18 +179,29 @@ def make_layer(w: Workload, layer: int = 0, device="cpu", n_ctx: int | None = No
             pos = needle_positions(w, layer, b, h, n_ctx)
             needles[b, h] = pos
             gq = _torch_gen(dev, w.seed, layer, b, h, 2)
+            # a query scale vector without the outlier gain (q_outliers False)
+            sq_free = torch.from_numpy(channel_scales(w, layer, b, h, 2, gain=False)).to(dev)
             for j in range(G):
                 if w.kind == "tiny":
                     # q = a planted key plus N(0, noise) noise
                     p = int(pos[j, 0])
                     qf = kf[p] + w.noise * torch.randn((d,), generator=gq, device=dev)
+                elif w.kind == "graded":
+                    # q = kappa * (y * s_q), s_q without outlier gain; the keys'
+                    # scores q.k/sqrt(d) then have standard deviation
+                    # kappa * sqrt(sum_i y_i^2 s_q,i^2 s_k,i^2 / d) = score_std
+                    sq = sk if w.q_outliers else sq_free
+                    y = torch.randn((d,), generator=gq, device=dev) * sq
+                    spread = torch.sqrt(torch.sum((y.double() * sk.double()) ** 2) / d)
+                    qf = (y * (w.score_std / float(spread))).float()
                 else:
                     # q = u; the needle keys are u plus scaled noise
-                    u = torch.randn((d,), generator=gq, device=dev) * sk
-                    for p in pos[j]:
+                    u = torch.randn((d,), generator=gq, device=dev) * (
+                        sk if w.q_outliers else sq_free)
+                    for i, p in enumerate(pos[j]):
                         if p >= 0:
-                            kf[int(p)] = u + w.noise * torch.randn((d,), generator=gq,
-                                                                    device=dev) * sk
+                            kf[int(p)] = u + needle_noise(w, i) * torch.randn(
+                                (d,), generator=gq, device=dev) * sk
                     qf = u
                 q[b, h * G + j] = qf.to(dt)
             k[b, h] = kf.to(dt)

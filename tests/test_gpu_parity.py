@@ -446,7 +446,7 @@ def test_decode_f16_rotation(ora, restore_rotation, restore_mode, mode):
 
 def test_quality_dense_reference_matches_oracle(ora):
     # the sweep's dense reference is exact attention over every row
-    from compressed_key_sparse_amd.quality import dense_attention
+    from quality import dense_attention
     w = synth.LLAMA32_GQA_1M.replace(hq=6, hkv=2, n_ctx=2000, cap=2000)
     lay = synth.make_layer(w, 0, DEV)
     got = dense_attention(lay["q"], lay["k"], lay["v"])
