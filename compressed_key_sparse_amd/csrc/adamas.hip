@@ -166,6 +166,9 @@ size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx, int
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_ctx < 1 || budget < 1 ||
       budget > kMaxBudget || !valid_dim(head_dim))
     return 0;
+  // the limits every entry point enforces (and which keep the plans' sizes
+  // far from overflowing)
+  if (n_ctx > INT32_MAX || (int64_t)B * Hq > kMaxGroups || Hq > 65535 || B > 65535) return 0;
   if (op == ADAMAS_OP_DECODE_STEP && Hq / Hkv > kMaxG) return 0;
   const int64_t rows = (int64_t)B * Hq;
   switch (op) {
@@ -186,8 +189,11 @@ int adamas_encode_keys(const void* x, int dtype, int batch, int heads, int64_t n
                        uint8_t* codes, int64_t cap, int64_t pos, void* x_copy_dst,
                        hipStream_t stream) {
   if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
-  if (batch < 1 || heads < 1 || n < 0 || pos < 0 || cap < 1 || pos + n > cap)
+  if (batch < 1 || heads < 1 || n < 0 || pos < 0 || cap < 1 || pos > cap || n > cap - pos)
     return ADAMAS_ERR_INVALID;
+  // x and the code cache must be addressable: batch * heads * cap rows of up
+  // to 256 elements (the products below then cannot overflow)
+  if (cap > (INT64_MAX / 1024) / ((int64_t)batch * heads)) return ADAMAS_ERR_INVALID;
   if (!aligned16(x) || !aligned16(codes)) return ADAMAS_ERR_INVALID;
   if (x_copy_dst != nullptr && !aligned16(x_copy_dst)) return ADAMAS_ERR_INVALID;
   if (n == 0) return ADAMAS_OK;
@@ -686,6 +692,7 @@ size_t adamas_static_scratch_need(int B, int Hq, int Hkv, int64_t n_ctx, int bud
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_ctx < 1 || budget < 1 ||
       budget > kMaxBudget || !valid_dim(head_dim) || Hq / Hkv > kMaxG)
     return 0;
+  if (n_ctx > INT32_MAX || (int64_t)B * Hq > kMaxGroups || Hq > 65535 || B > 65535) return 0;
   return plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).total;
 }
 

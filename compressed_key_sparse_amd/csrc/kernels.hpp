@@ -55,8 +55,9 @@ constexpr int kAttendRowsPerSlot = 4;  // rows a 16-lane slot holds in flight
 constexpr int kAttendRowsPerBatch = (kAttendThreads / 16) * kAttendRowsPerSlot;  // 256
 
 // ------------------------------------------------------------------ encode
-// §2.1 + §2.2 + §3.1 for keys (or queries): one wavefront per vector,
-// grid-stride over the batch*heads*n vectors of x[batch*heads][n][D].
+// §2.1 + §2.2 + §3.1 for keys (or queries): one 16-lane slot per vector
+// (kEncodeThreads / 16 vectors per workgroup), grid-stride over the
+// batch*heads*n vectors of x[batch*heads][n][D].
 template <int D>
 __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restrict__ x,
                                                            int is_bf16, int64_t n, int64_t nvec,

@@ -413,11 +413,14 @@ int adamas_decode_step_static(const void *q, const void *k, const void *v,
                               int head_dim, int64_t cap, int64_t n_ctx, int budget, float scale,
                               void *out, int32_t *idx_out, hipStream_t stream);
 
-/* Scratch bytes adamas_decode_step_static needs for a shape (0 if invalid). */
+/* Scratch bytes adamas_decode_step_static needs for a shape (0 if invalid or
+ * beyond the decode step's limits). */
 size_t adamas_static_scratch_need(int B, int Hq, int Hkv, int64_t n_ctx, int budget,
                                   int head_dim);
 
-/* Workspace bytes needed by `op` for the given shape (0 for invalid shapes). */
+/* Workspace bytes needed by `op` for the given shape (0 for invalid shapes and
+ * for shapes beyond the entry points' limits: n_ctx > INT32_MAX, B or Hq >
+ * 65535, B*Hq > 8192). */
 size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx,
                               int budget, int head_dim);
 
