@@ -26,7 +26,7 @@ __all__ = [
     "DECODE_GROUP_WAIT", "DECODE_SPLIT", "WS_CTRL_BYTES", "WS_STATUS_OFFSET", "ROTATE_OFF",
     "ROTATE_F32", "ROTATE_F16", "GroupWaitGaveUp", "set_wait_polls", "wait_polls",
     "DEFAULT_WAIT_POLLS", "PhaseRecorder", "decode_step_static", "STATIC_SCRATCH_BYTES",
-    "set_bucket_alpha", "bucket_alpha", "MAX_ALPHA_GROUPS",
+    "set_bucket_alpha", "bucket_alpha", "MAX_ALPHA_GROUPS", "decode_key_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -115,6 +115,7 @@ def load(variant: str | None = None):
     lib.adamas_bucket_alpha.argtypes = [P, i32]
     lib.adamas_bucket_alpha.restype = i32
     lib.adamas_decode_path.argtypes = [i32, i32, i32, i64, i32, i32]
+    lib.adamas_decode_key_bytes.argtypes = [i32, i32, i32, i64, i32, i32]
     lib.adamas_set_wait_polls.argtypes = [ctypes.c_uint32]
     lib.adamas_set_wait_polls.restype = i32
     lib.adamas_decode_step_static.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32,
@@ -410,6 +411,16 @@ def set_wait_polls(polls: int) -> None:
 def wait_polls() -> int:
     """The current group-wait bound (adamas_wait_polls)."""
     return int(load().adamas_wait_polls())
+
+
+def decode_key_bytes(B: int, Hq: int, Hkv: int, n_ctx: int, budget: int, head_dim: int) -> int:
+    """Bytes per chunk key the fused decode kernel keeps for this shape: 2, or 1
+    where grouped heads would otherwise take several rounds of workgroups
+    (adamas_decode_key_bytes)."""
+    r = load().adamas_decode_key_bytes(B, Hq, Hkv, n_ctx, budget, head_dim)
+    if r < 0:
+        raise AdamasError(-r, "adamas_decode_key_bytes")
+    return r
 
 
 def set_decode_mode(mode: int) -> None:

@@ -178,9 +178,11 @@ size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx, int
     case ADAMAS_OP_SPARSE_ATTEND:
       return round_up(plan_attend(rows, budget, head_dim, ADAMAS_WS_CTRL_BYTES).end, 256);
     case ADAMAS_OP_DECODE_STEP:
+      // every schedule and key width a decode step of this shape may take
       return std::max(
-          plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).total,
-          plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, kSizingCapacity).total);
+          {plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim, true).total,
+           plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim, false).total,
+           plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, kSizingCapacity).total});
     default: return 0;
   }
 }
@@ -484,7 +486,7 @@ int ragged_step(const void* q, const void* k_new, const void* v_new, void* k, vo
                                         head_dim))
     return ADAMAS_ERR_WORKSPACE;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  DecodePlan p = plan_decode(B, Hq, Hkv, max_len, budget, head_dim);
+  DecodePlan p = plan_decode(B, Hq, Hkv, max_len, budget, head_dim, false);
   if (ws_bytes < p.total) return ADAMAS_ERR_WORKSPACE;
   // paged with fused attention: the final workgroup keeps the page table row
   // in LDS after the candidate tile, when it is short and fits
@@ -603,6 +605,15 @@ int adamas_set_decode_mode(int mode) {
     return ADAMAS_ERR_INVALID;
   g_decode_mode.store(mode, std::memory_order_relaxed);
   return ADAMAS_OK;
+}
+
+int adamas_decode_key_bytes(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_ctx < 1 || budget < 1 ||
+      budget > kMaxBudget || !valid_dim(head_dim) || Hq / Hkv > kMaxG)
+    return -ADAMAS_ERR_INVALID;
+  if (n_ctx > INT32_MAX || (int64_t)B * Hq > kMaxGroups || Hq > 65535 || B > 65535)
+    return -ADAMAS_ERR_UNSUPPORTED;
+  return plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).u8 ? 1 : 2;
 }
 
 int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim) {

@@ -17,10 +17,10 @@
 
 namespace adm_host {
 
-template <int D, int G, bool BF, int RAG, bool OCC>
+template <int D, int G, bool BF, int RAG, bool OCC, bool U8 = false>
 void launch_decode_k(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
-  allow_lds(&k_decode<D, G, BF, RAG, OCC>, p.sel.lds);
-  k_decode<D, G, BF, RAG, OCC><<<grid, kDecodeThreads, p.sel.lds, s>>>(
+  allow_lds(&k_decode<D, G, BF, RAG, OCC, U8>, p.sel.lds);
+  k_decode<D, G, BF, RAG, OCC, U8><<<grid, kDecodeThreads, p.sel.lds, s>>>(
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
       p.sel.kpad_log2, p.sel.mcap, (p.fuse && !a.chist) ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
       a.out, a.n_sink, a.n_recent, a.rule, a.rg, RAG ? nullptr : a.chist,
@@ -34,6 +34,12 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
   const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
   const bool occ = G == 1 && wgs > kComputeUnits && 2 * p.sel.lds <= kLdsDecodeLimit;
   const int rag = a.rg.lens == nullptr ? 0 : (a.rg.pages == nullptr ? 1 : 2);
+  if constexpr (G >= 2 && D <= 128) {
+    if (p.u8 && rag == 0) {
+      launch_decode_k<D, G, BF, 0, false, true>(p, grid, s, a);
+      return;
+    }
+  }
   if constexpr (G == 1) {
     if (occ) {
       if (rag == 2)

@@ -749,9 +749,11 @@ ADM_DEV void key_masks(const uint32_t* ws, int t, uint32_t& ge, uint32_t& gt) {
 // kept.  Thread j owns tokens [16j, 16j+16), read once with 16-byte LDS loads
 // (threads past the chunk own nothing).
 constexpr int kCompactTpt = 16;
+// With tot_out, thread 0 gets (#below t) | (#at t) << 16 over the chunk there.
 template <int NT, class Emit, int TPT = kCompactTpt>
 ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t quota,
-                               uint32_t* s_tmp, Emit&& emit, const PhaseStamps* ps = nullptr) {
+                               uint32_t* s_tmp, Emit&& emit, const PhaseStamps* ps = nullptr,
+                               uint32_t* tot_out = nullptr) {
   static_assert(TPT % 8 == 0 && TPT <= 16, "whole 16-byte reads, one 16-bit mask");
   const int t0 = threadIdx.x * TPT;
   uint32_t ltm = 0, eqm = 0;  // bit i: token t0+i is below / at the threshold
@@ -792,6 +794,7 @@ ADM_DEV uint32_t chunk_collect(const uint16_t* sdist, int valid, int t, uint32_t
     }
   }
   if (ps) ps->mark_last_wave(19);  // tokens emitted
+  if (tot_out != nullptr && threadIdx.x == 0) *tot_out = tot;
   const uint32_t eq_all = tot >> 16;
   return (tot & 0xffffu) + (eq_all < quota ? eq_all : quota);
 }
@@ -904,6 +907,134 @@ ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* 
   }
   if (ps) ps->mark_last_wave(19);  // tokens emitted
   lds_sync();
+}
+
+// chunk_compact_heads over 8-bit keys: sdist8 [G][chunk] holds min(key, 255),
+// the histograms the exact keys.  Thread j owns tokens [32j, 32j + 32)
+// (chunk <= 32 * NT).  When every head's threshold key is below 255, a
+// stored key below the threshold is exact, 255 can only mean "above it", and
+// the result is chunk_compact_heads' on the exact keys; the function then
+// emits and returns true.  Otherwise (some head's kc-th smallest key is 255
+// or more) it emits nothing and returns false, with the thresholds in s_thr
+// and the staging rows' tails already set; the caller must then select from
+// exact keys.
+constexpr int kKeySat = 255;
+// Bytewise x < y over the four bytes of two words, as bit 7 of each byte of
+// the result (no borrow crosses a byte): below in the high bit, or equal high
+// bits and below in the low seven, the latter read from
+// (x | 0x80) - (y & 0x7f) per byte, whose high bit is set iff x's low seven
+// bits are not below y's.
+ADM_DEV uint32_t bytes_below(uint32_t x, uint32_t y) {
+  const uint32_t z = (x | 0x80808080u) - (y & 0x7F7F7F7Fu);
+  return ((~x & y) | (~(x ^ y) & ~z)) & 0x80808080u;
+}
+template <int NT, int NB, int G>
+ADM_DEV bool chunk_compact_heads_u8(const uint32_t* hist, int nbp, const uint8_t* sdist8,
+                                    int chunk, int valid, uint32_t kc, uint32_t* out, int kpad,
+                                    uint32_t* s_thr, uint32_t* s_sums,
+                                    const PhaseStamps* ps = nullptr) {
+  constexpr int NW = NT / kWave, BPL = (NB + kWave - 1) / kWave, TPT = 32;
+  static_assert(G <= NW, "one wavefront per head finds its threshold");
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  if (wid < G) {  // thresholds, as chunk_compact_heads
+    const uint32_t* h = hist + wid * nbp;
+    uint32_t v[BPL], sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int bin = lane * BPL + j;
+      v[j] = bin < NB ? h[bin] : 0u;
+      sum += v[j];
+    }
+    const uint32_t incl = wave_scan_incl(sum), excl = incl - sum;
+    if (excl < kc && kc <= incl) {
+      uint32_t acc = excl, lt = 0;
+      int t = 0;
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {
+        if (acc < kc && kc <= acc + v[j]) {
+          t = lane * BPL + j;
+          lt = acc;
+        }
+        acc += v[j];
+      }
+      s_thr[2 * wid] = (uint32_t)t;
+      s_thr[2 * wid + 1] = lt;
+    }
+  }
+  for (int i = threadIdx.x; i < G * kpad; i += NT) {
+    const int g = i / kpad, j = i - g * kpad;
+    if ((uint32_t)j >= kc) out[i] = 0xFFFFFFFFu;
+  }
+  lds_sync();
+  if (ps) ps->mark(16);  // thresholds found
+  bool exact = true;
+#pragma unroll
+  for (int g = 0; g < G; ++g) exact = exact && s_thr[2 * g] < (uint32_t)kKeySat;
+  if (!exact) return false;
+  // four keys per word, compared bytewise without borrows between bytes:
+  // counts of keys below t and up to t, and a 32-bit mask of this thread's
+  // tokens with key <= t (the ones the emission visits)
+  const int t0 = threadIdx.x * TPT;
+  const int nv = valid - t0;
+  uint32_t hit[G], mine[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint32_t t = s_thr[2 * g];
+    const uint32_t y = t * 0x01010101u, y1 = (t + 1u) * 0x01010101u;
+    uint32_t nlt = 0, nle = 0, h = 0;
+    if (t0 < valid) {
+      const uint4* src = reinterpret_cast<const uint4*>(sdist8 + g * chunk + t0);
+      const uint4 a = src[0], b4 = src[1];
+      const uint32_t w[TPT / 4] = {a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int j = 0; j < TPT / 4; ++j) {
+        const uint32_t x = w[j];
+        const int left = nv - 4 * j;  // keys past the chunk's valid end count nowhere
+        const uint32_t vm =
+            left >= 4 ? 0x80808080u : (left <= 0 ? 0u : 0x80808080u >> (32 - 8 * left));
+        const uint32_t lt = bytes_below(x, y) & vm, le = bytes_below(x, y1) & vm;
+        nlt += (uint32_t)__popc(lt);
+        nle += (uint32_t)__popc(le);
+        h |= (((le >> 7) * 0x01020408u) >> 24) << (4 * j);  // bit k of byte k -> bit 4j + k
+      }
+    }
+    hit[g] = h;
+    mine[g] = nlt | ((nle - nlt) << 16);
+  }
+  if (ps) ps->mark_last_wave(17);  // masks of every head done
+  uint32_t incl[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    incl[g] = wave_scan_incl(mine[g]);
+    if (lane == kWave - 1) s_sums[wid * G + g] = incl[g];
+  }
+  lds_sync();
+  if (ps) ps->mark(18);  // prefix over the workgroup
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint32_t pre = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) pre += w < wid ? s_sums[w * G + g] : 0u;
+    const uint32_t ex = pre + incl[g] - mine[g];
+    uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
+    const uint32_t quota = kc - s_thr[2 * g + 1];
+    const uint32_t t = s_thr[2 * g];
+    uint32_t* o = out + g * kpad;
+    for (uint32_t m = hit[g]; m != 0; m &= m - 1) {
+      const uint32_t tok = (uint32_t)(t0 + __ffs(m) - 1);
+      const uint32_t d = sdist8[g * chunk + tok];
+      if (d < t) {
+        o[ltb + (eqb < quota ? eqb : quota)] = (d << 16) | tok;
+        ++ltb;
+      } else {
+        if (eqb < quota) o[ltb + eqb] = (t << 16) | tok;
+        ++eqb;
+      }
+    }
+  }
+  if (ps) ps->mark_last_wave(19);  // tokens emitted
+  lds_sync();
+  return true;
 }
 
 // chunk_collect into out[] (LDS) as (D << 16) | token; entries [kept, pad_to)

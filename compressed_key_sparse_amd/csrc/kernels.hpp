@@ -250,6 +250,65 @@ ADM_DEV void scan_chunk(const Src& src, int valid, const QPlanes (&qp)[G], Sink&
   }
 }
 
+// scan_units with 8-bit keys (head_dim 64 and 128): each token's key
+// key(tok, d) is counted in hist (exact) and stored as min(key, 255) in
+// sdist8 [G][chunk].
+template <int D, int G, int NT, int U, class Src, class KeyFn>
+ADM_DEV void scan_units_u8(const Src& src, const uint4 (&w)[U], int base, int units,
+                           const QPlanes (&qp)[G], KeyFn&& keyfn, uint32_t* shist, int nbp,
+                           uint8_t* sdist8, int chunk) {
+  constexpr int K = D / 64;  // lanes per token
+  static_assert(K == 1 || K == 2, "8-bit keys for head_dim 64 and 128");
+  const int bnd = src.bound(units);
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int u = src.template unit<NT>(base, j);
+    const uint32_t p0 = therm_p(w[j].x), p1 = therm_p(w[j].y);
+    const uint32_t p2 = therm_p(w[j].z), p3 = therm_p(w[j].w);
+    const uint32_t t0 = therm_t(w[j].x, w[j].y), t1 = therm_t(w[j].z, w[j].w);
+    uint32_t dg[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      uint32_t s = __popc(p0 ^ qp[g].p[0]);
+      s = popc_acc(p1 ^ qp[g].p[1], s);
+      s = popc_acc(p2 ^ qp[g].p[2], s);
+      s = popc_acc(p3 ^ qp[g].p[3], s);
+      s = popc_acc(t0 ^ qp[g].t[0], s);
+      s = popc_acc(t1 ^ qp[g].t[1], s);
+      if constexpr (K == 2) s += swap_pair(s);
+      dg[g] = s;
+    }
+    if (u < bnd && (threadIdx.x & (K - 1)) == 0) {
+      const int tok = u / K;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t key = keyfn(tok, dg[g]);
+        atomicAdd(&shist[g * nbp + key], 1u);
+        sdist8[g * chunk + tok] = (uint8_t)(key < (uint32_t)kKeySat ? key : (uint32_t)kKeySat);
+      }
+    }
+  }
+}
+
+template <int D, int G, int NT, int U, class Src, class KeyFn>
+ADM_DEV void scan_chunk_u8(const Src& src, int valid, const QPlanes (&qp)[G], KeyFn&& keyfn,
+                           uint32_t* shist, int nbp, uint8_t* sdist8, int chunk,
+                           const uint4 (*first)[U] = nullptr) {
+  constexpr int kUnitsPerToken = D / 64, kStep = Src::template step<NT, U>();
+  const int units = valid * kUnitsPerToken, lim = src.limit(units);
+  int base = 0;
+  if (first != nullptr) {
+    if (lim > 0)
+      scan_units_u8<D, G, NT, U>(src, *first, 0, units, qp, keyfn, shist, nbp, sdist8, chunk);
+    base = kStep;
+  }
+  for (; base < lim; base += kStep) {
+    uint4 w[U];
+    scan_load<NT, U>(src, units, base, w);
+    scan_units_u8<D, G, NT, U>(src, w, base, units, qp, keyfn, shist, nbp, sdist8, chunk);
+  }
+}
+
 // Query planes for this thread's part of the row (D/64 consecutive lanes hold
 // one token's units; lane t of them takes words 4t..4t+3) from packed words in
 // LDS.
@@ -688,7 +747,13 @@ struct RaggedArgs {
 // then overlaps the other's scan.
 // RAG: 0 every sequence holds n_ctx rows; 1 ragged (RaggedArgs); 2 ragged
 // over paged pools.
-template <int D, int G, bool BF, int RAG, bool OCC = false>
+// U8 (grouped heads, head_dim <= 128, RAG 0): the chunk's keys are kept in
+// LDS as min(key, 255), one byte per (head, token), which fits twice the
+// chunk of 16-bit keys; a launch that would need two rounds of workgroups
+// then runs in one.  Keys below a chunk threshold under 255 are exact; a
+// chunk where some head's threshold reaches 255 rescans its codes half a
+// chunk at a time with exact 16-bit keys.
+template <int D, int G, bool BF, int RAG, bool OCC = false, bool U8 = false>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(OCC ? 8 : 1)))
 void k_decode(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -714,8 +779,12 @@ void k_decode(
   uint32_t* shist = sq + (G + 1) * W;
   const int n_stage = stage_heads(G, 1 << kpad_log2);
   uint32_t* sstage = shist + G * NBP;  // chunk candidates of n_stage heads
+  static_assert(!U8 || (G >= 2 && D <= 128 && RAG == 0 && !OCC), "8-bit key variant");
   uint16_t* sdist = reinterpret_cast<uint16_t*>(sstage + n_stage * (1 << kpad_log2));
-  uint32_t* s_fused = reinterpret_cast<uint32_t*>(sdist + G * chunk);  // 2G + NW*G words
+  uint8_t* sdist8 = reinterpret_cast<uint8_t*>(sdist);  // U8: [G][chunk] bytes
+  uint32_t* s_fused = reinterpret_cast<uint32_t*>(
+      U8 ? static_cast<void*>(sdist8 + G * chunk)
+         : static_cast<void*>(sdist + G * chunk));  // 2G + NW*G words
   // phase 2 (final selection + attention) layout, aliasing phase 1
   uint32_t* fhist = reinterpret_cast<uint32_t*>(region);
   float* s_part = reinterpret_cast<float*>(fhist + NBP);
@@ -844,7 +913,16 @@ void k_decode(
   // a chunk without always-kept tokens (the common case) skips the range test
   // (not in the paged two-per-CU build, where the second copy of the scan
   // costs spills under its 64-register cap)
-  if (!(OCC && RAG == 2) && keep.keeps_none(valid_mem))
+  if constexpr (U8) {
+    if (keep.keeps_none(valid_mem))
+      scan_chunk_u8<D, G, NT, kDecodeScanDepth>(
+          src, valid_mem, qp, [](int, uint32_t d) { return d + 1u; }, shist, NBP, sdist8, chunk,
+          &first);
+    else
+      scan_chunk_u8<D, G, NT, kDecodeScanDepth>(
+          src, valid_mem, qp, [&](int tok, uint32_t d) { return keep.key(tok, d); }, shist, NBP,
+          sdist8, chunk, &first);
+  } else if (!(OCC && RAG == 2) && keep.keeps_none(valid_mem))
     scan_chunk<D, G, NT, kDecodeScanDepth>(
         src, valid_mem, qp, [&](int g, int tok, uint32_t d) { sink(g, tok, d + 1u); }, &first);
   else
@@ -884,8 +962,57 @@ void k_decode(
   bool staged = false;
   if constexpr (G >= 2) {
     if (n_stage == G) {
-      chunk_compact_heads<NT, NB, G>(shist, NBP, sdist, chunk, valid, (uint32_t)kc, sstage, kpad,
-                                     s_fused, s_fused + 2 * G, &ps);
+      if constexpr (U8) {
+        const bool exact = chunk_compact_heads_u8<NT, NB, G>(
+            shist, NBP, sdist8, chunk, valid, (uint32_t)kc, sstage, kpad, s_fused,
+            s_fused + 2 * G, &ps);
+        if constexpr (3 * D + 1 >= kKeySat) {
+          if (!exact) {
+            // exact 16-bit keys, half a chunk at a time, in the bytes' place;
+            // s_tot: per head the (below, at) counts of earlier halves, and
+            // the count chunk_collect reports
+            constexpr int kHalf = NT * kCompactTpt;
+            uint16_t* sd16 = reinterpret_cast<uint16_t*>(sdist8);
+            uint32_t* s_thr = s_fused;
+            uint32_t* s_tot = s_fused + 2 * G;
+            if ((int)threadIdx.x < 2 * G) s_tot[threadIdx.x] = 0u;
+            QPlanes qh[G];
+            load_qplanes<D, G>(sq, qh);
+            for (int h0 = 0; h0 < valid; h0 += kHalf) {
+              const int hv = min(kHalf, valid - h0);
+              lds_sync();
+              scan_chunk<D, G, NT, kDecodeScanDepth>(
+                  ContigCodes{src.p + (int64_t)h0 * (D / 64)}, hv, qh,
+                  [&](int g, int tok, uint32_t d) {
+                    sd16[g * kHalf + tok] = (uint16_t)keep.key(h0 + tok, d);
+                  });
+              lds_sync();
+              for (int g = 0; g < G; ++g) {
+                const uint32_t t = s_thr[2 * g], quota = (uint32_t)kc - s_thr[2 * g + 1];
+                const uint32_t ltp = s_tot[2 * g], eqp = s_tot[2 * g + 1];
+                const uint32_t taken = eqp < quota ? eqp : quota, off = ltp + taken;
+                uint32_t* o = sstage + g * kpad;
+                chunk_collect<NT>(
+                    sd16 + g * kHalf, hv, (int)t, quota - taken, s_tmp,
+                    [&](uint32_t pos, uint32_t tok, uint32_t key) {
+                      o[off + pos] = (key << 16) | (uint32_t)(h0 + (int)tok);
+                    },
+                    nullptr, s_tot + 2 * G);
+                lds_sync();
+                if (threadIdx.x == 0) {
+                  const uint32_t tot = s_tot[2 * G];
+                  s_tot[2 * g] = ltp + (tot & 0xffffu);
+                  s_tot[2 * g + 1] = eqp + (tot >> 16);
+                }
+                lds_sync();
+              }
+            }
+          }
+        }
+      } else {
+        chunk_compact_heads<NT, NB, G>(shist, NBP, sdist, chunk, valid, (uint32_t)kc, sstage,
+                                       kpad, s_fused, s_fused + 2 * G, &ps);
+      }
       ps.mark(4);
       for (int g = 0; g < G; ++g) {
         const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;

@@ -94,10 +94,11 @@ inline int cand_slot(int budget, int chunk) {
   while (k < kmax) k *= 2;
   return k;
 }
-inline size_t decode_lds_scan(int D, int G, int c, int budget) {
+// key_bytes: 2, or 1 for the 8-bit key variant
+inline size_t decode_lds_scan(int D, int G, int c, int budget, int key_bytes = 2) {
   const int kpad = cand_slot(budget, c);
   return (size_t)(G + 1) * (D / 16) * 4 + (size_t)G * nbins_padded(D) * 4 +
-         (size_t)stage_heads(G, kpad) * kpad * 4 + (size_t)G * c * 2 +
+         (size_t)stage_heads(G, kpad) * kpad * 4 + (size_t)G * c * key_bytes +
          (size_t)(2 + kDecodeThreads / kWave) * G * 4;
 }
 // sel_rows = min(budget, n_ctx) indices are kept in LDS only when attention is fused.
@@ -123,6 +124,7 @@ inline AttendPlan plan_attend(int64_t rows, int sel_rows, int D, size_t start) {
 
 struct DecodePlan {
   SelectPlan sel;
+  bool u8 = false;  // k_decode keeps 8-bit keys (fewer rounds of workgroups)
   bool fuse = false;
   size_t idx_off = 0;
   AttendPlan att;
@@ -147,16 +149,39 @@ inline size_t split_select_lds(int D, int ncp, bool fused) {
 // adamas_decode_step: 1024-thread workgroups, chunks as large as LDS allows
 // (fewer candidates to merge), attention fused into the selecting workgroup
 // when the selection is small (at most two 256-row batches for the group).
-inline DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D) {
+// allow_u8: the launch may take the 8-bit key variant of k_decode (plain
+// contiguous decode steps; the ragged and paged steps keep 16-bit keys).
+inline DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D,
+                              bool allow_u8 = true) {
   DecodePlan p;
   const int G = Hq / Hkv;
   const int64_t rows = (int64_t)B * Hq;
-  int c = 16384;
-  while (c > 1024 && kTmpWords * 4 + decode_lds_scan(D, G, c, budget) > kLdsDecodeLimit) c /= 2;
-  while (c > 1024 && (int64_t)(c / 2) >= n_ctx) c /= 2;
-  // shorter chunks while the whole launch still fits one workgroup per
-  // compute unit: more of the device streams the code cache
-  while (c > 1024 && (int64_t)B * Hkv * ((n_ctx + c / 2 - 1) / (c / 2)) <= kComputeUnits) c /= 2;
+  auto chunk_for = [&](int c0, int key_bytes) {
+    int c = c0;
+    while (c > 1024 && kTmpWords * 4 + decode_lds_scan(D, G, c, budget, key_bytes) > kLdsDecodeLimit)
+      c /= 2;
+    while (c > 1024 && (int64_t)(c / 2) >= n_ctx) c /= 2;
+    // shorter chunks while the whole launch still fits one workgroup per
+    // compute unit: more of the device streams the code cache
+    while (c > 1024 && (int64_t)B * Hkv * ((n_ctx + c / 2 - 1) / (c / 2)) <= kComputeUnits)
+      c /= 2;
+    return c;
+  };
+  auto rounds = [&](int c) {
+    return ((int64_t)B * Hkv * ((n_ctx + c - 1) / c) + kComputeUnits - 1) / kComputeUnits;
+  };
+  int c = chunk_for(16384, 2);
+  // grouped heads whose 16-bit keys cap the chunk so that the launch takes
+  // more than one round: 8-bit keys hold chunks twice as long (up to 32768
+  // tokens, one compaction thread per 32), when that saves rounds and every
+  // head's candidates stage at once
+  if (allow_u8 && G >= 2 && D <= 128 && rounds(c) > 1) {
+    const int c8 = chunk_for(32768, 1);
+    if (rounds(c8) < rounds(c) && stage_heads(G, cand_slot(budget, c8)) == G) {
+      c = c8;
+      p.u8 = true;
+    }
+  }
   p.sel.chunk = c;
   finish_select_plan(p.sel, rows, n_ctx, budget, ADAMAS_WS_CTRL_BYTES);
   const int bsel = (int)(n_ctx < budget ? n_ctx : budget);
@@ -167,7 +192,7 @@ inline DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget,
   while (p.sel.mcap > 256 &&
          kTmpWords * 4 + decode_lds_final(D, sidx_rows, p.sel.mcap) > kLdsDecodeLimit)
     p.sel.mcap = (p.sel.mcap / 2 + 3) & ~3;
-  p.sel.lds = kTmpWords * 4 + std::max(decode_lds_scan(D, G, c, budget),
+  p.sel.lds = kTmpWords * 4 + std::max(decode_lds_scan(D, G, c, budget, p.u8 ? 1 : 2),
                                        decode_lds_final(D, sidx_rows, p.sel.mcap));
   p.idx_off = round_up(p.sel.end, 256);
   const size_t idx_end = p.idx_off + (size_t)rows * budget * sizeof(int32_t);

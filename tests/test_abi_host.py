@@ -301,3 +301,23 @@ def test_bucket_alpha_setter(lib):
     assert adamas.bucket_alpha() == [pytest.approx(0.3)]
     adamas.set_bucket_alpha(None)
     assert adamas.bucket_alpha() == []
+
+
+def test_decode_key_bytes_planning(lib):
+    """Grouped heads that would need two rounds of workgroups with 16-bit
+    chunk keys plan 8-bit keys; MHA, head_dim 256 and one-round launches keep
+    16-bit keys; invalid shapes raise."""
+    kb = adamas.decode_key_bytes
+    assert kb(1, 24, 8, 1048576, 1024, 128) == 1      # the 1M-token GQA layer
+    assert kb(1, 24, 8, 1048576, 1024, 64) == 1
+    assert kb(1, 32, 32, 131072, 256, 128) == 2       # MHA
+    assert kb(1, 24, 8, 1048576, 1024, 256) == 2      # head_dim 256
+    assert kb(1, 24, 8, 32768, 256, 128) == 2         # one round either way
+    assert kb(2, 24, 8, 300000, 1024, 128) == 1       # the GPU parity shapes
+    assert kb(16, 4, 2, 140000, 256, 128) == 1
+    assert kb(16, 4, 2, 140000, 1024, 128) == 1
+    with pytest.raises(adamas.AdamasError):
+        kb(1, 24, 7, 1000, 64, 128)
+    # the workspace covers both key widths of a shape
+    ws = lib.adamas_workspace_bytes(2, 2, 24, 8, 300000, 1024, 128)
+    assert ws > 0
