@@ -182,7 +182,8 @@ size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx, int
       return std::max(
           {plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim, true).total,
            plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim, false).total,
-           plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, kSizingCapacity).total});
+           plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, kSizingCapacity, true).total,
+           plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, kComputeUnits, true).total});
     default: return 0;
   }
 }
@@ -396,7 +397,8 @@ int decode_step_impl(const void* q, const void* k, const void* v, const uint8_t*
   // for the latter
   if (!no_group_wait &&
       (mode == ADAMAS_DECODE_GROUP_WAIT || (mode == ADAMAS_DECODE_AUTO && (!p.fuse || many)))) {
-    const GroupPlan gp = plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, device_capacity());
+    const GroupPlan gp = plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, device_capacity(),
+                                        mode == ADAMAS_DECODE_GROUP_WAIT);
     if (gp.ok) {
       if (ws_bytes < gp.total) return ADAMAS_ERR_WORKSPACE;
       DecodeArgs a{q, k, v, k_codes, Hq, Hkv, cap, n_ctx, budget, attend_qscale(scale, head_dim),
@@ -613,6 +615,15 @@ int adamas_decode_key_bytes(int B, int Hq, int Hkv, int64_t n_ctx, int budget, i
     return -ADAMAS_ERR_INVALID;
   if (n_ctx > INT32_MAX || (int64_t)B * Hq > kMaxGroups || Hq > 65535 || B > 65535)
     return -ADAMAS_ERR_UNSUPPORTED;
+  // the group-wait kernel when the current mode would take it on this device
+  const int path = adamas_decode_path(B, Hq, Hkv, n_ctx, budget, head_dim);
+  if (path == ADAMAS_DECODE_GROUP_WAIT)
+    return plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, device_capacity(),
+                          g_decode_mode.load(std::memory_order_relaxed) ==
+                              ADAMAS_DECODE_GROUP_WAIT)
+                   .u8
+               ? 1
+               : 2;
   return plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).u8 ? 1 : 2;
 }
 
@@ -629,7 +640,8 @@ int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int he
   if (mode == ADAMAS_DECODE_AUTO && p.fuse && !many) return ADAMAS_DECODE_LAST_ARRIVAL;
   const int64_t capacity = device_capacity();
   if (capacity <= 0) return -ADAMAS_ERR_DEVICE;
-  if (plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, capacity).ok)
+  if (plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, capacity,
+                     mode == ADAMAS_DECODE_GROUP_WAIT).ok)
     return ADAMAS_DECODE_GROUP_WAIT;
   if (mode == ADAMAS_DECODE_GROUP_WAIT) return -ADAMAS_ERR_UNSUPPORTED;
   return many && p.split_ok ? ADAMAS_DECODE_SPLIT : ADAMAS_DECODE_LAST_ARRIVAL;

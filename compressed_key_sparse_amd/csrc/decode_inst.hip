@@ -59,16 +59,29 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
     launch_decode_k<D, G, BF, 0, false>(p, grid, s, a);
 }
 
-template <int D, int G, bool BF>
-void launch_decode_gs_t(const GroupPlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a,
+template <int D, int G, bool BF, bool U8>
+void launch_decode_gs_k(const GroupPlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a,
                         uint8_t* w) {
-  k_decode_gs<D, G, BF><<<grid, kDecodeThreads, p.lds, s>>>(
+  allow_lds(&k_decode_gs<D, G, BF, U8>, p.lds);
+  k_decode_gs<D, G, BF, U8><<<grid, kDecodeThreads, p.lds, s>>>(
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.chunk, p.n_chunks, a.budget, p.cmax,
       a.qscale, reinterpret_cast<uint16_t*>(w + p.hist_off),
       reinterpret_cast<float*>(w + p.part_off), reinterpret_cast<uint32_t*>(w + kCtrlSelect),
       reinterpret_cast<uint32_t*>(w + kCtrlAttend),
       reinterpret_cast<uint32_t*>(w + ADAMAS_WS_STATUS_OFFSET), a.wait_polls, a.idx, a.out,
       a.n_sink, a.n_recent, a.rule, a.stamps);
+}
+
+template <int D, int G, bool BF>
+void launch_decode_gs_t(const GroupPlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a,
+                        uint8_t* w) {
+  if constexpr (G >= 2 && D <= 128) {
+    if (p.u8) {
+      launch_decode_gs_k<D, G, BF, true>(p, grid, s, a, w);
+      return;
+    }
+  }
+  launch_decode_gs_k<D, G, BF, false>(p, grid, s, a, w);
 }
 
 #define ADM_INST_G(g)                                                                        \

@@ -683,6 +683,7 @@ struct GroupThreshold {
   uint32_t lt, lt_before, ties_before;
 };
 constexpr int kTmpGrpLtBefore = 21, kTmpGrpTiesBefore = 22, kTmpGroupCounts = 24;
+constexpr int kTmpHalfTotals = 23;  // k_decode_gs re-scan: a half chunk's counts
 
 template <int NT>
 ADM_DEV GroupThreshold find_group_threshold(uint32_t tot, uint32_t bef, int nbins, uint32_t K,
@@ -1035,6 +1036,53 @@ ADM_DEV bool chunk_compact_heads_u8(const uint32_t* hist, int nbp, const uint8_t
   if (ps) ps->mark_last_wave(19);  // tokens emitted
   lds_sync();
   return true;
+}
+
+// chunk_collect over 8-bit keys (min(key, 255), t < 255, so every key that
+// is kept is exact): thread j owns tokens [32j, 32j + 32) of the chunk
+// (valid <= 32 * NT), counted with bytewise compares; emit(pos, token, key)
+// as chunk_collect.  With tot_out, thread 0 gets (#below t) | (#at t) << 16.
+template <int NT, class Emit>
+ADM_DEV uint32_t chunk_collect_u8(const uint8_t* skey, int valid, int t, uint32_t quota,
+                                  uint32_t* s_tmp, Emit&& emit, uint32_t* tot_out = nullptr) {
+  constexpr int TPT = 32;
+  const int t0 = threadIdx.x * TPT;
+  const int nv = valid - t0;
+  const uint32_t y = (uint32_t)t * 0x01010101u, y1 = (uint32_t)(t + 1) * 0x01010101u;
+  uint32_t nlt = 0, nle = 0, hit = 0;
+  if (t0 < valid) {
+    const uint4* src = reinterpret_cast<const uint4*>(skey + t0);
+    const uint4 a = src[0], b4 = src[1];
+    const uint32_t w[TPT / 4] = {a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int j = 0; j < TPT / 4; ++j) {
+      const int left = nv - 4 * j;
+      const uint32_t vm =
+          left >= 4 ? 0x80808080u : (left <= 0 ? 0u : 0x80808080u >> (32 - 8 * left));
+      const uint32_t lt = bytes_below(w[j], y) & vm, le = bytes_below(w[j], y1) & vm;
+      nlt += (uint32_t)__popc(lt);
+      nle += (uint32_t)__popc(le);
+      hit |= (((le >> 7) * 0x01020408u) >> 24) << (4 * j);
+    }
+  }
+  const uint32_t mine = nlt | ((nle - nlt) << 16);
+  uint32_t tot;
+  const uint32_t ex = block_scan_incl<NT>(mine, s_tmp, &tot) - mine;
+  uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
+  for (uint32_t m = hit; m != 0; m &= m - 1) {
+    const uint32_t tok = (uint32_t)(t0 + __ffs(m) - 1);
+    const uint32_t d = skey[tok];
+    if (d < (uint32_t)t) {
+      emit(ltb + (eqb < quota ? eqb : quota), tok, d);
+      ++ltb;
+    } else {
+      if (eqb < quota) emit(ltb + eqb, tok, (uint32_t)t);
+      ++eqb;
+    }
+  }
+  if (tot_out != nullptr && threadIdx.x == 0) *tot_out = tot;
+  const uint32_t eq_all = tot >> 16;
+  return (tot & 0xffffu) + (eq_all < quota ? eq_all : quota);
 }
 
 // chunk_collect into out[] (LDS) as (D << 16) | token; entries [kept, pad_to)

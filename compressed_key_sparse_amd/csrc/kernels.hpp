@@ -968,10 +968,11 @@ void k_decode(
             s_fused + 2 * G, &ps);
         if constexpr (3 * D + 1 >= kKeySat) {
           if (!exact) {
-            // exact 16-bit keys, half a chunk at a time, in the bytes' place;
-            // s_tot: per head the (below, at) counts of earlier halves, and
-            // the count chunk_collect reports
-            constexpr int kHalf = NT * kCompactTpt;
+            // exact 16-bit keys, half a chunk at a time, in the bytes' place
+            // (G halves of 16-bit keys fill the G chunks of bytes); s_tot:
+            // per head the (below, at) counts of earlier halves, and the
+            // count chunk_collect reports
+            const int kHalf = chunk / 2;  // <= NT * kCompactTpt tokens
             uint16_t* sd16 = reinterpret_cast<uint16_t*>(sdist8);
             uint32_t* s_thr = s_fused;
             uint32_t* s_tot = s_fused + 2 * G;
@@ -1151,6 +1152,19 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
   constexpr int CR = kNbinsHist(D), CQ = CR / 8;
   const uint16_t* h = chist + row * ncp * CR;
+  // the first EPL*64 candidates of this wavefront's first chunk, loaded now
+  // so that they arrive while the counts are summed
+  const int kpad_pre = 1 << kpad_log2;
+  const int c_pre = (int)blockIdx.x * chunks_per_seg + wid;
+  const bool has_pre = c_pre < min(n_chunks, ((int)blockIdx.x + 1) * chunks_per_seg);
+  uint4 pre[EPL / 4];
+#pragma unroll
+  for (int u = 0; u < EPL / 4; ++u) {
+    const int i = lane * EPL + 4 * u;
+    pre[u] = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
+    if (has_pre && i < kpad_pre)
+      pre[u] = *reinterpret_cast<const uint4*>(cand + ((row * n_chunks + c_pre) << kpad_log2) + i);
+  }
   for (int i = threadIdx.x; i < nbins; i += NT) s_hist[i] = 0;
   for (int i = threadIdx.x; i < n_chunks; i += NT) s_first[i] = 0;
   lds_sync();
@@ -1297,7 +1311,10 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
       for (int u = 0; u < EPL / 4; ++u) {
         const int i = base + lane * EPL + 4 * u;
         uint4 e = make_uint4(0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu);
-        if (i < kpad) e = *reinterpret_cast<const uint4*>(list + i);
+        if (base == 0 && c == c_pre)
+          e = pre[u];
+        else if (i < kpad)
+          e = *reinterpret_cast<const uint4*>(list + i);
         v[4 * u] = e.x;
         v[4 * u + 1] = e.y;
         v[4 * u + 2] = e.z;
@@ -1406,7 +1423,10 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_select(
 // workgroup of the group merges the partials by log-sum-exp.
 //   ghist  [B*Hq][n_chunks][NBH] u16   part [B*Hq][n_chunks][PWP] f32
 //   cmax   >= min(budget, n_ctx, chunk), a multiple of 4 (LDS index rows)
-template <int D, int G, bool BF>
+// U8 (grouped heads, head_dim <= 128): the chunk's keys are kept as
+// min(key, 255), one byte each, as in k_decode; a head whose group threshold
+// reaches 255 re-scans the chunk half at a time with exact 16-bit keys.
+template <int D, int G, bool BF, bool U8 = false>
 __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ k_codes, int Hq, int Hkv, int64_t cap, int64_t n_ctx, int chunk,
@@ -1434,7 +1454,9 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   uint32_t* s_bef = s_tot + NBP;
   int32_t* sidx = reinterpret_cast<int32_t*>(s_bef + NBP);
   uint8_t* region = reinterpret_cast<uint8_t*>(sidx + G * cmax);
+  static_assert(!U8 || (G >= 2 && D <= 128), "8-bit key variant");
   uint16_t* sdist = reinterpret_cast<uint16_t*>(region);  // scan and selection
+  uint8_t* sdist8 = region;                               // U8: [G][chunk] bytes
   float* s_part = reinterpret_cast<float*>(region);       // attention, after selection
   float* s_res = s_part + NW * PW + NT / 16;
   float* s_merge = reinterpret_cast<float*>(region);      // merge, last workgroup
@@ -1471,7 +1493,16 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     sdist[g * chunk + tok] = (uint16_t)key;
     atomicAdd(&shist[g * NBP + key], 1u);
   };
-  if (keep.keeps_none(valid))
+  if constexpr (U8) {
+    if (keep.keeps_none(valid))
+      scan_chunk_u8<D, G, NT, kDecodeScanDepth>(
+          src, valid, qp, [](int, uint32_t d) { return d + 1u; }, shist, NBP, sdist8, chunk,
+          &first);
+    else
+      scan_chunk_u8<D, G, NT, kDecodeScanDepth>(
+          src, valid, qp, [&](int tok, uint32_t d) { return keep.key(tok, d); }, shist, NBP,
+          sdist8, chunk, &first);
+  } else if (keep.keeps_none(valid))
     scan_chunk<D, G, NT, kDecodeScanDepth>(
         src, valid, qp, [&](int g, int tok, uint32_t d) { sink(g, tok, d + 1u); }, &first);
   else
@@ -1542,12 +1573,55 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     const uint32_t off = gt.lt_before + before;
     int32_t* sg = sidx + g * cmax;
     int32_t* ig = idx ? idx + row * budget + off : nullptr;
-    const uint32_t kept = chunk_collect<NT>(sdist + g * chunk, valid, gt.t, mine_q, s_tmp,
+    uint32_t kept = 0;
+    if constexpr (U8) {
+      if (gt.t < kKeySat) {
+        kept = chunk_collect_u8<NT>(sdist8 + g * chunk, valid, gt.t, mine_q, s_tmp,
+                                    [&](uint32_t pos, uint32_t t, uint32_t) {
+                                      const int32_t tok = (int32_t)(t0 + t);
+                                      sg[pos] = tok;
+                                      if (ig) ig[pos] = tok;
+                                    });
+      } else if constexpr (3 * D + 1 >= kKeySat) {
+        // exact 16-bit keys of head g, half a chunk at a time, written over
+        // its own byte keys (a half of 16-bit keys fills one head's bytes)
+        const int kHalf = chunk / 2;  // <= NT * kCompactTpt tokens
+        uint16_t* sd16 = reinterpret_cast<uint16_t*>(sdist8 + g * chunk);
+        uint32_t* s_half = s_tmp + kTmpHalfTotals;  // chunk_collect's totals
+        QPlanes qh[G];
+        load_qplanes<D, G>(sq, qh);
+        uint32_t lt_prev = 0, eq_prev = 0;
+        for (int h0 = 0; h0 < valid; h0 += kHalf) {
+          const int hv = min(kHalf, valid - h0);
+          lds_sync();
+          scan_chunk<D, G, NT, kDecodeScanDepth>(
+              ContigCodes{src.p + (int64_t)h0 * (D / 64)}, hv, qh,
+              [&](int gg, int tok, uint32_t d) {
+                if (gg == g) sd16[tok] = (uint16_t)keep.key(h0 + tok, d);
+              });
+          lds_sync();
+          const uint32_t taken = eq_prev < mine_q ? eq_prev : mine_q, hoff = lt_prev + taken;
+          kept += chunk_collect<NT>(sd16, hv, gt.t, mine_q - taken, s_tmp,
+                                    [&](uint32_t pos, uint32_t t, uint32_t) {
+                                      const int32_t tok = (int32_t)(t0 + h0 + (int)t);
+                                      sg[hoff + pos] = tok;
+                                      if (ig) ig[hoff + pos] = tok;
+                                    },
+                                    nullptr, s_half);
+          lds_sync();
+          const uint32_t tot = s_half[0];
+          lt_prev += tot & 0xffffu;
+          eq_prev += tot >> 16;
+        }
+      }
+    } else {
+      kept = chunk_collect<NT>(sdist + g * chunk, valid, gt.t, mine_q, s_tmp,
                                [&](uint32_t pos, uint32_t t, uint32_t) {
                                  const int32_t tok = (int32_t)(t0 + t);
                                  sg[pos] = tok;
                                  if (ig) ig[pos] = tok;
                                });
+    }
     if (threadIdx.x == 0) s_cnt[g] = kept;
     if (idx && c == 0)
       for (int j = bsel + (int)threadIdx.x; j < budget; j += NT) idx[row * budget + j] = -1;

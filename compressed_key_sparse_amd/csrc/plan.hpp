@@ -225,22 +225,27 @@ inline bool many_candidates(const DecodePlan& p) {
 // (more compute units streaming), and no smaller than 1024 tokens.
 struct GroupPlan {
   bool ok = false;
+  bool u8 = false;  // k_decode_gs keeps 8-bit keys (chunks that fit the device)
   int chunk = 0, n_chunks = 0, cmax = 0;
   size_t lds = 0, hist_off = 0, part_off = 0, total = 0;
 };
 
-inline size_t decode_gs_lds(int D, int G, int c, int cmax) {
+inline size_t decode_gs_lds(int D, int G, int c, int cmax, int key_bytes = 2) {
   const int nw = kDecodeThreads / kWave;
   const size_t pwp = (size_t)((2 + D + 3) & ~3);
   const size_t attend = ((size_t)nw * (2 + D) + kDecodeThreads / 16 + pwp) * 4;
   const size_t merge = (size_t)kGsMergeTile * pwp * 4;
   return (size_t)kTmpWords * 4 + 32 * 4 + (size_t)G * (D / 16) * 4 +
          (size_t)(G + 2) * nbins_padded(D) * 4 + (size_t)G * cmax * 4 +
-         std::max({(size_t)G * c * 2, attend, merge});
+         std::max({(size_t)G * c * key_bytes, attend, merge});
 }
 
+// allow_u8: the 8-bit key variant may take shapes the 16-bit one cannot
+// hold at once (a forced group wait; the automatic choice does not take it:
+// with tens of chunks per group its histogram exchange and merge cost more
+// than the split schedule's second launch).
 inline GroupPlan plan_decode_gs(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D,
-                         int64_t capacity) {
+                                int64_t capacity, bool allow_u8 = false) {
   GroupPlan p;
   const int G = Hq / Hkv;
   const int64_t groups = (int64_t)B * Hkv, rows = (int64_t)B * Hq;
@@ -261,6 +266,24 @@ inline GroupPlan plan_decode_gs(int B, int Hq, int Hkv, int64_t n_ctx, int budge
   p.part_off = round_up(p.hist_off + (size_t)rows * p.n_chunks * nbh * 2, 256);
   p.total = round_up(p.part_off + (size_t)rows * p.n_chunks * pwp * 4, 256);
   p.ok = p.lds <= kLdsLimit && groups * p.n_chunks <= capacity && groups <= kMaxGroups;
+  // grouped heads whose 16-bit keys need more chunks than the device holds
+  // at once: 8-bit keys in chunks up to 32768 tokens and the whole LDS
+  if (!p.ok && allow_u8 && G >= 2 && D <= 128 && groups <= kMaxGroups) {
+    auto lds8 = [&](int cc) { return decode_gs_lds(D, G, cc, cmax_of(cc), 1); };
+    int c8 = 32768;
+    while (c8 > 1024 && lds8(c8) > kLdsDecodeLimit) c8 /= 2;
+    while (c8 > 1024 && groups * chunks_of(c8 / 2) <= capacity) c8 /= 2;
+    if (lds8(c8) <= kLdsDecodeLimit && groups * chunks_of(c8) <= capacity) {
+      p.u8 = true;
+      p.chunk = c8;
+      p.n_chunks = (int)chunks_of(c8);
+      p.cmax = cmax_of(c8);
+      p.lds = lds8(c8);
+      p.part_off = round_up(p.hist_off + (size_t)rows * p.n_chunks * nbh * 2, 256);
+      p.total = round_up(p.part_off + (size_t)rows * p.n_chunks * pwp * 4, 256);
+      p.ok = true;
+    }
+  }
   return p;
 }
 

@@ -272,13 +272,16 @@ int adamas_bucket_alpha(float* alpha_out, int cap);
 int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim);
 
 /*
- * Bytes per chunk key the fused decode kernel keeps in LDS for this shape
- * (host-side planning only): 2, or 1 where grouped heads (head_dim 64 or
- * 128) would otherwise need more than one round of workgroups; one-byte
- * keys hold chunks twice as long.  Results do not depend on it (one-byte
- * keys saturate at 255, and a chunk whose selection reaches 255 is
- * re-scanned with exact keys).  The ragged and paged steps always keep 2.
- * Negated status for a shape adamas_decode_step rejects.
+ * Bytes per chunk key the decode kernel of the schedule adamas_decode_path
+ * reports keeps in LDS for this shape (host-side planning; without a device
+ * the last-arrival and split kernel's): 2, or 1 where grouped heads
+ * (head_dim 64 or 128) would otherwise need more than one round of
+ * workgroups (last-arrival, split) or more workgroups than the device holds
+ * at once (group wait); one-byte keys hold chunks twice as long.  Results do
+ * not depend on it (one-byte keys saturate at 255, and a chunk whose
+ * selection reaches 255 is re-scanned with exact keys).  The ragged and
+ * paged steps always keep 2.  Negated status for a shape adamas_decode_step
+ * rejects.
  */
 int adamas_decode_key_bytes(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim);
 

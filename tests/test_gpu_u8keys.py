@@ -9,8 +9,10 @@ case (every chunk threshold far below 255); the second builds caches whose
 keys are far from every query (codes near the complement of the query's,
 distances around 290 for head_dim 128), so whole sequences are selected
 from re-scanned chunks, with ties at the threshold split across halves.
-Selection bit for bit, output within the dtype's bound, under each
-schedule that runs the fused kernel."""
+The group-wait kernel takes one-byte keys where 16-bit ones would need
+more chunks than the device holds at once, with the same exact re-scan.
+Selection bit for bit, output within the dtype's bound, under every
+schedule."""
 import numpy as np
 import pytest
 import torch
@@ -44,13 +46,17 @@ def gqa_case(ora):
     return lay, codes, q, k, v, ocodes
 
 
+MODES = [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_SPLIT, adamas.DECODE_GROUP_WAIT]
+
+
 @pytest.mark.parametrize("budget", [256, 1024])
-@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_SPLIT])
+@pytest.mark.parametrize("mode", MODES)
 def test_u8_keys_gqa(ora, gqa_case, mode, budget):
     lay, codes, q, k, v, ocodes = gqa_case
-    assert adamas.decode_key_bytes(2, 24, 8, 300000, budget, 128) == 1
     log(f"GQA 24/8, 2 x 300000 tokens, budget {budget}, mode {mode}")
     adamas.set_decode_mode(mode)
+    assert adamas.decode_path(2, 24, 8, 300000, budget, 128) == mode
+    assert adamas.decode_key_bytes(2, 24, 8, 300000, budget, 128) == 1
     idx = torch.empty((2, 24, budget), dtype=torch.int32, device=DEV)
     out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, 300000, budget, idx_out=idx)
     torch.cuda.synchronize()
@@ -77,14 +83,17 @@ def _far_caches(B, Hkv, G, n, d, n_far, seed):
     return q, k, v
 
 
-@pytest.mark.parametrize("budget", [256, 1024])
-@pytest.mark.parametrize("mode", [adamas.DECODE_LAST_ARRIVAL, adamas.DECODE_SPLIT])
-def test_u8_keys_exact_rescan(ora, mode, budget):
-    B, Hkv, G, n, d = 16, 2, 2, 140000, 128
-    assert adamas.decode_key_bytes(B, Hkv * G, Hkv, n, budget, d) == 1
+@pytest.mark.parametrize("shape", [(2, 2, 256), (2, 2, 1024), (1, 8, 256)],
+                         ids=lambda s: f"hkv{s[0]}-g{s[1]}-b{s[2]}")
+@pytest.mark.parametrize("mode", MODES)
+def test_u8_keys_exact_rescan(ora, mode, shape):
+    Hkv, G, budget = shape
+    B, n, d = 16, 140000, 128
     log(f"far keys: {B} x {Hkv * G}/{Hkv} heads x {n} tokens, budget {budget}, mode {mode}")
     adamas.set_rotation(False)
     adamas.set_decode_mode(mode)
+    assert adamas.decode_path(B, Hkv * G, Hkv, n, budget, d) == mode
+    assert adamas.decode_key_bytes(B, Hkv * G, Hkv, n, budget, d) == 1
     n_far = [n] * 7 + [70000] + [0] * 8    # 7 sequences all far, one half, 8 none
     q, k, v = _far_caches(B, Hkv, G, n, d, n_far, seed=81)
     codes = torch.zeros((B, Hkv, n, d // 4), dtype=torch.uint8, device=DEV)
@@ -96,12 +105,13 @@ def test_u8_keys_exact_rescan(ora, mode, budget):
     ocodes = ora.encode_keys(kh, rotate=False)
     assert np.array_equal(codes.cpu().numpy(), ocodes)
     oout, o64, oidx = ora.decode_step(qh, kh, vh, ocodes, n, budget, rotate=False)
-    # every 32768-token chunk of a far sequence has its kc-th smallest key
-    # (distance + 1) at 255 or above: the kernel must re-scan it
+    # every chunk of a far sequence (16384 or 32768 tokens as planned) has
+    # its kc-th smallest key (distance + 1) at 255 or above: the kernel must
+    # re-scan it
     qc = ora.encode_keys(qh[:, :, None, :], rotate=False)[:, :, 0]
     dist = ora.score(qc[:1], ocodes[:1], n_ctx=n)[0]
-    for c0 in range(0, n, 32768):
-        part = np.sort(dist[:, c0:c0 + 32768], axis=-1)
+    for c0 in range(0, n, 16384):
+        part = np.sort(dist[:, c0:c0 + 16384], axis=-1)
         kc = min(budget, part.shape[-1])
         assert part[:, kc - 1].min() + 1 >= 255, f"chunk at {c0} would not re-scan"
     got = idx.cpu().numpy()
