@@ -86,6 +86,9 @@ def parse():
     ap.add_argument("--graph-only", action="store_true",
                     help="skip the eager timed pass and the trailing recall launch, so the last "
                          "steps*layers decode dispatches of a kernel trace are the timed replays")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="write the headline HBM traffic file from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, then WRITE_SIZE) and exit")
     ap.add_argument("--phases", action="store_true",
                     help="per-phase timeline of the workload's decode launches from the "
                          "measurement build (libadamas_phases.so); prints a table, no JSON line")
@@ -94,8 +97,11 @@ def parse():
 
 # ---------------------------------------------------------------- profiles
 KERNEL_SOURCES = ("compressed_key_sparse_amd/csrc/adamas.hip",
+                  "compressed_key_sparse_amd/csrc/decode_inst.hip",
+                  "compressed_key_sparse_amd/csrc/plan.hpp",
                   "compressed_key_sparse_amd/csrc/kernels.hpp",
-                  "compressed_key_sparse_amd/csrc/device_common.hpp")
+                  "compressed_key_sparse_amd/csrc/device_common.hpp",
+                  "include/adamas.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_llama2-128k_hbm_traffic.json")
 
 
@@ -119,6 +125,53 @@ def measured_traffic():
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+def _counter_means(dirpath: str, counter: str):
+    """{(kernel name, grid): mean value per dispatch} of one PMC counter."""
+    import csv
+    import glob
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for f in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    acc[(r.get("Kernel_Name", ""), r.get("Grid_Size", ""))].append(
+                        float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(fetch_dir: str, write_dir: str, out: str = TRAFFIC_FILE):
+    """HBM bytes per headline decode launch from a FETCH_SIZE and a
+    WRITE_SIZE run (each of bench.py --no-graph --copy-calibration), each
+    counter scaled by what it reads for the calibration conversion (1 GiB
+    fp32 read, 512 MiB bf16 written, grid 2^25); written with the kernel
+    source hash so that a later kernel change voids it."""
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+
+    def pick(m, pred):
+        hits = [v for (name, grid), v in m.items() if pred(name, grid)]
+        if len(hits) != 1:
+            raise SystemExit(f"bench.py --traffic-from: expected one matching kernel, got {len(hits)}")
+        return hits[0]
+
+    dec = lambda name, grid: name.startswith("void adm::k_decode<128, 1, true, 0,")
+    cal = lambda name, grid: "bfloat16_copy_kernel" in name and grid == str(1 << 25)
+    fk, wk = pick(fetch, dec), pick(write, dec)
+    fs, ws = (1 << 30) / 1024 / pick(fetch, cal), (1 << 29) / 1024 / pick(write, cal)
+    traffic = int(round((fk * fs + wk * ws) * 1024))
+    alg = algorithmic_bytes(1, 32, 32, 128, 131072, 256, 2)
+    res = {"kernel": "k_decode<128,1,bf16,plain>", "workload": "llama2-mha-128k-32layers budget 256",
+           "kernel_source_hash": kernel_source_hash(), "fetch_kib_per_dispatch": round(fk, 1),
+           "write_kib_per_dispatch": round(wk, 1), "fetch_scale": round(fs, 5),
+           "write_scale": round(ws, 5), "traffic_bytes_per_launch": traffic,
+           "algorithmic_bytes_per_launch": alg}
+    with open(out, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(res))
+    print(f"# traffic {traffic} bytes per launch = {traffic / alg:.4f} x algorithmic")
 
 
 def summarize_trace(dirpath: str, last: int):
@@ -182,6 +235,9 @@ def summarize(dirpath: str):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.summarize:
         if args.last:
             summarize_trace(args.summarize, args.last)
