@@ -231,6 +231,25 @@ def summarize(dirpath: str):
         print("dispatches  counter      mean_value  grid  kernel")
         for (name, cn, grid), vals in sorted(acc.items()):
             print(f"{len(vals):10d}  {cn:11s} {sum(vals)/len(vals):12.1f}  {grid}  {name[:100]}")
+        # ratios of the LDS and occupancy counters, per kernel and grid
+        per = defaultdict(dict)
+        for (name, cn, grid), vals in acc.items():
+            per[(name, grid)][cn] = sum(vals) / len(vals)
+        rows = []
+        for (name, grid), c in sorted(per.items()):
+            if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
+                conf = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+                occ = (c["SQ_WAVE_CYCLES"] / c["SQ_BUSY_CU_CYCLES"]
+                       if c.get("SQ_BUSY_CU_CYCLES") else float("nan"))
+                valu = (100 * c["SQ_ACTIVE_INST_VALU"] / (256 * c["GRBM_GUI_ACTIVE"])
+                        if c.get("GRBM_GUI_ACTIVE") and "SQ_ACTIVE_INST_VALU" in c else float("nan"))
+                rows.append(f"{conf:9.4f}  {occ:10.2f}  {valu:9.1f}  {grid}  {name[:90]}")
+        if rows:
+            print("# derived: LDS bank-conflict cycles / LDS-active cycles; waves resident per busy CU "
+                  "(SQ_WAVE_CYCLES / SQ_BUSY_CU_CYCLES); VALU busy % "
+                  "(100 * SQ_ACTIVE_INST_VALU / (256 CUs * GRBM_GUI_ACTIVE))")
+            print("conflict  waves/CU    valu_%  grid  kernel")
+            print("\n".join(rows))
 
 
 def main():
@@ -443,7 +462,8 @@ PHASE_NAMES = {
                12: "merged out stored", 13: "rows gathered, last wavefront",
                14: "slot sums, last wavefront", 16: "chunk: thresholds (grouped heads)",
                17: "chunk: masks, last wavefront", 18: "chunk: prefix over workgroup",
-               19: "chunk: tokens emitted, last wavefront"},
+               19: "chunk: tokens emitted, last wavefront", 20: "final: counts, last wavefront",
+               21: "final: prefix", 22: "final: placed, last wavefront"},
     "split": {0: "entry", 1: "threshold", 2: "placement", 3: "tokens copied",
               9: "rows gathered + weighted", 10: "partials merged", 11: "partial handed over",
               12: "merged out stored", 13: "rows gathered, last wavefront",

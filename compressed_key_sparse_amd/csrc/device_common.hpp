@@ -1158,7 +1158,9 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
   }
   uint32_t tot;
   const uint32_t mine = lt | (eq << 16);
+  if (ps) ps->mark_last_wave(20);  // counts below / at the threshold
   const uint32_t ex = block_scan_incl<NT>(mine, s_tmp, &tot) - mine;
+  if (ps) ps->mark(21);  // prefix over the workgroup
   uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -1180,6 +1182,7 @@ ADM_DEV void final_select(const uint32_t* cand, int M, int kpad_log2, int chunk,
   }
   if (idx)
     for (int j = bsel + threadIdx.x; j < budget; j += NT) idx[j] = -1;
+  if (ps) ps->mark_last_wave(22);  // tokens placed
   lds_sync();
 }
 
