@@ -437,7 +437,10 @@ def main():
         "eager_ms_per_step": round(eager_ms, 4) if eager_ms is not None else None,
         "roofline": {"bound": "hbm", "kernel": "adamas_decode_step (one layer)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     # the counters were taken on this configuration only
+                     "traffic": measured_traffic() if (bud, n, B, Hq, d) == (256, 131072, 1, 32, 128)
+                     else None,
                      "bytes_per_launch": per_layer, "launch_us": round(avg_launch_us, 3),
                      "eager_event_launch_us": round(launch_us, 3) if launch_us else None},
         "step_ms": ({"p10": round(float(np.percentile(step_times, 10)), 4),
