@@ -28,20 +28,22 @@ def _dt(s):
     return torch.bfloat16 if s == "bf16" else torch.float32
 
 
+@pytest.mark.parametrize("rotate", [1, 2])
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_encode_bucket_alpha(ora, d, dt):
+def test_encode_bucket_alpha(ora, d, dt, rotate):
     table = [0.25, 0.75, 0.5, 0.3, 0.0, 1.2]
-    log(f"encode d={d} {dt} alpha={table}")
+    log(f"encode d={d} {dt} rotate={rotate} alpha={table}")
     adamas.set_bucket_alpha(table)
+    adamas.set_rotation(rotate)
     x = synth.random_values((2, 7, 611, d), _dt(dt), seed=61, device=DEV)
     codes = torch.zeros((2, 7, 611, d // 4), dtype=torch.uint8, device=DEV)
     adamas.encode_keys(x, codes)
     torch.cuda.synchronize()
-    ref = ora.encode_keys(host(x), alpha=table)
+    ref = ora.encode_keys(host(x), rotate=rotate, alpha=table)
     assert np.array_equal(codes.cpu().numpy(), ref)
     # and the table changes the codes of every head whose alpha is not 0.5
-    base = ora.encode_keys(host(x))
+    base = ora.encode_keys(host(x), rotate=rotate)
     for h in range(7):
         same = np.array_equal(ref[:, h], base[:, h])
         assert same == (table[h % 6] == 0.5), f"head {h}"
@@ -108,3 +110,39 @@ def test_alpha_half_table_is_the_fixed_rule(ora):
         torch.cuda.synchronize()
         res.append((codes.cpu(), idx.cpu(), out.cpu()))
     assert all(torch.equal(a, b) for a, b in zip(*res))
+
+
+def test_captured_graph_keeps_its_table(ora):
+    """A launch takes the bucketing table by value: a graph captured under one
+    table replays with it after the process-wide table has changed."""
+    log("graph captured under one alpha table, replayed under another")
+    w = synth.LLAMA32_GQA_1M.replace(hq=6, hkv=2, n_ctx=12000, cap=12000, budget=128)
+    lay = synth.make_layer(w, 8, DEV)
+    table = [0.3, 0.65]
+    adamas.set_bucket_alpha(table)
+    codes = torch.zeros((1, 2, 12000, 32), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    s = torch.cuda.Stream(DEV)
+    ws = adamas.Workspace(DEV)
+    ws.get(adamas.workspace_bytes(adamas.OP_DECODE_STEP, 1, 6, 2, 12000, 128, 128))
+    idx = torch.empty((1, 6, 128), dtype=torch.int32, device=DEV)
+    out = torch.empty_like(lay["q"])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, 12000, 128, out=out, idx_out=idx,
+                           ws=ws, stream=s)   # warm-up outside the capture
+        with torch.cuda.graph(g, stream=s):
+            adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, 12000, 128, out=out,
+                               idx_out=idx, ws=ws, stream=s)
+    torch.cuda.synchronize()
+    adamas.set_bucket_alpha([0.9, 0.1])
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    ocodes = ora.encode_keys(k, alpha=table)
+    oout, o64, oidx = ora.decode_step(q, k, v, ocodes, 12000, 128, alpha=table)
+    for rep in range(3):
+        idx.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), oidx), f"replay {rep}"
+        check_out(ora, out, q, k, v, oidx, oout, o64, f"graph replay {rep}")
