@@ -65,6 +65,24 @@ def test_u8_keys_gqa(ora, gqa_case, mode, budget):
     check_out(ora, out, q, k, v, oidx, oout, o64, f"u8 keys GQA budget {budget} mode {mode}")
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_u8_keys_gqa_keep_set(ora, gqa_case, mode):
+    """Always-kept sinks and recent window (key 0) through the one-byte keys."""
+    lay, codes, q, k, v, ocodes = gqa_case
+    log(f"GQA 24/8, 2 x 300000 tokens, budget 512 with 4 sinks and a 64-token window, mode {mode}")
+    adamas.set_decode_mode(mode)
+    assert adamas.decode_key_bytes(2, 24, 8, 300000, 512, 128) == 1
+    idx = torch.empty((2, 24, 512), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, 300000, 512, idx_out=idx,
+                             n_sink=4, n_recent=64)
+    torch.cuda.synchronize()
+    oout, o64, oidx = ora.decode_step(q, k, v, ocodes, 300000, 512, n_sink=4, n_recent=64)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, oidx)
+    assert np.isin(np.arange(4), got[0, 0]).all() and np.isin(np.arange(299936, 300000), got[1, 5]).all()
+    check_out(ora, out, q, k, v, oidx, oout, o64, f"u8 keys keep set mode {mode}")
+
+
 def _far_caches(B, Hkv, G, n, d, n_far, seed):
     """q: per (sequence, KV head) a +-1 pattern shared by its G query heads
     (codes 0 and 3 with the rotation off); keys of sequence b's tokens below
