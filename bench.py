@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="write the headline HBM traffic file from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--decode-mode", default="auto",
+                    choices=("auto", "last-arrival", "group-wait", "split"),
+                    help="schedule of the decode step (adamas_set_decode_mode); auto by default")
     ap.add_argument("--phases", action="store_true",
                     help="per-phase timeline of the workload's decode launches from the "
                          "measurement build (libadamas_phases.so); prints a table, no JSON line")
@@ -280,6 +283,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     adamas.load(variant="phases" if args.phases else None)
+    adamas.set_decode_mode({"auto": adamas.DECODE_AUTO, "last-arrival": adamas.DECODE_LAST_ARRIVAL,
+                            "group-wait": adamas.DECODE_GROUP_WAIT,
+                            "split": adamas.DECODE_SPLIT}[args.decode_mode])
     if args.phases:
         return bench_phases(args, dev)
     if args.workload == "llama3.2-3b-gqa-1m":
