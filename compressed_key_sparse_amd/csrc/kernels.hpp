@@ -959,6 +959,18 @@ void k_decode(
     }
   }
   const int kc = min(budget, valid);
+  // one chunk per head: its kc = bsel candidates, in token order, are the
+  // selection itself, so the step needs neither their hand-over, an arrival
+  // nor a final selection.  solo: the attention follows at once; solo_sel
+  // (attention in a later launch): the index rows are written from here
+  const bool one = RAG == 0 && n_chunks == 1 && chist == nullptr;
+  const bool solo = one && fuse_attend && bsel <= NT && (G == 1 || n_stage == G);
+  const bool solo_sel = one && !fuse_attend;
+  const auto write_idx = [&](int g, const uint32_t* st) {
+    const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
+    for (int j = threadIdx.x; j < budget; j += NT)
+      idx[row * budget + j] = j < bsel ? (int32_t)(st[j] & 0xffffu) : -1;
+  };
   bool staged = false;
   if constexpr (G >= 2) {
     if (n_stage == G) {
@@ -1017,7 +1029,10 @@ void k_decode(
       ps.mark(4);
       for (int g = 0; g < G; ++g) {
         const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
-        lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage + g * kpad, kpad);
+        if (solo_sel)
+          write_idx(g, sstage + g * kpad);
+        else if (!solo)
+          lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage + g * kpad, kpad);
       }
       staged = true;
     }
@@ -1031,11 +1046,54 @@ void k_decode(
                         s_tmp, [](uint32_t, uint32_t) {}, &ps);
       lds_sync();
       ps.mark(4);
-      lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
+      if (solo_sel)
+        write_idx(g, sstage);
+      else if (!solo)
+        lds_to_shared<NT>(cand + (row * n_chunks + c) * kpad, sstage, kpad);
     }
+  }
+  if (solo_sel) {
+    ps.mark(11);
+    ps.flush();
+    return;
   }
   if (chist != nullptr) {  // k_split_select takes it from here
     ps.mark(5);
+    ps.flush();
+    return;
+  }
+  if (solo) {
+    // the token lists go to registers first (the attention's LDS overlaps the
+    // staged rows), then, per head, to the index row and the attention
+    int32_t mine[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      mine[g] = (int)threadIdx.x < bsel ? (int32_t)(sstage[g * kpad + threadIdx.x] & 0xffffu)
+                                        : -1;
+    lds_sync();
+    ps.mark(8);
+    const int64_t kvrow0 = ((int64_t)b * Hkv + hkv) * cap;
+#pragma unroll 1
+    for (int g = 0; g < G; ++g) {
+      const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
+      int32_t tok = mine[0];  // mine[g] by selects (a variable index would spill)
+#pragma unroll
+      for (int u = 1; u < G; ++u) tok = u == g ? mine[u] : tok;
+      if ((int)threadIdx.x < bsel) sidx[threadIdx.x] = tok;
+      if (idx) {
+        for (int j = threadIdx.x; j < budget; j += NT)
+          idx[row * budget + j] = j < bsel ? tok : -1;
+      }
+      lds_sync();
+      attend_rows<D, BF, NT>(q, k, v, row * D, kvrow0, cap, sidx, bsel, qscale, s_part, s_res,
+                             RowOverride{}, PageMap{}, &ps);
+      if (threadIdx.x < D) {
+        const float L = s_res[1];
+        store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? s_res[2 + threadIdx.x] / L : 0.0f);
+      }
+      lds_sync();
+    }
+    ps.mark(11);
     ps.flush();
     return;
   }

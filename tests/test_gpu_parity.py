@@ -368,6 +368,64 @@ def test_decode_keep(ora, restore_mode, mode, n, budget, n_sink, n_recent):
     check_out(ora, out, q, k, v, oidx, oout, o64, "keep")
 
 
+# ------------------------- one chunk per KV head (selection = its candidates)
+# Contexts of at most one chunk: the chunk workgroup's candidates are the
+# selection, so it attends over them directly (fused attention) or writes the
+# index rows for the attention launch.  Heads of one, two, three and eight
+# query rows, budgets at the fused limit and beyond the context, a single
+# row, always-kept tokens, a batch.
+_SOLO_CASES = {
+    "mha-f32-d64-777-b512": (synth.TINY.replace(hq=2, hkv=2, n_ctx=777, cap=800,
+                                                budget=512), 0, 0),
+    "gqa2-bf16-1000-b256": (synth.LLAMA32_GQA_1M.replace(hq=2, hkv=1, n_ctx=1000, cap=1000,
+                                                         budget=256), 0, 0),
+    "gqa2-bf16-1-b64": (synth.LLAMA32_GQA_1M.replace(hq=4, hkv=2, n_ctx=1, cap=8, budget=64),
+                        0, 0),
+    "gqa2-f32-d64-keep": (synth.TINY.replace(hq=6, hkv=3, n_ctx=1024, cap=1024, budget=100),
+                          4, 16),
+    "mha-bf16-batch2-keep": (synth.LLAMA2_32K.replace(batch=2, hq=3, hkv=3, n_ctx=1023,
+                                                      cap=1030, budget=64), 1, 100),
+    "gqa2-d256-bf16-1024-b200": (synth.LLAMA2_32K.replace(hq=4, hkv=2, head_dim=256, n_ctx=1024,
+                                                          cap=1024, budget=200), 0, 0),
+    # selections attended in a second launch (more than two 256-row batches
+    # per KV head): the chunk workgroup writes the index rows itself
+    "mha-bf16-1024-b700": (synth.LLAMA2_32K.replace(hq=2, hkv=2, n_ctx=1024, cap=1024,
+                                                    budget=700), 0, 0),
+    "gqa3-bf16-999-b256-keep": (synth.LLAMA32_GQA_1M.replace(hq=6, hkv=2, n_ctx=999, cap=1000,
+                                                             budget=256), 2, 30),
+    "gqa8-f32-d64-1000-b64": (synth.TINY.replace(hq=8, hkv=1, n_ctx=1000, cap=1000, budget=64),
+                              0, 0),
+    "gqa8-bf16-600-b2048": (synth.LLAMA32_GQA_1M.replace(hq=8, hkv=1, n_ctx=600, cap=600,
+                                                         budget=2048), 0, 0),
+}
+
+
+@pytest.mark.parametrize("mode", [adamas.DECODE_AUTO, adamas.DECODE_LAST_ARRIVAL,
+                                  adamas.DECODE_GROUP_WAIT, adamas.DECODE_SPLIT])
+@pytest.mark.parametrize("case", sorted(_SOLO_CASES))
+def test_decode_single_chunk(ora, restore_mode, mode, case):
+    w, n_sink, n_recent = _SOLO_CASES[case]
+    log(f"decode single chunk mode {mode} {case}")
+    adamas.set_decode_mode(mode)
+    lay = synth.make_layer(w, 0, DEV)
+    codes = torch.zeros((w.batch, w.hkv, w.cap, w.head_dim // 4), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    ws = adamas.Workspace(DEV)
+    idx = torch.empty((w.batch, w.hq, w.budget), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, w.n_ctx, w.budget,
+                             idx_out=idx, ws=ws, n_sink=n_sink, n_recent=n_recent)
+    out_noidx = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, w.n_ctx, w.budget,
+                                   ws=ws, n_sink=n_sink, n_recent=n_recent)
+    torch.cuda.synchronize()
+    assert not ws.buf[:adamas.WS_CTRL_BYTES].any(), "control bytes or status word left set"
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    oout, o64, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), w.n_ctx, w.budget, 0.0,
+                                      n_sink, n_recent)
+    assert np.array_equal(idx.cpu().numpy(), oidx), "selection differs"
+    check_out(ora, out, q, k, v, oidx, oout, o64, case)
+    assert torch.equal(out, out_noidx)
+
+
 # --------------------------------------- rotation switched off (ablation)
 @pytest.fixture
 def restore_rotation():

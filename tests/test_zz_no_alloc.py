@@ -69,3 +69,13 @@ def test_static_scratch_rejects_a_shape_beyond_it():
         adamas.decode_step_static(q, big_cap, big_cap, big_codes, 131072, 131072)
     assert e.value.status == 3          # ADAMAS_ERR_WORKSPACE
     del kv, codes
+
+
+def test_static_scratch_single_chunk(ora):
+    # contexts of one chunk: the chunk workgroup's candidates are the selection
+    log("static scratch: 8 q / 2 kv heads x 900 tokens, budget 300 (attention in its own launch)")
+    w = synth.LLAMA32_GQA_1M.replace(hq=8, hkv=2, n_ctx=900, cap=900, budget=300)
+    _pair(ora, w, 300, 900, 2)
+    log("static scratch: then 2 heads x 1000 tokens, budget 128 (fused attention)")
+    w = synth.LLAMA2_32K.replace(hq=2, hkv=2, n_ctx=1000, cap=1000, budget=128)
+    _pair(ora, w, 128, 1000, 3)
