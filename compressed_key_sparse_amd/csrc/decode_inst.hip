@@ -17,10 +17,10 @@
 
 namespace adm_host {
 
-template <int D, int G, bool BF, int RAG, bool OCC, bool U8 = false>
+template <int D, int G, bool BF, int RAG, bool OCC, bool U8 = false, bool ONE = false>
 void launch_decode_k(const DecodePlan& p, dim3 grid, hipStream_t s, const DecodeArgs& a) {
-  allow_lds(&k_decode<D, G, BF, RAG, OCC, U8>, p.sel.lds);
-  k_decode<D, G, BF, RAG, OCC, U8><<<grid, kDecodeThreads, p.sel.lds, s>>>(
+  allow_lds(&k_decode<D, G, BF, RAG, OCC, U8, ONE>, p.sel.lds);
+  k_decode<D, G, BF, RAG, OCC, U8, ONE><<<grid, kDecodeThreads, p.sel.lds, s>>>(
       a.q, a.k, a.v, a.kc, a.Hq, a.Hkv, a.cap, a.n_ctx, p.sel.chunk, p.sel.n_chunks, a.budget,
       p.sel.kpad_log2, p.sel.mcap, (p.fuse && !a.chist) ? 1 : 0, a.qscale, a.cand, a.ctr, a.idx,
       a.out, a.n_sink, a.n_recent, a.rule, a.rg, RAG ? nullptr : a.chist,
@@ -40,9 +40,14 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
       return;
     }
   }
+  // one chunk per KV head: the variant that selects and attends (or writes
+  // the index rows) without a hand-over
+  const bool one = rag == 0 && p.sel.n_chunks == 1 && a.chist == nullptr;
   if constexpr (G == 1) {
     if (occ) {
-      if (rag == 2)
+      if (one)
+        launch_decode_k<D, G, BF, 0, true, false, true>(p, grid, s, a);
+      else if (rag == 2)
         launch_decode_k<D, G, BF, 2, true>(p, grid, s, a);
       else if (rag == 1)
         launch_decode_k<D, G, BF, 1, true>(p, grid, s, a);
@@ -51,7 +56,9 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
       return;
     }
   }
-  if (rag == 2)
+  if (one)
+    launch_decode_k<D, G, BF, 0, false, false, true>(p, grid, s, a);
+  else if (rag == 2)
     launch_decode_k<D, G, BF, 2, false>(p, grid, s, a);
   else if (rag == 1)
     launch_decode_k<D, G, BF, 1, false>(p, grid, s, a);

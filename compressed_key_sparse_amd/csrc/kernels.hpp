@@ -747,13 +747,15 @@ struct RaggedArgs {
 // then overlaps the other's scan.
 // RAG: 0 every sequence holds n_ctx rows; 1 ragged (RaggedArgs); 2 ragged
 // over paged pools.
+// ONE (RAG 0, 16-bit keys): launches of one chunk per KV head; with
+// n_chunks == 1 the chunk's candidates are the selection (see below).
 // U8 (grouped heads, head_dim <= 128, RAG 0): the chunk's keys are kept in
 // LDS as min(key, 255), one byte per (head, token), which fits twice the
 // chunk of 16-bit keys; a launch that would need two rounds of workgroups
 // then runs in one.  Keys below a chunk threshold under 255 are exact; a
 // chunk where some head's threshold reaches 255 rescans its codes half a
 // chunk at a time with exact 16-bit keys.
-template <int D, int G, bool BF, int RAG, bool OCC = false, bool U8 = false>
+template <int D, int G, bool BF, int RAG, bool OCC = false, bool U8 = false, bool ONE = false>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(OCC ? 8 : 1)))
 void k_decode(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -780,6 +782,7 @@ void k_decode(
   const int n_stage = stage_heads(G, 1 << kpad_log2);
   uint32_t* sstage = shist + G * NBP;  // chunk candidates of n_stage heads
   static_assert(!U8 || (G >= 2 && D <= 128 && RAG == 0 && !OCC), "8-bit key variant");
+  static_assert(!ONE || (RAG == 0 && !U8), "single-chunk variant");
   uint16_t* sdist = reinterpret_cast<uint16_t*>(sstage + n_stage * (1 << kpad_log2));
   uint8_t* sdist8 = reinterpret_cast<uint8_t*>(sdist);  // U8: [G][chunk] bytes
   uint32_t* s_fused = reinterpret_cast<uint32_t*>(
@@ -963,7 +966,9 @@ void k_decode(
   // selection itself, so the step needs neither their hand-over, an arrival
   // nor a final selection.  solo: the attention follows at once; solo_sel
   // (attention in a later launch): the index rows are written from here
-  const bool one = RAG == 0 && n_chunks == 1 && chist == nullptr;
+  // (a separate instantiation, so that the multi-chunk kernels keep their
+  // registers and code as they are)
+  const bool one = ONE && n_chunks == 1 && chist == nullptr;
   const bool solo = one && fuse_attend && bsel <= NT && (G == 1 || n_stage == G);
   const bool solo_sel = one && !fuse_attend;
   const auto write_idx = [&](int g, const uint32_t* st) {
