@@ -34,6 +34,12 @@ void instantiate() {
   hipLaunchKernelGGL((k_decode<128, 3, true, 1, false>), dim3(1), dim3(1024), 0, 0, nullptr,
       nullptr, nullptr, nullptr, 0, 0, (int64_t)0, (int64_t)0, 0, 0, 0, 0, 0, 0, 0.f, nullptr,
       nullptr, nullptr, nullptr, 0, 0, EncodeRule{}, RaggedArgs{}, nullptr, 0, nullptr);
+  hipLaunchKernelGGL((k_decode<128, 3, true, 0, false, true>), dim3(1), dim3(1024), 0, 0,
+      nullptr, nullptr, nullptr, nullptr, 0, 0, (int64_t)0, (int64_t)0, 0, 0, 0, 0, 0, 0, 0.f,
+      nullptr, nullptr, nullptr, nullptr, 0, 0, EncodeRule{}, RaggedArgs{}, nullptr, 0, nullptr);
+  hipLaunchKernelGGL((k_decode<128, 2, true, 0, false, false, true>), dim3(1), dim3(1024), 0, 0,
+      nullptr, nullptr, nullptr, nullptr, 0, 0, (int64_t)0, (int64_t)0, 0, 0, 0, 0, 0, 0, 0.f,
+      nullptr, nullptr, nullptr, nullptr, 0, 0, EncodeRule{}, RaggedArgs{}, nullptr, 0, nullptr);
   hipLaunchKernelGGL((k_decode_gs<128, 1, true>), dim3(1), dim3(1024), 0, 0, nullptr, nullptr,
       nullptr, nullptr, 0, 0, (int64_t)0, (int64_t)0, 0, 0, 0, 0, 0.f, nullptr, nullptr, nullptr,
       nullptr, nullptr, 0u, nullptr, nullptr, 0, 0, EncodeRule{}, nullptr);
