@@ -27,6 +27,7 @@ __all__ = [
     "ROTATE_F32", "ROTATE_F16", "GroupWaitGaveUp", "set_wait_polls", "wait_polls",
     "DEFAULT_WAIT_POLLS", "PhaseRecorder", "decode_step_static", "STATIC_SCRATCH_BYTES",
     "set_bucket_alpha", "bucket_alpha", "MAX_ALPHA_GROUPS", "decode_key_bytes",
+    "decode_chunk_tokens",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -116,6 +117,7 @@ def load(variant: str | None = None):
     lib.adamas_bucket_alpha.restype = i32
     lib.adamas_decode_path.argtypes = [i32, i32, i32, i64, i32, i32]
     lib.adamas_decode_key_bytes.argtypes = [i32, i32, i32, i64, i32, i32]
+    lib.adamas_decode_chunk_tokens.argtypes = [i32, i32, i32, i64, i32, i32]
     lib.adamas_set_wait_polls.argtypes = [ctypes.c_uint32]
     lib.adamas_set_wait_polls.restype = i32
     lib.adamas_decode_step_static.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64, i64, i32,
@@ -420,6 +422,15 @@ def decode_key_bytes(B: int, Hq: int, Hkv: int, n_ctx: int, budget: int, head_di
     r = load().adamas_decode_key_bytes(B, Hq, Hkv, n_ctx, budget, head_dim)
     if r < 0:
         raise AdamasError(-r, "adamas_decode_key_bytes")
+    return r
+
+
+def decode_chunk_tokens(B: int, Hq: int, Hkv: int, n_ctx: int, budget: int, head_dim: int) -> int:
+    """Tokens per chunk the decode step plans for this shape
+    (adamas_decode_chunk_tokens)."""
+    r = load().adamas_decode_chunk_tokens(B, Hq, Hkv, n_ctx, budget, head_dim)
+    if r < 0:
+        raise AdamasError(-r, "adamas_decode_chunk_tokens")
     return r
 
 

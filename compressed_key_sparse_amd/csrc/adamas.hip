@@ -182,6 +182,7 @@ size_t adamas_workspace_bytes(int op, int B, int Hq, int Hkv, int64_t n_ctx, int
       return std::max(
           {plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim, true).total,
            plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim, false).total,
+           plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim, false, false).total,
            plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, kSizingCapacity, true).total,
            plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, kComputeUnits, true).total});
     default: return 0;
@@ -299,6 +300,9 @@ int launch_last_arrival(const DecodePlan& p, const DecodeArgs& a, int B, int hea
                         uint8_t* w, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const dim3 grid((unsigned)p.sel.n_chunks, (unsigned)a.Hkv, (unsigned)B);
+  // 32768-token chunks are compacted a half at a time only by the two-per-CU build
+  if (p.big && !decode_two_per_cu(p, G, (int64_t)p.sel.n_chunks * a.Hkv * B))
+    return ADAMAS_ERR_UNSUPPORTED;
   bool ok = false;
   with_dim(head_dim, [&](auto dc) {
     constexpr int D = decltype(dc)::value;
@@ -488,7 +492,7 @@ int ragged_step(const void* q, const void* k_new, const void* v_new, void* k, vo
                                         head_dim))
     return ADAMAS_ERR_WORKSPACE;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  DecodePlan p = plan_decode(B, Hq, Hkv, max_len, budget, head_dim, false);
+  DecodePlan p = plan_decode(B, Hq, Hkv, max_len, budget, head_dim, false, pages == nullptr);
   if (ws_bytes < p.total) return ADAMAS_ERR_WORKSPACE;
   // paged with fused attention: the final workgroup keeps the page table row
   // in LDS after the candidate tile, when it is short and fits
@@ -625,6 +629,18 @@ int adamas_decode_key_bytes(int B, int Hq, int Hkv, int64_t n_ctx, int budget, i
                ? 1
                : 2;
   return plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).u8 ? 1 : 2;
+}
+
+int adamas_decode_chunk_tokens(int B, int Hq, int Hkv, int64_t n_ctx, int budget,
+                               int head_dim) {
+  const int kb = adamas_decode_key_bytes(B, Hq, Hkv, n_ctx, budget, head_dim);
+  if (kb < 0) return kb;
+  if (adamas_decode_path(B, Hq, Hkv, n_ctx, budget, head_dim) == ADAMAS_DECODE_GROUP_WAIT)
+    return plan_decode_gs(B, Hq, Hkv, n_ctx, budget, head_dim, device_capacity(),
+                          g_decode_mode.load(std::memory_order_relaxed) ==
+                              ADAMAS_DECODE_GROUP_WAIT)
+        .chunk;
+  return plan_decode(B, Hq, Hkv, n_ctx, budget, head_dim).sel.chunk;
 }
 
 int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim) {

@@ -32,7 +32,7 @@ void launch_decode_t(const DecodePlan& p, dim3 grid, hipStream_t s, const Decode
   // MHA launches of several rounds run two workgroups per compute unit
   // when their LDS allows it
   const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
-  const bool occ = G == 1 && wgs > kComputeUnits && 2 * p.sel.lds <= kLdsDecodeLimit;
+  const bool occ = decode_two_per_cu(p, G, wgs);  // always so for 32768-token chunks
   const int rag = a.rg.lens == nullptr ? 0 : (a.rg.pages == nullptr ? 1 : 2);
   if constexpr (G >= 2 && D <= 128) {
     if (p.u8 && rag == 0) {

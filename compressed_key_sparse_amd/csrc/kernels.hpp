@@ -1047,8 +1047,39 @@ void k_decode(
       const int64_t row = (int64_t)b * Hq + (int64_t)hkv * G + g;
       const Threshold thr = find_threshold<NT>(shist + g * NBP, NB, (uint32_t)kc, s_tmp);
       ps.mark(3);
-      chunk_compact<NT>(sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt, sstage, kc, kpad,
-                        s_tmp, [](uint32_t, uint32_t) {}, &ps);
+      bool halves = false;
+      if constexpr (OCC && G == 1 && RAG != 2) halves = valid > NT * kCompactTpt;
+      if (!halves) {
+        chunk_compact<NT>(sdist + g * chunk, valid, thr, (uint32_t)kc - thr.lt, sstage, kc,
+                          kpad, s_tmp, [](uint32_t, uint32_t) {}, &ps);
+      } else {
+        // chunks of more than NT * kCompactTpt tokens (multi-round MHA
+        // launches): one compaction pass per half, in token order; s_tot
+        // holds the (below, at) threshold counts of the earlier halves and
+        // the count chunk_collect reports
+        constexpr int kHalf = NT * kCompactTpt;
+        uint32_t* s_tot = s_fused;
+        if (threadIdx.x < 2) s_tot[threadIdx.x] = 0u;
+        const uint32_t quota = (uint32_t)kc - thr.lt;
+        for (int h0 = 0; h0 < valid; h0 += kHalf) {
+          lds_sync();
+          const uint32_t ltp = s_tot[0], eqp = s_tot[1];
+          const uint32_t taken = eqp < quota ? eqp : quota, off = ltp + taken;
+          chunk_collect<NT>(
+              sdist + g * chunk + h0, min(kHalf, valid - h0), thr.t, quota - taken, s_tmp,
+              [&](uint32_t pos, uint32_t tok, uint32_t key) {
+                sstage[off + pos] = (key << 16) | (uint32_t)(h0 + (int)tok);
+              },
+              nullptr, s_tot + 2);
+          lds_sync();
+          if (threadIdx.x == 0) {
+            const uint32_t tot = s_tot[2];
+            s_tot[0] = ltp + (tot & 0xffffu);
+            s_tot[1] = eqp + (tot >> 16);
+          }
+        }
+        for (int j = kc + (int)threadIdx.x; j < kpad; j += NT) sstage[j] = 0xFFFFFFFFu;
+      }
       lds_sync();
       ps.mark(4);
       if (solo_sel)

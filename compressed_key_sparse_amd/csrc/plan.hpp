@@ -125,6 +125,7 @@ inline AttendPlan plan_attend(int64_t rows, int sel_rows, int D, size_t start) {
 struct DecodePlan {
   SelectPlan sel;
   bool u8 = false;  // k_decode keeps 8-bit keys (fewer rounds of workgroups)
+  bool big = false;  // MHA chunks of 32768 tokens, two workgroups per CU, compacted by halves
   bool fuse = false;
   size_t idx_off = 0;
   AttendPlan att;
@@ -146,16 +147,27 @@ inline size_t split_select_lds(int D, int ncp, bool fused) {
   return b;
 }
 
+// The rest of a decode plan once its chunk (and key width) are fixed.
+inline void finish_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int64_t n_ctx, int budget,
+                               int D, int c);
+
+// Whether a last-arrival launch of the plan runs two workgroups per CU (the
+// OCC build): MHA launches of more than one round whose LDS allows it.
+inline bool decode_two_per_cu(const DecodePlan& p, int G, int64_t wgs) {
+  return G == 1 && wgs > kComputeUnits && 2 * p.sel.lds <= kLdsDecodeLimit;
+}
+
 // adamas_decode_step: 1024-thread workgroups, chunks as large as LDS allows
 // (fewer candidates to merge), attention fused into the selecting workgroup
 // when the selection is small (at most two 256-row batches for the group).
 // allow_u8: the launch may take the 8-bit key variant of k_decode (plain
 // contiguous decode steps; the ragged and paged steps keep 16-bit keys).
+// allow_big: MHA launches of several rounds may take 32768-token chunks
+// (not the paged step, whose wavefront stretches must stay inside a page).
 inline DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int D,
-                              bool allow_u8 = true) {
+                              bool allow_u8 = true, bool allow_big = true) {
   DecodePlan p;
   const int G = Hq / Hkv;
-  const int64_t rows = (int64_t)B * Hq;
   auto chunk_for = [&](int c0, int key_bytes) {
     int c = c0;
     while (c > 1024 && kTmpWords * 4 + decode_lds_scan(D, G, c, budget, key_bytes) > kLdsDecodeLimit)
@@ -170,7 +182,18 @@ inline DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget,
   auto rounds = [&](int c) {
     return ((int64_t)B * Hkv * ((n_ctx + c - 1) / c) + kComputeUnits - 1) / kComputeUnits;
   };
+  // 16-bit keys: at most 16384 tokens, one compaction pass of 16 per thread
   int c = chunk_for(16384, 2);
+  // MHA launches of several rounds: chunks twice as long while two
+  // workgroups still share a CU halve the workgroups, candidate lists and
+  // final merges (the chunk is compacted a half at a time)
+  if (allow_big && G == 1 && c == 16384 && rounds(c) > 1 && rounds(2 * c) < rounds(c) &&
+      2 * (kTmpWords * 4 + decode_lds_scan(D, 1, 2 * c, budget, 2)) <= kLdsDecodeLimit) {
+    DecodePlan q;
+    q.big = true;
+    finish_decode_plan(q, B, Hq, Hkv, n_ctx, budget, D, 2 * c);
+    if (decode_two_per_cu(q, G, (int64_t)B * Hkv * q.sel.n_chunks)) return q;
+  }
   // grouped heads whose 16-bit keys cap the chunk so that the launch takes
   // more than one round: 8-bit keys hold chunks twice as long (up to 32768
   // tokens, one compaction thread per 32), when that saves rounds and every
@@ -182,6 +205,14 @@ inline DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget,
       p.u8 = true;
     }
   }
+  finish_decode_plan(p, B, Hq, Hkv, n_ctx, budget, D, c);
+  return p;
+}
+
+inline void finish_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int64_t n_ctx, int budget,
+                               int D, int c) {
+  const int G = Hq / Hkv;
+  const int64_t rows = (int64_t)B * Hq;
   p.sel.chunk = c;
   finish_select_plan(p.sel, rows, n_ctx, budget, ADAMAS_WS_CTRL_BYTES);
   const int bsel = (int)(n_ctx < budget ? n_ctx : budget);
@@ -209,13 +240,14 @@ inline DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t n_ctx, int budget,
     end = p.spart_off + (size_t)rows * p.segs * (size_t)((2 + D + 3) & ~3) * 4;
   }
   p.total = round_up(end, 256);
-  return p;
 }
 
-// More chunk candidates per head than one LDS tile holds: one workgroup
-// selecting from them all would take several passes over global memory.
+// More chunk candidates per head than the selecting workgroup holds in
+// registers (four per thread): it would select from them in LDS tiles, and
+// the separate selection is faster (1M-token MHA layer, budget 256, 32
+// chunks of 256 candidates per head: 184 against 190 us).
 inline bool many_candidates(const DecodePlan& p) {
-  return (int64_t)p.sel.n_chunks * p.sel.kpad > kMaxCandTile;
+  return (int64_t)p.sel.n_chunks * p.sel.kpad > 4 * kDecodeThreads;
 }
 
 // adamas_decode_step with group waits (k_decode_gs): every workgroup of the

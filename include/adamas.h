@@ -196,8 +196,8 @@ int adamas_decode_step(const void *q, const void *k, const void *v,
  *    (ADAMAS_ERR_UNSUPPORTED when forced beyond).
  *  - ADAMAS_DECODE_AUTO (default): LAST_ARRIVAL while its last workgroup can
  *    attend over the whole selection itself (G * ceil(min(budget, n_ctx) /
- *    256) <= 2) from at most 8192 chunk candidates per head; otherwise
- *    GROUP_WAIT where the shape fits, else SPLIT beyond 8192 candidates, else
+ *    256) <= 2) from at most 4096 chunk candidates per head; otherwise
+ *    GROUP_WAIT where the shape fits, else SPLIT beyond 4096 candidates, else
  *    LAST_ARRIVAL with a separate attention launch.
  * Returns ADAMAS_OK, or ADAMAS_ERR_INVALID for an unknown mode.
  */
@@ -284,6 +284,19 @@ int adamas_decode_path(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int he
  * rejects.
  */
 int adamas_decode_key_bytes(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim);
+
+/*
+ * Tokens per chunk (the code rows one decode workgroup scans, §2.3) that
+ * adamas_decode_step plans for this shape under the schedule
+ * adamas_decode_path reports: at least 1024, at most 16384 with 16-bit keys,
+ * 32768 with one-byte keys or for multi-headed (one query per KV head)
+ * launches of more than one round of workgroups, which then run two
+ * workgroups per compute unit and select from each chunk a half at a time.
+ * Host-side planning only; results do not depend on it.  The ragged step
+ * plans the same chunks with 16-bit keys, the paged step at most 16384.
+ * Negated status for a shape adamas_decode_step rejects.
+ */
+int adamas_decode_chunk_tokens(int B, int Hq, int Hkv, int64_t n_ctx, int budget, int head_dim);
 
 /*
  * adamas_select_topk and adamas_decode_step with a set of tokens that is

@@ -321,3 +321,26 @@ def test_decode_key_bytes_planning(lib):
     # the workspace covers both key widths of a shape
     ws = lib.adamas_workspace_bytes(2, 2, 24, 8, 300000, 1024, 128)
     assert ws > 0
+
+
+def test_decode_chunk_planning(lib):
+    """Chunk lengths the decode step plans: 16384 tokens at most with 16-bit
+    keys, shorter while the launch still fits one round, 32768 with one-byte
+    keys and for multi-headed launches of several rounds that keep two
+    workgroups per compute unit; invalid shapes raise."""
+    ct = adamas.decode_chunk_tokens
+    assert ct(1, 32, 32, 131072, 256, 128) == 16384   # the 128K layer: one round
+    assert ct(1, 32, 32, 32768, 256, 128) == 4096     # shorter chunks fill the device
+    assert ct(1, 1, 1, 1024, 64, 64) == 1024
+    assert ct(16, 32, 32, 65536, 512, 128) == 32768   # batch 16: eight rounds become four
+    assert ct(8, 32, 32, 40000, 256, 128) == 32768
+    assert ct(16, 32, 32, 65536, 512, 256) == 32768
+    assert ct(1, 24, 8, 1048576, 1024, 128) == 32768  # one-byte keys
+    assert ct(1, 24, 8, 1048576, 1024, 256) == 16384
+    # one round of 32768-token chunks would leave one workgroup per compute unit
+    assert ct(2, 32, 32, 131072, 256, 128) == 16384
+    assert ct(8, 32, 32, 20001, 256, 128) == 16384
+    with pytest.raises(adamas.AdamasError):
+        ct(1, 24, 7, 1000, 64, 128)
+    # the workspace covers the plan of either chunk length
+    assert lib.adamas_workspace_bytes(2, 16, 32, 32, 65536, 512, 128) > 0

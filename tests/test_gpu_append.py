@@ -191,3 +191,10 @@ def test_append_many_rounds(ora):
     log("append step over 256 KV heads x 2 chunks (two workgroups per compute unit)")
     w = synth.LLAMA2_32K.replace(batch=8, hq=32, hkv=32, n_ctx=20001, cap=20001, budget=256)
     _run(ora, w, [20000, 9000, 16384, 1, 0, 12345, 16383, 19999], 20001, 256)
+
+
+def test_append_long_chunks(ora):
+    log("append step over 256 KV heads x 2 chunks of up to 32768 tokens (two per compute unit)")
+    w = synth.LLAMA2_32K.replace(batch=8, hq=32, hkv=32, n_ctx=40001, cap=40001, budget=256)
+    assert adamas.decode_chunk_tokens(8, 32, 32, 40001, 256, 128) == 32768
+    _run(ora, w, [40000, 9000, 32768, 1, 0, 32767, 16384, 39999], 40001, 256)

@@ -368,6 +368,44 @@ def test_decode_keep(ora, restore_mode, mode, n, budget, n_sink, n_recent):
     check_out(ora, out, q, k, v, oidx, oout, o64, "keep")
 
 
+# ------------------------- 32768-token chunks (multi-round MHA launches)
+# Launches of several rounds of one-query-per-KV-head workgroups run two per
+# compute unit with chunks of 32768 tokens, each selected a half at a time;
+# the second chunk here is a 7232-token tail.
+_LONG_CASES = {
+    "bf16-d128-b256": (synth.LLAMA2_32K.replace(batch=8, hq=32, hkv=32, n_ctx=40000, cap=40000,
+                                                budget=256), 0, 0),
+    "bf16-d128-b512-keep": (synth.LLAMA2_32K.replace(batch=8, hq=32, hkv=32, n_ctx=40000,
+                                                     cap=40010, budget=512), 3, 200),
+    "f32-d64-b100": (synth.TINY.replace(batch=8, hq=32, hkv=32, n_ctx=40000, cap=40000,
+                                        budget=100), 0, 0),
+}
+
+
+@pytest.mark.parametrize("mode", [adamas.DECODE_AUTO, adamas.DECODE_SPLIT])
+@pytest.mark.parametrize("case", sorted(_LONG_CASES))
+def test_decode_long_chunks(ora, restore_mode, mode, case):
+    w, n_sink, n_recent = _LONG_CASES[case]
+    log(f"decode 32768-token chunks mode {mode} {case}")
+    adamas.set_decode_mode(mode)
+    assert adamas.decode_chunk_tokens(w.batch, w.hq, w.hkv, w.n_ctx, w.budget,
+                                      w.head_dim) == 32768
+    lay = synth.make_layer(w, 0, DEV)
+    codes = torch.zeros((w.batch, w.hkv, w.cap, w.head_dim // 4), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    ws = adamas.Workspace(DEV)
+    idx = torch.empty((w.batch, w.hq, w.budget), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, w.n_ctx, w.budget,
+                             idx_out=idx, ws=ws, n_sink=n_sink, n_recent=n_recent)
+    torch.cuda.synchronize()
+    assert not ws.buf[:adamas.WS_CTRL_BYTES].any(), "control bytes or status word left set"
+    q, k, v = (host(lay[x]) for x in ("q", "k", "v"))
+    oout, o64, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), w.n_ctx, w.budget, 0.0,
+                                      n_sink, n_recent)
+    assert np.array_equal(idx.cpu().numpy(), oidx), "selection differs"
+    check_out(ora, out, q, k, v, oidx, oout, o64, case)
+
+
 # ------------------------- one chunk per KV head (selection = its candidates)
 # Contexts of at most one chunk: the chunk workgroup's candidates are the
 # selection, so it attends over them directly (fused attention) or writes the
