@@ -929,12 +929,97 @@ ADM_DEV uint32_t bytes_below(uint32_t x, uint32_t y) {
   const uint32_t z = (x | 0x80808080u) - (y & 0x7F7F7F7Fu);
   return ((~x & y) | (~(x ^ y) & ~z)) & 0x80808080u;
 }
+// The ordered selection of G heads at given thresholds over one-byte keys
+// (every threshold below 255): head g keeps each token of the chunk with key
+// < thr_of(g) and the first quota_of(g) (lowest index) with key ==
+// thr_of(g), calling emit(g, pos, token, key) with pos its rank in token
+// order among head g's kept tokens; with kept non-null, kept[g] (LDS) gets
+// the number kept.  Thread j owns tokens [32j, 32j + 32) (valid <= 32 * NT);
+// four keys per word are compared bytewise without borrows between bytes.
+// s_sums holds NW * G words.  Ends with a workgroup barrier.
+template <int NT, int G, class ThrOf, class QuotaOf, class Emit>
+ADM_DEV void collect_heads_u8(const uint8_t* sdist8, int chunk, int valid, ThrOf&& thr_of,
+                              QuotaOf&& quota_of, uint32_t* s_sums, Emit&& emit,
+                              uint32_t* kept = nullptr, const PhaseStamps* ps = nullptr) {
+  constexpr int NW = NT / kWave, TPT = 32;
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  // counts of keys below t and up to t, and a 32-bit mask of this thread's
+  // tokens with key <= t (the ones the emission visits)
+  const int t0 = threadIdx.x * TPT;
+  const int nv = valid - t0;
+  uint32_t hit[G], mine[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint32_t t = thr_of(g);
+    const uint32_t y = t * 0x01010101u, y1 = (t + 1u) * 0x01010101u;
+    uint32_t nlt = 0, nle = 0, h = 0;
+    if (t0 < valid) {
+      const uint4* src = reinterpret_cast<const uint4*>(sdist8 + g * chunk + t0);
+      const uint4 a = src[0], b4 = src[1];
+      const uint32_t w[TPT / 4] = {a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int j = 0; j < TPT / 4; ++j) {
+        const uint32_t x = w[j];
+        const int left = nv - 4 * j;  // keys past the chunk's valid end count nowhere
+        const uint32_t vm =
+            left >= 4 ? 0x80808080u : (left <= 0 ? 0u : 0x80808080u >> (32 - 8 * left));
+        const uint32_t lt = bytes_below(x, y) & vm, le = bytes_below(x, y1) & vm;
+        nlt += (uint32_t)__popc(lt);
+        nle += (uint32_t)__popc(le);
+        h |= (((le >> 7) * 0x01020408u) >> 24) << (4 * j);  // bit k of byte k -> bit 4j + k
+      }
+    }
+    hit[g] = h;
+    mine[g] = nlt | ((nle - nlt) << 16);
+  }
+  if (ps) ps->mark_last_wave(17);  // masks of every head done
+  uint32_t incl[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    incl[g] = wave_scan_incl(mine[g]);
+    if (lane == kWave - 1) s_sums[wid * G + g] = incl[g];
+  }
+  lds_sync();
+  if (ps) ps->mark(18);  // prefix over the workgroup
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint32_t pre = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t s = s_sums[w * G + g];
+      pre += w < wid ? s : 0u;
+      all += s;
+    }
+    const uint32_t ex = pre + incl[g] - mine[g];
+    uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
+    const uint32_t quota = quota_of(g);
+    const uint32_t t = thr_of(g);
+    if (kept && threadIdx.x == 0) {
+      const uint32_t eq_all = all >> 16;
+      kept[g] = (all & 0xffffu) + (eq_all < quota ? eq_all : quota);
+    }
+    for (uint32_t m = hit[g]; m != 0; m &= m - 1) {
+      const uint32_t tok = (uint32_t)(t0 + __ffs(m) - 1);
+      const uint32_t d = sdist8[g * chunk + tok];
+      if (d < t) {
+        emit(g, ltb + (eqb < quota ? eqb : quota), tok, d);
+        ++ltb;
+      } else {
+        if (eqb < quota) emit(g, ltb + eqb, tok, t);
+        ++eqb;
+      }
+    }
+  }
+  if (ps) ps->mark_last_wave(19);  // tokens emitted
+  lds_sync();
+}
+
 template <int NT, int NB, int G>
 ADM_DEV bool chunk_compact_heads_u8(const uint32_t* hist, int nbp, const uint8_t* sdist8,
                                     int chunk, int valid, uint32_t kc, uint32_t* out, int kpad,
                                     uint32_t* s_thr, uint32_t* s_sums,
                                     const PhaseStamps* ps = nullptr) {
-  constexpr int NW = NT / kWave, BPL = (NB + kWave - 1) / kWave, TPT = 32;
+  constexpr int NW = NT / kWave, BPL = (NB + kWave - 1) / kWave;
   static_assert(G <= NW, "one wavefront per head finds its threshold");
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   if (wid < G) {  // thresholds, as chunk_compact_heads
@@ -972,69 +1057,13 @@ ADM_DEV bool chunk_compact_heads_u8(const uint32_t* hist, int nbp, const uint8_t
 #pragma unroll
   for (int g = 0; g < G; ++g) exact = exact && s_thr[2 * g] < (uint32_t)kKeySat;
   if (!exact) return false;
-  // four keys per word, compared bytewise without borrows between bytes:
-  // counts of keys below t and up to t, and a 32-bit mask of this thread's
-  // tokens with key <= t (the ones the emission visits)
-  const int t0 = threadIdx.x * TPT;
-  const int nv = valid - t0;
-  uint32_t hit[G], mine[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint32_t t = s_thr[2 * g];
-    const uint32_t y = t * 0x01010101u, y1 = (t + 1u) * 0x01010101u;
-    uint32_t nlt = 0, nle = 0, h = 0;
-    if (t0 < valid) {
-      const uint4* src = reinterpret_cast<const uint4*>(sdist8 + g * chunk + t0);
-      const uint4 a = src[0], b4 = src[1];
-      const uint32_t w[TPT / 4] = {a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-      for (int j = 0; j < TPT / 4; ++j) {
-        const uint32_t x = w[j];
-        const int left = nv - 4 * j;  // keys past the chunk's valid end count nowhere
-        const uint32_t vm =
-            left >= 4 ? 0x80808080u : (left <= 0 ? 0u : 0x80808080u >> (32 - 8 * left));
-        const uint32_t lt = bytes_below(x, y) & vm, le = bytes_below(x, y1) & vm;
-        nlt += (uint32_t)__popc(lt);
-        nle += (uint32_t)__popc(le);
-        h |= (((le >> 7) * 0x01020408u) >> 24) << (4 * j);  // bit k of byte k -> bit 4j + k
-      }
-    }
-    hit[g] = h;
-    mine[g] = nlt | ((nle - nlt) << 16);
-  }
-  if (ps) ps->mark_last_wave(17);  // masks of every head done
-  uint32_t incl[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    incl[g] = wave_scan_incl(mine[g]);
-    if (lane == kWave - 1) s_sums[wid * G + g] = incl[g];
-  }
-  lds_sync();
-  if (ps) ps->mark(18);  // prefix over the workgroup
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    uint32_t pre = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) pre += w < wid ? s_sums[w * G + g] : 0u;
-    const uint32_t ex = pre + incl[g] - mine[g];
-    uint32_t ltb = ex & 0xffffu, eqb = ex >> 16;
-    const uint32_t quota = kc - s_thr[2 * g + 1];
-    const uint32_t t = s_thr[2 * g];
-    uint32_t* o = out + g * kpad;
-    for (uint32_t m = hit[g]; m != 0; m &= m - 1) {
-      const uint32_t tok = (uint32_t)(t0 + __ffs(m) - 1);
-      const uint32_t d = sdist8[g * chunk + tok];
-      if (d < t) {
-        o[ltb + (eqb < quota ? eqb : quota)] = (d << 16) | tok;
-        ++ltb;
-      } else {
-        if (eqb < quota) o[ltb + eqb] = (t << 16) | tok;
-        ++eqb;
-      }
-    }
-  }
-  if (ps) ps->mark_last_wave(19);  // tokens emitted
-  lds_sync();
+  collect_heads_u8<NT, G>(
+      sdist8, chunk, valid, [&](int g) { return s_thr[2 * g]; },
+      [&](int g) { return kc - s_thr[2 * g + 1]; }, s_sums,
+      [&](int g, uint32_t pos, uint32_t tok, uint32_t key) {
+        out[g * kpad + pos] = (key << 16) | tok;
+      },
+      nullptr, ps);
   return true;
 }
 

@@ -1544,7 +1544,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   ps.mark(0);
   uint32_t* sq = s_sums + 32;
   uint32_t* shist = sq + G * W;
-  uint32_t* s_tot = shist + G * NBP;  // group counts per bin: all chunks, chunks before
+  uint32_t* s_tot = shist + G * NBP;  // one head's group counts per bin: all chunks, chunks before
   uint32_t* s_bef = s_tot + NBP;
   int32_t* sidx = reinterpret_cast<int32_t*>(s_bef + NBP);
   uint8_t* region = reinterpret_cast<uint8_t*>(sidx + G * cmax);
@@ -1630,16 +1630,17 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
   const int bsel = (int)min((int64_t)budget, n_ctx);
   uint32_t* s_cnt = s_tmp + kTmpGroupCounts;  // rows kept per query head
   if (!complete && (int)threadIdx.x < G) s_cnt[threadIdx.x] = 0;
-  for (int g = 0; g < (complete ? G : 0); ++g) {
-    const int64_t row = row0 + g;
-    // the group's histograms: one 16-byte row segment (8 bins of one chunk)
-    // per thread, summed into LDS
-    for (int i = threadIdx.x; i < 2 * NBP; i += NT) s_tot[i] = 0;
-    lds_sync();
-    {
+  uint32_t* s_grp = s_sums;  // per head: t, lt, lt_before, ties_before
+  if constexpr (G == 1) {
+    // one head: 16-byte row segments (8 bins of one chunk), one per thread,
+    // summed into LDS with atomics, and the threshold with its counts in the
+    // chunks before this one from find_group_threshold
+    if (complete) {
+      for (int i = threadIdx.x; i < 2 * NBP; i += NT) s_tot[i] = 0;
+      lds_sync();
       constexpr int SEG = NBH / 8;
       const __amdgpu_buffer_rsrc_t r =
-          make_rsrc(ghist + row * n_chunks * NBH, (uint32_t)(n_chunks * NBH * 2));
+          make_rsrc(ghist + row0 * n_chunks * NBH, (uint32_t)(n_chunks * NBH * 2));
       for (int i0 = 0; i0 < n_chunks * SEG; i0 += NT) {
         const int i = i0 + (int)threadIdx.x;
         const int cc = i / SEG, b0 = (i % SEG) * 8;
@@ -1655,11 +1656,169 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
           }
         }
       }
+      lds_sync();
+      const uint32_t tot = (int)threadIdx.x < NB ? s_tot[threadIdx.x] : 0u;
+      const uint32_t bef = (int)threadIdx.x < NB ? s_bef[threadIdx.x] : 0u;
+      const GroupThreshold gt =
+          find_group_threshold<NT>(tot, bef, NB, (uint32_t)bsel, s_sums, s_tmp);
+      // (find_group_threshold ends with a barrier after its last use of s_sums)
+      if (threadIdx.x == 0) {
+        s_grp[0] = (uint32_t)gt.t;
+        s_grp[1] = gt.lt;
+        s_grp[2] = gt.lt_before;
+        s_grp[3] = gt.ties_before;
+      }
     }
     lds_sync();
-    const uint32_t tot = (int)threadIdx.x < NB ? s_tot[threadIdx.x] : 0u;
-    const uint32_t bef = (int)threadIdx.x < NB ? s_bef[threadIdx.x] : 0u;
-    const GroupThreshold gt = find_group_threshold<NT>(tot, bef, NB, (uint32_t)bsel, s_sums, s_tmp);
+  } else {
+    // the group's histograms summed for every query head at once, all loads in
+    // one round: thread i takes one 8-bin segment (i % (G * SEG)) of one head
+    // and every P-th chunk from i / (G * SEG), adds its sums into s_grp_tot
+    // (this chunk's own rows, published above, are no longer needed) and
+    // keeps in registers its sum over those of its chunks before this one.
+    // s_grp (in s_sums): per head t, lt, lt_before, ties_before.
+    constexpr int SEG = NBH / 8, SEGS = G * SEG, P = NT / SEGS;
+    static_assert(P >= 1, "one histogram segment per thread at least");
+    uint32_t* s_grp_tot = shist;
+    const int hseg = (int)threadIdx.x < P * SEGS ? (int)threadIdx.x % SEGS : -1;
+    const int hq = (int)threadIdx.x / SEGS;
+    const int hg = hseg >= 0 ? hseg / SEG : 0, hb0 = hseg >= 0 ? (hseg - hg * SEG) * 8 : 0;
+    uint32_t bef8[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (complete) {
+      for (int i = threadIdx.x; i < G * NBP; i += NT) s_grp_tot[i] = 0u;
+      if ((int)threadIdx.x < 4 * G) s_grp[threadIdx.x] = 0u;
+    }
+    lds_sync();
+    if (complete && hseg >= 0) {
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(ghist + (row0 + hg) * n_chunks * NBH, (uint32_t)(n_chunks * NBH * 2));
+      uint32_t tot8[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      constexpr int UL = 8;  // segment loads in flight per thread
+      for (int c0 = hq; c0 < n_chunks; c0 += UL * P) {
+        u32x4 h[UL];
+#pragma unroll
+        for (int u = 0; u < UL; ++u) {
+          const int cc = c0 + u * P;
+          h[u] = cc < n_chunks ? load_shared_x4(r, (uint32_t)(cc * NBH + hb0) * 2u)
+                               : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < UL; ++u) {
+          const uint32_t hw[4] = {h[u].x, h[u].y, h[u].z, h[u].w};
+          const bool before = c0 + u * P < c;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t x = (hw[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+            tot8[j] += x;
+            bef8[j] += before ? x : 0u;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (hb0 + j < NB && tot8[j] != 0u) atomicAdd(&s_grp_tot[hg * NBP + hb0 + j], tot8[j]);
+    }
+    lds_sync();
+    // thresholds: wavefront g scans head g's summed bins
+    if (complete && wid < G) {
+      constexpr int BPL = (NB + kWave - 1) / kWave;
+      const uint32_t* h = s_grp_tot + wid * NBP;
+      uint32_t v[BPL], sum = 0;
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {
+        const int bin = lane * BPL + j;
+        v[j] = bin < NB ? h[bin] : 0u;
+        sum += v[j];
+      }
+      const uint32_t incl = wave_scan_incl(sum), excl = incl - sum;
+      const uint32_t K = (uint32_t)bsel;
+      if (excl < K && K <= incl) {
+        uint32_t acc = excl, lt = 0;
+        int tb = 0;
+#pragma unroll
+        for (int j = 0; j < BPL; ++j) {
+          if (acc < K && K <= acc + v[j]) {
+            tb = lane * BPL + j;
+            lt = acc;
+          }
+          acc += v[j];
+        }
+        s_grp[4 * wid] = (uint32_t)tb;
+        s_grp[4 * wid + 1] = lt;
+      }
+    }
+    lds_sync();
+    // the chunks before this one: their counts below and at each threshold,
+    // summed over each wavefront first (one LDS atomic per wavefront and head
+    // instead of one per thread on the same two words)
+    if (complete) {
+      uint32_t lt_b = 0, eq_b = 0;
+      if (hseg >= 0) {
+        const int tb = (int)s_grp[4 * hg];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          lt_b += hb0 + j < tb ? bef8[j] : 0u;
+          eq_b += hb0 + j == tb ? bef8[j] : 0u;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const bool here = hseg >= 0 && hg == g;
+        const uint32_t sl = __builtin_amdgcn_readlane(wave_scan_incl(here ? lt_b : 0u), kWave - 1);
+        const uint32_t se = __builtin_amdgcn_readlane(wave_scan_incl(here ? eq_b : 0u), kWave - 1);
+        if (lane == 0) {
+          if (sl) atomicAdd(&s_grp[4 * g + 2], sl);
+          if (se) atomicAdd(&s_grp[4 * g + 3], se);
+        }
+      }
+    }
+    lds_sync();
+  }
+  // this chunk's share of head g's threshold ties and where its tokens start
+  // in the ascending selection (no subtraction wraps)
+  const auto share = [&](int g, uint32_t& mine_q, uint32_t& off) {
+    const uint32_t quota = (uint32_t)bsel - s_grp[4 * g + 1];  // ties the group keeps
+    const uint32_t tb = s_grp[4 * g + 3], before = tb < quota ? tb : quota;
+    mine_q = quota - before;
+    off = s_grp[4 * g + 2] + before;
+  };
+  bool heads_at_once = false;
+  if constexpr (U8) {
+    heads_at_once = complete;
+#pragma unroll
+    for (int g = 0; g < G; ++g) heads_at_once = heads_at_once && s_grp[4 * g] < (uint32_t)kKeySat;
+  }
+  if (heads_at_once) {
+    // every head's share in one pass over the byte keys (the summed
+    // histograms in shist are no longer needed: their rows hold the prefix)
+    collect_heads_u8<NT, G>(
+        sdist8, chunk, valid, [&](int g) { return s_grp[4 * g]; },
+        [&](int g) {
+          uint32_t mq, off;
+          share(g, mq, off);
+          return mq;
+        },
+        shist,
+        [&](int g, uint32_t pos, uint32_t t, uint32_t) {
+          const int32_t tok = (int32_t)(t0 + t);
+          sidx[g * cmax + pos] = tok;
+          if (idx) {
+            uint32_t mq, off;
+            share(g, mq, off);
+            idx[(row0 + g) * budget + off + pos] = tok;
+          }
+        },
+        s_cnt);
+    if (idx && c == 0)
+      for (int j = (int)threadIdx.x; j < G * (budget - bsel); j += NT) {
+        const int g = j / (budget - bsel);
+        idx[(row0 + g) * budget + bsel + (j - g * (budget - bsel))] = -1;
+      }
+  }
+  for (int g = 0; g < (complete && !heads_at_once ? G : 0); ++g) {
+    const int64_t row = row0 + g;
+    const GroupThreshold gt{(int)s_grp[4 * g], s_grp[4 * g + 1], s_grp[4 * g + 2],
+                            s_grp[4 * g + 3]};
     const uint32_t quota = (uint32_t)bsel - gt.lt;  // ties at t the whole group keeps
     // ties kept by the chunks before, then this chunk's share (no subtraction wraps)
     const uint32_t before = gt.ties_before < quota ? gt.ties_before : quota;
@@ -1737,14 +1896,17 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
     ps.flush();
     return;
   }
-  for (int g = 0; g < G; ++g) {
-    const int64_t row = row0 + g;
+  // merge: every head's chunk partials by log-sum-exp, all heads at once;
+  // tiles of nt chunks (the whole group when the chunk's key region holds
+  // it) pass through LDS, thread j merging dimension j % D of head j / D.
+  // One head: tiles of kGsMergeTile partials, thread j < D merging dim j.
+  if constexpr (G == 1) {
     float M = -INFINITY, L = 0.0f, O = 0.0f;
     for (int c0 = 0; c0 < n_chunks; c0 += kGsMergeTile) {
       const int nt = min(kGsMergeTile, n_chunks - c0);
       lds_sync();
       shared_to_lds<NT>(reinterpret_cast<uint32_t*>(s_merge),
-                        reinterpret_cast<const uint32_t*>(part + (row * n_chunks + c0) * PWP),
+                        reinterpret_cast<const uint32_t*>(part + (row0 * n_chunks + c0) * PWP),
                         nt * PWP);
       lds_sync();
       if ((int)threadIdx.x < D) {
@@ -1760,7 +1922,59 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode_gs(
         }
       }
     }
-    if ((int)threadIdx.x < D) store_out<BF>(out, row * D + threadIdx.x, L > 0.0f ? O / L : 0.0f);
+    if ((int)threadIdx.x < D) store_out<BF>(out, row0 * D + threadIdx.x, L > 0.0f ? O / L : 0.0f);
+  } else {
+    const int region_words = max(G * chunk * (U8 ? 1 : 2) / 4, kGsMergeTile * PWP);
+    const int nt_max = max(1, region_words / (G * PWP));
+    constexpr int PAIRS = (G * D + NT - 1) / NT;
+    float M[PAIRS], L[PAIRS], O[PAIRS];
+#pragma unroll
+    for (int u = 0; u < PAIRS; ++u) {
+      M[u] = -INFINITY;
+      L[u] = 0.0f;
+      O[u] = 0.0f;
+    }
+    for (int c0 = 0; c0 < n_chunks; c0 += nt_max) {
+      const int nt = min(nt_max, n_chunks - c0);
+      lds_sync();
+      if (nt == n_chunks) {  // the group's rows are contiguous
+        shared_to_lds<NT>(reinterpret_cast<uint32_t*>(s_merge),
+                          reinterpret_cast<const uint32_t*>(part + row0 * n_chunks * PWP),
+                          G * n_chunks * PWP);
+      } else {
+        for (int g = 0; g < G; ++g)
+          shared_to_lds<NT>(reinterpret_cast<uint32_t*>(s_merge + g * nt * PWP),
+                            reinterpret_cast<const uint32_t*>(part + ((row0 + g) * n_chunks + c0) * PWP),
+                            nt * PWP);
+      }
+      lds_sync();
+#pragma unroll
+      for (int u = 0; u < PAIRS; ++u) {
+        const int j = (int)threadIdx.x + u * NT;
+        if (j < G * D) {
+          const int g = j / D, d = j - g * D;
+          const float* pg = s_merge + g * nt * PWP;
+          for (int i = 0; i < nt; ++i) {
+            const float mi = pg[i * PWP];
+            if (mi == -INFINITY) continue;
+            const float Mn = fmaxf(M[u], mi);
+            const float a = (M[u] == -INFINITY) ? 0.0f : exp2f(M[u] - Mn);
+            const float bb = exp2f(mi - Mn);
+            L[u] = L[u] * a + pg[i * PWP + 1] * bb;
+            O[u] = O[u] * a + pg[i * PWP + 2 + d] * bb;
+            M[u] = Mn;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PAIRS; ++u) {
+      const int j = (int)threadIdx.x + u * NT;
+      if (j < G * D) {
+        const int g = j / D, d = j - g * D;
+        store_out<BF>(out, (row0 + g) * D + d, L[u] > 0.0f ? O[u] / L[u] : 0.0f);
+      }
+    }
   }
   if (threadIdx.x == 0) {
     arrive_hist[grp] = 0;
