@@ -60,7 +60,7 @@ def algorithmic_bytes(B, Hq, Hkv, d, n_ctx, budget, elem_bytes):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--budget", type=int, default=256)
     ap.add_argument("--layers", type=int, default=None, help="override the 32-layer stack")
