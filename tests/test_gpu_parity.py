@@ -587,3 +587,40 @@ def test_group_wait_give_up_is_reported(ora, restore_mode):
     oout, o64, oidx = ora.decode_step(q, k, v, ora.encode_keys(k), w.n_ctx, w.budget)
     assert np.array_equal(idx.cpu().numpy(), oidx)
     check_out(ora, out, q, k, v, oidx, oout, o64, "after a give-up")
+
+
+@pytest.mark.parametrize("hq,hkv,n,budget,key_bytes", [(6, 2, 20000, 256, 2),
+                                                       (24, 8, 300000, 1024, 1)])
+def test_group_wait_give_up_grouped_heads(restore_mode, hq, hkv, n, budget, key_bytes):
+    """The same give-up for grouped heads (16-bit and one-byte keys): the
+    status word is set, the control bytes are left zero, and a re-armed
+    workspace then gives the same result as a fresh one."""
+    w = synth.LLAMA32_GQA_1M.replace(hq=hq, hkv=hkv, n_ctx=n, cap=n, budget=budget)
+    adamas.set_decode_mode(adamas.DECODE_GROUP_WAIT)
+    assert adamas.decode_path(1, hq, hkv, n, budget, 128) == adamas.DECODE_GROUP_WAIT
+    assert adamas.decode_key_bytes(1, hq, hkv, n, budget, 128) == key_bytes
+    log(f"group wait give-up, {hq}/{hkv} heads x {n} tokens, {key_bytes}-byte keys")
+    lay = synth.make_layer(w, 0, DEV)
+    codes = torch.zeros((1, hkv, n, 32), dtype=torch.uint8, device=DEV)
+    adamas.encode_keys(lay["k"], codes)
+    ws = adamas.Workspace(DEV)
+    try:
+        adamas.set_wait_polls(0)
+        adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, n, budget, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        adamas.set_wait_polls(adamas.DEFAULT_WAIT_POLLS)
+    assert ws.status() != 0, "no give-up reported"
+    assert ws.control_bytes_clear(), "arrival counters left set after a give-up"
+    with pytest.raises(adamas.GroupWaitGaveUp):
+        ws.check()
+    idx = torch.empty((1, hq, budget), dtype=torch.int32, device=DEV)
+    out = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, n, budget, idx_out=idx, ws=ws,
+                             check=True)
+    idx2 = torch.empty_like(idx)
+    out2 = adamas.decode_step(lay["q"], lay["k"], lay["v"], codes, n, budget, idx_out=idx2,
+                              ws=adamas.Workspace(DEV), check=True)
+    torch.cuda.synchronize()
+    assert ws.status() == 0 and ws.control_bytes_clear()
+    assert torch.equal(idx, idx2) and torch.equal(out, out2)
+
