@@ -389,6 +389,7 @@ def main():
     torch.cuda.synchronize()
     stream_gbs = sr.numel() * 4 * 5 / (s0.elapsed_time(s1) * 1e-3) / 1e9
     del sr, sink
+    cr_us, cr_gbs = code_read_floor([lay["codes"] for lay in layers], stream, K, args.warmup)
 
     if args.copy_calibration:
         # a plain conversion kernel of known traffic (reads 1 GiB of fp32,
@@ -456,6 +457,7 @@ def main():
         "stream_read": {"kernel": "adamas_stream_read over 4 GiB", "gbs": round(stream_gbs, 1),
                         "frac_of_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
                         "decode_over_stream": round(achieved / stream_gbs, 4)},
+        "code_read": code_read_entry(cr_us, cr_gbs, achieved, L),
         "needle_recall": recall,
         "decode_path": adamas.decode_path(B, Hq, Hkv, n, bud, d),
         "cpu_baseline": cpu,
@@ -598,6 +600,42 @@ def stream_read_gbs(dev):
     return sr.numel() * 4 * 5 / (s0.elapsed_time(s1) * 1e-3) / 1e9
 
 
+def code_read_floor(code_caches, stream, K, warmup):
+    """The same streaming read over each layer's code cache in turn (the
+    bytes one decode launch scans, nothing else), replayed as a HIP graph like
+    the decode steps: the time a launch needs to read its codes at this size,
+    ramp-up and drain included.  -> (us per cache, GB/s)."""
+    import torch
+
+    import compressed_key_sparse_amd as adamas
+    sinks = [adamas.stream_read(c, stream=stream) for c in code_caches]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for c, k in zip(code_caches, sinks):
+                adamas.stream_read(c, k, stream=stream)
+        for _ in range(warmup):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(K):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (K * len(code_caches))
+    nbytes = code_caches[0].numel() * code_caches[0].element_size()
+    return us, nbytes / (us * 1e-6) / 1e9
+
+
+def code_read_entry(us, gbs, achieved, n_caches):
+    return {"kernel": f"adamas_stream_read of each code cache in turn ({n_caches}), graph replay",
+            "us_per_cache": round(us, 3), "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "decode_over_code_read": round(achieved / gbs, 4)}
+
+
 def timed_launches(launch, n_launch, stream, K):
     """Call launch(i) for i in [0, n_launch) K times, HIP events around each
     call on `stream` -> (ms per pass of n_launch calls, mean launch us)."""
@@ -697,6 +735,7 @@ def bench_single(args, dev, w):
     if ws.status() != 0:
         raise SystemExit("bench.py: a group-wait decode step gave up waiting")
     per_launch = algorithmic_bytes(B, Hq, Hkv, d, n, bud, 4 if w.dtype == "f32" else 2)
+    cr_us, cr_gbs = code_read_floor([r[1] for r in reps], stream, K, args.warmup)
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline([r[0] for r in reps[:4]], w.replace(layers=1), n, bud,
@@ -711,6 +750,7 @@ def bench_single(args, dev, w):
                        "p50": round(float(np.percentile(per, 50)), 3),
                        "p90": round(float(np.percentile(per, 90)), 3)},
          "eager_event_launch_us": round(launch_us, 3),
+         "code_read": code_read_entry(cr_us, cr_gbs, per_launch / (us * 1e-6) / 1e9, R),
          "decode_path": adamas.decode_path(B, Hq, Hkv, n, bud, d)}, cpu)
 
 
@@ -769,6 +809,7 @@ def bench_gqa(args, dev):
         raise SystemExit("bench.py: a group-wait decode step gave up waiting (workspace status "
                          "word set): the timed outputs are invalid")
     per_launch = algorithmic_bytes(B, Hq, Hkv, d, n, bud, 2)
+    cr_us, cr_gbs = code_read_floor([c for _, c, _ in layers], stream, K, args.warmup)
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline([layers[0][0]], w.replace(layers=1), n, bud, args.cpu_seconds)
@@ -780,6 +821,7 @@ def bench_gqa(args, dev):
         "adamas_decode_step (one layer)", per_launch, ms * 1e3, stream_read_gbs(dev),
         {"eager_ms_per_step": round(eager_ms / 4, 4),
          "eager_event_launch_us": round(launch_us, 3),
+         "code_read": code_read_entry(cr_us, cr_gbs, per_launch / (ms * 1e-3) / 1e9, 4),
          "decode_path": adamas.decode_path(B, Hq, Hkv, n, bud, d)}, cpu)
 
 
