@@ -892,22 +892,24 @@ class BatchAppendState:
                                       k_new=self.kn, v_new=self.vn, out=self.out,
                                       idx_out=idx_out, ws=self.ws, stream=self.s1)
 
-    def encode_chunk(self, i):
-        """Enqueue step i's prefill chunk on s2 (its sequence is i mod 16)."""
+    def encode_chunk(self, i, stream=None):
+        """Enqueue step i's prefill chunk (its sequence is i mod 16) on s2, or
+        on `stream`."""
         import torch
 
         import compressed_key_sparse_amd as adamas
         b, n, P = i % self.w.batch, self.w.n_ctx, self.PAGE
-        with torch.cuda.stream(self.s2):
+        s = self.s2 if stream is None else stream
+        with torch.cuda.stream(s):
             ch = self.chunks[i % len(self.chunks)]
             if self.paged:   # the chunk's four pages, one encode call each
                 for j, pg in enumerate(self.spare):
                     adamas.encode_keys(ch[:, :, j * P:(j + 1) * P].contiguous(),
                                        self.cp[pg:pg + 1], x_copy=self.kp[pg:pg + 1],
-                                       stream=self.s2)
+                                       stream=s)
             else:
                 adamas.encode_keys(ch, self.codes[b:b + 1], pos=n, x_copy=self.k[b:b + 1],
-                                   stream=self.s2)
+                                   stream=s)
 
     def step(self, i, timed=None, idx_out=None):
         self.s2.wait_stream(self.s1)
@@ -925,7 +927,13 @@ def bench_batch_append(args, dev):
     and decodes (one launch on stream 1) while a 4096-token chunk for sequence
     (step mod 16) is encoded and its K rows copied into the reserved tail rows
     [65536, 69632) on stream 2 (BatchAppendState).  Timed eagerly (the
-    chunk's sequence changes every step): step = both streams done."""
+    chunk's sequence changes every step).  The chunk writes rows no decode
+    step reads, so stream 1 never waits for stream 2 inside the timed region:
+    step i's chunk starts once step i - 1's decode is done (an event that
+    stream 2 waits for) and runs beside step i's decode; both streams are
+    joined at the ends of the K steps, and step time = that region / K.  The
+    same K steps with both streams joined after every step (step_joined_ms)
+    add a cross-stream wait each way per step."""
     import numpy as np
     import torch
 
@@ -936,22 +944,51 @@ def bench_batch_append(args, dev):
     print(f"[bench] setup: batch {B} x {Hq} heads x {n} rows, budget {bud}, append", file=sys.stderr,
           flush=True)
     st = BatchAppendState(w, dev, bud, paged=args.paged)
-    s1, step, decode = st.s1, st.step, st.decode
+    s1, s2, step, decode = st.s1, st.s2, st.step, st.decode
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(K)]
+
+    def event_pairs():
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(K)]
+
+    # the timed run: chunk i on stream 2 after decode i - 1, beside decode i
+    pairs = event_pairs()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s1)
+    s2.wait_stream(s1)
+    for i in range(K):
+        if i > 0:
+            s2.wait_event(pairs[i - 1][1])
+        st.encode_chunk(i)
+        pairs[i][0].record(s1)
+        decode()
+        pairs[i][1].record(s1)
+    s1.wait_stream(s2)
+    e1.record(s1)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    launch_us = float(np.mean([a.elapsed_time(b) for a, b in pairs]) * 1e3)
+    # the same steps with both streams joined after each one
+    jpairs = event_pairs()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     marks[0].record(s1)
     for i in range(K):
-        step(i, pairs[i])
+        step(i, jpairs[i])
         marks[i + 1].record(s1)
     torch.cuda.synchronize()
     step_times = [marks[i].elapsed_time(marks[i + 1]) for i in range(K)]
-    ms = marks[0].elapsed_time(marks[K]) / K
-    launch_us = float(np.mean([a.elapsed_time(b) for a, b in pairs]) * 1e3)
+    # and with each chunk on stream 1, before its step's decode (no overlap)
+    o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o0.record(s1)
+    for i in range(K):
+        st.encode_chunk(i, stream=s1)
+        decode()
+    o1.record(s1)
+    torch.cuda.synchronize()
+    one_stream_ms = o0.elapsed_time(o1) / K
     # decode alone (no chunk on stream 2), for the launch's uncontended rate
     alone_ms, alone_us = timed_launches(lambda i: decode(), 1, s1, K)
     # plus the new rows: k_new, v_new read, K, V and code rows written
@@ -966,13 +1003,15 @@ def bench_batch_append(args, dev):
         {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
          "n_ctx": n, "budget": bud, "prefill_chunk": w.chunk,
          "layout": "paged, 1024-token pages, shuffled" if args.paged else "contiguous",
-         "timing": "eager, two streams, step = both done"},
+         "timing": "eager; chunk i on stream 2 beside decode i, streams joined at the ends"},
         ("adamas_decode_paged_step" if args.paged else "adamas_decode_append_step")
         + " (16 sequences, 4096-token chunk encoding beside it)",
         per_launch, launch_us, stream_read_gbs(dev),
-        {"step_ms": {"p10": round(float(np.percentile(step_times, 10)), 4),
-                     "p50": round(float(np.percentile(step_times, 50)), 4),
-                     "p90": round(float(np.percentile(step_times, 90)), 4)},
+        {"step_joined_ms": {"mean": round(marks[0].elapsed_time(marks[K]) / K, 4),
+                            "p10": round(float(np.percentile(step_times, 10)), 4),
+                            "p50": round(float(np.percentile(step_times, 50)), 4),
+                            "p90": round(float(np.percentile(step_times, 90)), 4)},
+         "one_stream_ms": round(one_stream_ms, 4),
          "hbm_gbs_step": round((per_launch + chunk_bytes) / (ms * 1e-3) / 1e9, 1),
          "decode_alone_us": round(alone_us, 3),
          "decode_alone_gbs": round(per_launch / (alone_us * 1e-6) / 1e9, 1)}, cpu)
