@@ -253,6 +253,13 @@ ADM_DEV uint4 load_stream(const uint4* p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// Streaming 16-byte store of data no kernel reads back soon (non-temporal).
+ADM_DEV void store_stream(uint4* p, uint4 v) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<v4u*>(p));
+}
+
 // ------------------------------------------------------- lane exchanges
 // x from lane (lane ^ M) of the wavefront, without the LDS crossbar:
 //   M = 1, 2: DPP quad permutations [1,0,3,2], [2,3,0,1];

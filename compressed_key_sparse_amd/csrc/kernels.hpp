@@ -68,7 +68,9 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
   // a 16-lane slot per vector: lane l holds dimensions [l*EL, l*EL + EL), so
   // the butterflies of distance below EL stay in registers and the others
   // (EL, 2EL, 4EL, 8EL) are DPP exchanges inside the slot's row of 16 lanes;
-  // each lane moves 16 bytes or more of the vector per access
+  // each lane moves 16 bytes or more of the vector per access.  The rows are
+  // read once and their copies not read back soon: non-temporal accesses
+  // (they slow a decode streaming beside the encoder less)
   constexpr int EL = D / 16, SLOTS = kEncodeThreads / 16;
   constexpr int kGroupLanes = (D > 128 ? 128 : D) / EL;  // lanes of one absmax group
   const int l16 = threadIdx.x & 15;
@@ -90,10 +92,11 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
       } else {
 #pragma unroll
         for (int k = 0; k < NB / 16; ++k) {
-          const uint4 t = reinterpret_cast<const uint4*>(s8)[k];
+          const uint4 t = load_stream(reinterpret_cast<const uint4*>(s8) + k);
           w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
           if (copy != nullptr)
-            reinterpret_cast<uint4*>(static_cast<uint16_t*>(copy) + row * D + l16 * EL)[k] = t;
+            store_stream(
+                reinterpret_cast<uint4*>(static_cast<uint16_t*>(copy) + row * D + l16 * EL) + k, t);
         }
       }
 #pragma unroll
@@ -103,11 +106,12 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
       const uint4* s4 = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + src);
 #pragma unroll
       for (int k = 0; k < EL / 4; ++k) {
-        const uint4 t = s4[k];
+        const uint4 t = load_stream(s4 + k);
         y[4 * k] = __uint_as_float(t.x); y[4 * k + 1] = __uint_as_float(t.y);
         y[4 * k + 2] = __uint_as_float(t.z); y[4 * k + 3] = __uint_as_float(t.w);
         if (copy != nullptr)
-          reinterpret_cast<uint4*>(static_cast<float*>(copy) + row * D + l16 * EL)[k] = t;
+          store_stream(reinterpret_cast<uint4*>(static_cast<float*>(copy) + row * D + l16 * EL) + k,
+                       t);
       }
     }
     if (rule.rotate == 1)
