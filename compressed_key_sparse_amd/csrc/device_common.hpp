@@ -927,15 +927,63 @@ ADM_DEV void chunk_compact_heads(const uint32_t* hist, int nbp, const uint16_t* 
 // and the staging rows' tails already set; the caller must then select from
 // exact keys.
 constexpr int kKeySat = 255;
-// Bytewise x < y over the four bytes of two words, as bit 7 of each byte of
-// the result (no borrow crosses a byte): below in the high bit, or equal high
-// bits and below in the low seven, the latter read from
-// (x | 0x80) - (y & 0x7f) per byte, whose high bit is set iff x's low seven
-// bits are not below y's.
-ADM_DEV uint32_t bytes_below(uint32_t x, uint32_t y) {
-  const uint32_t z = (x | 0x80808080u) - (y & 0x7F7F7F7Fu);
-  return ((~x & y) | (~(x ^ y) & ~z)) & 0x80808080u;
+// x < u in each byte of x, for one byte value u in all four bytes, as bit 7
+// of each byte of the result (the others clear).  xm = x | 0x80808080; c holds
+// u in each byte (LO, u <= 128) or u - 128 (HI, u >= 128).  Per byte,
+// xm - c = 0x80 + (x & 0x7F) - c_b never borrows from the next byte, and its
+// bit 7 (z7) is set iff x's low seven bits are >= c_b.  LO: x < u iff x's bit
+// 7 and z7 are both clear (u = 128: c_b = 128 leaves z7 clear, x < 128 iff
+// bit 7 of x is); HI: iff either of them is clear.
+template <bool HI>
+ADM_HOST_DEV inline uint32_t bytes_below_u(uint32_t x, uint32_t xm, uint32_t c) {
+  const uint32_t z = xm - c;
+  return ~(HI ? (x & z) : (x | z)) & 0x80808080u;
 }
+// Bits 7, 15, 23, 31 of m to bits 0..3: the multiplier's four terms move bit
+// 7 + 8k to 28 + k; the other products land on distinct bits (no carries)
+// below 28 or past 31.
+ADM_HOST_DEV inline uint32_t byte_flags_nibble(uint32_t m) { return (m * 0x00204081u) >> 28; }
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+// Counts and hit mask of one thread's 32 one-byte keys k[0..32) (LDS, 16-byte
+// aligned) against a threshold t <= 254: nlt = #keys < t, nle = #keys <= t,
+// bit i of hit set iff k[i] <= t.  Keys from nv on (all when nv <= 0) count
+// nowhere: they are read as 255, which no such threshold reaches.
+ADM_DEV void byte_key_counts(const uint8_t* k, int nv, uint32_t t, uint32_t& nlt,
+                             uint32_t& nle, uint32_t& hit) {
+  nlt = nle = hit = 0;
+  if (nv <= 0) return;
+  const uint4 a = reinterpret_cast<const uint4*>(k)[0], b = reinterpret_cast<const uint4*>(k)[1];
+  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  if (nv < 32) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int left = nv - 4 * j;
+      w[j] |= left >= 4 ? 0u : (left <= 0 ? 0xFFFFFFFFu : 0xFFFFFFFFu << (8 * left));
+    }
+  }
+  const auto pass = [&](auto hi, uint32_t c0, uint32_t c1) {
+    constexpr bool HI = decltype(hi)::value;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = w[j], xm = x | 0x80808080u;
+      const uint32_t lt = bytes_below_u<HI>(x, xm, c0), le = bytes_below_u<HI>(x, xm, c1);
+      nlt += (uint32_t)__popc(lt);
+      nle += (uint32_t)__popc(le);
+      hit |= byte_flags_nibble(le) << (4 * j);
+    }
+  };
+  // keys below t and below t + 1, both with the LO form while t + 1 <= 128
+  if (t <= 127u)
+    pass(BoolC<false>{}, t * 0x01010101u, (t + 1u) * 0x01010101u);
+  else
+    pass(BoolC<true>{}, (t - 128u) * 0x01010101u, (t - 127u) * 0x01010101u);
+}
+
 // The ordered selection of G heads at given thresholds over one-byte keys
 // (every threshold below 255): head g keeps each token of the chunk with key
 // < thr_of(g) and the first quota_of(g) (lowest index) with key ==
@@ -957,26 +1005,8 @@ ADM_DEV void collect_heads_u8(const uint8_t* sdist8, int chunk, int valid, ThrOf
   uint32_t hit[G], mine[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const uint32_t t = thr_of(g);
-    const uint32_t y = t * 0x01010101u, y1 = (t + 1u) * 0x01010101u;
-    uint32_t nlt = 0, nle = 0, h = 0;
-    if (t0 < valid) {
-      const uint4* src = reinterpret_cast<const uint4*>(sdist8 + g * chunk + t0);
-      const uint4 a = src[0], b4 = src[1];
-      const uint32_t w[TPT / 4] = {a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-      for (int j = 0; j < TPT / 4; ++j) {
-        const uint32_t x = w[j];
-        const int left = nv - 4 * j;  // keys past the chunk's valid end count nowhere
-        const uint32_t vm =
-            left >= 4 ? 0x80808080u : (left <= 0 ? 0u : 0x80808080u >> (32 - 8 * left));
-        const uint32_t lt = bytes_below(x, y) & vm, le = bytes_below(x, y1) & vm;
-        nlt += (uint32_t)__popc(lt);
-        nle += (uint32_t)__popc(le);
-        h |= (((le >> 7) * 0x01020408u) >> 24) << (4 * j);  // bit k of byte k -> bit 4j + k
-      }
-    }
-    hit[g] = h;
+    uint32_t nlt, nle;
+    byte_key_counts(sdist8 + g * chunk + t0, nv, thr_of(g), nlt, nle, hit[g]);
     mine[g] = nlt | ((nle - nlt) << 16);
   }
   if (ps) ps->mark_last_wave(17);  // masks of every head done
@@ -1084,23 +1114,8 @@ ADM_DEV uint32_t chunk_collect_u8(const uint8_t* skey, int valid, int t, uint32_
   constexpr int TPT = 32;
   const int t0 = threadIdx.x * TPT;
   const int nv = valid - t0;
-  const uint32_t y = (uint32_t)t * 0x01010101u, y1 = (uint32_t)(t + 1) * 0x01010101u;
-  uint32_t nlt = 0, nle = 0, hit = 0;
-  if (t0 < valid) {
-    const uint4* src = reinterpret_cast<const uint4*>(skey + t0);
-    const uint4 a = src[0], b4 = src[1];
-    const uint32_t w[TPT / 4] = {a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-    for (int j = 0; j < TPT / 4; ++j) {
-      const int left = nv - 4 * j;
-      const uint32_t vm =
-          left >= 4 ? 0x80808080u : (left <= 0 ? 0u : 0x80808080u >> (32 - 8 * left));
-      const uint32_t lt = bytes_below(w[j], y) & vm, le = bytes_below(w[j], y1) & vm;
-      nlt += (uint32_t)__popc(lt);
-      nle += (uint32_t)__popc(le);
-      hit |= (((le >> 7) * 0x01020408u) >> 24) << (4 * j);
-    }
-  }
+  uint32_t nlt, nle, hit;
+  byte_key_counts(skey + t0, nv, (uint32_t)t, nlt, nle, hit);
   const uint32_t mine = nlt | ((nle - nlt) << 16);
   uint32_t tot;
   const uint32_t ex = block_scan_incl<NT>(mine, s_tmp, &tot) - mine;
