@@ -30,7 +30,8 @@ Prints ONE JSON line with:
                             encoded and copied on a second stream.  With
                             --paged the caches are a shuffled pool of
                             1024-token pages (adamas_decode_paged_step) and
-                            the chunk fills four spare pool pages.
+                            the chunk fills four spare pool pages
+                            (adamas_encode_keys_paged).
 """
 from __future__ import annotations
 
@@ -832,8 +833,8 @@ class BatchAppendState:
     4096-token chunk for sequence (step mod 16) is encoded and its K rows
     copied into the reserved tail rows [65536, 69632) on stream s2.  With
     paged=True the same rows sit in a shuffled pool of 1024-token pages and
-    the chunk fills four spare pool pages.  The parity tests build the same
-    state and check the same calls."""
+    the chunk fills four spare pool pages (one adamas_encode_keys_paged
+    call).  The parity tests build the same state and check the same calls."""
 
     PAGE = 1024
 
@@ -857,6 +858,7 @@ class BatchAppendState:
             perm = np.random.default_rng(5).permutation(n_pages)
             self.table = torch.from_numpy(perm[:B * per].reshape(B, per).astype(np.int32)).to(dev)
             self.spare = [int(x) for x in perm[B * per:]]
+            self.spare_table = torch.tensor([self.spare], dtype=torch.int32, device=dev)
             self.kp = torch.empty((n_pages, Hkv, P, d), dtype=w.torch_dtype, device=dev)
             self.vp = torch.empty_like(self.kp)
             self.cp = torch.empty((n_pages, Hkv, P, d // 4), dtype=torch.uint8, device=dev)
@@ -902,11 +904,9 @@ class BatchAppendState:
         s = self.s2 if stream is None else stream
         with torch.cuda.stream(s):
             ch = self.chunks[i % len(self.chunks)]
-            if self.paged:   # the chunk's four pages, one encode call each
-                for j, pg in enumerate(self.spare):
-                    adamas.encode_keys(ch[:, :, j * P:(j + 1) * P].contiguous(),
-                                       self.cp[pg:pg + 1], x_copy=self.kp[pg:pg + 1],
-                                       stream=s)
+            if self.paged:   # the chunk into its four spare pool pages, one call
+                adamas.encode_keys_paged(ch, self.cp, self.spare_table, x_pool=self.kp,
+                                         stream=s)
             else:
                 adamas.encode_keys(ch, self.codes[b:b + 1], pos=n, x_copy=self.k[b:b + 1],
                                    stream=s)

@@ -86,6 +86,8 @@ def load(variant: str | None = None):
     P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)
     lib.adamas_encode_keys.argtypes = [P, i32, i32, i32, i64, i32, P, i64, i64, P, P]
+    lib.adamas_encode_keys_paged.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, i32, i32,
+                                             i32, i64, P]
     lib.adamas_score.argtypes = [P, P, i32, i32, i32, i32, i64, i64, P, P]
     lib.adamas_select_topk.argtypes = [P, i32, i32, i64, i32, i32, P, P, sz, P]
     lib.adamas_sparse_attend.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i64, i32, f32, P, P,
@@ -134,7 +136,7 @@ def load(variant: str | None = None):
     lib.adamas_wall_clock_khz.restype = i32
     for fn in ("adamas_set_decode_mode", "adamas_decode_path"):
         getattr(lib, fn).restype = i32
-    for fn in ("adamas_encode_keys", "adamas_score", "adamas_select_topk", "adamas_sparse_attend",
+    for fn in ("adamas_encode_keys", "adamas_encode_keys_paged", "adamas_score", "adamas_select_topk", "adamas_sparse_attend",
                "adamas_decode_step", "adamas_select_topk_keep", "adamas_decode_step_keep",
                "adamas_decode_append_step", "adamas_decode_paged_step"):
         getattr(lib, fn).restype = i32
@@ -258,6 +260,34 @@ def encode_keys(x: torch.Tensor, codes: torch.Tensor, pos: int = 0,
                                    _stream(x, stream))
     _check(st, "adamas_encode_keys")
     return codes
+
+
+def encode_keys_paged(x: torch.Tensor, code_pool: torch.Tensor, page_table: torch.Tensor,
+                      pos: int = 0, x_pool: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """x [batch][heads][n][d] (tokens [pos, pos+n) of each sequence) -> the code
+    rows in code_pool [n_pages][heads][page][d/4] that page_table [batch][max_pages]
+    maps them to (adamas_encode_keys_paged); x_pool: optional raw-row pool."""
+    if x.dim() != 4 or code_pool.dim() != 4 or code_pool.dtype != torch.uint8:
+        raise ValueError("x must be [batch][heads][n][d] and code_pool uint8 "
+                         "[n_pages][heads][page][d/4]")
+    batch, heads, n, d = x.shape
+    n_pages, page = code_pool.shape[0], code_pool.shape[2]
+    if tuple(code_pool.shape) != (n_pages, heads, page, d // 4):
+        raise ValueError(f"code_pool shape {tuple(code_pool.shape)} does not match x "
+                         f"{tuple(x.shape)}")
+    if (page_table.dim() != 2 or page_table.shape[0] != batch or
+            page_table.dtype != torch.int32):
+        raise ValueError("page_table must be int32 [batch][max_pages]")
+    if x_pool is not None and (tuple(x_pool.shape) != (n_pages, heads, page, d) or
+                               x_pool.dtype != x.dtype):
+        raise ValueError("x_pool must be [n_pages][heads][page][d] of x's dtype")
+    st = load().adamas_encode_keys_paged(
+        _dev_ptr(x, "x"), _dtype_code(x), batch, heads, n, d, _dev_ptr(code_pool, "code_pool"),
+        _dev_ptr(x_pool, "x_pool"), _dev_ptr(page_table, "page_table"), page, n_pages,
+        page_table.shape[1], pos, _stream(x, stream))
+    _check(st, "adamas_encode_keys_paged")
+    return code_pool
 
 
 def encode_query(q: torch.Tensor, stream=None) -> torch.Tensor:

@@ -213,6 +213,39 @@ int adamas_encode_keys(const void* x, int dtype, int batch, int heads, int64_t n
   return launch_status();
 }
 
+int adamas_encode_keys_paged(const void* x, int dtype, int batch, int heads, int64_t n,
+                             int head_dim, uint8_t* code_pool, void* x_pool,
+                             const int32_t* page_table, int page_size, int n_pages,
+                             int max_pages, int64_t pos, hipStream_t stream) {
+  if (!valid_dtype(dtype) || !valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;
+  if (page_size < 1024 || page_size > 16384 || (page_size & (page_size - 1)) != 0)
+    return ADAMAS_ERR_UNSUPPORTED;
+  if (batch < 1 || heads < 1 || n < 0 || pos < 0 || n_pages < 1 || max_pages < 1)
+    return ADAMAS_ERR_INVALID;
+  const int64_t logical = (int64_t)max_pages * page_size;
+  if (pos > logical || n > logical - pos) return ADAMAS_ERR_INVALID;
+  // pool rows n_pages * heads * page_size of up to 256 elements must be addressable
+  if ((int64_t)n_pages * heads > (INT64_MAX / 1024) / page_size) return ADAMAS_ERR_INVALID;
+  if ((int64_t)batch * heads > (INT64_MAX / 1024) / (n > 0 ? n : 1)) return ADAMAS_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(code_pool) || page_table == nullptr ||
+      (reinterpret_cast<uintptr_t>(page_table) & 3) != 0)
+    return ADAMAS_ERR_INVALID;
+  if (x_pool != nullptr && !aligned16(x_pool)) return ADAMAS_ERR_INVALID;
+  if (n == 0) return ADAMAS_OK;
+  const int64_t nvec = (int64_t)batch * heads * n;
+  const int64_t slots = kEncodeThreads / 16;
+  const int64_t blocks64 = (nvec + slots - 1) / slots;
+  const unsigned blocks = (unsigned)(blocks64 < 8192 ? blocks64 : 8192);
+  int log2 = 0;
+  while ((1 << log2) < page_size) ++log2;
+  const EncodePages pg{page_table, max_pages, log2, n_pages};
+  with_dim(head_dim, [&](auto dc) {
+    k_encode<decltype(dc)::value, true><<<blocks, kEncodeThreads, 0, stream>>>(
+        x, dtype == ADAMAS_BF16, n, nvec, code_pool, 0, pos, x_pool, heads, encode_rule(), pg);
+  });
+  return launch_status();
+}
+
 int adamas_score(const uint8_t* q_codes, const uint8_t* k_codes, int B, int Hq, int Hkv,
                  int head_dim, int64_t cap, int64_t n_ctx, uint16_t* dist, hipStream_t stream) {
   if (!valid_dim(head_dim)) return ADAMAS_ERR_UNSUPPORTED;

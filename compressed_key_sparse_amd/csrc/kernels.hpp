@@ -58,13 +58,23 @@ constexpr int kAttendRowsPerBatch = (kAttendThreads / 16) * kAttendRowsPerSlot; 
 // §2.1 + §2.2 + §3.1 for keys (or queries): one 16-lane slot per vector
 // (kEncodeThreads / 16 vectors per workgroup), grid-stride over the
 // batch*heads*n vectors of x[batch*heads][n][D].
-template <int D>
+// With PG the code rows (and copies) go to pools of pages instead: token t
+// of sequence b, head h, is pool row (table[b][t >> page_log2] * heads + h)
+// * page + t % page; a token whose table entry is outside [0, n_pages) is
+// not stored.
+struct EncodePages {
+  const int32_t* table;  // [batch][max_pages]
+  int max_pages, page_log2, n_pages;
+};
+
+template <int D, bool PG = false>
 __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restrict__ x,
                                                            int is_bf16, int64_t n, int64_t nvec,
                                                            uint8_t* __restrict__ codes,
                                                            int64_t cap, int64_t pos,
                                                            void* __restrict__ copy, int heads,
-                                                           EncodeRule rule) {
+                                                           EncodeRule rule,
+                                                           EncodePages pg = {}) {
   // a 16-lane slot per vector: lane l holds dimensions [l*EL, l*EL + EL), so
   // the butterflies of distance below EL stay in registers and the others
   // (EL, 2EL, 4EL, 8EL) are DPP exchanges inside the slot's row of 16 lanes;
@@ -77,7 +87,14 @@ __global__ __launch_bounds__(kEncodeThreads) void k_encode(const void* __restric
   const int64_t nslots = (int64_t)gridDim.x * SLOTS;
   for (int64_t v = (int64_t)blockIdx.x * SLOTS + (threadIdx.x >> 4); v < nvec; v += nslots) {
     const int64_t bh = v / n;
-    const int64_t row = bh * cap + pos + (v - bh * n);
+    int64_t row = bh * cap + pos + (v - bh * n);
+    if constexpr (PG) {
+      const int64_t b = bh / heads, t = pos + (v - bh * n);
+      const int32_t id = pg.table[b * pg.max_pages + (t >> pg.page_log2)];
+      if (id < 0 || id >= pg.n_pages) continue;  // the same for the slot's 16 lanes
+      row = (((int64_t)id * heads + (bh - b * heads)) << pg.page_log2) +
+            (t & ((int64_t{1} << pg.page_log2) - 1));
+    }
     const int64_t src = v * D + l16 * EL;
     float y[EL];
     if (is_bf16) {

@@ -360,6 +360,35 @@ int adamas_decode_append_step(const void *q, const void *k_new, const void *v_ne
                               int32_t *idx_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * adamas_encode_keys into paged pools (the layout of adamas_decode_paged_step
+ * below): §2.1 rotation, §2.2 bucketing and §3.1 packing of a block of keys,
+ * each token's code row (and, with x_pool, its raw row) written to the pool
+ * page that its sequence's page table names; the article builds its
+ * compressed cache this way, a chunk of tokens at a time (§3.1).
+ *   x          [batch][heads][n][head_dim] elements of `dtype`: tokens
+ *              [pos, pos + n) of each of `batch` sequences.
+ *   code_pool  [n_pages][heads][page_size][head_dim/4] bytes.
+ *   x_pool     nullable; [n_pages][heads][page_size][head_dim] elements of
+ *              `dtype` receiving a verbatim copy of each row (a K pool).
+ *   page_table [batch][max_pages] int32 device memory; token t of sequence
+ *              b, head h, goes to pool row
+ *              (page_table[b][t / page_size] * heads + h) * page_size
+ *              + t % page_size.  Only the entries of pages that [pos, pos+n)
+ *              spans are read; a token whose entry lies outside [0, n_pages)
+ *              is not stored.  No other byte of the pools is touched.
+ *   page_size  a power of two in [1024, 16384].
+ * Requires batch, heads >= 1, n >= 0, pos >= 0, pos + n <= max_pages *
+ * page_size, n_pages, max_pages >= 1; x, code_pool, x_pool 16-byte aligned
+ * and page_table 4-byte aligned (else ADAMAS_ERR_INVALID; a page_size
+ * outside the range ADAMAS_ERR_UNSUPPORTED).  n = 0 is a no-op.  Codes are
+ * bit-identical to adamas_encode_keys' for the same rows.
+ */
+int adamas_encode_keys_paged(const void *x, int dtype, int batch, int heads, int64_t n,
+                             int head_dim, uint8_t *code_pool, void *x_pool,
+                             const int32_t *page_table, int page_size, int n_pages,
+                             int max_pages, int64_t pos, hipStream_t stream);
+
+/*
  * adamas_decode_append_step over paged caches.  The article's compressed
  * cache is built in chunks of a fixed number of tokens (§3.1, chunk_size
  * 1024); here every cache is a pool of such pages shared by all sequences,

@@ -77,6 +77,33 @@ def test_encode_validation(lib):
     assert f(A, 1, 1, 1, 0, 128, A, 8, 0, None, None) == OK            # n = 0: no-op
 
 
+def test_encode_paged_validation(lib):
+    f = lib.adamas_encode_keys_paged
+
+    def call(**kw):
+        return f(kw.get("x", A), kw.get("dt", 1), kw.get("batch", 2), 4, kw.get("n", 1500),
+                 kw.get("d", 128), kw.get("pool", A), kw.get("xpool", None),
+                 kw.get("table", A), kw.get("page", 1024), kw.get("n_pages", 8),
+                 kw.get("max_pages", 2), kw.get("pos", 100), None)
+    assert call(d=96) == UNSUPPORTED
+    assert call(dt=2) == UNSUPPORTED
+    assert call(page=1000) == UNSUPPORTED           # not a power of two
+    assert call(page=512) == UNSUPPORTED
+    assert call(page=32768) == UNSUPPORTED
+    assert call(pos=600) == INVALID                 # 600 + 1500 > 2 pages of 1024
+    assert call(n=-1) == INVALID
+    assert call(pos=-1) == INVALID
+    assert call(batch=0) == INVALID
+    assert call(n_pages=0) == INVALID
+    assert call(max_pages=0) == INVALID
+    assert call(x=MIS) == INVALID
+    assert call(pool=None) == INVALID
+    assert call(xpool=MIS) == INVALID
+    assert call(table=None) == INVALID
+    assert call(table=A + 2) == INVALID
+    assert call(n=0) == OK                          # a no-op
+
+
 def test_score_validation(lib):
     f = lib.adamas_score
     assert f(A, A, 1, 6, 4, 128, 100, 10, A, None) == INVALID          # Hq % Hkv
