@@ -112,3 +112,33 @@ def test_paged_pools_from_one_call_decode_alike(ora):
         outs.append((idx.cpu(), out.cpu()))
     assert torch.equal(outs[0][0], outs[1][0])
     assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_encode_paged_graph_replay(ora):
+    """Captured once in a HIP graph and replayed over new key values (the same
+    buffers refilled between replays, with eager work in between): every
+    replay leaves the oracle's rows in the pages."""
+    B, H, n, d, P, pos = 2, 4, 1500, 128, 1024, 700
+    per = (pos + n + P - 1) // P
+    n_pages = B * per + 1
+    table = torch.from_numpy(
+        np.random.default_rng(4).permutation(n_pages)[:B * per].reshape(B, per).astype(np.int32)
+    ).to(DEV)
+    x = torch.empty((B, H, n, d), dtype=torch.bfloat16, device=DEV)
+    code_pool = torch.zeros((n_pages, H, P, d // 4), dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream(DEV)
+    x.copy_(synth.random_values(x.shape, x.dtype, seed=1, device=DEV))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        adamas.encode_keys_paged(x, code_pool, table, pos=pos, stream=s)
+    tab = table.cpu().numpy()
+    for rep in range(3):
+        log(f"encode_paged graph replay {rep}")
+        x.copy_(synth.random_values(x.shape, x.dtype, seed=10 + rep, device=DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = _expected(np.zeros((n_pages, H, P, d // 4), np.uint8), ora.encode_keys(host(x)),
+                         tab, pos, n, P, [])
+        assert np.array_equal(code_pool.cpu().numpy(), want)
